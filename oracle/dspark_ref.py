@@ -1,0 +1,302 @@
+"""Plain float64 reference of DSpark's per-round token path.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import anything in ``oracle/``.  It shares no code, header, table or helper
+with the HIP library; the two meet only on the seeded inputs of ``workloads``.
+
+Every function follows one passage of the pages (cited by page title and the
+section / equation it sits in) and is written for a reader to check by eye:
+one request at a time, one position at a time, whole-vocabulary numpy vectors,
+float64 throughout.
+
+Sources (page titles):
+  [R]  "DSpark: Confidence-Scheduled Speculative Decoding with Semi-Autoregressive
+       Generation" technical review (zhongzhuzhou.org), sections "Speculative
+       Decoding: Draft, Then Verify", "The Sequential Correction" (Eq. 4),
+       "Instantiation 1: The Markov Head" (Eq. 5), "The Confidence Head" (Eq. 8),
+       "Deriving the Acceptance-Rate Identity" (Eq. 8a-8c), "The Hardware-Aware
+       Prefix Scheduler" (survival products), "Common Questions Answered"
+       (greedy decoding), "Putting It All Together" (decode-round pseudocode).
+  [E]  "Speculative decoding, from zero to DSpark" (bittide.aicompass.dev),
+       section 2 "The loop, and why it's lossless" (residual rule, bonus token).
+  [Z]  robotworld.top review (Chinese), section on the confidence head (the
+       accept rate clamped to [0, 1]).
+
+Readings where the pages are silent (each listed in the design doc):
+  * temperature T divides the summed logits, draft and target alike; T = 0 is
+    the argmax limit with the lowest index winning ties;
+  * a categorical draw is the inverse CDF: the first v (ascending vocabulary
+    order, sequential float64 cumulative sum) with C(v) > u; if rounding leaves
+    no such v, the last v with p(v) > 0;
+  * the residual norm(max(0, p_t - p_d)) is drawn by rejection against p_t
+    (propose v ~ p_t, keep it with probability max(0, 1 - p_d(v)/p_t(v))), at
+    most ``max_proposals`` times, then by the inverse CDF of the residual
+    itself; both routes have exactly the residual law;
+  * the survival products use the analytical acceptance c*_k for every block
+    position along the drafted prefix, or given confidences when supplied.
+"""
+
+import math
+
+import numpy as np
+
+from . import philox
+
+EXEMPT_RADIUS = 1e-6   # draws closer than this to a decision boundary may differ on the GPU
+
+
+# ----------------------------------------------------------------------------
+# Inputs
+# ----------------------------------------------------------------------------
+
+def weights_as_f64(w, wdtype):
+    """The exact float64 values of a weight array stored as bf16 bit patterns
+    (uint16) or as float32."""
+    if wdtype == "bf16":
+        bits = np.asarray(w, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    if wdtype == "f32":
+        return np.asarray(w, dtype=np.float32).astype(np.float64)
+    raise ValueError("unknown weight dtype %r" % (wdtype,))
+
+
+# ----------------------------------------------------------------------------
+# Distributions
+# ----------------------------------------------------------------------------
+
+def markov_bias(W1, W2, prev):
+    """Eq. 5 of [R] ("Instantiation 1: The Markov Head"): the bigram bias row
+    B(prev, .) = W1[prev] W2, a length-V vector."""
+    return W1[prev] @ W2
+
+
+def draft_logits(U_row, W1, W2, prev, T):
+    """Logits of one draft position, Eq. 4 of [R]: base logits U_k plus the
+    Markov bias of the previous token, divided by the temperature (T > 0) or
+    left unscaled for the argmax limit (T = 0)."""
+    l = np.asarray(U_row, dtype=np.float64) + markov_bias(W1, W2, prev)
+    return l / T if T > 0 else l
+
+
+def target_logits(tgt_row, T):
+    """Target logits of one position, divided by the temperature when T > 0."""
+    l = np.asarray(tgt_row, dtype=np.float64)
+    return l / T if T > 0 else l
+
+
+def softmax(l):
+    """Exact per-position softmax (the normalised exponential of Eq. 4 of [R]).
+    Returns (p, log-normaliser).  -inf logits get probability 0."""
+    m = np.max(l)
+    e = np.exp(l - m)
+    z = e.sum()
+    return e / z, m + math.log(z)
+
+
+def first_argmax(l):
+    """argmax with the lowest index winning ties (np.argmax returns the first)."""
+    return int(np.argmax(l))
+
+
+def inverse_cdf(p, u):
+    """Categorical draw by inverse CDF: the first v with C(v) > u, where
+    C(v) = p(0) + ... + p(v) is summed sequentially in ascending order.
+    Returns (v, distance of u to the nearer edge of v's CDF interval)."""
+    C = np.cumsum(p)
+    v = int(np.searchsorted(C, u, side="right"))
+    if v >= len(p):
+        v = int(np.flatnonzero(p > 0)[-1])
+    lo = C[v - 1] if v > 0 else 0.0
+    return v, min(abs(u - lo), abs(C[v] - u))
+
+
+# ----------------------------------------------------------------------------
+# Draft: semi-autoregressive Markov-head sampling
+# ----------------------------------------------------------------------------
+
+def markov_draft(U, W1, W2, x0, T, seeds, rnd, requests=None):
+    """Sample the gamma block positions of every request left to right
+    ([R] "The Sequential Correction", Eq. 4; Markov bias Eq. 5; the decode-round
+    pseudocode steps 3-5).  Position k uses the token drawn at k-1, the anchor
+    x0 at k = 1.
+
+    U: [B][gamma][V] float32 base logits; W1 [V][r], W2 [r][V] float64 values;
+    x0: [B] anchors; seeds: [B] uint64 request keys; rnd: round counter.
+    Returns dict with tokens [B][gamma] int32, prob [B][gamma] (p_d^k(x_k)),
+    lse [B][gamma] (log-normaliser of the draft logits; 0 at T = 0) and dist
+    [B][gamma] (distance of each uniform to its CDF edge; top-2 logit gap at
+    T = 0).  Only rows in ``requests`` (default: all) are computed.
+    """
+    B, gamma, V = U.shape
+    reqs = range(B) if requests is None else requests
+    tokens = np.full((B, gamma), -1, dtype=np.int32)
+    prob = np.full((B, gamma), np.nan)
+    lse = np.full((B, gamma), np.nan)
+    dist = np.full((B, gamma), np.inf)
+    for b in reqs:
+        prev = int(x0[b])
+        for k in range(1, gamma + 1):
+            l = draft_logits(U[b, k - 1], W1, W2, prev, T)
+            if T == 0:
+                x = first_argmax(l)
+                top2 = np.partition(l, -2)[-2:]
+                tokens[b, k - 1], prob[b, k - 1], lse[b, k - 1] = x, 1.0, 0.0
+                dist[b, k - 1] = top2[1] - top2[0]
+            else:
+                p, z = softmax(l)
+                u = philox.uniform(int(seeds[b]), rnd, k, philox.STREAM_DRAFT)
+                x, d = inverse_cdf(p, u)
+                tokens[b, k - 1], prob[b, k - 1], lse[b, k - 1] = x, p[x], z
+                dist[b, k - 1] = d
+            prev = x
+    return dict(tokens=tokens, prob=prob, lse=lse, dist=dist)
+
+
+# ----------------------------------------------------------------------------
+# Verify: lossless rejection sampling
+# ----------------------------------------------------------------------------
+
+def residual_sample(pt, pd, seed, rnd, j, max_proposals, dists):
+    """Draw from norm(max(0, p_t - p_d)), the resampling law at the first
+    rejection ([E] section 2).
+
+    Rejection against p_t: proposal i takes words 0 and 1 of the stream-2
+    block (rnd, j, 2, i); v ~ p_t by inverse CDF, kept iff
+    u_acc < max(0, 1 - p_d(v)/p_t(v)).  One round keeps v with probability
+    max(0, p_t(v) - p_d(v)), so a kept v follows the residual law.  After
+    ``max_proposals`` misses the residual itself is drawn by inverse CDF with
+    stream 3; if it has no mass (possible only by rounding) p_t is used.
+    Appends every boundary distance to ``dists``.
+    """
+    for i in range(max_proposals):
+        w = philox.block(seed, rnd, j, philox.STREAM_RESIDUAL, i)
+        u_prop, u_acc = philox.to_uniform(w[0]), philox.to_uniform(w[1])
+        v, d = inverse_cdf(pt, u_prop)
+        dists.append(d)
+        keep = max(0.0, 1.0 - pd[v] / pt[v])
+        dists.append(abs(u_acc - keep))
+        if u_acc < keep:
+            return v
+    res = np.maximum(0.0, pt - pd)
+    mass = res.sum()
+    u = philox.uniform(seed, rnd, j, philox.STREAM_FALLBACK)
+    v, d = inverse_cdf(res / mass if mass > 0 else pt, u)
+    dists.append(d)
+    return v
+
+
+def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=16,
+           requests=None):
+    """Rejection-sampling verification of every request's drafted block
+    ([R] "Speculative Decoding: Draft, Then Verify" step 3; [E] section 2).
+
+    Left to right, x_k is accepted with probability
+    alpha_k = min(1, p_t^k(x_k) / p_d^k(x_k)) (accept iff u < alpha_k, u from
+    stream 1).  The first rejection at j emits a residual draw and stops; if
+    all gamma positions pass, a bonus token is drawn from the target row
+    gamma+1 (stream 2, index 0).  At T = 0 acceptance is the exact match
+    x_k == argmax tgt_k and the correction / bonus is the target argmax
+    ([R] "Common Questions Answered", greedy decoding).
+
+    tgt: [B][gamma+1][V].  p_d^k is recomputed here from U, W1, W2 and the
+    drafted prefix.  Returns dict: accept_len [B] (n), out_tokens [B][gamma+1]
+    (x_1..x_n, y, -1...), accept_prob [B][gamma] (alpha_k of tested positions,
+    NaN after), min_dist [B] (smallest boundary distance of all draws of the
+    request; inf at T = 0).
+    """
+    B, gamma, V = U.shape
+    reqs = range(B) if requests is None else requests
+    accept_len = np.full(B, -1, dtype=np.int32)
+    out_tokens = np.full((B, gamma + 1), -1, dtype=np.int32)
+    accept_prob = np.full((B, gamma), np.nan)
+    min_dist = np.full(B, np.inf)
+    for b in reqs:
+        seed = int(seeds[b])
+        prev = int(x0[b])
+        dists = []
+        emitted = []
+        n = gamma
+        for k in range(1, gamma + 1):
+            x = int(draft_tokens[b, k - 1])
+            lt = target_logits(tgt[b, k - 1], T)
+            if T == 0:
+                y = first_argmax(lt)
+                accept_prob[b, k - 1] = 1.0 if y == x else 0.0
+                if y == x:
+                    emitted.append(x)
+                    prev = x
+                    continue
+                emitted.append(y)
+                n = k - 1
+                break
+            pd, _ = softmax(draft_logits(U[b, k - 1], W1, W2, prev, T))
+            pt, _ = softmax(lt)
+            alpha = min(1.0, pt[x] / pd[x])
+            accept_prob[b, k - 1] = alpha
+            u = philox.uniform(seed, rnd, k, philox.STREAM_ACCEPT)
+            dists.append(abs(u - alpha))
+            if u < alpha:
+                emitted.append(x)
+                prev = x
+                continue
+            emitted.append(residual_sample(pt, pd, seed, rnd, k, max_proposals, dists))
+            n = k - 1
+            break
+        if n == gamma:
+            lt = target_logits(tgt[b, gamma], T)
+            if T == 0:
+                emitted.append(first_argmax(lt))
+            else:
+                pt, _ = softmax(lt)
+                u = philox.uniform(seed, rnd, gamma + 1, philox.STREAM_RESIDUAL)
+                y, d = inverse_cdf(pt, u)
+                dists.append(d)
+                emitted.append(y)
+        accept_len[b] = n
+        out_tokens[b, :len(emitted)] = emitted
+        min_dist[b] = min(dists) if dists else np.inf
+    return dict(accept_len=accept_len, out_tokens=out_tokens,
+                accept_prob=accept_prob, min_dist=min_dist)
+
+
+# ----------------------------------------------------------------------------
+# Survival products
+# ----------------------------------------------------------------------------
+
+def acceptance_rate(pd, pt):
+    """Analytical acceptance of one position, Eq. 8a of [R]:
+    sum_v min(p_d(v), p_t(v)), clamped to [0, 1] as the accept-rate label is in
+    [Z]."""
+    return min(1.0, max(0.0, float(np.minimum(pd, pt).sum())))
+
+
+def survival(U, W1, W2, x0, draft_tokens, tgt, T, conf=None, requests=None):
+    """Prefix survival a_{b,k} = prod_{i<=k} c_{b,i} ([R] "The Hardware-Aware
+    Prefix Scheduler", step 1 of Algorithm 1).
+
+    With ``conf`` ([B][gamma]) the products are taken of the given
+    confidences.  Otherwise c_{b,k} is the analytical acceptance c*_k of Eq. 8
+    at every block position along the drafted prefix (all gamma positions,
+    also those after a rejection); at T = 0 it is the indicator
+    x_k == argmax tgt_k.  Returns (c_star [B][gamma] or None, survival).
+    """
+    if conf is not None:
+        conf = np.asarray(conf, dtype=np.float64)
+        return None, np.cumprod(conf, axis=1)
+    B, gamma, V = U.shape
+    reqs = range(B) if requests is None else requests
+    c = np.full((B, gamma), np.nan)
+    for b in reqs:
+        prev = int(x0[b])
+        for k in range(1, gamma + 1):
+            x = int(draft_tokens[b, k - 1])
+            lt = target_logits(tgt[b, k - 1], T)
+            if T == 0:
+                c[b, k - 1] = 1.0 if first_argmax(lt) == x else 0.0
+            else:
+                pd, _ = softmax(draft_logits(U[b, k - 1], W1, W2, prev, T))
+                pt, _ = softmax(lt)
+                c[b, k - 1] = acceptance_rate(pd, pt)
+            prev = x
+    return c, np.cumprod(c, axis=1)
