@@ -14,7 +14,9 @@ layout below is this implementation's reading:
 * counter = (round, position k, stream, index)  one block of four words
 * streams: 0 draft sample, 1 acceptance test, 2 residual proposal / bonus,
   3 exact residual fallback
-* a uniform in (0, 1) is ((w >> 11) + 0.5) * 2**-53, exact in float64.
+* a uniform in (0, 1) is ((w >> 12) + 0.5) * 2**-52: 52 integer bits plus a
+  half need 53 significant bits, so the value is exact in float64 and lies in
+  [2**-53, 1 - 2**-53].
 """
 
 MASK64 = (1 << 64) - 1
@@ -56,8 +58,8 @@ def philox4x64(counter, key, rounds=10):
 
 
 def to_uniform(word):
-    """Map a 64-bit word to the float64 uniform ((w >> 11) + 0.5) / 2**53 in (0, 1)."""
-    return ((int(word) >> 11) + 0.5) * (2.0 ** -53)
+    """Map a 64-bit word to the float64 uniform ((w >> 12) + 0.5) / 2**52 in (0, 1)."""
+    return ((int(word) >> 12) + 0.5) * (2.0 ** -52)
 
 
 def block(seed, rnd, k, stream, index=0):

@@ -52,13 +52,16 @@ def test_stream_layout_counters():
 
 
 def test_uniform_map_is_open_interval_and_exact():
-    assert philox.to_uniform(0) == 2.0 ** -54
-    assert philox.to_uniform(philox.MASK64) == 1.0 - 2.0 ** -54
-    # 53-bit grid: neighbouring top-53-bit values differ by exactly 2**-53
+    from fractions import Fraction
+    assert philox.to_uniform(0) == 2.0 ** -53
+    top = philox.to_uniform(philox.MASK64)
+    assert top < 1.0 and Fraction(top) == 1 - Fraction(1, 2 ** 53)
+    # every word maps to exactly ((w >> 12) + 1/2) / 2**52, no rounding
+    for w in (0x123456789ABCDEF0, philox.MASK64 - 4095, 1 << 63, (1 << 63) - 1):
+        assert Fraction(philox.to_uniform(w)) == (Fraction(w >> 12) + Fraction(1, 2)) / 2 ** 52
+    # low 12 bits are ignored
     w = 0x123456789ABCDEF0
-    assert philox.to_uniform(w + (1 << 11)) - philox.to_uniform(w) == 2.0 ** -53
-    # low 11 bits are ignored
-    assert philox.to_uniform(w | 0x7FF) == philox.to_uniform(w & ~0x7FF)
+    assert philox.to_uniform(w | 0xFFF) == philox.to_uniform(w & ~0xFFF)
 
 
 def test_uniforms_look_uniform():
