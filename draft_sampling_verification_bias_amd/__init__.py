@@ -1,0 +1,245 @@
+"""Python binding of libdspark: DSpark's per-round token path on MI355X.
+
+Thin ctypes marshalling over the C ABI declared in ``include/dspark.h``:
+every step of the path runs in the library's HIP kernels; this module only
+checks tensor metadata, passes device pointers and the current HIP stream,
+and raises on a non-zero status.  PyTorch provides device memory and streams.
+
+Functions (same names as the C entry points, without the ``dspark_`` prefix):
+  markov_bias, markov_draft, verify, survival, workspace_size, version.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "DsparkError", "OP_DRAFT", "OP_VERIFY", "OP_SURVIVAL", "MAX_RESIDUAL_PROPOSALS",
+    "library_path", "load", "version", "workspace_size", "markov_bias",
+    "markov_draft", "verify", "survival",
+]
+
+OP_DRAFT, OP_VERIFY, OP_SURVIVAL = 0, 1, 2
+_F32, _BF16 = 0, 1
+MAX_RESIDUAL_PROPOSALS = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, func, status, message):
+        super().__init__("%s failed: %s (status %d)" % (func, message, status))
+        self.status = status
+
+
+def library_path():
+    return os.path.join(_HERE, "libdspark.so")
+
+
+def load():
+    """Load libdspark.so (built in-tree by ``python -m draft_sampling_verification_bias_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError("libdspark.so is not built (%s); run "
+                           "`python -m draft_sampling_verification_bias_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    P, I, F, U64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_size_t
+    lib.dspark_version.restype = I
+    lib.dspark_version.argtypes = []
+    lib.dspark_status_string.restype = ctypes.c_char_p
+    lib.dspark_status_string.argtypes = [I]
+    lib.dspark_workspace_size.restype = SZ
+    lib.dspark_workspace_size.argtypes = [I, I, I, I, I]
+    lib.dspark_markov_bias.restype = I
+    lib.dspark_markov_bias.argtypes = [P, P, I, P, I, I, I, P, P]
+    lib.dspark_markov_draft.restype = I
+    lib.dspark_markov_draft.argtypes = [P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_verify.restype = I
+    lib.dspark_verify.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_survival.restype = I
+    lib.dspark_survival.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P]
+    _LIB = lib
+    return lib
+
+
+def version():
+    return load().dspark_version()
+
+
+def workspace_size(op, B, gamma, V, r):
+    return int(load().dspark_workspace_size(op, B, gamma, V, r))
+
+
+def _check(func, status):
+    if status != 0:
+        msg = load().dspark_status_string(status).decode()
+        raise DsparkError(func, status, msg)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+def _wdtype(W1, W2):
+    if W1.dtype != W2.dtype:
+        raise ValueError("W1 and W2 must share a dtype")
+    if W1.dtype == torch.bfloat16:
+        return _BF16
+    if W1.dtype == torch.float32:
+        return _F32
+    raise ValueError("weights must be bfloat16 or float32, got %s" % W1.dtype)
+
+
+def _stream(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(op, B, gamma, V, r, workspace, device):
+    need = workspace_size(op, B, gamma, V, r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def markov_bias(W1, W2, tokens, out=None, stream=None):
+    """out[i] = W1[tokens[i]] @ W2 (float32 [n][V])."""
+    V, r = W1.shape
+    _dev(W1, "W1")
+    _dev(W2, "W2", W1.dtype, (r, V))
+    _dev(tokens, "tokens", torch.int32)
+    n = tokens.numel()
+    if out is None:
+        out = torch.empty((n, V), dtype=torch.float32, device=W1.device)
+    _dev(out, "out", torch.float32, (n, V))
+    st = load().dspark_markov_bias(_p(W1), _p(W2), _wdtype(W1, W2), _p(tokens), n, V, r, _p(out),
+                                   _stream(stream, W1.device))
+    _check("dspark_markov_bias", st)
+    return out
+
+
+def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=None, stream=None):
+    """Draft gamma tokens per request.  Returns (draft_tokens, draft_prob, draft_lse)."""
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    _dev(U, "U", torch.float32)
+    _dev(W1, "W1", None, (V, r))
+    _dev(W2, "W2", W1.dtype, (r, V))
+    _dev(x0, "x0", torch.int32, (B,))
+    if seeds is not None:
+        _dev(seeds, "seeds", torch.uint64, (B,))
+    if out is None:
+        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    tok, prob, lse = out
+    _dev(tok, "draft_tokens", torch.int32, (B, gamma))
+    _dev(prob, "draft_prob", torch.float32, (B, gamma))
+    _dev(lse, "draft_lse", torch.float32, (B, gamma))
+    ws, nbytes = _workspace(OP_DRAFT, B, gamma, V, r, workspace, dev)
+    st = load().dspark_markov_draft(_p(U), _p(W1), _p(W2), _wdtype(W1, W2), _p(x0), B, gamma, V, r,
+                                    float(temperature), _p(seeds), int(rnd), _p(tok), _p(prob), _p(lse),
+                                    _p(ws), nbytes, _stream(stream, dev))
+    _check("dspark_markov_draft", st)
+    return tok, prob, lse
+
+
+def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, rnd, out=None,
+           with_accept_prob=True, workspace=None, stream=None):
+    """Rejection-sampling verification.  Returns (accept_len, out_tokens, accept_prob or None)."""
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    dev = target.device
+    _dev(target, "target", torch.float32)
+    r = W1.shape[1] if W1 is not None else 16
+    if U is not None:
+        _dev(U, "U", torch.float32, (B, gamma, V))
+    if W1 is not None:
+        _dev(W1, "W1", None, (V, r))
+        _dev(W2, "W2", W1.dtype, (r, V))
+    wd = _wdtype(W1, W2) if W1 is not None else _BF16
+    _dev(x0, "x0", torch.int32, (B,))
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, gamma))
+    if draft_prob is not None:
+        _dev(draft_prob, "draft_prob", torch.float32, (B, gamma))
+    if seeds is not None:
+        _dev(seeds, "seeds", torch.uint64, (B,))
+    if out is None:
+        out = (torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B, gamma + 1), dtype=torch.int32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev) if with_accept_prob else None)
+    alen, otok, aprob = out
+    _dev(alen, "accept_len", torch.int32, (B,))
+    _dev(otok, "out_tokens", torch.int32, (B, gamma + 1))
+    if aprob is not None:
+        _dev(aprob, "accept_prob", torch.float32, (B, gamma))
+    ws, nbytes = _workspace(OP_VERIFY, B, gamma, V, r, workspace, dev)
+    st = load().dspark_verify(_p(U), _p(W1), _p(W2), wd, _p(x0), _p(draft_tokens), _p(draft_prob), _p(target),
+                              B, gamma, V, r, float(temperature), _p(seeds), int(rnd), _p(alen), _p(otok),
+                              _p(aprob), _p(ws), nbytes, _stream(stream, dev))
+    _check("dspark_verify", st)
+    return alen, otok, aprob
+
+
+def survival(U, W1, W2, x0, draft_tokens, draft_lse, target, temperature, conf=None, out=None,
+             with_c_star=True, workspace=None, stream=None):
+    """Prefix survival products.  Returns (c_star or None, survival)."""
+    if conf is not None:
+        B, gamma = conf.shape
+        dev = conf.device
+        _dev(conf, "conf", torch.float32)
+        surv = out[1] if out is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        _dev(surv, "survival", torch.float32, (B, gamma))
+        st = load().dspark_survival(None, None, None, _BF16, None, None, None, None, _p(conf), B, gamma, 2, 16,
+                                    0.0, None, _p(surv), None, 0, _stream(stream, dev))
+        _check("dspark_survival", st)
+        return None, surv
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    dev = target.device
+    _dev(target, "target", torch.float32)
+    r = W1.shape[1] if W1 is not None else 16
+    if U is not None:
+        _dev(U, "U", torch.float32, (B, gamma, V))
+    if W1 is not None:
+        _dev(W1, "W1", None, (V, r))
+        _dev(W2, "W2", W1.dtype, (r, V))
+    wd = _wdtype(W1, W2) if W1 is not None else _BF16
+    _dev(x0, "x0", torch.int32, (B,))
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, gamma))
+    if draft_lse is not None:
+        _dev(draft_lse, "draft_lse", torch.float32, (B, gamma))
+    if out is None:
+        out = (torch.empty((B, gamma), dtype=torch.float32, device=dev) if with_c_star else None,
+               torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    cst, surv = out
+    if cst is not None:
+        _dev(cst, "c_star", torch.float32, (B, gamma))
+    _dev(surv, "survival", torch.float32, (B, gamma))
+    ws, nbytes = _workspace(OP_SURVIVAL, B, gamma, V, r, workspace, dev)
+    st = load().dspark_survival(_p(U), _p(W1), _p(W2), wd, _p(x0), _p(draft_tokens), _p(draft_lse), _p(target),
+                                None, B, gamma, V, r, float(temperature), _p(cst), _p(surv), _p(ws), nbytes,
+                                _stream(stream, dev))
+    _check("dspark_survival", st)
+    return cst, surv

@@ -1,0 +1,175 @@
+// The libdspark C ABI: argument validation (host only, before any HIP call),
+// workspace sizing and dispatch to the kernel launchers.
+#include <math.h>
+#include <stdint.h>
+
+#include "dspark.h"
+#include "launch.hpp"
+
+using namespace dspark;
+
+namespace {
+
+constexpr int kMaxB = 65536;
+constexpr int kMaxGamma = 32;
+constexpr int kMaxR = 512;
+
+bool sizes_ok(int B, int gamma, int V, int r) {
+  return B >= 1 && B <= kMaxB && gamma >= 1 && gamma <= kMaxGamma && V >= 2 && r >= 16 && r <= kMaxR &&
+         r % 16 == 0;
+}
+
+bool temp_ok(float T) { return isfinite(T) && T >= 0.0f; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// A required pointer: non-null and aligned.
+bool req(const void* p, size_t a) { return p != nullptr && aligned(p, a); }
+
+// An optional pointer: null, or aligned.
+bool opt(const void* p, size_t a) { return p == nullptr || aligned(p, a); }
+
+bool dtype_ok(dspark_dtype d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
+
+dspark_status from_hip(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int dspark_version(void) { return 100; }
+
+const char* dspark_status_string(dspark_status s) {
+  switch (s) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DSPARK_ERR_UNSUPPORTED: return "unsupported weight dtype";
+    case DSPARK_ERR_WORKSPACE: return "workspace too small";
+    case DSPARK_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t dspark_workspace_size(dspark_op op, int B, int gamma, int V, int r) {
+  if (!sizes_ok(B, gamma, V, r)) return 0;
+  switch (op) {
+    case DSPARK_OP_DRAFT: return draft_workspace(B, gamma, V, r);
+    case DSPARK_OP_VERIFY: return verify_workspace(B, gamma, V, r);
+    case DSPARK_OP_SURVIVAL: return survival_workspace(B, gamma, V, r);
+    default: return 0;
+  }
+}
+
+dspark_status dspark_markov_bias(const void* W1, const void* W2, dspark_dtype wdtype, const int32_t* tokens,
+                                 int n, int V, int r, float* out, hipStream_t stream) {
+  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!sizes_ok(1, 1, V, r) || n < 1 || n > (1 << 20)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!req(W1, 16) || !req(W2, 16) || !req(tokens, 4) || !req(out, 4)) return DSPARK_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_markov_bias(W1, W2, wdtype == DSPARK_BF16, tokens, n, V, r, out, stream));
+}
+
+dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
+                                  const int32_t* x0, int B, int gamma, int V, int r, float temperature,
+                                  const uint64_t* seeds, uint64_t round, int32_t* draft_tokens, float* draft_prob,
+                                  float* draft_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(x0, 4) || !req(draft_tokens, 4) ||
+      !req(draft_prob, 4) || !req(draft_lse, 4) || !req(workspace, 16))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (temperature > 0.0f && !req(seeds, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < draft_workspace(B, gamma, V, r)) return DSPARK_ERR_WORKSPACE;
+  DraftArgs a = {};
+  a.U = U;
+  a.W1 = W1;
+  a.W2 = W2;
+  a.x0 = x0;
+  a.seeds = seeds;
+  a.round = round;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.r = r;
+  a.temperature = temperature;
+  a.tokens = draft_tokens;
+  a.prob = draft_prob;
+  a.lse = draft_lse;
+  a.ws = workspace;
+  return from_hip(launch_draft(a, wdtype == DSPARK_BF16, stream));
+}
+
+dspark_status dspark_verify(const float* U, const void* W1, const void* W2, dspark_dtype wdtype, const int32_t* x0,
+                            const int32_t* draft_tokens, const float* draft_prob, const float* target_logits, int B,
+                            int gamma, int V, int r, float temperature, const uint64_t* seeds, uint64_t round,
+                            int32_t* accept_len, int32_t* out_tokens, float* accept_prob, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
+  const bool greedy = temperature == 0.0f;
+  if (!req(x0, 4) || !req(draft_tokens, 4) || !req(target_logits, 16) || !req(accept_len, 4) ||
+      !req(out_tokens, 4) || !opt(accept_prob, 4) || !req(workspace, 16))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!greedy && (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(draft_prob, 4) || !req(seeds, 8)))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < verify_workspace(B, gamma, V, r)) return DSPARK_ERR_WORKSPACE;
+  VerifyArgs a = {};
+  a.U = U;
+  a.W1 = W1;
+  a.W2 = W2;
+  a.x0 = x0;
+  a.draft_tokens = draft_tokens;
+  a.draft_prob = draft_prob;
+  a.target = target_logits;
+  a.seeds = seeds;
+  a.round = round;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.r = r;
+  a.temperature = temperature;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.accept_prob = accept_prob;
+  a.ws = workspace;
+  return from_hip(launch_verify(a, wdtype == DSPARK_BF16, stream));
+}
+
+dspark_status dspark_survival(const float* U, const void* W1, const void* W2, dspark_dtype wdtype, const int32_t* x0,
+                              const int32_t* draft_tokens, const float* draft_lse, const float* target_logits,
+                              const float* conf, int B, int gamma, int V, int r, float temperature, float* c_star,
+                              float* survival, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!req(survival, 4)) return DSPARK_ERR_INVALID_ARGUMENT;
+  SurvivalArgs a = {};
+  a.B = B;
+  a.gamma = gamma;
+  a.survival = survival;
+  if (conf) {
+    if (B < 1 || B > kMaxB || gamma < 1 || gamma > kMaxGamma || !aligned(conf, 4))
+      return DSPARK_ERR_INVALID_ARGUMENT;
+    a.conf = conf;
+    return from_hip(launch_survival(a, false, stream));
+  }
+  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
+  const bool greedy = temperature == 0.0f;
+  if (!req(x0, 4) || !req(draft_tokens, 4) || !req(target_logits, 16) || !opt(c_star, 4) || !req(workspace, 16))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!greedy && (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(draft_lse, 4)))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < survival_workspace(B, gamma, V, r)) return DSPARK_ERR_WORKSPACE;
+  a.U = U;
+  a.W1 = W1;
+  a.W2 = W2;
+  a.x0 = x0;
+  a.draft_tokens = draft_tokens;
+  a.draft_lse = draft_lse;
+  a.target = target_logits;
+  a.V = V;
+  a.r = r;
+  a.temperature = temperature;
+  a.c_star = c_star;
+  a.ws = workspace;
+  return from_hip(launch_survival(a, wdtype == DSPARK_BF16, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+// Device helpers shared by the libdspark kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC'11).  Ten rounds of the 4x64 S-box: the two even words are
+// multiplied by the round multipliers, the 128-bit products' high halves are
+// crossed over and mixed with the odd words and the round key, the low
+// halves become the new odd words.  The key advances by the Weyl constants
+// between rounds.
+// ---------------------------------------------------------------------------
+struct Philox4 {
+  uint64_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                                 uint64_t key0, uint64_t key1) {
+  constexpr uint64_t kMulA = 0xD2E7470EE14C6C93ull;
+  constexpr uint64_t kMulB = 0xCA5A826395121157ull;
+  constexpr uint64_t kWeylA = 0x9E3779B97F4A7C15ull;
+  constexpr uint64_t kWeylB = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t hiA = __umul64hi(kMulA, c0), loA = kMulA * c0;
+    const uint64_t hiB = __umul64hi(kMulB, c2), loB = kMulB * c2;
+    const uint64_t n0 = hiB ^ c1 ^ key0;
+    const uint64_t n2 = hiA ^ c3 ^ key1;
+    c0 = n0;
+    c1 = loB;
+    c2 = n2;
+    c3 = loA;
+    key0 += kWeylA;
+    key1 += kWeylB;
+  }
+  Philox4 r;
+  r.w[0] = c0;
+  r.w[1] = c1;
+  r.w[2] = c2;
+  r.w[3] = c3;
+  return r;
+}
+
+// Random stream ids of the counter layout (round, position, stream, index).
+enum : uint64_t { kStreamDraft = 0, kStreamAccept = 1, kStreamResidual = 2, kStreamFallback = 3 };
+
+__device__ __forceinline__ Philox4 draw_block(uint64_t seed, uint64_t round, uint64_t pos,
+                                              uint64_t stream, uint64_t index) {
+  return philox4x64_10(round, pos, stream, index, seed, 0);
+}
+
+// A 64-bit word to the double ((w >> 12) + 0.5) * 2^-52: exact, inside (0, 1).
+__device__ __forceinline__ double unit_uniform(uint64_t w) {
+  return ((double)(w >> 12) + 0.5) * 0x1p-52;
+}
+
+// ---------------------------------------------------------------------------
+// Reductions.  Wave-wide ones use cross-lane shuffles; block-wide ones go
+// through a small LDS array of one slot per wave.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Argmax pair: larger value wins, the lower index on equal values.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o);
+    const int oi = __shfl_xor(i, o);
+    argmax_merge(v, i, ov, oi);
+  }
+}
+
+// Inclusive prefix sum across a wave (Hillis-Steele).
+__device__ __forceinline__ double wave_inclusive_scan(double x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Block-wide helpers for blockDim.x == kBlock (a multiple of 64, <= 1024).
+// `scratch` must hold kBlock / 64 elements; the functions synchronise.
+template <int kBlock>
+__device__ __forceinline__ float block_max(float x, float* scratch) {
+  constexpr int kWaves = kBlock / kWave;
+  x = wave_max(x);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = x;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+
+template <int kBlock, typename T>
+__device__ __forceinline__ T block_sum(T x, T* scratch) {
+  constexpr int kWaves = kBlock / kWave;
+  x = wave_sum(x);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = x;
+  __syncthreads();
+  T r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r += scratch[i];
+  __syncthreads();
+  return r;
+}
+
+template <int kBlock>
+__device__ __forceinline__ void block_argmax(float& v, int& idx, float* sv, int* si) {
+  constexpr int kWaves = kBlock / kWave;
+  wave_argmax(v, idx);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sv[w] = v;
+    si[w] = idx;
+  }
+  __syncthreads();
+  v = sv[0];
+  idx = si[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) argmax_merge(v, idx, sv[i], si[i]);
+  __syncthreads();
+}
+
+// Exclusive block prefix sum in thread order; also returns the block total.
+// `scratch` holds kBlock / 64 doubles.
+template <int kBlock>
+__device__ __forceinline__ double block_exclusive_scan(double x, double* scratch, double& total) {
+  constexpr int kWaves = kBlock / kWave;
+  const double incl = wave_inclusive_scan(x);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == kWave - 1) scratch[w] = incl;
+  __syncthreads();
+  double before = 0.0;
+  total = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) before += scratch[i];
+    total += scratch[i];
+  }
+  __syncthreads();
+  return before + incl - x;
+}
+
+// bf16 bit pattern to float (exact).
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// 2^x for the softmax terms: the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace dspark

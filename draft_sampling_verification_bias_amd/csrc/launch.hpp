@@ -1,0 +1,133 @@
+// Internal launchers of the libdspark kernels.  Host code only; arguments are
+// validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dspark.h"
+
+namespace dspark {
+
+// Vocabulary columns per tile of the MFMA tile pass and of the target passes.
+constexpr int kTileCols = 128;
+constexpr int kTgtCols = 1024;
+
+inline int tiles_of(int V, int cols) { return (V + cols - 1) / cols; }
+
+// Which per-(row, tile) summary the tile pass writes.
+enum TileMode : int {
+  kModeSample = 0,   // (max l, sum 2^((l - max) * cf))      stochastic draft
+  kModeGreedy = 1,   // (max l, argmax as int bits)          greedy draft
+  kModeOverlap = 2,  // (sum min(p_d, p_t), 0)               analytical survival
+  kModeBias = 3,     // writes the bias rows themselves       dspark_markov_bias
+};
+
+// Logical rows of the tile pass.  Row R belongs to request b = R / kper at
+// block position kk = (kper == 1 ? k0 : R % kper); its previous token is x0[b]
+// when kk == 0 and tokens[b * gamma + kk - 1] otherwise; its base-logit row is
+// U[b][kk][:] and its target row target[b][kk][:].
+struct TileArgs {
+  const float* U;
+  const void* W1;
+  const void* W2;
+  const int32_t* x0;
+  const int32_t* tokens;
+  const float* target;
+  const float* lse_d;   // [B][gamma] natural-log normaliser of the draft (overlap mode)
+  const float* lt2;     // [nrows] log2 normaliser of the target row (overlap mode)
+  float2* partials;     // [nrows][ntiles]
+  float* bias_out;      // [nrows][V] (bias mode)
+  int nrows, kper, k0;
+  int B, gamma, V, r, ntiles;
+  float cf;             // log2(e) / T; unused at T == 0
+};
+
+hipError_t launch_tile_pass(const TileArgs& a, int mode, bool bf16, hipStream_t s);
+
+struct DraftArgs {
+  const float* U;
+  const void* W1;
+  const void* W2;
+  const int32_t* x0;
+  const uint64_t* seeds;
+  uint64_t round;
+  int B, gamma, V, r;
+  float temperature;
+  int32_t* tokens;
+  float* prob;
+  float* lse;
+  void* ws;
+};
+
+size_t draft_workspace(int B, int gamma, int V, int r);
+hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s);
+
+struct VerifyArgs {
+  const float* U;
+  const void* W1;
+  const void* W2;
+  const int32_t* x0;
+  const int32_t* draft_tokens;
+  const float* draft_prob;
+  const float* target;
+  const uint64_t* seeds;
+  uint64_t round;
+  int B, gamma, V, r;
+  float temperature;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  float* accept_prob;
+  void* ws;
+  double inv_t_d;  // 1 / T, filled in by launch_verify
+};
+
+size_t verify_workspace(int B, int gamma, int V, int r);
+hipError_t launch_verify(const VerifyArgs& a, bool bf16, hipStream_t s);
+
+struct SurvivalArgs {
+  const float* U;
+  const void* W1;
+  const void* W2;
+  const int32_t* x0;
+  const int32_t* draft_tokens;
+  const float* draft_lse;
+  const float* target;
+  const float* conf;
+  int B, gamma, V, r;
+  float temperature;
+  float* c_star;
+  float* survival;
+  void* ws;
+};
+
+size_t survival_workspace(int B, int gamma, int V, int r);
+hipError_t launch_survival(const SurvivalArgs& a, bool bf16, hipStream_t s);
+
+// Target-row statistics (verify.hip), shared by verify and survival.
+//   list mode (list != null): row li is request list[li] at block position
+//     kk0; summaries go to row b of tpart.
+//   all mode: row R = b * gamma + kk for kk < gamma; summaries go to row R.
+// Sample mode writes (max t, sum 2^((t - max) * cf)) per 1024-column tile;
+// greedy mode (max t, argmax as int bits).
+struct TStatsArgs {
+  const float* target;
+  const int* list;
+  const int* count;  // device count (list mode)
+  int nall;          // rows in all mode
+  int kk0;
+  int gamma, V, ntv;
+  float cf;
+  float2* tpart;
+};
+
+hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, hipStream_t s);
+
+hipError_t launch_markov_bias(const void* W1, const void* W2, bool bf16, const int32_t* tokens,
+                              int n, int V, int r, float* out, hipStream_t s);
+
+// Round a byte count up to a 256-byte boundary (workspace carving).
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace dspark

@@ -1,0 +1,505 @@
+// dspark_verify: lossless rejection-sampling verification.
+//
+// Follows the DSpark technical review, "Speculative Decoding: Draft, Then
+// Verify" (step 3: accept x_k with probability min(1, p_t^k(x_k)/p_d^k(x_k)),
+// the first rejection ends the block) and "Speculative decoding, from zero to
+// DSpark", section 2 (on rejection draw from norm(max(0, p_t - p_d)); if all
+// positions pass, a bonus token from the position after the block).  At
+// temperature 0 acceptance is the exact argmax match of "Common Questions
+// Answered".
+//
+// Positions are processed in order with early exit: phase k only streams the
+// target rows of requests that are still alive at k (their list is built by
+// phase k-1), so each request reads target rows 1..n+1 and no more.  A phase is
+// one target-statistics kernel (per-tile max / exp-sum over 1024 columns) and
+// one decision kernel (one workgroup per request).  Residual draws propose
+// from p_t with the tile summaries and need p_d at one token only, rebuilt by
+// an r-term dot product; the rare exact-residual fallback runs two more
+// kernels over only the requests that need it.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "select.hpp"
+
+namespace dspark {
+
+constexpr int kVThreads = 256;
+constexpr int kColsPerThread = kTgtCols / kVThreads;  // 4
+
+struct FallbackInfo {
+  int j;        // rejected position (1-based)
+  int prev;     // x_{j-1}
+  double M, Z;  // target row max and exp-sum (base 2, scaled by cf)
+  double pdx;   // p_d^j(x_j)
+  double lx;    // draft logit of x_j (U + bias), float64
+};
+
+struct VerifyWs {
+  float2* tpart;        // [B][ntv] target tile summaries
+  int* lists;           // [gamma + 2][B] request lists per phase (index k)
+  int* counts;          // [gamma + 2]: counts[k] phase sizes, counts[0] fallback count
+  int* fb_list;         // [B]
+  FallbackInfo* fb;     // [B] indexed by request
+  double* fb_part;      // [B][ntv] residual mass per tile
+};
+
+static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
+  const int ntv = tiles_of(V, kTgtCols);
+  char* p = reinterpret_cast<char*>(ws);
+  VerifyWs w;
+  w.tpart = reinterpret_cast<float2*>(p);
+  p += align256((size_t)B * ntv * sizeof(float2));
+  w.lists = reinterpret_cast<int*>(p);
+  p += align256((size_t)(gamma + 2) * B * sizeof(int));
+  w.counts = reinterpret_cast<int*>(p);
+  p += align256((size_t)(gamma + 2) * sizeof(int));
+  w.fb_list = reinterpret_cast<int*>(p);
+  p += align256((size_t)B * sizeof(int));
+  w.fb = reinterpret_cast<FallbackInfo*>(p);
+  p += align256((size_t)B * sizeof(FallbackInfo));
+  w.fb_part = reinterpret_cast<double*>(p);
+  return w;
+}
+
+size_t verify_workspace(int B, int gamma, int V, int r) {
+  (void)r;
+  const int ntv = tiles_of(V, kTgtCols);
+  return align256((size_t)B * ntv * sizeof(float2)) + align256((size_t)(gamma + 2) * B * sizeof(int)) +
+         align256((size_t)(gamma + 2) * sizeof(int)) + align256((size_t)B * sizeof(int)) +
+         align256((size_t)B * sizeof(FallbackInfo)) + align256((size_t)B * ntv * sizeof(double));
+}
+
+template <bool kBf16>
+__device__ __forceinline__ double wval(const void* W, size_t idx) {
+  if constexpr (kBf16) {
+    return (double)bf16_to_float(reinterpret_cast<const uint16_t*>(W)[idx]);
+  } else {
+    return (double)reinterpret_cast<const float*>(W)[idx];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Target-row statistics, shared with dspark_survival.
+//   list mode (list != null): row li is request list[li] at block position
+//     kk0; summaries go to row b of tpart.
+//   all mode: row R = b * gamma + kk for kk < gamma; summaries go to row R.
+// Sample mode writes (max t, sum 2^((t - max) * cf)); greedy mode (max t,
+// argmax bits).
+// ---------------------------------------------------------------------------
+template <bool kGreedy>
+__global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
+  __shared__ float sv[kVThreads / kWave];
+  __shared__ int si[kVThreads / kWave];
+  const int nrows = a.list ? *a.count : a.nall;
+  const long long items = (long long)nrows * a.ntv;
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int li = (int)(it / a.ntv);
+    const int tile = (int)(it - (long long)li * a.ntv);
+    int b, kk, orow;
+    if (a.list) {
+      b = a.list[li];
+      kk = a.kk0;
+      orow = b;
+    } else {
+      b = li / a.gamma;
+      kk = li - b * a.gamma;
+      orow = li;
+    }
+    const float* row = a.target + ((size_t)b * (a.gamma + 1) + kk) * (size_t)a.V;
+    const int c0 = tile * kTgtCols + threadIdx.x * kColsPerThread;
+    float x[kColsPerThread];
+    if (c0 + kColsPerThread <= a.V && (a.V & 3) == 0) {
+      const float4 q = *reinterpret_cast<const float4*>(row + c0);
+      x[0] = q.x; x[1] = q.y; x[2] = q.z; x[3] = q.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kColsPerThread; ++j) x[j] = c0 + j < a.V ? row[c0 + j] : -__builtin_inff();
+    }
+    if constexpr (kGreedy) {
+      float bv = x[0];
+      int bi = c0;
+#pragma unroll
+      for (int j = 1; j < kColsPerThread; ++j) {
+        if (x[j] > bv) {
+          bv = x[j];
+          bi = c0 + j;
+        }
+      }
+      block_argmax<kVThreads>(bv, bi, sv, si);
+      if (threadIdx.x == 0) a.tpart[(size_t)orow * a.ntv + tile] = make_float2(bv, __int_as_float(bi));
+    } else {
+      float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      m = block_max<kVThreads>(m, sv);
+      float s = 0.0f;
+      if (m != -__builtin_inff()) {
+#pragma unroll
+        for (int j = 0; j < kColsPerThread; ++j) s += fast_exp2((x[j] - m) * a.cf);
+      }
+      s = block_sum<kVThreads, float>(s, sv);
+      if (threadIdx.x == 0) a.tpart[(size_t)orow * a.ntv + tile] = make_float2(m, s);
+    }
+  }
+}
+
+hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, hipStream_t s) {
+  const long long items = (long long)max_rows * a.ntv;
+  const int grid = (int)(items < 16384 ? items : 16384);
+  if (grid <= 0) return hipSuccess;
+  if (greedy) {
+    hipLaunchKernelGGL((target_stats_kernel<true>), dim3(grid), dim3(kVThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((target_stats_kernel<false>), dim3(grid), dim3(kVThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Initialisation: outputs to their "not reached" values, validity check of
+// every request's tokens, and the ordered list of phase 1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kVThreads) void verify_init_kernel(VerifyArgs a, VerifyWs w) {
+  __shared__ PickScratch ps;
+  const int g = a.gamma;
+  if (threadIdx.x < g + 2) w.counts[threadIdx.x] = 0;
+  int running = 0;
+  for (int base = 0; base < a.B; base += kVThreads) {
+    const int b = base + threadIdx.x;
+    int valid = 0;
+    if (b < a.B) {
+      valid = a.x0[b] >= 0 && a.x0[b] < a.V;
+      for (int k = 0; k < g; ++k) {
+        const int t = a.draft_tokens[(size_t)b * g + k];
+        valid &= (t >= 0 && t < a.V);
+        if (a.accept_prob) a.accept_prob[(size_t)b * g + k] = __builtin_nanf("");
+      }
+      for (int k = 0; k <= g; ++k) a.out_tokens[(size_t)b * (g + 1) + k] = -1;
+      a.accept_len[b] = -1;
+    }
+    double tot;
+    const double ex = block_exclusive_scan<kVThreads>((double)valid, ps.red, tot);
+    if (valid) w.lists[(size_t)1 * a.B + running + (int)ex] = b;
+    running += (int)tot;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) w.counts[1] = running;
+}
+
+// ---------------------------------------------------------------------------
+// Decision kernel of phase k.
+// ---------------------------------------------------------------------------
+struct DecideCtx {
+  const float2* P;   // tile summaries of the request's target row
+  const float* trow; // target row
+  float M;           // row max
+  double cf;
+  int ntv, V;
+};
+
+// Categorical draw from p_t with uniform u: tile search over the summaries,
+// then a rescan of one 1024-column tile.  `sterm` holds kTgtCols doubles.
+__device__ int sample_target(const DecideCtx& c, double u, PickScratch& ps, double* sterm,
+                             double* total_out) {
+  auto tile_weight = [&](int t) -> double {
+    const float2 p = c.P[t];
+    return p.x == -__builtin_inff() ? 0.0 : (double)p.y * exp2((double)(p.x - c.M) * c.cf);
+  };
+  double base = 0.0, total = 0.0;
+  int ts = block_pick_uniform<kVThreads>(c.ntv, tile_weight, u, ps, &base, &total);
+  if (ts < 0) ts = 0;
+  const double q = u * total;
+  const float mt = c.P[ts].x;
+  const double scale = exp2((double)(mt - c.M) * c.cf);
+  const float cff = (float)c.cf;
+  for (int j = threadIdx.x; j < kTgtCols; j += kVThreads) {
+    const int v = ts * kTgtCols + j;
+    const float x = v < c.V ? c.trow[v] : -__builtin_inff();
+    const float e = x == -__builtin_inff() ? 0.0f : fast_exp2((x - mt) * cff);
+    sterm[j] = (double)e * scale;
+  }
+  __syncthreads();
+  auto col_weight = [&](int j) -> double { return sterm[j]; };
+  int col = block_pick_target<kVThreads>(kTgtCols, col_weight, q - base, ps, nullptr);
+  if (col < 0) col = 0;
+  if (total_out) *total_out = total;
+  return ts * kTgtCols + col;
+}
+
+// Draft logit U[v] + W1[prev] . W2[:, v] in float64 (all threads receive it).
+template <bool kBf16>
+__device__ double draft_logit(const VerifyArgs& a, const float* urow, const double* sw1, int v, double* red) {
+  double s = 0.0;
+  for (int j = threadIdx.x; j < a.r; j += kVThreads) s += sw1[j] * wval<kBf16>(a.W2, (size_t)j * a.V + v);
+  s = block_sum<kVThreads, double>(s, red);
+  return (double)urow[v] + s;
+}
+
+template <bool kGreedy, bool kBf16>
+__global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs w, int k, float cf_f,
+                                                                 int ntv) {
+  __shared__ PickScratch ps;
+  __shared__ double sterm[kTgtCols];
+  __shared__ double sw1[512];
+  __shared__ double sred[kVThreads / kWave];
+  __shared__ float sv[kVThreads / kWave];
+  __shared__ int si[kVThreads / kWave];
+  const int g = a.gamma;
+  const int count = w.counts[k];
+  const double cf = (double)cf_f;
+  for (int li = blockIdx.x; li < count; li += gridDim.x) {
+    const int b = w.lists[(size_t)k * a.B + li];
+    const float2* P = w.tpart + (size_t)b * ntv;
+    const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
+    if constexpr (kGreedy) {
+      float bv = -__builtin_inff();
+      int bi = INT_MAX;
+      for (int t = threadIdx.x; t < ntv; t += kVThreads) argmax_merge(bv, bi, P[t].x, __float_as_int(P[t].y));
+      block_argmax<kVThreads>(bv, bi, sv, si);
+      if (threadIdx.x == 0) {
+        if (k <= g) {
+          const int x = a.draft_tokens[(size_t)b * g + k - 1];
+          const bool acc = bi == x;
+          if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = acc ? 1.0f : 0.0f;
+          if (acc) {
+            a.out_tokens[(size_t)b * (g + 1) + k - 1] = x;
+            const int pos = atomicAdd(&w.counts[k + 1], 1);
+            w.lists[(size_t)(k + 1) * a.B + pos] = b;
+          } else {
+            a.out_tokens[(size_t)b * (g + 1) + k - 1] = bi;
+            a.accept_len[b] = k - 1;
+          }
+        } else {
+          a.out_tokens[(size_t)b * (g + 1) + g] = bi;
+          a.accept_len[b] = g;
+        }
+      }
+      continue;
+    } else {
+      float lm = -__builtin_inff();
+      for (int t = threadIdx.x; t < ntv; t += kVThreads) lm = fmaxf(lm, P[t].x);
+      DecideCtx c;
+      c.P = P;
+      c.trow = trow;
+      c.M = block_max<kVThreads>(lm, sv);
+      c.cf = cf;
+      c.ntv = ntv;
+      c.V = a.V;
+      const uint64_t seed = a.seeds[b];
+      if (k > g) {  // bonus token from the position after the block
+        const double u = unit_uniform(draw_block(seed, a.round, g + 1, kStreamResidual, 0).w[0]);
+        const int y = sample_target(c, u, ps, sterm, nullptr);
+        if (threadIdx.x == 0) {
+          a.out_tokens[(size_t)b * (g + 1) + g] = y;
+          a.accept_len[b] = g;
+        }
+        continue;
+      }
+      auto tile_weight = [&](int t) -> double {
+        const float2 p = P[t];
+        return p.x == -__builtin_inff() ? 0.0 : (double)p.y * exp2((double)(p.x - c.M) * cf);
+      };
+      const double Z = block_total<kVThreads>(ntv, tile_weight, ps);
+      const int x = a.draft_tokens[(size_t)b * g + k - 1];
+      const double ptx = exp2((double)(trow[x] - c.M) * cf) / Z;
+      const double pdx = (double)a.draft_prob[(size_t)b * g + k - 1];
+      const double alpha = fmin(1.0, ptx / pdx);
+      const double u = unit_uniform(draw_block(seed, a.round, k, kStreamAccept, 0).w[0]);
+      if (threadIdx.x == 0 && a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = (float)alpha;
+      if (u < alpha) {
+        if (threadIdx.x == 0) {
+          a.out_tokens[(size_t)b * (g + 1) + k - 1] = x;
+          const int pos = atomicAdd(&w.counts[k + 1], 1);
+          w.lists[(size_t)(k + 1) * a.B + pos] = b;
+        }
+        continue;
+      }
+      // Rejected at j = k: residual draw by proposals from p_t.
+      const int prev = k == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + k - 2];
+      for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1[j] = wval<kBf16>(a.W1, (size_t)prev * a.r + j);
+      __syncthreads();
+      const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
+      const double lx = draft_logit<kBf16>(a, urow, sw1, x, sred);
+      int found = -1;
+      for (int i = 0; i < DSPARK_MAX_RESIDUAL_PROPOSALS; ++i) {
+        const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
+        const double up = unit_uniform(d.w[0]);
+        const double ua = unit_uniform(d.w[1]);
+        const int v = sample_target(c, up, ps, sterm, nullptr);
+        const double ptv = exp2((double)(trow[v] - c.M) * cf) / Z;
+        const double lv = draft_logit<kBf16>(a, urow, sw1, v, sred);
+        const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
+        const double keep = fmax(0.0, 1.0 - pdv / ptv);
+        if (ua < keep) {
+          found = v;
+          break;
+        }
+      }
+      if (threadIdx.x == 0) {
+        a.accept_len[b] = k - 1;
+        if (found >= 0) {
+          a.out_tokens[(size_t)b * (g + 1) + k - 1] = found;
+        } else {
+          FallbackInfo f;
+          f.j = k;
+          f.prev = prev;
+          f.M = (double)c.M;
+          f.Z = Z;
+          f.pdx = pdx;
+          f.lx = lx;
+          w.fb[b] = f;
+          const int pos = atomicAdd(&w.counts[0], 1);
+          w.fb_list[pos] = b;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact residual fallback: mass of max(0, p_t - p_d) per 1024-column tile,
+// then one inverse-CDF draw with the stream-3 uniform.
+// ---------------------------------------------------------------------------
+template <bool kBf16>
+__device__ void residual_terms(const VerifyArgs& a, const FallbackInfo& f, int b, int tile, const double* sw1,
+                               double cf, double* res /* [kColsPerThread] */) {
+  const int g = a.gamma;
+  const float* trow = a.target + ((size_t)b * (g + 1) + (f.j - 1)) * (size_t)a.V;
+  const float* urow = a.U + ((size_t)b * g + (f.j - 1)) * (size_t)a.V;
+  const int c0 = tile * kTgtCols + threadIdx.x * kColsPerThread;
+#pragma unroll
+  for (int q = 0; q < kColsPerThread; ++q) {
+    const int v = c0 + q;
+    res[q] = 0.0;
+    if (v < a.V) {
+      const float t = trow[v];
+      const double pt = t == -__builtin_inff() ? 0.0 : exp2((double)(t - (float)f.M) * cf) / f.Z;
+      double s = 0.0;
+      for (int j = 0; j < a.r; ++j) s += sw1[j] * wval<kBf16>(a.W2, (size_t)j * a.V + v);
+      const float uu = urow[v];
+      const double pd = uu == -__builtin_inff() ? 0.0 : f.pdx * exp(((double)uu + s - f.lx) * a.inv_t_d);
+      res[q] = fmax(0.0, pt - pd);
+    }
+  }
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kVThreads) void residual_stats_kernel(VerifyArgs a, VerifyWs w, float cf_f, int ntv) {
+  __shared__ double sw1[512];
+  __shared__ double sred[kVThreads / kWave];
+  const int count = w.counts[0];
+  const long long items = (long long)count * ntv;
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int li = (int)(it / ntv);
+    const int tile = (int)(it - (long long)li * ntv);
+    const int b = w.fb_list[li];
+    const FallbackInfo f = w.fb[b];
+    for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1[j] = wval<kBf16>(a.W1, (size_t)f.prev * a.r + j);
+    __syncthreads();
+    double res[kColsPerThread];
+    residual_terms<kBf16>(a, f, b, tile, sw1, (double)cf_f, res);
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < kColsPerThread; ++q) s += res[q];
+    s = block_sum<kVThreads, double>(s, sred);
+    if (threadIdx.x == 0) w.fb_part[(size_t)b * ntv + tile] = s;
+  }
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kVThreads) void residual_select_kernel(VerifyArgs a, VerifyWs w, float cf_f, int ntv) {
+  __shared__ PickScratch ps;
+  __shared__ double sterm[kTgtCols];
+  __shared__ double sw1[512];
+  const int count = w.counts[0];
+  const int g = a.gamma;
+  for (int li = blockIdx.x; li < count; li += gridDim.x) {
+    const int b = w.fb_list[li];
+    const FallbackInfo f = w.fb[b];
+    const double u = unit_uniform(draw_block(a.seeds[b], a.round, f.j, kStreamFallback, 0).w[0]);
+    const double* FP = w.fb_part + (size_t)b * ntv;
+    auto tile_mass = [&](int t) -> double { return FP[t]; };
+    double base = 0.0, total = 0.0;
+    int ts = block_pick_uniform<kVThreads>(ntv, tile_mass, u, ps, &base, &total);
+    int y;
+    if (total > 0.0 && ts >= 0) {
+      for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1[j] = wval<kBf16>(a.W1, (size_t)f.prev * a.r + j);
+      __syncthreads();
+      double res[kColsPerThread];
+      residual_terms<kBf16>(a, f, b, ts, sw1, (double)cf_f, res);
+#pragma unroll
+      for (int q = 0; q < kColsPerThread; ++q) sterm[threadIdx.x * kColsPerThread + q] = res[q];
+      __syncthreads();
+      auto col_weight = [&](int j) -> double { return sterm[j]; };
+      int col = block_pick_target<kVThreads>(kTgtCols, col_weight, u * total - base, ps, nullptr);
+      if (col < 0) col = 0;
+      y = ts * kTgtCols + col;
+    } else {
+      // No residual mass (possible only through rounding): draw from p_t.
+      DecideCtx c;
+      c.P = w.tpart + (size_t)b * ntv;
+      c.trow = a.target + ((size_t)b * (g + 1) + (f.j - 1)) * (size_t)a.V;
+      c.M = (float)f.M;
+      c.cf = (double)cf_f;
+      c.ntv = ntv;
+      c.V = a.V;
+      y = sample_target(c, u, ps, sterm, nullptr);
+    }
+    if (threadIdx.x == 0) a.out_tokens[(size_t)b * (g + 1) + f.j - 1] = y;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
+  VerifyArgs a = a_in;
+  const bool greedy = a.temperature == 0.0f;
+  a.inv_t_d = greedy ? 0.0 : 1.0 / (double)a.temperature;
+  const int ntv = tiles_of(a.V, kTgtCols);
+  const float cf = greedy ? 0.0f : (float)(1.4426950408889634 / (double)a.temperature);
+  VerifyWs w = carve_verify(a.ws, a.B, a.gamma, a.V);
+
+  hipLaunchKernelGGL(verify_init_kernel, dim3(1), dim3(kVThreads), 0, s, a, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int dgrid = a.B < 2048 ? a.B : 2048;
+  for (int k = 1; k <= a.gamma + 1; ++k) {
+    TStatsArgs t = {};
+    t.target = a.target;
+    t.list = w.lists + (size_t)k * a.B;
+    t.count = w.counts + k;
+    t.kk0 = k - 1;
+    t.gamma = a.gamma;
+    t.V = a.V;
+    t.ntv = ntv;
+    t.cf = cf;
+    t.tpart = w.tpart;
+    e = launch_target_stats(t, greedy, a.B, s);
+    if (e != hipSuccess) return e;
+    if (greedy) {
+      hipLaunchKernelGGL((verify_decide_kernel<true, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, k, cf, ntv);
+    } else if (bf16) {
+      hipLaunchKernelGGL((verify_decide_kernel<false, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, k, cf, ntv);
+    } else {
+      hipLaunchKernelGGL((verify_decide_kernel<false, false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, k, cf, ntv);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!greedy) {
+    const long long items = (long long)a.B * ntv;
+    const int sgrid = (int)(items < 4096 ? items : 4096);
+    if (bf16) {
+      hipLaunchKernelGGL((residual_stats_kernel<true>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+      hipLaunchKernelGGL((residual_select_kernel<true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+    } else {
+      hipLaunchKernelGGL((residual_stats_kernel<false>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+      hipLaunchKernelGGL((residual_select_kernel<false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dspark

@@ -1,0 +1,209 @@
+/*
+ * libdspark: DSpark's per-round token path on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page titles; sections, equations):
+ *   [R] "DSpark: Confidence-Scheduled Speculative Decoding with
+ *       Semi-Autoregressive Generation", technical review (zhongzhuzhou.org):
+ *       "Speculative Decoding: Draft, Then Verify" (step 3), "The Sequential
+ *       Correction" (Eq. 4), "Instantiation 1: The Markov Head" (Eq. 5),
+ *       "The Confidence Head" (Eq. 8), "Deriving the Acceptance-Rate Identity
+ *       Behind Equation 8" (Eq. 8a-8c), "The Hardware-Aware Prefix Scheduler"
+ *       (cumulative products), "Common Questions Answered" (greedy decoding),
+ *       "Putting It All Together: The Full Decode Loop as Pseudocode".
+ *   [E] "Speculative decoding, from zero to DSpark", section 2 "The loop, and
+ *       why it's lossless" (residual rule, bonus token).
+ *   [Z] "DSpark：置信度调度的半自回归投机解码" (robotworld.top review),
+ *       confidence-head paragraph (accept-rate label clamped to [0, 1]).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Symbols: B requests, gamma draft positions, V vocabulary size, r Markov
+ * rank, T temperature.  Position k runs 1..gamma (stored 0-based).
+ *
+ * Memory.  Every array pointer is a DEVICE pointer to contiguous row-major
+ * memory, aligned to 16 bytes, owned by the caller.  The library allocates
+ * nothing and keeps no state between calls; scratch memory is the caller's
+ * `workspace` of at least dspark_workspace_size(op, ...) bytes, which must not
+ * be shared by calls that may run concurrently.
+ *
+ * Layouts.
+ *   U       float32 [B][gamma][V]      base logits U_k of the parallel backbone
+ *   W1      [V][r]                     Markov embedding (bf16 or float32)
+ *   W2      [r][V]                     Markov projection (same dtype as W1)
+ *   x0      int32 [B]                  anchors (the previous round's last token)
+ *   target  float32 [B][gamma+1][V]    target logits; row gamma+1 is the bonus
+ *                                      position after the block
+ *   seeds   uint64 [B]                 per-request Philox4x64-10 keys
+ *
+ * Random numbers.  Each draw is word w of Philox4x64-10 (Salmon, Moraes,
+ * Dror, Shaw, SC'11) under key (seeds[b], 0) at counter (round, k, stream, i),
+ * mapped to the double ((w >> 12) + 0.5) * 2^-52 in (0, 1).  Streams: 0 draft
+ * sample, 1 acceptance test, 2 residual proposals (word 0 proposal, word 1
+ * keep test, index i = proposal number) and the bonus token (k = gamma+1,
+ * i = 0), 3 exact residual fallback.  `round` is the caller's round counter:
+ * the same (seeds, round, inputs) give bit-identical outputs.
+ *
+ * Sampling.  A categorical draw with uniform u takes the first token v, in
+ * ascending vocabulary order, whose cumulative probability exceeds u.  At
+ * T == 0 every draw becomes an argmax, lowest index on ties, and no random
+ * numbers are used.
+ *
+ * Streams and errors.  Every call is asynchronous on `stream` and returns once
+ * its kernels are enqueued; outputs are valid after the stream is
+ * synchronised.  Arguments are validated on the host before any HIP call:
+ * DSPARK_ERR_INVALID_ARGUMENT for sizes out of range (1 <= B <= 65536,
+ * 1 <= gamma <= 32, 2 <= V < 2^31, 16 <= r <= 512 with r % 16 == 0, T finite
+ * and >= 0), a NULL required pointer or a misaligned one;
+ * DSPARK_ERR_UNSUPPORTED for an unknown weight dtype; DSPARK_ERR_WORKSPACE for
+ * a workspace smaller than dspark_workspace_size; DSPARK_ERR_HIP when a
+ * launch fails.  On error the outputs are unspecified.  Logits must be finite
+ * or -inf, and no row may be all -inf.  A token id outside [0, V) in x0 or
+ * draft_tokens is detected on the device: that request's outputs become -1
+ * (tokens, accept_len) and NaN (probabilities); the other requests are
+ * unaffected.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_INVALID_ARGUMENT = -1,
+  DSPARK_ERR_UNSUPPORTED = -2,
+  DSPARK_ERR_WORKSPACE = -3,
+  DSPARK_ERR_HIP = -4
+} dspark_status;
+
+/* Storage type of W1 and W2. */
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* Which entry point a workspace is sized for. */
+typedef enum { DSPARK_OP_DRAFT = 0, DSPARK_OP_VERIFY = 1, DSPARK_OP_SURVIVAL = 2 } dspark_op;
+
+/* Maximum number of residual proposals drawn against p_t before the exact
+ * residual inverse CDF (stream 3) is used. */
+#define DSPARK_MAX_RESIDUAL_PROPOSALS 16
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int dspark_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* dspark_status_string(dspark_status s);
+
+/* Bytes of device workspace that `op` needs for these sizes; 0 when the sizes
+ * are out of range.  The workspace needs no initialisation. */
+size_t dspark_workspace_size(dspark_op op, int B, int gamma, int V, int r);
+
+/*
+ * dspark_markov_bias -- rows of the rank-r bigram bias, Eq. 5 of [R]
+ * ("Instantiation 1: The Markov Head"):  out[i][v] = sum_j W1[tokens[i]][j] W2[j][v].
+ *
+ *   tokens  int32 [n]           previous tokens, 0 <= tokens[i] < V
+ *   out     float32 [n][V]      fp32 accumulation of the exact products; a row
+ *                               whose token is out of range is all NaN
+ * n >= 1.  Needs no workspace.
+ */
+dspark_status dspark_markov_bias(const void* W1, const void* W2, dspark_dtype wdtype,
+                                 const int32_t* tokens, int n, int V, int r,
+                                 float* out, hipStream_t stream);
+
+/*
+ * dspark_markov_draft -- semi-autoregressive block sampling of [R]
+ * "The Sequential Correction" (Eq. 4) with the Markov head (Eq. 5).
+ *
+ * For every request b and k = 1..gamma, left to right:
+ *   l_k(v)  = U[b][k][v] + W1[x_{k-1}] . W2[:, v]      (x_0 = x0[b])
+ *   p_d^k   = softmax(l_k / T)  over the whole vocabulary
+ *   x_k     = categorical draw from p_d^k with the stream-0 uniform at (round, k)
+ * At T == 0, x_k = argmax l_k, draft_prob = 1 and draft_lse = 0.
+ *
+ * Outputs:
+ *   draft_tokens  int32   [B][gamma]  x_1..x_gamma
+ *   draft_prob    float32 [B][gamma]  p_d^k(x_k)
+ *   draft_lse     float32 [B][gamma]  log sum_v exp(l_k(v) / T), the log
+ *                                     normaliser of p_d^k (used by
+ *                                     dspark_survival)
+ * Workspace: dspark_workspace_size(DSPARK_OP_DRAFT, B, gamma, V, r).
+ */
+dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2,
+                                  dspark_dtype wdtype, const int32_t* x0,
+                                  int B, int gamma, int V, int r, float temperature,
+                                  const uint64_t* seeds, uint64_t round,
+                                  int32_t* draft_tokens, float* draft_prob, float* draft_lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_verify -- lossless rejection-sampling verification of the drafted
+ * blocks: [R] "Speculative Decoding: Draft, Then Verify" step 3 and [E]
+ * section 2.
+ *
+ * For every request b, k = 1..gamma left to right, with p_t^k = softmax(target[b][k] / T):
+ *   alpha_k = min(1, p_t^k(x_k) / p_d^k(x_k))   (p_d^k(x_k) = draft_prob[b][k])
+ *   accept x_k iff the stream-1 uniform at (round, k) is < alpha_k.
+ * At the first rejection j, one token is drawn from norm(max(0, p_t^j - p_d^j))
+ * and the block ends (n = j - 1): proposals v ~ p_t^j (stream 2, word 0,
+ * index i) are kept with probability max(0, 1 - p_d^j(v) / p_t^j(v)) (stream 2,
+ * word 1); after DSPARK_MAX_RESIDUAL_PROPOSALS misses the residual itself is
+ * drawn by inverse CDF with the stream-3 uniform at (round, j).  p_d^j(v) is
+ * rebuilt from U, W1, W2 and x_{j-1}.  If all gamma positions pass (n = gamma)
+ * a bonus token is drawn from p_t^{gamma+1} with the stream-2 uniform at
+ * (round, gamma+1, index 0).
+ * At T == 0 acceptance is the exact match x_k == argmax target[b][k] and the
+ * correction or bonus token is argmax target[b][n+1] ([R] "Common Questions
+ * Answered").
+ *
+ * Inputs draft_tokens / draft_prob are dspark_markov_draft's outputs.
+ * Outputs:
+ *   accept_len   int32   [B]          n in 0..gamma
+ *   out_tokens   int32   [B][gamma+1] x_1..x_n, then the correction or bonus
+ *                                     token, then -1
+ *   accept_prob  float32 [B][gamma]   alpha_k for the tested positions
+ *                                     k <= min(n+1, gamma), NaN after; NULL to skip
+ * Workspace: dspark_workspace_size(DSPARK_OP_VERIFY, B, gamma, V, r).
+ */
+dspark_status dspark_verify(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
+                            const int32_t* x0, const int32_t* draft_tokens,
+                            const float* draft_prob, const float* target_logits,
+                            int B, int gamma, int V, int r, float temperature,
+                            const uint64_t* seeds, uint64_t round,
+                            int32_t* accept_len, int32_t* out_tokens, float* accept_prob,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_survival -- prefix survival products a_{b,k} = prod_{i<=k} c_{b,i}
+ * of [R] "The Hardware-Aware Prefix Scheduler".
+ *
+ * Confidence mode (conf != NULL, float32 [B][gamma]): c = conf; U, W1, W2,
+ * x0, draft_tokens, draft_lse and target_logits are not read and may be NULL,
+ * and c_star is not written.
+ * Analytical mode (conf == NULL): c_{b,k} = c*_k = clamp(sum_v min(p_d^k(v),
+ * p_t^k(v)), 0, 1), the acceptance probability of Eq. 8a / 8c with the
+ * clamp of [Z], at every block position k = 1..gamma along the drafted prefix;
+ * p_d^k(v) = exp(l_k(v) / T - draft_lse[b][k]).  At T == 0, c*_k is the
+ * indicator x_k == argmax target[b][k].
+ *
+ * Outputs: c_star float32 [B][gamma] (analytical mode; NULL to skip) and
+ * survival float32 [B][gamma].
+ * Workspace: dspark_workspace_size(DSPARK_OP_SURVIVAL, B, gamma, V, r); 0
+ * bytes are needed in confidence mode.
+ */
+dspark_status dspark_survival(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
+                              const int32_t* x0, const int32_t* draft_tokens,
+                              const float* draft_lse, const float* target_logits,
+                              const float* conf, int B, int gamma, int V, int r,
+                              float temperature, float* c_star, float* survival,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

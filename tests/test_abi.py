@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/dspark.h declares, and rejects bad arguments on the host with the
+documented status codes before any HIP call is made."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+dsp = pytest.importorskip("draft_sampling_verification_bias_amd")
+
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+FAKE = 0x100000          # non-null, 16-byte aligned, never dereferenced (validation fails first)
+MISALIGNED = 0x100004
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsp.library_path()):
+        pytest.fail("libdspark.so is not built: run python -m draft_sampling_verification_bias_amd.build")
+    return dsp.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dspark_markov_draft", "dspark_verify", "dspark_survival", "dspark_markov_bias",
+              "dspark_workspace_size", "dspark_status_string", "dspark_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dspark_version() >= 100
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+        s = lib.dspark_status_string(code)
+        assert s and len(s) > 1
+    assert lib.dspark_status_string(123) == b"unknown status"
+
+
+@pytest.mark.parametrize("op", [dsp.OP_DRAFT, dsp.OP_VERIFY, dsp.OP_SURVIVAL])
+def test_workspace_size(lib, op):
+    small = dsp.workspace_size(op, 4, 4, 1000, 16)
+    big = dsp.workspace_size(op, 256, 7, 151936, 256)
+    assert 0 < small < big
+    # out-of-range sizes give 0
+    for args in ((0, 4, 1000, 16), (4, 0, 1000, 16), (4, 33, 1000, 16), (4, 4, 1, 16),
+                 (4, 4, 1000, 8), (4, 4, 1000, 24), (4, 4, 1000, 528), (65537, 4, 1000, 16)):
+        assert dsp.workspace_size(op, *args) == 0
+    assert dsp.workspace_size(7, 4, 4, 1000, 16) == 0
+
+
+def _draft(lib, **kw):
+    a = dict(U=FAKE, W1=FAKE, W2=FAKE, wd=1, x0=FAKE, B=4, gamma=4, V=1000, r=16, T=1.0, seeds=FAKE,
+             rnd=0, tok=FAKE, prob=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.dspark_markov_draft(a["U"], a["W1"], a["W2"], a["wd"], a["x0"], a["B"], a["gamma"], a["V"],
+                                   a["r"], a["T"], a["seeds"], a["rnd"], a["tok"], a["prob"], a["lse"],
+                                   a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(gamma=0), INVALID), (dict(gamma=33), INVALID), (dict(V=1), INVALID),
+    (dict(r=8), INVALID), (dict(r=40), INVALID), (dict(T=-1.0), INVALID), (dict(T=float("nan")), INVALID),
+    (dict(T=float("inf")), INVALID), (dict(U=None), INVALID), (dict(W2=None), INVALID),
+    (dict(tok=None), INVALID), (dict(seeds=None), INVALID), (dict(U=MISALIGNED), INVALID),
+    (dict(ws=None), INVALID), (dict(wd=5), UNSUPPORTED), (dict(wsb=16), WORKSPACE),
+])
+def test_draft_rejects_bad_arguments(lib, kw, status):
+    assert _draft(lib, **kw) == status
+
+
+def _verify(lib, **kw):
+    a = dict(U=FAKE, W1=FAKE, W2=FAKE, wd=1, x0=FAKE, dt=FAKE, dp=FAKE, tgt=FAKE, B=4, gamma=4, V=1000, r=16,
+             T=1.0, seeds=FAKE, rnd=0, alen=FAKE, otok=FAKE, aprob=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.dspark_verify(a["U"], a["W1"], a["W2"], a["wd"], a["x0"], a["dt"], a["dp"], a["tgt"], a["B"],
+                             a["gamma"], a["V"], a["r"], a["T"], a["seeds"], a["rnd"], a["alen"], a["otok"],
+                             a["aprob"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=70000), INVALID), (dict(tgt=None), INVALID), (dict(alen=None), INVALID),
+    (dict(dp=None), INVALID), (dict(tgt=MISALIGNED), INVALID), (dict(wd=9), UNSUPPORTED),
+    (dict(wsb=0), WORKSPACE), (dict(T=-0.5), INVALID),
+])
+def test_verify_rejects_bad_arguments(lib, kw, status):
+    assert _verify(lib, **kw) == status
+
+
+def test_survival_rejects_bad_arguments(lib):
+    s = lib.dspark_survival
+    # confidence mode: bad sizes, missing output
+    assert s(None, None, None, 1, None, None, None, None, FAKE, 0, 4, 2, 16, 0.0, None, FAKE, None, 0, None) == INVALID
+    assert s(None, None, None, 1, None, None, None, None, FAKE, 4, 4, 2, 16, 0.0, None, None, None, 0, None) == INVALID
+    # analytical mode: missing target, bad dtype, small workspace
+    assert s(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 1 << 30,
+             None) == INVALID
+    assert s(FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 1 << 30,
+             None) == UNSUPPORTED
+    assert s(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 8,
+             None) == WORKSPACE
+
+
+def test_markov_bias_rejects_bad_arguments(lib):
+    f = lib.dspark_markov_bias
+    assert f(FAKE, FAKE, 1, FAKE, 0, 1000, 16, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 1, FAKE, 4, 1000, 17, FAKE, None) == INVALID
+    assert f(FAKE, None, 1, FAKE, 4, 1000, 16, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 2, FAKE, 4, 1000, 16, FAKE, None) == UNSUPPORTED

@@ -1,0 +1,244 @@
+"""GPU parity of libdspark against the float64 oracle, through the C ABI.
+
+Every case runs the HIP path on the device and the oracle on the CPU on the
+same seeded bytes, then compares element by element with the tolerances in
+``parity.py``.  Small cases (several tiles, ragged vocabulary tails, ragged
+row blocks) compare every request; the full-size workloads compare a sample of
+requests, which the oracle computes one by one, in the launch configuration
+the benchmark times.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import (Dev, compare_draft, compare_survival, compare_verify, f64_weights, seeds_tensor)
+
+torch = pytest.importorskip("torch")
+dsp = pytest.importorskip("draft_sampling_verification_bias_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    dsp.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_path(wl, reqs, label, check_verify=True, check_survival=True):
+    """Draft, verify and survival on the GPU; oracle on ``reqs``; compare."""
+    say("[%s] B=%d V=%d r=%d gamma=%d T=%g %s" % (label, wl.B, wl.V, wl.r, wl.gamma, wl.T, wl.wdtype))
+    d = Dev(wl)
+    tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
+    torch.cuda.synchronize()
+    tok_h, prob_h, lse_h = tok.cpu().numpy(), prob.cpu().numpy(), lse.cpu().numpy()
+    W1f, W2f = f64_weights(wl)
+    ref = oracle.markov_draft(wl.U, W1f, W2f, wl.x0, wl.T, wl.seeds, wl.rnd, requests=reqs)
+    n, ex, whole = compare_draft(ref, tok_h, prob_h, lse_h, reqs, wl.T)
+    say("[%s] draft: %d positions equal, %d exempt draws" % (label, n, ex))
+    assert n > 0
+    if check_verify:
+        alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd)
+        torch.cuda.synchronize()
+        vreq = sorted(whole)
+        vref = oracle.verify(wl.U, W1f, W2f, wl.x0, tok_h, wl.tgt, wl.T, wl.seeds, wl.rnd, requests=vreq)
+        nv, exv = compare_verify(vref, alen.cpu().numpy(), otok.cpu().numpy(), aprob.cpu().numpy(), vreq, wl.T)
+        lens = alen.cpu().numpy()
+        say("[%s] verify: %d requests equal, %d exempt; mean accepted %.3f" % (label, nv, exv, lens.mean()))
+        assert nv > 0
+    if check_survival:
+        cst, surv = dsp.survival(d.U, d.W1, d.W2, d.x0, tok, lse, d.tgt, wl.T)
+        torch.cuda.synchronize()
+        sreq = sorted(whole)
+        rc, ra = oracle.survival(wl.U, W1f, W2f, wl.x0, tok_h, wl.tgt, wl.T, requests=sreq)
+        compare_survival(rc, ra, cst.cpu().numpy(), surv.cpu().numpy(), sreq)
+        say("[%s] survival: %d requests equal" % (label, len(sreq)))
+    return tok_h
+
+
+# ---------------------------------------------------------------------------
+# The Markov bias contraction alone (Eq. 5): MFMA / VALU against float64.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("wdtype,V,r,n", [("bf16", 1000, 16, 5), ("bf16", 4099, 256, 70), ("bf16", 130, 512, 33),
+                                          ("f32", 1000, 16, 4), ("f32", 777, 48, 9)])
+def test_markov_bias_rows(wdtype, V, r, n):
+    rng = np.random.default_rng(7)
+    W1f = rng.standard_normal((V, r), dtype=np.float32) * np.float32(0.1)
+    W2f = rng.standard_normal((r, V), dtype=np.float32) * np.float32(0.1)
+    if wdtype == "bf16":
+        W1b, W2b = workloads.f32_to_bf16_bits(W1f), workloads.f32_to_bf16_bits(W2f)
+        W1, W2 = oracle.weights_as_f64(W1b, "bf16"), oracle.weights_as_f64(W2b, "bf16")
+        dW1 = torch.from_numpy(W1b.view(np.int16)).cuda().view(torch.bfloat16)
+        dW2 = torch.from_numpy(W2b.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        W1, W2 = W1f.astype(np.float64), W2f.astype(np.float64)
+        dW1, dW2 = torch.from_numpy(W1f).cuda(), torch.from_numpy(W2f).cuda()
+    toks = rng.integers(0, V, size=n).astype(np.int32)
+    toks[0] = V - 1
+    out = dsp.markov_bias(dW1, dW2, torch.from_numpy(toks).cuda()).cpu().numpy()
+    for i, t in enumerate(toks):
+        ref = oracle.markov_bias(W1, W2, int(t))
+        bound = np.abs(W1[t]) @ np.abs(W2)          # sum of |products|: fp32 summation bound
+        err = np.abs(out[i].astype(np.float64) - ref)
+        assert np.all(err <= 2.0 * r * 2.0 ** -24 * bound + 1e-30), (i, float(err.max()))
+
+
+def test_markov_bias_marks_invalid_rows_nan():
+    V, r = 300, 32
+    W1 = torch.randn(V, r).cuda().to(torch.bfloat16)
+    W2 = torch.randn(r, V).cuda().to(torch.bfloat16)
+    toks = torch.tensor([3, V, -1, 5], dtype=torch.int32).cuda()
+    out = dsp.markov_bias(W1, W2, toks).cpu().numpy()
+    assert np.all(np.isfinite(out[[0, 3]])) and np.all(np.isnan(out[[1, 2]]))
+
+
+# ---------------------------------------------------------------------------
+# Oracle-sized cases: every request compared.
+# ---------------------------------------------------------------------------
+SMALL = [
+    ("tiny_v1000_b4", {}),
+    ("v151936_b32", dict(V=4099, B=37, gamma=5)),
+    ("v151936_b32", dict(V=1537, B=16, gamma=7, r=128, w_std=0.2)),
+    ("v151936_b256_t07", dict(V=3001, B=40, r=64)),
+    ("greedy_v151936_b512", dict(V=5003, B=70, r=32)),
+    ("v262144_b128", dict(V=2053, B=33, r=48)),
+    ("tiny_v1000_b4", dict(V=2, B=3, gamma=2)),
+    ("v151936_b32", dict(V=5, B=2, gamma=3, r=16)),
+    ("v151936_b32", dict(V=130, B=1, gamma=1, r=512)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=["%s-%s" % (n, "-".join("%s%s" % i for i in kw.items())) for n, kw in SMALL])
+def test_small_parity(name, kw):
+    wl = workloads.make(name, **kw)
+    run_path(wl, list(range(wl.B)), name)
+
+
+def test_tiny_fp32_temperature_07():
+    wl = workloads.make("tiny_v1000_b4", T=0.7)
+    run_path(wl, list(range(wl.B)), "tiny-T0.7")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: GPU on all requests, oracle on a sample.
+# ---------------------------------------------------------------------------
+FULL = ["v151936_b32", "v151936_b256_t07", "greedy_v151936_b512", "v262144_b128"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    wl = workloads.make(name)
+    rng = np.random.default_rng(11)
+    reqs = sorted(set([0, wl.B - 1] + rng.choice(wl.B, size=4, replace=False).tolist()))
+    run_path(wl, reqs, name)
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Edge cases and properties.
+# ---------------------------------------------------------------------------
+def test_single_finite_logit_rows():
+    """Rows that are -inf except one token: the draft must pick it with p = 1,
+    the target agrees, so every position passes and the bonus is that row's
+    only token."""
+    wl = workloads.make("v151936_b32", V=517, B=9, gamma=4, r=32)
+    rng = np.random.default_rng(3)
+    only = rng.integers(0, wl.V, size=(wl.B, wl.gamma + 1))
+    wl.U[:] = -np.inf
+    wl.tgt[:] = -np.inf
+    for b in range(wl.B):
+        for k in range(wl.gamma):
+            wl.U[b, k, only[b, k]] = rng.standard_normal()
+            wl.tgt[b, k, only[b, k]] = rng.standard_normal()
+        wl.tgt[b, wl.gamma, only[b, wl.gamma]] = 0.0
+    tok = run_path(wl, list(range(wl.B)), "one-finite")
+    assert np.array_equal(tok, only[:, :wl.gamma])
+
+
+def test_invalid_anchor_is_reported_per_request():
+    wl = workloads.make("v151936_b32", V=1100, B=6, gamma=3, r=32)
+    wl.x0[2] = wl.V
+    wl.x0[4] = -3
+    d = Dev(wl)
+    tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
+    alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd)
+    cst, surv = dsp.survival(d.U, d.W1, d.W2, d.x0, tok, lse, d.tgt, wl.T)
+    tok, prob, alen, otok, surv = (t.cpu().numpy() for t in (tok, prob, alen, otok, surv))
+    for b in (2, 4):
+        assert np.all(tok[b] == -1) and np.all(np.isnan(prob[b]))
+        assert alen[b] == -1 and np.all(otok[b] == -1) and np.all(np.isnan(surv[b]))
+    good = [0, 1, 3, 5]
+    W1f, W2f = f64_weights(wl)
+    ref = oracle.markov_draft(wl.U, W1f, W2f, wl.x0, wl.T, wl.seeds, wl.rnd, requests=good)
+    n, _, whole = compare_draft(ref, tok, prob, lse.cpu().numpy(), good, wl.T)
+    assert n > 0 and whole
+
+
+def test_draft_is_deterministic_and_round_sensitive():
+    wl = workloads.make("v151936_b256_t07", V=2500, B=64, r=64)
+    d = Dev(wl)
+    a = [t.cpu().numpy() for t in dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, 5)]
+    b = [t.cpu().numpy() for t in dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, 5)]
+    c = [t.cpu().numpy() for t in dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, 6)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert not np.array_equal(a[0], c[0])
+
+
+def test_confidence_mode_survival_matches_printed_products():
+    """Confidence mode on the cumulative products printed in the technical
+    review ("The Hardware-Aware Prefix Scheduler" two-request trace and the
+    step-7 table of "A Three-Request Numeric Trace Through the Whole Loop")."""
+    rows = [([0.9, 0.5], [0.9, 0.45], None), ([0.6, 0.6], [0.6, 0.36], None),
+            ([0.95, 0.85, 0.70], [0.950, 0.808, 0.565], 3), ([0.80, 0.55, 0.30], [0.800, 0.440, 0.132], 3),
+            ([0.65, 0.25, 0.10], [0.650, 0.163, 0.016], 3)]
+    for conf, printed, dec in rows:
+        c = torch.tensor([conf], dtype=torch.float32).cuda()
+        _, s = dsp.survival(None, None, None, None, None, None, None, 0.0, conf=c)
+        s = s.cpu().numpy()[0]
+        if dec is None:
+            assert np.allclose(s, printed, rtol=1e-6)
+        else:
+            assert np.array_equal(np.round(s.astype(np.float64), dec), np.round(np.array(printed), dec))
+    rng = np.random.default_rng(1)
+    conf = rng.random((300, 7)).astype(np.float32)
+    _, s = dsp.survival(None, None, None, None, None, None, None, 0.0, conf=torch.from_numpy(conf).cuda())
+    _, ref = oracle.survival(None, None, None, None, None, None, 0.0, conf=conf)
+    assert np.allclose(s.cpu().numpy(), ref, rtol=1e-6, atol=0)
+
+
+def test_first_emitted_token_follows_target_law():
+    """Losslessness on the device: with one fixed context and 20000 request
+    keys, the first emitted token of a round (accepted draft or residual) must
+    follow p_t^1 (chi-square, p-value floor 1e-4)."""
+    from scipy import stats
+    V, r, gamma, B = 6, 16, 3, 20000
+    rng = np.random.default_rng(42)
+    U1 = rng.standard_normal((gamma, V)).astype(np.float32) * 1.5
+    T1 = rng.standard_normal((gamma + 1, V)).astype(np.float32) * 1.5
+    W1 = rng.standard_normal((V, r)).astype(np.float32) * 0.3
+    W2 = rng.standard_normal((r, V)).astype(np.float32) * 0.3
+    U = torch.from_numpy(np.broadcast_to(U1, (B, gamma, V)).copy()).cuda()
+    tgt = torch.from_numpy(np.broadcast_to(T1, (B, gamma + 1, V)).copy()).cuda()
+    x0 = torch.full((B,), 2, dtype=torch.int32).cuda()
+    seeds = seeds_tensor(workloads.request_seeds(9, B))
+    dW1, dW2 = torch.from_numpy(W1).cuda(), torch.from_numpy(W2).cuda()
+    tok, prob, lse = dsp.markov_draft(U, dW1, dW2, x0, 1.0, seeds, 0)
+    alen, otok, _ = dsp.verify(U, dW1, dW2, x0, tok, prob, tgt, 1.0, seeds, 0)
+    first = otok[:, 0].cpu().numpy()
+    pt1, _ = oracle.softmax(T1[0].astype(np.float64))
+    counts = np.bincount(first, minlength=V)
+    p = stats.chisquare(counts, pt1 * B).pvalue
+    assert p > 1e-4, (counts, pt1 * B, p)
