@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of DSpark's per-round token path on one MI355X.
+
+Metric: verified draft positions per second, B * gamma / t_step, where one
+step is one round of the gated path -- dspark_markov_draft followed by
+dspark_verify -- over one batch of the V=151936, r=256, gamma=7, B=256,
+T=0.7 synthetic workload (bf16 Markov weights, float32 logits), with the
+inputs resident in HBM.  The round counter changes every step, so the drafts
+and the accepted lengths change while the input bytes stay fixed.
+
+Printed (one JSON line): the metric, the fraction of the 8 TB/s HBM peak that
+the step's compulsory bytes reach, the roofline of the dominant kernel (the
+draft tile pass, timed live with HIP events on its own stream), the analytical
+dspark_survival time (reported beside the gated path), and the float64 oracle
+timed on the host cores on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import multiprocessing
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK = 8.0e12            # bytes/s, MI355X published peak
+MFMA_BF16_PEAK = 2.5e15      # dense bf16 FLOP/s, MI355X published peak
+METRIC = "verified draft positions/sec, V=151936 γ=7 B=256; % of HBM roofline"
+TILE_COLS = 128              # vocabulary columns per tile of the tile pass
+PMC_FILE = os.path.join(ROOT, "profiles", "tile_pass_sample_v151936_b256_pmc.json")
+TILE_SRC = os.path.join(ROOT, "draft_sampling_verification_bias_amd", "csrc", "tile_pass.hip")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample of requests
+# ---------------------------------------------------------------------------
+_CTX = {}
+
+
+def _oracle_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+
+
+def _oracle_round(b):
+    import oracle
+    wl, W1f, W2f = _CTX["wl"], _CTX["W1f"], _CTX["W2f"]
+    d = oracle.markov_draft(wl.U, W1f, W2f, wl.x0, wl.T, wl.seeds, wl.rnd, requests=[b])
+    v = oracle.verify(wl.U, W1f, W2f, wl.x0, d["tokens"], wl.tgt, wl.T, wl.seeds, wl.rnd, requests=[b])
+    return int(v["accept_len"][b])
+
+
+def cpu_baseline(wl, nreq):
+    import oracle
+    _CTX["wl"] = wl
+    _CTX["W1f"] = oracle.weights_as_f64(wl.W1, wl.wdtype)
+    _CTX["W2f"] = oracle.weights_as_f64(wl.W2, wl.wdtype)
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), nreq))
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(workers, initializer=_oracle_worker_init) as pool:
+        pool.map(int, range(workers))  # start the workers before timing
+        t0 = time.perf_counter()
+        pool.map(_oracle_round, range(nreq), chunksize=1)
+        t1 = time.perf_counter()
+    secs = t1 - t0
+    return {"value": nreq * wl.gamma / secs, "unit": "positions/s", "cores": workers, "kind": "oracle",
+            "sample": "draft+verify of requests 0..%d of %s (float64 numpy, %d worker processes x 1 thread, "
+                      "%.1f s wall)" % (nreq - 1, wl.name, workers, secs)}
+
+
+# ---------------------------------------------------------------------------
+def tile_pass_bytes(B, V, r):
+    """Algorithmic bytes of one draft tile-pass launch: the U_k rows, the whole
+    of W2 once, the gathered W1 rows and the per-(row, tile) summaries."""
+    ntiles = (V + TILE_COLS - 1) // TILE_COLS
+    return 4 * B * V + 2 * r * V + 2 * B * r + 8 * B * ntiles
+
+
+def step_bytes(B, gamma, V, r, accept_len):
+    """Compulsory bytes of one round (draft + verify): all U rows, target rows
+    1..n_b+1 of each request, W2 once, the W1 rows gathered by the draft and by
+    the residual of the rejecting requests."""
+    n = accept_len.astype(np.int64)
+    rej = int((n < gamma).sum())
+    return 4 * B * gamma * V + 4 * V * int((n + 1).sum()) + 2 * r * V + 2 * r * (B * gamma + rej)
+
+
+def pmc_traffic():
+    """HBM bytes per tile-pass launch from the committed counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    with open(PMC_FILE) as f:
+        rec = json.load(f)
+    src = hashlib.sha256(open(TILE_SRC, "rb").read()).hexdigest()
+    if rec.get("tile_pass_sha256") != src:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v151936_b256_t07", choices=workloads.NAMES)
+    ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the oracle baseline (0: skip)")
+    ap.add_argument("--survival-steps", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path is sharded by request with no exchange between "
+              "GPUs, and runs with more than one GPU are not part of this build (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    log("building workload %s" % args.workload)
+    wl = workloads.make(args.workload)
+    B, gamma, V, r, T = wl.B, wl.gamma, wl.V, wl.r, wl.T
+
+    cpu = None
+    if args.cpu_sample > 0:
+        log("timing the oracle on %d requests" % args.cpu_sample)
+        cpu = cpu_baseline(wl, min(args.cpu_sample, B))
+        log("oracle: %.1f positions/s on %d cores" % (cpu["value"], cpu["cores"]))
+
+    import torch
+    import draft_sampling_verification_bias_amd as dsp
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    U = torch.from_numpy(wl.U).to(dev)
+    tgt = torch.from_numpy(wl.tgt).to(dev)
+    if wl.wdtype == "bf16":
+        W1 = torch.from_numpy(wl.W1.view(np.int16)).to(dev).view(torch.bfloat16)
+        W2 = torch.from_numpy(wl.W2.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        W1, W2 = torch.from_numpy(wl.W1).to(dev), torch.from_numpy(wl.W2).to(dev)
+    x0 = torch.from_numpy(wl.x0).to(dev)
+    seeds = torch.from_numpy(wl.seeds.view(np.int64)).to(dev).view(torch.uint64)
+    del wl.U, wl.tgt
+
+    ws_d = torch.empty(dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, r), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(dsp.workspace_size(dsp.OP_VERIFY, B, gamma, V, r), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(dsp.workspace_size(dsp.OP_SURVIVAL, B, gamma, V, r), dtype=torch.uint8, device=dev)
+    dout = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+            torch.empty((B, gamma), dtype=torch.float32, device=dev),
+            torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    nsteps = args.steps
+    vouts = [(torch.empty((B,), dtype=torch.int32, device=dev),
+              torch.empty((B, gamma + 1), dtype=torch.int32, device=dev),
+              torch.empty((B, gamma), dtype=torch.float32, device=dev)) for _ in range(max(nsteps, 1))]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, rnd):
+        dsp.markov_draft(U, W1, W2, x0, T, seeds, rnd, out=dout, workspace=ws_d, stream=stream)
+        dsp.verify(U, W1, W2, x0, dout[0], dout[1], tgt, T, seeds, rnd, out=vouts[i % len(vouts)],
+                   workspace=ws_v, stream=stream)
+
+    log("warmup %d steps" % args.warmup)
+    for i in range(args.warmup):
+        step(i, i)
+    torch.cuda.synchronize()
+
+    log("timing %d steps" % nsteps)
+    dsp.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(nsteps):
+        step(i, 1000 + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = dsp.profile_read()
+    dsp.profile_enable(False)
+
+    secs = t1 - t0
+    ms_per_step = secs / nsteps * 1e3
+    lens = np.stack([vouts[i][0].cpu().numpy() for i in range(nsteps)])
+    bytes_steps = [step_bytes(B, gamma, V, r, lens[i]) for i in range(nsteps)]
+    mean_bytes = float(np.mean(bytes_steps))
+    hbm_frac = mean_bytes / (secs / nsteps) / HBM_PEAK
+    accepted = float((lens + 1).sum()) / secs
+
+    # dominant kernel: the draft tile pass (sample mode at T > 0, argmax mode at T = 0)
+    kname = "tile_pass_sample" if T > 0 else "tile_pass_greedy"
+    launches, kms = prof.get(kname, (0, 0.0))
+    k_avg_s = kms / max(launches, 1) / 1e3
+    k_bytes = tile_pass_bytes(B, V, r)
+    achieved = k_bytes / k_avg_s if k_avg_s > 0 else 0.0
+    traffic = pmc_traffic()
+    roofline = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": kname,
+                "avg_launch_us": k_avg_s * 1e6, "bytes_per_launch": k_bytes}
+    kernels = {k: {"launches": n, "avg_us": ms / n * 1e3, "ms_per_step": ms / nsteps} for k, (n, ms) in prof.items()}
+
+    # survival (analytical), timed beside the gated path
+    surv_ms = None
+    if args.survival_steps > 0:
+        cst = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        sv = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        dsp.markov_draft(U, W1, W2, x0, T, seeds, 1000, out=dout, workspace=ws_d, stream=stream)
+        for _ in range(2):
+            dsp.survival(U, W1, W2, x0, dout[0], dout[2], tgt, T, out=(cst, sv), workspace=ws_s, stream=stream)
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        for _ in range(args.survival_steps):
+            dsp.survival(U, W1, W2, x0, dout[0], dout[2], tgt, T, out=(cst, sv), workspace=ws_s, stream=stream)
+        torch.cuda.synchronize()
+        surv_ms = (time.perf_counter() - s0) / args.survival_steps * 1e3
+
+    flops = 2.0 * r * V * (B * gamma + float((lens < gamma).sum()) / nsteps)
+    out = {
+        "metric": METRIC,
+        "value": B * gamma * nsteps / secs,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": nsteps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "V": V, "r": r, "gamma": gamma, "T": T,
+                   "weights": wl.wdtype, "logits": "f32"},
+        "hbm_fraction": hbm_frac,
+        "bytes_per_step": mean_bytes,
+        "mfma_fraction": flops / (secs / nsteps) / MFMA_BF16_PEAK,
+        "accepted_tokens_per_s": accepted,
+        "mean_accept_len": float(lens.mean()),
+        "roofline": roofline,
+        "kernels": kernels,
+        "survival_ms": surv_ms,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

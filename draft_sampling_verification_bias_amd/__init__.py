@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "DsparkError", "OP_DRAFT", "OP_VERIFY", "OP_SURVIVAL", "MAX_RESIDUAL_PROPOSALS",
     "library_path", "load", "version", "workspace_size", "markov_bias",
-    "markov_draft", "verify", "survival",
+    "markov_draft", "verify", "survival", "profile_enable", "profile_read",
 ]
 
 OP_DRAFT, OP_VERIFY, OP_SURVIVAL = 0, 1, 2
@@ -63,6 +63,13 @@ def load():
     lib.dspark_verify.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
     lib.dspark_survival.restype = I
     lib.dspark_survival.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P]
+    lib.dspark_profile_enable.restype = I
+    lib.dspark_profile_enable.argtypes = [I]
+    lib.dspark_profile_kinds.restype = I
+    lib.dspark_profile_kinds.argtypes = []
+    lib.dspark_profile_get.restype = I
+    lib.dspark_profile_get.argtypes = [I, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_longlong),
+                                       ctypes.POINTER(ctypes.c_double)]
     _LIB = lib
     return lib
 
@@ -73,6 +80,24 @@ def version():
 
 def workspace_size(op, B, gamma, V, r):
     return int(load().dspark_workspace_size(op, B, gamma, V, r))
+
+
+def profile_enable(on=True):
+    """Start (clearing earlier records) or stop per-kernel HIP-event timing."""
+    _check("dspark_profile_enable", load().dspark_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """{kernel name: (launches, total milliseconds)} of the recorded launches."""
+    lib = load()
+    out = {}
+    for kind in range(lib.dspark_profile_kinds()):
+        name, n, ms = ctypes.c_char_p(), ctypes.c_longlong(), ctypes.c_double()
+        _check("dspark_profile_get", lib.dspark_profile_get(kind, ctypes.byref(name), ctypes.byref(n),
+                                                            ctypes.byref(ms)))
+        if n.value:
+            out[name.value.decode()] = (int(n.value), float(ms.value))
+    return out
 
 
 def _check(func, status):

@@ -150,6 +150,7 @@ size_t draft_workspace(int B, int gamma, int V, int r) {
 
 template <bool kGreedy, bool kBf16>
 static hipError_t launch_select(const SelectArgs& s, hipStream_t st) {
+  ProfScope prof(st, kProfDraftSelect);
   hipLaunchKernelGGL((draft_select_kernel<kGreedy, kBf16>), dim3(s.B), dim3(kSelThreads), 0, st, s);
   return hipGetLastError();
 }

@@ -127,6 +127,27 @@ hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, h
 hipError_t launch_markov_bias(const void* W1, const void* W2, bool bf16, const int32_t* tokens,
                               int n, int V, int r, float* out, hipStream_t s);
 
+// Kernel kinds of the optional event timing (profile.cpp).
+enum ProfKind : int {
+  kProfTileSample = 0, kProfTileGreedy, kProfTileOverlap, kProfTileBias, kProfDraftSelect,
+  kProfVerifyInit, kProfTargetStats, kProfVerifyDecide, kProfResidualStats, kProfResidualSelect,
+  kProfSurvivalConf, kProfSurvivalTnorm, kProfSurvivalFinish, kProfKinds
+};
+
+// Brackets the launches made during its lifetime with HIP events when timing
+// is enabled (dspark_profile_enable); otherwise does nothing.
+class ProfScope {
+ public:
+  ProfScope(hipStream_t s, int kind);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  hipStream_t stream_;
+  int index_;
+};
+
 // Round a byte count up to a 256-byte boundary (workspace carving).
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

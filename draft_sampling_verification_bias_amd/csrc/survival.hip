@@ -129,6 +129,7 @@ __global__ __launch_bounds__(kSThreads) void survival_finish_kernel(SurvivalArgs
 hipError_t launch_survival(const SurvivalArgs& a, bool bf16, hipStream_t s) {
   if (a.conf) {
     const int threads = 256;
+    ProfScope prof(s, kProfSurvivalConf);
     hipLaunchKernelGGL(survival_conf_kernel, dim3((a.B + threads - 1) / threads), dim3(threads), 0, s, a.conf, a.B,
                        a.gamma, a.survival);
     return hipGetLastError();
@@ -151,10 +152,13 @@ hipError_t launch_survival(const SurvivalArgs& a, bool bf16, hipStream_t s) {
   hipError_t e = launch_target_stats(t, greedy, rows, s);
   if (e != hipSuccess) return e;
 
-  if (greedy) {
-    hipLaunchKernelGGL((survival_tnorm_kernel<true>), dim3(rows), dim3(kSThreads), 0, s, a, w, ntv, cf);
-  } else {
-    hipLaunchKernelGGL((survival_tnorm_kernel<false>), dim3(rows), dim3(kSThreads), 0, s, a, w, ntv, cf);
+  {
+    ProfScope prof(s, kProfSurvivalTnorm);
+    if (greedy) {
+      hipLaunchKernelGGL((survival_tnorm_kernel<true>), dim3(rows), dim3(kSThreads), 0, s, a, w, ntv, cf);
+    } else {
+      hipLaunchKernelGGL((survival_tnorm_kernel<false>), dim3(rows), dim3(kSThreads), 0, s, a, w, ntv, cf);
+    }
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -181,8 +185,10 @@ hipError_t launch_survival(const SurvivalArgs& a, bool bf16, hipStream_t s) {
     ta.cf = cf;
     e = launch_tile_pass(ta, kModeOverlap, bf16, s);
     if (e != hipSuccess) return e;
+    ProfScope prof(s, kProfSurvivalFinish);
     hipLaunchKernelGGL((survival_finish_kernel<false>), dim3(a.B), dim3(kSThreads), 0, s, a, w, ntd);
   } else {
+    ProfScope prof(s, kProfSurvivalFinish);
     hipLaunchKernelGGL((survival_finish_kernel<true>), dim3(a.B), dim3(kSThreads), 0, s, a, w, ntd);
   }
   return hipGetLastError();

@@ -248,6 +248,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_pass_kernel(TileArgs a) {
 template <int kMode, bool kBf16>
 static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
   const size_t lds = kBf16 ? (size_t)kTileCols * (a.r + 8) * sizeof(uint16_t) : 0;
+  ProfScope prof(s, kProfTileSample + kMode);
   hipLaunchKernelGGL((tile_pass_kernel<kMode, kBf16>), dim3(a.ntiles), dim3(kTileThreads), lds, s, a);
   return hipGetLastError();
 }

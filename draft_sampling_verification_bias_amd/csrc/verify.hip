@@ -146,6 +146,7 @@ hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, h
   const long long items = (long long)max_rows * a.ntv;
   const int grid = (int)(items < 16384 ? items : 16384);
   if (grid <= 0) return hipSuccess;
+  ProfScope prof(s, kProfTargetStats);
   if (greedy) {
     hipLaunchKernelGGL((target_stats_kernel<true>), dim3(grid), dim3(kVThreads), 0, s, a);
   } else {
@@ -458,7 +459,10 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
   const float cf = greedy ? 0.0f : (float)(1.4426950408889634 / (double)a.temperature);
   VerifyWs w = carve_verify(a.ws, a.B, a.gamma, a.V);
 
-  hipLaunchKernelGGL(verify_init_kernel, dim3(1), dim3(kVThreads), 0, s, a, w);
+  {
+    ProfScope prof(s, kProfVerifyInit);
+    hipLaunchKernelGGL(verify_init_kernel, dim3(1), dim3(kVThreads), 0, s, a, w);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -476,6 +480,7 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
     t.tpart = w.tpart;
     e = launch_target_stats(t, greedy, a.B, s);
     if (e != hipSuccess) return e;
+    ProfScope prof(s, kProfVerifyDecide);
     if (greedy) {
       hipLaunchKernelGGL((verify_decide_kernel<true, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, k, cf, ntv);
     } else if (bf16) {
@@ -489,12 +494,21 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
   if (!greedy) {
     const long long items = (long long)a.B * ntv;
     const int sgrid = (int)(items < 4096 ? items : 4096);
-    if (bf16) {
-      hipLaunchKernelGGL((residual_stats_kernel<true>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
-      hipLaunchKernelGGL((residual_select_kernel<true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
-    } else {
-      hipLaunchKernelGGL((residual_stats_kernel<false>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
-      hipLaunchKernelGGL((residual_select_kernel<false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+    {
+      ProfScope prof(s, kProfResidualStats);
+      if (bf16) {
+        hipLaunchKernelGGL((residual_stats_kernel<true>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+      } else {
+        hipLaunchKernelGGL((residual_stats_kernel<false>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+      }
+    }
+    {
+      ProfScope prof(s, kProfResidualSelect);
+      if (bf16) {
+        hipLaunchKernelGGL((residual_select_kernel<true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+      } else {
+        hipLaunchKernelGGL((residual_select_kernel<false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+      }
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -202,6 +202,20 @@ dspark_status dspark_survival(const float* U, const void* W1, const void* W2, ds
                               float temperature, float* c_star, float* survival,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Per-kernel timing (tracing).  dspark_profile_enable(1) clears earlier
+ * records and makes every later kernel launch of the library record a HIP
+ * event before and after it on its stream; dspark_profile_enable(0) stops
+ * recording.  dspark_profile_get(kind, ...) waits for the recorded events of
+ * one kernel kind (0 <= kind < dspark_profile_kinds()) and returns its name (a
+ * static string), the number of launches recorded and their summed elapsed
+ * milliseconds.  Events are host-side objects created on first use and
+ * reused; no device memory is allocated.
+ */
+dspark_status dspark_profile_enable(int on);
+int dspark_profile_kinds(void);
+dspark_status dspark_profile_get(int kind, const char** name, long long* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

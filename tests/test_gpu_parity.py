@@ -211,7 +211,8 @@ def test_confidence_mode_survival_matches_printed_products():
         if dec is None:
             assert np.allclose(s, printed, rtol=1e-6)
         else:
-            assert np.array_equal(np.round(s.astype(np.float64), dec), np.round(np.array(printed), dec))
+            # printed to `dec` decimals: within half a unit of the last printed digit
+            assert np.all(np.abs(s.astype(np.float64) - np.array(printed)) <= 0.5 * 10.0 ** -dec + 1e-7)
     rng = np.random.default_rng(1)
     conf = rng.random((300, 7)).astype(np.float32)
     _, s = dsp.survival(None, None, None, None, None, None, None, 0.0, conf=torch.from_numpy(conf).cuda())
