@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--workload", default="v151936_b256_t07", choices=workloads.NAMES)
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the oracle baseline (0: skip)")
     ap.add_argument("--survival-steps", type=int, default=10)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="copy this many MiB device to device once before timing (a reference kernel of known "
+                         "traffic for hardware counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path is sharded by request with no exchange between "
@@ -173,19 +176,36 @@ def main():
         dsp.verify(U, W1, W2, x0, dout[0], dout[1], tgt, T, seeds, rnd, out=vouts[i % len(vouts)],
                    workspace=ws_v, stream=stream)
 
+    if args.copy_probe_mb > 0:
+        src = torch.ones(args.copy_probe_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     log("warmup %d steps" % args.warmup)
     for i in range(args.warmup):
         step(i, i)
     torch.cuda.synchronize()
 
     log("timing %d steps" % nsteps)
-    dsp.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(nsteps):
         step(i, 1000 + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+
+    # The same steps again with a HIP event pair around every kernel launch
+    # (on the launch stream) for the per-kernel durations.
+    log("timing %d steps with per-kernel events" % nsteps)
+    dsp.profile_enable(True)
+    torch.cuda.synchronize()
+    p0 = time.perf_counter()
+    for i in range(nsteps):
+        step(i, 1000 + i)
+    torch.cuda.synchronize()
+    p1 = time.perf_counter()
     prof = dsp.profile_read()
     dsp.profile_enable(False)
 
@@ -247,6 +267,7 @@ def main():
         "mean_accept_len": float(lens.mean()),
         "roofline": roofline,
         "kernels": kernels,
+        "ms_per_step_with_events": (p1 - p0) / nsteps * 1e3,
         "survival_ms": surv_ms,
         "cpu_baseline": cpu,
     }

@@ -17,6 +17,7 @@
 namespace dspark {
 
 constexpr int kSelThreads = 256;
+constexpr int kCachedTiles = 4096;   // tile summaries kept in LDS up to V = 524288
 
 struct SelectArgs {
   const float* U;
@@ -56,7 +57,8 @@ template <bool kGreedy, bool kBf16>
 __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a) {
   __shared__ PickScratch ps;
   __shared__ float sw1[512];
-  __shared__ float sbias[2][kTileCols];
+  __shared__ float2 spart[kCachedTiles];
+  __shared__ float sbias[8][kTileCols];
   __shared__ float sl[kTileCols];
   __shared__ double sterm[kTileCols];
   __shared__ float sv[kSelThreads / kWave];
@@ -91,12 +93,30 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
     }
     return;
   } else {
+    // One read of the tile summaries (kept in LDS when they fit) together
+    // with the W1 row of the previous token.
+    const bool cached = a.ntiles <= kCachedTiles;
+    float w1v[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int j = tid + q * kSelThreads;
+      w1v[q] = j < a.r ? w1_at<kBf16>(a.W1, (size_t)prev * a.r + j) : 0.0f;
+    }
     float lm = -__builtin_inff();
-    for (int t = tid; t < a.ntiles; t += kSelThreads) lm = fmaxf(lm, P[t].x);
+    for (int t = tid; t < a.ntiles; t += kSelThreads) {
+      const float2 p = P[t];
+      if (cached) spart[t] = p;
+      lm = fmaxf(lm, p.x);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int j = tid + q * kSelThreads;
+      if (j < a.r) sw1[j] = w1v[q];
+    }
     const float M = block_max<kSelThreads>(lm, sv);
     const double cf = (double)a.cf;
     auto tile_weight = [&](int t) -> double {
-      const float2 p = P[t];
+      const float2 p = cached ? spart[t] : P[t];
       return p.x == -__builtin_inff() ? 0.0 : (double)p.y * exp2((double)(p.x - M) * cf);
     };
     const double u = unit_uniform(draw_block(a.seeds[b], a.round, a.k, kStreamDraft, 0).w[0]);
@@ -104,27 +124,58 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
     int ts = block_pick_uniform<kSelThreads>(a.ntiles, tile_weight, u, ps, &base, &total);
     if (ts < 0) ts = 0;
     const double q = u * total;
-    const float mt = P[ts].x;
+    const float mt = cached ? spart[ts].x : P[ts].x;
     const double scale = exp2((double)(mt - M) * cf);
 
-    // Rescan tile ts: rebuild the 128 logits with a VALU dot product per column.
-    for (int j = tid; j < a.r; j += kSelThreads) sw1[j] = w1_at<kBf16>(a.W1, (size_t)prev * a.r + j);
-    __syncthreads();
+    // Rescan tile ts: rebuild its 128 logits.  Thread t owns columns
+    // 4 (t % 32) .. +3 and one of 8 slices of the r products; each thread keeps
+    // its whole slice of W2 loads in flight, then the slices are summed in LDS
+    // in a fixed order.
     {
-      const int col = tid % kTileCols, half = tid / kTileCols;
-      const int v = ts * kTileCols + col;
-      const int kh = a.r / 2;
-      float acc = 0.0f;
-      if (v < a.V) {
-        for (int j = half * kh; j < (half + 1) * kh; ++j) acc = fmaf(sw1[j], w2_at<kBf16>(a.W2, (size_t)j * a.V + v), acc);
+      const int quad = tid & 31, slice = tid >> 5;
+      const int kslice = a.r / 8;                 // r % 16 == 0, so kslice is even
+      const int c = ts * kTileCols + 4 * quad;
+      const bool vec = kBf16 && (c + 4 <= a.V) && ((a.V & 3) == 0);
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j0 = slice * kslice; j0 < (slice + 1) * kslice; j0 += 32) {
+        float w[32][4];
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) {
+          const int j = j0 + jj;
+          if (j < (slice + 1) * kslice) {
+            if (vec) {
+              const uint2 p = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.W2) + (size_t)j * a.V + c);
+              w[jj][0] = __uint_as_float(p.x << 16);
+              w[jj][1] = __uint_as_float(p.x & 0xffff0000u);
+              w[jj][2] = __uint_as_float(p.y << 16);
+              w[jj][3] = __uint_as_float(p.y & 0xffff0000u);
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) w[jj][q] = c + q < a.V ? w2_at<kBf16>(a.W2, (size_t)j * a.V + c + q) : 0.0f;
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[jj][q] = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) {
+          const float e = (j0 + jj < (slice + 1) * kslice) ? sw1[j0 + jj] : 0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] = fmaf(e, w[jj][q], acc[q]);
+        }
       }
-      sbias[half][col] = acc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sbias[slice][4 * quad + q] = acc[q];
     }
     __syncthreads();
     if (tid < kTileCols) {
       const int v = ts * kTileCols + tid;
+      float bias = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) bias += sbias[g][tid];
       float l = -__builtin_inff();
-      if (v < a.V) l = a.U[((size_t)b * a.gamma + (a.k - 1)) * a.V + v] + (sbias[0][tid] + sbias[1][tid]);
+      if (v < a.V) l = a.U[((size_t)b * a.gamma + (a.k - 1)) * a.V + v] + bias;
       const float e = l == -__builtin_inff() ? 0.0f : fast_exp2((l - mt) * a.cf);
       sl[tid] = l;
       sterm[tid] = (double)e * scale;

@@ -41,6 +41,7 @@ struct TileArgs {
   float* bias_out;      // [nrows][V] (bias mode)
   int nrows, kper, k0;
   int B, gamma, V, r, ntiles;
+  int rows_per_group, ngroups;  // set by launch_tile_pass
   float cf;             // log2(e) / T; unused at T == 0
 };
 

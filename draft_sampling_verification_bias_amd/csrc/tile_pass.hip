@@ -22,6 +22,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kTileThreads = 256;
 constexpr int kNB = kTileCols / 32;  // 32-column MFMA blocks per tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kRowsPerGroup = 128;   // rows of one workgroup: one 32-row block per wave
 
 struct RowInfo {
   int b, kk;
@@ -43,56 +44,61 @@ __device__ __forceinline__ int prev_token(const TileArgs& a, RowInfo ri) {
   return ri.kk == 0 ? a.x0[ri.b] : a.tokens[(size_t)ri.b * a.gamma + ri.kk - 1];
 }
 
-// Half-wave (32-lane) reductions: lanes 0..31 and 32..63 reduce separately.
-__device__ __forceinline__ float half_max(float x) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float half_sum(float x) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ __forceinline__ void half_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o);
-    const int oi = __shfl_xor(i, o);
-    argmax_merge(v, i, ov, oi);
-  }
-}
+// ---------------------------------------------------------------------------
+// Column mapping.  MFMA output block nb (0..3), column n (0..31) of a tile is
+// vocabulary column v0 + 4 n + nb, so the four values a lane holds for one
+// row are four consecutive columns: U and target rows are read with one
+// 16-byte load per accumulator register, 512 contiguous bytes per half-wave.
+// ---------------------------------------------------------------------------
 
-// Stage W2[0:r][v0:v0+128] into LDS transposed, column-major with a padded
-// pitch, so that each lane reads its 8 consecutive-k bf16 MFMA operand with one
-// 16-byte LDS load.
-__device__ __forceinline__ void stage_w2_tile(const uint16_t* __restrict__ W2, uint16_t* sW, int r,
-                                              int V, int v0, int pitch) {
-  const int items = (r / 2) * (kTileCols / 4);
+// Stage W2[0:r][v0:v0+128] into LDS as [block nb][column n][k] (padded pitch),
+// so each lane reads its 8 consecutive-k bf16 MFMA operand with one 16-byte
+// LDS load.  A work item is 8 rows k of 4 columns: eight 8-byte global loads,
+// all issued before any LDS store, then one 16-byte LDS store per column.
+__device__ __forceinline__ void stage_w2_tile(const uint16_t* __restrict__ W2, uint16_t* sW, int r, int V, int v0,
+                                              int pitch) {
+  constexpr int kPerPass = 4;                        // items per thread per pass
+  const int items = (r / 8) * (kTileCols / 4);       // (k octet, column quad)
   const bool full = (v0 + kTileCols <= V) && ((V & 3) == 0);
-  for (int it = threadIdx.x; it < items; it += kTileThreads) {
-    const int cq = it % (kTileCols / 4);
-    const int kp = it / (kTileCols / 4);
-    const int kA = 2 * kp;
-    const int c = v0 + 4 * cq;
-    uint16_t e0[4], e1[4];
-    if (full) {
-      const uint2 p0 = *reinterpret_cast<const uint2*>(W2 + (size_t)kA * V + c);
-      const uint2 p1 = *reinterpret_cast<const uint2*>(W2 + (size_t)(kA + 1) * V + c);
-      e0[0] = p0.x & 0xffff; e0[1] = p0.x >> 16; e0[2] = p0.y & 0xffff; e0[3] = p0.y >> 16;
-      e1[0] = p1.x & 0xffff; e1[1] = p1.x >> 16; e1[2] = p1.y & 0xffff; e1[3] = p1.y >> 16;
-    } else {
+  for (int base = 0; base < items; base += kPerPass * kTileThreads) {
+    uint2 p[kPerPass][8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool ok = c + q < V;
-        e0[q] = ok ? W2[(size_t)kA * V + c + q] : (uint16_t)0;
-        e1[q] = ok ? W2[(size_t)(kA + 1) * V + c + q] : (uint16_t)0;
+    for (int j = 0; j < kPerPass; ++j) {
+      const int it = base + j * kTileThreads + threadIdx.x;
+      const int n = it % (kTileCols / 4);
+      const int k8 = 8 * (it / (kTileCols / 4));
+      const int c = v0 + 4 * n;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        if (it < items && full) {
+          p[j][kk] = *reinterpret_cast<const uint2*>(W2 + (size_t)(k8 + kk) * V + c);
+        } else if (it < items) {
+          uint32_t e[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] = c + q < V ? W2[(size_t)(k8 + kk) * V + c + q] : 0u;
+          p[j][kk] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        } else {
+          p[j][kk] = make_uint2(0u, 0u);
+        }
       }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<uint32_t*>(sW + (size_t)(4 * cq + q) * pitch + kA) =
-          (uint32_t)e0[q] | ((uint32_t)e1[q] << 16);
+    for (int j = 0; j < kPerPass; ++j) {
+      const int it = base + j * kTileThreads + threadIdx.x;
+      if (it >= items) break;
+      const int n = it % (kTileCols / 4);
+      const int k8 = 8 * (it / (kTileCols / 4));
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        uint32_t h[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const uint32_t wrd = (nb < 2) ? p[j][kk].x : p[j][kk].y;
+          h[kk] = (nb & 1) ? (wrd >> 16) : (wrd & 0xffffu);
+        }
+        const uint4 v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        *reinterpret_cast<uint4*>(sW + (size_t)(nb * 32 + n) * pitch + k8) = v;
+      }
     }
   }
 }
@@ -100,24 +106,283 @@ __device__ __forceinline__ void stage_w2_tile(const uint16_t* __restrict__ W2, u
 // Row index of accumulator register i for this lane in the 32x32 MFMA output.
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
+// Four consecutive columns c..c+3 of a row, -inf past the end of the row.
+__device__ __forceinline__ float4 load4(const float* __restrict__ row, int c, int V, bool full) {
+  if (full) return *reinterpret_cast<const float4*>(row + c);
+  float4 r;
+  r.x = c < V ? row[c] : -__builtin_inff();
+  r.y = c + 1 < V ? row[c + 1] : -__builtin_inff();
+  r.z = c + 2 < V ? row[c + 2] : -__builtin_inff();
+  r.w = c + 3 < V ? row[c + 3] : -__builtin_inff();
+  return r;
+}
+
+__device__ __forceinline__ float comp(const float4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; }
+
+// (max, sum of 2^((x - max) cf)) pairs: merge (m, s) with (om, os).
+struct MergeMS {
+  float cf;
+  __device__ __forceinline__ void operator()(float& m, float& s, float om, float os) const {
+    const float M = fmaxf(m, om);
+    const float lo = fminf(m, om);
+    const float e = M == -__builtin_inff() ? 0.0f : fast_exp2((lo - M) * cf);
+    const float sh = m >= om ? s : os;
+    const float sl = m >= om ? os : s;
+    s = sh + sl * e;
+    m = M;
+  }
+};
+
+// (value, index as float bits): larger value, lower index on ties.
+struct MergeArgmax {
+  __device__ __forceinline__ void operator()(float& v, float& ib, float ov, float oib) const {
+    int i = __float_as_int(ib);
+    argmax_merge(v, i, ov, __float_as_int(oib));
+    ib = __int_as_float(i);
+  }
+};
+
+struct MergeSum {
+  __device__ __forceinline__ void operator()(float& v, float& u, float ov, float ou) const {
+    v += ov;
+    u += ou;
+  }
+};
+
+// One exchange of the transposing reduction: with H = half the live count,
+// a lane keeps elements [0, H) or [H, 2H) (by its bit `o`) merged with the
+// partner's copy of the same elements.
+template <int H, class M>
+__device__ __forceinline__ void xstep(float (&a)[16], float (&b)[16], int lane, int o, const M& merge) {
+  const bool hi = (lane & o) != 0;
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    float ka = hi ? a[j + H] : a[j], kb = hi ? b[j + H] : b[j];
+    const float sa = hi ? a[j] : a[j + H], sb = hi ? b[j] : b[j + H];
+    const float ra = __shfl_xor(sa, o), rb = __shfl_xor(sb, o);
+    merge(ka, kb, ra, rb);
+    a[j] = ka;
+    b[j] = kb;
+  }
+}
+
+// Reduce 16 per-lane row values over the 32 lanes of each half-wave.  On
+// return a[0], b[0] hold the result for register (lane & 31) >> 1 in both
+// lanes of each even/odd pair.
+template <class M>
+__device__ __forceinline__ void transpose_reduce(float (&a)[16], float (&b)[16], int lane, const M& merge) {
+  xstep<8>(a, b, lane, 16, merge);
+  xstep<4>(a, b, lane, 8, merge);
+  xstep<2>(a, b, lane, 4, merge);
+  xstep<1>(a, b, lane, 2, merge);
+  const float ra = __shfl_xor(a[0], 1), rb = __shfl_xor(b[0], 1);
+  merge(a[0], b[0], ra, rb);
+}
+
+// Grid mapping: block -> (tile, row group).  With several row groups the
+// groups of one tile go to blocks b, b+8, ... -- the same XCD under the
+// round-robin dispatch of workgroups to the 8 XCDs -- so the W2 tile is
+// re-read from that XCD's L2.
+__device__ __forceinline__ bool block_tile(const TileArgs& a, int& tile, int& group) {
+  const int b = blockIdx.x;
+  if (a.ngroups == 1) {
+    tile = b;
+    group = 0;
+  } else {
+    const int slot = b / 8;
+    tile = (slot / a.ngroups) * 8 + (b % 8);
+    group = slot % a.ngroups;
+  }
+  return tile < a.ntiles;
+}
+
+// ---------------------------------------------------------------------------
+// Fast path of the sample and argmax modes: bf16 weights, r = 256, a full
+// 128-column tile of a vocabulary whose size is a multiple of 4, a full
+// 128-row group, and base-logit rows at a constant stride (one block position
+// of every request, or all positions of consecutive requests).  No guards, no
+// per-row index arithmetic beyond one base pointer and a constant stride.
+// ---------------------------------------------------------------------------
+constexpr int kFastR = 256;
+
+// Pack the 16-bit halves selected by `sel` of two words: v_perm_b32.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+template <int kMode>
+__device__ __forceinline__ void tile_fast(const TileArgs& a, int tile, int group, uint16_t* sW) {
+  constexpr int kPitch = kFastR + 8;
+  constexpr int kItems = (kFastR / 8) * (kTileCols / 4) / kTileThreads;  // 4
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int n = lane & 31;
+  const int v0 = tile * kTileCols;
+  const int c4 = v0 + 4 * n;
+  const int R0 = group * kRowsPerGroup + wave * 32;
+  const size_t V = (size_t)a.V;
+
+  // Previous token of the lane's A row.
+  const int arow = R0 + n;
+  const int prev = prev_token(a, row_info(a, arow));
+  const bool ok = (unsigned)prev < (unsigned)a.V;
+
+  // Base-logit rows of the 16 accumulator registers: row R at U + R * rs + k0 * V.
+  const size_t rs = a.kper == 1 ? (size_t)a.gamma * V : V;
+  const float* ubase = a.U + (size_t)(R0 + 4 * (lane >> 5)) * rs + (a.kper == 1 ? (size_t)a.k0 * V : 0) + c4;
+  float4 u4[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    u4[i] = *reinterpret_cast<const float4*>(ubase + (size_t)(8 * (i >> 2) + (i & 3)) * rs);
+
+  // W2 tile: eight k rows x four columns per item, then one 16-byte LDS store per column.
+  const uint16_t* W2 = reinterpret_cast<const uint16_t*>(a.W2);
+  uint2 p[kItems][8];
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const int it = j * kTileThreads + threadIdx.x;
+    const int q = it % (kTileCols / 4);
+    const int k8 = 8 * (it / (kTileCols / 4));
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) p[j][kk] = *reinterpret_cast<const uint2*>(W2 + (size_t)(k8 + kk) * V + v0 + 4 * q);
+  }
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const int it = j * kTileThreads + threadIdx.x;
+    const int q = it % (kTileCols / 4);
+    const int k8 = 8 * (it / (kTileCols / 4));
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const uint32_t sel = (nb & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t w[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) w[kk] = nb < 2 ? p[j][kk].x : p[j][kk].y;
+      const uint4 v = make_uint4(perm(w[1], w[0], sel), perm(w[3], w[2], sel), perm(w[5], w[4], sel),
+                                 perm(w[7], w[6], sel));
+      *reinterpret_cast<uint4*>(sW + (size_t)(nb * 32 + q) * kPitch + k8) = v;
+    }
+  }
+
+  // A operand fragments: row n of E = W1[prev], k-chunk lane / 32.
+  const int koff = 8 * (lane >> 5);
+  const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + koff;
+  bf16x8 av[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) av[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
+  if (!ok) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) av[j][q] = (__bf16)0.0f;
+  }
+  __syncthreads();
+
+  f32x16 acc[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[nb][i] = 0.0f;
+  const uint16_t* bcol = sW + (size_t)n * kPitch + koff;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(bcol + (size_t)nb * 32 * kPitch + j * 16);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], bv, acc[nb], 0, 0, 0);
+    }
+  }
+
+  float ra[16], rb2[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float x0 = acc[0][i] + u4[i].x, x1 = acc[1][i] + u4[i].y;
+    const float x2 = acc[2][i] + u4[i].z, x3 = acc[3][i] + u4[i].w;
+    if constexpr (kMode == kModeSample) {
+      const float m = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+      const float mc = m * a.cf;
+      float sum = fast_exp2(fmaf(x0, a.cf, -mc)) + fast_exp2(fmaf(x1, a.cf, -mc)) +
+                  (fast_exp2(fmaf(x2, a.cf, -mc)) + fast_exp2(fmaf(x3, a.cf, -mc)));
+      ra[i] = m;
+      rb2[i] = m == -__builtin_inff() ? 0.0f : sum;
+    } else {
+      float bv = x0;
+      int bi = c4;
+      if (x1 > bv) { bv = x1; bi = c4 + 1; }
+      if (x2 > bv) { bv = x2; bi = c4 + 2; }
+      if (x3 > bv) { bv = x3; bi = c4 + 3; }
+      ra[i] = bv;
+      rb2[i] = __int_as_float(bi);
+    }
+  }
+  if constexpr (kMode == kModeSample) {
+    transpose_reduce(ra, rb2, lane, MergeMS{a.cf});
+  } else {
+    transpose_reduce(ra, rb2, lane, MergeArgmax{});
+  }
+  if ((lane & 1) == 0) {
+    const int R = R0 + acc_row((lane & 31) >> 1, lane);
+    a.partials[(size_t)R * a.ntiles + tile] = make_float2(ra[0], rb2[0]);
+  }
+}
+
 template <int kMode, bool kBf16>
-__global__ __launch_bounds__(kTileThreads) void tile_pass_kernel(TileArgs a) {
+__global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void tile_pass_kernel(TileArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int tile = blockIdx.x;
+  int tile, group;
+  if (!block_tile(a, tile, group)) return;
+  if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
+    const bool fast = a.r == kFastR && (a.V & 3) == 0 && (tile + 1) * kTileCols <= a.V &&
+                      (group + 1) * kRowsPerGroup <= a.nrows && (a.kper == 1 || a.kper == a.gamma);
+    if (fast) {
+      tile_fast<kMode>(a, tile, group, reinterpret_cast<uint16_t*>(smem));
+      return;
+    }
+  }
   const int v0 = tile * kTileCols;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int pitch = a.r + 8;
+  const int n = lane & 31;
+  const int c4 = v0 + 4 * n;                       // first of this lane's 4 columns
+  const bool full = (v0 + kTileCols <= a.V) && ((a.V & 3) == 0);
   uint16_t* sW = reinterpret_cast<uint16_t*>(smem);
+
+  const int row0 = group * a.rows_per_group;
+  const int row1 = min(a.nrows, row0 + a.rows_per_group);
+  const int nrb = (row1 - row0 + 31) / 32;
+  const int ksteps = a.r / 16;
+
+  // The epilogue's row loads of a row block are issued before anything that
+  // waits: for the first row block even before the W2 tile is staged.
+  float4 u4[16];
+  float4 t4[kMode == kModeOverlap ? 16 : 1];
+  auto issue_rows = [&](int rb) {
+    const int R0 = row0 + rb * 32;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int R = R0 + acc_row(i, lane);
+      if (rb < nrb && R < row1 && kMode != kModeBias) {
+        const RowInfo ri = row_info(a, R);
+        u4[i] = load4(a.U + ((size_t)ri.b * a.gamma + ri.kk) * (size_t)a.V, c4, a.V, full);
+        if constexpr (kMode == kModeOverlap)
+          t4[i] = load4(a.target + ((size_t)ri.b * (a.gamma + 1) + ri.kk) * (size_t)a.V, c4, a.V, full);
+      } else {
+        u4[i] = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff());
+        if constexpr (kMode == kModeOverlap) t4[i] = u4[i];
+      }
+    }
+  };
+  issue_rows(wave);
 
   if constexpr (kBf16) {
     stage_w2_tile(reinterpret_cast<const uint16_t*>(a.W2), sW, a.r, a.V, v0, pitch);
     __syncthreads();
   }
 
-  const int nrb = (a.nrows + 31) / 32;
-  const int ksteps = a.r / 16;
   for (int rb = wave; rb < nrb; rb += kTileThreads / kWave) {
+    const int R0 = row0 + rb * 32;
+    if (rb != wave) issue_rows(rb);
+
     f32x16 acc[kNB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
@@ -126,26 +391,33 @@ __global__ __launch_bounds__(kTileThreads) void tile_pass_kernel(TileArgs a) {
 
     if constexpr (kBf16) {
       // A operand: the lane's row (lane % 32) of E = W1[prev], k-chunk lane / 32.
-      const int arow = rb * 32 + (lane & 31);
+      const int arow = R0 + (lane & 31);
       int prev = -1;
-      if (arow < a.nrows) prev = prev_token(a, row_info(a, arow));
+      if (arow < row1) prev = prev_token(a, row_info(a, arow));
       const bool ok = prev >= 0 && prev < a.V;
       const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * a.r;
       const int koff = 8 * (lane >> 5);
       const uint16_t* bcol = sW + (size_t)(lane & 31) * pitch + koff;
-#pragma unroll 4
-      for (int ks = 0; ks < ksteps; ++ks) {
-        bf16x8 av;
-        if (ok) {
-          av = *reinterpret_cast<const bf16x8*>(w1row + ks * 16 + koff);
-        } else {
+      for (int k0 = 0; k0 < ksteps; k0 += 16) {
+        bf16x8 av[16];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) av[j] = (__bf16)0.0f;
+        for (int j = 0; j < 16; ++j) {
+          if (ok && k0 + j < ksteps) {
+            av[j] = *reinterpret_cast<const bf16x8*>(w1row + (k0 + j) * 16 + koff);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) av[j][q] = (__bf16)0.0f;
+          }
         }
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(bcol + (size_t)nb * 32 * pitch + ks * 16);
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[nb], 0, 0, 0);
+        for (int j = 0; j < 16; ++j) {
+          if (k0 + j < ksteps) {
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+              const bf16x8 bv = *reinterpret_cast<const bf16x8*>(bcol + (size_t)nb * 32 * pitch + (k0 + j) * 16);
+              acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], bv, acc[nb], 0, 0, 0);
+            }
+          }
         }
       }
     } else {
@@ -155,18 +427,15 @@ __global__ __launch_bounds__(kTileThreads) void tile_pass_kernel(TileArgs a) {
       int prevs[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int R = rb * 32 + acc_row(i, lane);
+        const int R = R0 + acc_row(i, lane);
         int p = -1;
-        if (R < a.nrows) p = prev_token(a, row_info(a, R));
+        if (R < row1) p = prev_token(a, row_info(a, R));
         prevs[i] = (p >= 0 && p < a.V) ? p : -1;
       }
       for (int kq = 0; kq < a.r; ++kq) {
         float w2v[kNB];
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const int c = v0 + nb * 32 + (lane & 31);
-          w2v[nb] = c < a.V ? W2f[(size_t)kq * a.V + c] : 0.0f;
-        }
+        for (int nb = 0; nb < kNB; ++nb) w2v[nb] = c4 + nb < a.V ? W2f[(size_t)kq * a.V + c4 + nb] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float e = prevs[i] >= 0 ? W1f[(size_t)prevs[i] * a.r + kq] : 0.0f;
@@ -176,72 +445,82 @@ __global__ __launch_bounds__(kTileThreads) void tile_pass_kernel(TileArgs a) {
       }
     }
 
-    // Epilogue: register i holds row acc_row(i, lane), column lane % 32 of each block.
+    if constexpr (kMode == kModeBias) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int R = R0 + acc_row(i, lane);
+        if (R >= row1) continue;
+        const int p = a.x0[R];
+        const float nanv = __builtin_nanf("");
+        const bool ok = p >= 0 && p < a.V;
+        float* orow = a.bias_out + (size_t)R * a.V;
+        if (full) {
+          *reinterpret_cast<float4*>(orow + c4) =
+              ok ? make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]) : make_float4(nanv, nanv, nanv, nanv);
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb)
+            if (c4 + nb < a.V) orow[c4 + nb] = ok ? acc[nb][i] : nanv;
+        }
+      }
+      continue;
+    }
+
+    // Epilogue: register i holds row acc_row(i, lane), columns c4..c4+3.
+    float ra[16], rb2[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int R = rb * 32 + acc_row(i, lane);
-      const bool rok = R < a.nrows;
-      const RowInfo ri = row_info(a, rok ? R : 0);
-      const size_t urow = ((size_t)ri.b * a.gamma + ri.kk) * (size_t)a.V;
-      if constexpr (kMode == kModeBias) {
-        if (rok) {
-#pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) {
-            const int c = v0 + nb * 32 + (lane & 31);
-            if (c < a.V) {
-              const int p = a.x0[R];
-              a.bias_out[(size_t)R * a.V + c] = (p >= 0 && p < a.V) ? acc[nb][i] : __builtin_nanf("");
-            }
-          }
-        }
-        continue;
-      }
       float x[kNB];
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const int c = v0 + nb * 32 + (lane & 31);
-        x[nb] = (rok && c < a.V) ? acc[nb][i] + a.U[urow + c] : -__builtin_inff();
-      }
+      for (int nb = 0; nb < kNB; ++nb) x[nb] = acc[nb][i] + comp(u4[i], nb);  // -inf stays -inf
       if constexpr (kMode == kModeSample) {
-        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mx = half_max(mx);
-        float s = 0.0f;
-        if (mx != -__builtin_inff()) {
+        const float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        float sum = 0.0f;
+        if (m != -__builtin_inff()) {
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) s += fast_exp2((x[nb] - mx) * a.cf);
+          for (int nb = 0; nb < kNB; ++nb) sum += fast_exp2((x[nb] - m) * a.cf);
         }
-        s = half_sum(s);
-        if (rok && (lane & 31) == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(mx, s);
+        ra[i] = m;
+        rb2[i] = sum;
       } else if constexpr (kMode == kModeGreedy) {
         float bv = x[0];
-        int bi = v0 + (lane & 31);
+        int bi = c4;
 #pragma unroll
         for (int nb = 1; nb < kNB; ++nb) {
           if (x[nb] > bv) {
             bv = x[nb];
-            bi = v0 + nb * 32 + (lane & 31);
+            bi = c4 + nb;
           }
         }
-        half_argmax(bv, bi);
-        if (rok && (lane & 31) == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(bv, __int_as_float(bi));
+        ra[i] = bv;
+        rb2[i] = __int_as_float(bi);
       } else {  // kModeOverlap
-        const size_t trow = ((size_t)ri.b * (a.gamma + 1) + ri.kk) * (size_t)a.V;
-        const float ld2 = rok ? a.lse_d[(size_t)ri.b * a.gamma + ri.kk] * kLog2e : 0.0f;
-        const float lt2 = rok ? a.lt2[R] : 0.0f;
-        float s = 0.0f;
+        const int R = R0 + acc_row(i, lane);
+        float sum = 0.0f;
+        if (R < row1) {
+          const RowInfo ri = row_info(a, R);
+          const float ld2 = a.lse_d[(size_t)ri.b * a.gamma + ri.kk] * kLog2e;
+          const float lt2 = a.lt2[R];
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const int c = v0 + nb * 32 + (lane & 31);
-          if (rok && c < a.V) {
+          for (int nb = 0; nb < kNB; ++nb) {
             const float pd = fast_exp2(x[nb] * a.cf - ld2);
-            const float pt = fast_exp2(a.target[trow + c] * a.cf - lt2);
-            s += fminf(pd, pt);
+            const float pt = fast_exp2(comp(t4[kMode == kModeOverlap ? i : 0], nb) * a.cf - lt2);
+            sum += fminf(pd, pt);
           }
         }
-        s = half_sum(s);
-        if (rok && (lane & 31) == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(s, 0.0f);
+        ra[i] = sum;
+        rb2[i] = 0.0f;
       }
     }
+    if constexpr (kMode == kModeSample) {
+      transpose_reduce(ra, rb2, lane, MergeMS{a.cf});
+    } else if constexpr (kMode == kModeGreedy) {
+      transpose_reduce(ra, rb2, lane, MergeArgmax{});
+    } else {
+      transpose_reduce(ra, rb2, lane, MergeSum{});
+    }
+    const int R = R0 + acc_row((lane & 31) >> 1, lane);
+    if ((lane & 1) == 0 && R < row1) a.partials[(size_t)R * a.ntiles + tile] = make_float2(ra[0], rb2[0]);
   }
 }
 
@@ -249,7 +528,11 @@ template <int kMode, bool kBf16>
 static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
   const size_t lds = kBf16 ? (size_t)kTileCols * (a.r + 8) * sizeof(uint16_t) : 0;
   ProfScope prof(s, kProfTileSample + kMode);
-  hipLaunchKernelGGL((tile_pass_kernel<kMode, kBf16>), dim3(a.ntiles), dim3(kTileThreads), lds, s, a);
+  TileArgs g = a;
+  g.rows_per_group = kRowsPerGroup;
+  g.ngroups = (a.nrows + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int blocks = g.ngroups == 1 ? a.ntiles : ((a.ntiles + 7) / 8) * 8 * g.ngroups;
+  hipLaunchKernelGGL((tile_pass_kernel<kMode, kBf16>), dim3(blocks), dim3(kTileThreads), lds, s, g);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
   p += align256((size_t)B * sizeof(int));
   w.fb = reinterpret_cast<FallbackInfo*>(p);
   p += align256((size_t)B * sizeof(FallbackInfo));
-  w.fb_part = reinterpret_cast<double*>(p);
+  w.fb_part = reinterpret_cast<double*>(p);  // [B][ceil(V / kResCols)]
   return w;
 }
 
@@ -67,7 +67,7 @@ size_t verify_workspace(int B, int gamma, int V, int r) {
   const int ntv = tiles_of(V, kTgtCols);
   return align256((size_t)B * ntv * sizeof(float2)) + align256((size_t)(gamma + 2) * B * sizeof(int)) +
          align256((size_t)(gamma + 2) * sizeof(int)) + align256((size_t)B * sizeof(int)) +
-         align256((size_t)B * sizeof(FallbackInfo)) + align256((size_t)B * ntv * sizeof(double));
+         align256((size_t)B * sizeof(FallbackInfo)) + align256((size_t)B * tiles_of(V, 256) * sizeof(double));
 }
 
 template <bool kBf16>
@@ -87,15 +87,24 @@ __device__ __forceinline__ double wval(const void* W, size_t idx) {
 // Sample mode writes (max t, sum 2^((t - max) * cf)); greedy mode (max t,
 // argmax bits).
 // ---------------------------------------------------------------------------
+constexpr int kTilesPerItem = 4;
+
+// Each work item is kTilesPerItem consecutive 1024-column tiles of one row:
+// every thread issues its four 16-byte loads at once and the four tiles share
+// one set of block reductions.
 template <bool kGreedy>
 __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
-  __shared__ float sv[kVThreads / kWave];
-  __shared__ int si[kVThreads / kWave];
+  constexpr int kWaves = kVThreads / kWave;
+  __shared__ float sv[kWaves][kTilesPerItem];
+  __shared__ float ss[kWaves][kTilesPerItem];
+  __shared__ int si[kWaves][kTilesPerItem];
   const int nrows = a.list ? *a.count : a.nall;
-  const long long items = (long long)nrows * a.ntv;
+  const int ngrp = (a.ntv + kTilesPerItem - 1) / kTilesPerItem;
+  const long long items = (long long)nrows * ngrp;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   for (long long it = blockIdx.x; it < items; it += gridDim.x) {
-    const int li = (int)(it / a.ntv);
-    const int tile = (int)(it - (long long)li * a.ntv);
+    const int li = (int)(it / ngrp);
+    const int tg = (int)(it - (long long)li * ngrp);
     int b, kk, orow;
     if (a.list) {
       b = a.list[li];
@@ -107,43 +116,86 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
       orow = li;
     }
     const float* row = a.target + ((size_t)b * (a.gamma + 1) + kk) * (size_t)a.V;
-    const int c0 = tile * kTgtCols + threadIdx.x * kColsPerThread;
-    float x[kColsPerThread];
-    if (c0 + kColsPerThread <= a.V && (a.V & 3) == 0) {
-      const float4 q = *reinterpret_cast<const float4*>(row + c0);
-      x[0] = q.x; x[1] = q.y; x[2] = q.z; x[3] = q.w;
-    } else {
+    float x[kTilesPerItem][kColsPerThread];
 #pragma unroll
-      for (int j = 0; j < kColsPerThread; ++j) x[j] = c0 + j < a.V ? row[c0 + j] : -__builtin_inff();
+    for (int j = 0; j < kTilesPerItem; ++j) {
+      const int c0 = (tg * kTilesPerItem + j) * kTgtCols + threadIdx.x * kColsPerThread;
+      if (c0 + kColsPerThread <= a.V && (a.V & 3) == 0) {
+        const float4 q = *reinterpret_cast<const float4*>(row + c0);
+        x[j][0] = q.x; x[j][1] = q.y; x[j][2] = q.z; x[j][3] = q.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < kColsPerThread; ++e) x[j][e] = c0 + e < a.V ? row[c0 + e] : -__builtin_inff();
+      }
     }
     if constexpr (kGreedy) {
-      float bv = x[0];
-      int bi = c0;
+      float bv[kTilesPerItem];
+      int bi[kTilesPerItem];
 #pragma unroll
-      for (int j = 1; j < kColsPerThread; ++j) {
-        if (x[j] > bv) {
-          bv = x[j];
-          bi = c0 + j;
+      for (int j = 0; j < kTilesPerItem; ++j) {
+        const int c0 = (tg * kTilesPerItem + j) * kTgtCols + threadIdx.x * kColsPerThread;
+        bv[j] = x[j][0];
+        bi[j] = c0;
+#pragma unroll
+        for (int e = 1; e < kColsPerThread; ++e) {
+          if (x[j][e] > bv[j]) {
+            bv[j] = x[j][e];
+            bi[j] = c0 + e;
+          }
+        }
+        wave_argmax(bv[j], bi[j]);
+        if (lane == 0) {
+          sv[wave][j] = bv[j];
+          si[wave][j] = bi[j];
         }
       }
-      block_argmax<kVThreads>(bv, bi, sv, si);
-      if (threadIdx.x == 0) a.tpart[(size_t)orow * a.ntv + tile] = make_float2(bv, __int_as_float(bi));
-    } else {
-      float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      m = block_max<kVThreads>(m, sv);
-      float s = 0.0f;
-      if (m != -__builtin_inff()) {
+      __syncthreads();
+      if (threadIdx.x < kTilesPerItem) {
+        const int j = threadIdx.x, t = tg * kTilesPerItem + j;
+        float v = sv[0][j];
+        int i = si[0][j];
 #pragma unroll
-        for (int j = 0; j < kColsPerThread; ++j) s += fast_exp2((x[j] - m) * a.cf);
+        for (int w = 1; w < kWaves; ++w) argmax_merge(v, i, sv[w][j], si[w][j]);
+        if (t < a.ntv) a.tpart[(size_t)orow * a.ntv + t] = make_float2(v, __int_as_float(i));
       }
-      s = block_sum<kVThreads, float>(s, sv);
-      if (threadIdx.x == 0) a.tpart[(size_t)orow * a.ntv + tile] = make_float2(m, s);
+      __syncthreads();
+    } else {
+      float m[kTilesPerItem];
+#pragma unroll
+      for (int j = 0; j < kTilesPerItem; ++j) {
+        m[j] = wave_max(fmaxf(fmaxf(x[j][0], x[j][1]), fmaxf(x[j][2], x[j][3])));
+        if (lane == 0) sv[wave][j] = m[j];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kTilesPerItem; ++j) {
+        float M = sv[0][j];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sv[w][j]);
+        float sum = 0.0f;
+        if (M != -__builtin_inff()) {
+#pragma unroll
+          for (int e = 0; e < kColsPerThread; ++e) sum += fast_exp2((x[j][e] - M) * a.cf);
+        }
+        m[j] = M;
+        sum = wave_sum(sum);
+        if (lane == 0) ss[wave][j] = sum;
+      }
+      __syncthreads();
+      if (threadIdx.x < kTilesPerItem) {
+        const int j = threadIdx.x, t = tg * kTilesPerItem + j;
+        float S = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) S += ss[w][j];
+        if (t < a.ntv) a.tpart[(size_t)orow * a.ntv + t] = make_float2(m[j], S);
+      }
+      __syncthreads();
     }
   }
 }
 
 hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, hipStream_t s) {
-  const long long items = (long long)max_rows * a.ntv;
+  const long long items = (long long)max_rows * ((a.ntv + kTilesPerItem - 1) / kTilesPerItem);
   const int grid = (int)(items < 16384 ? items : 16384);
   if (grid <= 0) return hipSuccess;
   ProfScope prof(s, kProfTargetStats);
@@ -235,18 +287,100 @@ __device__ double draft_logit(const VerifyArgs& a, const float* urow, const doub
   return (double)urow[v] + s;
 }
 
+// ---------------------------------------------------------------------------
+// Wave-level draw from p_t for the fast path (at most kPrefixMax tiles): the
+// cumulative tile weights are in LDS (scum[t] = weight of tiles < t), so a draw
+// is a binary search plus a rescan of one 1024-column tile by one wave, 16
+// consecutive columns per lane.  Same rule as the block search: the first
+// column whose cumulative weight exceeds q; the last positive one if rounding
+// leaves none.
+// ---------------------------------------------------------------------------
+constexpr int kPrefixMax = 1024;
+
+__device__ int wave_sample_target(const DecideCtx& c, const double* scum, int last_pos_tile, double q) {
+  const int lane = threadIdx.x & (kWave - 1);
+  // first tile t with scum[t + 1] > q
+  int lo = 0, hi = c.ntv;  // answer in [0, ntv]; ntv means "none"
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (scum[mid + 1] > q) hi = mid; else lo = mid + 1;
+  }
+  const int ts = lo < c.ntv ? lo : last_pos_tile;
+  const double base = scum[ts];
+  const double ql = q - base;
+  const float mt = c.P[ts].x;
+  const double scale = exp2((double)(mt - c.M) * c.cf);
+  const float cff = (float)c.cf;
+  const int c0 = ts * kTgtCols + lane * 16;
+  float x[16];
+  if (c0 + 16 <= c.V && (c.V & 3) == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v4 = *reinterpret_cast<const float4*>(c.trow + c0 + 4 * j);
+      x[4 * j] = v4.x; x[4 * j + 1] = v4.y; x[4 * j + 2] = v4.z; x[4 * j + 3] = v4.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = c0 + j < c.V ? c.trow[c0 + j] : -__builtin_inff();
+  }
+  double term[16];
+  double local = 0.0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float e = x[j] == -__builtin_inff() ? 0.0f : fast_exp2((x[j] - mt) * cff);
+    term[j] = (double)e * scale;
+    local += term[j];
+  }
+  const double incl = wave_inclusive_scan(local);
+  const double excl = incl - local;
+  const unsigned long long cross = __ballot(local > 0.0 && excl + local > ql);
+  const unsigned long long pos = __ballot(local > 0.0);
+  const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+  int col = -1;
+  if (lane == owner) {
+    double cum = excl;
+    int lastp = -1;
+    for (int j = 0; j < 16; ++j) {
+      if (term[j] > 0.0) {
+        lastp = j;
+        if (col < 0 && cum + term[j] > ql) col = j;
+      }
+      cum += term[j];
+    }
+    if (col < 0) col = lastp < 0 ? 0 : lastp;
+    col += lane * 16;
+  }
+  col = __shfl(col, owner);
+  return ts * kTgtCols + col;
+}
+
+// W1[prev] . W2[:, v] + U[v] in float64, summed by one wave.
+template <bool kBf16>
+__device__ double wave_draft_logit(const VerifyArgs& a, const float* urow, const double* sw1, int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  double s = 0.0;
+  for (int j = lane; j < a.r; j += kWave) s += sw1[j] * wval<kBf16>(a.W2, (size_t)j * a.V + v);
+  s = wave_sum(s);
+  return (double)urow[v] + s;
+}
+
 template <bool kGreedy, bool kBf16>
 __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs w, int k, float cf_f,
                                                                  int ntv) {
+  constexpr int kWaves = kVThreads / kWave;
   __shared__ PickScratch ps;
   __shared__ double sterm[kTgtCols];
+  __shared__ double scum[kPrefixMax + 1];
   __shared__ double sw1[512];
-  __shared__ double sred[kVThreads / kWave];
-  __shared__ float sv[kVThreads / kWave];
-  __shared__ int si[kVThreads / kWave];
+  __shared__ double sred[kWaves];
+  __shared__ float sv[kWaves];
+  __shared__ int si[kWaves];
+  __shared__ int s_pass[kWaves], s_tok[kWaves], s_lastpos;
   const int g = a.gamma;
   const int count = w.counts[k];
   const double cf = (double)cf_f;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const bool fast = ntv <= kPrefixMax;
   for (int li = blockIdx.x; li < count; li += gridDim.x) {
     const int b = w.lists[(size_t)k * a.B + li];
     const float2* P = w.tpart + (size_t)b * ntv;
@@ -286,20 +420,51 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       c.ntv = ntv;
       c.V = a.V;
       const uint64_t seed = a.seeds[b];
+      auto tile_weight = [&](int t) -> double {
+        const float2 p = P[t];
+        return p.x == -__builtin_inff() ? 0.0 : (double)p.y * exp2((double)(p.x - c.M) * cf);
+      };
+      // Normaliser, and on the fast path the cumulative tile weights in LDS.
+      double Z;
+      if (fast) {
+        const int cs = (ntv + kVThreads - 1) / kVThreads;
+        const int t0 = min(ntv, (int)threadIdx.x * cs), t1 = min(ntv, t0 + cs);
+        double local = 0.0;
+        for (int t = t0; t < t1; ++t) local += tile_weight(t);
+        if (threadIdx.x == 0) s_lastpos = 0;
+        const double excl = block_exclusive_scan<kVThreads>(local, ps.red, Z);
+        double cum = excl;
+        for (int t = t0; t < t1; ++t) {
+          const double wt = tile_weight(t);
+          cum += wt;
+          scum[t + 1] = cum;
+          if (wt > 0.0) atomicMax(&s_lastpos, t);
+        }
+        if (threadIdx.x == 0) scum[0] = 0.0;
+        __syncthreads();
+      } else {
+        Z = block_total<kVThreads>(ntv, tile_weight, ps);
+      }
       if (k > g) {  // bonus token from the position after the block
         const double u = unit_uniform(draw_block(seed, a.round, g + 1, kStreamResidual, 0).w[0]);
-        const int y = sample_target(c, u, ps, sterm, nullptr);
+        int y;
+        if (fast) {
+          if (wave == 0) {
+            const int v = wave_sample_target(c, scum, s_lastpos, u * Z);
+            if (lane == 0) s_tok[0] = v;
+          }
+          __syncthreads();
+          y = s_tok[0];
+          __syncthreads();
+        } else {
+          y = sample_target(c, u, ps, sterm, nullptr);
+        }
         if (threadIdx.x == 0) {
           a.out_tokens[(size_t)b * (g + 1) + g] = y;
           a.accept_len[b] = g;
         }
         continue;
       }
-      auto tile_weight = [&](int t) -> double {
-        const float2 p = P[t];
-        return p.x == -__builtin_inff() ? 0.0 : (double)p.y * exp2((double)(p.x - c.M) * cf);
-      };
-      const double Z = block_total<kVThreads>(ntv, tile_weight, ps);
       const int x = a.draft_tokens[(size_t)b * g + k - 1];
       const double ptx = exp2((double)(trow[x] - c.M) * cf) / Z;
       const double pdx = (double)a.draft_prob[(size_t)b * g + k - 1];
@@ -321,18 +486,47 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
       const double lx = draft_logit<kBf16>(a, urow, sw1, x, sred);
       int found = -1;
-      for (int i = 0; i < DSPARK_MAX_RESIDUAL_PROPOSALS; ++i) {
-        const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
-        const double up = unit_uniform(d.w[0]);
-        const double ua = unit_uniform(d.w[1]);
-        const int v = sample_target(c, up, ps, sterm, nullptr);
-        const double ptv = exp2((double)(trow[v] - c.M) * cf) / Z;
-        const double lv = draft_logit<kBf16>(a, urow, sw1, v, sred);
-        const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
-        const double keep = fmax(0.0, 1.0 - pdv / ptv);
-        if (ua < keep) {
-          found = v;
-          break;
+      if (fast) {
+        // Proposals in batches of one per wave; the first passing index wins.
+        for (int i0 = 0; i0 < DSPARK_MAX_RESIDUAL_PROPOSALS && found < 0; i0 += kWaves) {
+          const int i = i0 + wave;
+          int pass = 0, v = -1;
+          if (i < DSPARK_MAX_RESIDUAL_PROPOSALS) {
+            const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
+            const double up = unit_uniform(d.w[0]);
+            const double ua = unit_uniform(d.w[1]);
+            v = wave_sample_target(c, scum, s_lastpos, up * Z);
+            const double ptv = exp2((double)(trow[v] - c.M) * cf) / Z;
+            const double lv = wave_draft_logit<kBf16>(a, urow, sw1, v);
+            const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
+            const double keep = fmax(0.0, 1.0 - pdv / ptv);
+            pass = ua < keep;
+          }
+          if (lane == 0) {
+            s_pass[wave] = pass;
+            s_tok[wave] = v;
+          }
+          __syncthreads();
+#pragma unroll
+          for (int ww = 0; ww < kWaves; ++ww) {
+            if (found < 0 && s_pass[ww]) found = s_tok[ww];
+          }
+          __syncthreads();
+        }
+      } else {
+        for (int i = 0; i < DSPARK_MAX_RESIDUAL_PROPOSALS; ++i) {
+          const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
+          const double up = unit_uniform(d.w[0]);
+          const double ua = unit_uniform(d.w[1]);
+          const int v = sample_target(c, up, ps, sterm, nullptr);
+          const double ptv = exp2((double)(trow[v] - c.M) * cf) / Z;
+          const double lv = draft_logit<kBf16>(a, urow, sw1, v, sred);
+          const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
+          const double keep = fmax(0.0, 1.0 - pdv / ptv);
+          if (ua < keep) {
+            found = v;
+            break;
+          }
         }
       }
       if (threadIdx.x == 0) {
@@ -352,88 +546,119 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
           w.fb_list[pos] = b;
         }
       }
+      __syncthreads();
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Exact residual fallback: mass of max(0, p_t - p_d) per 1024-column tile,
-// then one inverse-CDF draw with the stream-3 uniform.
+// Exact residual fallback: mass of max(0, p_t - p_d) per 256-column chunk,
+// then one inverse-CDF draw with the stream-3 uniform.  p_d needs the bias at
+// every column of the row, so each chunk rebuilds 256 bias values: thread t
+// owns columns 4 (t % 64) .. +3 of the chunk and a quarter of the r products,
+// with all of its W2 loads in flight; the quarters are summed in LDS in a
+// fixed order, so both kernels obtain bit-identical residual terms.
 // ---------------------------------------------------------------------------
+constexpr int kResCols = 256;
+
 template <bool kBf16>
-__device__ void residual_terms(const VerifyArgs& a, const FallbackInfo& f, int b, int tile, const double* sw1,
-                               double cf, double* res /* [kColsPerThread] */) {
+__device__ double residual_term(const VerifyArgs& a, const FallbackInfo& f, int b, int chunk, const float* sw1f,
+                                float (*sbias)[kResCols], double cf) {
   const int g = a.gamma;
-  const float* trow = a.target + ((size_t)b * (g + 1) + (f.j - 1)) * (size_t)a.V;
-  const float* urow = a.U + ((size_t)b * g + (f.j - 1)) * (size_t)a.V;
-  const int c0 = tile * kTgtCols + threadIdx.x * kColsPerThread;
+  const int quad = threadIdx.x & 63, slice = threadIdx.x >> 6;
+  const int kq = a.r / 4;  // r % 16 == 0
+  const int c = chunk * kResCols + 4 * quad;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bool vec = kBf16 && (c + 4 <= a.V) && ((a.V & 3) == 0);
+  for (int j0 = slice * kq; j0 < (slice + 1) * kq; j0 += 32) {
+    float wv[32][4];
 #pragma unroll
-  for (int q = 0; q < kColsPerThread; ++q) {
-    const int v = c0 + q;
-    res[q] = 0.0;
-    if (v < a.V) {
-      const float t = trow[v];
-      const double pt = t == -__builtin_inff() ? 0.0 : exp2((double)(t - (float)f.M) * cf) / f.Z;
-      double s = 0.0;
-      for (int j = 0; j < a.r; ++j) s += sw1[j] * wval<kBf16>(a.W2, (size_t)j * a.V + v);
-      const float uu = urow[v];
-      const double pd = uu == -__builtin_inff() ? 0.0 : f.pdx * exp(((double)uu + s - f.lx) * a.inv_t_d);
-      res[q] = fmax(0.0, pt - pd);
+    for (int jj = 0; jj < 32; ++jj) {
+      const int j = j0 + jj;
+      if (j < (slice + 1) * kq && vec) {
+        const uint2 p = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.W2) + (size_t)j * a.V + c);
+        wv[jj][0] = __uint_as_float(p.x << 16);
+        wv[jj][1] = __uint_as_float(p.x & 0xffff0000u);
+        wv[jj][2] = __uint_as_float(p.y << 16);
+        wv[jj][3] = __uint_as_float(p.y & 0xffff0000u);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          wv[jj][q] = (j < (slice + 1) * kq && c + q < a.V) ? (float)wval<kBf16>(a.W2, (size_t)j * a.V + c + q) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) {
+      const float e = j0 + jj < (slice + 1) * kq ? sw1f[j0 + jj] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(e, wv[jj][q], acc[q]);
     }
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sbias[slice][4 * quad + q] = acc[q];
+  __syncthreads();
+  const int v = chunk * kResCols + threadIdx.x;
+  double res = 0.0;
+  if (v < a.V) {
+    const float bias = (sbias[0][threadIdx.x] + sbias[1][threadIdx.x]) + (sbias[2][threadIdx.x] + sbias[3][threadIdx.x]);
+    const float t = a.target[((size_t)b * (g + 1) + (f.j - 1)) * (size_t)a.V + v];
+    const float uu = a.U[((size_t)b * g + (f.j - 1)) * (size_t)a.V + v];
+    const double pt = t == -__builtin_inff() ? 0.0 : exp2((double)(t - (float)f.M) * cf) / f.Z;
+    const double pd = uu == -__builtin_inff() ? 0.0 : f.pdx * exp(((double)uu + (double)bias - f.lx) * a.inv_t_d);
+    res = fmax(0.0, pt - pd);
+  }
+  __syncthreads();
+  return res;
 }
 
 template <bool kBf16>
-__global__ __launch_bounds__(kVThreads) void residual_stats_kernel(VerifyArgs a, VerifyWs w, float cf_f, int ntv) {
-  __shared__ double sw1[512];
+__global__ __launch_bounds__(kVThreads) void residual_stats_kernel(VerifyArgs a, VerifyWs w, float cf_f, int ntr) {
+  __shared__ float sw1f[512];
+  __shared__ float sbias[4][kResCols];
   __shared__ double sred[kVThreads / kWave];
   const int count = w.counts[0];
-  const long long items = (long long)count * ntv;
+  const long long items = (long long)count * ntr;
   for (long long it = blockIdx.x; it < items; it += gridDim.x) {
-    const int li = (int)(it / ntv);
-    const int tile = (int)(it - (long long)li * ntv);
+    const int li = (int)(it / ntr);
+    const int chunk = (int)(it - (long long)li * ntr);
     const int b = w.fb_list[li];
     const FallbackInfo f = w.fb[b];
-    for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1[j] = wval<kBf16>(a.W1, (size_t)f.prev * a.r + j);
+    for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1f[j] = (float)wval<kBf16>(a.W1, (size_t)f.prev * a.r + j);
     __syncthreads();
-    double res[kColsPerThread];
-    residual_terms<kBf16>(a, f, b, tile, sw1, (double)cf_f, res);
-    double s = 0.0;
-#pragma unroll
-    for (int q = 0; q < kColsPerThread; ++q) s += res[q];
-    s = block_sum<kVThreads, double>(s, sred);
-    if (threadIdx.x == 0) w.fb_part[(size_t)b * ntv + tile] = s;
+    const double res = residual_term<kBf16>(a, f, b, chunk, sw1f, sbias, (double)cf_f);
+    const double s = block_sum<kVThreads, double>(res, sred);
+    if (threadIdx.x == 0) w.fb_part[(size_t)b * ntr + chunk] = s;
   }
 }
 
 template <bool kBf16>
-__global__ __launch_bounds__(kVThreads) void residual_select_kernel(VerifyArgs a, VerifyWs w, float cf_f, int ntv) {
+__global__ __launch_bounds__(kVThreads) void residual_select_kernel(VerifyArgs a, VerifyWs w, float cf_f, int ntv,
+                                                                   int ntr) {
   __shared__ PickScratch ps;
   __shared__ double sterm[kTgtCols];
-  __shared__ double sw1[512];
+  __shared__ float sw1f[512];
+  __shared__ float sbias[4][kResCols];
   const int count = w.counts[0];
   const int g = a.gamma;
   for (int li = blockIdx.x; li < count; li += gridDim.x) {
     const int b = w.fb_list[li];
     const FallbackInfo f = w.fb[b];
     const double u = unit_uniform(draw_block(a.seeds[b], a.round, f.j, kStreamFallback, 0).w[0]);
-    const double* FP = w.fb_part + (size_t)b * ntv;
-    auto tile_mass = [&](int t) -> double { return FP[t]; };
+    const double* FP = w.fb_part + (size_t)b * ntr;
+    auto chunk_mass = [&](int t) -> double { return FP[t]; };
     double base = 0.0, total = 0.0;
-    int ts = block_pick_uniform<kVThreads>(ntv, tile_mass, u, ps, &base, &total);
+    const int ts = block_pick_uniform<kVThreads>(ntr, chunk_mass, u, ps, &base, &total);
     int y;
     if (total > 0.0 && ts >= 0) {
-      for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1[j] = wval<kBf16>(a.W1, (size_t)f.prev * a.r + j);
+      for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1f[j] = (float)wval<kBf16>(a.W1, (size_t)f.prev * a.r + j);
       __syncthreads();
-      double res[kColsPerThread];
-      residual_terms<kBf16>(a, f, b, ts, sw1, (double)cf_f, res);
-#pragma unroll
-      for (int q = 0; q < kColsPerThread; ++q) sterm[threadIdx.x * kColsPerThread + q] = res[q];
+      const double res = residual_term<kBf16>(a, f, b, ts, sw1f, sbias, (double)cf_f);
+      sterm[threadIdx.x] = res;
       __syncthreads();
       auto col_weight = [&](int j) -> double { return sterm[j]; };
-      int col = block_pick_target<kVThreads>(kTgtCols, col_weight, u * total - base, ps, nullptr);
+      int col = block_pick_target<kVThreads>(kResCols, col_weight, u * total - base, ps, nullptr);
       if (col < 0) col = 0;
-      y = ts * kTgtCols + col;
+      y = ts * kResCols + col;
     } else {
       // No residual mass (possible only through rounding): draw from p_t.
       DecideCtx c;
@@ -492,22 +717,23 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (!greedy) {
-    const long long items = (long long)a.B * ntv;
-    const int sgrid = (int)(items < 4096 ? items : 4096);
+    const int ntr = tiles_of(a.V, kResCols);
+    const long long items = (long long)a.B * ntr;
+    const int sgrid = (int)(items < 1024 ? items : 1024);
     {
       ProfScope prof(s, kProfResidualStats);
       if (bf16) {
-        hipLaunchKernelGGL((residual_stats_kernel<true>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+        hipLaunchKernelGGL((residual_stats_kernel<true>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntr);
       } else {
-        hipLaunchKernelGGL((residual_stats_kernel<false>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+        hipLaunchKernelGGL((residual_stats_kernel<false>), dim3(sgrid), dim3(kVThreads), 0, s, a, w, cf, ntr);
       }
     }
     {
       ProfScope prof(s, kProfResidualSelect);
       if (bf16) {
-        hipLaunchKernelGGL((residual_select_kernel<true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+        hipLaunchKernelGGL((residual_select_kernel<true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv, ntr);
       } else {
-        hipLaunchKernelGGL((residual_select_kernel<false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv);
+        hipLaunchKernelGGL((residual_select_kernel<false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, cf, ntv, ntr);
       }
     }
     e = hipGetLastError();

@@ -117,6 +117,10 @@ SMALL = [
     ("tiny_v1000_b4", dict(V=2, B=3, gamma=2)),
     ("v151936_b32", dict(V=5, B=2, gamma=3, r=16)),
     ("v151936_b32", dict(V=130, B=1, gamma=1, r=512)),
+    # r = 256, V % 4 == 0: full tiles and full 128-row groups take the guard-free
+    # path, the ragged last tile and the 2-row tail group the general one
+    ("v151936_b32", dict(V=4100, B=130, gamma=3)),
+    ("greedy_v151936_b512", dict(V=2052, B=131, gamma=3)),
 ]
 
 
@@ -243,3 +247,36 @@ def test_first_emitted_token_follows_target_law():
     counts = np.bincount(first, minlength=V)
     p = stats.chisquare(counts, pt1 * B).pvalue
     assert p > 1e-4, (counts, pt1 * B, p)
+
+
+def test_exact_residual_fallback_rows():
+    """Target rows a hair away from the draft rows: rejections are rare and,
+    when they happen, the residual mass is so small that most of them exhaust
+    the 16 proposals and take the exact residual inverse CDF (stream 3)."""
+    V, r, gamma, B = 300, 16, 3, 2000
+    rng = np.random.default_rng(5)
+    U = rng.standard_normal((B, gamma, V)).astype(np.float32)
+    W1 = (rng.standard_normal((V, r)) * 0.3).astype(np.float32)
+    W2 = (rng.standard_normal((r, V)) * 0.3).astype(np.float32)
+    x0 = rng.integers(0, V, size=B).astype(np.int32)
+    seeds = workloads.request_seeds(3, B)
+    dU, dW1, dW2 = torch.from_numpy(U).cuda(), torch.from_numpy(W1).cuda(), torch.from_numpy(W2).cuda()
+    dx0, dseeds = torch.from_numpy(x0).cuda(), seeds_tensor(seeds)
+    tok, prob, lse = dsp.markov_draft(dU, dW1, dW2, dx0, 1.0, dseeds, 4)
+    tok_h = tok.cpu().numpy()
+    W1d, W2d = W1.astype(np.float64), W2.astype(np.float64)
+    tgt = np.empty((B, gamma + 1, V), dtype=np.float32)
+    prev = x0.copy()
+    for k in range(gamma):
+        tgt[:, k] = (U[:, k].astype(np.float64) + W1d[prev] @ W2d + rng.normal(0, 0.03, (B, V))).astype(np.float32)
+        prev = tok_h[:, k]
+    tgt[:, gamma] = rng.standard_normal((B, V)).astype(np.float32)
+    alen, otok, aprob = dsp.verify(dU, dW1, dW2, dx0, tok, prob, torch.from_numpy(tgt).cuda(), 1.0, dseeds, 4)
+    ref_d = oracle.markov_draft(U, W1d, W2d, x0, 1.0, seeds, 4)
+    n, ex, whole = compare_draft(ref_d, tok_h, prob.cpu().numpy(), lse.cpu().numpy(), list(range(B)), 1.0)
+    reqs = sorted(whole)
+    vref = oracle.verify(U, W1d, W2d, x0, tok_h, tgt, 1.0, seeds, 4, requests=reqs)
+    nv, exv = compare_verify(vref, alen.cpu().numpy(), otok.cpu().numpy(), aprob.cpu().numpy(), reqs, 1.0)
+    rejected = int((alen.cpu().numpy() < gamma).sum())
+    say("[fallback] %d requests equal, %d exempt, %d rejected" % (nv, exv, rejected))
+    assert rejected >= 20
