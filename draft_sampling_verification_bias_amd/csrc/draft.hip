@@ -18,6 +18,7 @@ namespace dspark {
 
 constexpr int kSelThreads = 256;
 constexpr int kCachedTiles = 4096;   // tile summaries kept in LDS up to V = 524288
+constexpr int kPerThread = 8;        // summaries loaded per thread before the first use
 
 struct SelectArgs {
   const float* U;
@@ -67,6 +68,17 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const size_t out = (size_t)b * a.gamma + (a.k - 1);
+  // The tile summaries are loaded up front (all loads of a thread in flight
+  // together) while the previous token is fetched.
+  const float2* P = a.partials + (size_t)b * a.ntiles;
+  float2 pr[kPerThread];
+  if constexpr (!kGreedy) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int t = tid + j * kSelThreads;
+      pr[j] = t < a.ntiles ? P[t] : make_float2(-__builtin_inff(), 0.0f);
+    }
+  }
   const int prev = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
   if (prev < 0 || prev >= a.V) {  // invalid anchor or earlier position: propagate
     if (tid == 0) {
@@ -76,7 +88,6 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
     }
     return;
   }
-  const float2* P = a.partials + (size_t)b * a.ntiles;
 
   if constexpr (kGreedy) {
     float bv = -__builtin_inff();
@@ -100,10 +111,19 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int j = tid + q * kSelThreads;
-      w1v[q] = j < a.r ? w1_at<kBf16>(a.W1, (size_t)prev * a.r + j) : 0.0f;
+      const float v = w1_at<kBf16>(a.W1, (size_t)prev * a.r + (j < a.r ? j : 0));  // clamped: no branch
+      w1v[q] = j < a.r ? v : 0.0f;
     }
     float lm = -__builtin_inff();
-    for (int t = tid; t < a.ntiles; t += kSelThreads) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int t = tid + j * kSelThreads;
+      if (t < a.ntiles) {
+        if (cached) spart[t] = pr[j];
+        lm = fmaxf(lm, pr[j].x);
+      }
+    }
+    for (int t = tid + kPerThread * kSelThreads; t < a.ntiles; t += kSelThreads) {
       const float2 p = P[t];
       if (cached) spart[t] = p;
       lm = fmaxf(lm, p.x);
@@ -115,13 +135,18 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
     }
     const float M = block_max<kSelThreads>(lm, sv);
     const double cf = (double)a.cf;
-    auto tile_weight = [&](int t) -> double {
-      const float2 p = cached ? spart[t] : P[t];
-      return p.x == -__builtin_inff() ? 0.0 : (double)p.y * exp2((double)(p.x - M) * cf);
+    auto weight_of = [&](float2 p) -> double {
+      return p.x == -__builtin_inff() ? 0.0 : (double)p.y * (double)fast_exp2((p.x - M) * a.cf);
     };
     const double u = unit_uniform(draw_block(a.seeds[b], a.round, a.k, kStreamDraft, 0).w[0]);
     double total = 0.0, base = 0.0;
-    int ts = block_pick_uniform<kSelThreads>(a.ntiles, tile_weight, u, ps, &base, &total);
+    int ts;
+    if (cached) {
+      ts = block_pick_uniform<kSelThreads>(a.ntiles, [&](int t) { return weight_of(spart[t]); }, u, ps, &base,
+                                           &total);
+    } else {
+      ts = block_pick_uniform<kSelThreads>(a.ntiles, [&](int t) { return weight_of(P[t]); }, u, ps, &base, &total);
+    }
     if (ts < 0) ts = 0;
     const double q = u * total;
     const float mt = cached ? spart[ts].x : P[ts].x;
@@ -137,30 +162,36 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
       const int c = ts * kTileCols + 4 * quad;
       const bool vec = kBf16 && (c + 4 <= a.V) && ((a.V & 3) == 0);
       float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int j0 = slice * kslice; j0 < (slice + 1) * kslice; j0 += 32) {
+      const int jend = (slice + 1) * kslice;
+      // Loads use clamped indices so that every load of a chunk is issued
+      // before the first use; out-of-range terms are zeroed afterwards.
+      for (int j0 = slice * kslice; j0 < jend; j0 += 32) {
         float w[32][4];
+        if (vec) {
 #pragma unroll
-        for (int jj = 0; jj < 32; ++jj) {
-          const int j = j0 + jj;
-          if (j < (slice + 1) * kslice) {
-            if (vec) {
-              const uint2 p = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.W2) + (size_t)j * a.V + c);
-              w[jj][0] = __uint_as_float(p.x << 16);
-              w[jj][1] = __uint_as_float(p.x & 0xffff0000u);
-              w[jj][2] = __uint_as_float(p.y << 16);
-              w[jj][3] = __uint_as_float(p.y & 0xffff0000u);
-            } else {
+          for (int jj = 0; jj < 32; ++jj) {
+            const int j = min(j0 + jj, jend - 1);
+            const uint2 p = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.W2) + (size_t)j * a.V + c);
+            w[jj][0] = __uint_as_float(p.x << 16);
+            w[jj][1] = __uint_as_float(p.x & 0xffff0000u);
+            w[jj][2] = __uint_as_float(p.y << 16);
+            w[jj][3] = __uint_as_float(p.y & 0xffff0000u);
+          }
+        } else {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) w[jj][q] = c + q < a.V ? w2_at<kBf16>(a.W2, (size_t)j * a.V + c + q) : 0.0f;
+          for (int jj = 0; jj < 32; ++jj) {
+            const int j = min(j0 + jj, jend - 1);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int cc = c + q < a.V ? c + q : a.V - 1;
+              const float v = w2_at<kBf16>(a.W2, (size_t)j * a.V + cc);
+              w[jj][q] = c + q < a.V ? v : 0.0f;
             }
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) w[jj][q] = 0.0f;
           }
         }
 #pragma unroll
         for (int jj = 0; jj < 32; ++jj) {
-          const float e = (j0 + jj < (slice + 1) * kslice) ? sw1[j0 + jj] : 0.0f;
+          const float e = (j0 + jj < jend) ? sw1[j0 + jj] : 0.0f;
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[q] = fmaf(e, w[jj][q], acc[q]);
         }

@@ -107,8 +107,9 @@ size_t survival_workspace(int B, int gamma, int V, int r);
 hipError_t launch_survival(const SurvivalArgs& a, bool bf16, hipStream_t s);
 
 // Target-row statistics (verify.hip), shared by verify and survival.
-//   list mode (list != null): row li is request list[li] at block position
-//     kk0; summaries go to row b of tpart.
+//   list mode (list != null): rows_per_req rows (block positions kk0, kk0+1,
+//     ...) of each listed request b; summaries of row j go to row
+//     b * orow_stride + j of tpart.
 //   all mode: row R = b * gamma + kk for kk < gamma; summaries go to row R.
 // Sample mode writes (max t, sum 2^((t - max) * cf)) per 1024-column tile;
 // greedy mode (max t, argmax as int bits).
@@ -118,6 +119,8 @@ struct TStatsArgs {
   const int* count;  // device count (list mode)
   int nall;          // rows in all mode
   int kk0;
+  int rows_per_req;  // list mode: block positions kk0, kk0+1, ... of each listed request
+  int orow_stride;   // list mode: summaries of (b, row) go to row b * orow_stride + row
   int gamma, V, ntv;
   float cf;
   float2* tpart;

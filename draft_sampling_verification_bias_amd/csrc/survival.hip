@@ -144,6 +144,8 @@ hipError_t launch_survival(const SurvivalArgs& a, bool bf16, hipStream_t s) {
   TStatsArgs t = {};
   t.target = a.target;
   t.nall = rows;
+  t.rows_per_req = 1;
+  t.orow_stride = 1;
   t.gamma = a.gamma;
   t.V = a.V;
   t.ntv = ntv;

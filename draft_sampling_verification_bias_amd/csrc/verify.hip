@@ -25,20 +25,22 @@
 namespace dspark {
 
 constexpr int kVThreads = 256;
+constexpr int kRowsPerPhase = 2;   // block positions verified per phase
 constexpr int kColsPerThread = kTgtCols / kVThreads;  // 4
 
 struct FallbackInfo {
   int j;        // rejected position (1-based)
   int prev;     // x_{j-1}
+  int phase_row;  // row of position j within its phase's summaries
   double M, Z;  // target row max and exp-sum (base 2, scaled by cf)
   double pdx;   // p_d^j(x_j)
   double lx;    // draft logit of x_j (U + bias), float64
 };
 
 struct VerifyWs {
-  float2* tpart;        // [B][ntv] target tile summaries
-  int* lists;           // [gamma + 2][B] request lists per phase (index k)
-  int* counts;          // [gamma + 2]: counts[k] phase sizes, counts[0] fallback count
+  float2* tpart;        // [B][kRowsPerPhase][ntv] target tile summaries of the current phase
+  int* lists;           // [gamma + 2][B] request lists per phase (index ph = 1, 2, ...)
+  int* counts;          // [gamma + 2]: counts[ph] phase sizes, counts[0] fallback count
   int* fb_list;         // [B]
   FallbackInfo* fb;     // [B] indexed by request
   double* fb_part;      // [B][ntv] residual mass per tile
@@ -49,7 +51,7 @@ static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
   char* p = reinterpret_cast<char*>(ws);
   VerifyWs w;
   w.tpart = reinterpret_cast<float2*>(p);
-  p += align256((size_t)B * ntv * sizeof(float2));
+  p += align256((size_t)B * kRowsPerPhase * ntv * sizeof(float2));
   w.lists = reinterpret_cast<int*>(p);
   p += align256((size_t)(gamma + 2) * B * sizeof(int));
   w.counts = reinterpret_cast<int*>(p);
@@ -65,7 +67,7 @@ static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
 size_t verify_workspace(int B, int gamma, int V, int r) {
   (void)r;
   const int ntv = tiles_of(V, kTgtCols);
-  return align256((size_t)B * ntv * sizeof(float2)) + align256((size_t)(gamma + 2) * B * sizeof(int)) +
+  return align256((size_t)B * kRowsPerPhase * ntv * sizeof(float2)) + align256((size_t)(gamma + 2) * B * sizeof(int)) +
          align256((size_t)(gamma + 2) * sizeof(int)) + align256((size_t)B * sizeof(int)) +
          align256((size_t)B * sizeof(FallbackInfo)) + align256((size_t)B * tiles_of(V, 256) * sizeof(double));
 }
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
   __shared__ float sv[kWaves][kTilesPerItem];
   __shared__ float ss[kWaves][kTilesPerItem];
   __shared__ int si[kWaves][kTilesPerItem];
-  const int nrows = a.list ? *a.count : a.nall;
+  const int nrows = a.list ? *a.count * a.rows_per_req : a.nall;
   const int ngrp = (a.ntv + kTilesPerItem - 1) / kTilesPerItem;
   const long long items = (long long)nrows * ngrp;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -107,9 +109,10 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
     const int tg = (int)(it - (long long)li * ngrp);
     int b, kk, orow;
     if (a.list) {
-      b = a.list[li];
-      kk = a.kk0;
-      orow = b;
+      const int req = li / a.rows_per_req, row = li - req * a.rows_per_req;
+      b = a.list[req];
+      kk = a.kk0 + row;
+      orow = b * a.orow_stride + row;
     } else {
       b = li / a.gamma;
       kk = li - b * a.gamma;
@@ -364,189 +367,365 @@ __device__ double wave_draft_logit(const VerifyArgs& a, const float* urow, const
   return (double)urow[v] + s;
 }
 
+// Decision kernel for rows of more than kPrefixMax tiles: the same decisions
+// as verify_decide_kernel below, with block-wide searches over the tile
+// summaries in global memory.
 template <bool kGreedy, bool kBf16>
-__global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs w, int k, float cf_f,
+__global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(VerifyArgs a, VerifyWs w, int ph,
+                                                                         float cf_f, int ntv) {
+  __shared__ PickScratch ps;
+  __shared__ double sterm[kTgtCols];
+  __shared__ double sw1[512];
+  __shared__ double sred[kVThreads / kWave];
+  __shared__ float sv[kVThreads / kWave];
+  __shared__ int si[kVThreads / kWave];
+  const int g = a.gamma;
+  const int k0 = 2 * ph - 1, k1 = min(2 * ph, g + 1);
+  const int count = w.counts[ph];
+  const double cf = (double)cf_f;
+  for (int li = blockIdx.x; li < count; li += gridDim.x) {
+    const int b = w.lists[(size_t)ph * a.B + li];
+    for (int k = k0; k <= k1; ++k) {
+      const float2* P = w.tpart + ((size_t)b * kRowsPerPhase + (k - k0)) * ntv;
+      const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
+      bool accepted = false;
+      if constexpr (kGreedy) {
+        float bv = -__builtin_inff();
+        int bi = INT_MAX;
+        for (int t = threadIdx.x; t < ntv; t += kVThreads) argmax_merge(bv, bi, P[t].x, __float_as_int(P[t].y));
+        block_argmax<kVThreads>(bv, bi, sv, si);
+        if (k <= g) {
+          const int x = a.draft_tokens[(size_t)b * g + k - 1];
+          accepted = bi == x;
+          if (threadIdx.x == 0) {
+            if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = accepted ? 1.0f : 0.0f;
+            a.out_tokens[(size_t)b * (g + 1) + k - 1] = accepted ? x : bi;
+            if (!accepted) a.accept_len[b] = k - 1;
+          }
+        } else if (threadIdx.x == 0) {
+          a.out_tokens[(size_t)b * (g + 1) + g] = bi;
+          a.accept_len[b] = g;
+        }
+      } else {
+        float lm = -__builtin_inff();
+        for (int t = threadIdx.x; t < ntv; t += kVThreads) lm = fmaxf(lm, P[t].x);
+        DecideCtx c;
+        c.P = P;
+        c.trow = trow;
+        c.M = block_max<kVThreads>(lm, sv);
+        c.cf = cf;
+        c.ntv = ntv;
+        c.V = a.V;
+        const uint64_t seed = a.seeds[b];
+        auto tile_weight = [&](int t) -> double {
+          const float2 p = P[t];
+          return p.x == -__builtin_inff() ? 0.0 : (double)p.y * exp2((double)(p.x - c.M) * cf);
+        };
+        const double Z = block_total<kVThreads>(ntv, tile_weight, ps);
+        if (k > g) {  // bonus token from the position after the block
+          const double u = unit_uniform(draw_block(seed, a.round, g + 1, kStreamResidual, 0).w[0]);
+          const int y = sample_target(c, u, ps, sterm, nullptr);
+          if (threadIdx.x == 0) {
+            a.out_tokens[(size_t)b * (g + 1) + g] = y;
+            a.accept_len[b] = g;
+          }
+        } else {
+          const int x = a.draft_tokens[(size_t)b * g + k - 1];
+          const double ptx = exp2((double)(trow[x] - c.M) * cf) / Z;
+          const double pdx = (double)a.draft_prob[(size_t)b * g + k - 1];
+          const double alpha = fmin(1.0, ptx / pdx);
+          const double u = unit_uniform(draw_block(seed, a.round, k, kStreamAccept, 0).w[0]);
+          accepted = u < alpha;
+          if (threadIdx.x == 0) {
+            if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = (float)alpha;
+            if (accepted) a.out_tokens[(size_t)b * (g + 1) + k - 1] = x;
+          }
+          if (!accepted) {
+            const int prev = k == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + k - 2];
+            for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1[j] = wval<kBf16>(a.W1, (size_t)prev * a.r + j);
+            __syncthreads();
+            const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
+            const double lx = draft_logit<kBf16>(a, urow, sw1, x, sred);
+            int found = -1;
+            for (int i = 0; i < DSPARK_MAX_RESIDUAL_PROPOSALS; ++i) {
+              const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
+              const double up = unit_uniform(d.w[0]);
+              const double ua = unit_uniform(d.w[1]);
+              const int v = sample_target(c, up, ps, sterm, nullptr);
+              const double ptv = exp2((double)(trow[v] - c.M) * cf) / Z;
+              const double lv = draft_logit<kBf16>(a, urow, sw1, v, sred);
+              const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
+              const double keep = fmax(0.0, 1.0 - pdv / ptv);
+              if (ua < keep) {
+                found = v;
+                break;
+              }
+            }
+            if (threadIdx.x == 0) {
+              a.accept_len[b] = k - 1;
+              if (found >= 0) {
+                a.out_tokens[(size_t)b * (g + 1) + k - 1] = found;
+              } else {
+                FallbackInfo f;
+                f.j = k;
+                f.prev = prev;
+                f.phase_row = k - k0;
+                f.M = (double)c.M;
+                f.Z = Z;
+                f.pdx = pdx;
+                f.lx = lx;
+                w.fb[b] = f;
+                const int pos = atomicAdd(&w.counts[0], 1);
+                w.fb_list[pos] = b;
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if (!accepted) break;
+      if (k == k1 && threadIdx.x == 0) {
+        const int pos = atomicAdd(&w.counts[ph + 1], 1);
+        w.lists[(size_t)(ph + 1) * a.B + pos] = b;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decision kernel for rows of at most kPrefixMax tiles.  The loads are issued
+// in three dependent batches -- the request id; then everything that depends
+// only on the request (its tile summaries, drafted and previous tokens, p_d,
+// key); then everything that depends on those tokens (target logit, base
+// logit, W1 row, W2 column of the drafted token) -- so an accepted position
+// costs three memory round trips and a rejection two more per batch of four
+// residual proposals.
+// ---------------------------------------------------------------------------
+constexpr int kTilesPerThreadFast = kPrefixMax / kVThreads;  // 4
+
+// W1[prev] . W2[:, v] + U[v] in float64, summed by one wave; the W2 loads of a
+// lane are issued together (clamped indices, zeroed terms).
+template <bool kBf16>
+__device__ double wave_draft_logit_batched(const VerifyArgs& a, const float* urow, const float* sw1, int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float wv[512 / kWave];
+  const float uv = urow[v];
+#pragma unroll
+  for (int m = 0; m < 512 / kWave; ++m) {
+    const int j = lane + m * kWave;
+    wv[m] = (float)wval<kBf16>(a.W2, (size_t)(j < a.r ? j : 0) * a.V + v);
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int m = 0; m < 512 / kWave; ++m) {
+    const int j = lane + m * kWave;
+    if (j < a.r) s += (double)sw1[j] * (double)wv[m];
+  }
+  s = wave_sum(s);
+  return (double)uv + s;
+}
+
+template <bool kGreedy, bool kBf16>
+__global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs w, int ph, float cf_f,
                                                                  int ntv) {
   constexpr int kWaves = kVThreads / kWave;
   __shared__ PickScratch ps;
-  __shared__ double sterm[kTgtCols];
   __shared__ double scum[kPrefixMax + 1];
-  __shared__ double sw1[512];
+  __shared__ float sw1[512];
   __shared__ double sred[kWaves];
   __shared__ float sv[kWaves];
   __shared__ int si[kWaves];
   __shared__ int s_pass[kWaves], s_tok[kWaves], s_lastpos;
   const int g = a.gamma;
-  const int count = w.counts[k];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int k0 = 2 * ph - 1, k1 = min(2 * ph, g + 1);
+  const int count = w.counts[ph];
   const double cf = (double)cf_f;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const bool fast = ntv <= kPrefixMax;
   for (int li = blockIdx.x; li < count; li += gridDim.x) {
-    const int b = w.lists[(size_t)k * a.B + li];
-    const float2* P = w.tpart + (size_t)b * ntv;
-    const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
-    if constexpr (kGreedy) {
-      float bv = -__builtin_inff();
-      int bi = INT_MAX;
-      for (int t = threadIdx.x; t < ntv; t += kVThreads) argmax_merge(bv, bi, P[t].x, __float_as_int(P[t].y));
-      block_argmax<kVThreads>(bv, bi, sv, si);
-      if (threadIdx.x == 0) {
+    const int b = w.lists[(size_t)ph * a.B + li];
+    const uint64_t seed = kGreedy ? 0 : a.seeds[b];
+    for (int k = k0; k <= k1; ++k) {
+      const float2* P = w.tpart + ((size_t)b * kRowsPerPhase + (k - k0)) * ntv;
+      const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
+      // batch 1: the row's tile summaries and the tokens of position k
+      float2 pv[kTilesPerThreadFast];
+#pragma unroll
+      for (int j = 0; j < kTilesPerThreadFast; ++j) {
+        const int t = tid * kTilesPerThreadFast + j;
+        pv[j] = P[t < ntv ? t : ntv - 1];
+      }
+      int x = 0, prev = 0;
+      double pdx = 1.0;
+      if (k <= g) {
+        x = a.draft_tokens[(size_t)b * g + k - 1];
+        prev = k == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + k - 2];
+        if constexpr (!kGreedy) pdx = (double)a.draft_prob[(size_t)b * g + k - 1];
+      }
+      bool accepted = false;  // uniform across the block
+      if constexpr (kGreedy) {
+        float bv = -__builtin_inff();
+        int bi = INT_MAX;
+#pragma unroll
+        for (int j = 0; j < kTilesPerThreadFast; ++j) {
+          const int t = tid * kTilesPerThreadFast + j;
+          if (t < ntv) argmax_merge(bv, bi, pv[j].x, __float_as_int(pv[j].y));
+        }
+        block_argmax<kVThreads>(bv, bi, sv, si);
         if (k <= g) {
-          const int x = a.draft_tokens[(size_t)b * g + k - 1];
-          const bool acc = bi == x;
-          if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = acc ? 1.0f : 0.0f;
-          if (acc) {
-            a.out_tokens[(size_t)b * (g + 1) + k - 1] = x;
-            const int pos = atomicAdd(&w.counts[k + 1], 1);
-            w.lists[(size_t)(k + 1) * a.B + pos] = b;
-          } else {
-            a.out_tokens[(size_t)b * (g + 1) + k - 1] = bi;
-            a.accept_len[b] = k - 1;
+          accepted = bi == x;
+          if (tid == 0) {
+            if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = accepted ? 1.0f : 0.0f;
+            a.out_tokens[(size_t)b * (g + 1) + k - 1] = accepted ? x : bi;
+            if (!accepted) a.accept_len[b] = k - 1;
           }
-        } else {
+        } else if (tid == 0) {
           a.out_tokens[(size_t)b * (g + 1) + g] = bi;
           a.accept_len[b] = g;
         }
-      }
-      continue;
-    } else {
-      float lm = -__builtin_inff();
-      for (int t = threadIdx.x; t < ntv; t += kVThreads) lm = fmaxf(lm, P[t].x);
-      DecideCtx c;
-      c.P = P;
-      c.trow = trow;
-      c.M = block_max<kVThreads>(lm, sv);
-      c.cf = cf;
-      c.ntv = ntv;
-      c.V = a.V;
-      const uint64_t seed = a.seeds[b];
-      auto tile_weight = [&](int t) -> double {
-        const float2 p = P[t];
-        return p.x == -__builtin_inff() ? 0.0 : (double)p.y * exp2((double)(p.x - c.M) * cf);
-      };
-      // Normaliser, and on the fast path the cumulative tile weights in LDS.
-      double Z;
-      if (fast) {
-        const int cs = (ntv + kVThreads - 1) / kVThreads;
-        const int t0 = min(ntv, (int)threadIdx.x * cs), t1 = min(ntv, t0 + cs);
-        double local = 0.0;
-        for (int t = t0; t < t1; ++t) local += tile_weight(t);
-        if (threadIdx.x == 0) s_lastpos = 0;
-        const double excl = block_exclusive_scan<kVThreads>(local, ps.red, Z);
-        double cum = excl;
-        for (int t = t0; t < t1; ++t) {
-          const double wt = tile_weight(t);
-          cum += wt;
-          scum[t + 1] = cum;
-          if (wt > 0.0) atomicMax(&s_lastpos, t);
-        }
-        if (threadIdx.x == 0) scum[0] = 0.0;
-        __syncthreads();
       } else {
-        Z = block_total<kVThreads>(ntv, tile_weight, ps);
-      }
-      if (k > g) {  // bonus token from the position after the block
-        const double u = unit_uniform(draw_block(seed, a.round, g + 1, kStreamResidual, 0).w[0]);
-        int y;
-        if (fast) {
-          if (wave == 0) {
-            const int v = wave_sample_target(c, scum, s_lastpos, u * Z);
-            if (lane == 0) s_tok[0] = v;
-          }
-          __syncthreads();
-          y = s_tok[0];
-          __syncthreads();
-        } else {
-          y = sample_target(c, u, ps, sterm, nullptr);
-        }
-        if (threadIdx.x == 0) {
-          a.out_tokens[(size_t)b * (g + 1) + g] = y;
-          a.accept_len[b] = g;
-        }
-        continue;
-      }
-      const int x = a.draft_tokens[(size_t)b * g + k - 1];
-      const double ptx = exp2((double)(trow[x] - c.M) * cf) / Z;
-      const double pdx = (double)a.draft_prob[(size_t)b * g + k - 1];
-      const double alpha = fmin(1.0, ptx / pdx);
-      const double u = unit_uniform(draw_block(seed, a.round, k, kStreamAccept, 0).w[0]);
-      if (threadIdx.x == 0 && a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = (float)alpha;
-      if (u < alpha) {
-        if (threadIdx.x == 0) {
-          a.out_tokens[(size_t)b * (g + 1) + k - 1] = x;
-          const int pos = atomicAdd(&w.counts[k + 1], 1);
-          w.lists[(size_t)(k + 1) * a.B + pos] = b;
-        }
-        continue;
-      }
-      // Rejected at j = k: residual draw by proposals from p_t.
-      const int prev = k == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + k - 2];
-      for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1[j] = wval<kBf16>(a.W1, (size_t)prev * a.r + j);
-      __syncthreads();
-      const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
-      const double lx = draft_logit<kBf16>(a, urow, sw1, x, sred);
-      int found = -1;
-      if (fast) {
-        // Proposals in batches of one per wave; the first passing index wins.
-        for (int i0 = 0; i0 < DSPARK_MAX_RESIDUAL_PROPOSALS && found < 0; i0 += kWaves) {
-          const int i = i0 + wave;
-          int pass = 0, v = -1;
-          if (i < DSPARK_MAX_RESIDUAL_PROPOSALS) {
-            const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
-            const double up = unit_uniform(d.w[0]);
-            const double ua = unit_uniform(d.w[1]);
-            v = wave_sample_target(c, scum, s_lastpos, up * Z);
-            const double ptv = exp2((double)(trow[v] - c.M) * cf) / Z;
-            const double lv = wave_draft_logit<kBf16>(a, urow, sw1, v);
-            const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
-            const double keep = fmax(0.0, 1.0 - pdv / ptv);
-            pass = ua < keep;
-          }
-          if (lane == 0) {
-            s_pass[wave] = pass;
-            s_tok[wave] = v;
-          }
-          __syncthreads();
+        // batch 2: depends on the drafted and previous tokens
+        const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
+        float tx = 0.0f, ux = 0.0f, w1v[2] = {0.0f, 0.0f}, w2v[2] = {0.0f, 0.0f};
+        if (k <= g) {
+          tx = trow[x];
+          ux = urow[x];
 #pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) {
-            if (found < 0 && s_pass[ww]) found = s_tok[ww];
-          }
-          __syncthreads();
-        }
-      } else {
-        for (int i = 0; i < DSPARK_MAX_RESIDUAL_PROPOSALS; ++i) {
-          const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
-          const double up = unit_uniform(d.w[0]);
-          const double ua = unit_uniform(d.w[1]);
-          const int v = sample_target(c, up, ps, sterm, nullptr);
-          const double ptv = exp2((double)(trow[v] - c.M) * cf) / Z;
-          const double lv = draft_logit<kBf16>(a, urow, sw1, v, sred);
-          const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
-          const double keep = fmax(0.0, 1.0 - pdv / ptv);
-          if (ua < keep) {
-            found = v;
-            break;
+          for (int q = 0; q < 2; ++q) {
+            const int j = tid + q * kVThreads;
+            const int jc = j < a.r ? j : 0;
+            w1v[q] = (float)wval<kBf16>(a.W1, (size_t)prev * a.r + jc);
+            w2v[q] = (float)wval<kBf16>(a.W2, (size_t)jc * a.V + x);
           }
         }
-      }
-      if (threadIdx.x == 0) {
-        a.accept_len[b] = k - 1;
-        if (found >= 0) {
-          a.out_tokens[(size_t)b * (g + 1) + k - 1] = found;
+        // normaliser and cumulative tile weights
+        float lm = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < kTilesPerThreadFast; ++j) {
+          const int t = tid * kTilesPerThreadFast + j;
+          if (t < ntv) lm = fmaxf(lm, pv[j].x);
+        }
+        const float M = block_max<kVThreads>(lm, sv);
+        double wt[kTilesPerThreadFast], local = 0.0;
+#pragma unroll
+        for (int j = 0; j < kTilesPerThreadFast; ++j) {
+          const int t = tid * kTilesPerThreadFast + j;
+          wt[j] = (t < ntv && pv[j].x != -__builtin_inff())
+                      ? (double)pv[j].y * (double)fast_exp2((pv[j].x - M) * cf_f)
+                      : 0.0;
+          local += wt[j];
+        }
+        if (tid == 0) s_lastpos = 0;
+        double Z;
+        const double excl = block_exclusive_scan<kVThreads>(local, ps.red, Z);
+        {
+          double cum = excl;
+#pragma unroll
+          for (int j = 0; j < kTilesPerThreadFast; ++j) {
+            const int t = tid * kTilesPerThreadFast + j;
+            cum += wt[j];
+            if (t < ntv) {
+              scum[t + 1] = cum;
+              if (wt[j] > 0.0) atomicMax(&s_lastpos, t);
+            }
+          }
+          if (tid == 0) scum[0] = 0.0;
+        }
+        __syncthreads();
+        DecideCtx c;
+        c.P = P;
+        c.trow = trow;
+        c.M = M;
+        c.cf = cf;
+        c.ntv = ntv;
+        c.V = a.V;
+        if (k > g) {  // bonus token from the position after the block
+          const double u = unit_uniform(draw_block(seed, a.round, g + 1, kStreamResidual, 0).w[0]);
+          if (wave == 0) {
+            const int y = wave_sample_target(c, scum, s_lastpos, u * Z);
+            if (lane == 0) {
+              a.out_tokens[(size_t)b * (g + 1) + g] = y;
+              a.accept_len[b] = g;
+            }
+          }
         } else {
-          FallbackInfo f;
-          f.j = k;
-          f.prev = prev;
-          f.M = (double)c.M;
-          f.Z = Z;
-          f.pdx = pdx;
-          f.lx = lx;
-          w.fb[b] = f;
-          const int pos = atomicAdd(&w.counts[0], 1);
-          w.fb_list[pos] = b;
+          const double ptx = exp2((double)(tx - M) * cf) / Z;
+          const double alpha = fmin(1.0, ptx / pdx);
+          const double u = unit_uniform(draw_block(seed, a.round, k, kStreamAccept, 0).w[0]);
+          accepted = u < alpha;
+          if (tid == 0) {
+            if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = (float)alpha;
+            if (accepted) a.out_tokens[(size_t)b * (g + 1) + k - 1] = x;
+          }
+          if (!accepted) {
+            // Rejected at k: residual draw by proposals from p_t, one per wave.
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int j = tid + q * kVThreads;
+              if (j < a.r) sw1[j] = w1v[q];
+            }
+            double part = 0.0;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int j = tid + q * kVThreads;
+              if (j < a.r) part += (double)w1v[q] * (double)w2v[q];
+            }
+            const double lx = (double)ux + block_sum<kVThreads, double>(part, sred);
+            int found = -1;
+            for (int i0 = 0; i0 < DSPARK_MAX_RESIDUAL_PROPOSALS && found < 0; i0 += kWaves) {
+              const int i = i0 + wave;
+              int pass = 0, v = -1;
+              if (i < DSPARK_MAX_RESIDUAL_PROPOSALS) {
+                const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
+                const double up = unit_uniform(d.w[0]);
+                const double ua = unit_uniform(d.w[1]);
+                v = wave_sample_target(c, scum, s_lastpos, up * Z);
+                const float tv = trow[v];
+                const double lv = wave_draft_logit_batched<kBf16>(a, urow, sw1, v);
+                const double ptv = exp2((double)(tv - M) * cf) / Z;
+                const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
+                const double keep = fmax(0.0, 1.0 - pdv / ptv);
+                pass = ua < keep;
+              }
+              if (lane == 0) {
+                s_pass[wave] = pass;
+                s_tok[wave] = v;
+              }
+              __syncthreads();
+#pragma unroll
+              for (int ww = 0; ww < kWaves; ++ww) {
+                if (found < 0 && s_pass[ww]) found = s_tok[ww];
+              }
+              __syncthreads();
+            }
+            if (tid == 0) {
+              a.accept_len[b] = k - 1;
+              if (found >= 0) {
+                a.out_tokens[(size_t)b * (g + 1) + k - 1] = found;
+              } else {
+                FallbackInfo f;
+                f.j = k;
+                f.prev = prev;
+                f.phase_row = k - k0;
+                f.M = (double)M;
+                f.Z = Z;
+                f.pdx = pdx;
+                f.lx = lx;
+                w.fb[b] = f;
+                const int pos = atomicAdd(&w.counts[0], 1);
+                w.fb_list[pos] = b;
+              }
+            }
+          }
         }
       }
       __syncthreads();
+      if (!accepted) break;  // rejection, or the bonus token: the request is finished
+      if (k == k1) {         // accepted the last position of this phase: alive in the next one
+        if (tid == 0) {
+          const int pos = atomicAdd(&w.counts[ph + 1], 1);
+          w.lists[(size_t)(ph + 1) * a.B + pos] = b;
+        }
+      }
     }
   }
 }
@@ -662,7 +841,7 @@ __global__ __launch_bounds__(kVThreads) void residual_select_kernel(VerifyArgs a
     } else {
       // No residual mass (possible only through rounding): draw from p_t.
       DecideCtx c;
-      c.P = w.tpart + (size_t)b * ntv;
+      c.P = w.tpart + ((size_t)b * kRowsPerPhase + f.phase_row) * ntv;
       c.trow = a.target + ((size_t)b * (g + 1) + (f.j - 1)) * (size_t)a.V;
       c.M = (float)f.M;
       c.cf = (double)cf_f;
@@ -692,26 +871,42 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   const int dgrid = a.B < 2048 ? a.B : 2048;
-  for (int k = 1; k <= a.gamma + 1; ++k) {
+  const int nph = (a.gamma + 1 + kRowsPerPhase - 1) / kRowsPerPhase;
+  for (int ph = 1; ph <= nph; ++ph) {
+    const int k0 = kRowsPerPhase * (ph - 1) + 1;
     TStatsArgs t = {};
     t.target = a.target;
-    t.list = w.lists + (size_t)k * a.B;
-    t.count = w.counts + k;
-    t.kk0 = k - 1;
+    t.list = w.lists + (size_t)ph * a.B;
+    t.count = w.counts + ph;
+    t.kk0 = k0 - 1;
+    t.rows_per_req = min(kRowsPerPhase, a.gamma + 2 - k0);
+    t.orow_stride = kRowsPerPhase;
     t.gamma = a.gamma;
     t.V = a.V;
     t.ntv = ntv;
     t.cf = cf;
     t.tpart = w.tpart;
-    e = launch_target_stats(t, greedy, a.B, s);
+    e = launch_target_stats(t, greedy, a.B * t.rows_per_req, s);
     if (e != hipSuccess) return e;
     ProfScope prof(s, kProfVerifyDecide);
-    if (greedy) {
-      hipLaunchKernelGGL((verify_decide_kernel<true, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, k, cf, ntv);
+    if (ntv <= kPrefixMax) {
+      if (greedy) {
+        hipLaunchKernelGGL((verify_decide_kernel<true, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, cf, ntv);
+      } else if (bf16) {
+        hipLaunchKernelGGL((verify_decide_kernel<false, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, cf, ntv);
+      } else {
+        hipLaunchKernelGGL((verify_decide_kernel<false, false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, cf,
+                           ntv);
+      }
+    } else if (greedy) {
+      hipLaunchKernelGGL((verify_decide_generic_kernel<true, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, cf,
+                         ntv);
     } else if (bf16) {
-      hipLaunchKernelGGL((verify_decide_kernel<false, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, k, cf, ntv);
+      hipLaunchKernelGGL((verify_decide_generic_kernel<false, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph,
+                         cf, ntv);
     } else {
-      hipLaunchKernelGGL((verify_decide_kernel<false, false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, k, cf, ntv);
+      hipLaunchKernelGGL((verify_decide_generic_kernel<false, false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph,
+                         cf, ntv);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -121,6 +121,9 @@ SMALL = [
     # path, the ragged last tile and the 2-row tail group the general one
     ("v151936_b32", dict(V=4100, B=130, gamma=3)),
     ("greedy_v151936_b512", dict(V=2052, B=131, gamma=3)),
+    # more than 1024 target tiles per row: the decision kernel's general path
+    ("v151936_b32", dict(V=1048580, B=2, gamma=2, r=16)),
+    ("greedy_v151936_b512", dict(V=1048580, B=3, gamma=2, r=16)),
 ]
 
 
