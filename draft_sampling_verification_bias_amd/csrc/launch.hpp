@@ -42,6 +42,8 @@ struct TileArgs {
   int nrows, kper, k0;
   int B, gamma, V, r, ntiles;
   int rows_per_group, ngroups;  // set by launch_tile_pass
+  int row_begin, row_end;       // rows and tiles covered by one launch (set by launch_tile_pass)
+  int tile_begin, tile_count;
   float cf;             // log2(e) / T; unused at T == 0
 };
 

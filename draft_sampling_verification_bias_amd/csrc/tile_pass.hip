@@ -193,7 +193,9 @@ __device__ __forceinline__ bool block_tile(const TileArgs& a, int& tile, int& gr
     tile = (slot / a.ngroups) * 8 + (b % 8);
     group = slot % a.ngroups;
   }
-  return tile < a.ntiles;
+  const bool ok = tile < a.tile_count;
+  tile += a.tile_begin;
+  return ok;
 }
 
 // ---------------------------------------------------------------------------
@@ -210,119 +212,140 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// The W2 tile of the fast path lives in LDS row-major, one 256-byte row per
+// k, its sixteen 16-byte chunks permuted by an XOR of the row: chunk c of row k
+// sits in slot c ^ (4 (k mod 4)).  The permutation lets the transposing LDS
+// reads below hit distinct banks; the DMA copy applies it on the global side.
+__device__ __forceinline__ int w2_slot(int row, int chunk) { return chunk ^ (4 * (row & 3)); }
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int kMode>
-__device__ __forceinline__ void tile_fast(const TileArgs& a, int tile, int group, uint16_t* sW) {
-  constexpr int kPitch = kFastR + 8;
-  constexpr int kItems = (kFastR / 8) * (kTileCols / 4) / kTileThreads;  // 4
+__device__ __forceinline__ void tile_fast(const TileArgs& a, int tile, int row0, unsigned char* smem) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int n = lane & 31;
+  const int n = lane & 31, hh = lane >> 5;
   const int v0 = tile * kTileCols;
-  const int c4 = v0 + 4 * n;
-  const int R0 = group * kRowsPerGroup + wave * 32;
   const size_t V = (size_t)a.V;
-
-  // Previous token of the lane's A row.
-  const int arow = R0 + n;
-  const int prev = prev_token(a, row_info(a, arow));
-  const bool ok = (unsigned)prev < (unsigned)a.V;
-
-  // Base-logit rows of the 16 accumulator registers: row R at U + R * rs + k0 * V.
-  const size_t rs = a.kper == 1 ? (size_t)a.gamma * V : V;
-  const float* ubase = a.U + (size_t)(R0 + 4 * (lane >> 5)) * rs + (a.kper == 1 ? (size_t)a.k0 * V : 0) + c4;
-  float4 u4[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    u4[i] = *reinterpret_cast<const float4*>(ubase + (size_t)(8 * (i >> 2) + (i & 3)) * rs);
-
-  // W2 tile: eight k rows x four columns per item, then one 16-byte LDS store per column.
   const uint16_t* W2 = reinterpret_cast<const uint16_t*>(a.W2);
-  uint2 p[kItems][8];
+
+  // 1. W2[0:256][v0:v0+128] into LDS by DMA: each wave copies 64 rows, four
+  //    rows (1 KB) per instruction, lane l writing 16 bytes at byte 16 l.
 #pragma unroll
-  for (int j = 0; j < kItems; ++j) {
-    const int it = j * kTileThreads + threadIdx.x;
-    const int q = it % (kTileCols / 4);
-    const int k8 = 8 * (it / (kTileCols / 4));
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) p[j][kk] = *reinterpret_cast<const uint2*>(W2 + (size_t)(k8 + kk) * V + v0 + 4 * q);
-  }
-#pragma unroll
-  for (int j = 0; j < kItems; ++j) {
-    const int it = j * kTileThreads + threadIdx.x;
-    const int q = it % (kTileCols / 4);
-    const int k8 = 8 * (it / (kTileCols / 4));
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const uint32_t sel = (nb & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t w[8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) w[kk] = nb < 2 ? p[j][kk].x : p[j][kk].y;
-      const uint4 v = make_uint4(perm(w[1], w[0], sel), perm(w[3], w[2], sel), perm(w[5], w[4], sel),
-                                 perm(w[7], w[6], sel));
-      *reinterpret_cast<uint4*>(sW + (size_t)(nb * 32 + q) * kPitch + k8) = v;
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int rbase = 64 * wave + 4 * i;
+    const int row = rbase + (lane >> 4);
+    const int chunk = w2_slot(row, lane & 15);  // the XOR permutation is its own inverse
+    __builtin_amdgcn_global_load_lds(W2 + (size_t)row * V + v0 + 8 * chunk,
+                                     (lds_void*)(smem + (size_t)rbase * 256), 16, 0, 0);
   }
 
-  // A operand fragments: row n of E = W1[prev], k-chunk lane / 32.
-  const int koff = 8 * (lane >> 5);
-  const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + koff;
-  bf16x8 av[16];
+  // 2. Base logits: lane (n, hh) owns request row R, columns v0 + 32 nb + 8 q + 4 hh + 0..3.
+  const int R = row0 + 32 * wave + n;
+  const size_t rs = a.kper == 1 ? (size_t)a.gamma * V : V;
+  const float* urow = a.U + (size_t)R * rs + (a.kper == 1 ? (size_t)a.k0 * V : 0) + v0 + 4 * hh;
+  float4 u[kNB][4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) av[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
+  for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[nb][q] = *reinterpret_cast<const float4*>(urow + 32 * nb + 8 * q);
+
+  // 3. B operand: row R of E = W1[prev], k-chunk hh of each 16-wide k step.
+  const int prev = prev_token(a, row_info(a, R));
+  const bool ok = (unsigned)prev < (unsigned)a.V;
+  const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
+  bf16x8 ev[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ev[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
   if (!ok) {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) av[j][q] = (__bf16)0.0f;
+      for (int e = 0; e < 8; ++e) ev[j][e] = (__bf16)0.0f;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the DMA writes are counted like loads
   __syncthreads();
 
+  // 4. bias^T = W2^T E^T: A operand W2^T[m][k] read with the transposing LDS
+  //    load (each 16-lane group reads a 4 k x 16 column block and every lane
+  //    receives 4 consecutive k of one column), two reads per 8 k.
   f32x16 acc[kNB];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[nb][i] = 0.0f;
-  const uint16_t* bcol = sW + (size_t)n * kPitch + koff;
+  const int trow = 8 * hh + ((lane & 15) >> 2);               // + 16 j + 4 h
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // + 32 nb
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(bcol + (size_t)nb * 32 * kPitch + j * 16);
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], bv, acc[nb], 0, 0, 0);
+      bf16x8 av;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 16 * j + 4 * h + trow;
+        const int col = 32 * nb + tcol;
+        const int addr = row * 256 + w2_slot(row, col >> 3) * 16 + (col & 7) * 2;
+        const bf16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(smem + addr));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[4 * h + e] = t[e];
+      }
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[j], acc[nb], 0, 0, 0);
     }
   }
 
-  float ra[16], rb2[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float x0 = acc[0][i] + u4[i].x, x1 = acc[1][i] + u4[i].y;
-    const float x2 = acc[2][i] + u4[i].z, x3 = acc[3][i] + u4[i].w;
-    if constexpr (kMode == kModeSample) {
-      const float m = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
-      const float mc = m * a.cf;
-      float sum = fast_exp2(fmaf(x0, a.cf, -mc)) + fast_exp2(fmaf(x1, a.cf, -mc)) +
-                  (fast_exp2(fmaf(x2, a.cf, -mc)) + fast_exp2(fmaf(x3, a.cf, -mc)));
-      ra[i] = m;
-      rb2[i] = m == -__builtin_inff() ? 0.0f : sum;
-    } else {
-      float bv = x0;
-      int bi = c4;
-      if (x1 > bv) { bv = x1; bi = c4 + 1; }
-      if (x2 > bv) { bv = x2; bi = c4 + 2; }
-      if (x3 > bv) { bv = x3; bi = c4 + 3; }
-      ra[i] = bv;
-      rb2[i] = __int_as_float(bi);
-    }
-  }
+  // 5. Epilogue: register i of block nb is column v0 + 32 nb + 8 (i / 4) + 4 hh
+  //    + i % 4 of row R; the row's tile summary is an in-lane reduction over 64
+  //    values and one merge with the partner lane (lane ^ 32).
+  const int cbase = v0 + 4 * hh;
   if constexpr (kMode == kModeSample) {
-    transpose_reduce(ra, rb2, lane, MergeMS{a.cf});
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[nb][i] + comp(u[nb][i >> 2], i & 3));
+    const float mc = m * a.cf;
+    float sum = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(acc[nb][i] + comp(u[nb][i >> 2], i & 3), a.cf, -mc));
+    if (m == -__builtin_inff()) sum = 0.0f;
+    const float om = __shfl_xor(m, 32), os = __shfl_xor(sum, 32);
+    MergeMS{a.cf}(m, sum, om, os);
+    if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(m, sum);
   } else {
-    transpose_reduce(ra, rb2, lane, MergeArgmax{});
+    float bv = -__builtin_inff();
+    int bpos = 0;
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = acc[nb][i] + comp(u[nb][i >> 2], i & 3);
+        if (x > bv) {  // columns visited in ascending order: the lowest index wins ties
+          bv = x;
+          bpos = nb * 16 + i;
+        }
+      }
+    int bi = cbase + 32 * (bpos >> 4) + 8 * ((bpos >> 2) & 3) + (bpos & 3);
+    const float ov = __shfl_xor(bv, 32);
+    const int oi = __shfl_xor(bi, 32);
+    argmax_merge(bv, bi, ov, oi);
+    if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(bv, __int_as_float(bi));
   }
-  if ((lane & 1) == 0) {
-    const int R = R0 + acc_row((lane & 31) >> 1, lane);
-    a.partials[(size_t)R * a.ntiles + tile] = make_float2(ra[0], rb2[0]);
-  }
+}
+
+// The fast path as its own kernel (own register allocation): full tiles of
+// full 128-row groups, one (tile, group) per workgroup, groups of a tile on
+// the same XCD.
+template <int kMode>
+__global__ __launch_bounds__(kTileThreads, 2) void tile_fast_kernel(TileArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int tile, group;
+  if (!block_tile(a, tile, group)) return;
+  tile_fast<kMode>(a, tile, group * kRowsPerGroup, smem);
 }
 
 template <int kMode, bool kBf16>
@@ -330,14 +353,6 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
   extern __shared__ __align__(16) unsigned char smem[];
   int tile, group;
   if (!block_tile(a, tile, group)) return;
-  if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
-    const bool fast = a.r == kFastR && (a.V & 3) == 0 && (tile + 1) * kTileCols <= a.V &&
-                      (group + 1) * kRowsPerGroup <= a.nrows && (a.kper == 1 || a.kper == a.gamma);
-    if (fast) {
-      tile_fast<kMode>(a, tile, group, reinterpret_cast<uint16_t*>(smem));
-      return;
-    }
-  }
   const int v0 = tile * kTileCols;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -347,8 +362,8 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
   const bool full = (v0 + kTileCols <= a.V) && ((a.V & 3) == 0);
   uint16_t* sW = reinterpret_cast<uint16_t*>(smem);
 
-  const int row0 = group * a.rows_per_group;
-  const int row1 = min(a.nrows, row0 + a.rows_per_group);
+  const int row0 = a.row_begin + group * a.rows_per_group;
+  const int row1 = min(a.row_end, row0 + a.rows_per_group);
   const int nrb = (row1 - row0 + 31) / 32;
   const int ksteps = a.r / 16;
 
@@ -524,15 +539,50 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
   }
 }
 
+// Rows [row_begin, row_end) x tiles [tile_begin, tile_begin + tile_count) with
+// the one-tile-per-workgroup kernel.
 template <int kMode, bool kBf16>
-static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
+static void launch_tiles(const TileArgs& a, int row_begin, int row_end, int tile_begin, int tile_count,
+                         hipStream_t s) {
+  if (row_end <= row_begin || tile_count <= 0) return;
   const size_t lds = kBf16 ? (size_t)kTileCols * (a.r + 8) * sizeof(uint16_t) : 0;
-  ProfScope prof(s, kProfTileSample + kMode);
   TileArgs g = a;
   g.rows_per_group = kRowsPerGroup;
-  g.ngroups = (a.nrows + kRowsPerGroup - 1) / kRowsPerGroup;
-  const int blocks = g.ngroups == 1 ? a.ntiles : ((a.ntiles + 7) / 8) * 8 * g.ngroups;
+  g.ngroups = (row_end - row_begin + kRowsPerGroup - 1) / kRowsPerGroup;
+  g.row_begin = row_begin;
+  g.row_end = row_end;
+  g.tile_begin = tile_begin;
+  g.tile_count = tile_count;
+  const int blocks = g.ngroups == 1 ? tile_count : ((tile_count + 7) / 8) * 8 * g.ngroups;
   hipLaunchKernelGGL((tile_pass_kernel<kMode, kBf16>), dim3(blocks), dim3(kTileThreads), lds, s, g);
+}
+
+template <int kMode, bool kBf16>
+static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
+  ProfScope prof(s, kProfTileSample + kMode);
+  const int full_groups = a.nrows / kRowsPerGroup;
+  const int full_tiles = (a.V & 3) == 0 ? a.V / kTileCols : 0;
+  const bool fast = kBf16 && (kMode == kModeSample || kMode == kModeGreedy) && a.r == kFastR &&
+                    (a.kper == 1 || a.kper == a.gamma) && full_groups > 0 && full_tiles > 0;
+  if (!fast) {
+    launch_tiles<kMode, kBf16>(a, 0, a.nrows, 0, a.ntiles, s);
+    return hipGetLastError();
+  }
+  if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
+    TileArgs g = a;
+    g.ngroups = full_groups;
+    g.rows_per_group = kRowsPerGroup;
+    g.row_begin = 0;
+    g.row_end = full_groups * kRowsPerGroup;
+    g.tile_begin = 0;
+    g.tile_count = full_tiles;
+    const int blocks = full_groups == 1 ? full_tiles : ((full_tiles + 7) / 8) * 8 * full_groups;
+    const size_t lds = (size_t)kFastR * kTileCols * sizeof(uint16_t);
+    hipLaunchKernelGGL((tile_fast_kernel<kMode>), dim3(blocks), dim3(kTileThreads), lds, s, g);
+  }
+  // Remainders: rows past the full groups (all tiles), the partial last tile.
+  launch_tiles<kMode, kBf16>(a, full_groups * kRowsPerGroup, a.nrows, 0, a.ntiles, s);
+  launch_tiles<kMode, kBf16>(a, 0, full_groups * kRowsPerGroup, full_tiles, a.ntiles - full_tiles, s);
   return hipGetLastError();
 }
 
