@@ -199,60 +199,114 @@ __device__ __forceinline__ bool block_tile(const TileArgs& a, int& tile, int& gr
 }
 
 // ---------------------------------------------------------------------------
-// Fast path of the sample and argmax modes: bf16 weights, r = 256, a full
-// 128-column tile of a vocabulary whose size is a multiple of 4, a full
-// 128-row group, and base-logit rows at a constant stride (one block position
-// of every request, or all positions of consecutive requests).  No guards, no
-// per-row index arithmetic beyond one base pointer and a constant stride.
+// Fast path of the sample and argmax modes: bf16 weights, r = 256, full
+// 128-column tiles of a vocabulary whose size is a multiple of 4, full 128-row
+// groups, and base-logit rows at a constant stride (one block position of
+// every request, or all positions of consecutive requests).
+//
+// A workgroup owns one 128-row group and a contiguous range of tiles, walked
+// as 64-column halves: while the MFMA and the epilogue of one half run, the
+// W2 block of the next half is on its way into the other LDS buffer (global
+// -> LDS DMA) and its U block into a second register set, so every workgroup
+// keeps loads in flight instead of alternating between loading and computing.
+// The W1 rows (the B operand) are loaded once per workgroup.
+//
+// LDS: two 256 x 64 bf16 buffers (32 KB each), rows of 128 bytes whose 16-byte
+// chunks are permuted by an XOR with 4 ((k / 2) mod 2), which keeps the four
+// rows of a transposing read on disjoint banks.
 // ---------------------------------------------------------------------------
 constexpr int kFastR = 256;
-
-// Pack the 16-bit halves selected by `sel` of two words: v_perm_b32.
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// The W2 tile of the fast path lives in LDS row-major, one 256-byte row per
-// k, its sixteen 16-byte chunks permuted by an XOR of the row: chunk c of row k
-// sits in slot c ^ (4 (k mod 4)).  The permutation lets the transposing LDS
-// reads below hit distinct banks; the DMA copy applies it on the global side.
-__device__ __forceinline__ int w2_slot(int row, int chunk) { return chunk ^ (4 * (row & 3)); }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+constexpr int kHalfCols = 64;
+constexpr int kHalfBytes = kFastR * kHalfCols * 2;  // 32 KB
+
+__device__ __forceinline__ int w2h_slot(int row, int chunk) { return chunk ^ (4 * ((row >> 1) & 1)); }
+
+// One 16-byte global -> LDS DMA per lane: lane l writes LDS bytes
+// [dst + 16 l, dst + 16 l + 16) (dst wave-uniform, passed in M0).  Issued as
+// a statement the compiler does not model, so it adds no wait of its own for
+// the LDS destination: the caller orders the copy before the LDS reads with
+// wait_vmem and a barrier.  The source is a wave-uniform base plus a per-lane
+// byte offset below 2^32.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, unsigned char* dst) {
+  const unsigned lds = (unsigned)(unsigned long)((lds_void*)dst);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// vmcnt-only wait (expcnt, lgkmcnt left at their maxima); n <= 63.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Block -> (row group, column slice).  With the workgroup count a multiple of
+// 8, consecutive indices are placed on one XCD (workgroups are dealt to the
+// 8 XCDs round robin), so the row groups of a slice share that XCD's L2 copy
+// of the W2 blocks.
+__device__ __forceinline__ void pipe_block(int ngroups, int nslices, int& group, int& slice) {
+  const int total = ngroups * nslices;
+  const int b = blockIdx.x;
+  const int idx = (total & 7) == 0 ? (b & 7) * (total >> 3) + (b >> 3) : b;
+  group = idx % ngroups;
+  slice = idx / ngroups;
+}
+
 template <int kMode>
-__device__ __forceinline__ void tile_fast(const TileArgs& a, int tile, int row0, unsigned char* smem) {
+__global__ __launch_bounds__(kTileThreads, 2) void tile_pipe_kernel(TileArgs a, int nslices) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int group, slice;
+  pipe_block(a.ngroups, nslices, group, slice);
+  const int t_begin = a.tile_begin + (int)((long long)slice * a.tile_count / nslices);
+  const int t_end = a.tile_begin + (int)((long long)(slice + 1) * a.tile_count / nslices);
+  if (t_begin >= t_end) return;
+
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int n = lane & 31, hh = lane >> 5;
-  const int v0 = tile * kTileCols;
   const size_t V = (size_t)a.V;
   const uint16_t* W2 = reinterpret_cast<const uint16_t*>(a.W2);
+  unsigned char* buf0 = smem;
+  unsigned char* buf1 = smem + kHalfBytes;
 
-  // 1. W2[0:256][v0:v0+128] into LDS by DMA: each wave copies 64 rows, four
-  //    rows (1 KB) per instruction, lane l writing 16 bytes at byte 16 l.
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int rbase = 64 * wave + 4 * i;
-    const int row = rbase + (lane >> 4);
-    const int chunk = w2_slot(row, lane & 15);  // the XOR permutation is its own inverse
-    __builtin_amdgcn_global_load_lds(W2 + (size_t)row * V + v0 + 8 * chunk,
-                                     (lds_void*)(smem + (size_t)rbase * 256), 16, 0, 0);
-  }
-
-  // 2. Base logits: lane (n, hh) owns request row R, columns v0 + 32 nb + 8 q + 4 hh + 0..3.
-  const int R = row0 + 32 * wave + n;
+  // Lane (n, hh) owns request row R; in a half starting at column c it holds
+  // columns c + 32 nb + 8 q + 4 hh + 0..3 (nb = 0, 1; q = 0..3).
+  const int R = group * kRowsPerGroup + 32 * wave + n;
   const size_t rs = a.kper == 1 ? (size_t)a.gamma * V : V;
-  const float* urow = a.U + (size_t)R * rs + (a.kper == 1 ? (size_t)a.k0 * V : 0) + v0 + 4 * hh;
-  float4 u[kNB][4];
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) u[nb][q] = *reinterpret_cast<const float4*>(urow + 32 * nb + 8 * q);
+  const float* urow = a.U + (size_t)R * rs + (a.kper == 1 ? (size_t)a.k0 * V : 0) + 4 * hh;
 
-  // 3. B operand: row R of E = W1[prev], k-chunk hh of each 16-wide k step.
+  // Byte offset of this lane's 16-byte W2 chunk in the first DMA of a half:
+  // row 64 wave + l / 8 (8 rows per instruction), slot l % 8 of the permuted
+  // row (the XOR permutation is its own inverse and is the same for the rows
+  // 8 i + l / 8 of every instruction i).
+  const int w2row = 64 * wave + (lane >> 3);
+  const uint32_t w2off = ((uint32_t)w2row * (uint32_t)V + 8u * (uint32_t)w2h_slot(w2row, lane & 7)) * 2u;
+
+  // The lane's U values of the half, then W2[0:256][c:c+64] -> buf by DMA
+  // (each wave 64 rows, 8 rows per instruction): 16 vector memory
+  // instructions per wave, in this order (the DMA statements are volatile and
+  // clobber memory, so the loads cannot be moved past them).
+  auto issue = [&](int c, unsigned char* buf, float4 (&u)[2][4]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[nb][q] = *reinterpret_cast<const float4*>(urow + c + 32 * nb + 8 * q);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rbase = 64 * wave + 8 * i;
+      dma16(W2 + c, w2off + (uint32_t)(i * 16) * (uint32_t)V, buf + (size_t)rbase * 128);
+    }
+  };
+
+  float4 uA[2][4], uB[2][4];
+  issue(t_begin * kTileCols, buf0, uA);
+
+  // B operand: row R of E = W1[prev], k-chunk hh of each 16-wide k step.
   const int prev = prev_token(a, row_info(a, R));
   const bool ok = (unsigned)prev < (unsigned)a.V;
   const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
@@ -265,87 +319,133 @@ __device__ __forceinline__ void tile_fast(const TileArgs& a, int tile, int row0,
 #pragma unroll
       for (int e = 0; e < 8; ++e) ev[j][e] = (__bf16)0.0f;
   }
-  __builtin_amdgcn_s_waitcnt(0);  // the DMA writes are counted like loads
-  __syncthreads();
 
-  // 4. bias^T = W2^T E^T: A operand W2^T[m][k] read with the transposing LDS
-  //    load (each 16-lane group reads a 4 k x 16 column block and every lane
-  //    receives 4 consecutive k of one column), two reads per 8 k.
-  f32x16 acc[kNB];
+  const int trow = 8 * hh + ((lane & 15) >> 2);             // + 16 j + 4 h
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 nb
+  // bias^T of one half (A = W2^T by transposing LDS reads, B = E^T), plus U.
+  auto logits = [&](const unsigned char* buf, const float4 (&u)[2][4], float (&x)[2][16]) {
+    f32x16 acc[2];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[nb][i] = 0.0f;
-  const int trow = 8 * hh + ((lane & 15) >> 2);               // + 16 j + 4 h
-  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // + 32 nb
+      for (int i = 0; i < 16; ++i) acc[nb][i] = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 16; ++j) {
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      bf16x8 av;
+      for (int nb = 0; nb < 2; ++nb) {
+        bf16x8 av;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 16 * j + 4 * h + trow;
-        const int col = 32 * nb + tcol;
-        const int addr = row * 256 + w2_slot(row, col >> 3) * 16 + (col & 7) * 2;
-        const bf16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(smem + addr));
+        for (int h = 0; h < 2; ++h) {
+          const int row = 16 * j + 4 * h + trow;
+          const int col = 32 * nb + tcol;
+          const int addr = row * 128 + w2h_slot(row, col >> 3) * 16 + (col & 7) * 2;
+          const bf16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + addr));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) av[4 * h + e] = t[e];
+          for (int e = 0; e < 4; ++e) av[4 * h + e] = t[e];
+        }
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[j], acc[nb], 0, 0, 0);
       }
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[j], acc[nb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[nb][i] = acc[nb][i] + comp(u[nb][i >> 2], i & 3);
+  };
+
+  // Per half: wait for its loads (issued one half earlier) and for every wave
+  // to be done with the other buffer, then issue the next half's loads into
+  // the other buffer and register set, then compute.  After the full wait the
+  // compiler knows the half's U registers are complete and adds no waits of
+  // its own that would also cover the loads in flight.
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    const int c0 = tile * kTileCols;
+    float x[2][16];
+    float m0, s0, bv0;
+    int bp0;
+
+    // first half (buf0, uA)
+    __builtin_amdgcn_sched_barrier(0);  // keep the previous half's work before the wait
+    wait_vmem<0>();
+    __syncthreads();
+    issue(c0 + kHalfCols, buf1, uB);
+    logits(buf0, uA, x);
+    if constexpr (kMode == kModeSample) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, x[nb][i]);
+      const float mc = m * a.cf;
+      float sum = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(x[nb][i], a.cf, -mc));
+      m0 = m;
+      s0 = m == -__builtin_inff() ? 0.0f : sum;
+      asm volatile("" : "+v"(m0), "+v"(s0));  // finish this half's epilogue here, not in the next half
+    } else {
+      float bv = -__builtin_inff();
+      int bpos = 0;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (x[nb][i] > bv) {  // ascending columns: the lowest index wins ties
+            bv = x[nb][i];
+            bpos = nb * 16 + i;
+          }
+      bv0 = bv;
+      bp0 = bpos;
+      asm volatile("" : "+v"(bv0), "+v"(bp0));
+    }
+
+    // second half (buf1, uB)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem<0>();
+    __syncthreads();
+    if (tile + 1 < t_end) issue(c0 + kTileCols, buf0, uA);
+    logits(buf1, uB, x);
+    if constexpr (kMode == kModeSample) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, x[nb][i]);
+      const float mc = m * a.cf;
+      float sum = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(x[nb][i], a.cf, -mc));
+      if (m == -__builtin_inff()) sum = 0.0f;
+      const MergeMS merge{a.cf};
+      merge(m, sum, m0, s0);
+      const float om = __shfl_xor(m, 32), os = __shfl_xor(sum, 32);
+      merge(m, sum, om, os);
+      if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(m, sum);
+    } else {
+      float bv = -__builtin_inff();
+      int bpos = 0;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (x[nb][i] > bv) {
+            bv = x[nb][i];
+            bpos = nb * 16 + i;
+          }
+      const int cb = c0 + 4 * hh;
+      int b0 = cb + 32 * (bp0 >> 4) + 8 * ((bp0 >> 2) & 3) + (bp0 & 3);
+      const int b1 = cb + kHalfCols + 32 * (bpos >> 4) + 8 * ((bpos >> 2) & 3) + (bpos & 3);
+      float bvm = bv0;
+      argmax_merge(bvm, b0, bv, b1);
+      const float ov = __shfl_xor(bvm, 32);
+      const int oi = __shfl_xor(b0, 32);
+      argmax_merge(bvm, b0, ov, oi);
+      if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(bvm, __int_as_float(b0));
     }
   }
-
-  // 5. Epilogue: register i of block nb is column v0 + 32 nb + 8 (i / 4) + 4 hh
-  //    + i % 4 of row R; the row's tile summary is an in-lane reduction over 64
-  //    values and one merge with the partner lane (lane ^ 32).
-  const int cbase = v0 + 4 * hh;
-  if constexpr (kMode == kModeSample) {
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[nb][i] + comp(u[nb][i >> 2], i & 3));
-    const float mc = m * a.cf;
-    float sum = 0.0f;
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(acc[nb][i] + comp(u[nb][i >> 2], i & 3), a.cf, -mc));
-    if (m == -__builtin_inff()) sum = 0.0f;
-    const float om = __shfl_xor(m, 32), os = __shfl_xor(sum, 32);
-    MergeMS{a.cf}(m, sum, om, os);
-    if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(m, sum);
-  } else {
-    float bv = -__builtin_inff();
-    int bpos = 0;
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = acc[nb][i] + comp(u[nb][i >> 2], i & 3);
-        if (x > bv) {  // columns visited in ascending order: the lowest index wins ties
-          bv = x;
-          bpos = nb * 16 + i;
-        }
-      }
-    int bi = cbase + 32 * (bpos >> 4) + 8 * ((bpos >> 2) & 3) + (bpos & 3);
-    const float ov = __shfl_xor(bv, 32);
-    const int oi = __shfl_xor(bi, 32);
-    argmax_merge(bv, bi, ov, oi);
-    if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(bv, __int_as_float(bi));
-  }
-}
-
-// The fast path as its own kernel (own register allocation): full tiles of
-// full 128-row groups, one (tile, group) per workgroup, groups of a tile on
-// the same XCD.
-template <int kMode>
-__global__ __launch_bounds__(kTileThreads, 2) void tile_fast_kernel(TileArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  int tile, group;
-  if (!block_tile(a, tile, group)) return;
-  tile_fast<kMode>(a, tile, group * kRowsPerGroup, smem);
 }
 
 template <int kMode, bool kBf16>
@@ -539,6 +639,19 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
   }
 }
 
+// Compute units of the current device (cached per device).
+static int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // Rows [row_begin, row_end) x tiles [tile_begin, tile_begin + tile_count) with
 // the one-tile-per-workgroup kernel.
 template <int kMode, bool kBf16>
@@ -562,8 +675,10 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
   ProfScope prof(s, kProfTileSample + kMode);
   const int full_groups = a.nrows / kRowsPerGroup;
   const int full_tiles = (a.V & 3) == 0 ? a.V / kTileCols : 0;
+  // (The pipelined kernel addresses W2 with 32-bit byte offsets: 2 r V < 2^32.)
   const bool fast = kBf16 && (kMode == kModeSample || kMode == kModeGreedy) && a.r == kFastR &&
-                    (a.kper == 1 || a.kper == a.gamma) && full_groups > 0 && full_tiles > 0;
+                    (a.kper == 1 || a.kper == a.gamma) && full_groups > 0 && full_tiles > 0 &&
+                    (size_t)2 * kFastR * (size_t)a.V < ((size_t)1 << 32);
   if (!fast) {
     launch_tiles<kMode, kBf16>(a, 0, a.nrows, 0, a.ntiles, s);
     return hipGetLastError();
@@ -576,9 +691,14 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
     g.row_end = full_groups * kRowsPerGroup;
     g.tile_begin = 0;
     g.tile_count = full_tiles;
-    const int blocks = full_groups == 1 ? full_tiles : ((full_tiles + 7) / 8) * 8 * full_groups;
-    const size_t lds = (size_t)kFastR * kTileCols * sizeof(uint16_t);
-    hipLaunchKernelGGL((tile_fast_kernel<kMode>), dim3(blocks), dim3(kTileThreads), lds, s, g);
+    // Two resident workgroups per CU (64 KB of LDS each); the column slices
+    // of every row group together fill them once.
+    int nslices = 2 * compute_units() / full_groups;
+    if (nslices >= 8) nslices &= ~7;
+    nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
+    const size_t lds = 2 * (size_t)kHalfBytes;
+    hipLaunchKernelGGL((tile_pipe_kernel<kMode>), dim3(full_groups * nslices), dim3(kTileThreads), lds, s, g,
+                       nslices);
   }
   // Remainders: rows past the full groups (all tiles), the partial last tile.
   launch_tiles<kMode, kBf16>(a, full_groups * kRowsPerGroup, a.nrows, 0, a.ntiles, s);
