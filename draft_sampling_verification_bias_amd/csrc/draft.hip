@@ -224,6 +224,210 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sampling select for rows of at most kWaveTiles tile summaries: the same draw
+// as draft_select_kernel with wave-level searches and one barrier.
+//
+// Every wave runs the tile search on its own (lane l owns the contiguous
+// summaries [l cs, l cs + cs)), so the search needs only cross-lane shuffles.
+// The rescan of the picked tile is split by k over the four waves: a lane
+// owns 8 columns and every fourth k of its wave's quarter, with all of its
+// W2 loads (and the W1 and U values it needs) issued together.  The quarters
+// meet in LDS and wave 0 draws the column.
+// ---------------------------------------------------------------------------
+constexpr int kWaveTiles = 2048;                 // up to V = 262144
+constexpr int kWavePer = kWaveTiles / kWave;      // summaries per lane (max)
+constexpr int kMaxRQuarter = 512 / 4;             // k per wave (r <= 512)
+
+template <bool kBf16>
+__global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectArgs a) {
+  __shared__ float sbias[4][kTileCols];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const size_t out = (size_t)b * a.gamma + (a.k - 1);
+  const int nt = a.ntiles;
+  const int cs = (nt + kWave - 1) / kWave;
+  const int t0 = min(nt, lane * cs);
+  const int t1 = min(nt, t0 + cs);
+  const float2* P = a.partials + (size_t)b * nt;
+
+  // batch 1: this lane's summaries (clamped indices, all loads in flight),
+  // the previous token, the key
+  float2 pr[kWavePer];
+#pragma unroll
+  for (int j = 0; j < kWavePer; ++j) {
+    const int t = t0 + j;
+    pr[j] = P[t < t1 ? t : (t1 > 0 ? t1 - 1 : 0)];
+  }
+  const int prev = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
+  const uint64_t seed = a.seeds[b];
+  if (prev < 0 || prev >= a.V) {  // invalid anchor or earlier position: propagate
+    if (threadIdx.x == 0) {
+      a.tokens[out] = -1;
+      a.prob[out] = __builtin_nanf("");
+      a.lse[out] = __builtin_nanf("");
+    }
+    return;
+  }
+
+  // row max, tile weights, their lane prefix, the picked tile
+  float lm = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kWavePer; ++j)
+    if (t0 + j < t1) lm = fmaxf(lm, pr[j].x);
+  const float M = wave_max(lm);
+  auto weight = [&](const float2& p) -> double {
+    return p.x == -__builtin_inff() ? 0.0 : (double)p.y * (double)fast_exp2((p.x - M) * a.cf);
+  };
+  double local = 0.0;
+#pragma unroll
+  for (int j = 0; j < kWavePer; ++j)
+    if (t0 + j < t1) local += weight(pr[j]);
+  const double incl = wave_inclusive_scan(local);
+  const double excl = incl - local;
+  const double total = __shfl(incl, kWave - 1);
+  const double u = unit_uniform(draw_block(seed, a.round, a.k, kStreamDraft, 0).w[0]);
+  const double q = u * total;
+  const unsigned long long cross = __ballot(local > 0.0 && incl > q);
+  const unsigned long long pos = __ballot(local > 0.0);
+  const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+  int ts = -1;
+  double base = 0.0;
+  float mt = 0.0f;
+  if (lane == owner) {
+    double cum = excl, lastbase = 0.0;
+    int lastpos = -1;
+    float lastm = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kWavePer; ++j) {
+      if (t0 + j < t1) {
+        const double w = weight(pr[j]);
+        if (w > 0.0) {
+          lastpos = t0 + j;
+          lastbase = cum;
+          lastm = pr[j].x;
+          if (ts < 0 && cum + w > q) {
+            ts = t0 + j;
+            base = cum;
+            mt = pr[j].x;
+          }
+        }
+        cum += w;
+      }
+    }
+    if (ts < 0) {
+      ts = lastpos < 0 ? 0 : lastpos;
+      base = lastpos < 0 ? 0.0 : lastbase;
+      mt = lastpos < 0 ? M : lastm;
+    }
+  }
+  ts = __shfl(ts, owner);
+  base = __shfl(base, owner);
+  mt = __shfl(mt, owner);
+
+  // batch 2: the wave's quarter of the bias of tile ts.  Lane (cg, kr) owns
+  // columns c .. c+7 and k = kq wave + kr + 4 i.
+  const int kq = a.r / 4;  // r % 16 == 0
+  const int nk = kq / 4;
+  const int cg = lane & 15, kr = lane >> 4;
+  const int c = ts * kTileCols + 8 * cg;
+  const size_t V = (size_t)a.V;
+  const float* urow = a.U + ((size_t)b * a.gamma + (a.k - 1)) * V;
+  const int uc = ts * kTileCols + 2 * lane;  // wave 0: columns uc, uc + 1
+  const float u0 = uc < a.V ? urow[uc] : 0.0f;
+  const float u1 = uc + 1 < a.V ? urow[uc + 1] : 0.0f;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  const bool vec = c + 8 <= a.V && (a.V & 7) == 0;
+  for (int i0 = 0; i0 < nk; i0 += 16) {
+    float e[16];
+    float w[16][8];
+    // clamped k: every load of the chunk is issued before the first use
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = w1_at<kBf16>(a.W1, (size_t)prev * a.r + wave * kq + kr + 4 * min(i0 + i, nk - 1));
+    if (kBf16 && vec) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int k = wave * kq + kr + 4 * min(i0 + i, nk - 1);
+        const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W2) + (size_t)k * V + c);
+        w[i][0] = __uint_as_float(p.x << 16);
+        w[i][1] = __uint_as_float(p.x & 0xffff0000u);
+        w[i][2] = __uint_as_float(p.y << 16);
+        w[i][3] = __uint_as_float(p.y & 0xffff0000u);
+        w[i][4] = __uint_as_float(p.z << 16);
+        w[i][5] = __uint_as_float(p.z & 0xffff0000u);
+        w[i][6] = __uint_as_float(p.w << 16);
+        w[i][7] = __uint_as_float(p.w & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int k = wave * kq + kr + 4 * min(i0 + i, nk - 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int cc = c + j < a.V ? c + j : a.V - 1;
+          const float v = w2_at<kBf16>(a.W2, (size_t)k * V + cc);
+          w[i][j] = c + j < a.V ? v : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float ei = i0 + i < nk ? e[i] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(ei, w[i][j], acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    acc[j] += __shfl_xor(acc[j], 16);
+    acc[j] += __shfl_xor(acc[j], 32);
+  }
+  if (kr == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sbias[wave][8 * cg + j] = acc[j];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  // wave 0: the two columns of each lane, the column draw within tile ts
+  const double cf = (double)a.cf;
+  const double scale = exp2((double)(mt - M) * cf);
+  float l2[2];
+  double term[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cc = 2 * lane + h;
+    const float bias = ((sbias[0][cc] + sbias[1][cc]) + sbias[2][cc]) + sbias[3][cc];
+    const float uv = h == 0 ? u0 : u1;
+    const float l = uc + h < a.V ? uv + bias : -__builtin_inff();
+    const float e = l == -__builtin_inff() ? 0.0f : fast_exp2((l - mt) * a.cf);
+    l2[h] = l;
+    term[h] = (double)e * scale;
+  }
+  const double loc2 = term[0] + term[1];
+  const double inc2 = wave_inclusive_scan(loc2);
+  const double exc2 = inc2 - loc2;
+  const double q2 = q - base;
+  const unsigned long long cross2 = __ballot(loc2 > 0.0 && inc2 > q2);
+  const unsigned long long pos2 = __ballot(loc2 > 0.0);
+  const int own2 = cross2 ? __ffsll((long long)cross2) - 1 : (pos2 ? 63 - __clzll((long long)pos2) : 0);
+  if (lane == own2) {
+    int h;
+    if (cross2) {
+      h = (term[0] > 0.0 && exc2 + term[0] > q2) ? 0 : 1;
+    } else {
+      h = term[1] > 0.0 ? 1 : 0;
+    }
+    const float l = l2[h];
+    a.tokens[out] = ts * kTileCols + 2 * lane + h;
+    a.prob[out] = (float)(exp2((double)(l - M) * cf) / total);
+    a.lse[out] = (float)((double)M * a.inv_t + log(total));
+  }
+}
+
 size_t draft_workspace(int B, int gamma, int V, int r) {
   (void)gamma;
   (void)r;
@@ -285,6 +489,14 @@ hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s) {
     sa.k = k;
     if (greedy) {
       e = bf16 ? launch_select<true, true>(sa, s) : launch_select<true, false>(sa, s);
+    } else if (ntiles <= kWaveTiles) {
+      ProfScope prof(s, kProfDraftSelect);
+      if (bf16) {
+        hipLaunchKernelGGL((draft_select_wave_kernel<true>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+      } else {
+        hipLaunchKernelGGL((draft_select_wave_kernel<false>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+      }
+      e = hipGetLastError();
     } else {
       e = bf16 ? launch_select<false, true>(sa, s) : launch_select<false, false>(sa, s);
     }
