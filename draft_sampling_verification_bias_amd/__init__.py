@@ -22,7 +22,7 @@ __all__ = [
 
 OP_DRAFT, OP_VERIFY, OP_SURVIVAL = 0, 1, 2
 _F32, _BF16 = 0, 1
-MAX_RESIDUAL_PROPOSALS = 16
+MAX_RESIDUAL_PROPOSALS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

@@ -12,7 +12,7 @@ namespace dspark {
 
 // Vocabulary columns per tile of the MFMA tile pass and of the target passes.
 constexpr int kTileCols = 128;
-constexpr int kTgtCols = 1024;
+constexpr int kTgtCols = 256;
 
 inline int tiles_of(int V, int cols) { return (V + cols - 1) / cols; }
 
@@ -113,7 +113,7 @@ hipError_t launch_survival(const SurvivalArgs& a, bool bf16, hipStream_t s);
 //     ...) of each listed request b; summaries of row j go to row
 //     b * orow_stride + j of tpart.
 //   all mode: row R = b * gamma + kk for kk < gamma; summaries go to row R.
-// Sample mode writes (max t, sum 2^((t - max) * cf)) per 1024-column tile;
+// Sample mode writes (max t, sum 2^((t - max) * cf)) per kTgtCols-column tile;
 // greedy mode (max t, argmax as int bits).
 struct TStatsArgs {
   const float* target;
@@ -126,6 +126,8 @@ struct TStatsArgs {
   int gamma, V, ntv;
   float cf;
   float2* tpart;
+  const int32_t* draft_tokens;  // with tx_out: the drafted tokens [B][gamma]
+  float* tx_out;                // list mode, optional: target logit of the drafted token per output row
 };
 
 hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, hipStream_t s);

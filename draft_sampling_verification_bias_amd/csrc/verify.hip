@@ -26,7 +26,6 @@ namespace dspark {
 
 constexpr int kVThreads = 256;
 constexpr int kRowsPerPhase = 2;   // block positions verified per phase
-constexpr int kColsPerThread = kTgtCols / kVThreads;  // 4
 
 struct FallbackInfo {
   int j;        // rejected position (1-based)
@@ -44,6 +43,7 @@ struct VerifyWs {
   int* fb_list;         // [B]
   FallbackInfo* fb;     // [B] indexed by request
   double* fb_part;      // [B][ntv] residual mass per tile
+  float* txv;           // [B][kRowsPerPhase] target logit of the drafted token, current phase
 };
 
 static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
@@ -61,6 +61,8 @@ static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
   w.fb = reinterpret_cast<FallbackInfo*>(p);
   p += align256((size_t)B * sizeof(FallbackInfo));
   w.fb_part = reinterpret_cast<double*>(p);  // [B][ceil(V / kResCols)]
+  p += align256((size_t)B * tiles_of(V, 256) * sizeof(double));
+  w.txv = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -69,7 +71,8 @@ size_t verify_workspace(int B, int gamma, int V, int r) {
   const int ntv = tiles_of(V, kTgtCols);
   return align256((size_t)B * kRowsPerPhase * ntv * sizeof(float2)) + align256((size_t)(gamma + 2) * B * sizeof(int)) +
          align256((size_t)(gamma + 2) * sizeof(int)) + align256((size_t)B * sizeof(int)) +
-         align256((size_t)B * sizeof(FallbackInfo)) + align256((size_t)B * tiles_of(V, 256) * sizeof(double));
+         align256((size_t)B * sizeof(FallbackInfo)) + align256((size_t)B * tiles_of(V, 256) * sizeof(double)) +
+         align256((size_t)B * kRowsPerPhase * sizeof(float));
 }
 
 template <bool kBf16>
@@ -89,21 +92,21 @@ __device__ __forceinline__ double wval(const void* W, size_t idx) {
 // Sample mode writes (max t, sum 2^((t - max) * cf)); greedy mode (max t,
 // argmax bits).
 // ---------------------------------------------------------------------------
-constexpr int kTilesPerItem = 4;
+constexpr int kStatWaveTiles = 4;                                   // tiles per wave per item
+constexpr int kStatItemTiles = kStatWaveTiles * (kVThreads / kWave);  // 16 tiles = 4096 columns
 
-// Each work item is kTilesPerItem consecutive 1024-column tiles of one row:
-// every thread issues its four 16-byte loads at once and the four tiles share
-// one set of block reductions.
+// Each work item is kStatItemTiles consecutive kTgtCols-column tiles of one
+// row; a wave owns kStatWaveTiles of them, a lane four consecutive columns of
+// each (one 16-byte load per tile, all issued together), and every reduction
+// is a wave reduction.  With tx_out set (list mode), the lane holding the
+// row's drafted token also stores its target logit.
 template <bool kGreedy>
 __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
-  constexpr int kWaves = kVThreads / kWave;
-  __shared__ float sv[kWaves][kTilesPerItem];
-  __shared__ float ss[kWaves][kTilesPerItem];
-  __shared__ int si[kWaves][kTilesPerItem];
   const int nrows = a.list ? *a.count * a.rows_per_req : a.nall;
-  const int ngrp = (a.ntv + kTilesPerItem - 1) / kTilesPerItem;
+  const int ngrp = (a.ntv + kStatItemTiles - 1) / kStatItemTiles;
   const long long items = (long long)nrows * ngrp;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const bool full_rows = (a.V & 3) == 0;
   for (long long it = blockIdx.x; it < items; it += gridDim.x) {
     const int li = (int)(it / ngrp);
     const int tg = (int)(it - (long long)li * ngrp);
@@ -119,86 +122,54 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
       orow = li;
     }
     const float* row = a.target + ((size_t)b * (a.gamma + 1) + kk) * (size_t)a.V;
-    float x[kTilesPerItem][kColsPerThread];
+    const int x = (a.tx_out && kk < a.gamma) ? a.draft_tokens[(size_t)b * a.gamma + kk] : -1;
+    const int tw = tg * kStatItemTiles + wave * kStatWaveTiles;  // first tile of this wave
+    float v[kStatWaveTiles][4];
 #pragma unroll
-    for (int j = 0; j < kTilesPerItem; ++j) {
-      const int c0 = (tg * kTilesPerItem + j) * kTgtCols + threadIdx.x * kColsPerThread;
-      if (c0 + kColsPerThread <= a.V && (a.V & 3) == 0) {
+    for (int j = 0; j < kStatWaveTiles; ++j) {
+      const int c0 = (tw + j) * kTgtCols + 4 * lane;
+      if (full_rows && c0 + 4 <= a.V) {
         const float4 q = *reinterpret_cast<const float4*>(row + c0);
-        x[j][0] = q.x; x[j][1] = q.y; x[j][2] = q.z; x[j][3] = q.w;
+        v[j][0] = q.x; v[j][1] = q.y; v[j][2] = q.z; v[j][3] = q.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < kColsPerThread; ++e) x[j][e] = c0 + e < a.V ? row[c0 + e] : -__builtin_inff();
+        for (int e = 0; e < 4; ++e) v[j][e] = c0 + e < a.V ? row[c0 + e] : -__builtin_inff();
       }
     }
-    if constexpr (kGreedy) {
-      float bv[kTilesPerItem];
-      int bi[kTilesPerItem];
 #pragma unroll
-      for (int j = 0; j < kTilesPerItem; ++j) {
-        const int c0 = (tg * kTilesPerItem + j) * kTgtCols + threadIdx.x * kColsPerThread;
-        bv[j] = x[j][0];
-        bi[j] = c0;
+    for (int j = 0; j < kStatWaveTiles; ++j) {
+      const int t = tw + j;
+      if (t >= a.ntv) break;  // uniform across the wave
+      const int c0 = t * kTgtCols + 4 * lane;
+      if ((unsigned)(x - c0) < 4u) a.tx_out[orow] = v[j][x - c0 == 0 ? 0 : x - c0 == 1 ? 1 : x - c0 == 2 ? 2 : 3];
+      if constexpr (kGreedy) {
+        float bv = v[j][0];
+        int bi = c0;
 #pragma unroll
-        for (int e = 1; e < kColsPerThread; ++e) {
-          if (x[j][e] > bv[j]) {
-            bv[j] = x[j][e];
-            bi[j] = c0 + e;
+        for (int e = 1; e < 4; ++e) {
+          if (v[j][e] > bv) {
+            bv = v[j][e];
+            bi = c0 + e;
           }
         }
-        wave_argmax(bv[j], bi[j]);
-        if (lane == 0) {
-          sv[wave][j] = bv[j];
-          si[wave][j] = bi[j];
-        }
-      }
-      __syncthreads();
-      if (threadIdx.x < kTilesPerItem) {
-        const int j = threadIdx.x, t = tg * kTilesPerItem + j;
-        float v = sv[0][j];
-        int i = si[0][j];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) argmax_merge(v, i, sv[w][j], si[w][j]);
-        if (t < a.ntv) a.tpart[(size_t)orow * a.ntv + t] = make_float2(v, __int_as_float(i));
-      }
-      __syncthreads();
-    } else {
-      float m[kTilesPerItem];
-#pragma unroll
-      for (int j = 0; j < kTilesPerItem; ++j) {
-        m[j] = wave_max(fmaxf(fmaxf(x[j][0], x[j][1]), fmaxf(x[j][2], x[j][3])));
-        if (lane == 0) sv[wave][j] = m[j];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kTilesPerItem; ++j) {
-        float M = sv[0][j];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sv[w][j]);
+        wave_argmax(bv, bi);
+        if (lane == 0) a.tpart[(size_t)orow * a.ntv + t] = make_float2(bv, __int_as_float(bi));
+      } else {
+        const float m = wave_max(fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3])));
         float sum = 0.0f;
-        if (M != -__builtin_inff()) {
+        if (m != -__builtin_inff()) {
 #pragma unroll
-          for (int e = 0; e < kColsPerThread; ++e) sum += fast_exp2((x[j][e] - M) * a.cf);
+          for (int e = 0; e < 4; ++e) sum += fast_exp2((v[j][e] - m) * a.cf);
         }
-        m[j] = M;
         sum = wave_sum(sum);
-        if (lane == 0) ss[wave][j] = sum;
+        if (lane == 0) a.tpart[(size_t)orow * a.ntv + t] = make_float2(m, sum);
       }
-      __syncthreads();
-      if (threadIdx.x < kTilesPerItem) {
-        const int j = threadIdx.x, t = tg * kTilesPerItem + j;
-        float S = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) S += ss[w][j];
-        if (t < a.ntv) a.tpart[(size_t)orow * a.ntv + t] = make_float2(m[j], S);
-      }
-      __syncthreads();
     }
   }
 }
 
 hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, hipStream_t s) {
-  const long long items = (long long)max_rows * ((a.ntv + kTilesPerItem - 1) / kTilesPerItem);
+  const long long items = (long long)max_rows * ((a.ntv + kStatItemTiles - 1) / kStatItemTiles);
   const int grid = (int)(items < 16384 ? items : 16384);
   if (grid <= 0) return hipSuccess;
   ProfScope prof(s, kProfTargetStats);
@@ -253,7 +224,7 @@ struct DecideCtx {
 };
 
 // Categorical draw from p_t with uniform u: tile search over the summaries,
-// then a rescan of one 1024-column tile.  `sterm` holds kTgtCols doubles.
+// then a rescan of one kTgtCols-column tile.  `sterm` holds kTgtCols doubles.
 __device__ int sample_target(const DecideCtx& c, double u, PickScratch& ps, double* sterm,
                              double* total_out) {
   auto tile_weight = [&](int t) -> double {
@@ -290,83 +261,9 @@ __device__ double draft_logit(const VerifyArgs& a, const float* urow, const doub
   return (double)urow[v] + s;
 }
 
+constexpr int kPrefixMax = 1024;  // target tiles per row on the fast decision path (V <= 262144)
+
 // ---------------------------------------------------------------------------
-// Wave-level draw from p_t for the fast path (at most kPrefixMax tiles): the
-// cumulative tile weights are in LDS (scum[t] = weight of tiles < t), so a draw
-// is a binary search plus a rescan of one 1024-column tile by one wave, 16
-// consecutive columns per lane.  Same rule as the block search: the first
-// column whose cumulative weight exceeds q; the last positive one if rounding
-// leaves none.
-// ---------------------------------------------------------------------------
-constexpr int kPrefixMax = 1024;
-
-__device__ int wave_sample_target(const DecideCtx& c, const double* scum, int last_pos_tile, double q) {
-  const int lane = threadIdx.x & (kWave - 1);
-  // first tile t with scum[t + 1] > q
-  int lo = 0, hi = c.ntv;  // answer in [0, ntv]; ntv means "none"
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (scum[mid + 1] > q) hi = mid; else lo = mid + 1;
-  }
-  const int ts = lo < c.ntv ? lo : last_pos_tile;
-  const double base = scum[ts];
-  const double ql = q - base;
-  const float mt = c.P[ts].x;
-  const double scale = exp2((double)(mt - c.M) * c.cf);
-  const float cff = (float)c.cf;
-  const int c0 = ts * kTgtCols + lane * 16;
-  float x[16];
-  if (c0 + 16 <= c.V && (c.V & 3) == 0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 v4 = *reinterpret_cast<const float4*>(c.trow + c0 + 4 * j);
-      x[4 * j] = v4.x; x[4 * j + 1] = v4.y; x[4 * j + 2] = v4.z; x[4 * j + 3] = v4.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = c0 + j < c.V ? c.trow[c0 + j] : -__builtin_inff();
-  }
-  double term[16];
-  double local = 0.0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float e = x[j] == -__builtin_inff() ? 0.0f : fast_exp2((x[j] - mt) * cff);
-    term[j] = (double)e * scale;
-    local += term[j];
-  }
-  const double incl = wave_inclusive_scan(local);
-  const double excl = incl - local;
-  const unsigned long long cross = __ballot(local > 0.0 && excl + local > ql);
-  const unsigned long long pos = __ballot(local > 0.0);
-  const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
-  int col = -1;
-  if (lane == owner) {
-    double cum = excl;
-    int lastp = -1;
-    for (int j = 0; j < 16; ++j) {
-      if (term[j] > 0.0) {
-        lastp = j;
-        if (col < 0 && cum + term[j] > ql) col = j;
-      }
-      cum += term[j];
-    }
-    if (col < 0) col = lastp < 0 ? 0 : lastp;
-    col += lane * 16;
-  }
-  col = __shfl(col, owner);
-  return ts * kTgtCols + col;
-}
-
-// W1[prev] . W2[:, v] + U[v] in float64, summed by one wave.
-template <bool kBf16>
-__device__ double wave_draft_logit(const VerifyArgs& a, const float* urow, const double* sw1, int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-  double s = 0.0;
-  for (int j = lane; j < a.r; j += kWave) s += sw1[j] * wval<kBf16>(a.W2, (size_t)j * a.V + v);
-  s = wave_sum(s);
-  return (double)urow[v] + s;
-}
-
 // Decision kernel for rows of more than kPrefixMax tiles: the same decisions
 // as verify_decide_kernel below, with block-wide searches over the tile
 // summaries in global memory.
@@ -493,240 +390,402 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
 }
 
 // ---------------------------------------------------------------------------
-// Decision kernel for rows of at most kPrefixMax tiles.  The loads are issued
-// in three dependent batches -- the request id; then everything that depends
-// only on the request (its tile summaries, drafted and previous tokens, p_d,
-// key); then everything that depends on those tokens (target logit, base
-// logit, W1 row, W2 column of the drafted token) -- so an accepted position
-// costs three memory round trips and a rejection two more per batch of four
-// residual proposals.
+// Decision kernel for rows of at most kPrefixMax target tiles: one workgroup
+// per listed request.  Every wave takes the same decisions from the same data
+// (no barrier on the acceptance path): one batch of loads brings the tile
+// summaries of the phase's rows, the drafted tokens, p_d(x) and the target
+// logits t(x) recorded by the statistics kernel; a second batch the draft
+// logits of the drafted tokens (needed only after a rejection, loaded
+// anyway).  A lane owns a contiguous share of the summaries, so the searches
+// over them are ballots and shuffles.  After a rejection the residual
+// proposals are evaluated 16 at a time -- four per wave, 16 lanes each --
+// and the waves agree on the lowest kept proposal through LDS.
 // ---------------------------------------------------------------------------
-constexpr int kTilesPerThreadFast = kPrefixMax / kVThreads;  // 4
+constexpr int kLaneTiles = kPrefixMax / kWave;                    // 16 summaries per lane
+constexpr int kPropBatch = 4 * (kVThreads / kWave);               // proposals per batch
+static_assert(DSPARK_MAX_RESIDUAL_PROPOSALS % kPropBatch == 0, "whole proposal batches");
 
-// W1[prev] . W2[:, v] + U[v] in float64, summed by one wave; the W2 loads of a
-// lane are issued together (clamped indices, zeroed terms).
-template <bool kBf16>
-__device__ double wave_draft_logit_batched(const VerifyArgs& a, const float* urow, const float* sw1, int v) {
+// Weight of a tile summary relative to the row maximum M (cf = log2(e) / T).
+__device__ __forceinline__ double tile_weight(const float2& p, float M, float cf) {
+  return p.x == -__builtin_inff() ? 0.0 : (double)p.y * (double)fast_exp2((p.x - M) * cf);
+}
+
+// The lane's share [t0, t1) of a row's tile summaries and the row's
+// normaliser: M = max, Z = sum of the tile weights, incl / excl = the
+// cumulative weight through / before this lane's share.
+struct RowScan {
+  float2 p[kLaneTiles];
+  int t0, t1;
+  float M;
+  double local, excl, incl, Z;
+};
+
+__device__ __forceinline__ void row_scan(RowScan& s, float cf) {
+  float lm = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kLaneTiles; ++j)
+    if (s.t0 + j < s.t1) lm = fmaxf(lm, s.p[j].x);
+  s.M = wave_max(lm);
+  double loc = 0.0;
+#pragma unroll
+  for (int j = 0; j < kLaneTiles; ++j)
+    if (s.t0 + j < s.t1) loc += tile_weight(s.p[j], s.M, cf);
+  s.local = loc;
+  s.incl = wave_inclusive_scan(loc);
+  s.excl = s.incl - loc;
+  s.Z = __shfl(s.incl, kWave - 1);
+}
+
+// Tile of the first cumulative weight above q (the last positive tile if
+// rounding leaves none), the cumulative weight before it and its maximum;
+// q is the same on every lane, the results are returned to every lane.
+__device__ __forceinline__ void tile_search(const RowScan& s, float cf, double q, int& ts, double& base,
+                                            float& mt) {
   const int lane = threadIdx.x & (kWave - 1);
-  float wv[512 / kWave];
+  const unsigned long long cross = __ballot(s.local > 0.0 && s.incl > q);
+  const unsigned long long pos = __ballot(s.local > 0.0);
+  const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+  int t = -1;
+  double bb = 0.0;
+  float m = s.M;
+  if (lane == owner) {
+    double cum = s.excl, lastbase = 0.0;
+    int lastpos = -1;
+    float lastm = s.M;
+#pragma unroll
+    for (int j = 0; j < kLaneTiles; ++j) {
+      if (s.t0 + j < s.t1) {
+        const double w = tile_weight(s.p[j], s.M, cf);
+        if (w > 0.0) {
+          lastpos = s.t0 + j;
+          lastbase = cum;
+          lastm = s.p[j].x;
+          if (t < 0 && cum + w > q) {
+            t = s.t0 + j;
+            bb = cum;
+            m = s.p[j].x;
+          }
+        }
+        cum += w;
+      }
+    }
+    if (t < 0) {
+      t = lastpos < 0 ? 0 : lastpos;
+      bb = lastpos < 0 ? 0.0 : lastbase;
+      m = lastm;
+    }
+  }
+  ts = __shfl(t, owner);
+  base = __shfl(bb, owner);
+  mt = __shfl(m, owner);
+}
+
+// Within each 16-lane group: the column of target tile ts (kTgtCols columns,
+// 16 per lane) whose cumulative weight first exceeds ql (the last positive
+// one if none), and its target logit.  ts, mt, ql may differ between groups.
+__device__ __forceinline__ void group_col_draw(const float* trow, int V, int ts, float mt, float M, float cf_f,
+                                               double cf, double ql, int& v_out, float& x_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int li = lane & 15, gbase = lane & ~15;
+  const int c0 = ts * kTgtCols + 16 * li;
+  float x[16];
+  if ((V & 3) == 0 && c0 + 16 <= V) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 q = *reinterpret_cast<const float4*>(trow + c0 + 4 * j);
+      x[4 * j] = q.x; x[4 * j + 1] = q.y; x[4 * j + 2] = q.z; x[4 * j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c = c0 + j < V ? c0 + j : V - 1;
+      const float v = trow[c];
+      x[j] = c0 + j < V ? v : -__builtin_inff();
+    }
+  }
+  const double scale = exp2((double)(mt - M) * cf);
+  float e[16];
+  double local = 0.0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    e[j] = x[j] == -__builtin_inff() ? 0.0f : fast_exp2((x[j] - mt) * cf_f);
+    local += (double)e[j] * scale;
+  }
+  double incl = local;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const double y = __shfl_up(incl, o);
+    if (li >= o) incl += y;
+  }
+  const double excl = incl - local;
+  const unsigned long long gmask = 0xffffull << gbase;
+  const unsigned long long cross = __ballot(local > 0.0 && incl > ql) & gmask;
+  const unsigned long long pos = __ballot(local > 0.0) & gmask;
+  const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : gbase);
+  int col = -1;
+  float xc = 0.0f;
+  if (lane == owner) {
+    double cum = excl;
+    int lastp = -1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const double t = (double)e[j] * scale;
+      if (t > 0.0) {
+        lastp = j;
+        if (col < 0 && cum + t > ql) col = j;
+      }
+      cum += t;
+    }
+    if (col < 0) col = lastp < 0 ? 0 : lastp;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j == col) xc = x[j];
+    col += c0;
+  }
+  v_out = __shfl(col, owner);
+  x_out = __shfl(xc, owner);
+}
+
+// Draft logit U[v] + W1[prev] . W2[:, v] in float64, summed by a 16-lane group
+// (lane li takes k = li + 16 m); v may differ between groups.
+template <bool kBf16>
+__device__ __forceinline__ double group_draft_logit(const VerifyArgs& a, const float* urow, int prev, int v) {
+  const int li = threadIdx.x & 15;
+  const int nm = a.r / 16;  // r % 16 == 0
   const float uv = urow[v];
+  double s = 0.0;
+  for (int m0 = 0; m0 < nm; m0 += 16) {
+    float e[16], wv[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int k = li + 16 * min(m0 + m, nm - 1);  // clamped: all loads issued before the first use
+      e[m] = (float)wval<kBf16>(a.W1, (size_t)prev * a.r + k);
+      wv[m] = (float)wval<kBf16>(a.W2, (size_t)k * a.V + v);
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      if (m0 + m < nm) s += (double)e[m] * (double)wv[m];
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+  return (double)uv + s;
+}
+
+// The same over a whole wave (lane l takes k = l + 64 m), for one v.
+template <bool kBf16>
+__device__ __forceinline__ double wave_draft_logit(const VerifyArgs& a, const float* urow, int prev, int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float uv = urow[v];
+  float e[512 / kWave], wv[512 / kWave];
 #pragma unroll
   for (int m = 0; m < 512 / kWave; ++m) {
-    const int j = lane + m * kWave;
-    wv[m] = (float)wval<kBf16>(a.W2, (size_t)(j < a.r ? j : 0) * a.V + v);
+    const int k = lane + m * kWave;
+    const int kc = k < a.r ? k : 0;
+    e[m] = (float)wval<kBf16>(a.W1, (size_t)prev * a.r + kc);
+    wv[m] = (float)wval<kBf16>(a.W2, (size_t)kc * a.V + v);
   }
   double s = 0.0;
 #pragma unroll
-  for (int m = 0; m < 512 / kWave; ++m) {
-    const int j = lane + m * kWave;
-    if (j < a.r) s += (double)sw1[j] * (double)wv[m];
-  }
-  s = wave_sum(s);
-  return (double)uv + s;
+  for (int m = 0; m < 512 / kWave; ++m)
+    if (lane + m * kWave < a.r) s += (double)e[m] * (double)wv[m];
+  return (double)uv + wave_sum(s);
 }
 
 template <bool kGreedy, bool kBf16>
 __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs w, int ph, float cf_f,
                                                                  int ntv) {
   constexpr int kWaves = kVThreads / kWave;
-  __shared__ PickScratch ps;
-  __shared__ double scum[kPrefixMax + 1];
-  __shared__ float sw1[512];
-  __shared__ double sred[kWaves];
-  __shared__ float sv[kWaves];
-  __shared__ int si[kWaves];
-  __shared__ int s_pass[kWaves], s_tok[kWaves], s_lastpos;
+  __shared__ int s_idx[kWaves], s_tok[kWaves];
   const int g = a.gamma;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-  const int k0 = 2 * ph - 1, k1 = min(2 * ph, g + 1);
-  const int count = w.counts[ph];
-  const double cf = (double)cf_f;
-  for (int li = blockIdx.x; li < count; li += gridDim.x) {
-    const int b = w.lists[(size_t)ph * a.B + li];
-    const uint64_t seed = kGreedy ? 0 : a.seeds[b];
-    for (int k = k0; k <= k1; ++k) {
-      const float2* P = w.tpart + ((size_t)b * kRowsPerPhase + (k - k0)) * ntv;
-      const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
-      // batch 1: the row's tile summaries and the tokens of position k
-      float2 pv[kTilesPerThreadFast];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int k0 = kRowsPerPhase * (ph - 1) + 1, k1 = min(k0 + kRowsPerPhase - 1, g + 1);
+  const int li = blockIdx.x;
+  if (li >= w.counts[ph]) return;
+  const int b = w.lists[(size_t)ph * a.B + li];
+  const int cs = (ntv + kWave - 1) / kWave;
+  const int t0 = min(ntv, lane * cs), t1 = min(ntv, t0 + cs);
+
+  // batch 1: summaries of the phase's rows, tokens, p_d(x), t(x), key
+  RowScan rs[kRowsPerPhase];
+  int xk[kRowsPerPhase], prevk[kRowsPerPhase];
+  float pdxk[kRowsPerPhase], txk[kRowsPerPhase];
 #pragma unroll
-      for (int j = 0; j < kTilesPerThreadFast; ++j) {
-        const int t = tid * kTilesPerThreadFast + j;
-        pv[j] = P[t < ntv ? t : ntv - 1];
-      }
-      int x = 0, prev = 0;
-      double pdx = 1.0;
+  for (int rr = 0; rr < kRowsPerPhase; ++rr) {
+    const float2* P = w.tpart + ((size_t)b * kRowsPerPhase + rr) * ntv;
+    rs[rr].t0 = t0;
+    rs[rr].t1 = t1;
+#pragma unroll
+    for (int j = 0; j < kLaneTiles; ++j) {
+      const int t = t0 + j;
+      rs[rr].p[j] = P[t < t1 ? t : (t1 > 0 ? t1 - 1 : 0)];
+    }
+    const int kc = min(k0 + rr, g);  // clamped position: loads stay in bounds
+    xk[rr] = a.draft_tokens[(size_t)b * g + kc - 1];
+    prevk[rr] = kc == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + kc - 2];
+    pdxk[rr] = kGreedy ? 1.0f : a.draft_prob[(size_t)b * g + kc - 1];
+    txk[rr] = kGreedy ? 0.0f : w.txv[(size_t)b * kRowsPerPhase + rr];
+  }
+
+  if constexpr (kGreedy) {
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerPhase; ++rr) {
+      const int k = k0 + rr;
+      if (k > k1) break;
+      float bv = -__builtin_inff();
+      int bi = INT_MAX;
+#pragma unroll
+      for (int j = 0; j < kLaneTiles; ++j)
+        if (t0 + j < t1) argmax_merge(bv, bi, rs[rr].p[j].x, __float_as_int(rs[rr].p[j].y));
+      wave_argmax(bv, bi);
+      bool accepted = false;
       if (k <= g) {
-        x = a.draft_tokens[(size_t)b * g + k - 1];
-        prev = k == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + k - 2];
-        if constexpr (!kGreedy) pdx = (double)a.draft_prob[(size_t)b * g + k - 1];
-      }
-      bool accepted = false;  // uniform across the block
-      if constexpr (kGreedy) {
-        float bv = -__builtin_inff();
-        int bi = INT_MAX;
-#pragma unroll
-        for (int j = 0; j < kTilesPerThreadFast; ++j) {
-          const int t = tid * kTilesPerThreadFast + j;
-          if (t < ntv) argmax_merge(bv, bi, pv[j].x, __float_as_int(pv[j].y));
+        accepted = bi == xk[rr];
+        if (threadIdx.x == 0) {
+          if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = accepted ? 1.0f : 0.0f;
+          a.out_tokens[(size_t)b * (g + 1) + k - 1] = accepted ? xk[rr] : bi;
+          if (!accepted) a.accept_len[b] = k - 1;
         }
-        block_argmax<kVThreads>(bv, bi, sv, si);
-        if (k <= g) {
-          accepted = bi == x;
-          if (tid == 0) {
-            if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = accepted ? 1.0f : 0.0f;
-            a.out_tokens[(size_t)b * (g + 1) + k - 1] = accepted ? x : bi;
-            if (!accepted) a.accept_len[b] = k - 1;
-          }
-        } else if (tid == 0) {
-          a.out_tokens[(size_t)b * (g + 1) + g] = bi;
+      } else if (threadIdx.x == 0) {
+        a.out_tokens[(size_t)b * (g + 1) + g] = bi;
+        a.accept_len[b] = g;
+      }
+      if (!accepted) return;
+      if (k == k1 && threadIdx.x == 0) {
+        const int pos = atomicAdd(&w.counts[ph + 1], 1);
+        w.lists[(size_t)(ph + 1) * a.B + pos] = b;
+      }
+    }
+  } else {
+    const uint64_t seed = a.seeds[b];
+    const double cf = (double)cf_f;
+    // batch 2: draft logits of the drafted tokens
+    double lxk[kRowsPerPhase];
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerPhase; ++rr) {
+      const int kc = min(k0 + rr, g);
+      const float* urow = a.U + ((size_t)b * g + (kc - 1)) * (size_t)a.V;
+      lxk[rr] = wave_draft_logit<kBf16>(a, urow, prevk[rr], xk[rr]);
+    }
+    // One block position; returns true when the request is finished (a
+    // rejection, or the bonus token).  Called with constant row indices so
+    // that the row state stays in registers.
+    auto position = [&](int rr, RowScan& s, int x, int prev, float pdxf, float tx, double lx) -> bool {
+      const int k = k0 + rr;
+      row_scan(s, cf_f);
+      const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
+      if (k > g) {  // bonus token from the position after the block
+        const double u = unit_uniform(draw_block(seed, a.round, g + 1, kStreamResidual, 0).w[0]);
+        const double q = u * s.Z;
+        int ts;
+        double base;
+        float mt;
+        tile_search(s, cf_f, q, ts, base, mt);
+        int y;
+        float ty;
+        group_col_draw(trow, a.V, ts, mt, s.M, cf_f, cf, q - base, y, ty);
+        if (threadIdx.x == 0) {
+          a.out_tokens[(size_t)b * (g + 1) + g] = y;
           a.accept_len[b] = g;
         }
-      } else {
-        // batch 2: depends on the drafted and previous tokens
-        const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
-        float tx = 0.0f, ux = 0.0f, w1v[2] = {0.0f, 0.0f}, w2v[2] = {0.0f, 0.0f};
-        if (k <= g) {
-          tx = trow[x];
-          ux = urow[x];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int j = tid + q * kVThreads;
-            const int jc = j < a.r ? j : 0;
-            w1v[q] = (float)wval<kBf16>(a.W1, (size_t)prev * a.r + jc);
-            w2v[q] = (float)wval<kBf16>(a.W2, (size_t)jc * a.V + x);
-          }
-        }
-        // normaliser and cumulative tile weights
-        float lm = -__builtin_inff();
-#pragma unroll
-        for (int j = 0; j < kTilesPerThreadFast; ++j) {
-          const int t = tid * kTilesPerThreadFast + j;
-          if (t < ntv) lm = fmaxf(lm, pv[j].x);
-        }
-        const float M = block_max<kVThreads>(lm, sv);
-        double wt[kTilesPerThreadFast], local = 0.0;
-#pragma unroll
-        for (int j = 0; j < kTilesPerThreadFast; ++j) {
-          const int t = tid * kTilesPerThreadFast + j;
-          wt[j] = (t < ntv && pv[j].x != -__builtin_inff())
-                      ? (double)pv[j].y * (double)fast_exp2((pv[j].x - M) * cf_f)
-                      : 0.0;
-          local += wt[j];
-        }
-        if (tid == 0) s_lastpos = 0;
-        double Z;
-        const double excl = block_exclusive_scan<kVThreads>(local, ps.red, Z);
-        {
-          double cum = excl;
-#pragma unroll
-          for (int j = 0; j < kTilesPerThreadFast; ++j) {
-            const int t = tid * kTilesPerThreadFast + j;
-            cum += wt[j];
-            if (t < ntv) {
-              scum[t + 1] = cum;
-              if (wt[j] > 0.0) atomicMax(&s_lastpos, t);
-            }
-          }
-          if (tid == 0) scum[0] = 0.0;
-        }
-        __syncthreads();
-        DecideCtx c;
-        c.P = P;
-        c.trow = trow;
-        c.M = M;
-        c.cf = cf;
-        c.ntv = ntv;
-        c.V = a.V;
-        if (k > g) {  // bonus token from the position after the block
-          const double u = unit_uniform(draw_block(seed, a.round, g + 1, kStreamResidual, 0).w[0]);
-          if (wave == 0) {
-            const int y = wave_sample_target(c, scum, s_lastpos, u * Z);
-            if (lane == 0) {
-              a.out_tokens[(size_t)b * (g + 1) + g] = y;
-              a.accept_len[b] = g;
-            }
-          }
-        } else {
-          const double ptx = exp2((double)(tx - M) * cf) / Z;
-          const double alpha = fmin(1.0, ptx / pdx);
-          const double u = unit_uniform(draw_block(seed, a.round, k, kStreamAccept, 0).w[0]);
-          accepted = u < alpha;
-          if (tid == 0) {
-            if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = (float)alpha;
-            if (accepted) a.out_tokens[(size_t)b * (g + 1) + k - 1] = x;
-          }
-          if (!accepted) {
-            // Rejected at k: residual draw by proposals from p_t, one per wave.
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int j = tid + q * kVThreads;
-              if (j < a.r) sw1[j] = w1v[q];
-            }
-            double part = 0.0;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int j = tid + q * kVThreads;
-              if (j < a.r) part += (double)w1v[q] * (double)w2v[q];
-            }
-            const double lx = (double)ux + block_sum<kVThreads, double>(part, sred);
-            int found = -1;
-            for (int i0 = 0; i0 < DSPARK_MAX_RESIDUAL_PROPOSALS && found < 0; i0 += kWaves) {
-              const int i = i0 + wave;
-              int pass = 0, v = -1;
-              if (i < DSPARK_MAX_RESIDUAL_PROPOSALS) {
-                const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
-                const double up = unit_uniform(d.w[0]);
-                const double ua = unit_uniform(d.w[1]);
-                v = wave_sample_target(c, scum, s_lastpos, up * Z);
-                const float tv = trow[v];
-                const double lv = wave_draft_logit_batched<kBf16>(a, urow, sw1, v);
-                const double ptv = exp2((double)(tv - M) * cf) / Z;
-                const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
-                const double keep = fmax(0.0, 1.0 - pdv / ptv);
-                pass = ua < keep;
-              }
-              if (lane == 0) {
-                s_pass[wave] = pass;
-                s_tok[wave] = v;
-              }
-              __syncthreads();
-#pragma unroll
-              for (int ww = 0; ww < kWaves; ++ww) {
-                if (found < 0 && s_pass[ww]) found = s_tok[ww];
-              }
-              __syncthreads();
-            }
-            if (tid == 0) {
-              a.accept_len[b] = k - 1;
-              if (found >= 0) {
-                a.out_tokens[(size_t)b * (g + 1) + k - 1] = found;
-              } else {
-                FallbackInfo f;
-                f.j = k;
-                f.prev = prev;
-                f.phase_row = k - k0;
-                f.M = (double)M;
-                f.Z = Z;
-                f.pdx = pdx;
-                f.lx = lx;
-                w.fb[b] = f;
-                const int pos = atomicAdd(&w.counts[0], 1);
-                w.fb_list[pos] = b;
-              }
-            }
-          }
-        }
+        return true;
       }
-      __syncthreads();
-      if (!accepted) break;  // rejection, or the bonus token: the request is finished
-      if (k == k1) {         // accepted the last position of this phase: alive in the next one
-        if (tid == 0) {
+      const double ptx = exp2((double)(tx - s.M) * cf) / s.Z;
+      const double pdx = (double)pdxf;
+      const double alpha = fmin(1.0, ptx / pdx);
+      const double u = unit_uniform(draw_block(seed, a.round, k, kStreamAccept, 0).w[0]);
+      const bool accepted = u < alpha;
+      if (threadIdx.x == 0) {
+        if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = (float)alpha;
+        if (accepted) a.out_tokens[(size_t)b * (g + 1) + k - 1] = x;
+      }
+      if (accepted) {
+        if (k == k1 && threadIdx.x == 0) {
           const int pos = atomicAdd(&w.counts[ph + 1], 1);
           w.lists[(size_t)(ph + 1) * a.B + pos] = b;
         }
+        return false;
       }
-    }
+
+      // Rejected at k: residual draw by proposals from p_t, 16 per batch.
+      const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
+      const int grp = lane >> 4;
+      int found = -1, ytok = -1;
+      for (int i0 = 0; i0 < DSPARK_MAX_RESIDUAL_PROPOSALS; i0 += kPropBatch) {
+        // the four proposals of this wave: tile searches (wave-wide), then one
+        // column draw and one draft logit per 16-lane group
+        double ql = 0.0, ua = 0.0;
+        int ts = 0;
+        float mt = 0.0f;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int i = i0 + 4 * wave + gq;
+          const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
+          const double q = unit_uniform(d.w[0]) * s.Z;
+          int tsq;
+          double bq;
+          float mq;
+          tile_search(s, cf_f, q, tsq, bq, mq);
+          if (gq == grp) {
+            ql = q - bq;
+            ua = unit_uniform(d.w[1]);
+            ts = tsq;
+            mt = mq;
+          }
+        }
+        int v;
+        float tv;
+        group_col_draw(trow, a.V, ts, mt, s.M, cf_f, cf, ql, v, tv);
+        const double lv = group_draft_logit<kBf16>(a, urow, prev, v);
+        const double ptv = exp2((double)(tv - s.M) * cf) / s.Z;
+        const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
+        const double keep = fmax(0.0, 1.0 - pdv / ptv);
+        const bool pass = ua < keep;
+        const unsigned long long kept = __ballot(pass && (lane & 15) == 0);
+        const int gi = kept ? (__ffsll((long long)kept) - 1) >> 4 : -1;
+        const int tok = __shfl(v, gi < 0 ? 0 : 16 * gi);
+        if (lane == 0) {
+          s_idx[wave] = gi < 0 ? INT_MAX : i0 + 4 * wave + gi;
+          s_tok[wave] = tok;
+        }
+        __syncthreads();
+        int best = INT_MAX, btok = -1;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          if (s_idx[ww] < best) {
+            best = s_idx[ww];
+            btok = s_tok[ww];
+          }
+        }
+        __syncthreads();
+        if (best != INT_MAX) {
+          found = best;
+          ytok = btok;
+          break;
+        }
+      }
+      if (threadIdx.x == 0) {
+        a.accept_len[b] = k - 1;
+        if (found >= 0) {
+          a.out_tokens[(size_t)b * (g + 1) + k - 1] = ytok;
+        } else {
+          FallbackInfo f;
+          f.j = k;
+          f.prev = prev;
+          f.phase_row = rr;
+          f.M = (double)s.M;
+          f.Z = s.Z;
+          f.pdx = pdx;
+          f.lx = lx;
+          w.fb[b] = f;
+          const int pos = atomicAdd(&w.counts[0], 1);
+          w.fb_list[pos] = b;
+        }
+      }
+      return true;
+    };
+    static_assert(kRowsPerPhase == 2, "two block positions per phase");
+    if (position(0, rs[0], xk[0], prevk[0], pdxk[0], txk[0], lxk[0])) return;
+    if (k0 + 1 <= k1) position(1, rs[1], xk[1], prevk[1], pdxk[1], txk[1], lxk[1]);
   }
 }
 
@@ -886,16 +945,18 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
     t.ntv = ntv;
     t.cf = cf;
     t.tpart = w.tpart;
+    t.draft_tokens = a.draft_tokens;
+    t.tx_out = greedy ? nullptr : w.txv;
     e = launch_target_stats(t, greedy, a.B * t.rows_per_req, s);
     if (e != hipSuccess) return e;
     ProfScope prof(s, kProfVerifyDecide);
-    if (ntv <= kPrefixMax) {
+    if (ntv <= kPrefixMax) {  // one workgroup per listed request
       if (greedy) {
-        hipLaunchKernelGGL((verify_decide_kernel<true, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, cf, ntv);
+        hipLaunchKernelGGL((verify_decide_kernel<true, true>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, cf, ntv);
       } else if (bf16) {
-        hipLaunchKernelGGL((verify_decide_kernel<false, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, cf, ntv);
+        hipLaunchKernelGGL((verify_decide_kernel<false, true>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, cf, ntv);
       } else {
-        hipLaunchKernelGGL((verify_decide_kernel<false, false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, cf,
+        hipLaunchKernelGGL((verify_decide_kernel<false, false>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, cf,
                            ntv);
       }
     } else if (greedy) {

@@ -90,7 +90,7 @@ typedef enum { DSPARK_OP_DRAFT = 0, DSPARK_OP_VERIFY = 1, DSPARK_OP_SURVIVAL = 2
 
 /* Maximum number of residual proposals drawn against p_t before the exact
  * residual inverse CDF (stream 3) is used. */
-#define DSPARK_MAX_RESIDUAL_PROPOSALS 16
+#define DSPARK_MAX_RESIDUAL_PROPOSALS 64
 
 /* Library version as major * 10000 + minor * 100 + patch. */
 int dspark_version(void);

@@ -186,7 +186,7 @@ def residual_sample(pt, pd, seed, rnd, j, max_proposals, dists):
     return v
 
 
-def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=16,
+def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=64,
            requests=None):
     """Rejection-sampling verification of every request's drafted block
     ([R] "Speculative Decoding: Draft, Then Verify" step 3; [E] section 2).

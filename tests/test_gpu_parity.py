@@ -255,7 +255,7 @@ def test_first_emitted_token_follows_target_law():
 def test_exact_residual_fallback_rows():
     """Target rows a hair away from the draft rows: rejections are rare and,
     when they happen, the residual mass is so small that most of them exhaust
-    the 16 proposals and take the exact residual inverse CDF (stream 3)."""
+    the 64 proposals and take the exact residual inverse CDF (stream 3)."""
     V, r, gamma, B = 300, 16, 3, 2000
     rng = np.random.default_rng(5)
     U = rng.standard_normal((B, gamma, V)).astype(np.float32)
