@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "DsparkError", "OP_DRAFT", "OP_VERIFY", "OP_SURVIVAL", "MAX_RESIDUAL_PROPOSALS",
     "library_path", "load", "version", "workspace_size", "markov_bias",
-    "markov_draft", "verify", "survival", "profile_enable", "profile_read",
+    "markov_draft", "verify", "transpose_w2", "survival", "profile_enable", "profile_read",
 ]
 
 OP_DRAFT, OP_VERIFY, OP_SURVIVAL = 0, 1, 2
@@ -60,7 +60,9 @@ def load():
     lib.dspark_markov_draft.restype = I
     lib.dspark_markov_draft.argtypes = [P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
     lib.dspark_verify.restype = I
-    lib.dspark_verify.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_transpose_w2.restype = I
+    lib.dspark_transpose_w2.argtypes = [P, I, I, I, P, P]
     lib.dspark_survival.restype = I
     lib.dspark_survival.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P]
     lib.dspark_profile_enable.restype = I
@@ -191,8 +193,9 @@ def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=Non
 
 
 def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, rnd, out=None,
-           with_accept_prob=True, workspace=None, stream=None):
-    """Rejection-sampling verification.  Returns (accept_len, out_tokens, accept_prob or None)."""
+           with_accept_prob=True, workspace=None, stream=None, W2T=None):
+    """Rejection-sampling verification.  Returns (accept_len, out_tokens, accept_prob or None).
+    W2T: optional transposed copy of W2 from transpose_w2."""
     B, g1, V = target.shape
     gamma = g1 - 1
     dev = target.device
@@ -204,6 +207,8 @@ def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, 
         _dev(W1, "W1", None, (V, r))
         _dev(W2, "W2", W1.dtype, (r, V))
     wd = _wdtype(W1, W2) if W1 is not None else _BF16
+    if W2T is not None:
+        _dev(W2T, "W2T", W2.dtype, (V, r))
     _dev(x0, "x0", torch.int32, (B,))
     _dev(draft_tokens, "draft_tokens", torch.int32, (B, gamma))
     if draft_prob is not None:
@@ -220,11 +225,25 @@ def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, 
     if aprob is not None:
         _dev(aprob, "accept_prob", torch.float32, (B, gamma))
     ws, nbytes = _workspace(OP_VERIFY, B, gamma, V, r, workspace, dev)
-    st = load().dspark_verify(_p(U), _p(W1), _p(W2), wd, _p(x0), _p(draft_tokens), _p(draft_prob), _p(target),
+    st = load().dspark_verify(_p(U), _p(W1), _p(W2), _p(W2T), wd, _p(x0), _p(draft_tokens), _p(draft_prob), _p(target),
                               B, gamma, V, r, float(temperature), _p(seeds), int(rnd), _p(alen), _p(otok),
                               _p(aprob), _p(ws), nbytes, _stream(stream, dev))
     _check("dspark_verify", st)
     return alen, otok, aprob
+
+
+def transpose_w2(W2, out=None, stream=None):
+    """W2 [r][V] -> a new (or the given) [V][r] tensor of the same dtype."""
+    r, V = W2.shape
+    dev = W2.device
+    _dev(W2, "W2", None)
+    wd = _wdtype(W2, W2)
+    if out is None:
+        out = torch.empty((V, r), dtype=W2.dtype, device=dev)
+    _dev(out, "W2T", W2.dtype, (V, r))
+    st = load().dspark_transpose_w2(_p(W2), wd, r, V, _p(out), _stream(stream, dev))
+    _check("dspark_transpose_w2", st)
+    return out
 
 
 def survival(U, W1, W2, x0, draft_tokens, draft_lse, target, temperature, conf=None, out=None,

@@ -98,7 +98,8 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
   return from_hip(launch_draft(a, wdtype == DSPARK_BF16, stream));
 }
 
-dspark_status dspark_verify(const float* U, const void* W1, const void* W2, dspark_dtype wdtype, const int32_t* x0,
+dspark_status dspark_verify(const float* U, const void* W1, const void* W2, const void* W2T, dspark_dtype wdtype,
+                            const int32_t* x0,
                             const int32_t* draft_tokens, const float* draft_prob, const float* target_logits, int B,
                             int gamma, int V, int r, float temperature, const uint64_t* seeds, uint64_t round,
                             int32_t* accept_len, int32_t* out_tokens, float* accept_prob, void* workspace,
@@ -109,13 +110,15 @@ dspark_status dspark_verify(const float* U, const void* W1, const void* W2, dspa
   if (!req(x0, 4) || !req(draft_tokens, 4) || !req(target_logits, 16) || !req(accept_len, 4) ||
       !req(out_tokens, 4) || !opt(accept_prob, 4) || !req(workspace, 16))
     return DSPARK_ERR_INVALID_ARGUMENT;
-  if (!greedy && (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(draft_prob, 4) || !req(seeds, 8)))
+  if (!greedy && (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !opt(W2T, 16) || !req(draft_prob, 4) ||
+                  !req(seeds, 8)))
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < verify_workspace(B, gamma, V, r)) return DSPARK_ERR_WORKSPACE;
   VerifyArgs a = {};
   a.U = U;
   a.W1 = W1;
   a.W2 = W2;
+  a.W2T = greedy ? nullptr : W2T;
   a.x0 = x0;
   a.draft_tokens = draft_tokens;
   a.draft_prob = draft_prob;
@@ -132,6 +135,12 @@ dspark_status dspark_verify(const float* U, const void* W1, const void* W2, dspa
   a.accept_prob = accept_prob;
   a.ws = workspace;
   return from_hip(launch_verify(a, wdtype == DSPARK_BF16, stream));
+}
+
+dspark_status dspark_transpose_w2(const void* W2, dspark_dtype wdtype, int r, int V, void* W2T, hipStream_t stream) {
+  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!sizes_ok(1, 1, V, r) || !req(W2, 16) || !req(W2T, 16) || W2 == W2T) return DSPARK_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_transpose_w2(W2, wdtype == DSPARK_BF16, r, V, W2T, stream));
 }
 
 dspark_status dspark_survival(const float* U, const void* W1, const void* W2, dspark_dtype wdtype, const int32_t* x0,

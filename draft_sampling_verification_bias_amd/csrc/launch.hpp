@@ -71,6 +71,7 @@ struct VerifyArgs {
   const float* U;
   const void* W1;
   const void* W2;
+  const void* W2T;  // optional [V][r] copy of W2
   const int32_t* x0;
   const int32_t* draft_tokens;
   const float* draft_prob;
@@ -131,6 +132,8 @@ struct TStatsArgs {
 };
 
 hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, hipStream_t s);
+
+hipError_t launch_transpose_w2(const void* W2, bool bf16, int r, int V, void* W2T, hipStream_t s);
 
 hipError_t launch_markov_bias(const void* W1, const void* W2, bool bf16, const int32_t* tokens,
                               int n, int V, int r, float* out, hipStream_t s);

@@ -26,6 +26,7 @@ namespace dspark {
 
 constexpr int kVThreads = 256;
 constexpr int kRowsPerPhase = 2;   // block positions verified per phase
+constexpr int kPropPre = 16;       // residual proposals whose uniforms are drawn ahead, per position
 
 struct FallbackInfo {
   int j;        // rejected position (1-based)
@@ -44,6 +45,10 @@ struct VerifyWs {
   FallbackInfo* fb;     // [B] indexed by request
   double* fb_part;      // [B][ntv] residual mass per tile
   float* txv;           // [B][kRowsPerPhase] target logit of the drafted token, current phase
+  int* alive;           // [B] the phase in which the request is still undecided (0: none)
+  double* lxv;          // [B][gamma] draft logit U[x_k] + W1[x_{k-1}] . W2[:, x_k] of every drafted token
+  double* u_acc;        // [B][gamma] acceptance uniforms (stream 1)
+  double2* u_prop;      // [B][gamma + 1][kPropPre] words 0, 1 of the first residual proposals (stream 2)
 };
 
 static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
@@ -63,6 +68,14 @@ static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
   w.fb_part = reinterpret_cast<double*>(p);  // [B][ceil(V / kResCols)]
   p += align256((size_t)B * tiles_of(V, 256) * sizeof(double));
   w.txv = reinterpret_cast<float*>(p);
+  p += align256((size_t)B * kRowsPerPhase * sizeof(float));
+  w.alive = reinterpret_cast<int*>(p);
+  p += align256((size_t)B * sizeof(int));
+  w.lxv = reinterpret_cast<double*>(p);
+  p += align256((size_t)B * gamma * sizeof(double));
+  w.u_acc = reinterpret_cast<double*>(p);
+  p += align256((size_t)B * gamma * sizeof(double));
+  w.u_prop = reinterpret_cast<double2*>(p);
   return w;
 }
 
@@ -72,7 +85,9 @@ size_t verify_workspace(int B, int gamma, int V, int r) {
   return align256((size_t)B * kRowsPerPhase * ntv * sizeof(float2)) + align256((size_t)(gamma + 2) * B * sizeof(int)) +
          align256((size_t)(gamma + 2) * sizeof(int)) + align256((size_t)B * sizeof(int)) +
          align256((size_t)B * sizeof(FallbackInfo)) + align256((size_t)B * tiles_of(V, 256) * sizeof(double)) +
-         align256((size_t)B * kRowsPerPhase * sizeof(float));
+         align256((size_t)B * kRowsPerPhase * sizeof(float)) + align256((size_t)B * sizeof(int)) +
+         align256((size_t)B * gamma * sizeof(double)) + align256((size_t)B * gamma * sizeof(double)) +
+         align256((size_t)B * (gamma + 1) * kPropPre * sizeof(double2));
 }
 
 template <bool kBf16>
@@ -185,9 +200,63 @@ hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, h
 // Initialisation: outputs to their "not reached" values, validity check of
 // every request's tokens, and the ordered list of phase 1.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kVThreads) void verify_init_kernel(VerifyArgs a, VerifyWs w) {
+__global__ __launch_bounds__(kVThreads) void verify_init_kernel(VerifyArgs a, VerifyWs w, int wbf16) {
   __shared__ PickScratch ps;
   const int g = a.gamma;
+  const int per_req = g + (g + 1) * kPropPre;
+  const int draw_blocks = (a.B * per_req + kVThreads - 1) / kVThreads;
+  if (blockIdx.x > draw_blocks) {
+    // The draft logit of every drafted token (needed after a rejection), one
+    // wave per (request, position): l = U[x] + W1[x_prev] . W2[:, x] with
+    // float64 products of the exact weights.
+    const int item = (blockIdx.x - 1 - draw_blocks) * (kVThreads / kWave) + threadIdx.x / kWave;
+    if (item >= a.B * g) return;
+    const int b = item / g, k = item - b * g;  // k 0-based
+    const int lane = threadIdx.x & (kWave - 1);
+    const int x = a.draft_tokens[(size_t)b * g + k];
+    const int prev = k == 0 ? a.x0[b] : a.draft_tokens[(size_t)b * g + k - 1];
+    if ((unsigned)x >= (unsigned)a.V || (unsigned)prev >= (unsigned)a.V) return;  // invalid request
+    const float* urow = a.U + ((size_t)b * g + k) * (size_t)a.V;
+    double sum = 0.0;
+    for (int j0 = 0; j0 < a.r; j0 += 4 * kWave) {
+      float e[4], wv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int j = j0 + lane + m * kWave;
+        const int jc = j < a.r ? j : 0;
+        e[m] = wbf16 ? bf16_to_float(reinterpret_cast<const uint16_t*>(a.W1)[(size_t)prev * a.r + jc])
+                     : reinterpret_cast<const float*>(a.W1)[(size_t)prev * a.r + jc];
+        const size_t wi = a.W2T ? (size_t)x * a.r + jc : (size_t)jc * a.V + x;
+        const void* W2x = a.W2T ? a.W2T : a.W2;
+        wv[m] = wbf16 ? bf16_to_float(reinterpret_cast<const uint16_t*>(W2x)[wi])
+                      : reinterpret_cast<const float*>(W2x)[wi];
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (j0 + lane + m * kWave < a.r) sum += (double)e[m] * (double)wv[m];
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) w.lxv[(size_t)b * g + k] = (double)urow[x] + sum;
+    return;
+  }
+  if (blockIdx.x > 0) {
+    // The random numbers of the decisions, drawn ahead so that no decision
+    // waits for a Philox evaluation: per (request, position) the acceptance
+    // uniform and the first kPropPre residual proposals (both words), the
+    // latter also at position gamma+1 (proposal 0 there is the bonus draw).
+    const int id = (blockIdx.x - 1) * kVThreads + threadIdx.x;
+    if (id >= a.B * per_req) return;
+    const int b = id / per_req, j = id - b * per_req;
+    const uint64_t seed = a.seeds[b];
+    if (j < g) {
+      w.u_acc[(size_t)b * g + j] = unit_uniform(draw_block(seed, a.round, j + 1, kStreamAccept, 0).w[0]);
+    } else {
+      const int kk = (j - g) / kPropPre, i = (j - g) - kk * kPropPre;
+      const Philox4 d = draw_block(seed, a.round, kk + 1, kStreamResidual, (uint64_t)i);
+      w.u_prop[((size_t)b * (g + 1) + kk) * kPropPre + i] = make_double2(unit_uniform(d.w[0]), unit_uniform(d.w[1]));
+    }
+    return;
+  }
   if (threadIdx.x < g + 2) w.counts[threadIdx.x] = 0;
   int running = 0;
   for (int base = 0; base < a.B; base += kVThreads) {
@@ -202,6 +271,7 @@ __global__ __launch_bounds__(kVThreads) void verify_init_kernel(VerifyArgs a, Ve
       }
       for (int k = 0; k <= g; ++k) a.out_tokens[(size_t)b * (g + 1) + k] = -1;
       a.accept_len[b] = -1;
+      w.alive[b] = valid ? 1 : 0;
     }
     double tot;
     const double ex = block_exclusive_scan<kVThreads>((double)valid, ps.red, tot);
@@ -384,6 +454,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
       if (k == k1 && threadIdx.x == 0) {
         const int pos = atomicAdd(&w.counts[ph + 1], 1);
         w.lists[(size_t)(ph + 1) * a.B + pos] = b;
+        w.alive[b] = ph + 1;
       }
     }
   }
@@ -403,7 +474,6 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
 // ---------------------------------------------------------------------------
 constexpr int kLaneTiles = kPrefixMax / kWave;                    // 16 summaries per lane
 constexpr int kPropBatch = 4 * (kVThreads / kWave);               // proposals per batch
-static_assert(DSPARK_MAX_RESIDUAL_PROPOSALS % kPropBatch == 0, "whole proposal batches");
 
 // Weight of a tile summary relative to the row maximum M (cf = log2(e) / T).
 __device__ __forceinline__ double tile_weight(const float2& p, float M, float cf) {
@@ -420,105 +490,111 @@ struct RowScan {
   double local, excl, incl, Z;
 };
 
-__device__ __forceinline__ void row_scan(RowScan& s, float cf) {
+__device__ __forceinline__ void row_scan(RowScan& s, float cf, double (&cumi)[kLaneTiles], unsigned& wmask) {
   float lm = -__builtin_inff();
 #pragma unroll
   for (int j = 0; j < kLaneTiles; ++j)
     if (s.t0 + j < s.t1) lm = fmaxf(lm, s.p[j].x);
   s.M = wave_max(lm);
   double loc = 0.0;
+  wmask = 0u;
 #pragma unroll
-  for (int j = 0; j < kLaneTiles; ++j)
-    if (s.t0 + j < s.t1) loc += tile_weight(s.p[j], s.M, cf);
+  for (int j = 0; j < kLaneTiles; ++j) {
+    const double wt = s.t0 + j < s.t1 ? tile_weight(s.p[j], s.M, cf) : 0.0;
+    if (wt > 0.0) wmask |= 1u << j;
+    loc += wt;
+    cumi[j] = wt;
+  }
   s.local = loc;
   s.incl = wave_inclusive_scan(loc);
   s.excl = s.incl - loc;
   s.Z = __shfl(s.incl, kWave - 1);
+  double cum = s.excl;  // the lane's inclusive cumulative weights, in tile order
+#pragma unroll
+  for (int j = 0; j < kLaneTiles; ++j) {
+    cum += cumi[j];
+    cumi[j] = cum;
+  }
 }
 
-// Tile of the first cumulative weight above q (the last positive tile if
-// rounding leaves none), the cumulative weight before it and its maximum;
-// q is the same on every lane, the results are returned to every lane.
-__device__ __forceinline__ void tile_search(const RowScan& s, float cf, double q, int& ts, double& base,
-                                            float& mt) {
+// Tile of the first cumulative weight above q among positive tiles (the last
+// positive tile if rounding leaves none), the cumulative weight before it
+// and its maximum.  q is the same on every lane; so are the results.
+__device__ __forceinline__ void tile_search(const RowScan& s, const double (&cumi)[kLaneTiles], unsigned wmask,
+                                            double q, int& ts_o, double& base_o, float& mt_o) {
   const int lane = threadIdx.x & (kWave - 1);
   const unsigned long long cross = __ballot(s.local > 0.0 && s.incl > q);
   const unsigned long long pos = __ballot(s.local > 0.0);
   const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
-  int t = -1;
+  int t = 0;
   double bb = 0.0;
   float m = s.M;
   if (lane == owner) {
-    double cum = s.excl, lastbase = 0.0;
-    int lastpos = -1;
-    float lastm = s.M;
+    int jp = -1, jl = -1;
 #pragma unroll
     for (int j = 0; j < kLaneTiles; ++j) {
-      if (s.t0 + j < s.t1) {
-        const double w = tile_weight(s.p[j], s.M, cf);
-        if (w > 0.0) {
-          lastpos = s.t0 + j;
-          lastbase = cum;
-          lastm = s.p[j].x;
-          if (t < 0 && cum + w > q) {
-            t = s.t0 + j;
-            bb = cum;
-            m = s.p[j].x;
-          }
-        }
-        cum += w;
+      if ((wmask >> j) & 1u) {
+        jl = j;
+        if (jp < 0 && cumi[j] > q) jp = j;
       }
     }
-    if (t < 0) {
-      t = lastpos < 0 ? 0 : lastpos;
-      bb = lastpos < 0 ? 0.0 : lastbase;
-      m = lastm;
+    const int jj = jp >= 0 ? jp : jl;
+#pragma unroll
+    for (int j = 0; j < kLaneTiles; ++j) {
+      if (j == jj) {
+        t = s.t0 + j;
+        bb = j == 0 ? s.excl : cumi[j > 0 ? j - 1 : 0];
+        m = s.p[j].x;
+      }
     }
   }
-  ts = __shfl(t, owner);
-  base = __shfl(bb, owner);
-  mt = __shfl(m, owner);
+  ts_o = __shfl(t, owner);
+  base_o = __shfl(bb, owner);
+  mt_o = __shfl(m, owner);
 }
 
-// Within each 16-lane group: the column of target tile ts (kTgtCols columns,
-// 16 per lane) whose cumulative weight first exceeds ql (the last positive
-// one if none), and its target logit.  ts, mt, ql may differ between groups.
-__device__ __forceinline__ void group_col_draw(const float* trow, int V, int ts, float mt, float M, float cf_f,
-                                               double cf, double ql, int& v_out, float& x_out) {
+// Within each group of kW lanes (16 or 64): the column of target tile ts
+// (kTgtCols columns, kTgtCols / kW per lane) whose cumulative weight first
+// exceeds ql (the last positive one if none), and its target logit.  ts, mt,
+// ql may differ between groups.
+template <int kW>
+__device__ __forceinline__ void col_draw(const float* trow, int V, int ts, float mt, float M, float cf_f, double cf,
+                                         double ql, int& v_out, float& x_out) {
+  constexpr int kC = kTgtCols / kW;  // columns per lane
   const int lane = threadIdx.x & (kWave - 1);
-  const int li = lane & 15, gbase = lane & ~15;
-  const int c0 = ts * kTgtCols + 16 * li;
-  float x[16];
-  if ((V & 3) == 0 && c0 + 16 <= V) {
+  const int li = lane & (kW - 1), gbase = lane & ~(kW - 1);
+  const int c0 = ts * kTgtCols + kC * li;
+  float x[kC];
+  if ((V & 3) == 0 && c0 + kC <= V) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kC / 4; ++j) {
       const float4 q = *reinterpret_cast<const float4*>(trow + c0 + 4 * j);
       x[4 * j] = q.x; x[4 * j + 1] = q.y; x[4 * j + 2] = q.z; x[4 * j + 3] = q.w;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kC; ++j) {
       const int c = c0 + j < V ? c0 + j : V - 1;
       const float v = trow[c];
       x[j] = c0 + j < V ? v : -__builtin_inff();
     }
   }
   const double scale = exp2((double)(mt - M) * cf);
-  float e[16];
+  float e[kC];
   double local = 0.0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < kC; ++j) {
     e[j] = x[j] == -__builtin_inff() ? 0.0f : fast_exp2((x[j] - mt) * cf_f);
     local += (double)e[j] * scale;
   }
   double incl = local;
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
+  for (int o = 1; o < kW; o <<= 1) {
     const double y = __shfl_up(incl, o);
     if (li >= o) incl += y;
   }
   const double excl = incl - local;
-  const unsigned long long gmask = 0xffffull << gbase;
+  const unsigned long long gmask = kW == 64 ? ~0ull : (((1ull << kW) - 1ull) << gbase);
   const unsigned long long cross = __ballot(local > 0.0 && incl > ql) & gmask;
   const unsigned long long pos = __ballot(local > 0.0) & gmask;
   const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : gbase);
@@ -528,7 +604,7 @@ __device__ __forceinline__ void group_col_draw(const float* trow, int V, int ts,
     double cum = excl;
     int lastp = -1;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kC; ++j) {
       const double t = (double)e[j] * scale;
       if (t > 0.0) {
         lastp = j;
@@ -538,7 +614,7 @@ __device__ __forceinline__ void group_col_draw(const float* trow, int V, int ts,
     }
     if (col < 0) col = lastp < 0 ? 0 : lastp;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < kC; ++j)
       if (j == col) xc = x[j];
     col += c0;
   }
@@ -546,69 +622,63 @@ __device__ __forceinline__ void group_col_draw(const float* trow, int V, int ts,
   x_out = __shfl(xc, owner);
 }
 
-// Draft logit U[v] + W1[prev] . W2[:, v] in float64, summed by a 16-lane group
-// (lane li takes k = li + 16 m); v may differ between groups.
-template <bool kBf16>
-__device__ __forceinline__ double group_draft_logit(const VerifyArgs& a, const float* urow, int prev, int v) {
-  const int li = threadIdx.x & 15;
-  const int nm = a.r / 16;  // r % 16 == 0
+// Draft logit U[v] + W1[prev] . W2[:, v] in float64, summed by a group of kW
+// lanes (lane li takes k = li + kW m); v may differ between groups.
+template <int kW, bool kBf16>
+__device__ __forceinline__ double draft_logit_at(const VerifyArgs& a, const float* urow, int prev, int v) {
+  constexpr int kCh = 256 / kW;  // products per lane per 256 k
+  const int li = threadIdx.x & (kW - 1);
   const float uv = urow[v];
   double s = 0.0;
-  for (int m0 = 0; m0 < nm; m0 += 16) {
-    float e[16], wv[16];
+  for (int k0 = 0; k0 < a.r; k0 += 256) {
+    float e[kCh], wv[kCh];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int k = li + 16 * min(m0 + m, nm - 1);  // clamped: all loads issued before the first use
-      e[m] = (float)wval<kBf16>(a.W1, (size_t)prev * a.r + k);
-      wv[m] = (float)wval<kBf16>(a.W2, (size_t)k * a.V + v);
+    for (int m = 0; m < kCh; ++m) {
+      const int k = k0 + li + kW * m;
+      const int kc = k < a.r ? k : 0;  // clamped: all loads issued before the first use
+      e[m] = (float)wval<kBf16>(a.W1, (size_t)prev * a.r + kc);
+      // with the transposed copy, the k of one load instruction are contiguous
+      wv[m] = a.W2T ? (float)wval<kBf16>(a.W2T, (size_t)v * a.r + kc) : (float)wval<kBf16>(a.W2, (size_t)kc * a.V + v);
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-      if (m0 + m < nm) s += (double)e[m] * (double)wv[m];
+    for (int m = 0; m < kCh; ++m)
+      if (k0 + li + kW * m < a.r) s += (double)e[m] * (double)wv[m];
   }
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+  for (int o = 1; o < kW; o <<= 1) s += __shfl_xor(s, o);
   return (double)uv + s;
 }
 
-// The same over a whole wave (lane l takes k = l + 64 m), for one v.
-template <bool kBf16>
-__device__ __forceinline__ double wave_draft_logit(const VerifyArgs& a, const float* urow, int prev, int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const float uv = urow[v];
-  float e[512 / kWave], wv[512 / kWave];
-#pragma unroll
-  for (int m = 0; m < 512 / kWave; ++m) {
-    const int k = lane + m * kWave;
-    const int kc = k < a.r ? k : 0;
-    e[m] = (float)wval<kBf16>(a.W1, (size_t)prev * a.r + kc);
-    wv[m] = (float)wval<kBf16>(a.W2, (size_t)kc * a.V + v);
-  }
-  double s = 0.0;
-#pragma unroll
-  for (int m = 0; m < 512 / kWave; ++m)
-    if (lane + m * kWave < a.r) s += (double)e[m] * (double)wv[m];
-  return (double)uv + wave_sum(s);
+// Words 0 and 1 of residual proposal i as uniforms (kept out of line: only
+// proposals past the first batch, which are rare, evaluate it here).
+__device__ __noinline__ double2 proposal_uniforms(uint64_t seed, uint64_t round, int k, int i) {
+  const Philox4 d = draw_block(seed, round, k, kStreamResidual, (uint64_t)i);
+  return make_double2(unit_uniform(d.w[0]), unit_uniform(d.w[1]));
 }
 
 template <bool kGreedy, bool kBf16>
 __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs w, int ph, float cf_f,
                                                                  int ntv) {
   constexpr int kWaves = kVThreads / kWave;
-  __shared__ int s_idx[kWaves], s_tok[kWaves];
+  __shared__ int s_idx[kWaves], s_tok[kWaves], s_last;
+  __shared__ double s_cum[kPrefixMax];  // inclusive cumulative tile weights (later proposal batches)
+  __shared__ float s_m[kPrefixMax];     // tile maxima
   const int g = a.gamma;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int k0 = kRowsPerPhase * (ph - 1) + 1, k1 = min(k0 + kRowsPerPhase - 1, g + 1);
-  const int li = blockIdx.x;
-  if (li >= w.counts[ph]) return;
-  const int b = w.lists[(size_t)ph * a.B + li];
+  const int b = blockIdx.x;
   const int cs = (ntv + kWave - 1) / kWave;
   const int t0 = min(ntv, lane * cs), t1 = min(ntv, t0 + cs);
 
-  // batch 1: summaries of the phase's rows, tokens, p_d(x), t(x), key
+  // One batch of loads, all addressed by the request id: whether the request
+  // is undecided in this phase, the summaries of the phase's rows, tokens,
+  // p_d(x), t(x) and the draft logit of x, and the uniforms drawn ahead.
+  const int alive = w.alive[b];
   RowScan rs[kRowsPerPhase];
   int xk[kRowsPerPhase], prevk[kRowsPerPhase];
   float pdxk[kRowsPerPhase], txk[kRowsPerPhase];
+  double uak[kRowsPerPhase], lxk[kRowsPerPhase];
+  double2 upk[kRowsPerPhase];  // lane l: proposal l % 16 of the row (proposal 0 of row gamma+1: the bonus)
 #pragma unroll
   for (int rr = 0; rr < kRowsPerPhase; ++rr) {
     const float2* P = w.tpart + ((size_t)b * kRowsPerPhase + rr) * ntv;
@@ -621,10 +691,26 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
     }
     const int kc = min(k0 + rr, g);  // clamped position: loads stay in bounds
     xk[rr] = a.draft_tokens[(size_t)b * g + kc - 1];
-    prevk[rr] = kc == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + kc - 2];
-    pdxk[rr] = kGreedy ? 1.0f : a.draft_prob[(size_t)b * g + kc - 1];
-    txk[rr] = kGreedy ? 0.0f : w.txv[(size_t)b * kRowsPerPhase + rr];
+    if constexpr (!kGreedy) {
+      prevk[rr] = kc == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + kc - 2];
+      pdxk[rr] = a.draft_prob[(size_t)b * g + kc - 1];
+      txk[rr] = w.txv[(size_t)b * kRowsPerPhase + rr];
+      lxk[rr] = w.lxv[(size_t)b * g + kc - 1];
+      uak[rr] = w.u_acc[(size_t)b * g + kc - 1];
+      const int kp = min(k0 + rr, g + 1);
+      upk[rr] = w.u_prop[((size_t)b * (g + 1) + kp - 1) * kPropPre + (lane & (kPropPre - 1))];
+    }
   }
+  if (alive != ph) return;
+
+  // accepted through the last position of the phase: undecided in the next
+  auto carry_on = [&]() {
+    if (threadIdx.x == 0) {
+      const int pos = atomicAdd(&w.counts[ph + 1], 1);
+      w.lists[(size_t)(ph + 1) * a.B + pos] = b;
+      w.alive[b] = ph + 1;
+    }
+  };
 
   if constexpr (kGreedy) {
 #pragma unroll
@@ -650,39 +736,29 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
         a.accept_len[b] = g;
       }
       if (!accepted) return;
-      if (k == k1 && threadIdx.x == 0) {
-        const int pos = atomicAdd(&w.counts[ph + 1], 1);
-        w.lists[(size_t)(ph + 1) * a.B + pos] = b;
-      }
+      if (k == k1) carry_on();
     }
   } else {
     const uint64_t seed = a.seeds[b];
     const double cf = (double)cf_f;
-    // batch 2: draft logits of the drafted tokens
-    double lxk[kRowsPerPhase];
-#pragma unroll
-    for (int rr = 0; rr < kRowsPerPhase; ++rr) {
-      const int kc = min(k0 + rr, g);
-      const float* urow = a.U + ((size_t)b * g + (kc - 1)) * (size_t)a.V;
-      lxk[rr] = wave_draft_logit<kBf16>(a, urow, prevk[rr], xk[rr]);
-    }
     // One block position; returns true when the request is finished (a
-    // rejection, or the bonus token).  Called with constant row indices so
-    // that the row state stays in registers.
-    auto position = [&](int rr, RowScan& s, int x, int prev, float pdxf, float tx, double lx) -> bool {
+    // rejection, or the bonus token).
+    auto position = [&](int rr, RowScan& s, int x, int prev, float pdxf, float tx, double lx, double uacc,
+                        double2 up0) -> bool {
       const int k = k0 + rr;
-      row_scan(s, cf_f);
+      double cumi[kLaneTiles];
+      unsigned wmask;
+      row_scan(s, cf_f, cumi, wmask);
       const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
       if (k > g) {  // bonus token from the position after the block
-        const double u = unit_uniform(draw_block(seed, a.round, g + 1, kStreamResidual, 0).w[0]);
-        const double q = u * s.Z;
+        const double q = __shfl(up0.x, 0) * s.Z;
         int ts;
         double base;
         float mt;
-        tile_search(s, cf_f, q, ts, base, mt);
+        tile_search(s, cumi, wmask, q, ts, base, mt);
         int y;
         float ty;
-        group_col_draw(trow, a.V, ts, mt, s.M, cf_f, cf, q - base, y, ty);
+        col_draw<kWave>(trow, a.V, ts, mt, s.M, cf_f, cf, q - base, y, ty);
         if (threadIdx.x == 0) {
           a.out_tokens[(size_t)b * (g + 1) + g] = y;
           a.accept_len[b] = g;
@@ -692,63 +768,35 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       const double ptx = exp2((double)(tx - s.M) * cf) / s.Z;
       const double pdx = (double)pdxf;
       const double alpha = fmin(1.0, ptx / pdx);
-      const double u = unit_uniform(draw_block(seed, a.round, k, kStreamAccept, 0).w[0]);
-      const bool accepted = u < alpha;
+      const bool accepted = uacc < alpha;
       if (threadIdx.x == 0) {
         if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = (float)alpha;
         if (accepted) a.out_tokens[(size_t)b * (g + 1) + k - 1] = x;
       }
       if (accepted) {
-        if (k == k1 && threadIdx.x == 0) {
-          const int pos = atomicAdd(&w.counts[ph + 1], 1);
-          w.lists[(size_t)(ph + 1) * a.B + pos] = b;
-        }
+        if (k == k1) carry_on();
         return false;
       }
 
-      // Rejected at k: residual draw by proposals from p_t, 16 per batch.
+      // Rejected at k: residual draw by proposals from p_t.  Proposal i is
+      // kept with probability max(0, 1 - p_d(v) / p_t(v)); the lowest kept i
+      // wins.  The first batch has one proposal per wave (most rejections end
+      // there), later ones four per wave, 16 lanes each.
       const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
-      const int grp = lane >> 4;
-      int found = -1, ytok = -1;
-      for (int i0 = 0; i0 < DSPARK_MAX_RESIDUAL_PROPOSALS; i0 += kPropBatch) {
-        // the four proposals of this wave: tile searches (wave-wide), then one
-        // column draw and one draft logit per 16-lane group
-        double ql = 0.0, ua = 0.0;
-        int ts = 0;
-        float mt = 0.0f;
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int i = i0 + 4 * wave + gq;
-          const Philox4 d = draw_block(seed, a.round, k, kStreamResidual, (uint64_t)i);
-          const double q = unit_uniform(d.w[0]) * s.Z;
-          int tsq;
-          double bq;
-          float mq;
-          tile_search(s, cf_f, q, tsq, bq, mq);
-          if (gq == grp) {
-            ql = q - bq;
-            ua = unit_uniform(d.w[1]);
-            ts = tsq;
-            mt = mq;
-          }
-        }
-        int v;
-        float tv;
-        group_col_draw(trow, a.V, ts, mt, s.M, cf_f, cf, ql, v, tv);
-        const double lv = group_draft_logit<kBf16>(a, urow, prev, v);
+      auto keep_test = [&](double ua, int v, float tv, double lv) -> bool {
         const double ptv = exp2((double)(tv - s.M) * cf) / s.Z;
         const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
-        const double keep = fmax(0.0, 1.0 - pdv / ptv);
-        const bool pass = ua < keep;
-        const unsigned long long kept = __ballot(pass && (lane & 15) == 0);
-        const int gi = kept ? (__ffsll((long long)kept) - 1) >> 4 : -1;
-        const int tok = __shfl(v, gi < 0 ? 0 : 16 * gi);
+        return ua < fmax(0.0, 1.0 - pdv / ptv);
+      };
+      // lowest kept proposal index over the waves (every wave receives it)
+      auto agree = [&](int idx, int tok, int& best, int& btok) {
         if (lane == 0) {
-          s_idx[wave] = gi < 0 ? INT_MAX : i0 + 4 * wave + gi;
+          s_idx[wave] = idx;
           s_tok[wave] = tok;
         }
         __syncthreads();
-        int best = INT_MAX, btok = -1;
+        best = INT_MAX;
+        btok = -1;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
           if (s_idx[ww] < best) {
@@ -757,15 +805,74 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
           }
         }
         __syncthreads();
-        if (best != INT_MAX) {
-          found = best;
-          ytok = btok;
-          break;
+      };
+      int found, ytok;
+      {
+        const double q = __shfl(up0.x, wave) * s.Z;
+        const double ua = __shfl(up0.y, wave);
+        int ts;
+        double bq;
+        float mt;
+        tile_search(s, cumi, wmask, q, ts, bq, mt);
+        int v;
+        float tv;
+        col_draw<kWave>(trow, a.V, ts, mt, s.M, cf_f, cf, q - bq, v, tv);
+        const double lv = draft_logit_at<kWave, kBf16>(a, urow, prev, v);
+        const bool pass = keep_test(ua, v, tv, lv);
+        agree(pass ? wave : INT_MAX, v, found, ytok);
+      }
+      const int grp = lane >> 4;
+      if (found == INT_MAX) {
+        // Later batches search by binary search over an LDS copy of the
+        // cumulative weights, one search per 16-lane group: the first tile
+        // whose inclusive cumulative weight exceeds q (it has positive
+        // weight), else the last positive tile -- the rule of tile_search.
+        if (wave == 0) {
+#pragma unroll
+          for (int j = 0; j < kLaneTiles; ++j) {
+            if (s.t0 + j < s.t1) {
+              s_cum[s.t0 + j] = cumi[j];
+              s_m[s.t0 + j] = s.p[j].x;
+            }
+          }
+          const unsigned long long pl = __ballot(wmask != 0u);
+          const int lw = pl ? 63 - __clzll((long long)pl) : 0;
+          if (lane == lw) s_last = wmask ? s.t0 + 31 - __clz(wmask) : 0;
         }
+        __syncthreads();
+      }
+      for (int i0 = kWaves; found == INT_MAX && i0 < DSPARK_MAX_RESIDUAL_PROPOSALS; i0 += kPropBatch) {
+        // uniforms of the batch: lane l holds proposal i0 + l % 16
+        const int ip = i0 + (lane & 15);
+        const double sx = __shfl(up0.x, ip & (kPropPre - 1)), sy = __shfl(up0.y, ip & (kPropPre - 1));
+        double2 pb = make_double2(sx, sy);
+        if (ip >= kPropPre) pb = proposal_uniforms(seed, a.round, k, ip);
+        // this group's proposal: i0 + 4 wave + grp
+        const int il = 4 * wave + grp;
+        const double q = __shfl(pb.x, il) * s.Z;
+        const double ua = __shfl(pb.y, il);
+        int lo = 0, hi = ntv;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_cum[mid] > q) hi = mid; else lo = mid + 1;
+        }
+        const int ts = lo < ntv ? lo : s_last;
+        const double ql = q - (ts > 0 ? s_cum[ts - 1] : 0.0);
+        const float mt = s_m[ts];
+        int v;
+        float tv;
+        col_draw<16>(trow, a.V, ts, mt, s.M, cf_f, cf, ql, v, tv);
+        const double lv = draft_logit_at<16, kBf16>(a, urow, prev, v);
+        const int i = i0 + 4 * wave + grp;
+        const bool pass = i < DSPARK_MAX_RESIDUAL_PROPOSALS && keep_test(ua, v, tv, lv);
+        const unsigned long long kept = __ballot(pass && (lane & 15) == 0);
+        const int gi = kept ? (__ffsll((long long)kept) - 1) >> 4 : -1;
+        const int tok = __shfl(v, gi < 0 ? 0 : 16 * gi);
+        agree(gi < 0 ? INT_MAX : i0 + 4 * wave + gi, tok, found, ytok);
       }
       if (threadIdx.x == 0) {
         a.accept_len[b] = k - 1;
-        if (found >= 0) {
+        if (found != INT_MAX) {
           a.out_tokens[(size_t)b * (g + 1) + k - 1] = ytok;
         } else {
           FallbackInfo f;
@@ -783,9 +890,20 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       }
       return true;
     };
-    static_assert(kRowsPerPhase == 2, "two block positions per phase");
-    if (position(0, rs[0], xk[0], prevk[0], pdxk[0], txk[0], lxk[0])) return;
-    if (k0 + 1 <= k1) position(1, rs[1], xk[1], prevk[1], pdxk[1], txk[1], lxk[1]);
+    // Rows in a rolled loop over a selected copy of the row state (one copy
+    // of the code; the selects stay in registers).
+#pragma unroll 1
+    for (int rr = 0; rr < kRowsPerPhase && k0 + rr <= k1; ++rr) {
+      const bool r1 = rr == 1;
+      RowScan cur;
+#pragma unroll
+      for (int j = 0; j < kLaneTiles; ++j) cur.p[j] = r1 ? rs[1].p[j] : rs[0].p[j];
+      cur.t0 = t0;
+      cur.t1 = t1;
+      if (position(rr, cur, r1 ? xk[1] : xk[0], r1 ? prevk[1] : prevk[0], r1 ? pdxk[1] : pdxk[0],
+                   r1 ? txk[1] : txk[0], r1 ? lxk[1] : lxk[0], r1 ? uak[1] : uak[0], r1 ? upk[1] : upk[0]))
+        return;
+    }
   }
 }
 
@@ -924,7 +1042,12 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
 
   {
     ProfScope prof(s, kProfVerifyInit);
-    hipLaunchKernelGGL(verify_init_kernel, dim3(1), dim3(kVThreads), 0, s, a, w);
+    // block 0: outputs and lists; then the uniforms; then the draft logits
+    const long long draws = (long long)a.B * (a.gamma + (a.gamma + 1) * kPropPre);
+    const long long draw_blocks = (draws + kVThreads - 1) / kVThreads;
+    const long long lx_blocks = ((long long)a.B * a.gamma + kVThreads / kWave - 1) / (kVThreads / kWave);
+    const int grid = greedy ? 1 : (int)(1 + draw_blocks + lx_blocks);
+    hipLaunchKernelGGL(verify_init_kernel, dim3(grid), dim3(kVThreads), 0, s, a, w, bf16 ? 1 : 0);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -160,6 +160,10 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
  * correction or bonus token is argmax target[b][n+1] ([R] "Common Questions
  * Answered").
  *
+ * W2T is optional (NULL to skip): W2 transposed, [V][r] in the weight dtype,
+ * as written by dspark_transpose_w2.  When given, p_d at a single token reads
+ * one contiguous row of W2T instead of r elements spread over W2; the results
+ * differ from the W2-only path only by the summation order of float64 sums.
  * Inputs draft_tokens / draft_prob are dspark_markov_draft's outputs.
  * Outputs:
  *   accept_len   int32   [B]          n in 0..gamma
@@ -169,13 +173,25 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
  *                                     k <= min(n+1, gamma), NaN after; NULL to skip
  * Workspace: dspark_workspace_size(DSPARK_OP_VERIFY, B, gamma, V, r).
  */
-dspark_status dspark_verify(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
+dspark_status dspark_verify(const float* U, const void* W1, const void* W2, const void* W2T, dspark_dtype wdtype,
                             const int32_t* x0, const int32_t* draft_tokens,
                             const float* draft_prob, const float* target_logits,
                             int B, int gamma, int V, int r, float temperature,
                             const uint64_t* seeds, uint64_t round,
                             int32_t* accept_len, int32_t* out_tokens, float* accept_prob,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_transpose_w2 -- W2T[v][j] = W2[j][v]: the Markov projection of [R]
+ * Eq. 5 stored vocabulary-major, for the single-token p_d evaluations of
+ * dspark_verify.  The weights are constant across rounds, so the copy is made
+ * once per model.
+ *
+ *   W2   [r][V] (bf16 or float32, per wdtype)
+ *   W2T  out, [V][r], same dtype; must not overlap W2
+ * 2 <= V < 2^31, 16 <= r <= 512 with r % 16 == 0.  Needs no workspace.
+ */
+dspark_status dspark_transpose_w2(const void* W2, dspark_dtype wdtype, int r, int V, void* W2T, hipStream_t stream);
 
 /*
  * dspark_survival -- prefix survival products a_{b,k} = prod_{i<=k} c_{b,i}

@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "dspark.h")
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
 FAKE = 0x100000          # non-null, 16-byte aligned, never dereferenced (validation fails first)
 MISALIGNED = 0x100004
+FAKE2 = 0x200000         # a second distinct fake pointer
 
 
 @pytest.fixture(scope="module")
@@ -85,10 +86,10 @@ def test_draft_rejects_bad_arguments(lib, kw, status):
 
 
 def _verify(lib, **kw):
-    a = dict(U=FAKE, W1=FAKE, W2=FAKE, wd=1, x0=FAKE, dt=FAKE, dp=FAKE, tgt=FAKE, B=4, gamma=4, V=1000, r=16,
-             T=1.0, seeds=FAKE, rnd=0, alen=FAKE, otok=FAKE, aprob=None, ws=FAKE, wsb=1 << 30)
+    a = dict(U=FAKE, W1=FAKE, W2=FAKE, W2T=None, wd=1, x0=FAKE, dt=FAKE, dp=FAKE, tgt=FAKE, B=4, gamma=4, V=1000,
+             r=16, T=1.0, seeds=FAKE, rnd=0, alen=FAKE, otok=FAKE, aprob=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
-    return lib.dspark_verify(a["U"], a["W1"], a["W2"], a["wd"], a["x0"], a["dt"], a["dp"], a["tgt"], a["B"],
+    return lib.dspark_verify(a["U"], a["W1"], a["W2"], a["W2T"], a["wd"], a["x0"], a["dt"], a["dp"], a["tgt"], a["B"],
                              a["gamma"], a["V"], a["r"], a["T"], a["seeds"], a["rnd"], a["alen"], a["otok"],
                              a["aprob"], a["ws"], a["wsb"], None)
 
@@ -96,7 +97,7 @@ def _verify(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(B=70000), INVALID), (dict(tgt=None), INVALID), (dict(alen=None), INVALID),
     (dict(dp=None), INVALID), (dict(tgt=MISALIGNED), INVALID), (dict(wd=9), UNSUPPORTED),
-    (dict(wsb=0), WORKSPACE), (dict(T=-0.5), INVALID),
+    (dict(wsb=0), WORKSPACE), (dict(T=-0.5), INVALID), (dict(W2T=MISALIGNED), INVALID),
 ])
 def test_verify_rejects_bad_arguments(lib, kw, status):
     assert _verify(lib, **kw) == status
@@ -114,6 +115,17 @@ def test_survival_rejects_bad_arguments(lib):
              None) == UNSUPPORTED
     assert s(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 8,
              None) == WORKSPACE
+
+
+def test_transpose_w2_rejects_bad_arguments(lib):
+    f = lib.dspark_transpose_w2
+    assert f(FAKE, 1, 8, 1000, FAKE2, None) == INVALID          # r below 16
+    assert f(FAKE, 1, 24, 1000, FAKE2, None) == INVALID         # r not a multiple of 16
+    assert f(FAKE, 1, 16, 1, FAKE2, None) == INVALID            # V below 2
+    assert f(None, 1, 16, 1000, FAKE2, None) == INVALID
+    assert f(FAKE, 1, 16, 1000, MISALIGNED, None) == INVALID
+    assert f(FAKE, 1, 16, 1000, FAKE, None) == INVALID          # in place
+    assert f(FAKE, 4, 16, 1000, FAKE2, None) == UNSUPPORTED
 
 
 def test_markov_bias_rejects_bad_arguments(lib):

@@ -58,6 +58,15 @@ def run_path(wl, reqs, label, check_verify=True, check_survival=True):
         lens = alen.cpu().numpy()
         say("[%s] verify: %d requests equal, %d exempt; mean accepted %.3f" % (label, nv, exv, lens.mean()))
         assert nv > 0
+        if wl.T > 0:  # the same decisions with the vocabulary-major copy of W2
+            W2T = dsp.transpose_w2(d.W2)
+            alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd, W2T=W2T)
+            torch.cuda.synchronize()
+            nv2, exv2 = compare_verify(vref, alen.cpu().numpy(), otok.cpu().numpy(), aprob.cpu().numpy(), vreq,
+                                       wl.T)
+            say("[%s] verify with W2T: %d requests equal, %d exempt" % (label, nv2, exv2))
+            assert nv2 > 0
+            del W2T
     if check_survival:
         cst, surv = dsp.survival(d.U, d.W1, d.W2, d.x0, tok, lse, d.tgt, wl.T)
         torch.cuda.synchronize()
@@ -151,6 +160,19 @@ def test_full_size_sampled_parity(name):
     reqs = sorted(set([0, wl.B - 1] + rng.choice(wl.B, size=4, replace=False).tolist()))
     run_path(wl, reqs, name)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,r,V", [(torch.bfloat16, 256, 151936), (torch.bfloat16, 48, 1001),
+                                        (torch.float32, 16, 130), (torch.float32, 512, 4099)])
+def test_transpose_w2_is_exact(dtype, r, V):
+    """W2T[v][j] == W2[j][v] bit for bit, ragged edges included."""
+    g = torch.Generator().manual_seed(r + V)
+    W2 = torch.randn((r, V), generator=g).to(dtype).cuda()
+    W2T = dsp.transpose_w2(W2)
+    torch.cuda.synchronize()
+    ref = W2.t().contiguous()
+    assert torch.equal(W2T.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       ref.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
 
 
 # ---------------------------------------------------------------------------
