@@ -25,7 +25,7 @@
 namespace dspark {
 
 constexpr int kVThreads = 256;
-constexpr int kRowsPerPhase = 2;   // block positions verified per phase
+constexpr int kPreRows = 2;        // block positions of a phase whose inputs the decision kernel loads up front
 constexpr int kPropPre = 16;       // residual proposals whose uniforms are drawn ahead, per position
 
 struct FallbackInfo {
@@ -38,25 +38,59 @@ struct FallbackInfo {
 };
 
 struct VerifyWs {
-  float2* tpart;        // [B][kRowsPerPhase][ntv] target tile summaries of the current phase
+  int lmax;             // longest phase (block positions)
+  float2* tpart;        // [B][lmax][ntv] target tile summaries of the current phase
   int* lists;           // [gamma + 2][B] request lists per phase (index ph = 1, 2, ...)
   int* counts;          // [gamma + 2]: counts[ph] phase sizes, counts[0] fallback count
   int* fb_list;         // [B]
   FallbackInfo* fb;     // [B] indexed by request
   double* fb_part;      // [B][ntv] residual mass per tile
-  float* txv;           // [B][kRowsPerPhase] target logit of the drafted token, current phase
+  float* txv;           // [B][lmax] target logit of the drafted token, current phase
   int* alive;           // [B] the phase in which the request is still undecided (0: none)
   double* lxv;          // [B][gamma] draft logit U[x_k] + W1[x_{k-1}] . W2[:, x_k] of every drafted token
   double* u_acc;        // [B][gamma] acceptance uniforms (stream 1)
   double2* u_prop;      // [B][gamma + 1][kPropPre] words 0, 1 of the first residual proposals (stream 2)
 };
 
+// Phase schedule of the block positions 1..gamma+1.  Sampling verifies
+// position 1 alone (about half of the requests end there), then positions 2
+// and 3, then the rest; greedy verification goes two positions at a time.
+// Each phase streams the target rows of the requests still undecided.
+struct Phases {
+  int n;
+  int k0[40], k1[40];
+};
+
+static Phases phase_schedule(int gamma, bool greedy) {
+  Phases p;
+  p.n = 0;
+  int k = 1;
+  const int last = gamma + 1;
+  while (k <= last) {
+    int len;
+    if (greedy) {
+      len = 2;
+    } else {
+      len = p.n == 0 ? 1 : (p.n == 1 ? 2 : last - k + 1);
+    }
+    p.k0[p.n] = k;
+    p.k1[p.n] = min(last, k + len - 1);
+    k = p.k1[p.n] + 1;
+    ++p.n;
+  }
+  return p;
+}
+
+// Longest phase of either schedule.
+static int max_phase_rows(int gamma) { return max(2, gamma + 1 - 3); }
+
 static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
   const int ntv = tiles_of(V, kTgtCols);
   char* p = reinterpret_cast<char*>(ws);
   VerifyWs w;
+  w.lmax = max_phase_rows(gamma);
   w.tpart = reinterpret_cast<float2*>(p);
-  p += align256((size_t)B * kRowsPerPhase * ntv * sizeof(float2));
+  p += align256((size_t)B * w.lmax * ntv * sizeof(float2));
   w.lists = reinterpret_cast<int*>(p);
   p += align256((size_t)(gamma + 2) * B * sizeof(int));
   w.counts = reinterpret_cast<int*>(p);
@@ -68,7 +102,7 @@ static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
   w.fb_part = reinterpret_cast<double*>(p);  // [B][ceil(V / kResCols)]
   p += align256((size_t)B * tiles_of(V, 256) * sizeof(double));
   w.txv = reinterpret_cast<float*>(p);
-  p += align256((size_t)B * kRowsPerPhase * sizeof(float));
+  p += align256((size_t)B * w.lmax * sizeof(float));
   w.alive = reinterpret_cast<int*>(p);
   p += align256((size_t)B * sizeof(int));
   w.lxv = reinterpret_cast<double*>(p);
@@ -82,10 +116,11 @@ static VerifyWs carve_verify(void* ws, int B, int gamma, int V) {
 size_t verify_workspace(int B, int gamma, int V, int r) {
   (void)r;
   const int ntv = tiles_of(V, kTgtCols);
-  return align256((size_t)B * kRowsPerPhase * ntv * sizeof(float2)) + align256((size_t)(gamma + 2) * B * sizeof(int)) +
+  const int lmax = max_phase_rows(gamma);
+  return align256((size_t)B * lmax * ntv * sizeof(float2)) + align256((size_t)(gamma + 2) * B * sizeof(int)) +
          align256((size_t)(gamma + 2) * sizeof(int)) + align256((size_t)B * sizeof(int)) +
          align256((size_t)B * sizeof(FallbackInfo)) + align256((size_t)B * tiles_of(V, 256) * sizeof(double)) +
-         align256((size_t)B * kRowsPerPhase * sizeof(float)) + align256((size_t)B * sizeof(int)) +
+         align256((size_t)B * lmax * sizeof(float)) + align256((size_t)B * sizeof(int)) +
          align256((size_t)B * gamma * sizeof(double)) + align256((size_t)B * gamma * sizeof(double)) +
          align256((size_t)B * (gamma + 1) * kPropPre * sizeof(double2));
 }
@@ -338,8 +373,8 @@ constexpr int kPrefixMax = 1024;  // target tiles per row on the fast decision p
 // as verify_decide_kernel below, with block-wide searches over the tile
 // summaries in global memory.
 template <bool kGreedy, bool kBf16>
-__global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(VerifyArgs a, VerifyWs w, int ph,
-                                                                         float cf_f, int ntv) {
+__global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(VerifyArgs a, VerifyWs w, int ph, int k0,
+                                                                         int k1, float cf_f, int ntv) {
   __shared__ PickScratch ps;
   __shared__ double sterm[kTgtCols];
   __shared__ double sw1[512];
@@ -347,13 +382,12 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
   __shared__ float sv[kVThreads / kWave];
   __shared__ int si[kVThreads / kWave];
   const int g = a.gamma;
-  const int k0 = 2 * ph - 1, k1 = min(2 * ph, g + 1);
   const int count = w.counts[ph];
   const double cf = (double)cf_f;
   for (int li = blockIdx.x; li < count; li += gridDim.x) {
     const int b = w.lists[(size_t)ph * a.B + li];
     for (int k = k0; k <= k1; ++k) {
-      const float2* P = w.tpart + ((size_t)b * kRowsPerPhase + (k - k0)) * ntv;
+      const float2* P = w.tpart + ((size_t)b * w.lmax + (k - k0)) * ntv;
       const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
       bool accepted = false;
       if constexpr (kGreedy) {
@@ -657,15 +691,14 @@ __device__ __noinline__ double2 proposal_uniforms(uint64_t seed, uint64_t round,
 }
 
 template <bool kGreedy, bool kBf16>
-__global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs w, int ph, float cf_f,
-                                                                 int ntv) {
+__global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs w, int ph, int k0, int k1,
+                                                                 float cf_f, int ntv) {
   constexpr int kWaves = kVThreads / kWave;
   __shared__ int s_idx[kWaves], s_tok[kWaves], s_last;
   __shared__ double s_cum[kPrefixMax];  // inclusive cumulative tile weights (later proposal batches)
   __shared__ float s_m[kPrefixMax];     // tile maxima
   const int g = a.gamma;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int k0 = kRowsPerPhase * (ph - 1) + 1, k1 = min(k0 + kRowsPerPhase - 1, g + 1);
   const int b = blockIdx.x;
   const int cs = (ntv + kWave - 1) / kWave;
   const int t0 = min(ntv, lane * cs), t1 = min(ntv, t0 + cs);
@@ -674,33 +707,41 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
   // is undecided in this phase, the summaries of the phase's rows, tokens,
   // p_d(x), t(x) and the draft logit of x, and the uniforms drawn ahead.
   const int alive = w.alive[b];
-  RowScan rs[kRowsPerPhase];
-  int xk[kRowsPerPhase], prevk[kRowsPerPhase];
-  float pdxk[kRowsPerPhase], txk[kRowsPerPhase];
-  double uak[kRowsPerPhase], lxk[kRowsPerPhase];
-  double2 upk[kRowsPerPhase];  // lane l: proposal l % 16 of the row (proposal 0 of row gamma+1: the bonus)
-#pragma unroll
-  for (int rr = 0; rr < kRowsPerPhase; ++rr) {
-    const float2* P = w.tpart + ((size_t)b * kRowsPerPhase + rr) * ntv;
-    rs[rr].t0 = t0;
-    rs[rr].t1 = t1;
+  // The inputs of one block position of the phase (row rr of the phase's
+  // summaries); positions past k1 are clamped so that every load stays in
+  // bounds (their values are not used).
+  struct RowIn {
+    int x, prev;
+    float pdx, tx;
+    double ua, lx;
+    double2 up;  // lane l: proposal l % 16 of the row (proposal 0 of row gamma+1: the bonus)
+  };
+  auto load_row = [&](int rr, RowScan& rsr, RowIn& in) {
+    const int rc = min(rr, w.lmax - 1);
+    const float2* P = w.tpart + ((size_t)b * w.lmax + rc) * ntv;
+    rsr.t0 = t0;
+    rsr.t1 = t1;
 #pragma unroll
     for (int j = 0; j < kLaneTiles; ++j) {
       const int t = t0 + j;
-      rs[rr].p[j] = P[t < t1 ? t : (t1 > 0 ? t1 - 1 : 0)];
+      rsr.p[j] = P[t < t1 ? t : (t1 > 0 ? t1 - 1 : 0)];
     }
-    const int kc = min(k0 + rr, g);  // clamped position: loads stay in bounds
-    xk[rr] = a.draft_tokens[(size_t)b * g + kc - 1];
+    const int kc = min(k0 + rr, g);
+    in.x = a.draft_tokens[(size_t)b * g + kc - 1];
     if constexpr (!kGreedy) {
-      prevk[rr] = kc == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + kc - 2];
-      pdxk[rr] = a.draft_prob[(size_t)b * g + kc - 1];
-      txk[rr] = w.txv[(size_t)b * kRowsPerPhase + rr];
-      lxk[rr] = w.lxv[(size_t)b * g + kc - 1];
-      uak[rr] = w.u_acc[(size_t)b * g + kc - 1];
+      in.prev = kc == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + kc - 2];
+      in.pdx = a.draft_prob[(size_t)b * g + kc - 1];
+      in.tx = w.txv[(size_t)b * w.lmax + rc];
+      in.lx = w.lxv[(size_t)b * g + kc - 1];
+      in.ua = w.u_acc[(size_t)b * g + kc - 1];
       const int kp = min(k0 + rr, g + 1);
-      upk[rr] = w.u_prop[((size_t)b * (g + 1) + kp - 1) * kPropPre + (lane & (kPropPre - 1))];
+      in.up = w.u_prop[((size_t)b * (g + 1) + kp - 1) * kPropPre + (lane & (kPropPre - 1))];
     }
-  }
+  };
+  RowScan rs[kPreRows];
+  RowIn rin[kPreRows];
+#pragma unroll
+  for (int rr = 0; rr < kPreRows; ++rr) load_row(rr, rs[rr], rin[rr]);
   if (alive != ph) return;
 
   // accepted through the last position of the phase: undecided in the next
@@ -712,9 +753,9 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
     }
   };
 
-  if constexpr (kGreedy) {
+  if constexpr (kGreedy) {  // greedy phases have at most kPreRows positions
 #pragma unroll
-    for (int rr = 0; rr < kRowsPerPhase; ++rr) {
+    for (int rr = 0; rr < kPreRows; ++rr) {
       const int k = k0 + rr;
       if (k > k1) break;
       float bv = -__builtin_inff();
@@ -725,10 +766,10 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       wave_argmax(bv, bi);
       bool accepted = false;
       if (k <= g) {
-        accepted = bi == xk[rr];
+        accepted = bi == rin[rr].x;
         if (threadIdx.x == 0) {
           if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = accepted ? 1.0f : 0.0f;
-          a.out_tokens[(size_t)b * (g + 1) + k - 1] = accepted ? xk[rr] : bi;
+          a.out_tokens[(size_t)b * (g + 1) + k - 1] = accepted ? rin[rr].x : bi;
           if (!accepted) a.accept_len[b] = k - 1;
         }
       } else if (threadIdx.x == 0) {
@@ -891,18 +932,23 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       return true;
     };
     // Rows in a rolled loop over a selected copy of the row state (one copy
-    // of the code; the selects stay in registers).
+    // of the code; the selects stay in registers); positions past the first
+    // kPreRows of the phase load their inputs when they are reached.
 #pragma unroll 1
-    for (int rr = 0; rr < kRowsPerPhase && k0 + rr <= k1; ++rr) {
-      const bool r1 = rr == 1;
+    for (int rr = 0; k0 + rr <= k1; ++rr) {
       RowScan cur;
+      RowIn in;
+      if (rr < kPreRows) {
+        const bool r1 = rr == 1;
 #pragma unroll
-      for (int j = 0; j < kLaneTiles; ++j) cur.p[j] = r1 ? rs[1].p[j] : rs[0].p[j];
-      cur.t0 = t0;
-      cur.t1 = t1;
-      if (position(rr, cur, r1 ? xk[1] : xk[0], r1 ? prevk[1] : prevk[0], r1 ? pdxk[1] : pdxk[0],
-                   r1 ? txk[1] : txk[0], r1 ? lxk[1] : lxk[0], r1 ? uak[1] : uak[0], r1 ? upk[1] : upk[0]))
-        return;
+        for (int j = 0; j < kLaneTiles; ++j) cur.p[j] = r1 ? rs[1].p[j] : rs[0].p[j];
+        cur.t0 = t0;
+        cur.t1 = t1;
+        in = r1 ? rin[1] : rin[0];
+      } else {
+        load_row(rr, cur, in);
+      }
+      if (position(rr, cur, in.x, in.prev, in.pdx, in.tx, in.lx, in.ua, in.up)) return;
     }
   }
 }
@@ -1018,7 +1064,7 @@ __global__ __launch_bounds__(kVThreads) void residual_select_kernel(VerifyArgs a
     } else {
       // No residual mass (possible only through rounding): draw from p_t.
       DecideCtx c;
-      c.P = w.tpart + ((size_t)b * kRowsPerPhase + f.phase_row) * ntv;
+      c.P = w.tpart + ((size_t)b * w.lmax + f.phase_row) * ntv;
       c.trow = a.target + ((size_t)b * (g + 1) + (f.j - 1)) * (size_t)a.V;
       c.M = (float)f.M;
       c.cf = (double)cf_f;
@@ -1053,16 +1099,17 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   const int dgrid = a.B < 2048 ? a.B : 2048;
-  const int nph = (a.gamma + 1 + kRowsPerPhase - 1) / kRowsPerPhase;
-  for (int ph = 1; ph <= nph; ++ph) {
-    const int k0 = kRowsPerPhase * (ph - 1) + 1;
+  const Phases sched = phase_schedule(a.gamma, greedy);
+  for (int pi = 0; pi < sched.n; ++pi) {
+    const int ph = pi + 1;
+    const int k0 = sched.k0[pi], k1 = sched.k1[pi];
     TStatsArgs t = {};
     t.target = a.target;
     t.list = w.lists + (size_t)ph * a.B;
     t.count = w.counts + ph;
     t.kk0 = k0 - 1;
-    t.rows_per_req = min(kRowsPerPhase, a.gamma + 2 - k0);
-    t.orow_stride = kRowsPerPhase;
+    t.rows_per_req = k1 - k0 + 1;
+    t.orow_stride = w.lmax;
     t.gamma = a.gamma;
     t.V = a.V;
     t.ntv = ntv;
@@ -1073,24 +1120,26 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
     e = launch_target_stats(t, greedy, a.B * t.rows_per_req, s);
     if (e != hipSuccess) return e;
     ProfScope prof(s, kProfVerifyDecide);
-    if (ntv <= kPrefixMax) {  // one workgroup per listed request
+    if (ntv <= kPrefixMax) {  // one workgroup per request (those not undecided in this phase exit)
       if (greedy) {
-        hipLaunchKernelGGL((verify_decide_kernel<true, true>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, cf, ntv);
-      } else if (bf16) {
-        hipLaunchKernelGGL((verify_decide_kernel<false, true>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, cf, ntv);
-      } else {
-        hipLaunchKernelGGL((verify_decide_kernel<false, false>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, cf,
+        hipLaunchKernelGGL((verify_decide_kernel<true, true>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1, cf,
                            ntv);
+      } else if (bf16) {
+        hipLaunchKernelGGL((verify_decide_kernel<false, true>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1,
+                           cf, ntv);
+      } else {
+        hipLaunchKernelGGL((verify_decide_kernel<false, false>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1,
+                           cf, ntv);
       }
     } else if (greedy) {
-      hipLaunchKernelGGL((verify_decide_generic_kernel<true, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, cf,
-                         ntv);
+      hipLaunchKernelGGL((verify_decide_generic_kernel<true, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, k0,
+                         k1, cf, ntv);
     } else if (bf16) {
       hipLaunchKernelGGL((verify_decide_generic_kernel<false, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph,
-                         cf, ntv);
+                         k0, k1, cf, ntv);
     } else {
       hipLaunchKernelGGL((verify_decide_generic_kernel<false, false>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph,
-                         cf, ntv);
+                         k0, k1, cf, ntv);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

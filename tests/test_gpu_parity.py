@@ -142,6 +142,39 @@ def test_small_parity(name, kw):
     run_path(wl, list(range(wl.B)), name)
 
 
+def test_long_phase_high_acceptance():
+    """Target rows equal to the draft logits along the drafted prefix: every
+    position is accepted, so every request runs through the last phase's
+    positions past the first two (inputs loaded when reached) to the bonus."""
+    V, r, gamma, B, T = 1000, 16, 7, 64, 1.0
+    rng = np.random.default_rng(21)
+    U = (rng.standard_normal((B, gamma, V)) * 2.0).astype(np.float32)
+    W1 = (rng.standard_normal((V, r)) * 0.3).astype(np.float32)
+    W2 = (rng.standard_normal((r, V)) * 0.3).astype(np.float32)
+    x0 = rng.integers(0, V, size=B).astype(np.int32)
+    seeds = workloads.request_seeds(9, B)
+    W1d, W2d = W1.astype(np.float64), W2.astype(np.float64)
+    ref_d = oracle.markov_draft(U, W1d, W2d, x0, T, seeds, 3)
+    tgt = np.empty((B, gamma + 1, V), dtype=np.float32)
+    prev = x0.copy()
+    for k in range(gamma):
+        tgt[:, k] = (U[:, k].astype(np.float64) + W1d[prev] @ W2d).astype(np.float32)
+        prev = ref_d["tokens"][:, k]
+    tgt[:, gamma] = rng.standard_normal((B, V)).astype(np.float32)
+    dU, dW1, dW2 = torch.from_numpy(U).cuda(), torch.from_numpy(W1).cuda(), torch.from_numpy(W2).cuda()
+    dx0, dseeds = torch.from_numpy(x0).cuda(), seeds_tensor(seeds)
+    tok, prob, lse = dsp.markov_draft(dU, dW1, dW2, dx0, T, dseeds, 3)
+    tok_h = tok.cpu().numpy()
+    n, ex, whole = compare_draft(ref_d, tok_h, prob.cpu().numpy(), lse.cpu().numpy(), list(range(B)), T)
+    alen, otok, aprob = dsp.verify(dU, dW1, dW2, dx0, tok, prob, torch.from_numpy(tgt).cuda(), T, dseeds, 3)
+    reqs = sorted(whole)
+    vref = oracle.verify(U, W1d, W2d, x0, tok_h, tgt, T, seeds, 3, requests=reqs)
+    nv, exv = compare_verify(vref, alen.cpu().numpy(), otok.cpu().numpy(), aprob.cpu().numpy(), reqs, T)
+    lens = alen.cpu().numpy()
+    say("[long-phase] %d requests equal, %d exempt, mean accepted %.3f" % (nv, exv, lens.mean()))
+    assert nv > 0 and (lens[reqs] == gamma).mean() > 0.9
+
+
 def test_tiny_fp32_temperature_07():
     wl = workloads.make("tiny_v1000_b4", T=0.7)
     run_path(wl, list(range(wl.B)), "tiny-T0.7")
