@@ -258,7 +258,9 @@ __device__ __forceinline__ void pipe_block(int ngroups, int nslices, int& group,
 }
 
 template <int kMode>
-__global__ __launch_bounds__(kTileThreads, 2) void tile_pipe_kernel(TileArgs a, int nslices) {
+__global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void tile_pipe_kernel(TileArgs a,
+                                                                                               int nslices) {
+  constexpr bool kOv = kMode == kModeOverlap;  // also streams the target rows
   extern __shared__ __align__(16) unsigned char smem[];
   int group, slice;
   pipe_block(a.ngroups, nslices, group, slice);
@@ -279,6 +281,16 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_pipe_kernel(TileArgs a, 
   const int R = group * kRowsPerGroup + 32 * wave + n;
   const size_t rs = a.kper == 1 ? (size_t)a.gamma * V : V;
   const float* urow = a.U + (size_t)R * rs + (a.kper == 1 ? (size_t)a.k0 * V : 0) + 4 * hh;
+  // overlap mode (rows b * gamma + kk, one per block position): the target row
+  // of (b, kk) and the draft / target log2 normalisers of the row
+  const float* tgrow = nullptr;
+  float ld2 = 0.0f, lt2 = 0.0f;
+  if constexpr (kOv) {
+    const RowInfo ri = row_info(a, R);
+    tgrow = a.target + ((size_t)ri.b * (a.gamma + 1) + ri.kk) * V + 4 * hh;
+    ld2 = a.lse_d[(size_t)ri.b * a.gamma + ri.kk] * kLog2e;
+    lt2 = a.lt2[R];
+  }
 
   // Byte offset of this lane's 16-byte W2 chunk in the first DMA of a half:
   // row 64 wave + l / 8 (8 rows per instruction), slot l % 8 of the permuted
@@ -291,11 +303,17 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_pipe_kernel(TileArgs a, 
   // (each wave 64 rows, 8 rows per instruction): 16 vector memory
   // instructions per wave, in this order (the DMA statements are volatile and
   // clobber memory, so the loads cannot be moved past them).
-  auto issue = [&](int c, unsigned char* buf, float4 (&u)[2][4]) {
+  auto issue = [&](int c, unsigned char* buf, float4 (&u)[2][4], float4 (&t)[2][4]) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) u[nb][q] = *reinterpret_cast<const float4*>(urow + c + 32 * nb + 8 * q);
+    if constexpr (kOv) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[nb][q] = *reinterpret_cast<const float4*>(tgrow + c + 32 * nb + 8 * q);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int rbase = 64 * wave + 8 * i;
@@ -304,7 +322,8 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_pipe_kernel(TileArgs a, 
   };
 
   float4 uA[2][4], uB[2][4];
-  issue(t_begin * kTileCols, buf0, uA);
+  float4 tA[2][4], tB[2][4];  // target values (overlap mode only)
+  issue(t_begin * kTileCols, buf0, uA, tA);
 
   // B operand: row R of E = W1[prev], k-chunk hh of each 16-wide k step.
   const int prev = prev_token(a, row_info(a, R));
@@ -367,9 +386,18 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_pipe_kernel(TileArgs a, 
     __builtin_amdgcn_sched_barrier(0);  // keep the previous half's work before the wait
     wait_vmem<0>();
     __syncthreads();
-    issue(c0 + kHalfCols, buf1, uB);
+    issue(c0 + kHalfCols, buf1, uB, tB);
     logits(buf0, uA, x);
-    if constexpr (kMode == kModeSample) {
+    if constexpr (kOv) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sum += fminf(fast_exp2(x[nb][i] * a.cf - ld2), fast_exp2(comp(tA[nb][i >> 2], i & 3) * a.cf - lt2));
+      s0 = sum;
+      asm volatile("" : "+v"(s0));
+    } else if constexpr (kMode == kModeSample) {
       float m = -__builtin_inff();
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
@@ -404,9 +432,18 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_pipe_kernel(TileArgs a, 
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem<0>();
     __syncthreads();
-    if (tile + 1 < t_end) issue(c0 + kTileCols, buf0, uA);
+    if (tile + 1 < t_end) issue(c0 + kTileCols, buf0, uA, tA);
     logits(buf1, uB, x);
-    if constexpr (kMode == kModeSample) {
+    if constexpr (kOv) {
+      float sum = s0;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sum += fminf(fast_exp2(x[nb][i] * a.cf - ld2), fast_exp2(comp(tB[nb][i >> 2], i & 3) * a.cf - lt2));
+      sum += __shfl_xor(sum, 32);
+      if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(sum, 0.0f);
+    } else if constexpr (kMode == kModeSample) {
       float m = -__builtin_inff();
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
@@ -676,14 +713,14 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
   const int full_groups = a.nrows / kRowsPerGroup;
   const int full_tiles = (a.V & 3) == 0 ? a.V / kTileCols : 0;
   // (The pipelined kernel addresses W2 with 32-bit byte offsets: 2 r V < 2^32.)
-  const bool fast = kBf16 && (kMode == kModeSample || kMode == kModeGreedy) && a.r == kFastR &&
+  const bool fast = kBf16 && (kMode == kModeSample || kMode == kModeGreedy || kMode == kModeOverlap) && a.r == kFastR &&
                     (a.kper == 1 || a.kper == a.gamma) && full_groups > 0 && full_tiles > 0 &&
                     (size_t)2 * kFastR * (size_t)a.V < ((size_t)1 << 32);
   if (!fast) {
     launch_tiles<kMode, kBf16>(a, 0, a.nrows, 0, a.ntiles, s);
     return hipGetLastError();
   }
-  if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
+  if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy || kMode == kModeOverlap)) {
     TileArgs g = a;
     g.ngroups = full_groups;
     g.rows_per_group = kRowsPerGroup;
@@ -691,9 +728,10 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
     g.row_end = full_groups * kRowsPerGroup;
     g.tile_begin = 0;
     g.tile_count = full_tiles;
-    // Two resident workgroups per CU (64 KB of LDS each); the column slices
-    // of every row group together fill them once.
-    int nslices = 2 * compute_units() / full_groups;
+    // Two resident workgroups per CU (64 KB of LDS each; one in overlap mode,
+    // whose waves also hold the target values); the column slices of every
+    // row group together fill them once.
+    int nslices = (kMode == kModeOverlap ? 1 : 2) * compute_units() / full_groups;
     if (nslices >= 8) nslices &= ~7;
     nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
     const size_t lds = 2 * (size_t)kHalfBytes;
