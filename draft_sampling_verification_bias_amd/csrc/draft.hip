@@ -34,6 +34,7 @@ struct SelectArgs {
   int32_t* tokens;
   float* prob;
   float* lse;
+  double* u_next;  // [2][B] stream-0 uniforms drawn one position ahead
 };
 
 template <bool kBf16>
@@ -262,6 +263,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
   }
   const int prev = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
   const uint64_t seed = a.seeds[b];
+  const double u_pre = a.k == 1 ? 0.0 : a.u_next[(size_t)((a.k - 1) & 1) * a.B + b];
   if (prev < 0 || prev >= a.V) {  // invalid anchor or earlier position: propagate
     if (threadIdx.x == 0) {
       a.tokens[out] = -1;
@@ -280,14 +282,19 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
   auto weight = [&](const float2& p) -> double {
     return p.x == -__builtin_inff() ? 0.0 : (double)p.y * (double)fast_exp2((p.x - M) * a.cf);
   };
+  double pw[kWavePer];  // the lane's tile weights, kept for the owner's search
   double local = 0.0;
 #pragma unroll
-  for (int j = 0; j < kWavePer; ++j)
-    if (t0 + j < t1) local += weight(pr[j]);
+  for (int j = 0; j < kWavePer; ++j) {
+    pw[j] = t0 + j < t1 ? weight(pr[j]) : 0.0;
+    local += pw[j];
+  }
   const double incl = wave_inclusive_scan(local);
   const double excl = incl - local;
   const double total = __shfl(incl, kWave - 1);
-  const double u = unit_uniform(draw_block(seed, a.round, a.k, kStreamDraft, 0).w[0]);
+  // the stream-0 uniform of this position: drawn by the previous position's
+  // select (see below), or here at the first position
+  const double u = a.k == 1 ? unit_uniform(draw_block(seed, a.round, 1, kStreamDraft, 0).w[0]) : u_pre;
   const double q = u * total;
   const unsigned long long cross = __ballot(local > 0.0 && incl > q);
   const unsigned long long pos = __ballot(local > 0.0);
@@ -302,7 +309,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
 #pragma unroll
     for (int j = 0; j < kWavePer; ++j) {
       if (t0 + j < t1) {
-        const double w = weight(pr[j]);
+        const double w = pw[j];
         if (w > 0.0) {
           lastpos = t0 + j;
           lastbase = cum;
@@ -373,6 +380,11 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
         }
       }
     }
+    if (i0 == 0 && threadIdx.x == 0 && a.k < a.gamma) {
+      // the next position's uniform, drawn while the loads above are in
+      // flight (two buffers: the next select reads one, writes the other)
+      a.u_next[(size_t)(a.k & 1) * a.B + b] = unit_uniform(draw_block(seed, a.round, a.k + 1, kStreamDraft, 0).w[0]);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float ei = i0 + i < nk ? e[i] : 0.0f;
@@ -431,7 +443,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
 size_t draft_workspace(int B, int gamma, int V, int r) {
   (void)gamma;
   (void)r;
-  return align256((size_t)B * tiles_of(V, kTileCols) * sizeof(float2));
+  return align256((size_t)B * tiles_of(V, kTileCols) * sizeof(float2)) + align256((size_t)2 * B * sizeof(double));
 }
 
 template <bool kGreedy, bool kBf16>
@@ -481,6 +493,8 @@ hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s) {
   sa.tokens = a.tokens;
   sa.prob = a.prob;
   sa.lse = a.lse;
+  sa.u_next = reinterpret_cast<double*>(reinterpret_cast<char*>(a.ws) +
+                                        align256((size_t)a.B * ntiles * sizeof(float2)));
 
   for (int k = 1; k <= a.gamma; ++k) {
     t.k0 = k - 1;
