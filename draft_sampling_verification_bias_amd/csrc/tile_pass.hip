@@ -199,10 +199,11 @@ __device__ __forceinline__ bool block_tile(const TileArgs& a, int& tile, int& gr
 }
 
 // ---------------------------------------------------------------------------
-// Fast path of the sample and argmax modes: bf16 weights, r = 256, full
-// 128-column tiles of a vocabulary whose size is a multiple of 4, full 128-row
-// groups, and base-logit rows at a constant stride (one block position of
-// every request, or all positions of consecutive requests).
+// Fast path of the sample, argmax and overlap modes: bf16 weights, r = 256,
+// full 128-column tiles of a vocabulary whose size is a multiple of 4, groups
+// of 128 rows (the last one may be partial), and base-logit rows at a
+// constant stride (one block position of every request, or all positions of
+// consecutive requests).
 //
 // A workgroup owns one 128-row group and a contiguous range of tiles, walked
 // as 64-column halves: while the MFMA and the epilogue of one half run, the
@@ -278,18 +279,22 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
 
   // Lane (n, hh) owns request row R; in a half starting at column c it holds
   // columns c + 32 nb + 8 q + 4 hh + 0..3 (nb = 0, 1; q = 0..3).
+  // Rows at or past row_end (the last group may be partial) read a valid row
+  // instead, are given no previous token and write nothing.
   const int R = group * kRowsPerGroup + 32 * wave + n;
+  const bool rowok = R < a.row_end;
+  const int Rc = rowok ? R : a.row_end - 1;
   const size_t rs = a.kper == 1 ? (size_t)a.gamma * V : V;
-  const float* urow = a.U + (size_t)R * rs + (a.kper == 1 ? (size_t)a.k0 * V : 0) + 4 * hh;
+  const float* urow = a.U + (size_t)Rc * rs + (a.kper == 1 ? (size_t)a.k0 * V : 0) + 4 * hh;
   // overlap mode (rows b * gamma + kk, one per block position): the target row
   // of (b, kk) and the draft / target log2 normalisers of the row
   const float* tgrow = nullptr;
   float ld2 = 0.0f, lt2 = 0.0f;
   if constexpr (kOv) {
-    const RowInfo ri = row_info(a, R);
+    const RowInfo ri = row_info(a, Rc);
     tgrow = a.target + ((size_t)ri.b * (a.gamma + 1) + ri.kk) * V + 4 * hh;
     ld2 = a.lse_d[(size_t)ri.b * a.gamma + ri.kk] * kLog2e;
-    lt2 = a.lt2[R];
+    lt2 = a.lt2[Rc];
   }
 
   // Byte offset of this lane's 16-byte W2 chunk in the first DMA of a half:
@@ -326,8 +331,8 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
   issue(t_begin * kTileCols, buf0, uA, tA);
 
   // B operand: row R of E = W1[prev], k-chunk hh of each 16-wide k step.
-  const int prev = prev_token(a, row_info(a, R));
-  const bool ok = (unsigned)prev < (unsigned)a.V;
+  const int prev = prev_token(a, row_info(a, Rc));
+  const bool ok = rowok && (unsigned)prev < (unsigned)a.V;
   const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
   bf16x8 ev[16];
 #pragma unroll
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
         for (int i = 0; i < 16; ++i)
           sum += fminf(fast_exp2(x[nb][i] * a.cf - ld2), fast_exp2(comp(tB[nb][i >> 2], i & 3) * a.cf - lt2));
       sum += __shfl_xor(sum, 32);
-      if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(sum, 0.0f);
+      if (hh == 0 && rowok) a.partials[(size_t)R * a.ntiles + tile] = make_float2(sum, 0.0f);
     } else if constexpr (kMode == kModeSample) {
       float m = -__builtin_inff();
 #pragma unroll
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
       merge(m, sum, m0, s0);
       const float om = __shfl_xor(m, 32), os = __shfl_xor(sum, 32);
       merge(m, sum, om, os);
-      if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(m, sum);
+      if (hh == 0 && rowok) a.partials[(size_t)R * a.ntiles + tile] = make_float2(m, sum);
     } else {
       float bv = -__builtin_inff();
       int bpos = 0;
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
       const float ov = __shfl_xor(bvm, 32);
       const int oi = __shfl_xor(b0, 32);
       argmax_merge(bvm, b0, ov, oi);
-      if (hh == 0) a.partials[(size_t)R * a.ntiles + tile] = make_float2(bvm, __int_as_float(b0));
+      if (hh == 0 && rowok) a.partials[(size_t)R * a.ntiles + tile] = make_float2(bvm, __int_as_float(b0));
     }
   }
 }
@@ -710,11 +715,11 @@ static void launch_tiles(const TileArgs& a, int row_begin, int row_end, int tile
 template <int kMode, bool kBf16>
 static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
   ProfScope prof(s, kProfTileSample + kMode);
-  const int full_groups = a.nrows / kRowsPerGroup;
+  const int groups = (a.nrows + kRowsPerGroup - 1) / kRowsPerGroup;  // the last one may be partial
   const int full_tiles = (a.V & 3) == 0 ? a.V / kTileCols : 0;
   // (The pipelined kernel addresses W2 with 32-bit byte offsets: 2 r V < 2^32.)
   const bool fast = kBf16 && (kMode == kModeSample || kMode == kModeGreedy || kMode == kModeOverlap) && a.r == kFastR &&
-                    (a.kper == 1 || a.kper == a.gamma) && full_groups > 0 && full_tiles > 0 &&
+                    (a.kper == 1 || a.kper == a.gamma) && full_tiles > 0 &&
                     (size_t)2 * kFastR * (size_t)a.V < ((size_t)1 << 32);
   if (!fast) {
     launch_tiles<kMode, kBf16>(a, 0, a.nrows, 0, a.ntiles, s);
@@ -722,25 +727,23 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
   }
   if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy || kMode == kModeOverlap)) {
     TileArgs g = a;
-    g.ngroups = full_groups;
+    g.ngroups = groups;
     g.rows_per_group = kRowsPerGroup;
     g.row_begin = 0;
-    g.row_end = full_groups * kRowsPerGroup;
+    g.row_end = a.nrows;
     g.tile_begin = 0;
     g.tile_count = full_tiles;
     // Two resident workgroups per CU (64 KB of LDS each; one in overlap mode,
     // whose waves also hold the target values); the column slices of every
     // row group together fill them once.
-    int nslices = (kMode == kModeOverlap ? 1 : 2) * compute_units() / full_groups;
+    int nslices = (kMode == kModeOverlap ? 1 : 2) * compute_units() / groups;
     if (nslices >= 8) nslices &= ~7;
     nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
     const size_t lds = 2 * (size_t)kHalfBytes;
-    hipLaunchKernelGGL((tile_pipe_kernel<kMode>), dim3(full_groups * nslices), dim3(kTileThreads), lds, s, g,
-                       nslices);
+    hipLaunchKernelGGL((tile_pipe_kernel<kMode>), dim3(groups * nslices), dim3(kTileThreads), lds, s, g, nslices);
   }
-  // Remainders: rows past the full groups (all tiles), the partial last tile.
-  launch_tiles<kMode, kBf16>(a, full_groups * kRowsPerGroup, a.nrows, 0, a.ntiles, s);
-  launch_tiles<kMode, kBf16>(a, 0, full_groups * kRowsPerGroup, full_tiles, a.ntiles - full_tiles, s);
+  // The partial last tile, all rows.
+  launch_tiles<kMode, kBf16>(a, 0, a.nrows, full_tiles, a.ntiles - full_tiles, s);
   return hipGetLastError();
 }
 
