@@ -490,6 +490,243 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide variant of the fast path for launches of at least 192 rows (sample and
+// argmax modes).  One 8-wave workgroup per CU owns a group of 256 rows, so a
+// W2 half block staged in LDS serves twice as many rows, and the W2 blocks go
+// through a ring of three LDS buffers.  Step j (one 64-column half):
+//   wait until W2(j) and U(j) have landed (the loads of half j + 1 stay in
+//   flight), barrier, DMA W2(j + 2) into the buffer of half j - 1,
+//   MFMA and epilogue of half j,
+//   load U(j + 2) into the register set of half j.
+// The MFMA and epilogue of a half thus run with the loads of the next two
+// halves in flight; the two-buffer kernel waits for all of its loads at every
+// half and so leaves the memory system idle while it computes.
+//
+// Wait counts.  Per wave a half is kRingDma DMA instructions (which the
+// compiler does not see) and 8 U loads (which it does), issued in the order
+// W2(j+2) ... U(j+2), so at the start of step j the operations issued after
+// U(j) are W2(j+1) and U(j+1) (when half j+1 exists) and at most one summary
+// store; a vmcnt of kRingDma + 8 lets exactly those stay in flight (a store
+// among them only makes the wait one operation stricter).  The compiler adds
+// its own waits for the U registers from the loads it sees; those are always
+// sufficient and at most somewhat stricter.
+// ---------------------------------------------------------------------------
+constexpr int kRingWaves = 8;
+constexpr int kRingThreads = kWave * kRingWaves;
+constexpr int kRingRows = 32 * kRingWaves;            // rows per group
+constexpr int kRingStages = 3;                        // W2 buffers in LDS
+constexpr int kRingKPerWave = kFastR / kRingWaves;    // W2 rows k staged per wave
+constexpr int kRingDma = kRingKPerWave / 8;           // DMA instructions per wave per half
+constexpr int kRingWait = kRingDma + 8;               // ops of one later half
+
+template <int kMode>
+__global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int nslices) {
+  static_assert(kMode == kModeSample || kMode == kModeGreedy, "ring kernel modes");
+  extern __shared__ __align__(16) unsigned char smem[];
+  int group, slice;
+  pipe_block(a.ngroups, nslices, group, slice);
+  const int t_begin = a.tile_begin + (int)((long long)slice * a.tile_count / nslices);
+  const int t_end = a.tile_begin + (int)((long long)(slice + 1) * a.tile_count / nslices);
+  if (t_begin >= t_end) return;
+  const int H = 2 * (t_end - t_begin);  // halves of this workgroup
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int n = lane & 31, hh = lane >> 5;
+  const size_t V = (size_t)a.V;
+  const uint16_t* W2 = reinterpret_cast<const uint16_t*>(a.W2);
+
+  // Lane (n, hh) of wave w owns request row R = 256 group + 32 w + n and, in a
+  // half starting at column c, columns c + 32 nb + 8 q + 4 hh + 0..3.  Rows at
+  // or past row_end read a valid row, get no previous token and write nothing.
+  const int R = group * kRingRows + 32 * wave + n;
+  const bool rowok = R < a.row_end;
+  const int Rc = rowok ? R : a.row_end - 1;
+  const size_t rs = a.kper == 1 ? (size_t)a.gamma * V : V;
+  const float* urow = a.U + (size_t)Rc * rs + (a.kper == 1 ? (size_t)a.k0 * V : 0) + 4 * hh;
+
+  // DMA lane mapping: wave w stages rows k = 32 w .. 32 w + 31, 8 per
+  // instruction, lane l the 16-byte slot l % 8 of row 32 w + 8 i + l / 8 (the
+  // XOR permutation depends on (k / 2) mod 2 only, the same for every i).
+  const int w2row = kRingKPerWave * wave + (lane >> 3);
+  const uint32_t w2off = ((uint32_t)w2row * (uint32_t)V + 8u * (uint32_t)w2h_slot(w2row, lane & 7)) * 2u;
+  const int c00 = t_begin * kTileCols;
+  auto bufp = [&](int j) -> unsigned char* { return smem + (size_t)(j % kRingStages) * kHalfBytes; };
+  auto issue_w2 = [&](int j) {
+    unsigned char* buf = bufp(j);
+    const int c = c00 + kHalfCols * j;
+#pragma unroll
+    for (int i = 0; i < kRingDma; ++i) {
+      const int rbase = kRingKPerWave * wave + 8 * i;
+      dma16(W2 + c, w2off + (uint32_t)(i * 16) * (uint32_t)V, buf + (size_t)rbase * 128);
+    }
+  };
+  auto issue_u = [&](int j, float4 (&u)[2][4]) {
+    const int c = c00 + kHalfCols * j;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[nb][q] = *reinterpret_cast<const float4*>(urow + c + 32 * nb + 8 * q);
+  };
+
+  // Issue order: W2(0), U(0), the previous token (waiting for it also waits
+  // for half 0, which step 0 needs anyway), the W1 row, W2(1), U(1).
+  float4 uA[2][4], uB[2][4];
+  issue_w2(0);
+  issue_u(0, uA);
+  const int prev = prev_token(a, row_info(a, Rc));
+  const bool ok = rowok && (unsigned)prev < (unsigned)a.V;
+  const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
+  bf16x8 ev[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ev[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
+  if (!ok) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ev[j][e] = (__bf16)0.0f;
+  }
+  issue_w2(1);
+  issue_u(1, uB);
+
+  const int trow = 8 * hh + ((lane & 15) >> 2);             // + 16 j + 4 h
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 nb
+  auto logits = [&](const unsigned char* buf, const float4 (&u)[2][4], float (&x)[2][16]) {
+    f32x16 acc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nb][i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        bf16x8 av;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 16 * j + 4 * h + trow;
+          const int col = 32 * nb + tcol;
+          const int addr = row * 128 + w2h_slot(row, col >> 3) * 16 + (col & 7) * 2;
+          const bf16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + addr));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[4 * h + e] = t[e];
+        }
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[j], acc[nb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[nb][i] = acc[nb][i] + comp(u[nb][i >> 2], i & 3);
+  };
+
+  // One tile = steps j, j + 1.
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    const bool more = tile + 1 < t_end;  // halves j + 2, j + 3 exist
+    const int j = 2 * (tile - t_begin);
+    const int c0 = tile * kTileCols;
+    float x[2][16];
+    float m0, s0, bv0;
+    int bp0;
+
+    // first half: step j (uA); half j + 1 always exists
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem<kRingWait>();
+    __syncthreads();
+    if (more) issue_w2(j + 2);
+    logits(bufp(j), uA, x);
+    if constexpr (kMode == kModeSample) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, x[nb][i]);
+      const float mc = m * a.cf;
+      float sum = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(x[nb][i], a.cf, -mc));
+      m0 = m;
+      s0 = m == -__builtin_inff() ? 0.0f : sum;
+      asm volatile("" : "+v"(m0), "+v"(s0));
+    } else {
+      float bv = -__builtin_inff();
+      int bpos = 0;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (x[nb][i] > bv) {  // ascending columns: the lowest index wins ties
+            bv = x[nb][i];
+            bpos = nb * 16 + i;
+          }
+      bv0 = bv;
+      bp0 = bpos;
+      asm volatile("" : "+v"(bv0), "+v"(bp0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // past the last half the loads are still issued (of half j again, whose
+    // lines are still cached, values unused): the loop keeps one shape and
+    // every path carries the same loads
+    issue_u(more ? j + 2 : j, uA);
+
+    // second half: step j + 1 (uB)
+    __builtin_amdgcn_sched_barrier(0);
+    // after U(j + 1): W2(j + 2) if it exists, then the eight loads into uA
+    if (more) {
+      wait_vmem<kRingWait>();
+    } else {
+      wait_vmem<8>();
+    }
+    __syncthreads();
+    if (more) issue_w2(j + 3);
+    logits(bufp(j + 1), uB, x);
+    if constexpr (kMode == kModeSample) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, x[nb][i]);
+      const float mc = m * a.cf;
+      float sum = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(x[nb][i], a.cf, -mc));
+      if (m == -__builtin_inff()) sum = 0.0f;
+      const MergeMS merge{a.cf};
+      merge(m, sum, m0, s0);
+      const float om = __shfl_xor(m, 32), os = __shfl_xor(sum, 32);
+      merge(m, sum, om, os);
+      if (hh == 0 && rowok) a.partials[(size_t)R * a.ntiles + tile] = make_float2(m, sum);
+    } else {
+      float bv = -__builtin_inff();
+      int bpos = 0;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (x[nb][i] > bv) {
+            bv = x[nb][i];
+            bpos = nb * 16 + i;
+          }
+      const int cb = c0 + 4 * hh;
+      int b0 = cb + 32 * (bp0 >> 4) + 8 * ((bp0 >> 2) & 3) + (bp0 & 3);
+      const int b1 = cb + kHalfCols + 32 * (bpos >> 4) + 8 * ((bpos >> 2) & 3) + (bpos & 3);
+      float bvm = bv0;
+      argmax_merge(bvm, b0, bv, b1);
+      const float ov = __shfl_xor(bvm, 32);
+      const int oi = __shfl_xor(b0, 32);
+      argmax_merge(bvm, b0, ov, oi);
+      if (hh == 0 && rowok) a.partials[(size_t)R * a.ntiles + tile] = make_float2(bvm, __int_as_float(b0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_u(more ? j + 3 : j + 1, uB);
+  }
+}
+
 template <int kMode, bool kBf16>
 __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void tile_pass_kernel(TileArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -694,6 +931,18 @@ static int compute_units() {
   return cached[dev];
 }
 
+// The ring kernel's LDS (96 KB) is above the default dynamic limit: raise the
+// limit once per process for each instantiation (the attribute belongs to the
+// kernel, not to a device).
+template <int kMode>
+static hipError_t ring_lds_attribute(size_t lds) {
+  static hipError_t state = hipErrorNotReady;
+  if (state == hipErrorNotReady)
+    state = hipFuncSetAttribute((const void*)tile_ring_kernel<kMode>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+  return state;
+}
+
 // Rows [row_begin, row_end) x tiles [tile_begin, tile_begin + tile_count) with
 // the one-tile-per-workgroup kernel.
 template <int kMode, bool kBf16>
@@ -724,6 +973,28 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
   if (!fast) {
     launch_tiles<kMode, kBf16>(a, 0, a.nrows, 0, a.ntiles, s);
     return hipGetLastError();
+  }
+  if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
+    // The wide ring kernel when its 256-row groups are at least 3/4 filled.
+    const int rgroups = (a.nrows + kRingRows - 1) / kRingRows;
+    if (4 * a.nrows >= 3 * rgroups * kRingRows) {
+      const size_t lds = (size_t)kRingStages * kHalfBytes;
+      const hipError_t e = ring_lds_attribute<kMode>(lds);
+      if (e != hipSuccess) return e;
+      TileArgs g = a;
+      g.ngroups = rgroups;
+      g.rows_per_group = kRingRows;
+      g.row_begin = 0;
+      g.row_end = a.nrows;
+      g.tile_begin = 0;
+      g.tile_count = full_tiles;
+      int nslices = compute_units() / rgroups;  // one workgroup per CU
+      if (nslices >= 8) nslices &= ~7;
+      nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
+      hipLaunchKernelGGL((tile_ring_kernel<kMode>), dim3(rgroups * nslices), dim3(kRingThreads), lds, s, g, nslices);
+      launch_tiles<kMode, kBf16>(a, 0, a.nrows, full_tiles, a.ntiles - full_tiles, s);
+      return hipGetLastError();
+    }
   }
   if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy || kMode == kModeOverlap)) {
     TileArgs g = a;
