@@ -180,4 +180,56 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
 // 2^x for the softmax terms: the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// Merges of per-lane partial summaries and the transposing wave reduction
+// built from them.
+// ---------------------------------------------------------------------------
+// (max, sum of 2^((x - max) cf)) pairs: merge (m, s) with (om, os).
+struct MergeMS {
+  float cf;
+  __device__ __forceinline__ void operator()(float& m, float& s, float om, float os) const {
+    const float M = fmaxf(m, om);
+    const float lo = fminf(m, om);
+    const float e = M == -__builtin_inff() ? 0.0f : fast_exp2((lo - M) * cf);
+    const float sh = m >= om ? s : os;
+    const float sl = m >= om ? os : s;
+    s = sh + sl * e;
+    m = M;
+  }
+};
+
+// (value, index as float bits): larger value, lower index on ties.
+struct MergeArgmax {
+  __device__ __forceinline__ void operator()(float& v, float& ib, float ov, float oib) const {
+    int i = __float_as_int(ib);
+    argmax_merge(v, i, ov, __float_as_int(oib));
+    ib = __int_as_float(i);
+  }
+};
+
+struct MergeSum {
+  __device__ __forceinline__ void operator()(float& v, float& u, float ov, float ou) const {
+    v += ov;
+    u += ou;
+  }
+};
+
+// One exchange of the transposing reduction: with H = half the live count,
+// a lane keeps elements [0, H) or [H, 2H) (by its bit `o`) merged with the
+// partner's copy of the same elements.
+template <int H, int N, class M>
+__device__ __forceinline__ void xstep(float (&a)[N], float (&b)[N], int lane, int o, const M& merge) {
+  static_assert(2 * H <= N, "live count");
+  const bool hi = (lane & o) != 0;
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    float ka = hi ? a[j + H] : a[j], kb = hi ? b[j + H] : b[j];
+    const float sa = hi ? a[j] : a[j + H], sb = hi ? b[j] : b[j + H];
+    const float ra = __shfl_xor(sa, o), rb = __shfl_xor(sb, o);
+    merge(ka, kb, ra, rb);
+    a[j] = ka;
+    b[j] = kb;
+  }
+}
+
 }  // namespace dspark

@@ -120,7 +120,9 @@ struct TStatsArgs {
   const float* target;
   const int* list;
   const int* count;  // device count (list mode)
+  int nreq;          // list mode: entries of the list buffer; request mode: requests
   int nall;          // rows in all mode
+  int max_rows;      // bound on the rows of one launch (set by launch_target_stats)
   int kk0;
   int rows_per_req;  // list mode: block positions kk0, kk0+1, ... of each listed request
   int orow_stride;   // list mode: summaries of (b, row) go to row b * orow_stride + row
@@ -132,6 +134,9 @@ struct TStatsArgs {
 };
 
 hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, hipStream_t s);
+
+// Compute units of the current device (queried once per device).
+int compute_units_of_device();
 
 hipError_t launch_transpose_w2(const void* W2, bool bf16, int r, int V, void* W2T, hipStream_t s);
 

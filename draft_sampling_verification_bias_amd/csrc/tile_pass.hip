@@ -119,53 +119,6 @@ __device__ __forceinline__ float4 load4(const float* __restrict__ row, int c, in
 
 __device__ __forceinline__ float comp(const float4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; }
 
-// (max, sum of 2^((x - max) cf)) pairs: merge (m, s) with (om, os).
-struct MergeMS {
-  float cf;
-  __device__ __forceinline__ void operator()(float& m, float& s, float om, float os) const {
-    const float M = fmaxf(m, om);
-    const float lo = fminf(m, om);
-    const float e = M == -__builtin_inff() ? 0.0f : fast_exp2((lo - M) * cf);
-    const float sh = m >= om ? s : os;
-    const float sl = m >= om ? os : s;
-    s = sh + sl * e;
-    m = M;
-  }
-};
-
-// (value, index as float bits): larger value, lower index on ties.
-struct MergeArgmax {
-  __device__ __forceinline__ void operator()(float& v, float& ib, float ov, float oib) const {
-    int i = __float_as_int(ib);
-    argmax_merge(v, i, ov, __float_as_int(oib));
-    ib = __int_as_float(i);
-  }
-};
-
-struct MergeSum {
-  __device__ __forceinline__ void operator()(float& v, float& u, float ov, float ou) const {
-    v += ov;
-    u += ou;
-  }
-};
-
-// One exchange of the transposing reduction: with H = half the live count,
-// a lane keeps elements [0, H) or [H, 2H) (by its bit `o`) merged with the
-// partner's copy of the same elements.
-template <int H, class M>
-__device__ __forceinline__ void xstep(float (&a)[16], float (&b)[16], int lane, int o, const M& merge) {
-  const bool hi = (lane & o) != 0;
-#pragma unroll
-  for (int j = 0; j < H; ++j) {
-    float ka = hi ? a[j + H] : a[j], kb = hi ? b[j + H] : b[j];
-    const float sa = hi ? a[j] : a[j + H], sb = hi ? b[j] : b[j + H];
-    const float ra = __shfl_xor(sa, o), rb = __shfl_xor(sb, o);
-    merge(ka, kb, ra, rb);
-    a[j] = ka;
-    b[j] = kb;
-  }
-}
-
 // Reduce 16 per-lane row values over the 32 lanes of each half-wave.  On
 // return a[0], b[0] hold the result for register (lane & 31) >> 1 in both
 // lanes of each even/odd pair.
@@ -570,17 +523,19 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
       for (int q = 0; q < 4; ++q) u[nb][q] = *reinterpret_cast<const float4*>(urow + c + 32 * nb + 8 * q);
   };
 
-  // Issue order: W2(0), U(0), the previous token (waiting for it also waits
-  // for half 0, which step 0 needs anyway), the W1 row, W2(1), U(1).
-  float4 uA[2][4], uB[2][4];
-  issue_w2(0);
-  issue_u(0, uA);
+  // Issue order: the previous token, alone (waiting for it then waits for
+  // nothing else), the W1 row, W2(0), U(0), W2(1), U(1).  Everything a
+  // workgroup needs for step 0 is thus requested before the bulk of the
+  // kernel's loads, and the W1 row ahead of the halves.
   const int prev = prev_token(a, row_info(a, Rc));
   const bool ok = rowok && (unsigned)prev < (unsigned)a.V;
   const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
   bf16x8 ev[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) ev[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
+  float4 uA[2][4], uB[2][4];
+  issue_w2(0);
+  issue_u(0, uA);
   if (!ok) {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
@@ -919,7 +874,7 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
 }
 
 // Compute units of the current device (cached per device).
-static int compute_units() {
+int compute_units_of_device() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -977,7 +932,7 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
   if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
     // The wide ring kernel when its 256-row groups are at least 3/4 filled.
     const int rgroups = (a.nrows + kRingRows - 1) / kRingRows;
-    if (4 * a.nrows >= 3 * rgroups * kRingRows) {
+    if (a.kper == 1 && 4 * a.nrows >= 3 * rgroups * kRingRows) {
       const size_t lds = (size_t)kRingStages * kHalfBytes;
       const hipError_t e = ring_lds_attribute<kMode>(lds);
       if (e != hipSuccess) return e;
@@ -988,7 +943,7 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
       g.row_end = a.nrows;
       g.tile_begin = 0;
       g.tile_count = full_tiles;
-      int nslices = compute_units() / rgroups;  // one workgroup per CU
+      int nslices = compute_units_of_device() / rgroups;  // one workgroup per CU
       if (nslices >= 8) nslices &= ~7;
       nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
       hipLaunchKernelGGL((tile_ring_kernel<kMode>), dim3(rgroups * nslices), dim3(kRingThreads), lds, s, g, nslices);
@@ -1007,7 +962,7 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
     // Two resident workgroups per CU (64 KB of LDS each; one in overlap mode,
     // whose waves also hold the target values); the column slices of every
     // row group together fill them once.
-    int nslices = (kMode == kModeOverlap ? 1 : 2) * compute_units() / groups;
+    int nslices = (kMode == kModeOverlap ? 1 : 2) * compute_units_of_device() / groups;
     if (nslices >= 8) nslices &= ~7;
     nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
     const size_t lds = 2 * (size_t)kHalfBytes;

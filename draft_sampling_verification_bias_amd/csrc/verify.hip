@@ -136,62 +136,93 @@ __device__ __forceinline__ double wval(const void* W, size_t idx) {
 
 // ---------------------------------------------------------------------------
 // Target-row statistics, shared with dspark_survival.
-//   list mode (list != null): row li is request list[li] at block position
-//     kk0; summaries go to row b of tpart.
+//   list mode (list != null): row li is request list[li / rows_per_req] at
+//     block position kk0 + li % rows_per_req; summaries of (b, row) go to row
+//     b * orow_stride + row of tpart.
+//   request mode (list == null, nreq > 0): the same rows and summary layout
+//     for every request b < nreq, with no list to look up.
 //   all mode: row R = b * gamma + kk for kk < gamma; summaries go to row R.
 // Sample mode writes (max t, sum 2^((t - max) * cf)); greedy mode (max t,
 // argmax bits).
 // ---------------------------------------------------------------------------
-constexpr int kStatWaveTiles = 4;                                   // tiles per wave per item
-constexpr int kStatItemTiles = kStatWaveTiles * (kVThreads / kWave);  // 16 tiles = 4096 columns
+constexpr int kStatBlocksPerCU = 8;
+constexpr int kStatWaveTiles = 8;                                   // tiles per wave per item
+constexpr int kStatItemTiles = kStatWaveTiles * (kVThreads / kWave);  // 32 tiles = 8192 columns
 
 // Each work item is kStatItemTiles consecutive kTgtCols-column tiles of one
 // row; a wave owns kStatWaveTiles of them, a lane four consecutive columns of
 // each (one 16-byte load per tile, all issued together), and every reduction
 // is a wave reduction.  With tx_out set (list mode), the lane holding the
-// row's drafted token also stores its target logit.
+// row's drafted token also stores its target logit.  In list mode the count
+// and the item's list entry are loaded together (the entry speculatively,
+// from inside the list buffer), so an item waits for two dependent loads:
+// those, then its row.
 template <bool kGreedy>
 __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
-  const int nrows = a.list ? *a.count * a.rows_per_req : a.nall;
   const int ngrp = (a.ntv + kStatItemTiles - 1) / kStatItemTiles;
-  const long long items = (long long)nrows * ngrp;
+  const long long items_max = (long long)a.max_rows * ngrp;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const bool full_rows = (a.V & 3) == 0;
-  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+
+  struct Item {
+    const float* row;
+    int x, orow, tw;
+    bool ok;
+  };
+  // Item `it`: its row, output row, drafted token and first tile; ok is false
+  // past the last row (list mode: past the device count, and so for every
+  // later item of this workgroup too, the items being in row order).
+  auto resolve = [&](long long it) -> Item {
+    Item m;
+    m.ok = it < items_max;
+    if (!m.ok) return m;
     const int li = (int)(it / ngrp);
     const int tg = (int)(it - (long long)li * ngrp);
-    int b, kk, orow;
+    int b, kk;
     if (a.list) {
       const int req = li / a.rows_per_req, row = li - req * a.rows_per_req;
-      b = a.list[req];
+      const int cnt = *a.count;                        // these two loads
+      b = a.list[req < a.nreq ? req : a.nreq - 1];     // go out together
+      m.ok = req < cnt;
       kk = a.kk0 + row;
-      orow = b * a.orow_stride + row;
+      m.orow = b * a.orow_stride + row;
+    } else if (a.nreq > 0) {
+      b = li / a.rows_per_req;
+      const int row = li - b * a.rows_per_req;
+      kk = a.kk0 + row;
+      m.orow = b * a.orow_stride + row;
     } else {
       b = li / a.gamma;
       kk = li - b * a.gamma;
-      orow = li;
+      m.orow = li;
     }
-    const float* row = a.target + ((size_t)b * (a.gamma + 1) + kk) * (size_t)a.V;
-    const int x = (a.tx_out && kk < a.gamma) ? a.draft_tokens[(size_t)b * a.gamma + kk] : -1;
-    const int tw = tg * kStatItemTiles + wave * kStatWaveTiles;  // first tile of this wave
-    float v[kStatWaveTiles][4];
+    m.row = a.target + ((size_t)b * (a.gamma + 1) + kk) * (size_t)a.V;
+    m.x = (m.ok && a.tx_out && kk < a.gamma) ? a.draft_tokens[(size_t)b * a.gamma + kk] : -1;
+    m.tw = tg * kStatItemTiles + wave * kStatWaveTiles;  // first tile of this wave
+    return m;
+  };
+  auto load = [&](const Item& m, float (&v)[kStatWaveTiles][4]) {
 #pragma unroll
     for (int j = 0; j < kStatWaveTiles; ++j) {
-      const int c0 = (tw + j) * kTgtCols + 4 * lane;
+      const int c0 = (m.tw + j) * kTgtCols + 4 * lane;
       if (full_rows && c0 + 4 <= a.V) {
-        const float4 q = *reinterpret_cast<const float4*>(row + c0);
+        const float4 q = *reinterpret_cast<const float4*>(m.row + c0);
         v[j][0] = q.x; v[j][1] = q.y; v[j][2] = q.z; v[j][3] = q.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[j][e] = c0 + e < a.V ? row[c0 + e] : -__builtin_inff();
+        for (int e = 0; e < 4; ++e) v[j][e] = c0 + e < a.V ? m.row[c0 + e] : -__builtin_inff();
       }
     }
+  };
+  auto reduce_store = [&](const Item& m, const float (&v)[kStatWaveTiles][4]) {
+    // per lane: one (max, sum) or (value, index) pair per tile; the drafted
+    // token's logit from the lane that holds it
+    float pa[kStatWaveTiles], pb[kStatWaveTiles];
 #pragma unroll
     for (int j = 0; j < kStatWaveTiles; ++j) {
-      const int t = tw + j;
-      if (t >= a.ntv) break;  // uniform across the wave
-      const int c0 = t * kTgtCols + 4 * lane;
-      if ((unsigned)(x - c0) < 4u) a.tx_out[orow] = v[j][x - c0 == 0 ? 0 : x - c0 == 1 ? 1 : x - c0 == 2 ? 2 : 3];
+      const int c0 = (m.tw + j) * kTgtCols + 4 * lane;
+      if ((unsigned)(m.x - c0) < 4u)
+        a.tx_out[m.orow] = v[j][m.x - c0 == 0 ? 0 : m.x - c0 == 1 ? 1 : m.x - c0 == 2 ? 2 : 3];
       if constexpr (kGreedy) {
         float bv = v[j][0];
         int bi = c0;
@@ -202,31 +233,75 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
             bi = c0 + e;
           }
         }
-        wave_argmax(bv, bi);
-        if (lane == 0) a.tpart[(size_t)orow * a.ntv + t] = make_float2(bv, __int_as_float(bi));
+        pa[j] = bv;
+        pb[j] = __int_as_float(bi);
       } else {
-        const float m = wave_max(fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3])));
+        const float mx = fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3]));
         float sum = 0.0f;
-        if (m != -__builtin_inff()) {
+        if (mx != -__builtin_inff()) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sum += fast_exp2((v[j][e] - m) * a.cf);
+          for (int e = 0; e < 4; ++e) sum += fast_exp2((v[j][e] - mx) * a.cf);
         }
-        sum = wave_sum(sum);
-        if (lane == 0) a.tpart[(size_t)orow * a.ntv + t] = make_float2(m, sum);
+        pa[j] = mx;
+        pb[j] = sum;
       }
     }
+    // Transposing reduction of the wave's kStatWaveTiles pairs: lane l ends
+    // with tile (l >> 3) & 7 of the wave, merged over all 64 lanes.
+    static_assert(kStatWaveTiles == 8, "three exchange steps, then three merges");
+    auto reduce = [&](const auto& merge) {
+      xstep<4>(pa, pb, lane, 32, merge);
+      xstep<2>(pa, pb, lane, 16, merge);
+      xstep<1>(pa, pb, lane, 8, merge);
+#pragma unroll
+      for (int o = 4; o > 0; o >>= 1) {
+        const float ra = __shfl_xor(pa[0], o), rb = __shfl_xor(pb[0], o);
+        merge(pa[0], pb[0], ra, rb);
+      }
+    };
+    if constexpr (kGreedy) {
+      reduce(MergeArgmax{});
+    } else {
+      reduce(MergeMS{a.cf});
+    }
+    const int t = m.tw + 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
+    if ((lane & 7) == 0 && t < a.ntv) a.tpart[(size_t)m.orow * a.ntv + t] = make_float2(pa[0], pb[0]);
+  };
+
+  // Grid-stride over the items with the next item's loads in flight while
+  // the current one is reduced (two register sets, roles swapped each turn).
+  long long it = blockIdx.x;
+  Item ca = resolve(it);
+  if (!ca.ok) return;
+  float va[kStatWaveTiles][4], vb[kStatWaveTiles][4];
+  load(ca, va);
+  for (;;) {
+    it += gridDim.x;
+    const Item cb = resolve(it);
+    if (cb.ok) load(cb, vb);
+    reduce_store(ca, va);
+    if (!cb.ok) return;
+    it += gridDim.x;
+    ca = resolve(it);
+    if (ca.ok) load(ca, va);
+    reduce_store(cb, vb);
+    if (!ca.ok) return;
   }
 }
 
 hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, hipStream_t s) {
   const long long items = (long long)max_rows * ((a.ntv + kStatItemTiles - 1) / kStatItemTiles);
-  const int grid = (int)(items < 16384 ? items : 16384);
+  // a few resident workgroups per CU, each walking many items
+  const long long cap = (long long)kStatBlocksPerCU * compute_units_of_device();
+  const int grid = (int)(items < cap ? items : cap);
   if (grid <= 0) return hipSuccess;
   ProfScope prof(s, kProfTargetStats);
+  TStatsArgs g = a;
+  g.max_rows = max_rows;
   if (greedy) {
-    hipLaunchKernelGGL((target_stats_kernel<true>), dim3(grid), dim3(kVThreads), 0, s, a);
+    hipLaunchKernelGGL((target_stats_kernel<true>), dim3(grid), dim3(kVThreads), 0, s, g);
   } else {
-    hipLaunchKernelGGL((target_stats_kernel<false>), dim3(grid), dim3(kVThreads), 0, s, a);
+    hipLaunchKernelGGL((target_stats_kernel<false>), dim3(grid), dim3(kVThreads), 0, s, g);
   }
   return hipGetLastError();
 }
@@ -1105,8 +1180,10 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
     const int k0 = sched.k0[pi], k1 = sched.k1[pi];
     TStatsArgs t = {};
     t.target = a.target;
-    t.list = w.lists + (size_t)ph * a.B;
+    // phase 1 tests every valid request: read its rows without the list
+    t.list = pi == 0 ? nullptr : w.lists + (size_t)ph * a.B;
     t.count = w.counts + ph;
+    t.nreq = a.B;
     t.kk0 = k0 - 1;
     t.rows_per_req = k1 - k0 + 1;
     t.orow_stride = w.lmax;
