@@ -896,8 +896,10 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
 
       // Rejected at k: residual draw by proposals from p_t.  Proposal i is
       // kept with probability max(0, 1 - p_d(v) / p_t(v)); the lowest kept i
-      // wins.  The first batch has one proposal per wave (most rejections end
-      // there), later ones four per wave, 16 lanes each.
+      // wins.  Proposals go in batches of 16, four per wave (16 lanes each):
+      // with the acceptance rates of typical drafts a batch of 16 almost
+      // always holds a kept proposal, so a second batch (another three
+      // dependent memory round trips) is rare.
       const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
       auto keep_test = [&](double ua, int v, float tv, double lv) -> bool {
         const double ptv = exp2((double)(tv - s.M) * cf) / s.Z;
@@ -922,42 +924,26 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
         }
         __syncthreads();
       };
-      int found, ytok;
-      {
-        const double q = __shfl(up0.x, wave) * s.Z;
-        const double ua = __shfl(up0.y, wave);
-        int ts;
-        double bq;
-        float mt;
-        tile_search(s, cumi, wmask, q, ts, bq, mt);
-        int v;
-        float tv;
-        col_draw<kWave>(trow, a.V, ts, mt, s.M, cf_f, cf, q - bq, v, tv);
-        const double lv = draft_logit_at<kWave, kBf16>(a, urow, prev, v);
-        const bool pass = keep_test(ua, v, tv, lv);
-        agree(pass ? wave : INT_MAX, v, found, ytok);
-      }
+      int found = INT_MAX, ytok = -1;
       const int grp = lane >> 4;
-      if (found == INT_MAX) {
-        // Later batches search by binary search over an LDS copy of the
-        // cumulative weights, one search per 16-lane group: the first tile
-        // whose inclusive cumulative weight exceeds q (it has positive
-        // weight), else the last positive tile -- the rule of tile_search.
-        if (wave == 0) {
+      // Each group's tile search is a binary search over an LDS copy of the
+      // cumulative weights: the first tile whose inclusive cumulative weight
+      // exceeds q (it has positive weight), else the last positive tile --
+      // the rule of tile_search.
+      if (wave == 0) {
 #pragma unroll
-          for (int j = 0; j < kLaneTiles; ++j) {
-            if (s.t0 + j < s.t1) {
-              s_cum[s.t0 + j] = cumi[j];
-              s_m[s.t0 + j] = s.p[j].x;
-            }
+        for (int j = 0; j < kLaneTiles; ++j) {
+          if (s.t0 + j < s.t1) {
+            s_cum[s.t0 + j] = cumi[j];
+            s_m[s.t0 + j] = s.p[j].x;
           }
-          const unsigned long long pl = __ballot(wmask != 0u);
-          const int lw = pl ? 63 - __clzll((long long)pl) : 0;
-          if (lane == lw) s_last = wmask ? s.t0 + 31 - __clz(wmask) : 0;
         }
-        __syncthreads();
+        const unsigned long long pl = __ballot(wmask != 0u);
+        const int lw = pl ? 63 - __clzll((long long)pl) : 0;
+        if (lane == lw) s_last = wmask ? s.t0 + 31 - __clz(wmask) : 0;
       }
-      for (int i0 = kWaves; found == INT_MAX && i0 < DSPARK_MAX_RESIDUAL_PROPOSALS; i0 += kPropBatch) {
+      __syncthreads();
+      for (int i0 = 0; found == INT_MAX && i0 < DSPARK_MAX_RESIDUAL_PROPOSALS; i0 += kPropBatch) {
         // uniforms of the batch: lane l holds proposal i0 + l % 16
         const int ip = i0 + (lane & 15);
         const double sx = __shfl(up0.x, ip & (kPropPre - 1)), sy = __shfl(up0.y, ip & (kPropPre - 1));
