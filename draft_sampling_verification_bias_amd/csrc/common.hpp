@@ -105,6 +105,72 @@ __device__ __forceinline__ double wave_inclusive_scan(double x) {
   return x;
 }
 
+// ---------------------------------------------------------------------------
+// Wave reductions and scans through DPP lane moves (VALU operations, a few
+// cycles each) instead of LDS permutes (an LDS round trip each): the rows of
+// 16 lanes first, then the four rows.  The orders of the additions differ
+// from the shuffle versions above, so sums may differ in the last bits.
+// ---------------------------------------------------------------------------
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowShr = 0x110;       // + n: row_shr:n
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// src moved by a DPP pattern; lanes without a source (or outside kRowMask)
+// read 0.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)src, kCtrl, kRowMask, 0xF, true);
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp_f32(float src) {
+  return __uint_as_float(dpp_u32<kCtrl, kRowMask>(__float_as_uint(src)));
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ double dpp_f64(double src) {
+  const uint64_t u = (uint64_t)__double_as_longlong(src);
+  const uint32_t lo = dpp_u32<kCtrl, kRowMask>((uint32_t)u);
+  const uint32_t hi = dpp_u32<kCtrl, kRowMask>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// The value of lane l (l wave-uniform).
+__device__ __forceinline__ float lane_f32(float x, int l) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), l));
+}
+__device__ __forceinline__ double lane_f64(double x, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ int lane_i32(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+// Maximum over the wave, returned to every lane.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_f32<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return fmaxf(fmaxf(lane_f32(x, 0), lane_f32(x, 16)), fmaxf(lane_f32(x, 32), lane_f32(x, 48)));
+}
+
+// Inclusive prefix sum across the wave: Hillis-Steele within each row of 16
+// lanes, then row 1 (3) adds the total of row 0 (2), then rows 2 and 3 add
+// the total of rows 0 and 1.
+__device__ __forceinline__ double wave_inclusive_scan_dpp(double x) {
+  x += dpp_f64<kDppRowShr + 1>(x);
+  x += dpp_f64<kDppRowShr + 2>(x);
+  x += dpp_f64<kDppRowShr + 4>(x);
+  x += dpp_f64<kDppRowShr + 8>(x);
+  x += dpp_f64<kDppRowBcast15, 0xA>(x);
+  x += dpp_f64<kDppRowBcast31, 0xC>(x);
+  return x;
+}
+
 // Block-wide helpers for blockDim.x == kBlock (a multiple of 64, <= 1024).
 // `scratch` must hold kBlock / 64 elements; the functions synchronise.
 template <int kBlock>

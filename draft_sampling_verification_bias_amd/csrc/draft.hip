@@ -236,6 +236,13 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
 // W2 loads (and the W1 and U values it needs) issued together.  The quarters
 // meet in LDS and wave 0 draws the column.
 // ---------------------------------------------------------------------------
+// The stream-0 uniform of position k, out of line: the draw is needed only
+// at the first position (later ones read the look-ahead value), and inline
+// the compiler evaluates it on every position to select the result.
+__device__ __noinline__ double draft_uniform(uint64_t seed, uint64_t round, int k) {
+  return unit_uniform(draw_block(seed, round, k, kStreamDraft, 0).w[0]);
+}
+
 constexpr int kWaveTiles = 2048;                 // up to V = 262144
 constexpr int kWavePer = kWaveTiles / kWave;      // summaries per lane (max)
 constexpr int kMaxRQuarter = 512 / 4;             // k per wave (r <= 512)
@@ -274,64 +281,60 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
   }
 
   // row max, tile weights, their lane prefix, the picked tile
+  // (selects rather than branches: every lane runs every j)
   float lm = -__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < kWavePer; ++j)
-    if (t0 + j < t1) lm = fmaxf(lm, pr[j].x);
-  const float M = wave_max(lm);
-  auto weight = [&](const float2& p) -> double {
-    return p.x == -__builtin_inff() ? 0.0 : (double)p.y * (double)fast_exp2((p.x - M) * a.cf);
-  };
+  for (int j = 0; j < kWavePer; ++j) lm = t0 + j < t1 ? fmaxf(lm, pr[j].x) : lm;
+  const float M = wave_max_dpp(lm);
   double pw[kWavePer];  // the lane's tile weights, kept for the owner's search
   double local = 0.0;
 #pragma unroll
   for (int j = 0; j < kWavePer; ++j) {
-    pw[j] = t0 + j < t1 ? weight(pr[j]) : 0.0;
+    const float e = fast_exp2((pr[j].x - M) * a.cf);
+    const bool live = t0 + j < t1 && pr[j].x != -__builtin_inff();
+    pw[j] = live ? (double)pr[j].y * (double)e : 0.0;
     local += pw[j];
   }
-  const double incl = wave_inclusive_scan(local);
+  const double incl = wave_inclusive_scan_dpp(local);
   const double excl = incl - local;
-  const double total = __shfl(incl, kWave - 1);
+  const double total = lane_f64(incl, kWave - 1);
   // the stream-0 uniform of this position: drawn by the previous position's
   // select (see below), or here at the first position
-  const double u = a.k == 1 ? unit_uniform(draw_block(seed, a.round, 1, kStreamDraft, 0).w[0]) : u_pre;
+  const double u = a.k == 1 ? draft_uniform(seed, a.round, 1) : u_pre;
   const double q = u * total;
   const unsigned long long cross = __ballot(local > 0.0 && incl > q);
   const unsigned long long pos = __ballot(local > 0.0);
   const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
-  int ts = -1;
-  double base = 0.0;
-  float mt = 0.0f;
-  if (lane == owner) {
-    double cum = excl, lastbase = 0.0;
-    int lastpos = -1;
-    float lastm = 0.0f;
+  // The owner's search, in selects rather than branches (every lane runs
+  // it, the owner's result is taken): the first positive tile whose
+  // inclusive cumulative weight exceeds q, else the last positive tile.
+  // pw[j] is 0 past the lane's last tile.
+  int ts = -1, lastpos = -1;
+  double base = 0.0, lastbase = 0.0;
+  float mt = 0.0f, lastm = 0.0f;
+  {
+    double cum = excl;
 #pragma unroll
     for (int j = 0; j < kWavePer; ++j) {
-      if (t0 + j < t1) {
-        const double w = pw[j];
-        if (w > 0.0) {
-          lastpos = t0 + j;
-          lastbase = cum;
-          lastm = pr[j].x;
-          if (ts < 0 && cum + w > q) {
-            ts = t0 + j;
-            base = cum;
-            mt = pr[j].x;
-          }
-        }
-        cum += w;
-      }
+      const double w = pw[j];
+      const bool posw = w > 0.0;
+      const bool hit = posw && ts < 0 && cum + w > q;
+      lastpos = posw ? t0 + j : lastpos;
+      lastbase = posw ? cum : lastbase;
+      lastm = posw ? pr[j].x : lastm;
+      ts = hit ? t0 + j : ts;
+      base = hit ? cum : base;
+      mt = hit ? pr[j].x : mt;
+      cum += w;
     }
-    if (ts < 0) {
-      ts = lastpos < 0 ? 0 : lastpos;
-      base = lastpos < 0 ? 0.0 : lastbase;
-      mt = lastpos < 0 ? M : lastm;
-    }
+    const bool none = ts < 0;
+    ts = none ? (lastpos < 0 ? 0 : lastpos) : ts;
+    base = none ? (lastpos < 0 ? 0.0 : lastbase) : base;
+    mt = none ? (lastpos < 0 ? M : lastm) : mt;
   }
-  ts = __shfl(ts, owner);
-  base = __shfl(base, owner);
-  mt = __shfl(mt, owner);
+  ts = lane_i32(ts, owner);
+  base = lane_f64(base, owner);
+  mt = lane_f32(mt, owner);
 
   // batch 2: the wave's quarter of the bias of tile ts.  Lane (cg, kr) owns
   // columns c .. c+7 and k = kq wave + kr + 4 i.
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
     term[h] = (double)e * scale;
   }
   const double loc2 = term[0] + term[1];
-  const double inc2 = wave_inclusive_scan(loc2);
+  const double inc2 = wave_inclusive_scan_dpp(loc2);
   const double exc2 = inc2 - loc2;
   const double q2 = q - base;
   const unsigned long long cross2 = __ballot(loc2 > 0.0 && inc2 > q2);
