@@ -599,25 +599,28 @@ struct RowScan {
   double local, excl, incl, Z;
 };
 
+// (Selects rather than branches, and DPP lane moves for the wave max and
+// scan: this sits on the critical path of every decision.)
 __device__ __forceinline__ void row_scan(RowScan& s, float cf, double (&cumi)[kLaneTiles], unsigned& wmask) {
   float lm = -__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < kLaneTiles; ++j)
-    if (s.t0 + j < s.t1) lm = fmaxf(lm, s.p[j].x);
-  s.M = wave_max(lm);
+  for (int j = 0; j < kLaneTiles; ++j) lm = s.t0 + j < s.t1 ? fmaxf(lm, s.p[j].x) : lm;
+  s.M = wave_max_dpp(lm);
   double loc = 0.0;
   wmask = 0u;
 #pragma unroll
   for (int j = 0; j < kLaneTiles; ++j) {
-    const double wt = s.t0 + j < s.t1 ? tile_weight(s.p[j], s.M, cf) : 0.0;
-    if (wt > 0.0) wmask |= 1u << j;
+    const float e = fast_exp2((s.p[j].x - s.M) * cf);
+    const bool live = s.t0 + j < s.t1 && s.p[j].x != -__builtin_inff();
+    const double wt = live ? (double)s.p[j].y * (double)e : 0.0;
+    wmask |= wt > 0.0 ? 1u << j : 0u;
     loc += wt;
     cumi[j] = wt;
   }
   s.local = loc;
-  s.incl = wave_inclusive_scan(loc);
+  s.incl = wave_inclusive_scan_dpp(loc);
   s.excl = s.incl - loc;
-  s.Z = __shfl(s.incl, kWave - 1);
+  s.Z = lane_f64(s.incl, kWave - 1);
   double cum = s.excl;  // the lane's inclusive cumulative weights, in tile order
 #pragma unroll
   for (int j = 0; j < kLaneTiles; ++j) {
@@ -631,35 +634,32 @@ __device__ __forceinline__ void row_scan(RowScan& s, float cf, double (&cumi)[kL
 // and its maximum.  q is the same on every lane; so are the results.
 __device__ __forceinline__ void tile_search(const RowScan& s, const double (&cumi)[kLaneTiles], unsigned wmask,
                                             double q, int& ts_o, double& base_o, float& mt_o) {
-  const int lane = threadIdx.x & (kWave - 1);
   const unsigned long long cross = __ballot(s.local > 0.0 && s.incl > q);
   const unsigned long long pos = __ballot(s.local > 0.0);
   const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+  // every lane runs the owner's search (selects, no branches); the owner's
+  // result is taken
+  int jp = -1, jl = -1;
+#pragma unroll
+  for (int j = 0; j < kLaneTiles; ++j) {
+    const bool on = (wmask >> j) & 1u;
+    jl = on ? j : jl;
+    jp = (jp < 0 && on && cumi[j] > q) ? j : jp;
+  }
+  const int jj = jp >= 0 ? jp : jl;
   int t = 0;
   double bb = 0.0;
   float m = s.M;
-  if (lane == owner) {
-    int jp = -1, jl = -1;
 #pragma unroll
-    for (int j = 0; j < kLaneTiles; ++j) {
-      if ((wmask >> j) & 1u) {
-        jl = j;
-        if (jp < 0 && cumi[j] > q) jp = j;
-      }
-    }
-    const int jj = jp >= 0 ? jp : jl;
-#pragma unroll
-    for (int j = 0; j < kLaneTiles; ++j) {
-      if (j == jj) {
-        t = s.t0 + j;
-        bb = j == 0 ? s.excl : cumi[j > 0 ? j - 1 : 0];
-        m = s.p[j].x;
-      }
-    }
+  for (int j = 0; j < kLaneTiles; ++j) {
+    const bool sel = j == jj;
+    t = sel ? s.t0 + j : t;
+    bb = sel ? (j == 0 ? s.excl : cumi[j > 0 ? j - 1 : 0]) : bb;
+    m = sel ? s.p[j].x : m;
   }
-  ts_o = __shfl(t, owner);
-  base_o = __shfl(bb, owner);
-  mt_o = __shfl(m, owner);
+  ts_o = lane_i32(t, owner);
+  base_o = lane_f64(bb, owner);
+  mt_o = lane_f32(m, owner);
 }
 
 // Within each group of kW lanes (16 or 64): the column of target tile ts
