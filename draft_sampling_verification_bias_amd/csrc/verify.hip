@@ -218,11 +218,23 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
     // per lane: one (max, sum) or (value, index) pair per tile; the drafted
     // token's logit from the lane that holds it
     float pa[kStatWaveTiles], pb[kStatWaveTiles];
+    {
+      // the drafted token's logit: one wave-uniform test per item, then the
+      // lane that holds it picks it out with selects (no dynamic indexing)
+      const int rel = m.x - m.tw * kTgtCols;
+      if ((unsigned)rel < (unsigned)(kStatWaveTiles * kTgtCols)) {
+        const int jx = rel / kTgtCols, cx = rel - jx * kTgtCols;
+        float val = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kStatWaveTiles; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val = (j == jx && e == (cx & 3)) ? v[j][e] : val;
+        if (lane == (cx >> 2)) a.tx_out[m.orow] = val;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kStatWaveTiles; ++j) {
       const int c0 = (m.tw + j) * kTgtCols + 4 * lane;
-      if ((unsigned)(m.x - c0) < 4u)
-        a.tx_out[m.orow] = v[j][m.x - c0 == 0 ? 0 : m.x - c0 == 1 ? 1 : m.x - c0 == 2 ? 2 : 3];
       if constexpr (kGreedy) {
         float bv = v[j][0];
         int bi = c0;
@@ -237,13 +249,12 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
         pb[j] = __int_as_float(bi);
       } else {
         const float mx = fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3]));
+        const float mc = mx * a.cf;
         float sum = 0.0f;
-        if (mx != -__builtin_inff()) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sum += fast_exp2((v[j][e] - mx) * a.cf);
-        }
+        for (int e = 0; e < 4; ++e) sum += fast_exp2(fmaf(v[j][e], a.cf, -mc));
         pa[j] = mx;
-        pb[j] = sum;
+        pb[j] = mx == -__builtin_inff() ? 0.0f : sum;
       }
     }
     // Transposing reduction of the wave's kStatWaveTiles pairs: lane l ends
