@@ -35,7 +35,20 @@ struct SelectArgs {
   float* prob;
   float* lse;
   double* u_next;  // [2][B] stream-0 uniforms drawn one position ahead
+  uint4* esw;      // optional: the drafted token's W1 row for the next tile pass
 };
+
+// Store W1 row x (bf16, r = 256) in the ring tile pass's operand layout for
+// request row b; thread c < 32 copies chunk c.
+template <bool kBf16>
+__device__ __forceinline__ void store_ring_operand(const SelectArgs& a, int b, int x, int c) {
+  if constexpr (kBf16) {
+    if (a.esw != nullptr && c < 32 && (unsigned)x < (unsigned)a.V) {
+      const uint4 v = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W1) + (size_t)x * 256)[c];
+      a.esw[ring_operand_index(b, c)] = v;
+    }
+  }
+}
 
 template <bool kBf16>
 __device__ __forceinline__ float w2_at(const void* W2, size_t idx) {
@@ -103,6 +116,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
       a.prob[out] = 1.0f;
       a.lse[out] = 0.0f;
     }
+    store_ring_operand<kBf16>(a, b, bi, tid);
     return;
   } else {
     // One read of the tile summaries (kept in LDS when they fit) together
@@ -222,6 +236,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
       a.prob[out] = (float)(exp2((double)(l - M) * cf) / total);
       a.lse[out] = (float)((double)M * a.inv_t + log(total));
     }
+    store_ring_operand<kBf16>(a, b, ts * kTileCols + c, tid);
   }
 }
 
@@ -429,6 +444,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
   const unsigned long long cross2 = __ballot(loc2 > 0.0 && inc2 > q2);
   const unsigned long long pos2 = __ballot(loc2 > 0.0);
   const int own2 = cross2 ? __ffsll((long long)cross2) - 1 : (pos2 ? 63 - __clzll((long long)pos2) : 0);
+  int mytok = 0;
   if (lane == own2) {
     int h;
     if (cross2) {
@@ -437,16 +453,19 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
       h = term[1] > 0.0 ? 1 : 0;
     }
     const float l = l2[h];
-    a.tokens[out] = ts * kTileCols + 2 * lane + h;
+    mytok = ts * kTileCols + 2 * lane + h;
+    a.tokens[out] = mytok;
     a.prob[out] = (float)(exp2((double)(l - M) * cf) / total);
     a.lse[out] = (float)((double)M * a.inv_t + log(total));
   }
+  store_ring_operand<kBf16>(a, b, lane_i32(mytok, own2), lane);
 }
 
 size_t draft_workspace(int B, int gamma, int V, int r) {
   (void)gamma;
-  (void)r;
-  return align256((size_t)B * tiles_of(V, kTileCols) * sizeof(float2)) + align256((size_t)2 * B * sizeof(double));
+  // tile summaries, look-ahead uniforms, ring-kernel operands (r = 256 only)
+  return align256((size_t)B * tiles_of(V, kTileCols) * sizeof(float2)) + align256((size_t)2 * B * sizeof(double)) +
+         (r == 256 ? align256(ring_operand_bytes(B)) : 0);
 }
 
 template <bool kGreedy, bool kBf16>
@@ -498,12 +517,22 @@ hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s) {
   sa.lse = a.lse;
   sa.u_next = reinterpret_cast<double*>(reinterpret_cast<char*>(a.ws) +
                                         align256((size_t)a.B * ntiles * sizeof(float2)));
+  // When the tile passes run the ring kernel, each selection also stores the
+  // drafted token's W1 row in that kernel's operand layout, and the next
+  // position's tile pass reads it instead of gathering W1 rows itself.
+  const int mode = greedy ? kModeGreedy : kModeSample;
+  uint4* esw = nullptr;
+  if (a.r == 256 && tile_pass_uses_ring(t, mode, bf16))
+    esw = reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.ws) + align256((size_t)a.B * ntiles * sizeof(float2)) +
+                                   align256((size_t)2 * a.B * sizeof(double)));
 
   for (int k = 1; k <= a.gamma; ++k) {
     t.k0 = k - 1;
-    hipError_t e = launch_tile_pass(t, greedy ? kModeGreedy : kModeSample, bf16, s);
+    t.esw = k >= 2 ? esw : nullptr;
+    hipError_t e = launch_tile_pass(t, mode, bf16, s);
     if (e != hipSuccess) return e;
     sa.k = k;
+    sa.esw = k < a.gamma ? esw : nullptr;
     if (greedy) {
       e = bf16 ? launch_select<true, true>(sa, s) : launch_select<true, false>(sa, s);
     } else if (ntiles <= kWaveTiles) {

@@ -45,9 +45,27 @@ struct TileArgs {
   int row_begin, row_end;       // rows and tiles covered by one launch (set by launch_tile_pass)
   int tile_begin, tile_count;
   float cf;             // log2(e) / T; unused at T == 0
+  const uint4* esw;     // optional: the W1 rows of the previous tokens in the ring
+                        // kernel's operand layout (see ring_operand_index)
 };
 
 hipError_t launch_tile_pass(const TileArgs& a, int mode, bool bf16, hipStream_t s);
+
+// Whether launch_tile_pass runs a's full tiles with the 256-row ring kernel.
+bool tile_pass_uses_ring(const TileArgs& a, int mode, bool bf16);
+
+// The ring kernel's MFMA B operand, stored ahead by the previous position's
+// selection: 16-byte chunk c (k = 8c .. 8c + 7) of the W1 row of request row
+// R's previous token sits at this index (in 16-byte units), so that wave w of
+// row group g reads, at k-step j, 64 consecutive chunks (one per lane).
+// Rows are grouped 256 to a group; r = 256 (32 chunks per row).
+__host__ __device__ inline size_t ring_operand_index(int R, int c) {
+  const int g = R >> 8, w = (R & 255) >> 5, n = R & 31;
+  return (((size_t)g * 8 + w) * 16 + (c >> 1)) * 64 + n + 32 * (c & 1);
+}
+
+// Bytes of that buffer for `rows` rows.
+inline size_t ring_operand_bytes(int rows) { return (size_t)((rows + 255) / 256) * 256 * 512; }
 
 struct DraftArgs {
   const float* U;

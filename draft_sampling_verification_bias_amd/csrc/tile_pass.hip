@@ -527,20 +527,36 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
   // nothing else), the W1 row, W2(0), U(0), W2(1), U(1).  Everything a
   // workgroup needs for step 0 is thus requested before the bulk of the
   // kernel's loads, and the W1 row ahead of the halves.
-  const int prev = prev_token(a, row_info(a, Rc));
-  const bool ok = rowok && (unsigned)prev < (unsigned)a.V;
-  const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
   bf16x8 ev[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) ev[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
   float4 uA[2][4], uB[2][4];
-  issue_w2(0);
-  issue_u(0, uA);
-  if (!ok) {
+  if (a.esw) {
+    // The operand stored by the previous position's selection: 16
+    // fully-coalesced 1 KB loads per wave, no dependence on the previous
+    // token.  (Rows whose previous token was invalid read a stale operand;
+    // their summaries are never used, the selection propagating the
+    // invalid token.)
+    const uint4* ew = a.esw + ((size_t)group * kRingWaves + wave) * 16 * kWave + lane;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < 16; ++j) {
+      const uint4 v = ew[(size_t)j * kWave];
+      ev[j] = __builtin_bit_cast(bf16x8, v);
+    }
+    issue_w2(0);
+    issue_u(0, uA);
+  } else {
+    const int prev = prev_token(a, row_info(a, Rc));
+    const bool ok = rowok && (unsigned)prev < (unsigned)a.V;
+    const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ev[j][e] = (__bf16)0.0f;
+    for (int j = 0; j < 16; ++j) ev[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
+    issue_w2(0);
+    issue_u(0, uA);
+    if (!ok) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ev[j][e] = (__bf16)0.0f;
+    }
   }
   issue_w2(1);
   issue_u(1, uB);
@@ -916,23 +932,36 @@ static void launch_tiles(const TileArgs& a, int row_begin, int row_end, int tile
   hipLaunchKernelGGL((tile_pass_kernel<kMode, kBf16>), dim3(blocks), dim3(kTileThreads), lds, s, g);
 }
 
+// Full 128-column tiles of the vocabulary on the fast paths (V % 4 == 0).
+static int fast_full_tiles(const TileArgs& a) { return (a.V & 3) == 0 ? a.V / kTileCols : 0; }
+
+// The fast paths: bf16 weights, r = 256, at least one full tile, rows at a
+// constant stride, and W2 addressed with 32-bit byte offsets (2 r V < 2^32).
+static bool fast_path(const TileArgs& a, int mode, bool bf16) {
+  return bf16 && (mode == kModeSample || mode == kModeGreedy || mode == kModeOverlap) && a.r == kFastR &&
+         (a.kper == 1 || a.kper == a.gamma) && fast_full_tiles(a) > 0 &&
+         (size_t)2 * kFastR * (size_t)a.V < ((size_t)1 << 32);
+}
+
+bool tile_pass_uses_ring(const TileArgs& a, int mode, bool bf16) {
+  const int rgroups = (a.nrows + kRingRows - 1) / kRingRows;
+  // the ring kernel when its 256-row groups are at least 3/4 filled
+  return fast_path(a, mode, bf16) && (mode == kModeSample || mode == kModeGreedy) && a.kper == 1 &&
+         4 * a.nrows >= 3 * rgroups * kRingRows;
+}
+
 template <int kMode, bool kBf16>
 static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
   ProfScope prof(s, kProfTileSample + kMode);
   const int groups = (a.nrows + kRowsPerGroup - 1) / kRowsPerGroup;  // the last one may be partial
-  const int full_tiles = (a.V & 3) == 0 ? a.V / kTileCols : 0;
-  // (The pipelined kernel addresses W2 with 32-bit byte offsets: 2 r V < 2^32.)
-  const bool fast = kBf16 && (kMode == kModeSample || kMode == kModeGreedy || kMode == kModeOverlap) && a.r == kFastR &&
-                    (a.kper == 1 || a.kper == a.gamma) && full_tiles > 0 &&
-                    (size_t)2 * kFastR * (size_t)a.V < ((size_t)1 << 32);
-  if (!fast) {
+  const int full_tiles = fast_full_tiles(a);
+  if (!fast_path(a, kMode, kBf16)) {
     launch_tiles<kMode, kBf16>(a, 0, a.nrows, 0, a.ntiles, s);
     return hipGetLastError();
   }
   if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
-    // The wide ring kernel when its 256-row groups are at least 3/4 filled.
     const int rgroups = (a.nrows + kRingRows - 1) / kRingRows;
-    if (a.kper == 1 && 4 * a.nrows >= 3 * rgroups * kRingRows) {
+    if (tile_pass_uses_ring(a, kMode, kBf16)) {
       const size_t lds = (size_t)kRingStages * kHalfBytes;
       const hipError_t e = ring_lds_attribute<kMode>(lds);
       if (e != hipSuccess) return e;
