@@ -134,6 +134,11 @@ SMALL = [
     # tiles per workgroup, then the ragged last tile
     ("v151936_b256_t07", dict(V=65540, B=200, gamma=2)),
     ("greedy_v151936_b512", dict(V=65540, B=200, gamma=2)),
+    # the ring kernel with three row groups
+    ("v151936_b256_t07", dict(V=20000, B=700, gamma=2)),
+    # rows of more than 2048 tiles under the ring kernel: the block-wide
+    # selection, which also stores the next position's W1 operand
+    ("v151936_b32", dict(V=264000, B=200, gamma=2)),
     # more than 1024 target tiles per row: the decision kernel's general path
     ("v151936_b32", dict(V=1048580, B=2, gamma=2, r=16)),
     ("greedy_v151936_b512", dict(V=1048580, B=3, gamma=2, r=16)),
