@@ -118,6 +118,7 @@ constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowBcast15 = 0x142;
 constexpr int kDppRowBcast31 = 0x143;
+constexpr int kDppRowRor8 = 0x128;      // row_ror:8, lane i of a row reads lane i ^ 8
 
 // src moved by a DPP pattern; lanes without a source (or outside kRowMask)
 // read 0.
@@ -296,6 +297,76 @@ __device__ __forceinline__ void xstep(float (&a)[N], float (&b)[N], int lane, in
     a[j] = ka;
     b[j] = kb;
   }
+}
+
+// Lane exchanges of gfx950's v_permlane32_swap / v_permlane16_swap.  After
+// swap32(x, y), lanes 0-31 of x keep x and lanes 32-63 of x hold y's lanes
+// 0-31, while y holds x's lanes 32-63 in its lanes 0-31 and keeps its own
+// lanes 32-63.  swap16 does the same between the odd 16-lane rows of x and
+// the even rows of y.  In both, a lane's two results are its own value and
+// the partner's (lane ^ 32, lane ^ 16): x's value in the lower lanes, y's in
+// the upper ones.
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
+// Transposing wave reduction of eight per-lane pairs (a[j], b[j]) under a
+// commutative merge.  On return every lane holds in a[0], b[0] element
+// 4 * bit5 + 2 * bit4 + bit3 of its lane index, merged over all 64 lanes.
+// The exchanges are lane swaps and DPP moves: no LDS.
+template <class M>
+__device__ __forceinline__ void wave_transpose8(float (&a)[8], float (&b)[8], int lane, const M& merge) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // lanes l, l ^ 32: element j below, j + 4 above
+    swap32(a[j], a[j + 4]);
+    swap32(b[j], b[j + 4]);
+    merge(a[j], b[j], a[j + 4], b[j + 4]);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {  // lanes l, l ^ 16: element j or j + 2
+    swap16(a[j], a[j + 2]);
+    swap16(b[j], b[j + 2]);
+    merge(a[j], b[j], a[j + 2], b[j + 2]);
+  }
+  {  // lanes l, l ^ 8: element 0 or 1
+    const bool hi = (lane & 8) != 0;
+    float ka = hi ? a[1] : a[0], kb = hi ? b[1] : b[0];
+    const float sa = hi ? a[0] : a[1], sb = hi ? b[0] : b[1];
+    merge(ka, kb, dpp_f32<kDppRowRor8>(sa), dpp_f32<kDppRowRor8>(sb));
+    a[0] = ka;
+    b[0] = kb;
+  }
+  // the eight lanes of each group: quad neighbours, then the other quad
+  merge(a[0], b[0], dpp_f32<kDppQuadSwap1>(a[0]), dpp_f32<kDppQuadSwap1>(b[0]));
+  merge(a[0], b[0], dpp_f32<kDppQuadSwap2>(a[0]), dpp_f32<kDppQuadSwap2>(b[0]));
+  merge(a[0], b[0], dpp_f32<kDppRowHalfMirror>(a[0]), dpp_f32<kDppRowHalfMirror>(b[0]));
+}
+
+// The same reduction for eight per-lane sums: s[0] ends with the total of
+// element 4 * bit5 + 2 * bit4 + bit3 of the lane index.
+__device__ __forceinline__ void wave_transpose_sum8(float (&s)[8], int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    swap32(s[j], s[j + 4]);
+    s[j] += s[j + 4];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    swap16(s[j], s[j + 2]);
+    s[j] += s[j + 2];
+  }
+  const bool hi = (lane & 8) != 0;
+  s[0] = (hi ? s[1] : s[0]) + dpp_f32<kDppRowRor8>(hi ? s[0] : s[1]);
+  s[0] += dpp_f32<kDppQuadSwap1>(s[0]);
+  s[0] += dpp_f32<kDppQuadSwap2>(s[0]);
+  s[0] += dpp_f32<kDppRowHalfMirror>(s[0]);
 }
 
 }  // namespace dspark

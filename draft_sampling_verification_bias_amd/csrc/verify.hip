@@ -11,7 +11,7 @@
 // Positions are processed in order with early exit: phase k only streams the
 // target rows of requests that are still alive at k (their list is built by
 // phase k-1), so each request reads target rows 1..n+1 and no more.  A phase is
-// one target-statistics kernel (per-tile max / exp-sum over 1024 columns) and
+// one target-statistics kernel (per-tile max / exp-sum over 256 columns) and
 // one decision kernel (one workgroup per request).  Residual draws propose
 // from p_t with the tile summaries and need p_d at one token only, rebuilt by
 // an r-term dot product; the rare exact-residual fallback runs two more
@@ -142,8 +142,9 @@ __device__ __forceinline__ double wval(const void* W, size_t idx) {
 //   request mode (list == null, nreq > 0): the same rows and summary layout
 //     for every request b < nreq, with no list to look up.
 //   all mode: row R = b * gamma + kk for kk < gamma; summaries go to row R.
-// Sample mode writes (max t, sum 2^((t - max) * cf)); greedy mode (max t,
-// argmax bits).
+// Sample mode writes (m, sum 2^((t - m) * cf)) with m the maximum over the
+// eight tiles of the tile's wave (any m >= the tile's own maximum gives the
+// same tile weight); greedy mode (max t, argmax bits).
 // ---------------------------------------------------------------------------
 constexpr int kStatBlocksPerCU = 8;
 constexpr int kStatWaveTiles = 8;                                   // tiles per wave per item
@@ -232,10 +233,11 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
         if (lane == (cx >> 2)) a.tx_out[m.orow] = val;
       }
     }
+    static_assert(kStatWaveTiles == 8, "the transposing reductions take eight tiles");
+    if constexpr (kGreedy) {
 #pragma unroll
-    for (int j = 0; j < kStatWaveTiles; ++j) {
-      const int c0 = (m.tw + j) * kTgtCols + 4 * lane;
-      if constexpr (kGreedy) {
+      for (int j = 0; j < kStatWaveTiles; ++j) {
+        const int c0 = (m.tw + j) * kTgtCols + 4 * lane;
         float bv = v[j][0];
         int bi = c0;
 #pragma unroll
@@ -247,33 +249,29 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
         }
         pa[j] = bv;
         pb[j] = __int_as_float(bi);
-      } else {
-        const float mx = fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3]));
-        const float mc = mx * a.cf;
+      }
+      wave_transpose8(pa, pb, lane, MergeArgmax{});
+    } else {
+      // One shift for all of the wave's tiles, the wave's maximum M: every
+      // tile's sum is taken relative to it, so merging sums is plain
+      // addition.  A term more than 126 / cf below M may flush to zero; it
+      // is below 2^-126 of the maximum's own term.
+      float lm = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < kStatWaveTiles; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lm = fmaxf(lm, v[j][e]);
+      const float M = wave_max_dpp(lm);
+      const float mc = M == -__builtin_inff() ? 0.0f : M * a.cf;
+#pragma unroll
+      for (int j = 0; j < kStatWaveTiles; ++j) {
         float sum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sum += fast_exp2(fmaf(v[j][e], a.cf, -mc));
-        pa[j] = mx;
-        pb[j] = mx == -__builtin_inff() ? 0.0f : sum;
+        pb[j] = sum;
       }
-    }
-    // Transposing reduction of the wave's kStatWaveTiles pairs: lane l ends
-    // with tile (l >> 3) & 7 of the wave, merged over all 64 lanes.
-    static_assert(kStatWaveTiles == 8, "three exchange steps, then three merges");
-    auto reduce = [&](const auto& merge) {
-      xstep<4>(pa, pb, lane, 32, merge);
-      xstep<2>(pa, pb, lane, 16, merge);
-      xstep<1>(pa, pb, lane, 8, merge);
-#pragma unroll
-      for (int o = 4; o > 0; o >>= 1) {
-        const float ra = __shfl_xor(pa[0], o), rb = __shfl_xor(pb[0], o);
-        merge(pa[0], pb[0], ra, rb);
-      }
-    };
-    if constexpr (kGreedy) {
-      reduce(MergeArgmax{});
-    } else {
-      reduce(MergeMS{a.cf});
+      wave_transpose_sum8(pb, lane);
+      pa[0] = M;
     }
     const int t = m.tw + 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
     if ((lane & 7) == 0 && t < a.ntv) a.tpart[(size_t)m.orow * a.ntv + t] = make_float2(pa[0], pb[0]);
