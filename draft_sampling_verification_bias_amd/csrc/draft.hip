@@ -259,10 +259,12 @@ __device__ __noinline__ double draft_uniform(uint64_t seed, uint64_t round, int 
 }
 
 constexpr int kWaveTiles = 2048;                 // up to V = 262144
-constexpr int kWavePer = kWaveTiles / kWave;      // summaries per lane (max)
 constexpr int kMaxRQuarter = 512 / 4;             // k per wave (r <= 512)
 
-template <bool kBf16>
+// kWavePer: summaries per lane, the smallest instantiated count that covers
+// the row (the searches are unrolled over it, and they sit on the critical
+// path of every position).
+template <bool kBf16, int kWavePer>
 __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectArgs a) {
   __shared__ float sbias[4][kTileCols];
   const int b = blockIdx.x;
@@ -461,6 +463,23 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
   store_ring_operand<kBf16>(a, b, lane_i32(mytok, own2), lane);
 }
 
+template <bool kBf16>
+static hipError_t launch_select_wave(const SelectArgs& sa, hipStream_t s) {
+  const int per = (sa.ntiles + kWave - 1) / kWave;
+  ProfScope prof(s, kProfDraftSelect);
+  if (per <= 8) {
+    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 8>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+  } else if (per <= 16) {
+    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 16>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+  } else if (per <= 20) {
+    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 20>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+  } else {
+    static_assert(kWaveTiles == 32 * kWave, "largest instantiation covers kWaveTiles");
+    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 32>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+  }
+  return hipGetLastError();
+}
+
 size_t draft_workspace(int B, int gamma, int V, int r) {
   (void)gamma;
   // tile summaries, look-ahead uniforms, ring-kernel operands (r = 256 only)
@@ -536,13 +555,7 @@ hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s) {
     if (greedy) {
       e = bf16 ? launch_select<true, true>(sa, s) : launch_select<true, false>(sa, s);
     } else if (ntiles <= kWaveTiles) {
-      ProfScope prof(s, kProfDraftSelect);
-      if (bf16) {
-        hipLaunchKernelGGL((draft_select_wave_kernel<true>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
-      } else {
-        hipLaunchKernelGGL((draft_select_wave_kernel<false>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
-      }
-      e = hipGetLastError();
+      e = bf16 ? launch_select_wave<true>(sa, s) : launch_select_wave<false>(sa, s);
     } else {
       e = bf16 ? launch_select<false, true>(sa, s) : launch_select<false, false>(sa, s);
     }

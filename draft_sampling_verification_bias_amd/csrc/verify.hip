@@ -590,7 +590,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
 // proposals are evaluated 16 at a time -- four per wave, 16 lanes each --
 // and the waves agree on the lowest kept proposal through LDS.
 // ---------------------------------------------------------------------------
-constexpr int kLaneTiles = kPrefixMax / kWave;                    // 16 summaries per lane
+constexpr int kLaneTilesMax = kPrefixMax / kWave;                 // 16 summaries per lane
 constexpr int kPropBatch = 4 * (kVThreads / kWave);               // proposals per batch
 
 // Weight of a tile summary relative to the row maximum M (cf = log2(e) / T).
@@ -601,8 +601,9 @@ __device__ __forceinline__ double tile_weight(const float2& p, float M, float cf
 // The lane's share [t0, t1) of a row's tile summaries and the row's
 // normaliser: M = max, Z = sum of the tile weights, incl / excl = the
 // cumulative weight through / before this lane's share.
+template <int kLT>
 struct RowScan {
-  float2 p[kLaneTiles];
+  float2 p[kLT];
   int t0, t1;
   float M;
   double local, excl, incl, Z;
@@ -610,15 +611,16 @@ struct RowScan {
 
 // (Selects rather than branches, and DPP lane moves for the wave max and
 // scan: this sits on the critical path of every decision.)
-__device__ __forceinline__ void row_scan(RowScan& s, float cf, double (&cumi)[kLaneTiles], unsigned& wmask) {
+template <int kLT>
+__device__ __forceinline__ void row_scan(RowScan<kLT>& s, float cf, double (&cumi)[kLT], unsigned& wmask) {
   float lm = -__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < kLaneTiles; ++j) lm = s.t0 + j < s.t1 ? fmaxf(lm, s.p[j].x) : lm;
+  for (int j = 0; j < kLT; ++j) lm = s.t0 + j < s.t1 ? fmaxf(lm, s.p[j].x) : lm;
   s.M = wave_max_dpp(lm);
   double loc = 0.0;
   wmask = 0u;
 #pragma unroll
-  for (int j = 0; j < kLaneTiles; ++j) {
+  for (int j = 0; j < kLT; ++j) {
     const float e = fast_exp2((s.p[j].x - s.M) * cf);
     const bool live = s.t0 + j < s.t1 && s.p[j].x != -__builtin_inff();
     const double wt = live ? (double)s.p[j].y * (double)e : 0.0;
@@ -632,7 +634,7 @@ __device__ __forceinline__ void row_scan(RowScan& s, float cf, double (&cumi)[kL
   s.Z = lane_f64(s.incl, kWave - 1);
   double cum = s.excl;  // the lane's inclusive cumulative weights, in tile order
 #pragma unroll
-  for (int j = 0; j < kLaneTiles; ++j) {
+  for (int j = 0; j < kLT; ++j) {
     cum += cumi[j];
     cumi[j] = cum;
   }
@@ -641,7 +643,8 @@ __device__ __forceinline__ void row_scan(RowScan& s, float cf, double (&cumi)[kL
 // Tile of the first cumulative weight above q among positive tiles (the last
 // positive tile if rounding leaves none), the cumulative weight before it
 // and its maximum.  q is the same on every lane; so are the results.
-__device__ __forceinline__ void tile_search(const RowScan& s, const double (&cumi)[kLaneTiles], unsigned wmask,
+template <int kLT>
+__device__ __forceinline__ void tile_search(const RowScan<kLT>& s, const double (&cumi)[kLT], unsigned wmask,
                                             double q, int& ts_o, double& base_o, float& mt_o) {
   const unsigned long long cross = __ballot(s.local > 0.0 && s.incl > q);
   const unsigned long long pos = __ballot(s.local > 0.0);
@@ -650,7 +653,7 @@ __device__ __forceinline__ void tile_search(const RowScan& s, const double (&cum
   // result is taken
   int jp = -1, jl = -1;
 #pragma unroll
-  for (int j = 0; j < kLaneTiles; ++j) {
+  for (int j = 0; j < kLT; ++j) {
     const bool on = (wmask >> j) & 1u;
     jl = on ? j : jl;
     jp = (jp < 0 && on && cumi[j] > q) ? j : jp;
@@ -660,7 +663,7 @@ __device__ __forceinline__ void tile_search(const RowScan& s, const double (&cum
   double bb = 0.0;
   float m = s.M;
 #pragma unroll
-  for (int j = 0; j < kLaneTiles; ++j) {
+  for (int j = 0; j < kLT; ++j) {
     const bool sel = j == jj;
     t = sel ? s.t0 + j : t;
     bb = sel ? (j == 0 ? s.excl : cumi[j > 0 ? j - 1 : 0]) : bb;
@@ -774,7 +777,7 @@ __device__ __noinline__ double2 proposal_uniforms(uint64_t seed, uint64_t round,
   return make_double2(unit_uniform(d.w[0]), unit_uniform(d.w[1]));
 }
 
-template <bool kGreedy, bool kBf16>
+template <bool kGreedy, bool kBf16, int kLT>
 __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs w, int ph, int k0, int k1,
                                                                  float cf_f, int ntv) {
   constexpr int kWaves = kVThreads / kWave;
@@ -800,13 +803,13 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
     double ua, lx;
     double2 up;  // lane l: proposal l % 16 of the row (proposal 0 of row gamma+1: the bonus)
   };
-  auto load_row = [&](int rr, RowScan& rsr, RowIn& in) {
+  auto load_row = [&](int rr, RowScan<kLT>& rsr, RowIn& in) {
     const int rc = min(rr, w.lmax - 1);
     const float2* P = w.tpart + ((size_t)b * w.lmax + rc) * ntv;
     rsr.t0 = t0;
     rsr.t1 = t1;
 #pragma unroll
-    for (int j = 0; j < kLaneTiles; ++j) {
+    for (int j = 0; j < kLT; ++j) {
       const int t = t0 + j;
       rsr.p[j] = P[t < t1 ? t : (t1 > 0 ? t1 - 1 : 0)];
     }
@@ -822,7 +825,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       in.up = w.u_prop[((size_t)b * (g + 1) + kp - 1) * kPropPre + (lane & (kPropPre - 1))];
     }
   };
-  RowScan rs[kPreRows];
+  RowScan<kLT> rs[kPreRows];
   RowIn rin[kPreRows];
 #pragma unroll
   for (int rr = 0; rr < kPreRows; ++rr) load_row(rr, rs[rr], rin[rr]);
@@ -845,7 +848,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       float bv = -__builtin_inff();
       int bi = INT_MAX;
 #pragma unroll
-      for (int j = 0; j < kLaneTiles; ++j)
+      for (int j = 0; j < kLT; ++j)
         if (t0 + j < t1) argmax_merge(bv, bi, rs[rr].p[j].x, __float_as_int(rs[rr].p[j].y));
       wave_argmax(bv, bi);
       bool accepted = false;
@@ -868,10 +871,10 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
     const double cf = (double)cf_f;
     // One block position; returns true when the request is finished (a
     // rejection, or the bonus token).
-    auto position = [&](int rr, RowScan& s, int x, int prev, float pdxf, float tx, double lx, double uacc,
+    auto position = [&](int rr, RowScan<kLT>& s, int x, int prev, float pdxf, float tx, double lx, double uacc,
                         double2 up0) -> bool {
       const int k = k0 + rr;
-      double cumi[kLaneTiles];
+      double cumi[kLT];
       unsigned wmask;
       row_scan(s, cf_f, cumi, wmask);
       const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
@@ -941,7 +944,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       // the rule of tile_search.
       if (wave == 0) {
 #pragma unroll
-        for (int j = 0; j < kLaneTiles; ++j) {
+        for (int j = 0; j < kLT; ++j) {
           if (s.t0 + j < s.t1) {
             s_cum[s.t0 + j] = cumi[j];
             s_m[s.t0 + j] = s.p[j].x;
@@ -1006,12 +1009,12 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
     // kPreRows of the phase load their inputs when they are reached.
 #pragma unroll 1
     for (int rr = 0; k0 + rr <= k1; ++rr) {
-      RowScan cur;
+      RowScan<kLT> cur;
       RowIn in;
       if (rr < kPreRows) {
         const bool r1 = rr == 1;
 #pragma unroll
-        for (int j = 0; j < kLaneTiles; ++j) cur.p[j] = r1 ? rs[1].p[j] : rs[0].p[j];
+        for (int j = 0; j < kLT; ++j) cur.p[j] = r1 ? rs[1].p[j] : rs[0].p[j];
         cur.t0 = t0;
         cur.t1 = t1;
         in = r1 ? rin[1] : rin[0];
@@ -1148,6 +1151,28 @@ __global__ __launch_bounds__(kVThreads) void residual_select_kernel(VerifyArgs a
 }
 
 // ---------------------------------------------------------------------------
+// The decision kernel instantiated for the smallest summaries-per-lane count
+// that covers ntv (its row searches are unrolled over that count).
+template <bool kGreedy, bool kBf16>
+static void launch_decide(const VerifyArgs& a, const VerifyWs& w, int ph, int k0, int k1, float cf, int ntv,
+                          hipStream_t s) {
+  const int per = (ntv + kWave - 1) / kWave;
+  if (per <= 8) {
+    hipLaunchKernelGGL((verify_decide_kernel<kGreedy, kBf16, 8>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1,
+                       cf, ntv);
+  } else if (per <= 10) {
+    hipLaunchKernelGGL((verify_decide_kernel<kGreedy, kBf16, 10>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1,
+                       cf, ntv);
+  } else if (per <= 12) {
+    hipLaunchKernelGGL((verify_decide_kernel<kGreedy, kBf16, 12>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1,
+                       cf, ntv);
+  } else {
+    static_assert(kLaneTilesMax == 16, "largest instantiation covers kPrefixMax");
+    hipLaunchKernelGGL((verify_decide_kernel<kGreedy, kBf16, 16>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1,
+                       cf, ntv);
+  }
+}
+
 hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
   VerifyArgs a = a_in;
   const bool greedy = a.temperature == 0.0f;
@@ -1194,14 +1219,11 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
     ProfScope prof(s, kProfVerifyDecide);
     if (ntv <= kPrefixMax) {  // one workgroup per request (those not undecided in this phase exit)
       if (greedy) {
-        hipLaunchKernelGGL((verify_decide_kernel<true, true>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1, cf,
-                           ntv);
+        launch_decide<true, true>(a, w, ph, k0, k1, cf, ntv, s);
       } else if (bf16) {
-        hipLaunchKernelGGL((verify_decide_kernel<false, true>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1,
-                           cf, ntv);
+        launch_decide<false, true>(a, w, ph, k0, k1, cf, ntv, s);
       } else {
-        hipLaunchKernelGGL((verify_decide_kernel<false, false>), dim3(a.B), dim3(kVThreads), 0, s, a, w, ph, k0, k1,
-                           cf, ntv);
+        launch_decide<false, false>(a, w, ph, k0, k1, cf, ntv, s);
       }
     } else if (greedy) {
       hipLaunchKernelGGL((verify_decide_generic_kernel<true, true>), dim3(dgrid), dim3(kVThreads), 0, s, a, w, ph, k0,
