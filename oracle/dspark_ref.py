@@ -187,7 +187,7 @@ def residual_sample(pt, pd, seed, rnd, j, max_proposals, dists):
 
 
 def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=64,
-           requests=None):
+           requests=None, lengths=None):
     """Rejection-sampling verification of every request's drafted block
     ([R] "Speculative Decoding: Draft, Then Verify" step 3; [E] section 2).
 
@@ -204,6 +204,13 @@ def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=64,
     (x_1..x_n, y, -1...), accept_prob [B][gamma] (alpha_k of tested positions,
     NaN after), min_dist [B] (smallest boundary distance of all draws of the
     request; inf at T = 0).
+
+    ``lengths`` ([B], optional): the scheduled verification lengths l_b of
+    [R] "The Hardware-Aware Prefix Scheduler" (Algorithm 1).  Only x_1..x_l
+    are offered to the target; if all of them pass, the bonus token comes
+    from the target row l+1 (stream 2 at position l+1, index 0), so l = 0
+    emits one token drawn from p_t^1 (plain decoding) and l = gamma is the
+    full block.
     """
     B, gamma, V = U.shape
     reqs = range(B) if requests is None else requests
@@ -216,8 +223,9 @@ def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=64,
         prev = int(x0[b])
         dists = []
         emitted = []
-        n = gamma
-        for k in range(1, gamma + 1):
+        ell = gamma if lengths is None else int(lengths[b])
+        n = ell
+        for k in range(1, ell + 1):
             x = int(draft_tokens[b, k - 1])
             lt = target_logits(tgt[b, k - 1], T)
             if T == 0:
@@ -243,13 +251,13 @@ def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=64,
             emitted.append(residual_sample(pt, pd, seed, rnd, k, max_proposals, dists))
             n = k - 1
             break
-        if n == gamma:
-            lt = target_logits(tgt[b, gamma], T)
+        if n == ell:
+            lt = target_logits(tgt[b, ell], T)
             if T == 0:
                 emitted.append(first_argmax(lt))
             else:
                 pt, _ = softmax(lt)
-                u = philox.uniform(seed, rnd, gamma + 1, philox.STREAM_RESIDUAL)
+                u = philox.uniform(seed, rnd, ell + 1, philox.STREAM_RESIDUAL)
                 y, d = inverse_cdf(pt, u)
                 dists.append(d)
                 emitted.append(y)
@@ -300,3 +308,55 @@ def survival(U, W1, W2, x0, draft_tokens, tgt, T, conf=None, requests=None):
                 c[b, k - 1] = acceptance_rate(pd, pt)
             prev = x
     return c, np.cumprod(c, axis=1)
+
+
+# ----------------------------------------------------------------------------
+# Hardware-aware prefix scheduler
+# ----------------------------------------------------------------------------
+
+def schedule(a, sps, early_stop=True, trace=None):
+    """Algorithm 1 of [R] "The Hardware-Aware Prefix Scheduler": per-request
+    verification lengths that maximise Theta = tau * SPS(B).
+
+    a: [R][gamma] prefix survival probabilities a_{r,j} (non-increasing in j);
+    sps: SPS(n) for n = 0, 1, ... (at least R (gamma + 1) + 1 entries), the
+    profiled throughput at n verified tokens.  Every (r, j) with a_{r,j} > 0
+    is a candidate; candidates are taken in descending a, ties to the lowest
+    request id ([R] "Common Questions Answered"), then the lowest position.
+    Starting from l = 0, B = R, tau = R, each candidate sets l_r = j and adds
+    one token to B and a_{r,j} to tau; Theta = tau * SPS(B) is kept as the
+    new best while it improves, and the scan stops at the first candidate
+    that does not improve it (the non-anticipating early stop of "The
+    Non-Anticipating Property").  ``early_stop=False`` scans every candidate
+    and keeps the global best: the anticipating variant the pages show to be
+    lossy, here only as a test of that claim.
+
+    Returns (lengths [R] int, Theta_best, margin): margin is the smallest
+    |Theta - Theta_best| over the comparisons made (a decision closer than
+    rounding may differ on the GPU).  With a list ``trace``, every admitted
+    candidate appends (r, j, B, tau, Theta), r and j 1-based as on the pages.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    R, gamma = a.shape
+    pool = [(a[r, j], r, j + 1) for r in range(R) for j in range(gamma) if a[r, j] > 0]
+    pool.sort(key=lambda e: (-e[0], e[1], e[2]))
+    cur = [0] * R
+    size = R
+    tau = float(R)
+    best = tau * float(sps[size])
+    best_len = list(cur)
+    margin = math.inf
+    for val, r, j in pool:
+        cur[r] = j
+        size += 1
+        tau += val
+        theta = tau * float(sps[size])
+        if trace is not None:
+            trace.append((r + 1, j, size, tau, theta))
+        margin = min(margin, abs(theta - best))
+        if theta > best:
+            best = theta
+            best_len = list(cur)
+        elif early_stop:
+            break
+    return np.array(best_len, dtype=np.int32), best, margin
