@@ -60,7 +60,9 @@ def load():
     lib.dspark_markov_draft.restype = I
     lib.dspark_markov_draft.argtypes = [P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
     lib.dspark_verify.restype = I
-    lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_schedule.restype = I
+    lib.dspark_schedule.argtypes = [P, P, I, I, I, P, P, P]
     lib.dspark_transpose_w2.restype = I
     lib.dspark_transpose_w2.argtypes = [P, I, I, I, P, P]
     lib.dspark_survival.restype = I
@@ -193,9 +195,10 @@ def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=Non
 
 
 def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, rnd, out=None,
-           with_accept_prob=True, workspace=None, stream=None, W2T=None):
+           with_accept_prob=True, workspace=None, stream=None, W2T=None, lengths=None):
     """Rejection-sampling verification.  Returns (accept_len, out_tokens, accept_prob or None).
-    W2T: optional transposed copy of W2 from transpose_w2."""
+    W2T: optional transposed copy of W2 from transpose_w2.  lengths: optional
+    int32 [B] scheduled verification lengths (from schedule)."""
     B, g1, V = target.shape
     gamma = g1 - 1
     dev = target.device
@@ -215,6 +218,8 @@ def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, 
         _dev(draft_prob, "draft_prob", torch.float32, (B, gamma))
     if seeds is not None:
         _dev(seeds, "seeds", torch.uint64, (B,))
+    if lengths is not None:
+        _dev(lengths, "lengths", torch.int32, (B,))
     if out is None:
         out = (torch.empty((B,), dtype=torch.int32, device=dev),
                torch.empty((B, gamma + 1), dtype=torch.int32, device=dev),
@@ -226,10 +231,33 @@ def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, 
         _dev(aprob, "accept_prob", torch.float32, (B, gamma))
     ws, nbytes = _workspace(OP_VERIFY, B, gamma, V, r, workspace, dev)
     st = load().dspark_verify(_p(U), _p(W1), _p(W2), _p(W2T), wd, _p(x0), _p(draft_tokens), _p(draft_prob), _p(target),
-                              B, gamma, V, r, float(temperature), _p(seeds), int(rnd), _p(alen), _p(otok),
-                              _p(aprob), _p(ws), nbytes, _stream(stream, dev))
+                              _p(lengths), B, gamma, V, r, float(temperature), _p(seeds), int(rnd), _p(alen),
+                              _p(otok), _p(aprob), _p(ws), nbytes, _stream(stream, dev))
     _check("dspark_verify", st)
     return alen, otok, aprob
+
+
+def schedule(survival, sps, out=None, with_theta=True, stream=None):
+    """Hardware-aware prefix scheduler: survival float32 [B][gamma], sps
+    float64 [n >= B (gamma + 1) + 1] (sps[n] = SPS(n)).  Returns (lengths
+    int32 [B], theta float64 [1] or None)."""
+    B, gamma = survival.shape
+    dev = survival.device
+    _dev(survival, "survival", torch.float32)
+    _dev(sps, "sps", torch.float64)
+    if sps.dim() != 1:
+        raise ValueError("sps must be one-dimensional")
+    if out is None:
+        out = (torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((1,), dtype=torch.float64, device=dev) if with_theta else None)
+    lengths, theta = out
+    _dev(lengths, "lengths", torch.int32, (B,))
+    if theta is not None:
+        _dev(theta, "theta", torch.float64, (1,))
+    st = load().dspark_schedule(_p(survival), _p(sps), int(sps.shape[0]), B, gamma, _p(lengths), _p(theta),
+                                _stream(stream, dev))
+    _check("dspark_schedule", st)
+    return lengths, theta
 
 
 def transpose_w2(W2, out=None, stream=None):

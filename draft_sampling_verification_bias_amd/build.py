@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "profile.cpp", "tile_pass.hip", "draft.hip", "verify.hip", "survival.hip", "weights.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "tile_pass.hip", "draft.hip", "verify.hip", "survival.hip", "weights.hip",
+           "schedule.hip"]
 
 
 def hipcc():

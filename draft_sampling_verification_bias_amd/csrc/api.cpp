@@ -100,15 +100,15 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
 
 dspark_status dspark_verify(const float* U, const void* W1, const void* W2, const void* W2T, dspark_dtype wdtype,
                             const int32_t* x0,
-                            const int32_t* draft_tokens, const float* draft_prob, const float* target_logits, int B,
-                            int gamma, int V, int r, float temperature, const uint64_t* seeds, uint64_t round,
-                            int32_t* accept_len, int32_t* out_tokens, float* accept_prob, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+                            const int32_t* draft_tokens, const float* draft_prob, const float* target_logits,
+                            const int32_t* lengths, int B, int gamma, int V, int r, float temperature,
+                            const uint64_t* seeds, uint64_t round, int32_t* accept_len, int32_t* out_tokens,
+                            float* accept_prob, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
   const bool greedy = temperature == 0.0f;
   if (!req(x0, 4) || !req(draft_tokens, 4) || !req(target_logits, 16) || !req(accept_len, 4) ||
-      !req(out_tokens, 4) || !opt(accept_prob, 4) || !req(workspace, 16))
+      !req(out_tokens, 4) || !opt(accept_prob, 4) || !opt(lengths, 4) || !req(workspace, 16))
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (!greedy && (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !opt(W2T, 16) || !req(draft_prob, 4) ||
                   !req(seeds, 8)))
@@ -133,8 +133,17 @@ dspark_status dspark_verify(const float* U, const void* W1, const void* W2, cons
   a.accept_len = accept_len;
   a.out_tokens = out_tokens;
   a.accept_prob = accept_prob;
+  a.lengths = lengths;
   a.ws = workspace;
   return from_hip(launch_verify(a, wdtype == DSPARK_BF16, stream));
+}
+
+dspark_status dspark_schedule(const float* survival, const double* sps, int sps_len, int B, int gamma,
+                              int32_t* lengths, double* theta, hipStream_t stream) {
+  if (B < 1 || gamma < 1 || gamma > kMaxGamma || (long long)B * gamma > kScheduleMax) return DSPARK_ERR_INVALID_ARGUMENT;
+  if ((long long)sps_len < (long long)B * (gamma + 1) + 1) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!req(survival, 4) || !req(sps, 8) || !req(lengths, 4) || !opt(theta, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_schedule(survival, sps, B, gamma, lengths, theta, stream));
 }
 
 dspark_status dspark_transpose_w2(const void* W2, dspark_dtype wdtype, int r, int V, void* W2T, hipStream_t stream) {

@@ -101,6 +101,7 @@ struct VerifyArgs {
   int32_t* accept_len;
   int32_t* out_tokens;
   float* accept_prob;
+  const int32_t* lengths;  // optional [B] scheduled verification lengths (null: gamma)
   void* ws;
   double inv_t_d;  // 1 / T, filled in by launch_verify
 };
@@ -156,6 +157,12 @@ hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, h
 // Compute units of the current device (queried once per device).
 int compute_units_of_device();
 
+// Hardware-aware prefix scheduler (schedule.hip): one workgroup, at most
+// kScheduleMax candidates (B * gamma).
+constexpr int kScheduleMax = 4096;
+hipError_t launch_schedule(const float* survival, const double* sps, int B, int gamma, int32_t* lengths,
+                           double* theta, hipStream_t s);
+
 hipError_t launch_transpose_w2(const void* W2, bool bf16, int r, int V, void* W2T, hipStream_t s);
 
 hipError_t launch_markov_bias(const void* W1, const void* W2, bool bf16, const int32_t* tokens,
@@ -165,7 +172,7 @@ hipError_t launch_markov_bias(const void* W1, const void* W2, bool bf16, const i
 enum ProfKind : int {
   kProfTileSample = 0, kProfTileGreedy, kProfTileOverlap, kProfTileBias, kProfDraftSelect,
   kProfVerifyInit, kProfTargetStats, kProfVerifyDecide, kProfResidualStats, kProfResidualSelect,
-  kProfSurvivalConf, kProfSurvivalTnorm, kProfSurvivalFinish, kProfKinds
+  kProfSurvivalConf, kProfSurvivalTnorm, kProfSurvivalFinish, kProfSchedule, kProfKinds
 };
 
 // Brackets the launches made during its lifetime with HIP events when timing

@@ -383,6 +383,7 @@ __global__ __launch_bounds__(kVThreads) void verify_init_kernel(VerifyArgs a, Ve
     int valid = 0;
     if (b < a.B) {
       valid = a.x0[b] >= 0 && a.x0[b] < a.V;
+      if (a.lengths) valid &= a.lengths[b] >= 0 && a.lengths[b] <= g;
       for (int k = 0; k < g; ++k) {
         const int t = a.draft_tokens[(size_t)b * g + k];
         valid &= (t >= 0 && t < a.V);
@@ -470,6 +471,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
   const double cf = (double)cf_f;
   for (int li = blockIdx.x; li < count; li += gridDim.x) {
     const int b = w.lists[(size_t)ph * a.B + li];
+    const int lb = a.lengths ? a.lengths[b] : g;  // scheduled length (validated by the init kernel)
     for (int k = k0; k <= k1; ++k) {
       const float2* P = w.tpart + ((size_t)b * w.lmax + (k - k0)) * ntv;
       const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
         int bi = INT_MAX;
         for (int t = threadIdx.x; t < ntv; t += kVThreads) argmax_merge(bv, bi, P[t].x, __float_as_int(P[t].y));
         block_argmax<kVThreads>(bv, bi, sv, si);
-        if (k <= g) {
+        if (k <= lb) {
           const int x = a.draft_tokens[(size_t)b * g + k - 1];
           accepted = bi == x;
           if (threadIdx.x == 0) {
@@ -487,9 +489,9 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
             a.out_tokens[(size_t)b * (g + 1) + k - 1] = accepted ? x : bi;
             if (!accepted) a.accept_len[b] = k - 1;
           }
-        } else if (threadIdx.x == 0) {
-          a.out_tokens[(size_t)b * (g + 1) + g] = bi;
-          a.accept_len[b] = g;
+        } else if (threadIdx.x == 0) {  // bonus token from the position after the scheduled block
+          a.out_tokens[(size_t)b * (g + 1) + lb] = bi;
+          a.accept_len[b] = lb;
         }
       } else {
         float lm = -__builtin_inff();
@@ -507,12 +509,12 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
           return p.x == -__builtin_inff() ? 0.0 : (double)p.y * exp2((double)(p.x - c.M) * cf);
         };
         const double Z = block_total<kVThreads>(ntv, tile_weight, ps);
-        if (k > g) {  // bonus token from the position after the block
-          const double u = unit_uniform(draw_block(seed, a.round, g + 1, kStreamResidual, 0).w[0]);
+        if (k > lb) {  // bonus token from the position after the scheduled block
+          const double u = unit_uniform(draw_block(seed, a.round, lb + 1, kStreamResidual, 0).w[0]);
           const int y = sample_target(c, u, ps, sterm, nullptr);
           if (threadIdx.x == 0) {
-            a.out_tokens[(size_t)b * (g + 1) + g] = y;
-            a.accept_len[b] = g;
+            a.out_tokens[(size_t)b * (g + 1) + lb] = y;
+            a.accept_len[b] = lb;
           }
         } else {
           const int x = a.draft_tokens[(size_t)b * g + k - 1];
@@ -794,6 +796,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
   // is undecided in this phase, the summaries of the phase's rows, tokens,
   // p_d(x), t(x) and the draft logit of x, and the uniforms drawn ahead.
   const int alive = w.alive[b];
+  const int lb = a.lengths ? a.lengths[b] : g;  // scheduled length (validated by the init kernel)
   // The inputs of one block position of the phase (row rr of the phase's
   // summaries); positions past k1 are clamped so that every load stays in
   // bounds (their values are not used).
@@ -852,16 +855,16 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
         if (t0 + j < t1) argmax_merge(bv, bi, rs[rr].p[j].x, __float_as_int(rs[rr].p[j].y));
       wave_argmax(bv, bi);
       bool accepted = false;
-      if (k <= g) {
+      if (k <= lb) {
         accepted = bi == rin[rr].x;
         if (threadIdx.x == 0) {
           if (a.accept_prob) a.accept_prob[(size_t)b * g + k - 1] = accepted ? 1.0f : 0.0f;
           a.out_tokens[(size_t)b * (g + 1) + k - 1] = accepted ? rin[rr].x : bi;
           if (!accepted) a.accept_len[b] = k - 1;
         }
-      } else if (threadIdx.x == 0) {
-        a.out_tokens[(size_t)b * (g + 1) + g] = bi;
-        a.accept_len[b] = g;
+      } else if (threadIdx.x == 0) {  // bonus token from the position after the scheduled block
+        a.out_tokens[(size_t)b * (g + 1) + lb] = bi;
+        a.accept_len[b] = lb;
       }
       if (!accepted) return;
       if (k == k1) carry_on();
@@ -878,7 +881,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       unsigned wmask;
       row_scan(s, cf_f, cumi, wmask);
       const float* trow = a.target + ((size_t)b * (g + 1) + (k - 1)) * (size_t)a.V;
-      if (k > g) {  // bonus token from the position after the block
+      if (k > lb) {  // bonus token from the position after the scheduled block
         const double q = __shfl(up0.x, 0) * s.Z;
         int ts;
         double base;
@@ -888,8 +891,8 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
         float ty;
         col_draw<kWave>(trow, a.V, ts, mt, s.M, cf_f, cf, q - base, y, ty);
         if (threadIdx.x == 0) {
-          a.out_tokens[(size_t)b * (g + 1) + g] = y;
-          a.accept_len[b] = g;
+          a.out_tokens[(size_t)b * (g + 1) + lb] = y;
+          a.accept_len[b] = lb;
         }
         return true;
       }

@@ -8,7 +8,8 @@
  *       Correction" (Eq. 4), "Instantiation 1: The Markov Head" (Eq. 5),
  *       "The Confidence Head" (Eq. 8), "Deriving the Acceptance-Rate Identity
  *       Behind Equation 8" (Eq. 8a-8c), "The Hardware-Aware Prefix Scheduler"
- *       (cumulative products), "Common Questions Answered" (greedy decoding),
+ *       (cumulative products, Algorithm 1), "The Non-Anticipating Property"
+ *       (Eq. 9-10), "Common Questions Answered" (greedy decoding, ties),
  *       "Putting It All Together: The Full Decode Loop as Pseudocode".
  *   [E] "Speculative decoding, from zero to DSpark", section 2 "The loop, and
  *       why it's lossless" (residual rule, bonus token).
@@ -160,22 +161,33 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
  * correction or bonus token is argmax target[b][n+1] ([R] "Common Questions
  * Answered").
  *
+ * lengths is optional (NULL: every request verifies its whole block): int32
+ * [B], the scheduled verification lengths l_b of [R] "The Hardware-Aware
+ * Prefix Scheduler" (as dspark_schedule writes them).  Only x_1..x_l are
+ * offered to the target: n <= l, and if all l pass, the bonus token is drawn
+ * from p_t^{l+1} (target row l+1) with the stream-2 uniform at (round, l+1,
+ * index 0), so l = 0 emits one token drawn from p_t^1 and l = gamma is the
+ * full block.  A length outside [0, gamma] invalidates that request like a
+ * bad token id.  The lengths must be fixed before the drafted tokens are
+ * seen (non-anticipating, [R] "The Non-Anticipating Property"): a schedule
+ * that depends on them changes the output law.
+ *
  * W2T is optional (NULL to skip): W2 transposed, [V][r] in the weight dtype,
  * as written by dspark_transpose_w2.  When given, p_d at a single token reads
  * one contiguous row of W2T instead of r elements spread over W2; the results
  * differ from the W2-only path only by the summation order of float64 sums.
  * Inputs draft_tokens / draft_prob are dspark_markov_draft's outputs.
  * Outputs:
- *   accept_len   int32   [B]          n in 0..gamma
+ *   accept_len   int32   [B]          n in 0..l (l = gamma without lengths)
  *   out_tokens   int32   [B][gamma+1] x_1..x_n, then the correction or bonus
  *                                     token, then -1
  *   accept_prob  float32 [B][gamma]   alpha_k for the tested positions
- *                                     k <= min(n+1, gamma), NaN after; NULL to skip
+ *                                     k <= min(n+1, l), NaN after; NULL to skip
  * Workspace: dspark_workspace_size(DSPARK_OP_VERIFY, B, gamma, V, r).
  */
 dspark_status dspark_verify(const float* U, const void* W1, const void* W2, const void* W2T, dspark_dtype wdtype,
                             const int32_t* x0, const int32_t* draft_tokens,
-                            const float* draft_prob, const float* target_logits,
+                            const float* draft_prob, const float* target_logits, const int32_t* lengths,
                             int B, int gamma, int V, int r, float temperature,
                             const uint64_t* seeds, uint64_t round,
                             int32_t* accept_len, int32_t* out_tokens, float* accept_prob,
@@ -217,6 +229,37 @@ dspark_status dspark_survival(const float* U, const void* W1, const void* W2, ds
                               const float* conf, int B, int gamma, int V, int r,
                               float temperature, float* c_star, float* survival,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_schedule -- the hardware-aware prefix scheduler, Algorithm 1 of [R]
+ * "The Hardware-Aware Prefix Scheduler": per-request verification lengths
+ * that maximise the expected token throughput Theta = tau * SPS(n).
+ *
+ *   survival  float32 [B][gamma]  a_{b,j}, the prefix survival products (as
+ *                                 dspark_survival writes them); entries <= 0
+ *                                 or NaN are not candidates
+ *   sps       float64 [sps_len]   sps[n] = SPS(n), the profiled target
+ *                                 throughput at n verified tokens;
+ *                                 sps_len >= B (gamma + 1) + 1
+ *   lengths   int32 [B]           out: l*_b in 0..gamma
+ *   theta     float64 [1]         out: Theta_best (NULL to skip)
+ *
+ * The candidates (b, j) are admitted in descending a_{b,j}, ties to the
+ * lowest request and then the lowest position ([R] "Common Questions
+ * Answered").  Starting from n = B verified tokens and tau = B, the m-th
+ * admission adds one token and a_{b,j} to tau; the scan keeps the admission
+ * while Theta = tau * sps[n] improves on the previous value and stops at the
+ * first one that does not (the early stop that keeps the schedule
+ * non-anticipating, [R] "The Non-Anticipating Property", Eq. 9-10).  l*_b is
+ * the largest position admitted for b; with survivals that do not increase
+ * along a block, the admitted positions of b are exactly 1..l*_b (Lemma 1).
+ * tau is summed in float64; decisions whose two Theta values agree to
+ * rounding may resolve either way.
+ * 1 <= gamma <= 32, 1 <= B * gamma <= 4096.  Asynchronous on `stream`; needs
+ * no workspace.
+ */
+dspark_status dspark_schedule(const float* survival, const double* sps, int sps_len, int B, int gamma,
+                              int32_t* lengths, double* theta, hipStream_t stream);
 
 /*
  * Per-kernel timing (tracing).  dspark_profile_enable(1) clears earlier

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("dspark_markov_draft", "dspark_verify", "dspark_survival", "dspark_markov_bias",
+    for n in ("dspark_markov_draft", "dspark_verify", "dspark_survival", "dspark_markov_bias", "dspark_schedule",
               "dspark_workspace_size", "dspark_status_string", "dspark_version"):
         assert n in names
 
@@ -86,18 +86,19 @@ def test_draft_rejects_bad_arguments(lib, kw, status):
 
 
 def _verify(lib, **kw):
-    a = dict(U=FAKE, W1=FAKE, W2=FAKE, W2T=None, wd=1, x0=FAKE, dt=FAKE, dp=FAKE, tgt=FAKE, B=4, gamma=4, V=1000,
-             r=16, T=1.0, seeds=FAKE, rnd=0, alen=FAKE, otok=FAKE, aprob=None, ws=FAKE, wsb=1 << 30)
+    a = dict(U=FAKE, W1=FAKE, W2=FAKE, W2T=None, wd=1, x0=FAKE, dt=FAKE, dp=FAKE, tgt=FAKE, lens=None, B=4, gamma=4,
+             V=1000, r=16, T=1.0, seeds=FAKE, rnd=0, alen=FAKE, otok=FAKE, aprob=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
-    return lib.dspark_verify(a["U"], a["W1"], a["W2"], a["W2T"], a["wd"], a["x0"], a["dt"], a["dp"], a["tgt"], a["B"],
-                             a["gamma"], a["V"], a["r"], a["T"], a["seeds"], a["rnd"], a["alen"], a["otok"],
-                             a["aprob"], a["ws"], a["wsb"], None)
+    return lib.dspark_verify(a["U"], a["W1"], a["W2"], a["W2T"], a["wd"], a["x0"], a["dt"], a["dp"], a["tgt"],
+                             a["lens"], a["B"], a["gamma"], a["V"], a["r"], a["T"], a["seeds"], a["rnd"], a["alen"],
+                             a["otok"], a["aprob"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=70000), INVALID), (dict(tgt=None), INVALID), (dict(alen=None), INVALID),
     (dict(dp=None), INVALID), (dict(tgt=MISALIGNED), INVALID), (dict(wd=9), UNSUPPORTED),
     (dict(wsb=0), WORKSPACE), (dict(T=-0.5), INVALID), (dict(W2T=MISALIGNED), INVALID),
+    (dict(lens=MISALIGNED - 2), INVALID),
 ])
 def test_verify_rejects_bad_arguments(lib, kw, status):
     assert _verify(lib, **kw) == status
@@ -134,3 +135,15 @@ def test_markov_bias_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, 1, FAKE, 4, 1000, 17, FAKE, None) == INVALID
     assert f(FAKE, None, 1, FAKE, 4, 1000, 16, FAKE, None) == INVALID
     assert f(FAKE, FAKE, 2, FAKE, 4, 1000, 16, FAKE, None) == UNSUPPORTED
+
+
+def test_schedule_rejects_bad_arguments(lib):
+    f = lib.dspark_schedule
+    # (survival, sps, sps_len, B, gamma, lengths, theta, stream)
+    assert f(FAKE, FAKE, 20, 4, 4, FAKE, None, None) == INVALID      # sps shorter than B (gamma + 1) + 1
+    assert f(FAKE, FAKE, 1 << 20, 0, 4, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 1 << 20, 4, 33, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 1 << 20, 1024, 5, FAKE, None, None) == INVALID  # more than 4096 candidates
+    assert f(None, FAKE, 1 << 20, 4, 4, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 1 << 20, 4, 4, None, None, None) == INVALID
+    assert f(FAKE, MISALIGNED, 1 << 20, 4, 4, FAKE, None, None) == INVALID

@@ -1,0 +1,199 @@
+"""GPU parity of the hardware-aware prefix scheduler (dspark_schedule) and of
+verification with scheduled lengths (dspark_verify's `lengths`) against the
+float64 oracle, through the C ABI.
+
+Lengths are compared exactly; Theta_best within 1e-12 relative.  A schedule
+whose deciding comparison the oracle makes within 1e-9 relative of a tie is
+exempt (the GPU sums tau in a different order) and counted.  Verification
+uses the tolerances of ``parity.py``.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from conftest import golden_path
+from parity import Dev, compare_draft, compare_verify, f64_weights
+
+torch = pytest.importorskip("torch")
+dsp = pytest.importorskip("draft_sampling_verification_bias_amd")
+
+pytestmark = pytest.mark.gpu
+
+THETA_RTOL = 1e-12
+TIE_RTOL = 1e-9
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    dsp.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _gpu_schedule(a, sps):
+    lengths, theta = dsp.schedule(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda(),
+                                  torch.from_numpy(np.ascontiguousarray(sps, dtype=np.float64)).cuda())
+    torch.cuda.synchronize()
+    return lengths.cpu().numpy(), float(theta.cpu().numpy()[0])
+
+
+def _check_schedule(a, sps, label):
+    """Returns 1 if the case was exempt (a near-tie decision), else 0."""
+    a32 = np.ascontiguousarray(a, dtype=np.float32)
+    ref_len, ref_theta, margin = oracle.schedule(a32.astype(np.float64), sps)
+    lengths, theta = _gpu_schedule(a32, sps)
+    if margin <= TIE_RTOL * abs(ref_theta):
+        say("[%s] exempt: deciding margin %.3g" % (label, margin))
+        return 1
+    assert (lengths == ref_len).all(), "[%s] lengths differ at requests %s" % (
+        label, np.flatnonzero(lengths != ref_len)[:10].tolist())
+    assert abs(theta - ref_theta) <= THETA_RTOL * abs(ref_theta), "[%s] theta %r vs %r" % (label, theta, ref_theta)
+    return 0
+
+
+def _printed():
+    ex, cur = [], None
+    for line in open(golden_path("scheduler_worked_examples.txt")):
+        line = line.strip()
+        if line.startswith("["):
+            cur = {"conf": []}
+            ex.append(cur)
+        elif line.startswith("conf "):
+            cur["conf"].append([float(x) for x in line.split()[1:]])
+        elif line.startswith("sps "):
+            pairs = [x.split(":") for x in line.split()[1:]]
+            sps = np.zeros(max(int(n) for n, _ in pairs) + 1)
+            for n, v in pairs:
+                sps[int(n)] = float(v)
+            cur["sps"] = sps
+        elif line.startswith("lengths "):
+            cur["lengths"] = [int(x) for x in line.split()[1:]]
+    return ex
+
+
+def test_schedule_printed_examples():
+    for e in _printed():
+        a = np.cumprod(np.array(e["conf"]), axis=1)
+        lengths, _ = _gpu_schedule(a, e["sps"])
+        assert lengths.tolist() == e["lengths"]
+        assert _check_schedule(a, e["sps"], "printed") == 0
+
+
+@pytest.mark.parametrize("B,gamma", [(1, 1), (1, 7), (7, 3), (256, 7), (512, 7), (585, 7), (128, 32), (4096, 1)])
+def test_schedule_random_parity(B, gamma):
+    rng = np.random.default_rng(B * 100 + gamma)
+    exempt = 0
+    cases = 0
+    for trial in range(6):
+        c = rng.uniform(0.2, 1.0, size=(B, gamma))
+        if trial == 1:
+            c = np.round(c * 4) / 4            # many exact ties (and c = 1: equal survivals within a request)
+        if trial == 2:
+            c[rng.random(c.shape) < 0.2] = 0.0  # zero survivals are not candidates
+        a = np.cumprod(c, axis=1)
+        half = rng.uniform(0.8, 3.0) * B
+        sps = workloads.sps_curve(B * (gamma + 1), half, rng.uniform(1.0, 4.0),
+                                  ripple=0.05 if trial >= 4 else 0.0, seed=trial)
+        exempt += _check_schedule(a, sps, "B=%d gamma=%d trial %d" % (B, gamma, trial))
+        cases += 1
+    say("[schedule B=%d gamma=%d] %d cases, %d exempt" % (B, gamma, cases, exempt))
+    assert exempt <= 1
+
+
+def test_schedule_admits_everything_on_a_flat_curve_and_nothing_on_a_cliff():
+    B, gamma = 300, 7
+    a = np.cumprod(np.full((B, gamma), 0.9), axis=1)
+    lengths, theta = _gpu_schedule(a, np.ones(B * (gamma + 1) + 1))
+    assert (lengths == gamma).all() and abs(theta - (B + a.astype(np.float32).astype(np.float64).sum())) < 1e-9
+    cliff = np.ones(B * (gamma + 1) + 1)
+    cliff[B + 1:] = 1e-3
+    lengths, theta = _gpu_schedule(a, cliff)
+    assert (lengths == 0).all() and theta == B
+
+
+def _scheduled_round(wl, lengths_h, label, reqs=None):
+    d = Dev(wl)
+    tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
+    torch.cuda.synchronize()
+    tok_h = tok.cpu().numpy()
+    W1f, W2f = f64_weights(wl)
+    reqs = list(range(wl.B)) if reqs is None else reqs
+    ref = oracle.markov_draft(wl.U, W1f, W2f, wl.x0, wl.T, wl.seeds, wl.rnd, requests=reqs)
+    n, ex, whole = compare_draft(ref, tok_h, prob.cpu().numpy(), lse.cpu().numpy(), reqs, wl.T)
+    lens_d = torch.from_numpy(np.ascontiguousarray(lengths_h, dtype=np.int32)).cuda()
+    W2T = dsp.transpose_w2(d.W2) if wl.T > 0 else None
+    alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd, W2T=W2T,
+                                   lengths=lens_d)
+    torch.cuda.synchronize()
+    vreq = sorted(whole)
+    vref = oracle.verify(wl.U, W1f, W2f, wl.x0, tok_h, wl.tgt, wl.T, wl.seeds, wl.rnd, requests=vreq,
+                         lengths=lengths_h)
+    alen_h = alen.cpu().numpy()
+    nv, exv = compare_verify(vref, alen_h, otok.cpu().numpy(), aprob.cpu().numpy(), vreq, wl.T)
+    say("[%s] scheduled verify: %d requests equal, %d exempt; mean length %.2f, mean accepted %.3f"
+        % (label, nv, exv, np.mean(lengths_h), alen_h[vreq].mean()))
+    assert nv > 0
+    return tok, lse, d, alen_h
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("v151936_b32", dict(V=4099, B=37, gamma=5)),
+    ("v151936_b256_t07", dict(V=3001, B=40, r=64)),
+    ("greedy_v151936_b512", dict(V=5003, B=70, r=32)),
+    ("v262144_b128", dict(V=2053, B=33, r=48)),
+])
+def test_verify_with_fixed_lengths(name, kw):
+    wl = workloads.make(name, **kw)
+    lengths = (np.arange(wl.B) % (wl.gamma + 1)).astype(np.int32)
+    _, _, _, alen = _scheduled_round(wl, lengths, name)
+    assert (alen <= lengths).all()
+
+
+def test_verify_invalid_length_is_reported_per_request():
+    wl = workloads.make("v151936_b32", V=1000, B=6, gamma=4, r=16)
+    d = Dev(wl)
+    tok, prob, _ = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
+    lengths = torch.tensor([4, -1, 2, 5, 0, 3], dtype=torch.int32, device="cuda")
+    alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd, lengths=lengths)
+    alen, otok, aprob = alen.cpu().numpy(), otok.cpu().numpy(), aprob.cpu().numpy()
+    for b in (1, 3):
+        assert alen[b] == -1 and (otok[b] == -1).all() and np.isnan(aprob[b]).all()
+    for b in (0, 2, 4, 5):
+        assert 0 <= alen[b] <= [4, -1, 2, 5, 0, 3][b]
+
+
+@pytest.mark.parametrize("name", ["v151936_b256_t07", "greedy_v151936_b512"])
+def test_full_size_scheduled_round(name):
+    """Draft, analytical survival, schedule and scheduled verification at full
+    size; the oracle checks the schedule of every request (from the GPU's
+    survival products) and the verification of a sample."""
+    wl = workloads.make(name)
+    d = Dev(wl)
+    tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
+    _, surv = dsp.survival(d.U, d.W1, d.W2, d.x0, tok, lse, d.tgt, wl.T, with_c_star=False)
+    sps = workloads.sps_curve(wl.B * (wl.gamma + 1), 1.5 * wl.B, 3.0)
+    lengths, theta = dsp.schedule(surv, torch.from_numpy(sps).cuda())
+    torch.cuda.synchronize()
+    surv_h, lengths_h = surv.cpu().numpy(), lengths.cpu().numpy()
+    ref_len, ref_theta, margin = oracle.schedule(surv_h.astype(np.float64), sps)
+    assert margin > TIE_RTOL * abs(ref_theta)
+    assert (lengths_h == ref_len).all()
+    assert abs(float(theta.cpu().numpy()[0]) - ref_theta) <= THETA_RTOL * abs(ref_theta)
+    say("[%s] schedule: mean length %.2f of %d" % (name, lengths_h.mean(), wl.gamma))
+    del d
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(5)
+    reqs = sorted(set([0, wl.B - 1] + rng.choice(wl.B, size=4, replace=False).tolist()))
+    _scheduled_round(wl, lengths_h, name + " scheduled", reqs=reqs)
+    torch.cuda.empty_cache()

@@ -178,3 +178,15 @@ def make(name, *, B=None, V=None, gamma=None, r=None, T=None, w_std=None,
     return Workload(name=name, V=Vn, r=R, gamma=G, B=Bn, T=float(spec["T"]),
                     wdtype=spec["wdtype"], U=U, W1=W1, W2=W2, x0=x0, tgt=tgt,
                     seeds=request_seeds(master_seed, Bn), rnd=int(rnd))
+
+
+def sps_curve(n_max, half, power, ripple=0.0, seed=0):
+    """A synthetic profiled throughput table SPS(n), n = 0..n_max, standing in
+    for the engine's measured steps-per-second curve over verified tokens:
+    1 / (1 + (n / half)^power), optionally times (1 + ripple * noise) with
+    noise uniform in [-1, 1] (a jagged curve).  float64."""
+    n = np.arange(n_max + 1, dtype=np.float64)
+    s = 1.0 / (1.0 + (n / float(half)) ** float(power))
+    if ripple:
+        s *= 1.0 + ripple * np.random.default_rng(seed).uniform(-1.0, 1.0, size=n.shape)
+    return s
