@@ -11,7 +11,8 @@ and the accepted lengths change while the input bytes stay fixed.
 Printed (one JSON line): the metric, the fraction of the 8 TB/s HBM peak that
 the step's compulsory bytes reach, the roofline of the dominant kernel (the
 draft tile pass, timed live with HIP events on its own stream), the analytical
-dspark_survival time (reported beside the gated path), and the float64 oracle
+dspark_survival time and the prefix scheduler with verification at its
+lengths (both reported beside the gated path), and the float64 oracle
 timed on the host cores on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
@@ -127,6 +128,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=256, help="requests in the oracle baseline (0: skip)")
     ap.add_argument("--cpu-rounds", type=int, default=6, help="rounds of those requests in the oracle baseline")
     ap.add_argument("--survival-steps", type=int, default=10)
+    ap.add_argument("--schedule-steps", type=int, default=20,
+                    help="timed calls of the prefix scheduler and of verification with its lengths (0: skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="copy this many MiB device to device once before timing (a reference kernel of known "
                          "traffic for hardware counter runs)")
@@ -251,6 +254,46 @@ def main():
         torch.cuda.synchronize()
         surv_ms = (time.perf_counter() - s0) / args.survival_steps * 1e3
 
+    # Hardware-aware prefix scheduler on the analytical survival products of
+    # one round, with a synthetic profiled throughput table; then the same
+    # round verified whole and with the scheduled lengths (reported beside
+    # the gated path).
+    sched = None
+    if args.schedule_steps > 0:
+        cst = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        sv = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        dsp.markov_draft(U, W1, W2, x0, T, seeds, 2000, out=dout, workspace=ws_d, stream=stream)
+        dsp.survival(U, W1, W2, x0, dout[0], dout[2], tgt, T, out=(cst, sv), workspace=ws_s, stream=stream)
+        half, power = 4.0 * B, 2.0
+        sps = torch.from_numpy(workloads.sps_curve(B * (gamma + 1), half, power)).to(dev)
+        lengths, theta = dsp.schedule(sv, sps, stream=stream)
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        for _ in range(args.schedule_steps):
+            dsp.schedule(sv, sps, out=(lengths, theta), stream=stream)
+        torch.cuda.synchronize()
+        sched_us = (time.perf_counter() - s0) / args.schedule_steps * 1e6
+        vo = vouts[0]
+
+        def timed_verify(lens_arg):
+            dsp.verify(U, W1, W2, x0, dout[0], dout[1], tgt, T, seeds, 2000, out=vo, W2T=W2T, workspace=ws_v,
+                       stream=stream, lengths=lens_arg)
+            torch.cuda.synchronize()
+            v0 = time.perf_counter()
+            for _ in range(args.schedule_steps):
+                dsp.verify(U, W1, W2, x0, dout[0], dout[1], tgt, T, seeds, 2000, out=vo, W2T=W2T, workspace=ws_v,
+                           stream=stream, lengths=lens_arg)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - v0) / args.schedule_steps * 1e3, vo[0].cpu().numpy()
+
+        full_ms, full_len = timed_verify(None)
+        sch_ms, sch_len = timed_verify(lengths)
+        lens_h = lengths.cpu().numpy()
+        sched = {"sps": "1/(1+(n/%g)^%g), n = verified tokens" % (half, power), "schedule_us": sched_us,
+                 "mean_length": float(lens_h.mean()), "theta_best": float(theta.cpu().numpy()[0]),
+                 "verify_full_ms": full_ms, "verify_scheduled_ms": sch_ms,
+                 "mean_accept_len_full": float(full_len.mean()), "mean_accept_len_scheduled": float(sch_len.mean())}
+
     flops = 2.0 * r * V * (B * gamma + float((lens < gamma).sum()) / nsteps)
     out = {
         "metric": METRIC,
@@ -276,6 +319,7 @@ def main():
         "kernels": kernels,
         "ms_per_step_with_events": (p1 - p0) / nsteps * 1e3,
         "survival_ms": surv_ms,
+        "schedule": sched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
