@@ -7,8 +7,8 @@ touches it and shares no code with it.
 
 Modules:
   philox      Philox4x64-10 (Salmon et al., SC'11) and the stream layout.
-  dspark_ref  draft, verify, survival and the prefix scheduler in plain
-              float64 numpy.
+  dspark_ref  draft, verify, survival, the confidence head and the prefix
+              scheduler in plain float64 numpy.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, brute-force enumeration, Monte Carlo laws or
@@ -19,6 +19,7 @@ from . import philox  # noqa: F401
 from .dspark_ref import (  # noqa: F401
     EXEMPT_RADIUS,
     acceptance_rate,
+    confidence,
     draft_logits,
     first_argmax,
     inverse_cdf,

@@ -360,3 +360,34 @@ def schedule(a, sps, early_stop=True, trace=None):
         elif early_stop:
             break
     return np.array(best_len, dtype=np.int32), best, margin
+
+
+# ----------------------------------------------------------------------------
+# Confidence head
+# ----------------------------------------------------------------------------
+
+def confidence(h, w, W1, x0, draft_tokens, sts=None, requests=None):
+    """Per-position confidence of Eq. 7 of [R] ("The Confidence Head"):
+    c_k = sigma(w . [h_k ; W1[x_{k-1}]]), with x_0 the anchor, followed by the
+    per-position temperature of Sequential Temperature Scaling (the same
+    section): the logit is divided by the calibrated temperature of position k
+    (temperature scaling of a sigmoid), c_k = sigma(z_k / t_k).
+
+    h: [B][gamma][d] hidden states; w: [d + r] head weights (hidden part
+    first); W1: [V][r] float64 Markov embedding; sts: [gamma] temperatures
+    (None: 1).  Returns c [B][gamma] in float64 (NaN for requests not in
+    ``requests``).
+    """
+    h = np.asarray(h, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, gamma, d = h.shape
+    reqs = range(B) if requests is None else requests
+    c = np.full((B, gamma), np.nan)
+    for b in reqs:
+        prev = int(x0[b])
+        for k in range(1, gamma + 1):
+            z = float(w[:d] @ h[b, k - 1]) + float(w[d:] @ W1[prev])
+            t = 1.0 if sts is None else float(sts[k - 1])
+            c[b, k - 1] = 1.0 / (1.0 + math.exp(-z / t))
+            prev = int(draft_tokens[b, k - 1])
+    return c
