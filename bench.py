@@ -11,8 +11,9 @@ and the accepted lengths change while the input bytes stay fixed.
 Printed (one JSON line): the metric, the fraction of the 8 TB/s HBM peak that
 the step's compulsory bytes reach, the roofline of the dominant kernel (the
 draft tile pass, timed live with HIP events on its own stream), the analytical
-dspark_survival time and the prefix scheduler with verification at its
-lengths (both reported beside the gated path), and the float64 oracle
+dspark_survival time and the scheduled round (confidence head, prefix
+scheduler, verification at its lengths; both reported beside the gated
+path), and the float64 oracle
 timed on the host cores on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
@@ -254,45 +255,66 @@ def main():
         torch.cuda.synchronize()
         surv_ms = (time.perf_counter() - s0) / args.survival_steps * 1e3
 
-    # Hardware-aware prefix scheduler on the analytical survival products of
-    # one round, with a synthetic profiled throughput table; then the same
-    # round verified whole and with the scheduled lengths (reported beside
-    # the gated path).
+    # The scheduled round of the pages' production flow, reported beside the
+    # gated path: confidence head (Eq. 7, synthetic hidden states of width
+    # 4096 and per-position temperatures) on the drafted tokens, survival
+    # products of the confidences, prefix scheduler with a synthetic profiled
+    # throughput table, verification at the scheduled lengths.  The same
+    # drafted round is also verified whole for comparison.
     sched = None
     if args.schedule_steps > 0:
-        cst = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        d_hidden = 4096
+        h_np, w_np, sts_np = workloads.confidence_inputs(B, gamma, d_hidden, r)
+        hd, wd_, stsd = (torch.from_numpy(h_np).to(dev), torch.from_numpy(w_np).to(dev),
+                         torch.from_numpy(sts_np).to(dev))
+        conf = torch.empty((B, gamma), dtype=torch.float32, device=dev)
         sv = torch.empty((B, gamma), dtype=torch.float32, device=dev)
-        dsp.markov_draft(U, W1, W2, x0, T, seeds, 2000, out=dout, workspace=ws_d, stream=stream)
-        dsp.survival(U, W1, W2, x0, dout[0], dout[2], tgt, T, out=(cst, sv), workspace=ws_s, stream=stream)
         half, power = 4.0 * B, 2.0
         sps = torch.from_numpy(workloads.sps_curve(B * (gamma + 1), half, power)).to(dev)
-        lengths, theta = dsp.schedule(sv, sps, stream=stream)
-        torch.cuda.synchronize()
-        s0 = time.perf_counter()
-        for _ in range(args.schedule_steps):
-            dsp.schedule(sv, sps, out=(lengths, theta), stream=stream)
-        torch.cuda.synchronize()
-        sched_us = (time.perf_counter() - s0) / args.schedule_steps * 1e6
+        lengths = torch.empty((B,), dtype=torch.int32, device=dev)
+        theta = torch.empty((1,), dtype=torch.float64, device=dev)
         vo = vouts[0]
 
-        def timed_verify(lens_arg):
-            dsp.verify(U, W1, W2, x0, dout[0], dout[1], tgt, T, seeds, 2000, out=vo, W2T=W2T, workspace=ws_v,
-                       stream=stream, lengths=lens_arg)
-            torch.cuda.synchronize()
-            v0 = time.perf_counter()
-            for _ in range(args.schedule_steps):
-                dsp.verify(U, W1, W2, x0, dout[0], dout[1], tgt, T, seeds, 2000, out=vo, W2T=W2T, workspace=ws_v,
-                           stream=stream, lengths=lens_arg)
-            torch.cuda.synchronize()
-            return (time.perf_counter() - v0) / args.schedule_steps * 1e3, vo[0].cpu().numpy()
+        def plan():
+            dsp.confidence(hd, wd_, W1, x0, dout[0], sts=stsd, out=conf, stream=stream)
+            dsp.survival(None, None, None, None, None, None, None, T, conf=conf, out=(None, sv), stream=stream)
+            dsp.schedule(sv, sps, out=(lengths, theta), stream=stream)
 
-        full_ms, full_len = timed_verify(None)
-        sch_ms, sch_len = timed_verify(lengths)
+        def verify_at(lens_arg, rnd):
+            dsp.verify(U, W1, W2, x0, dout[0], dout[1], tgt, T, seeds, rnd, out=vo, W2T=W2T, workspace=ws_v,
+                       stream=stream, lengths=lens_arg)
+
+        def timed(fn):
+            fn(0)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for i in range(args.schedule_steps):
+                fn(i)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t) / args.schedule_steps * 1e3
+
+        dsp.markov_draft(U, W1, W2, x0, T, seeds, 2000, out=dout, workspace=ws_d, stream=stream)
+        plan_ms = timed(lambda i: plan())
+        full_ms = timed(lambda i: verify_at(None, 2000))
+        full_len = vo[0].cpu().numpy()
+        sch_ms = timed(lambda i: verify_at(lengths, 2000))
+        sch_len = vo[0].cpu().numpy()
+
+        def round_scheduled(i):
+            dsp.markov_draft(U, W1, W2, x0, T, seeds, 3000 + i, out=dout, workspace=ws_d, stream=stream)
+            plan()
+            verify_at(lengths, 3000 + i)
+
+        round_ms = timed(round_scheduled)
         lens_h = lengths.cpu().numpy()
-        sched = {"sps": "1/(1+(n/%g)^%g), n = verified tokens" % (half, power), "schedule_us": sched_us,
-                 "mean_length": float(lens_h.mean()), "theta_best": float(theta.cpu().numpy()[0]),
+        sched = {"flow": "draft, confidence head (d=%d, STS), survival of the confidences, schedule, verify at the "
+                         "scheduled lengths" % d_hidden,
+                 "sps": "1/(1+(n/%g)^%g), n = verified tokens" % (half, power),
+                 "plan_ms": plan_ms, "mean_length": float(lens_h.mean()),
+                 "theta_best": float(theta.cpu().numpy()[0]),
                  "verify_full_ms": full_ms, "verify_scheduled_ms": sch_ms,
-                 "mean_accept_len_full": float(full_len.mean()), "mean_accept_len_scheduled": float(sch_len.mean())}
+                 "mean_accept_len_full": float(full_len.mean()), "mean_accept_len_scheduled": float(sch_len.mean()),
+                 "round_scheduled_ms": round_ms}
 
     flops = 2.0 * r * V * (B * gamma + float((lens < gamma).sum()) / nsteps)
     out = {

@@ -61,6 +61,8 @@ def load():
     lib.dspark_markov_draft.argtypes = [P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
     lib.dspark_verify.restype = I
     lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_confidence.restype = I
+    lib.dspark_confidence.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, P, P]
     lib.dspark_schedule.restype = I
     lib.dspark_schedule.argtypes = [P, P, I, I, I, P, P, P]
     lib.dspark_transpose_w2.restype = I
@@ -235,6 +237,29 @@ def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, 
                               _p(otok), _p(aprob), _p(ws), nbytes, _stream(stream, dev))
     _check("dspark_verify", st)
     return alen, otok, aprob
+
+
+def confidence(h, w, W1, x0, draft_tokens, sts=None, out=None, stream=None):
+    """Confidence head: h float32 [B][gamma][d], w float32 [d + r], W1 [V][r],
+    sts optional float32 [gamma].  Returns conf float32 [B][gamma]."""
+    B, gamma, d = h.shape
+    V, r = W1.shape
+    dev = h.device
+    _dev(h, "h", torch.float32)
+    _dev(w, "w", torch.float32, (d + r,))
+    _dev(W1, "W1", None)
+    wd = _wdtype(W1, W1)
+    _dev(x0, "x0", torch.int32, (B,))
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, gamma))
+    if sts is not None:
+        _dev(sts, "sts", torch.float32, (gamma,))
+    if out is None:
+        out = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    _dev(out, "conf", torch.float32, (B, gamma))
+    st = load().dspark_confidence(_p(h), _p(w), _p(W1), wd, _p(x0), _p(draft_tokens), _p(sts), B, gamma, d, V, r,
+                                  _p(out), _stream(stream, dev))
+    _check("dspark_confidence", st)
+    return out
 
 
 def schedule(survival, sps, out=None, with_theta=True, stream=None):

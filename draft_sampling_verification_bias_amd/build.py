@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libdspark.so")
 
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "profile.cpp", "tile_pass.hip", "draft.hip", "verify.hip", "survival.hip", "weights.hip",
-           "schedule.hip"]
+           "schedule.hip", "confidence.hip"]
 
 
 def hipcc():

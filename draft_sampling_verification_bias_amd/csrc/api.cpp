@@ -138,6 +138,30 @@ dspark_status dspark_verify(const float* U, const void* W1, const void* W2, cons
   return from_hip(launch_verify(a, wdtype == DSPARK_BF16, stream));
 }
 
+dspark_status dspark_confidence(const float* h, const float* w, const void* W1, dspark_dtype wdtype,
+                                const int32_t* x0, const int32_t* draft_tokens, const float* sts, int B, int gamma,
+                                int d, int V, int r, float* conf, hipStream_t stream) {
+  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma, V, r) || d < 1 || d > (1 << 20)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!req(h, 16) || !req(w, 16) || !req(W1, 16) || !req(x0, 4) || !req(draft_tokens, 4) || !opt(sts, 4) ||
+      !req(conf, 4))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  ConfArgs a = {};
+  a.h = h;
+  a.w = w;
+  a.W1 = W1;
+  a.x0 = x0;
+  a.tokens = draft_tokens;
+  a.sts = sts;
+  a.B = B;
+  a.gamma = gamma;
+  a.d = d;
+  a.V = V;
+  a.r = r;
+  a.conf = conf;
+  return from_hip(launch_confidence(a, wdtype == DSPARK_BF16, stream));
+}
+
 dspark_status dspark_schedule(const float* survival, const double* sps, int sps_len, int B, int gamma,
                               int32_t* lengths, double* theta, hipStream_t stream) {
   if (B < 1 || gamma < 1 || gamma > kMaxGamma || (long long)B * gamma > kScheduleMax) return DSPARK_ERR_INVALID_ARGUMENT;

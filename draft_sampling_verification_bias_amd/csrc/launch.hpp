@@ -157,6 +157,19 @@ hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, h
 // Compute units of the current device (queried once per device).
 int compute_units_of_device();
 
+// Confidence head (confidence.hip).
+struct ConfArgs {
+  const float* h;        // [B][gamma][d] hidden states
+  const float* w;        // [d + r] head weights, hidden part first
+  const void* W1;        // [V][r] Markov embedding
+  const int32_t* x0;     // [B]
+  const int32_t* tokens; // [B][gamma] drafted tokens
+  const float* sts;      // [gamma] temperatures (null: 1)
+  int B, gamma, d, V, r;
+  float* conf;           // [B][gamma]
+};
+hipError_t launch_confidence(const ConfArgs& a, bool bf16, hipStream_t s);
+
 // Hardware-aware prefix scheduler (schedule.hip): one workgroup, at most
 // kScheduleMax candidates (B * gamma).
 constexpr int kScheduleMax = 4096;
@@ -172,7 +185,7 @@ hipError_t launch_markov_bias(const void* W1, const void* W2, bool bf16, const i
 enum ProfKind : int {
   kProfTileSample = 0, kProfTileGreedy, kProfTileOverlap, kProfTileBias, kProfDraftSelect,
   kProfVerifyInit, kProfTargetStats, kProfVerifyDecide, kProfResidualStats, kProfResidualSelect,
-  kProfSurvivalConf, kProfSurvivalTnorm, kProfSurvivalFinish, kProfSchedule, kProfKinds
+  kProfSurvivalConf, kProfSurvivalTnorm, kProfSurvivalFinish, kProfSchedule, kProfConfidence, kProfKinds
 };
 
 // Brackets the launches made during its lifetime with HIP events when timing

@@ -231,6 +231,34 @@ dspark_status dspark_survival(const float* U, const void* W1, const void* W2, ds
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dspark_confidence -- the confidence head of [R] "The Confidence Head"
+ * (Eq. 7) with the per-position temperatures of Sequential Temperature
+ * Scaling (same section):
+ *   c_{b,k} = sigma(z / t_k),  z = w . [h_{b,k} ; W1[x_{k-1}]]   (x_0 = x0[b])
+ * for k = 1..gamma, the scalar the scheduler's survival products are built
+ * from (dspark_survival in confidence mode, then dspark_schedule) before the
+ * target runs.
+ *
+ *   h             float32 [B][gamma][d]  backbone hidden states h_k
+ *   w             float32 [d + r]        head weights: hidden part, then
+ *                                        embedding part (no bias term)
+ *   W1            [V][r]                 the Markov embedding of the draft
+ *   x0            int32 [B]              anchors
+ *   draft_tokens  int32 [B][gamma]       dspark_markov_draft's tokens (x_k
+ *                                        feeds position k+1; x_gamma is unused)
+ *   sts           float32 [gamma]        calibrated temperatures t_k > 0
+ *                                        (NULL: 1, the raw head)
+ *   conf          float32 [B][gamma]     out: c_{b,k}; NaN where the previous
+ *                                        token is outside [0, V)
+ * z is summed in float64 from the float32 products.  1 <= d <= 2^20; the
+ * other sizes as for dspark_markov_draft.  Asynchronous on `stream`; needs
+ * no workspace.
+ */
+dspark_status dspark_confidence(const float* h, const float* w, const void* W1, dspark_dtype wdtype,
+                                const int32_t* x0, const int32_t* draft_tokens, const float* sts, int B, int gamma,
+                                int d, int V, int r, float* conf, hipStream_t stream);
+
+/*
  * dspark_schedule -- the hardware-aware prefix scheduler, Algorithm 1 of [R]
  * "The Hardware-Aware Prefix Scheduler": per-request verification lengths
  * that maximise the expected token throughput Theta = tau * SPS(n).

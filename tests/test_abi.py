@@ -36,6 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dspark_markov_draft", "dspark_verify", "dspark_survival", "dspark_markov_bias", "dspark_schedule",
+              "dspark_confidence",
               "dspark_workspace_size", "dspark_status_string", "dspark_version"):
         assert n in names
 
@@ -147,3 +148,24 @@ def test_schedule_rejects_bad_arguments(lib):
     assert f(None, FAKE, 1 << 20, 4, 4, FAKE, None, None) == INVALID
     assert f(FAKE, FAKE, 1 << 20, 4, 4, None, None, None) == INVALID
     assert f(FAKE, MISALIGNED, 1 << 20, 4, 4, FAKE, None, None) == INVALID
+
+
+def test_confidence_rejects_bad_arguments(lib):
+    f = lib.dspark_confidence
+    # (h, w, W1, wdtype, x0, tokens, sts, B, gamma, d, V, r, conf, stream)
+    ok = [FAKE, FAKE, FAKE, 1, FAKE, FAKE, None, 4, 4, 64, 1000, 16, FAKE, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a9=0) == INVALID            # d = 0
+    assert call(a7=0) == INVALID            # B = 0
+    assert call(a11=24) == INVALID          # r not a multiple of 16
+    assert call(a0=None) == INVALID
+    assert call(a1=MISALIGNED) == INVALID   # w not 16-byte aligned
+    assert call(a6=MISALIGNED - 2) == INVALID
+    assert call(a12=None) == INVALID
+    assert call(a3=7) == UNSUPPORTED

@@ -182,7 +182,7 @@ def test_full_size_scheduled_round(name):
     d = Dev(wl)
     tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
     _, surv = dsp.survival(d.U, d.W1, d.W2, d.x0, tok, lse, d.tgt, wl.T, with_c_star=False)
-    sps = workloads.sps_curve(wl.B * (wl.gamma + 1), 1.5 * wl.B, 3.0)
+    sps = workloads.sps_curve(wl.B * (wl.gamma + 1), 4.0 * wl.B, 2.0)
     lengths, theta = dsp.schedule(surv, torch.from_numpy(sps).cuda())
     torch.cuda.synchronize()
     surv_h, lengths_h = surv.cpu().numpy(), lengths.cpu().numpy()

@@ -2,4 +2,4 @@
 benchmark.  Holds data recipes only."""
 
 from .gen import (NAMES, WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make, request_seeds,  # noqa: F401
-                  sps_curve)
+                  confidence_inputs, sps_curve)

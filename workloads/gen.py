@@ -190,3 +190,16 @@ def sps_curve(n_max, half, power, ripple=0.0, seed=0):
     if ripple:
         s *= 1.0 + ripple * np.random.default_rng(seed).uniform(-1.0, 1.0, size=n.shape)
     return s
+
+
+def confidence_inputs(B, gamma, d, r, seed=0, spread=1.5):
+    """Synthetic inputs of the confidence head: hidden states h ~ N(0, 1)
+    [B][gamma][d], head weights w [d + r] ~ N(0, spread / sqrt(d)) (so the
+    hidden part of the logit has standard deviation about `spread`) and
+    per-position temperatures rising from 0.8 to 1.6 over the block.
+    float32."""
+    rng = np.random.default_rng(5000 + seed)
+    h = _normal(rng, (B, gamma, d), 1.0)
+    w = _normal(rng, (d + r,), spread / np.sqrt(d))
+    sts = np.linspace(0.8, 1.6, gamma).astype(np.float32)
+    return h, w, sts
