@@ -13,8 +13,9 @@
 // block make the admitted positions of every request contiguous from 1.
 //
 // One workgroup: candidate keys (descending survival, then index) are sorted
-// in LDS by a bitonic network, the sorted survivals are summed in float64 by
-// a block scan, every thread tests Theta at its own admission counts, and the
+// by a bitonic network held in registers (shuffles within a wave, LDS only for
+// partners in other waves), the sorted survivals are summed in float64 by a
+// block scan, every thread tests Theta at its own admission counts, and the
 // first non-improving count is found by an LDS atomic minimum.
 #include <limits.h>
 
@@ -25,7 +26,23 @@ namespace dspark {
 
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedWaves = kSchedThreads / kWave;
+constexpr int kSchedPer = kScheduleMax / kSchedThreads;  // keys per lane at most (4)
 
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x, int m) {
+  const unsigned lo = __shfl_xor((unsigned)x, m), hi = __shfl_xor((unsigned)(x >> 32), m);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Compare-exchange of two keys: ascending order if up.
+__device__ __forceinline__ void cmp_swap(unsigned long long& a, unsigned long long& b, bool up) {
+  const unsigned long long lo = a < b ? a : b, hi = a < b ? b : a;
+  a = up ? lo : hi;
+  b = up ? hi : lo;
+}
+
+// kE keys per lane: the sort covers 1024 kE keys (kE = 1, 2 or 4), and every
+// stage of the network is resolved at compile time.
+template <int kE>
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __restrict__ surv,
                                                                  const double* __restrict__ sps, int B, int gamma,
                                                                  int32_t* __restrict__ lengths, double* theta_out) {
@@ -36,57 +53,103 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int n = B * gamma;
-  int np2 = 1;
-  while (np2 < n) np2 <<= 1;
+  constexpr int np2 = kSchedThreads * kE;
+  constexpr int E = kE;
+  // Lane `lane` of wave w holds the keys of indices w 64E + 64q + lane.
+  auto idx = [&](int q) { return wave * kWave * E + q * kWave + lane; };
 
   if (tid == 0) {
     s_valid = 0;
     s_stop = INT_MAX;
   }
   for (int i = tid; i < B; i += kSchedThreads) len[i] = 0;
-  __syncthreads();
   // Key of candidate i = r gamma + (j - 1): the complemented bits of its
   // (positive) survival above its index, so ascending keys are descending
   // survivals with ties in index order.  Non-candidates (a <= 0 or NaN) and
   // the padding sort last.
+  unsigned long long v[kSchedPer];
   int mine = 0;
-  for (int i = tid; i < np2; i += kSchedThreads) {
+#pragma unroll
+  for (int q = 0; q < kSchedPer; ++q) {
+    const int i = idx(q);
     unsigned long long k = ~0ull;
-    if (i < n) {
-      const float v = surv[i];
-      if (v > 0.0f) {
-        k = ((unsigned long long)(~__float_as_uint(v)) << 32) | (unsigned)i;
+    if (q < E && i < n) {
+      const float a = surv[i];
+      if (a > 0.0f) {
+        k = ((unsigned long long)(~__float_as_uint(a)) << 32) | (unsigned)i;
         ++mine;
       }
     }
-    key[i] = k;
+    v[q] = k;
   }
+  __syncthreads();
   if (mine) atomicAdd(&s_valid, mine);
   __syncthreads();
 
+  // This thread's share of the admission counts, and its throughput table
+  // entries, loaded now so that they arrive during the sort.
+  const int M = s_valid;
+  const int per = (M + kSchedThreads - 1) / kSchedThreads;  // <= kSchedPer
+  const int c0 = min(M, tid * per), c1 = min(M, c0 + per);
+  double sp[kSchedPer + 1];
+#pragma unroll
+  for (int t = 0; t <= kSchedPer; ++t) sp[t] = sps[B + min(c0 + t, c1)];
+
+  // Bitonic sort, ascending.  Partners at distance j < 64 are in other lanes
+  // of the wave (shuffles), 64 <= j < 64E in other registers of the lane,
+  // j >= 64E in other waves (through LDS, two barriers).
+#pragma unroll
   for (int k = 2; k <= np2; k <<= 1) {
+#pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < np2; i += kSchedThreads) {
-        const int p = i ^ j;
-        if (p > i) {
-          const unsigned long long x = key[i], y = key[p];
-          if ((x > y) == ((i & k) == 0)) {
-            key[i] = y;
-            key[p] = x;
+      if (j >= kWave * E) {
+#pragma unroll
+        for (int q = 0; q < kSchedPer; ++q)
+          if (q < E) key[idx(q)] = v[q];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kSchedPer; ++q) {
+          if (q < E) {
+            const int i = idx(q), p = i ^ j;
+            const unsigned long long y = key[p];
+            const bool keep_min = ((i & k) == 0) == (i < p);
+            v[q] = keep_min ? (v[q] < y ? v[q] : y) : (v[q] < y ? y : v[q]);
           }
         }
+        __syncthreads();
+      } else if (j >= kWave) {  // j = 64 or 128: pairs of registers (E >= 2)
+        if (j == kWave) {
+          cmp_swap(v[0], v[1], (idx(0) & k) == 0);
+          if (E == 4) cmp_swap(v[2], v[3], (idx(2) & k) == 0);
+        } else {
+          cmp_swap(v[0], v[2], (idx(0) & k) == 0);
+          cmp_swap(v[1], v[3], (idx(1) & k) == 0);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+          const unsigned long long y = shfl_xor_u64(v[q], j);
+          const int i = idx(q);
+          const bool keep_min = ((i & k) == 0) == ((lane & j) == 0);
+          v[q] = keep_min ? (v[q] < y ? v[q] : y) : (v[q] < y ? y : v[q]);
+        }
       }
-      __syncthreads();
     }
   }
+#pragma unroll
+  for (int q = 0; q < kSchedPer; ++q)
+    if (q < E) key[idx(q)] = v[q];
+  __syncthreads();
 
-  // Thread t owns the sorted candidates [t per, t per + per) of the M valid.
-  const int M = s_valid;
-  const int per = (M + kSchedThreads - 1) / kSchedThreads;
-  const int c0 = min(M, tid * per), c1 = min(M, c0 + per);
+  // Thread t owns the sorted candidates [c0, c1) of the M valid.
   auto value = [&](int pos) -> double { return (double)__uint_as_float(~(unsigned)(key[pos] >> 32)); };
+  double vals[kSchedPer];
   double local = 0.0;
-  for (int pos = c0; pos < c1; ++pos) local += value(pos);
+#pragma unroll
+  for (int t = 0; t < kSchedPer; ++t) {
+    vals[t] = c0 + t < c1 ? value(c0 + t) : 0.0;
+    local += vals[t];
+  }
   // exclusive block scan of the thread sums
   double incl = local;
   for (int o = 1; o < kWave; o <<= 1) {
@@ -99,25 +162,31 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
   for (int w = 0; w < wave; ++w) base += wtot[w];
   const double S0 = base + incl - local;  // sum of the survivals sorted before c0
 
-  // Theta(m) against Theta(m - 1) at this thread's admission counts m = pos + 1
+  // Theta(m) against Theta(m - 1) at this thread's admission counts m = c0 + t + 1
   const double Bd = (double)B;
-  double S = S0;
-  double prev_theta = (Bd + S) * sps[B + c0];
-  for (int pos = c0; pos < c1; ++pos) {
-    S += value(pos);
-    const double theta = (Bd + S) * sps[B + pos + 1];
-    if (!(theta > prev_theta)) {
-      atomicMin(&s_stop, pos + 1);
-      break;
+  {
+    double S = S0;
+    double prev_theta = (Bd + S) * sp[0];
+    bool going = true;
+#pragma unroll
+    for (int t = 0; t < kSchedPer; ++t) {
+      if (going && c0 + t < c1) {
+        S += vals[t];
+        const double theta = (Bd + S) * sp[t + 1];
+        if (!(theta > prev_theta)) {
+          atomicMin(&s_stop, c0 + t + 1);
+          going = false;
+        }
+        prev_theta = theta;
+      }
     }
-    prev_theta = theta;
   }
   __syncthreads();
   const int mstar = s_stop == INT_MAX ? M : s_stop - 1;
 
   for (int pos = tid; pos < mstar; pos += kSchedThreads) {
-    const unsigned idx = (unsigned)key[pos];
-    atomicMax(&len[idx / (unsigned)gamma], (int)(idx % (unsigned)gamma) + 1);
+    const unsigned id = (unsigned)key[pos];
+    atomicMax(&len[id / (unsigned)gamma], (int)(id % (unsigned)gamma) + 1);
   }
   // Theta_best = Theta(m*), summed in the order of the comparisons above by
   // the thread that owns candidate m* - 1
@@ -125,9 +194,15 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
     if (mstar == 0) {
       if (tid == 0) *theta_out = Bd * sps[B];
     } else if (c0 < mstar && mstar <= c1) {
-      double s = S0;
-      for (int pos = c0; pos < mstar; ++pos) s += value(pos);
-      *theta_out = (Bd + s) * sps[B + mstar];
+      double S = S0, th = 0.0;
+#pragma unroll
+      for (int t = 0; t < kSchedPer; ++t) {
+        if (c0 + t < mstar) {
+          S += vals[t];
+          th = (Bd + S) * sp[t + 1];
+        }
+      }
+      *theta_out = th;
     }
   }
   __syncthreads();
@@ -137,7 +212,15 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
 hipError_t launch_schedule(const float* survival, const double* sps, int B, int gamma, int32_t* lengths,
                            double* theta, hipStream_t s) {
   ProfScope prof(s, kProfSchedule);
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, lengths, theta);
+  const int n = B * gamma;
+  if (n <= kSchedThreads) {
+    hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, lengths, theta);
+  } else if (n <= 2 * kSchedThreads) {
+    hipLaunchKernelGGL(schedule_kernel<2>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, lengths, theta);
+  } else {
+    static_assert(kScheduleMax == 4 * kSchedThreads, "the largest instantiation covers kScheduleMax");
+    hipLaunchKernelGGL(schedule_kernel<4>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, lengths, theta);
+  }
   return hipGetLastError();
 }
 
