@@ -19,6 +19,7 @@ from . import philox  # noqa: F401
 from .dspark_ref import (  # noqa: F401
     EXEMPT_RADIUS,
     acceptance_rate,
+    admit_top,
     confidence,
     draft_logits,
     first_argmax,
@@ -27,6 +28,7 @@ from .dspark_ref import (  # noqa: F401
     markov_draft,
     residual_sample,
     schedule,
+    schedule_capacity,
     softmax,
     survival,
     target_logits,

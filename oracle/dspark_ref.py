@@ -391,3 +391,31 @@ def confidence(h, w, W1, x0, draft_tokens, sts=None, requests=None):
             c[b, k - 1] = 1.0 / (1.0 + math.exp(-z / t))
             prev = int(draft_tokens[b, k - 1])
     return c
+
+
+def schedule_capacity(a, sps):
+    """The capacity K of the asynchronous adaptation in [R] "The Asynchronous
+    Fix, and Why It Stays Lossless": the unconstrained search over the whole
+    sorted scan of Algorithm 1 (no early stop, so a jagged SPS curve cannot
+    trap it), run on survival products from two steps earlier.  K is the
+    number of draft-token admissions at the first maximum of Theta (0: none).
+    Returns (K, Theta at K)."""
+    a = np.asarray(a, dtype=np.float64)
+    lengths, best, _ = schedule(a, sps, early_stop=False)
+    return int(lengths.sum()), best
+
+
+def admit_top(a, K):
+    """The live half of the asynchronous adaptation (same section): the
+    current candidates, in Algorithm 1's order (descending a_{r,j}, ties to
+    the lowest request, then position, a > 0 only), fill the K admissions
+    decided earlier.  Returns the per-request lengths (largest admitted
+    position)."""
+    a = np.asarray(a, dtype=np.float64)
+    R, gamma = a.shape
+    pool = [(a[r, j], r, j + 1) for r in range(R) for j in range(gamma) if a[r, j] > 0]
+    pool.sort(key=lambda e: (-e[0], e[1], e[2]))
+    lengths = np.zeros(R, dtype=np.int32)
+    for _, r, j in pool[:max(0, int(K))]:
+        lengths[r] = max(lengths[r], j)
+    return lengths

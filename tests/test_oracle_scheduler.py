@@ -3,7 +3,9 @@ DSpark technical review, "The Hardware-Aware Prefix Scheduler") and of
 verification with scheduled lengths: the printed worked traces, Lemmas 1-2
 against brute force over every length assignment, and the non-anticipation
 counterexample of Eq. 9-10 as a law test through draft, scheduler and
-verifier."""
+verifier; and the asynchronous adaptation (capacity from an unconstrained
+search on earlier survivals, admission of the current top-K), pinned by the
+same printed curves, a jagged curve, brute force and a law test."""
 
 import itertools
 import math
@@ -248,3 +250,92 @@ def test_fixed_scheduled_lengths_keep_the_round_lossless(T):
         assert chisquare(second[x], law2 * second[x].sum()).pvalue > 1e-4
         tested += 1
     assert tested >= 2
+
+
+# ----------------------------------------------------------------------------
+# The asynchronous adaptation ("Adapting Algorithm 1 to Real Hardware: Two
+# Conflicts", "The Asynchronous Fix, and Why It Stays Lossless"): capacity K
+# from an unconstrained search on earlier survival products, admission of the
+# current top-K candidates.
+# ----------------------------------------------------------------------------
+
+def test_capacity_on_the_printed_curves_is_their_global_maximum():
+    ex = _examples()
+    for name, K in (("two", 1), ("three", 1), ("eq9", 0)):
+        e = ex[name]
+        a = np.cumprod(np.array(e["conf"]), axis=1)
+        k, theta = ref.schedule_capacity(a, e["sps"])
+        assert k == K and _close(theta, e["best"])
+
+
+def test_jagged_curve_traps_the_early_stop_but_not_the_capacity_search():
+    # Conflict 1: a cliff right after B = R stops the causal scan at once;
+    # the unconstrained search finds the maximum past it.
+    a = np.array([[0.9, 0.8, 0.7]])
+    sps = np.array([np.nan, 1.0, 0.5, 0.49, 0.48])
+    assert ref.schedule(a, sps)[0].tolist() == [0]
+    k, theta = ref.schedule_capacity(a, sps)
+    assert k == 3 and abs(theta - 3.4 * 0.48) < 1e-12
+
+
+def test_capacity_is_the_optimum_over_every_assignment_on_any_curve():
+    rng = np.random.default_rng(12)
+    for _ in range(60):
+        R, gamma = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        a = np.cumprod(rng.random((R, gamma)), axis=1)
+        sps = np.concatenate([[np.nan], rng.random(R * (gamma + 1))])   # jagged
+        k, theta = ref.schedule_capacity(a, sps)
+        brute = max((R + sum(a[r, :l].sum() for r, l in enumerate(ls))) * sps[R + sum(ls)]
+                    for ls in itertools.product(range(gamma + 1), repeat=R))
+        assert abs(theta - brute) < 1e-12
+        lengths = ref.admit_top(a, k)
+        assert lengths.sum() == k
+        assert abs((R + sum(a[r, :l].sum() for r, l in enumerate(lengths))) * sps[R + k] - theta) < 1e-12
+
+
+def test_top_k_admission_is_prefix_closed_and_bounded():
+    rng = np.random.default_rng(13)
+    a = np.cumprod(np.round(rng.uniform(0.2, 1.0, size=(9, 5)) * 4) / 4, axis=1)   # with ties
+    order = []
+    ref.schedule(a, np.ones(60), early_stop=False, trace=order)
+    for K in range(0, 50):
+        lengths = ref.admit_top(a, K)
+        assert lengths.sum() == min(K, 45)
+        # the admitted set is the first K candidates of Algorithm 1's order
+        seen = [0] * 9
+        for r, j, _, _, _ in order[:K]:
+            seen[r - 1] = max(seen[r - 1], j)
+        assert lengths.tolist() == seen
+    assert ref.admit_top(np.array([[0.5, 0.0], [0.0, 0.0]]), 5).tolist() == [1, 0]
+
+
+def _lagged_round(B, K, rnd):
+    """Two requests per pair: request 2i is the Eq. 9-10 counterexample
+    (p_d = (0.5, 0.5), p_t = (0.7, 0.3), c_2 = 0.9 after A and 0 after B),
+    request 2i+1 has survivals (0.7, 0.35) fixed.  With capacity K fixed
+    before the draft, the second admission goes to request 2i's position 2
+    after A (0.72 > 0.7) and to request 2i+1 otherwise."""
+    V, gamma = 2, 2
+    U = np.zeros((B, gamma, V), dtype=np.float32)
+    tgt = np.tile(np.log(np.array([0.7, 0.3])).astype(np.float32), (B, gamma + 1, 1))
+    W1, W2 = np.zeros((V, 2)), np.zeros((2, V))
+    x0 = np.zeros(B, dtype=np.int32)
+    seeds = (np.arange(B, dtype=np.uint64) + np.uint64(rnd * B)) * np.uint64(69069) + np.uint64(5)
+    d = ref.markov_draft(U, W1, W2, x0, 1.0, seeds, rnd)
+    lengths = np.empty(B, dtype=np.int32)
+    for p in range(0, B, 2):
+        c2 = 0.9 if d["tokens"][p, 0] == 0 else 0.0
+        a = np.array([[0.8, 0.8 * c2], [0.7, 0.35]])
+        lengths[p:p + 2] = ref.admit_top(a, K)
+    v = ref.verify(U, W1, W2, x0, d["tokens"], tgt, 1.0, seeds, rnd, lengths=lengths)
+    return v["out_tokens"][:, 0], lengths
+
+
+@pytest.mark.slow
+def test_lagged_capacity_admission_is_lossless():
+    n = 20000
+    first, lengths = _lagged_round(n, 2, 3)
+    assert set(np.unique(lengths[1::2])) == {0, 1}       # request 2i+1's admission varies with 2i's draft
+    for part in (first[0::2], first[1::2]):
+        m = len(part)
+        assert abs((part == 0).mean() - 0.7) < 5 * math.sqrt(0.21 / m)
