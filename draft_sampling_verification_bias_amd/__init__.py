@@ -16,11 +16,14 @@ import torch
 
 __all__ = [
     "DsparkError", "OP_DRAFT", "OP_VERIFY", "OP_SURVIVAL", "MAX_RESIDUAL_PROPOSALS",
+    "SCHEDULE_EARLY_STOP", "SCHEDULE_CAPACITY", "SCHEDULE_TOP_K",
     "library_path", "load", "version", "workspace_size", "markov_bias",
-    "markov_draft", "verify", "transpose_w2", "survival", "profile_enable", "profile_read",
+    "markov_draft", "verify", "transpose_w2", "survival", "confidence", "schedule", "profile_enable",
+    "profile_read",
 ]
 
 OP_DRAFT, OP_VERIFY, OP_SURVIVAL = 0, 1, 2
+SCHEDULE_EARLY_STOP, SCHEDULE_CAPACITY, SCHEDULE_TOP_K = 0, 1, 2
 _F32, _BF16 = 0, 1
 MAX_RESIDUAL_PROPOSALS = 64
 
@@ -64,7 +67,7 @@ def load():
     lib.dspark_confidence.restype = I
     lib.dspark_confidence.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, P, P]
     lib.dspark_schedule.restype = I
-    lib.dspark_schedule.argtypes = [P, P, I, I, I, P, P, P]
+    lib.dspark_schedule.argtypes = [P, P, I, I, I, I, P, P, P, P, P]
     lib.dspark_transpose_w2.restype = I
     lib.dspark_transpose_w2.argtypes = [P, I, I, I, P, P]
     lib.dspark_survival.restype = I
@@ -262,16 +265,23 @@ def confidence(h, w, W1, x0, draft_tokens, sts=None, out=None, stream=None):
     return out
 
 
-def schedule(survival, sps, out=None, with_theta=True, stream=None):
+def schedule(survival, sps, out=None, with_theta=True, stream=None, mode=None, capacity=None, capacity_out=None):
     """Hardware-aware prefix scheduler: survival float32 [B][gamma], sps
-    float64 [n >= B (gamma + 1) + 1] (sps[n] = SPS(n)).  Returns (lengths
-    int32 [B], theta float64 [1] or None)."""
+    float64 [n >= B (gamma + 1) + 1] (sps[n] = SPS(n)).  mode: SCHEDULE_EARLY_STOP
+    (default), SCHEDULE_CAPACITY (writes capacity_out, int32 [1], when given) or
+    SCHEDULE_TOP_K (capacity: int32 [1] device tensor).  Returns (lengths int32
+    [B], theta float64 [1] or None)."""
     B, gamma = survival.shape
     dev = survival.device
+    mode = SCHEDULE_EARLY_STOP if mode is None else int(mode)
     _dev(survival, "survival", torch.float32)
     _dev(sps, "sps", torch.float64)
     if sps.dim() != 1:
         raise ValueError("sps must be one-dimensional")
+    if capacity is not None:
+        _dev(capacity, "capacity", torch.int32, (1,))
+    if capacity_out is not None:
+        _dev(capacity_out, "capacity_out", torch.int32, (1,))
     if out is None:
         out = (torch.empty((B,), dtype=torch.int32, device=dev),
                torch.empty((1,), dtype=torch.float64, device=dev) if with_theta else None)
@@ -279,8 +289,8 @@ def schedule(survival, sps, out=None, with_theta=True, stream=None):
     _dev(lengths, "lengths", torch.int32, (B,))
     if theta is not None:
         _dev(theta, "theta", torch.float64, (1,))
-    st = load().dspark_schedule(_p(survival), _p(sps), int(sps.shape[0]), B, gamma, _p(lengths), _p(theta),
-                                _stream(stream, dev))
+    st = load().dspark_schedule(_p(survival), _p(sps), int(sps.shape[0]), B, gamma, mode, _p(capacity),
+                                _p(capacity_out), _p(lengths), _p(theta), _stream(stream, dev))
     _check("dspark_schedule", st)
     return lengths, theta
 

@@ -163,11 +163,17 @@ dspark_status dspark_confidence(const float* h, const float* w, const void* W1, 
 }
 
 dspark_status dspark_schedule(const float* survival, const double* sps, int sps_len, int B, int gamma,
+                              dspark_schedule_mode mode, const int32_t* capacity_in, int32_t* capacity_out,
                               int32_t* lengths, double* theta, hipStream_t stream) {
   if (B < 1 || gamma < 1 || gamma > kMaxGamma || (long long)B * gamma > kScheduleMax) return DSPARK_ERR_INVALID_ARGUMENT;
   if ((long long)sps_len < (long long)B * (gamma + 1) + 1) return DSPARK_ERR_INVALID_ARGUMENT;
   if (!req(survival, 4) || !req(sps, 8) || !req(lengths, 4) || !opt(theta, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
-  return from_hip(launch_schedule(survival, sps, B, gamma, lengths, theta, stream));
+  if (mode != DSPARK_SCHEDULE_EARLY_STOP && mode != DSPARK_SCHEDULE_CAPACITY && mode != DSPARK_SCHEDULE_TOP_K)
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (mode == DSPARK_SCHEDULE_TOP_K && !req(capacity_in, 4)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!opt(capacity_out, 4)) return DSPARK_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_schedule(survival, sps, B, gamma, (int)mode, capacity_in,
+                                  mode == DSPARK_SCHEDULE_CAPACITY ? capacity_out : nullptr, lengths, theta, stream));
 }
 
 dspark_status dspark_transpose_w2(const void* W2, dspark_dtype wdtype, int r, int V, void* W2T, hipStream_t stream) {

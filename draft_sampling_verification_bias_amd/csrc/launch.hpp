@@ -173,8 +173,11 @@ hipError_t launch_confidence(const ConfArgs& a, bool bf16, hipStream_t s);
 // Hardware-aware prefix scheduler (schedule.hip): one workgroup, at most
 // kScheduleMax candidates (B * gamma).
 constexpr int kScheduleMax = 4096;
-hipError_t launch_schedule(const float* survival, const double* sps, int B, int gamma, int32_t* lengths,
-                           double* theta, hipStream_t s);
+constexpr int kScheduleEarlyStop = 0;  // Algorithm 1
+constexpr int kScheduleCapacity = 1;   // first maximum of Theta over the whole scan
+constexpr int kScheduleTopK = 2;       // the first K candidates, K given on the device
+hipError_t launch_schedule(const float* survival, const double* sps, int B, int gamma, int mode,
+                           const int32_t* cap_in, int32_t* cap_out, int32_t* lengths, double* theta, hipStream_t s);
 
 hipError_t launch_transpose_w2(const void* W2, bool bf16, int r, int V, void* W2T, hipStream_t s);
 

@@ -12,6 +12,12 @@
 // position admitted for it; survivals that do not increase along a request's
 // block make the admitted positions of every request contiguous from 1.
 //
+// Two more modes serve the asynchronous adaptation of "The Asynchronous Fix,
+// and Why It Stays Lossless": the capacity search takes the first maximum of
+// Theta over every admission count (no early stop; run on earlier survival
+// products), and the top-K mode admits the first K sorted candidates of the
+// current products, K decided earlier.
+//
 // One workgroup: candidate keys (descending survival, then index) are sorted
 // by a bitonic network held in registers (shuffles within a wave, LDS only for
 // partners in other waves), the sorted survivals are summed in float64 by a
@@ -45,10 +51,14 @@ __device__ __forceinline__ void cmp_swap(unsigned long long& a, unsigned long lo
 template <int kE>
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __restrict__ surv,
                                                                  const double* __restrict__ sps, int B, int gamma,
+                                                                 int mode, const int32_t* __restrict__ cap_in,
+                                                                 int32_t* __restrict__ cap_out,
                                                                  int32_t* __restrict__ lengths, double* theta_out) {
   __shared__ unsigned long long key[kScheduleMax];
   __shared__ int len[kScheduleMax];
   __shared__ double wtot[kSchedWaves];
+  __shared__ double s_bt[kSchedWaves];
+  __shared__ int s_bm[kSchedWaves];
   __shared__ int s_valid, s_stop;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -162,9 +172,10 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
   for (int w = 0; w < wave; ++w) base += wtot[w];
   const double S0 = base + incl - local;  // sum of the survivals sorted before c0
 
-  // Theta(m) against Theta(m - 1) at this thread's admission counts m = c0 + t + 1
   const double Bd = (double)B;
-  {
+  int mstar;
+  if (mode == kScheduleEarlyStop) {
+    // Theta(m) against Theta(m - 1) at this thread's admission counts m = c0 + t + 1
     double S = S0;
     double prev_theta = (Bd + S) * sp[0];
     bool going = true;
@@ -180,16 +191,63 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
         prev_theta = theta;
       }
     }
+    __syncthreads();
+    mstar = s_stop == INT_MAX ? M : s_stop - 1;
+  } else if (mode == kScheduleCapacity) {
+    // The first maximum of Theta(m) over m = 0..M: this thread's counts
+    // c0..c1 (Theta(c0) from the sum before c0), then a block argmax with
+    // ties to the lower count.
+    double S = S0;
+    double bt = (Bd + S) * sp[0];
+    int bm = c0;
+#pragma unroll
+    for (int t = 0; t < kSchedPer; ++t) {
+      if (c0 + t < c1) {
+        S += vals[t];
+        const double theta = (Bd + S) * sp[t + 1];
+        if (theta > bt) {
+          bt = theta;
+          bm = c0 + t + 1;
+        }
+      }
+    }
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      const double ot = __shfl_xor(bt, o);
+      const int om = __shfl_xor(bm, o);
+      if (ot > bt || (ot == bt && om < bm)) {
+        bt = ot;
+        bm = om;
+      }
+    }
+    if (lane == 0) {
+      s_bt[wave] = bt;
+      s_bm[wave] = bm;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double t0 = s_bt[0];
+      int m0 = s_bm[0];
+      for (int w = 1; w < kSchedWaves; ++w) {
+        if (s_bt[w] > t0 || (s_bt[w] == t0 && s_bm[w] < m0)) {
+          t0 = s_bt[w];
+          m0 = s_bm[w];
+        }
+      }
+      s_stop = m0;
+      if (cap_out != nullptr) *cap_out = m0;
+    }
+    __syncthreads();
+    mstar = s_stop;
+  } else {  // kScheduleTopK: the capacity decided earlier, filled by the current ranking
+    mstar = min(max(cap_in[0], 0), M);
   }
-  __syncthreads();
-  const int mstar = s_stop == INT_MAX ? M : s_stop - 1;
 
   for (int pos = tid; pos < mstar; pos += kSchedThreads) {
     const unsigned id = (unsigned)key[pos];
     atomicMax(&len[id / (unsigned)gamma], (int)(id % (unsigned)gamma) + 1);
   }
-  // Theta_best = Theta(m*), summed in the order of the comparisons above by
-  // the thread that owns candidate m* - 1
+  // Theta(m*), summed in the order of the comparisons above by the thread
+  // that owns candidate m* - 1
   if (theta_out != nullptr) {
     if (mstar == 0) {
       if (tid == 0) *theta_out = Bd * sps[B];
@@ -209,17 +267,20 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
   for (int i = tid; i < B; i += kSchedThreads) lengths[i] = len[i];
 }
 
-hipError_t launch_schedule(const float* survival, const double* sps, int B, int gamma, int32_t* lengths,
-                           double* theta, hipStream_t s) {
+hipError_t launch_schedule(const float* survival, const double* sps, int B, int gamma, int mode,
+                           const int32_t* cap_in, int32_t* cap_out, int32_t* lengths, double* theta, hipStream_t s) {
   ProfScope prof(s, kProfSchedule);
   const int n = B * gamma;
   if (n <= kSchedThreads) {
-    hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, lengths, theta);
+    hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, mode, cap_in,
+                       cap_out, lengths, theta);
   } else if (n <= 2 * kSchedThreads) {
-    hipLaunchKernelGGL(schedule_kernel<2>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, lengths, theta);
+    hipLaunchKernelGGL(schedule_kernel<2>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, mode, cap_in,
+                       cap_out, lengths, theta);
   } else {
     static_assert(kScheduleMax == 4 * kSchedThreads, "the largest instantiation covers kScheduleMax");
-    hipLaunchKernelGGL(schedule_kernel<4>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, lengths, theta);
+    hipLaunchKernelGGL(schedule_kernel<4>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, mode, cap_in,
+                       cap_out, lengths, theta);
   }
   return hipGetLastError();
 }

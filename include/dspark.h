@@ -86,6 +86,13 @@ typedef enum {
 /* Storage type of W1 and W2. */
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 
+/* Admission rule of dspark_schedule. */
+typedef enum {
+  DSPARK_SCHEDULE_EARLY_STOP = 0,
+  DSPARK_SCHEDULE_CAPACITY = 1,
+  DSPARK_SCHEDULE_TOP_K = 2
+} dspark_schedule_mode;
+
 /* Which entry point a workspace is sized for. */
 typedef enum { DSPARK_OP_DRAFT = 0, DSPARK_OP_VERIFY = 1, DSPARK_OP_SURVIVAL = 2 } dspark_op;
 
@@ -283,10 +290,32 @@ dspark_status dspark_confidence(const float* h, const float* w, const void* W1, 
  * along a block, the admitted positions of b are exactly 1..l*_b (Lemma 1).
  * tau is summed in float64; decisions whose two Theta values agree to
  * rounding may resolve either way.
+ *
+ * mode selects the admission rule:
+ *   DSPARK_SCHEDULE_EARLY_STOP  Algorithm 1 as above (capacity_in and
+ *                               capacity_out are not used).
+ *   DSPARK_SCHEDULE_CAPACITY    the unconstrained search of [R] "The
+ *                               Asynchronous Fix, and Why It Stays Lossless":
+ *                               the admission count m* at the first maximum of
+ *                               Theta over the whole sorted scan (0..all
+ *                               candidates), written to capacity_out[0]
+ *                               (nullable) with the lengths and Theta of that
+ *                               admission.  Run on survival products from two
+ *                               steps earlier, m* is the capacity K.
+ *   DSPARK_SCHEDULE_TOP_K       the first min(K, candidates) sorted candidates
+ *                               of the current products are admitted, K =
+ *                               capacity_in[0] (device int32, decided
+ *                               earlier; negative counts as 0); theta is
+ *                               Theta at that admission.
+ * In every mode the lengths depend on the drafted tokens only through the
+ * survival products of positions that are admitted before them, which keeps
+ * verification lossless; a capacity computed from the current round's
+ * products would not.
  * 1 <= gamma <= 32, 1 <= B * gamma <= 4096.  Asynchronous on `stream`; needs
  * no workspace.
  */
 dspark_status dspark_schedule(const float* survival, const double* sps, int sps_len, int B, int gamma,
+                              dspark_schedule_mode mode, const int32_t* capacity_in, int32_t* capacity_out,
                               int32_t* lengths, double* theta, hipStream_t stream);
 
 /*

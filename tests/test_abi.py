@@ -140,14 +140,17 @@ def test_markov_bias_rejects_bad_arguments(lib):
 
 def test_schedule_rejects_bad_arguments(lib):
     f = lib.dspark_schedule
-    # (survival, sps, sps_len, B, gamma, lengths, theta, stream)
-    assert f(FAKE, FAKE, 20, 4, 4, FAKE, None, None) == INVALID      # sps shorter than B (gamma + 1) + 1
-    assert f(FAKE, FAKE, 1 << 20, 0, 4, FAKE, None, None) == INVALID
-    assert f(FAKE, FAKE, 1 << 20, 4, 33, FAKE, None, None) == INVALID
-    assert f(FAKE, FAKE, 1 << 20, 1024, 5, FAKE, None, None) == INVALID  # more than 4096 candidates
-    assert f(None, FAKE, 1 << 20, 4, 4, FAKE, None, None) == INVALID
-    assert f(FAKE, FAKE, 1 << 20, 4, 4, None, None, None) == INVALID
-    assert f(FAKE, MISALIGNED, 1 << 20, 4, 4, FAKE, None, None) == INVALID
+    # (survival, sps, sps_len, B, gamma, mode, capacity_in, capacity_out, lengths, theta, stream)
+    assert f(FAKE, FAKE, 20, 4, 4, 0, None, None, FAKE, None, None) == INVALID   # sps shorter than B (gamma + 1) + 1
+    assert f(FAKE, FAKE, 1 << 20, 0, 4, 0, None, None, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 1 << 20, 4, 33, 0, None, None, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 1 << 20, 1024, 5, 0, None, None, FAKE, None, None) == INVALID  # more than 4096 candidates
+    assert f(None, FAKE, 1 << 20, 4, 4, 0, None, None, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 1 << 20, 4, 4, 0, None, None, None, None, None) == INVALID
+    assert f(FAKE, MISALIGNED, 1 << 20, 4, 4, 0, None, None, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, 1 << 20, 4, 4, 3, None, None, FAKE, None, None) == INVALID     # unknown mode
+    assert f(FAKE, FAKE, 1 << 20, 4, 4, 2, None, None, FAKE, None, None) == INVALID     # top-K without a capacity
+    assert f(FAKE, FAKE, 1 << 20, 4, 4, 1, None, MISALIGNED - 2, FAKE, None, None) == INVALID
 
 
 def test_confidence_rejects_bad_arguments(lib):

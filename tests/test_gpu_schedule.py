@@ -197,3 +197,108 @@ def test_full_size_scheduled_round(name):
     reqs = sorted(set([0, wl.B - 1] + rng.choice(wl.B, size=4, replace=False).tolist()))
     _scheduled_round(wl, lengths_h, name + " scheduled", reqs=reqs)
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# The asynchronous adaptation: capacity from an unconstrained search over the
+# sorted scan, admission of the current top-K.
+# ---------------------------------------------------------------------------
+def _gpu_mode(a, sps, mode, K=None):
+    a32 = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    sps_d = torch.from_numpy(np.ascontiguousarray(sps, dtype=np.float64)).cuda()
+    cap_in = torch.tensor([K if K is not None else 0], dtype=torch.int32, device="cuda")
+    cap_out = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    lengths, theta = dsp.schedule(a32, sps_d, mode=mode, capacity=cap_in if K is not None else None,
+                                  capacity_out=cap_out)
+    torch.cuda.synchronize()
+    return lengths.cpu().numpy(), float(theta.cpu().numpy()[0]), int(cap_out.cpu().numpy()[0])
+
+
+def _theta_at(a, sps, K):
+    """Theta after K admissions, from the oracle's full scan."""
+    trace = []
+    oracle.schedule(a, sps, early_stop=False, trace=trace)
+    B = a.shape[0]
+    return B * sps[B] if K == 0 else trace[K - 1][4]
+
+
+@pytest.mark.parametrize("B,gamma", [(1, 3), (7, 3), (256, 7), (512, 7), (128, 32)])
+def test_capacity_search_and_top_k_parity(B, gamma):
+    rng = np.random.default_rng(7 * B + gamma)
+    exempt = 0
+    for trial in range(5):
+        c = rng.uniform(0.2, 1.0, size=(B, gamma))
+        if trial == 1:
+            c = np.round(c * 4) / 4
+        a = np.cumprod(c, axis=1).astype(np.float32).astype(np.float64)
+        sps = workloads.sps_curve(B * (gamma + 1), rng.uniform(0.8, 3.0) * B, rng.uniform(1.0, 4.0),
+                                  ripple=0.0 if trial == 0 else 0.2, seed=trial)
+        # capacity search
+        K, theta_ref = oracle.schedule_capacity(a, sps)
+        _, _, margin = oracle.schedule(a, sps, early_stop=False)
+        lengths, theta, cap = _gpu_mode(a, sps, dsp.SCHEDULE_CAPACITY)
+        if margin <= TIE_RTOL * abs(theta_ref):
+            exempt += 1
+        else:
+            assert cap == K, "capacity %d vs oracle %d" % (cap, K)
+            assert (lengths == oracle.admit_top(a, K)).all()
+            assert abs(theta - theta_ref) <= THETA_RTOL * abs(theta_ref)
+        # top-K admission for several capacities, including none and more than all
+        M = int((a > 0).sum())
+        for Kq in sorted({0, 1, M // 3, M, M + 5, -3}):
+            lengths, theta, cap = _gpu_mode(a, sps, dsp.SCHEDULE_TOP_K, K=Kq)
+            assert (lengths == oracle.admit_top(a, Kq)).all(), "top-K lengths differ at K=%d" % Kq
+            ref_theta = _theta_at(a, sps, min(max(Kq, 0), M))
+            assert abs(theta - ref_theta) <= THETA_RTOL * abs(ref_theta)
+            assert cap == -7  # capacity_out is written by the capacity search only
+    say("[capacity/top-K B=%d gamma=%d] 5 cases, %d exempt" % (B, gamma, exempt))
+    assert exempt <= 1
+
+
+def test_lagged_round_full_size():
+    """v151936_b256_t07 with the asynchronous adaptation: the capacity comes
+    from the confidences of an earlier round (another round counter), the
+    current round's confidences fill it, and the round is verified at those
+    lengths; the oracle checks the capacity, the lengths of every request and
+    the verification of a sample."""
+    wl = workloads.make("v151936_b256_t07")
+    d = Dev(wl)
+    h, w, sts = workloads.confidence_inputs(wl.B, wl.gamma, 4096, wl.r, seed=2)
+    hd, wdev, stsd = torch.from_numpy(h).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(sts).cuda()
+    sps = workloads.sps_curve(wl.B * (wl.gamma + 1), 4.0 * wl.B, 2.0, ripple=0.1)
+    sps_d = torch.from_numpy(sps).cuda()
+    # two rounds earlier: its drafted tokens, confidences, survival and capacity
+    tok_old, _, _ = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd + 7)
+    conf_old = dsp.confidence(hd, wdev, d.W1, d.x0, tok_old, sts=stsd)
+    _, surv_old = dsp.survival(None, None, None, None, None, None, None, wl.T, conf=conf_old)
+    cap = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dsp.schedule(surv_old, sps_d, mode=dsp.SCHEDULE_CAPACITY, capacity_out=cap)
+    # this round
+    tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
+    conf = dsp.confidence(hd, wdev, d.W1, d.x0, tok, sts=stsd)
+    _, surv = dsp.survival(None, None, None, None, None, None, None, wl.T, conf=conf)
+    lengths, _ = dsp.schedule(surv, sps_d, mode=dsp.SCHEDULE_TOP_K, capacity=cap)
+    W2T = dsp.transpose_w2(d.W2)
+    alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd, W2T=W2T,
+                                   lengths=lengths)
+    torch.cuda.synchronize()
+    W1f, W2f = f64_weights(wl)
+    K_ref, theta_ref = oracle.schedule_capacity(surv_old.cpu().numpy().astype(np.float64), sps)
+    _, _, margin = oracle.schedule(surv_old.cpu().numpy().astype(np.float64), sps, early_stop=False)
+    assert margin > TIE_RTOL * abs(theta_ref)
+    assert int(cap.cpu().numpy()[0]) == K_ref
+    lengths_h = lengths.cpu().numpy()
+    assert (lengths_h == oracle.admit_top(surv.cpu().numpy().astype(np.float64), K_ref)).all()
+    tok_h = tok.cpu().numpy()
+    rng = np.random.default_rng(17)
+    reqs = sorted(set([0, wl.B - 1] + rng.choice(wl.B, size=4, replace=False).tolist()))
+    ref_d = oracle.markov_draft(wl.U, W1f, W2f, wl.x0, wl.T, wl.seeds, wl.rnd, requests=reqs)
+    _, _, whole = compare_draft(ref_d, tok_h, prob.cpu().numpy(), lse.cpu().numpy(), reqs, wl.T)
+    vreq = sorted(whole)
+    vref = oracle.verify(wl.U, W1f, W2f, wl.x0, tok_h, wl.tgt, wl.T, wl.seeds, wl.rnd, requests=vreq,
+                         lengths=lengths_h)
+    nv, _ = compare_verify(vref, alen.cpu().numpy(), otok.cpu().numpy(), aprob.cpu().numpy(), vreq, wl.T)
+    say("[lagged round] capacity %d, mean length %.2f, %d verified requests equal" % (K_ref, lengths_h.mean(), nv))
+    assert nv > 0
+    del d, W2T
+    torch.cuda.empty_cache()
