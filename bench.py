@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=256, help="requests in the oracle baseline (0: skip)")
     ap.add_argument("--cpu-rounds", type=int, default=6, help="rounds of those requests in the oracle baseline")
     ap.add_argument("--survival-steps", type=int, default=10)
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="cold-cache figure: write this many MiB before each of K separately timed steps (0: skip)")
     ap.add_argument("--schedule-steps", type=int, default=20,
                     help="timed calls of the prefix scheduler and of verification with its lengths (0: skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -219,6 +221,28 @@ def main():
     p1 = time.perf_counter()
     prof = dsp.profile_read()
     dsp.profile_enable(False)
+
+    # Cold caches: before each step a write of flush_mb MiB evicts the 256 MB
+    # memory-side cache, as the target model's forward pass does between
+    # rounds.  Each step is timed alone with events on the launch stream; the
+    # flush is outside the timed interval.
+    cold = None
+    if args.flush_mb > 0:
+        scratch = torch.empty(args.flush_mb << 18, dtype=torch.float32, device=dev)
+        times = []
+        for i in range(nsteps):
+            scratch.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(i, 1000 + i)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scratch
+        med = float(np.median(times))
+        cold = {"flush_mib": args.flush_mb, "ms_per_step_median": med,
+                "ms_per_step_p10": float(np.percentile(times, 10)), "ms_per_step_p90": float(np.percentile(times, 90)),
+                "value": B * gamma / (med * 1e-3)}
 
     secs = t1 - t0
     ms_per_step = secs / nsteps * 1e3
@@ -340,6 +364,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "ms_per_step_with_events": (p1 - p0) / nsteps * 1e3,
+        "cold_cache": cold,
         "survival_ms": surv_ms,
         "schedule": sched,
         "cpu_baseline": cpu,
