@@ -7,8 +7,8 @@ touches it and shares no code with it.
 
 Modules:
   philox      Philox4x64-10 (Salmon et al., SC'11) and the stream layout.
-  dspark_ref  draft, verify, survival, the confidence head and the prefix
-              scheduler in plain float64 numpy.
+  dspark_ref  draft (Markov and RNN heads), verify, survival, the confidence
+              head and the prefix scheduler in plain float64 numpy.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, brute-force enumeration, Monte Carlo laws or
@@ -27,6 +27,8 @@ from .dspark_ref import (  # noqa: F401
     markov_bias,
     markov_draft,
     residual_sample,
+    rnn_draft,
+    round_to_bf16,
     schedule,
     schedule_capacity,
     softmax,

@@ -419,3 +419,76 @@ def admit_top(a, K):
     for _, r, j in pool[:max(0, int(K))]:
         lengths[r] = max(lengths[r], j)
     return lengths
+
+
+# ----------------------------------------------------------------------------
+# RNN head (the second sequential block)
+# ----------------------------------------------------------------------------
+
+def round_to_bf16(x):
+    """Nearest bfloat16 value (8 significant bits, ties to even) of float64
+    values, returned as float64.  Applied once to the float64 value itself
+    (no intermediate float32)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)   # numpy rounds halves to even
+
+
+def rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, rnd, bf16_operand=True, forced=None, requests=None):
+    """Block sampling with the RNN head of [R] "Instantiation 2: The RNN Head"
+    (Eq. 6) in place of the Markov bias: per request, s_0 = 0 and for
+    k = 1..gamma
+        z_k = [s_{k-1} ; W1[x_{k-1}] ; h_k]          (x_0 = the anchor)
+        (g, c, o) = Wp z_k                           (Wp: [3r][2r + d], rows
+                                                      gate, candidate, output)
+        s_k = sigma(g) s_{k-1} + (1 - sigma(g)) tanh(c)
+        e_k = tanh(o);  bias_k = e_k W2;  p_d^k = softmax((U_k + bias_k) / T)
+    then x_k is drawn as in markov_draft (same stream-0 uniforms), or taken
+    from ``forced`` [B][gamma] when given (for evaluating block laws).
+
+    Reading: with bf16 weights the output e_k is rounded to bf16 before the
+    projection (``bf16_operand``), as a bf16 model evaluates tanh(W_o z) W2;
+    everything else is float64.  Returns dict with tokens, prob, lse, dist as
+    markov_draft and E [B][gamma][r], the operand rows e_k used.
+    """
+    U = np.asarray(U)
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    reqs = range(B) if requests is None else requests
+    tokens = np.full((B, gamma), -1, dtype=np.int32)
+    prob = np.full((B, gamma), np.nan)
+    lse = np.full((B, gamma), np.nan)
+    dist = np.full((B, gamma), np.inf)
+    E = np.full((B, gamma, r), np.nan)
+    for b in reqs:
+        prev = int(x0[b])
+        state = np.zeros(r)
+        for k in range(1, gamma + 1):
+            z = np.concatenate([state, W1[prev], np.asarray(h[b, k - 1], dtype=np.float64)])
+            proj = Wp @ z
+            g, c, o = proj[:r], proj[r:2 * r], proj[2 * r:]
+            gate = 1.0 / (1.0 + np.exp(-g))
+            e = np.tanh(o)
+            if bf16_operand:
+                e = round_to_bf16(e)
+            E[b, k - 1] = e
+            l = np.asarray(U[b, k - 1], dtype=np.float64) + e @ W2
+            if T > 0:
+                l = l / T
+            state = gate * state + (1.0 - gate) * np.tanh(c)
+            if T == 0:
+                x = first_argmax(l) if forced is None else int(forced[b, k - 1])
+                top2 = np.partition(l, -2)[-2:]
+                tokens[b, k - 1], prob[b, k - 1], lse[b, k - 1] = x, 1.0, 0.0
+                dist[b, k - 1] = top2[1] - top2[0]
+            else:
+                p, zl = softmax(l)
+                if forced is None:
+                    u = philox.uniform(int(seeds[b]), rnd, k, philox.STREAM_DRAFT)
+                    x, d = inverse_cdf(p, u)
+                else:
+                    x, d = int(forced[b, k - 1]), np.inf
+                tokens[b, k - 1], prob[b, k - 1], lse[b, k - 1] = x, p[x], zl
+                dist[b, k - 1] = d
+            prev = x
+    return dict(tokens=tokens, prob=prob, lse=lse, dist=dist, E=E)
