@@ -150,6 +150,7 @@ struct TStatsArgs {
   float2* tpart;
   const int32_t* draft_tokens;  // with tx_out: the drafted tokens [B][gamma]
   float* tx_out;                // list mode, optional: target logit of the drafted token per output row
+  const int32_t* lengths;       // list mode, optional: scheduled lengths; rows past l_b + 1 are not read
 };
 
 hipError_t launch_target_stats(const TStatsArgs& a, bool greedy, int max_rows, hipStream_t s);

@@ -169,6 +169,7 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
     const float* row;
     int x, orow, tw;
     bool ok;
+    bool skip;  // a row past the request's scheduled bonus row: not read
   };
   // Item `it`: its row, output row, drafted token and first tile; ok is false
   // past the last row (list mode: past the device count, and so for every
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
   auto resolve = [&](long long it) -> Item {
     Item m;
     m.ok = it < items_max;
+    m.skip = false;
     if (!m.ok) return m;
     const int li = (int)(it / ngrp);
     const int tg = (int)(it - (long long)li * ngrp);
@@ -187,6 +189,9 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
       m.ok = req < cnt;
       kk = a.kk0 + row;
       m.orow = b * a.orow_stride + row;
+      // with scheduled lengths, the phase's rows past the bonus row l_b + 1
+      // are never decided
+      m.skip = m.ok && a.lengths != nullptr && kk > a.lengths[b];
     } else if (a.nreq > 0) {
       b = li / a.rows_per_req;
       const int row = li - b * a.rows_per_req;
@@ -198,11 +203,12 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
       m.orow = li;
     }
     m.row = a.target + ((size_t)b * (a.gamma + 1) + kk) * (size_t)a.V;
-    m.x = (m.ok && a.tx_out && kk < a.gamma) ? a.draft_tokens[(size_t)b * a.gamma + kk] : -1;
+    m.x = (m.ok && !m.skip && a.tx_out && kk < a.gamma) ? a.draft_tokens[(size_t)b * a.gamma + kk] : -1;
     m.tw = tg * kStatItemTiles + wave * kStatWaveTiles;  // first tile of this wave
     return m;
   };
   auto load = [&](const Item& m, float (&v)[kStatWaveTiles][4]) {
+    if (m.skip) return;
 #pragma unroll
     for (int j = 0; j < kStatWaveTiles; ++j) {
       const int c0 = (m.tw + j) * kTgtCols + 4 * lane;
@@ -216,6 +222,7 @@ __global__ __launch_bounds__(kVThreads) void target_stats_kernel(TStatsArgs a) {
     }
   };
   auto reduce_store = [&](const Item& m, const float (&v)[kStatWaveTiles][4]) {
+    if (m.skip) return;  // the same for every wave of the workgroup
     // per lane: one (max, sum) or (value, index) pair per tile; the drafted
     // token's logit from the lane that holds it
     float pa[kStatWaveTiles], pb[kStatWaveTiles];
@@ -1217,6 +1224,7 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
     t.tpart = w.tpart;
     t.draft_tokens = a.draft_tokens;
     t.tx_out = greedy ? nullptr : w.txv;
+    t.lengths = a.lengths;
     e = launch_target_stats(t, greedy, a.B * t.rows_per_req, s);
     if (e != hipSuccess) return e;
     ProfScope prof(s, kProfVerifyDecide);
