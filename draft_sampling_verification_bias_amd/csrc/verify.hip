@@ -146,7 +146,7 @@ __device__ __forceinline__ double wval(const void* W, size_t idx) {
 // eight tiles of the tile's wave (any m >= the tile's own maximum gives the
 // same tile weight); greedy mode (max t, argmax bits).
 // ---------------------------------------------------------------------------
-constexpr int kStatBlocksPerCU = 8;
+constexpr int kStatBlocksPerCU = 16;
 constexpr int kStatWaveTiles = 8;                                   // tiles per wave per item
 constexpr int kStatItemTiles = kStatWaveTiles * (kVThreads / kWave);  // 32 tiles = 8192 columns
 
