@@ -122,7 +122,7 @@ def test_schedule_admits_everything_on_a_flat_curve_and_nothing_on_a_cliff():
     assert (lengths == 0).all() and theta == B
 
 
-def _scheduled_round(wl, lengths_h, label, reqs=None):
+def _scheduled_round(wl, lengths_h, label, reqs=None, use_w2t=True):
     d = Dev(wl)
     tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
     torch.cuda.synchronize()
@@ -132,7 +132,7 @@ def _scheduled_round(wl, lengths_h, label, reqs=None):
     ref = oracle.markov_draft(wl.U, W1f, W2f, wl.x0, wl.T, wl.seeds, wl.rnd, requests=reqs)
     n, ex, whole = compare_draft(ref, tok_h, prob.cpu().numpy(), lse.cpu().numpy(), reqs, wl.T)
     lens_d = torch.from_numpy(np.ascontiguousarray(lengths_h, dtype=np.int32)).cuda()
-    W2T = dsp.transpose_w2(d.W2) if wl.T > 0 else None
+    W2T = dsp.transpose_w2(d.W2) if (wl.T > 0 and use_w2t) else None
     alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd, W2T=W2T,
                                    lengths=lens_d)
     torch.cuda.synchronize()
@@ -157,6 +157,25 @@ def test_verify_with_fixed_lengths(name, kw):
     wl = workloads.make(name, **kw)
     lengths = (np.arange(wl.B) % (wl.gamma + 1)).astype(np.int32)
     _, _, _, alen = _scheduled_round(wl, lengths, name)
+    assert (alen <= lengths).all()
+
+
+@pytest.mark.parametrize("name,kw", [
+    # more than 1024 target tiles per row: the decision kernel's general path
+    ("v151936_b32", dict(V=1048580, B=3, gamma=2, r=16)),
+    ("greedy_v151936_b512", dict(V=1048580, B=3, gamma=2, r=16)),
+])
+def test_verify_with_lengths_on_the_general_decision_path(name, kw):
+    wl = workloads.make(name, **kw)
+    lengths = np.array([0, 1, 2], dtype=np.int32)
+    _, _, _, alen = _scheduled_round(wl, lengths, name + " general")
+    assert (alen <= lengths).all()
+
+
+def test_verify_with_lengths_without_the_transposed_projection():
+    wl = workloads.make("v151936_b256_t07", V=3001, B=40, r=64)
+    lengths = ((np.arange(wl.B) * 5) % (wl.gamma + 1)).astype(np.int32)
+    _, _, _, alen = _scheduled_round(wl, lengths, "no W2T", use_w2t=False)
     assert (alen <= lengths).all()
 
 
