@@ -434,7 +434,7 @@ def round_to_bf16(x):
     return np.ldexp(np.round(m * 256.0) / 256.0, e)   # numpy rounds halves to even
 
 
-def rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, rnd, bf16_operand=True, forced=None, requests=None):
+def rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, rnd, bf16_operand=False, forced=None, requests=None):
     """Block sampling with the RNN head of [R] "Instantiation 2: The RNN Head"
     (Eq. 6) in place of the Markov bias: per request, s_0 = 0 and for
     k = 1..gamma
@@ -446,9 +446,9 @@ def rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, rnd, bf16_operand=True, forced=Non
     then x_k is drawn as in markov_draft (same stream-0 uniforms), or taken
     from ``forced`` [B][gamma] when given (for evaluating block laws).
 
-    Reading: with bf16 weights the output e_k is rounded to bf16 before the
-    projection (``bf16_operand``), as a bf16 model evaluates tanh(W_o z) W2;
-    everything else is float64.  Returns dict with tokens, prob, lse, dist as
+    Everything is float64; e_k enters the projection unrounded.  With
+    ``bf16_operand`` it is first rounded to bf16, as a model that keeps its
+    activations in bf16 would (an alternative reading, kept as an option).  Returns dict with tokens, prob, lse, dist as
     markov_draft and E [B][gamma][r], the operand rows e_k used.
     """
     U = np.asarray(U)

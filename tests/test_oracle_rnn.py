@@ -54,12 +54,14 @@ def test_output_reading_only_the_embedding_is_a_markov_head():
     Wp1 = Wp.copy()
     Wp1[2 * r:, :r] = 0.0          # output block: no state
     Wp1[2 * r:, 2 * r:] = 0.0      # ... and no hidden state
-    W1_eff = ref.round_to_bf16(np.tanh(W1 @ Wp1[2 * r:, r:2 * r].T))
-    for T in (1.0, 0.7, 0.0):
-        d_rnn = ref.rnn_draft(U, W1, W2, Wp1, h, x0, T, seeds, 6)
-        d_mk = ref.markov_draft(U, W1_eff, W2, x0, T, seeds, 6)
-        assert (d_rnn["tokens"] == d_mk["tokens"]).all()
-        np.testing.assert_allclose(d_rnn["prob"], d_mk["prob"], rtol=1e-12, atol=0)
+    emb = np.tanh(W1 @ Wp1[2 * r:, r:2 * r].T)
+    for rounded in (False, True):
+        W1_eff = ref.round_to_bf16(emb) if rounded else emb
+        for T in (1.0, 0.7, 0.0):
+            d_rnn = ref.rnn_draft(U, W1, W2, Wp1, h, x0, T, seeds, 6, bf16_operand=rounded)
+            d_mk = ref.markov_draft(U, W1_eff, W2, x0, T, seeds, 6)
+            assert (d_rnn["tokens"] == d_mk["tokens"]).all()
+            np.testing.assert_allclose(d_rnn["prob"], d_mk["prob"], rtol=1e-12, atol=0)
 
 
 def test_zero_initial_state_and_memory_beyond_one_step():
