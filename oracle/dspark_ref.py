@@ -434,7 +434,7 @@ def round_to_bf16(x):
     return np.ldexp(np.round(m * 256.0) / 256.0, e)   # numpy rounds halves to even
 
 
-def rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, rnd, bf16_operand=False, forced=None, requests=None):
+def rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, rnd, bf16_operand=False, forced=None, requests=None, hp=None):
     """Block sampling with the RNN head of [R] "Instantiation 2: The RNN Head"
     (Eq. 6) in place of the Markov bias: per request, s_0 = 0 and for
     k = 1..gamma
@@ -446,7 +446,10 @@ def rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, rnd, bf16_operand=False, forced=No
     then x_k is drawn as in markov_draft (same stream-0 uniforms), or taken
     from ``forced`` [B][gamma] when given (for evaluating block laws).
 
-    Everything is float64; e_k enters the projection unrounded.  With
+    ``hp`` ([B][gamma][3r], optional) is the hidden part W_p[:, 2r:] h_k given
+    precomputed (it depends on no drafted token, so the parallel stage can
+    produce it); ``Wp`` then needs only its first 2r columns and ``h`` is not
+    read.  Everything is float64; e_k enters the projection unrounded.  With
     ``bf16_operand`` it is first rounded to bf16, as a model that keeps its
     activations in bf16 would (an alternative reading, kept as an option).  Returns dict with tokens, prob, lse, dist as
     markov_draft and E [B][gamma][r], the operand rows e_k used.
@@ -464,8 +467,12 @@ def rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, rnd, bf16_operand=False, forced=No
         prev = int(x0[b])
         state = np.zeros(r)
         for k in range(1, gamma + 1):
-            z = np.concatenate([state, W1[prev], np.asarray(h[b, k - 1], dtype=np.float64)])
-            proj = Wp @ z
+            if hp is None:
+                z = np.concatenate([state, W1[prev], np.asarray(h[b, k - 1], dtype=np.float64)])
+                proj = Wp @ z
+            else:
+                z = np.concatenate([state, W1[prev]])
+                proj = np.asarray(Wp, dtype=np.float64)[:, :2 * r] @ z + np.asarray(hp[b, k - 1], dtype=np.float64)
             g, c, o = proj[:r], proj[r:2 * r], proj[2 * r:]
             gate = 1.0 / (1.0 + np.exp(-g))
             e = np.tanh(o)

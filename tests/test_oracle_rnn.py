@@ -102,3 +102,13 @@ def test_block_law_sums_to_one_and_matches_sampling():
         counts[tuple(int(t) for t in row)] += 1
     keys = sorted(law)
     assert chisquare([counts[k] for k in keys], [law[k] * n for k in keys]).pvalue > 1e-4
+
+
+def test_precomputed_hidden_part_is_the_same_draft():
+    U, W1, W2, Wp, h, x0, seeds = _case(seed=9)
+    r = W1.shape[1]
+    hp = np.einsum("bkd,jd->bkj", h.astype(np.float64), Wp[:, 2 * r:])
+    a = ref.rnn_draft(U, W1, W2, Wp, h, x0, 1.0, seeds, 4)
+    b = ref.rnn_draft(U, W1, W2, Wp[:, :2 * r], None, x0, 1.0, seeds, 4, hp=hp)
+    assert (a["tokens"] == b["tokens"]).all()
+    np.testing.assert_allclose(a["prob"], b["prob"], rtol=1e-12, atol=0)
