@@ -15,14 +15,14 @@ import os
 import torch
 
 __all__ = [
-    "DsparkError", "OP_DRAFT", "OP_VERIFY", "OP_SURVIVAL", "MAX_RESIDUAL_PROPOSALS",
+    "DsparkError", "OP_DRAFT", "OP_VERIFY", "OP_SURVIVAL", "OP_RNN_DRAFT", "MAX_RESIDUAL_PROPOSALS",
     "SCHEDULE_EARLY_STOP", "SCHEDULE_CAPACITY", "SCHEDULE_TOP_K",
     "library_path", "load", "version", "workspace_size", "markov_bias",
-    "markov_draft", "verify", "transpose_w2", "survival", "confidence", "schedule", "profile_enable",
+    "markov_draft", "rnn_draft", "verify", "transpose_w2", "survival", "confidence", "schedule", "profile_enable",
     "profile_read",
 ]
 
-OP_DRAFT, OP_VERIFY, OP_SURVIVAL = 0, 1, 2
+OP_DRAFT, OP_VERIFY, OP_SURVIVAL, OP_RNN_DRAFT = 0, 1, 2, 3
 SCHEDULE_EARLY_STOP, SCHEDULE_CAPACITY, SCHEDULE_TOP_K = 0, 1, 2
 _F32, _BF16 = 0, 1
 MAX_RESIDUAL_PROPOSALS = 64
@@ -62,6 +62,8 @@ def load():
     lib.dspark_markov_bias.argtypes = [P, P, I, P, I, I, I, P, P]
     lib.dspark_markov_draft.restype = I
     lib.dspark_markov_draft.argtypes = [P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_rnn_draft.restype = I
+    lib.dspark_rnn_draft.argtypes = [P, P, P, I, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, P, SZ, P]
     lib.dspark_verify.restype = I
     lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
     lib.dspark_confidence.restype = I
@@ -197,6 +199,41 @@ def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=Non
                                     _p(ws), nbytes, _stream(stream, dev))
     _check("dspark_markov_draft", st)
     return tok, prob, lse
+
+
+def rnn_draft(U, W1, W2, Wp, hp, x0, temperature, seeds, rnd, out=None, with_e=False, workspace=None,
+              stream=None):
+    """Draft gamma tokens per request with the RNN head (bf16 W1, W2; float32
+    Wp [3r][2r] and hp [B][gamma][3r]).  Returns (draft_tokens, draft_prob,
+    draft_lse, e or None)."""
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    _dev(U, "U", torch.float32)
+    _dev(W1, "W1", torch.bfloat16, (V, r))
+    _dev(W2, "W2", torch.bfloat16, (r, V))
+    _dev(Wp, "Wp", torch.float32, (3 * r, 2 * r))
+    _dev(hp, "hp", torch.float32, (B, gamma, 3 * r))
+    _dev(x0, "x0", torch.int32, (B,))
+    if seeds is not None:
+        _dev(seeds, "seeds", torch.uint64, (B,))
+    if out is None:
+        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma, r), dtype=torch.float32, device=dev) if with_e else None)
+    tok, prob, lse, e = out
+    _dev(tok, "draft_tokens", torch.int32, (B, gamma))
+    _dev(prob, "draft_prob", torch.float32, (B, gamma))
+    _dev(lse, "draft_lse", torch.float32, (B, gamma))
+    if e is not None:
+        _dev(e, "e", torch.float32, (B, gamma, r))
+    ws, nbytes = _workspace(OP_RNN_DRAFT, B, gamma, V, r, workspace, dev)
+    st = load().dspark_rnn_draft(_p(U), _p(W1), _p(W2), _wdtype(W1, W2), _p(Wp), _p(hp), _p(x0), B, gamma, V, r,
+                                 float(temperature), _p(seeds), int(rnd), _p(tok), _p(prob), _p(lse), _p(e),
+                                 _p(ws), nbytes, _stream(stream, dev))
+    _check("dspark_rnn_draft", st)
+    return tok, prob, lse, e
 
 
 def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, rnd, out=None,

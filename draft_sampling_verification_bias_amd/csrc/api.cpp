@@ -56,6 +56,7 @@ size_t dspark_workspace_size(dspark_op op, int B, int gamma, int V, int r) {
     case DSPARK_OP_DRAFT: return draft_workspace(B, gamma, V, r);
     case DSPARK_OP_VERIFY: return verify_workspace(B, gamma, V, r);
     case DSPARK_OP_SURVIVAL: return survival_workspace(B, gamma, V, r);
+    case DSPARK_OP_RNN_DRAFT: return rnn_draft_workspace(B, gamma, V, r);
     default: return 0;
   }
 }
@@ -96,6 +97,41 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
   a.lse = draft_lse;
   a.ws = workspace;
   return from_hip(launch_draft(a, wdtype == DSPARK_BF16, stream));
+}
+
+dspark_status dspark_rnn_draft(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
+                               const float* Wp, const float* hp, const int32_t* x0, int B, int gamma, int V, int r,
+                               float temperature, const uint64_t* seeds, uint64_t round, int32_t* draft_tokens,
+                               float* draft_prob, float* draft_lse, float* e_out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  if (wdtype != DSPARK_BF16) return DSPARK_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(Wp, 16) || !req(hp, 4) || !req(x0, 4) ||
+      !req(draft_tokens, 4) || !req(draft_prob, 4) || !req(draft_lse, 4) || !opt(e_out, 4) ||
+      !req(workspace, 16))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (temperature > 0.0f && !req(seeds, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < rnn_draft_workspace(B, gamma, V, r)) return DSPARK_ERR_WORKSPACE;
+  RnnDraftArgs a = {};
+  a.U = U;
+  a.W1 = W1;
+  a.W2 = W2;
+  a.Wp = Wp;
+  a.hp = hp;
+  a.x0 = x0;
+  a.seeds = seeds;
+  a.round = round;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.r = r;
+  a.temperature = temperature;
+  a.tokens = draft_tokens;
+  a.prob = draft_prob;
+  a.lse = draft_lse;
+  a.e_out = e_out;
+  a.ws = workspace;
+  return from_hip(launch_rnn_draft(a, stream));
 }
 
 dspark_status dspark_verify(const float* U, const void* W1, const void* W2, const void* W2T, dspark_dtype wdtype,

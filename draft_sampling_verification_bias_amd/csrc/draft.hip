@@ -36,6 +36,8 @@ struct SelectArgs {
   float* lse;
   double* u_next;  // [2][B] stream-0 uniforms drawn one position ahead
   uint4* esw;      // optional: the drafted token's W1 row for the next tile pass
+  int opnd_rows;   // 0: W1 rows of tokens.  n > 0: W1 is a table of operand rows (row
+                   // b * gamma + k - 1), each of n parts of r values summed to the operand
 };
 
 // Store W1 row x (bf16, r = 256) in the ring tile pass's operand layout for
@@ -68,6 +70,17 @@ __device__ __forceinline__ float w1_at(const void* W1, size_t idx) {
   }
 }
 
+// Element j of the operand row `row` (a token's W1 row, or the sum of the
+// parts of an operand-table row).
+template <bool kBf16>
+__device__ __forceinline__ float opnd_at(const SelectArgs& a, int row, int j) {
+  const int parts = a.opnd_rows > 0 ? a.opnd_rows : 1;
+  const size_t base = (size_t)row * parts * a.r + j;
+  float v = w1_at<kBf16>(a.W1, base);
+  for (int p = 1; p < parts; ++p) v += w1_at<kBf16>(a.W1, base + (size_t)p * a.r);
+  return v;
+}
+
 template <bool kGreedy, bool kBf16>
 __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a) {
   __shared__ PickScratch ps;
@@ -93,8 +106,9 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
       pr[j] = t < a.ntiles ? P[t] : make_float2(-__builtin_inff(), 0.0f);
     }
   }
-  const int prev = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
-  if (prev < 0 || prev >= a.V) {  // invalid anchor or earlier position: propagate
+  const int ptok = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
+  const int prev = a.opnd_rows ? b * a.gamma + a.k - 1 : ptok;  // the W1 row
+  if (ptok < 0 || ptok >= a.V) {  // invalid anchor or earlier position: propagate
     if (tid == 0) {
       a.tokens[out] = -1;
       a.prob[out] = __builtin_nanf("");
@@ -126,7 +140,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int j = tid + q * kSelThreads;
-      const float v = w1_at<kBf16>(a.W1, (size_t)prev * a.r + (j < a.r ? j : 0));  // clamped: no branch
+      const float v = opnd_at<kBf16>(a, prev, j < a.r ? j : 0);  // clamped: no branch
       w1v[q] = j < a.r ? v : 0.0f;
     }
     float lm = -__builtin_inff();
@@ -285,10 +299,11 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
     const int t = t0 + j;
     pr[j] = P[t < t1 ? t : (t1 > 0 ? t1 - 1 : 0)];
   }
-  const int prev = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
+  const int ptok = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
+  const int prev = a.opnd_rows ? b * a.gamma + a.k - 1 : ptok;  // the W1 row
   const uint64_t seed = a.seeds[b];
   const double u_pre = a.k == 1 ? 0.0 : a.u_next[(size_t)((a.k - 1) & 1) * a.B + b];
-  if (prev < 0 || prev >= a.V) {  // invalid anchor or earlier position: propagate
+  if (ptok < 0 || ptok >= a.V) {  // invalid anchor or earlier position: propagate
     if (threadIdx.x == 0) {
       a.tokens[out] = -1;
       a.prob[out] = __builtin_nanf("");
@@ -373,7 +388,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
     float w[16][8];
     // clamped k: every load of the chunk is issued before the first use
 #pragma unroll
-    for (int i = 0; i < 16; ++i) e[i] = w1_at<kBf16>(a.W1, (size_t)prev * a.r + wave * kq + kr + 4 * min(i0 + i, nk - 1));
+    for (int i = 0; i < 16; ++i) e[i] = opnd_at<kBf16>(a, prev, wave * kq + kr + 4 * min(i0 + i, nk - 1));
     if (kBf16 && vec) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -558,6 +573,197 @@ hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s) {
       e = bf16 ? launch_select_wave<true>(sa, s) : launch_select_wave<false>(sa, s);
     } else {
       e = bf16 ? launch_select<false, true>(sa, s) : launch_select<false, false>(sa, s);
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+
+// ---------------------------------------------------------------------------
+// Block sampling with the RNN head (DSpark, "Instantiation 2: The RNN Head",
+// Eq. 6).  Per request s_0 = 0 and, for k = 1..gamma,
+//   (g, c, o) = Wp [s_{k-1}; W1[x_{k-1}]] + hp_k
+//   s_k = sigmoid(g) s_{k-1} + (1 - sigmoid(g)) tanh(c),   e_k = tanh(o)
+// and the logits of position k are U_k + e_k W2, sampled exactly as the Markov
+// head's.  hp_k = Wp[:, 2r:] h_k depends on no drafted token, so the caller
+// brings it precomputed from the parallel stage.
+//
+// One cell launch per position: workgroup (request group, slice of jn state
+// units) stages z = [s_{k-1}; W1[x_{k-1}]] of its requests in LDS as float64,
+// and each thread forms the three projections of one (request, unit) in
+// float64.  e_k goes to the operand table as two bf16 parts (hi = bf16(e),
+// lo = bf16(e - hi)), so that the bf16 MFMA tile pass multiplies W2 by
+// hi + lo, which is e to about 2^-18 relative.  The state is double-buffered
+// in float64 (position k reads buffer (k - 1) & 1 and writes k & 1).
+// ---------------------------------------------------------------------------
+
+struct CellArgs {
+  const void* W1;
+  const float* Wp;     // [3r][2r]
+  const float* hp;     // [B][gamma][3r]
+  const int32_t* x0;
+  const int32_t* tokens;
+  double* state;       // [2][B][r]
+  uint16_t* opnd;      // [B * gamma][2r]: bf16 hi parts, then lo parts
+  float* e_out;        // optional [B][gamma][r]
+  int B, gamma, V, r, k, nreq, jn;
+};
+
+constexpr int kCellThreads = 256;
+
+__device__ __forceinline__ uint16_t bf16_round(float f) {
+  const uint32_t u = __float_as_uint(f);  // finite here: |e| <= 1
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
+  extern __shared__ double zs[];  // [nreq][2r]
+  const int r = a.r, r2 = 2 * a.r;
+  const int b0 = blockIdx.x * a.nreq;
+  const double* sprev = a.state + (size_t)((a.k - 1) & 1) * a.B * r;
+  double* snext = a.state + (size_t)(a.k & 1) * a.B * r;
+  for (int idx = threadIdx.x; idx < a.nreq * r2; idx += kCellThreads) {
+    const int i = idx / r2, c = idx - (idx / r2) * r2, b = b0 + i;
+    double v = 0.0;
+    if (b < a.B) {
+      if (c < r) {
+        v = a.k == 1 ? 0.0 : sprev[(size_t)b * r + c];
+      } else {
+        const int x = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
+        if ((unsigned)x < (unsigned)a.V) v = (double)w1_at<kBf16>(a.W1, (size_t)x * r + (c - r));
+      }
+    }
+    zs[idx] = v;
+  }
+  __syncthreads();
+  const int i = threadIdx.x / a.jn;
+  const int j = blockIdx.y * a.jn + threadIdx.x % a.jn;
+  const int b = b0 + i;
+  if (i >= a.nreq || b >= a.B || j >= r) return;
+  const double* z = zs + (size_t)i * r2;
+  const float4* wg = reinterpret_cast<const float4*>(a.Wp + (size_t)j * r2);
+  const float4* wc = reinterpret_cast<const float4*>(a.Wp + (size_t)(r + j) * r2);
+  const float4* wo = reinterpret_cast<const float4*>(a.Wp + (size_t)(2 * r + j) * r2);
+  double g = 0.0, c = 0.0, o = 0.0;
+  for (int q = 0; q < r2 / 4; ++q) {
+    const float4 x = wg[q], y = wc[q], w = wo[q];
+    const double z0 = z[4 * q], z1 = z[4 * q + 1], z2 = z[4 * q + 2], z3 = z[4 * q + 3];
+    g = fma((double)x.x, z0, g); g = fma((double)x.y, z1, g); g = fma((double)x.z, z2, g); g = fma((double)x.w, z3, g);
+    c = fma((double)y.x, z0, c); c = fma((double)y.y, z1, c); c = fma((double)y.z, z2, c); c = fma((double)y.w, z3, c);
+    o = fma((double)w.x, z0, o); o = fma((double)w.y, z1, o); o = fma((double)w.z, z2, o); o = fma((double)w.w, z3, o);
+  }
+  const size_t row = (size_t)b * a.gamma + a.k - 1;
+  const float* h = a.hp + row * 3 * r;
+  g += (double)h[j];
+  c += (double)h[r + j];
+  o += (double)h[2 * r + j];
+  const double sg = 1.0 / (1.0 + exp(-g));
+  snext[(size_t)b * r + j] = sg * z[j] + (1.0 - sg) * tanh(c);
+  const float e = (float)tanh(o);
+  const uint16_t hi = bf16_round(e);
+  const uint16_t lo = bf16_round(e - bf16_to_float(hi));
+  a.opnd[row * r2 + j] = hi;
+  a.opnd[row * r2 + r + j] = lo;
+  if (a.e_out) a.e_out[row * r + j] = e;
+}
+
+size_t rnn_draft_workspace(int B, int gamma, int V, int r) {
+  // the Markov draft's buffers without the ring operands, then the state
+  // and the operand table
+  return align256((size_t)B * tiles_of(V, kTileCols) * sizeof(float2)) + align256((size_t)2 * B * sizeof(double)) +
+         align256((size_t)2 * B * r * sizeof(double)) + align256((size_t)B * gamma * 2 * r * sizeof(uint16_t));
+}
+
+hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
+  const bool greedy = a.temperature == 0.0f;
+  const int ntiles = tiles_of(a.V, kTileCols);
+  char* ws = reinterpret_cast<char*>(a.ws);
+  float2* partials = reinterpret_cast<float2*>(ws);
+  ws += align256((size_t)a.B * ntiles * sizeof(float2));
+  double* u_next = reinterpret_cast<double*>(ws);
+  ws += align256((size_t)2 * a.B * sizeof(double));
+  double* state = reinterpret_cast<double*>(ws);
+  ws += align256((size_t)2 * a.B * a.r * sizeof(double));
+  uint16_t* opnd = reinterpret_cast<uint16_t*>(ws);
+  const float cf = greedy ? 0.0f : (float)(1.4426950408889634 / (double)a.temperature);
+
+  CellArgs ca = {};
+  ca.W1 = a.W1;
+  ca.Wp = a.Wp;
+  ca.hp = a.hp;
+  ca.x0 = a.x0;
+  ca.tokens = a.tokens;
+  ca.state = state;
+  ca.opnd = opnd;
+  ca.e_out = a.e_out;
+  ca.B = a.B;
+  ca.gamma = a.gamma;
+  ca.V = a.V;
+  ca.r = a.r;
+  ca.nreq = a.r <= 256 ? 8 : 4;          // z of the group: at most 32 KB of LDS
+  ca.jn = kCellThreads / ca.nreq;
+  const dim3 cgrid((a.B + ca.nreq - 1) / ca.nreq, (a.r + ca.jn - 1) / ca.jn);
+  const size_t clds = (size_t)ca.nreq * 2 * a.r * sizeof(double);
+
+  TileArgs t = {};
+  t.U = a.U;
+  t.W1 = opnd;
+  t.W2 = a.W2;
+  t.x0 = a.x0;
+  t.tokens = a.tokens;
+  t.partials = partials;
+  t.nrows = a.B;
+  t.kper = 1;
+  t.B = a.B;
+  t.gamma = a.gamma;
+  t.V = a.V;
+  t.r = a.r;
+  t.ntiles = ntiles;
+  t.cf = cf;
+  t.opnd_rows = 2;
+
+  SelectArgs sa = {};
+  sa.U = a.U;
+  sa.W1 = opnd;
+  sa.W2 = a.W2;
+  sa.x0 = a.x0;
+  sa.seeds = a.seeds;
+  sa.round = a.round;
+  sa.partials = partials;
+  sa.B = a.B;
+  sa.gamma = a.gamma;
+  sa.V = a.V;
+  sa.r = a.r;
+  sa.ntiles = ntiles;
+  sa.cf = cf;
+  sa.inv_t = greedy ? 0.0 : 1.0 / (double)a.temperature;
+  sa.tokens = a.tokens;
+  sa.prob = a.prob;
+  sa.lse = a.lse;
+  sa.u_next = u_next;
+  sa.opnd_rows = 2;
+
+  const int mode = greedy ? kModeGreedy : kModeSample;
+  for (int k = 1; k <= a.gamma; ++k) {
+    ca.k = k;
+    {
+      ProfScope prof(s, kProfRnnCell);
+      hipLaunchKernelGGL(rnn_cell_kernel<true>, cgrid, dim3(kCellThreads), clds, s, ca);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    t.k0 = k - 1;
+    e = launch_tile_pass(t, mode, true, s);
+    if (e != hipSuccess) return e;
+    sa.k = k;
+    if (greedy) {
+      e = launch_select<true, true>(sa, s);
+    } else if (ntiles <= kWaveTiles) {
+      e = launch_select_wave<true>(sa, s);
+    } else {
+      e = launch_select<false, true>(sa, s);
     }
     if (e != hipSuccess) return e;
   }

@@ -47,6 +47,9 @@ struct TileArgs {
   float cf;             // log2(e) / T; unused at T == 0
   const uint4* esw;     // optional: the W1 rows of the previous tokens in the ring
                         // kernel's operand layout (see ring_operand_index)
+  int opnd_rows;        // 0: W1 rows of previous tokens.  n > 0: W1 is a table of operand
+                        // rows, row b * gamma + kk for request b at block position kk, each
+                        // of n parts of r values whose sum is the operand (generic kernel)
 };
 
 hipError_t launch_tile_pass(const TileArgs& a, int mode, bool bf16, hipStream_t s);
@@ -84,6 +87,28 @@ struct DraftArgs {
 
 size_t draft_workspace(int B, int gamma, int V, int r);
 hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s);
+
+// Block sampling with the RNN head (bf16 W1 and W2 only).
+struct RnnDraftArgs {
+  const float* U;
+  const void* W1;
+  const void* W2;
+  const float* Wp;   // [3r][2r] recurrent and token columns of the cell projection
+  const float* hp;   // [B][gamma][3r] hidden-state part of the projection
+  const int32_t* x0;
+  const uint64_t* seeds;
+  uint64_t round;
+  int B, gamma, V, r;
+  float temperature;
+  int32_t* tokens;
+  float* prob;
+  float* lse;
+  float* e_out;      // optional [B][gamma][r]
+  void* ws;
+};
+
+size_t rnn_draft_workspace(int B, int gamma, int V, int r);
+hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s);
 
 struct VerifyArgs {
   const float* U;
@@ -189,7 +214,7 @@ hipError_t launch_markov_bias(const void* W1, const void* W2, bool bf16, const i
 enum ProfKind : int {
   kProfTileSample = 0, kProfTileGreedy, kProfTileOverlap, kProfTileBias, kProfDraftSelect,
   kProfVerifyInit, kProfTargetStats, kProfVerifyDecide, kProfResidualStats, kProfResidualSelect,
-  kProfSurvivalConf, kProfSurvivalTnorm, kProfSurvivalFinish, kProfSchedule, kProfConfidence, kProfKinds
+  kProfSurvivalConf, kProfSurvivalTnorm, kProfSurvivalFinish, kProfSchedule, kProfConfidence, kProfRnnCell, kProfKinds
 };
 
 // Brackets the launches made during its lifetime with HIP events when timing

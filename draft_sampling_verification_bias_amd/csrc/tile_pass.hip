@@ -40,8 +40,16 @@ __device__ __forceinline__ RowInfo row_info(const TileArgs& a, int R) {
   return ri;
 }
 
+// The W1 row of row (b, kk): the previous token's, or with operand rows the
+// table row b * gamma + kk.
 __device__ __forceinline__ int prev_token(const TileArgs& a, RowInfo ri) {
+  if (a.opnd_rows) return ri.b * a.gamma + ri.kk;
   return ri.kk == 0 ? a.x0[ri.b] : a.tokens[(size_t)ri.b * a.gamma + ri.kk - 1];
+}
+
+// Whether that row exists (a token id inside the vocabulary).
+__device__ __forceinline__ bool prev_ok(const TileArgs& a, int prev) {
+  return a.opnd_rows ? prev >= 0 : (unsigned)prev < (unsigned)a.V;
 }
 
 // ---------------------------------------------------------------------------
@@ -285,7 +293,7 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
 
   // B operand: row R of E = W1[prev], k-chunk hh of each 16-wide k step.
   const int prev = prev_token(a, row_info(a, Rc));
-  const bool ok = rowok && (unsigned)prev < (unsigned)a.V;
+  const bool ok = rowok && prev_ok(a, prev);
   const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
   bf16x8 ev[16];
 #pragma unroll
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
     issue_u(0, uA);
   } else {
     const int prev = prev_token(a, row_info(a, Rc));
-    const bool ok = rowok && (unsigned)prev < (unsigned)a.V;
+    const bool ok = rowok && prev_ok(a, prev);
     const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
 #pragma unroll
     for (int j = 0; j < 16; ++j) ev[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
@@ -759,11 +767,16 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
       const int arow = R0 + (lane & 31);
       int prev = -1;
       if (arow < row1) prev = prev_token(a, row_info(a, arow));
-      const bool ok = prev >= 0 && prev < a.V;
-      const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * a.r;
+      const bool ok = arow < row1 && prev_ok(a, prev);
+      // Operand rows may hold several parts of r values (a bf16 value and its
+      // bf16 remainder); every part multiplies the same staged W2 tile.
+      const int parts = a.opnd_rows > 0 ? a.opnd_rows : 1;
+      const uint16_t* w1base = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * parts * a.r;
       const int koff = 8 * (lane >> 5);
       const uint16_t* bcol = sW + (size_t)(lane & 31) * pitch + koff;
+      for (int part = 0; part < parts; ++part)
       for (int k0 = 0; k0 < ksteps; k0 += 16) {
+        const uint16_t* w1row = w1base + (size_t)part * a.r;
         bf16x8 av[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -789,13 +802,14 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
       // float32 weights: each lane forms its 16 rows x 4 columns directly.
       const float* W1f = reinterpret_cast<const float*>(a.W1);
       const float* W2f = reinterpret_cast<const float*>(a.W2);
+      const int parts = a.opnd_rows > 0 ? a.opnd_rows : 1;
       int prevs[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int R = R0 + acc_row(i, lane);
         int p = -1;
         if (R < row1) p = prev_token(a, row_info(a, R));
-        prevs[i] = (p >= 0 && p < a.V) ? p : -1;
+        prevs[i] = (R < row1 && prev_ok(a, p)) ? p : -1;
       }
       for (int kq = 0; kq < a.r; ++kq) {
         float w2v[kNB];
@@ -803,7 +817,9 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
         for (int nb = 0; nb < kNB; ++nb) w2v[nb] = c4 + nb < a.V ? W2f[(size_t)kq * a.V + c4 + nb] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = prevs[i] >= 0 ? W1f[(size_t)prevs[i] * a.r + kq] : 0.0f;
+          float e = 0.0f;
+          if (prevs[i] >= 0)
+            for (int part = 0; part < parts; ++part) e += W1f[((size_t)prevs[i] * parts + part) * a.r + kq];
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) acc[nb][i] = fmaf(e, w2v[nb], acc[nb][i]);
         }
@@ -935,11 +951,11 @@ static void launch_tiles(const TileArgs& a, int row_begin, int row_end, int tile
 // Full 128-column tiles of the vocabulary on the fast paths (V % 4 == 0).
 static int fast_full_tiles(const TileArgs& a) { return (a.V & 3) == 0 ? a.V / kTileCols : 0; }
 
-// The fast paths: bf16 weights, r = 256, at least one full tile, rows at a
-// constant stride, and W2 addressed with 32-bit byte offsets (2 r V < 2^32).
+// The fast paths: bf16 weights, r = 256, W1 rows of previous tokens, at least
+// one full tile, rows at a constant stride, and W2 addressed with 32-bit byte offsets (2 r V < 2^32).
 static bool fast_path(const TileArgs& a, int mode, bool bf16) {
   return bf16 && (mode == kModeSample || mode == kModeGreedy || mode == kModeOverlap) && a.r == kFastR &&
-         (a.kper == 1 || a.kper == a.gamma) && fast_full_tiles(a) > 0 &&
+         a.opnd_rows == 0 && (a.kper == 1 || a.kper == a.gamma) && fast_full_tiles(a) > 0 &&
          (size_t)2 * kFastR * (size_t)a.V < ((size_t)1 << 32);
 }
 

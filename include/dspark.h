@@ -94,7 +94,12 @@ typedef enum {
 } dspark_schedule_mode;
 
 /* Which entry point a workspace is sized for. */
-typedef enum { DSPARK_OP_DRAFT = 0, DSPARK_OP_VERIFY = 1, DSPARK_OP_SURVIVAL = 2 } dspark_op;
+typedef enum {
+  DSPARK_OP_DRAFT = 0,
+  DSPARK_OP_VERIFY = 1,
+  DSPARK_OP_SURVIVAL = 2,
+  DSPARK_OP_RNN_DRAFT = 3
+} dspark_op;
 
 /* Maximum number of residual proposals drawn against p_t before the exact
  * residual inverse CDF (stream 3) is used. */
@@ -147,6 +152,39 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
                                   const uint64_t* seeds, uint64_t round,
                                   int32_t* draft_tokens, float* draft_prob, float* draft_lse,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_rnn_draft -- the same block sampling with the RNN head of [R]
+ * "Instantiation 2: The RNN Head" (Eq. 6) in place of the Markov bias.
+ *
+ * For every request b, s_0 = 0 and for k = 1..gamma, left to right:
+ *   (g, c, o) = Wp [s_{k-1} ; W1[x_{k-1}]] + hp[b][k-1]     (x_0 = x0[b])
+ *   s_k       = sigmoid(g) s_{k-1} + (1 - sigmoid(g)) tanh(c)
+ *   e_k       = tanh(o)
+ *   l_k(v)    = U[b][k][v] + e_k . W2[:, v]
+ * then x_k, draft_prob and draft_lse exactly as dspark_markov_draft (same
+ * stream-0 uniforms, same greedy rule at T == 0).
+ *
+ *   W1, W2  bf16 only (wdtype must be DSPARK_BF16)
+ *   Wp      float32 [3r][2r]   rows: gate, candidate, output; columns: the
+ *                              state s_{k-1}, then the token embedding
+ *   hp      float32 [B][gamma][3r]  the hidden-state part of the projection,
+ *                              W_p[:, 2r:] h_k, computed by the caller (it
+ *                              depends on no drafted token)
+ *   e_out   float32 [B][gamma][r] or NULL: the e_k used
+ * The cell runs in float64; e_k enters the bf16 tile pass as two bf16 parts
+ * (e_k to about 2^-18 relative).  A position after an invalid anchor or
+ * token is -1 / NaN as in dspark_markov_draft.
+ * Workspace: dspark_workspace_size(DSPARK_OP_RNN_DRAFT, B, gamma, V, r).
+ * Errors: DSPARK_ERR_UNSUPPORTED for float32 weights, otherwise as
+ * dspark_markov_draft.
+ */
+dspark_status dspark_rnn_draft(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
+                               const float* Wp, const float* hp, const int32_t* x0,
+                               int B, int gamma, int V, int r, float temperature,
+                               const uint64_t* seeds, uint64_t round,
+                               int32_t* draft_tokens, float* draft_prob, float* draft_lse, float* e_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dspark_verify -- lossless rejection-sampling verification of the drafted

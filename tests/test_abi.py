@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dspark_markov_draft", "dspark_verify", "dspark_survival", "dspark_markov_bias", "dspark_schedule",
-              "dspark_confidence",
+              "dspark_confidence", "dspark_rnn_draft",
               "dspark_workspace_size", "dspark_status_string", "dspark_version"):
         assert n in names
 
@@ -54,7 +54,7 @@ def test_version_and_status_strings(lib):
     assert lib.dspark_status_string(123) == b"unknown status"
 
 
-@pytest.mark.parametrize("op", [dsp.OP_DRAFT, dsp.OP_VERIFY, dsp.OP_SURVIVAL])
+@pytest.mark.parametrize("op", [dsp.OP_DRAFT, dsp.OP_VERIFY, dsp.OP_SURVIVAL, dsp.OP_RNN_DRAFT])
 def test_workspace_size(lib, op):
     small = dsp.workspace_size(op, 4, 4, 1000, 16)
     big = dsp.workspace_size(op, 256, 7, 151936, 256)
@@ -84,6 +84,32 @@ def _draft(lib, **kw):
 ])
 def test_draft_rejects_bad_arguments(lib, kw, status):
     assert _draft(lib, **kw) == status
+
+
+def _rnn_draft(lib, **kw):
+    a = dict(U=FAKE, W1=FAKE, W2=FAKE, wd=1, Wp=FAKE, hp=FAKE, x0=FAKE, B=4, gamma=4, V=1000, r=16, T=1.0,
+             seeds=FAKE, rnd=0, tok=FAKE, prob=FAKE, lse=FAKE, e=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.dspark_rnn_draft(a["U"], a["W1"], a["W2"], a["wd"], a["Wp"], a["hp"], a["x0"], a["B"], a["gamma"],
+                                a["V"], a["r"], a["T"], a["seeds"], a["rnd"], a["tok"], a["prob"], a["lse"], a["e"],
+                                a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(gamma=33), INVALID), (dict(r=40), INVALID), (dict(T=-1.0), INVALID),
+    (dict(Wp=None), INVALID), (dict(hp=None), INVALID), (dict(Wp=MISALIGNED), INVALID),
+    (dict(hp=MISALIGNED - 2), INVALID), (dict(e=MISALIGNED - 2), INVALID), (dict(seeds=None), INVALID),
+    (dict(wd=0), UNSUPPORTED), (dict(wd=5), UNSUPPORTED), (dict(wsb=16), WORKSPACE),
+])
+def test_rnn_draft_rejects_bad_arguments(lib, kw, status):
+    assert _rnn_draft(lib, **kw) == status
+
+
+def test_rnn_draft_workspace_holds_the_state_and_operands():
+    B, gamma, V, r = 256, 7, 151936, 256
+    extra = dsp.workspace_size(dsp.OP_RNN_DRAFT, B, gamma, V, r) - dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, r)
+    # float64 state (two buffers) and bf16 operand rows of 2r, less the ring operands
+    assert extra >= 2 * B * r * 8 + B * gamma * 2 * r * 2 - ((B + 255) // 256) * 256 * 512
 
 
 def _verify(lib, **kw):

@@ -203,3 +203,14 @@ def confidence_inputs(B, gamma, d, r, seed=0, spread=1.5):
     w = _normal(rng, (d + r,), spread / np.sqrt(d))
     sts = np.linspace(0.8, 1.6, gamma).astype(np.float32)
     return h, w, sts
+
+
+def rnn_inputs(B, gamma, r, seed=0, gain=1.5, hp_std=0.5):
+    """Synthetic inputs of the RNN head: the cell projection's state and token
+    columns Wp [3r][2r] ~ N(0, gain / sqrt(2r)) and its hidden-state part hp
+    [B][gamma][3r] ~ N(0, hp_std), the share a random hidden state of the
+    target would contribute.  float32."""
+    rng = np.random.default_rng(5000 + seed)
+    Wp = _normal(rng, (3 * r, 2 * r), gain / np.sqrt(2.0 * r))
+    hp = _normal(rng, (B, gamma, 3 * r), hp_std)
+    return Wp, hp
