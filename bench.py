@@ -13,7 +13,8 @@ the step's compulsory bytes reach, the roofline of the dominant kernel (the
 draft tile pass, timed live with HIP events on its own stream), the analytical
 dspark_survival time and the scheduled round (confidence head, prefix
 scheduler, verification at its lengths; both reported beside the gated
-path), and the float64 oracle
+path), the RNN-head draft at the same sizes beside the Markov draft, and the
+float64 oracle
 timed on the host cores on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
@@ -133,6 +134,8 @@ def main():
                     help="cold-cache figure: write this many MiB before each of K separately timed steps (0: skip)")
     ap.add_argument("--schedule-steps", type=int, default=20,
                     help="timed calls of the prefix scheduler and of verification with its lengths (0: skip)")
+    ap.add_argument("--rnn-steps", type=int, default=10,
+                    help="timed calls of the RNN-head draft beside the Markov draft (0: skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="copy this many MiB device to device once before timing (a reference kernel of known "
                          "traffic for hardware counter runs)")
@@ -340,6 +343,44 @@ def main():
                  "mean_accept_len_full": float(full_len.mean()), "mean_accept_len_scheduled": float(sch_len.mean()),
                  "round_scheduled_ms": round_ms}
 
+    # Block sampling with the RNN head (Eq. 6) at the same sizes, timed beside
+    # the Markov draft: synthetic cell projection and hidden-state part.
+    rnn = None
+    if args.rnn_steps > 0 and wl.wdtype == "bf16":
+        Wp_np, hp_np = workloads.rnn_inputs(B, gamma, r)
+        Wp_d, hp_d = torch.from_numpy(Wp_np).to(dev), torch.from_numpy(hp_np).to(dev)
+        ws_r = torch.empty(dsp.workspace_size(dsp.OP_RNN_DRAFT, B, gamma, V, r), dtype=torch.uint8, device=dev)
+        rout = dout + (None,)
+
+        def rnn_step(i):
+            dsp.rnn_draft(U, W1, W2, Wp_d, hp_d, x0, T, seeds, 4000 + i, out=rout, workspace=ws_r, stream=stream)
+
+        def markov_step(i):
+            dsp.markov_draft(U, W1, W2, x0, T, seeds, 4000 + i, out=dout, workspace=ws_d, stream=stream)
+
+        def per_call_ms(fn):
+            fn(0)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for i in range(args.rnn_steps):
+                fn(i)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t) / args.rnn_steps * 1e3
+
+        rnn_ms = per_call_ms(rnn_step)
+        markov_ms = per_call_ms(markov_step)
+        dsp.profile_enable(True)
+        for i in range(args.rnn_steps):
+            rnn_step(i)
+        torch.cuda.synchronize()
+        rprof = dsp.profile_read()
+        dsp.profile_enable(False)
+        rnn = {"draft_ms": rnn_ms, "markov_draft_ms": markov_ms,
+               "positions_per_s": B * gamma / (rnn_ms * 1e-3),
+               "kernels": {k: {"launches": n, "avg_us": ms / n * 1e3, "ms_per_call": ms / args.rnn_steps}
+                           for k, (n, ms) in rprof.items()}}
+        del ws_r, Wp_d, hp_d
+
     flops = 2.0 * r * V * (B * gamma + float((lens < gamma).sum()) / nsteps)
     out = {
         "metric": METRIC,
@@ -367,6 +408,7 @@ def main():
         "cold_cache": cold,
         "survival_ms": surv_ms,
         "schedule": sched,
+        "rnn_draft": rnn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

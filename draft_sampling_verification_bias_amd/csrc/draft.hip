@@ -590,12 +590,14 @@ hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s) {
 // brings it precomputed from the parallel stage.
 //
 // One cell launch per position: workgroup (request group, slice of jn state
-// units) stages z = [s_{k-1}; W1[x_{k-1}]] of its requests in LDS as float64,
-// and each thread forms the three projections of one (request, unit) in
-// float64.  e_k goes to the operand table as two bf16 parts (hi = bf16(e),
-// lo = bf16(e - hi)), so that the bf16 MFMA tile pass multiplies W2 by
-// hi + lo, which is e to about 2^-18 relative.  The state is double-buffered
-// in float64 (position k reads buffer (k - 1) & 1 and writes k & 1).
+// units) stages z = [s_{k-1}; W1[x_{k-1}]] of its requests in LDS and streams
+// its rows of Wp through LDS in column chunks; each thread forms the three
+// projections of one (request, unit).  The cell computes in float32, the
+// precision of its inputs Wp and hp.  e_k goes to the operand table as two
+// bf16 parts (hi = bf16(e), lo = bf16(e - hi)), so that the bf16 MFMA tile
+// pass multiplies W2 by hi + lo, which is e to about 2^-18 relative.  The
+// state is double-buffered (position k reads buffer (k - 1) & 1 and writes
+// k & 1).
 // ---------------------------------------------------------------------------
 
 struct CellArgs {
@@ -604,7 +606,7 @@ struct CellArgs {
   const float* hp;     // [B][gamma][3r]
   const int32_t* x0;
   const int32_t* tokens;
-  double* state;       // [2][B][r]
+  float* state;        // [2][B][r]
   uint16_t* opnd;      // [B * gamma][2r]: bf16 hi parts, then lo parts
   float* e_out;        // optional [B][gamma][r]
   int B, gamma, V, r, k, nreq, jn;
@@ -619,49 +621,123 @@ __device__ __forceinline__ uint16_t bf16_round(float f) {
 
 template <bool kBf16>
 __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
-  extern __shared__ double zs[];  // [nreq][2r]
+  // LDS: z of the group [nreq][2r], then one chunk of the workgroup's 3 jn
+  // rows of Wp, [3 jn][chunk + 1] (the odd pitch puts the rows a wave reads
+  // in different banks).
+  extern __shared__ float zs[];
   const int r = a.r, r2 = 2 * a.r;
+  const int jn = a.jn, chunk = kCellThreads * 8 / jn, pitch = chunk + 1;
+  float* sw = zs + (size_t)a.nreq * r2;
   const int b0 = blockIdx.x * a.nreq;
-  const double* sprev = a.state + (size_t)((a.k - 1) & 1) * a.B * r;
-  double* snext = a.state + (size_t)(a.k & 1) * a.B * r;
-  for (int idx = threadIdx.x; idx < a.nreq * r2; idx += kCellThreads) {
-    const int i = idx / r2, c = idx - (idx / r2) * r2, b = b0 + i;
-    double v = 0.0;
-    if (b < a.B) {
-      if (c < r) {
-        v = a.k == 1 ? 0.0 : sprev[(size_t)b * r + c];
-      } else {
-        const int x = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
-        if ((unsigned)x < (unsigned)a.V) v = (double)w1_at<kBf16>(a.W1, (size_t)x * r + (c - r));
-      }
+  const int j0 = blockIdx.y * jn;
+  const float* sprev = a.state + (size_t)((a.k - 1) & 1) * a.B * r;
+  float* snext = a.state + (size_t)(a.k & 1) * a.B * r;
+
+  // Wp chunk loads: 3 jn rows x chunk columns = 6 float4 per thread,
+  // consecutive threads along a row (chunk * 4 contiguous bytes per row).
+  constexpr int kLoads = 6;
+  const int q4 = chunk / 4;
+  float4 wv[kLoads];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int idx = l * kCellThreads + threadIdx.x;
+      const int lr = idx / q4, cq = idx - (idx / q4) * q4;     // local row 0 .. 3 jn - 1
+      const int g = lr / jn, jj = lr - (lr / jn) * jn;
+      const int j = min(j0 + jj, r - 1);                         // rows past r: clamped, unused
+      wv[l] = c0 + 4 * cq < r2 ? *reinterpret_cast<const float4*>(a.Wp + (size_t)(g * r + j) * r2 + c0 + 4 * cq)
+                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);  // past the row (2r % chunk != 0)
     }
-    zs[idx] = v;
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int idx = l * kCellThreads + threadIdx.x;
+      const int lr = idx / q4, cq = idx - (idx / q4) * q4;
+      float* d = sw + (size_t)lr * pitch + 4 * cq;
+      d[0] = wv[l].x;
+      d[1] = wv[l].y;
+      d[2] = wv[l].z;
+      d[3] = wv[l].w;
+    }
+  };
+  __shared__ int sx[8];  // x_{k-1} of each request of the group
+  if (threadIdx.x < a.nreq) {
+    const int b = b0 + threadIdx.x;
+    sx[threadIdx.x] = b >= a.B ? -1 : (a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2]);
+  }
+  load_chunk(0);
+  const int i = threadIdx.x / jn, jj = threadIdx.x - (threadIdx.x / jn) * jn;
+  const int j = j0 + jj;
+  const int b = b0 + i;
+  const bool mine = b < a.B && j < r;
+  const size_t row = (size_t)b * a.gamma + a.k - 1;
+  float hv[3] = {0.0f, 0.0f, 0.0f};
+  if (mine) {
+    const float* h = a.hp + row * 3 * r;
+    hv[0] = h[j];
+    hv[1] = h[r + j];
+    hv[2] = h[2 * r + j];
   }
   __syncthreads();
-  const int i = threadIdx.x / a.jn;
-  const int j = blockIdx.y * a.jn + threadIdx.x % a.jn;
-  const int b = b0 + i;
-  if (i >= a.nreq || b >= a.B || j >= r) return;
-  const double* z = zs + (size_t)i * r2;
-  const float4* wg = reinterpret_cast<const float4*>(a.Wp + (size_t)j * r2);
-  const float4* wc = reinterpret_cast<const float4*>(a.Wp + (size_t)(r + j) * r2);
-  const float4* wo = reinterpret_cast<const float4*>(a.Wp + (size_t)(2 * r + j) * r2);
-  double g = 0.0, c = 0.0, o = 0.0;
-  for (int q = 0; q < r2 / 4; ++q) {
-    const float4 x = wg[q], y = wc[q], w = wo[q];
-    const double z0 = z[4 * q], z1 = z[4 * q + 1], z2 = z[4 * q + 2], z3 = z[4 * q + 3];
-    g = fma((double)x.x, z0, g); g = fma((double)x.y, z1, g); g = fma((double)x.z, z2, g); g = fma((double)x.w, z3, g);
-    c = fma((double)y.x, z0, c); c = fma((double)y.y, z1, c); c = fma((double)y.z, z2, c); c = fma((double)y.w, z3, c);
-    o = fma((double)w.x, z0, o); o = fma((double)w.y, z1, o); o = fma((double)w.z, z2, o); o = fma((double)w.w, z3, o);
+
+  // z = [s_{k-1}; W1[x_{k-1}]]: every load issued before the first LDS store
+  // (nreq * 2r <= 4096, so at most 16 values per thread).
+  constexpr int kZ = 16;
+  const int nz = a.nreq * r2;
+  float zv[kZ];
+#pragma unroll
+  for (int t = 0; t < kZ; ++t) {
+    const int idx = t * kCellThreads + threadIdx.x;
+    const int zi = idx / r2, zc = idx - (idx / r2) * r2, zb = b0 + zi;
+    float v = 0.0f;
+    if (idx < nz && zb < a.B) {
+      if (zc < r) {
+        if (a.k > 1) v = sprev[(size_t)zb * r + zc];
+      } else {
+        const int x = sx[zi];
+        if ((unsigned)x < (unsigned)a.V) v = w1_at<kBf16>(a.W1, (size_t)x * r + (zc - r));
+      }
+    }
+    zv[t] = v;
   }
-  const size_t row = (size_t)b * a.gamma + a.k - 1;
-  const float* h = a.hp + row * 3 * r;
-  g += (double)h[j];
-  c += (double)h[r + j];
-  o += (double)h[2 * r + j];
-  const double sg = 1.0 / (1.0 + exp(-g));
-  snext[(size_t)b * r + j] = sg * z[j] + (1.0 - sg) * tanh(c);
-  const float e = (float)tanh(o);
+#pragma unroll
+  for (int t = 0; t < kZ; ++t) {
+    const int idx = t * kCellThreads + threadIdx.x;
+    if (idx < nz) zs[idx] = zv[t];
+  }
+
+  const float* z = zs + (size_t)i * r2;
+  const float* wg = sw + (size_t)jj * pitch;
+  const float* wc = sw + (size_t)(jn + jj) * pitch;
+  const float* wo = sw + (size_t)(2 * jn + jj) * pitch;
+  // two partial sums per projection (even and odd columns): shorter chains
+  float g = 0.0f, c = 0.0f, o = 0.0f, g2 = 0.0f, c2 = 0.0f, o2 = 0.0f;
+  for (int c0 = 0; c0 < r2; c0 += chunk) {
+    __syncthreads();  // the previous chunk is consumed (first pass: z is staged)
+    store_chunk();
+    __syncthreads();
+    if (c0 + chunk < r2) load_chunk(c0 + chunk);  // in flight during the products
+    const int cn = min(chunk, r2 - c0);  // even: 2r % 32 == 0
+#pragma unroll 4
+    for (int q = 0; q < cn; q += 2) {
+      const float za = z[c0 + q], zb = z[c0 + q + 1];
+      g = fmaf(wg[q], za, g);
+      c = fmaf(wc[q], za, c);
+      o = fmaf(wo[q], za, o);
+      g2 = fmaf(wg[q + 1], zb, g2);
+      c2 = fmaf(wc[q + 1], zb, c2);
+      o2 = fmaf(wo[q + 1], zb, o2);
+    }
+  }
+
+  if (!mine) return;
+  g += g2 + hv[0];
+  c += c2 + hv[1];
+  o += o2 + hv[2];
+  const float sg = 1.0f / (1.0f + expf(-g));
+  snext[(size_t)b * r + j] = sg * z[j] + (1.0f - sg) * tanhf(c);
+  const float e = tanhf(o);
   const uint16_t hi = bf16_round(e);
   const uint16_t lo = bf16_round(e - bf16_to_float(hi));
   a.opnd[row * r2 + j] = hi;
@@ -673,7 +749,7 @@ size_t rnn_draft_workspace(int B, int gamma, int V, int r) {
   // the Markov draft's buffers without the ring operands, then the state
   // and the operand table
   return align256((size_t)B * tiles_of(V, kTileCols) * sizeof(float2)) + align256((size_t)2 * B * sizeof(double)) +
-         align256((size_t)2 * B * r * sizeof(double)) + align256((size_t)B * gamma * 2 * r * sizeof(uint16_t));
+         align256((size_t)2 * B * r * sizeof(float)) + align256((size_t)B * gamma * 2 * r * sizeof(uint16_t));
 }
 
 hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
@@ -684,8 +760,8 @@ hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
   ws += align256((size_t)a.B * ntiles * sizeof(float2));
   double* u_next = reinterpret_cast<double*>(ws);
   ws += align256((size_t)2 * a.B * sizeof(double));
-  double* state = reinterpret_cast<double*>(ws);
-  ws += align256((size_t)2 * a.B * a.r * sizeof(double));
+  float* state = reinterpret_cast<float*>(ws);
+  ws += align256((size_t)2 * a.B * a.r * sizeof(float));
   uint16_t* opnd = reinterpret_cast<uint16_t*>(ws);
   const float cf = greedy ? 0.0f : (float)(1.4426950408889634 / (double)a.temperature);
 
@@ -702,10 +778,11 @@ hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
   ca.gamma = a.gamma;
   ca.V = a.V;
   ca.r = a.r;
-  ca.nreq = a.r <= 256 ? 8 : 4;          // z of the group: at most 32 KB of LDS
+  ca.nreq = a.r <= 256 ? 8 : 4;          // z of the group: at most 16 KB of LDS
   ca.jn = kCellThreads / ca.nreq;
   const dim3 cgrid((a.B + ca.nreq - 1) / ca.nreq, (a.r + ca.jn - 1) / ca.jn);
-  const size_t clds = (size_t)ca.nreq * 2 * a.r * sizeof(double);
+  const int chunk = kCellThreads * 8 / ca.jn;  // Wp columns per LDS stage: 6 float4 loads per thread
+  const size_t clds = ((size_t)ca.nreq * 2 * a.r + (size_t)3 * ca.jn * (chunk + 1)) * sizeof(float);
 
   TileArgs t = {};
   t.U = a.U;

@@ -219,9 +219,12 @@ __device__ __forceinline__ void pipe_block(int ngroups, int nslices, int& group,
   slice = idx / ngroups;
 }
 
-template <int kMode>
-__global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void tile_pipe_kernel(TileArgs a,
-                                                                                               int nslices) {
+// kParts == 2: operand-table rows of two bf16 parts (value, remainder), each
+// multiplied by the same W2 fragments; the second operand set needs the
+// register file of one workgroup per CU, as the overlap mode's target values do.
+template <int kMode, int kParts>
+__global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap || kParts == 2 ? 1 : 2) void tile_pipe_kernel(
+    TileArgs a, int nslices) {
   constexpr bool kOv = kMode == kModeOverlap;  // also streams the target rows
   extern __shared__ __align__(16) unsigned char smem[];
   int group, slice;
@@ -294,15 +297,20 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
   // B operand: row R of E = W1[prev], k-chunk hh of each 16-wide k step.
   const int prev = prev_token(a, row_info(a, Rc));
   const bool ok = rowok && prev_ok(a, prev);
-  const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
-  bf16x8 ev[16];
+  const uint16_t* w1row =
+      reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kParts * kFastR + 8 * hh;
+  bf16x8 ev[kParts][16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) ev[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
+  for (int p = 0; p < kParts; ++p)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ev[p][j] = *reinterpret_cast<const bf16x8*>(w1row + p * kFastR + j * 16);
   if (!ok) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int p = 0; p < kParts; ++p)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ev[j][e] = (__bf16)0.0f;
+      for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ev[p][j][e] = (__bf16)0.0f;
   }
 
   const int trow = 8 * hh + ((lane & 15) >> 2);             // + 16 j + 4 h
@@ -328,7 +336,9 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void t
 #pragma unroll
           for (int e = 0; e < 4; ++e) av[4 * h + e] = t[e];
         }
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[j], acc[nb], 0, 0, 0);
+#pragma unroll
+        for (int p = 0; p < kParts; ++p)
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[p][j], acc[nb], 0, 0, 0);
       }
     }
 #pragma unroll
@@ -951,11 +961,12 @@ static void launch_tiles(const TileArgs& a, int row_begin, int row_end, int tile
 // Full 128-column tiles of the vocabulary on the fast paths (V % 4 == 0).
 static int fast_full_tiles(const TileArgs& a) { return (a.V & 3) == 0 ? a.V / kTileCols : 0; }
 
-// The fast paths: bf16 weights, r = 256, W1 rows of previous tokens, at least
-// one full tile, rows at a constant stride, and W2 addressed with 32-bit byte offsets (2 r V < 2^32).
+// The fast paths: bf16 weights, r = 256, W1 rows of previous tokens (or
+// two-part operand rows, pipelined kernel only), at least one full tile, rows
+// at a constant stride, and W2 addressed with 32-bit byte offsets (2 r V < 2^32).
 static bool fast_path(const TileArgs& a, int mode, bool bf16) {
   return bf16 && (mode == kModeSample || mode == kModeGreedy || mode == kModeOverlap) && a.r == kFastR &&
-         a.opnd_rows == 0 && (a.kper == 1 || a.kper == a.gamma) && fast_full_tiles(a) > 0 &&
+         (a.opnd_rows == 0 || (a.opnd_rows == 2 && mode != kModeOverlap)) && (a.kper == 1 || a.kper == a.gamma) && fast_full_tiles(a) > 0 &&
          (size_t)2 * kFastR * (size_t)a.V < ((size_t)1 << 32);
 }
 
@@ -963,6 +974,7 @@ bool tile_pass_uses_ring(const TileArgs& a, int mode, bool bf16) {
   const int rgroups = (a.nrows + kRingRows - 1) / kRingRows;
   // the ring kernel when its 256-row groups are at least 3/4 filled
   return fast_path(a, mode, bf16) && (mode == kModeSample || mode == kModeGreedy) && a.kper == 1 &&
+         a.opnd_rows == 0 &&
          4 * a.nrows >= 3 * rgroups * kRingRows;
 }
 
@@ -1005,13 +1017,20 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
     g.tile_begin = 0;
     g.tile_count = full_tiles;
     // Two resident workgroups per CU (64 KB of LDS each; one in overlap mode,
-    // whose waves also hold the target values); the column slices of every
-    // row group together fill them once.
-    int nslices = (kMode == kModeOverlap ? 1 : 2) * compute_units_of_device() / groups;
+    // whose waves also hold the target values, and with two-part operands);
+    // the column slices of every row group together fill them once.
+    const bool one_per_cu = kMode == kModeOverlap || a.opnd_rows == 2;
+    int nslices = (one_per_cu ? 1 : 2) * compute_units_of_device() / groups;
     if (nslices >= 8) nslices &= ~7;
     nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
     const size_t lds = 2 * (size_t)kHalfBytes;
-    hipLaunchKernelGGL((tile_pipe_kernel<kMode>), dim3(groups * nslices), dim3(kTileThreads), lds, s, g, nslices);
+    if (kMode != kModeOverlap && a.opnd_rows == 2) {
+      hipLaunchKernelGGL((tile_pipe_kernel<kMode, kMode == kModeOverlap ? 1 : 2>), dim3(groups * nslices),
+                         dim3(kTileThreads), lds, s, g, nslices);
+    } else {
+      hipLaunchKernelGGL((tile_pipe_kernel<kMode, 1>), dim3(groups * nslices), dim3(kTileThreads), lds, s, g,
+                         nslices);
+    }
   }
   // The partial last tile, all rows.
   launch_tiles<kMode, kBf16>(a, 0, a.nrows, full_tiles, a.ntiles - full_tiles, s);

@@ -172,8 +172,8 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
  *                              W_p[:, 2r:] h_k, computed by the caller (it
  *                              depends on no drafted token)
  *   e_out   float32 [B][gamma][r] or NULL: the e_k used
- * The cell runs in float64; e_k enters the bf16 tile pass as two bf16 parts
- * (e_k to about 2^-18 relative).  A position after an invalid anchor or
+ * The cell computes in float32 (the precision of Wp and hp); e_k enters the
+ * bf16 tile pass as two bf16 parts (e_k to about 2^-18 relative).  A position after an invalid anchor or
  * token is -1 / NaN as in dspark_markov_draft.
  * Workspace: dspark_workspace_size(DSPARK_OP_RNN_DRAFT, B, gamma, V, r).
  * Errors: DSPARK_ERR_UNSUPPORTED for float32 weights, otherwise as

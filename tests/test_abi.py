@@ -108,8 +108,8 @@ def test_rnn_draft_rejects_bad_arguments(lib, kw, status):
 def test_rnn_draft_workspace_holds_the_state_and_operands():
     B, gamma, V, r = 256, 7, 151936, 256
     extra = dsp.workspace_size(dsp.OP_RNN_DRAFT, B, gamma, V, r) - dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, r)
-    # float64 state (two buffers) and bf16 operand rows of 2r, less the ring operands
-    assert extra >= 2 * B * r * 8 + B * gamma * 2 * r * 2 - ((B + 255) // 256) * 256 * 512
+    # float32 state (two buffers) and bf16 operand rows of 2r, less the ring operands
+    assert extra >= 2 * B * r * 4 + B * gamma * 2 * r * 2 - ((B + 255) // 256) * 256 * 512
 
 
 def _verify(lib, **kw):
