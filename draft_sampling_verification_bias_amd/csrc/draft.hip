@@ -36,8 +36,6 @@ struct SelectArgs {
   float* lse;
   double* u_next;  // [2][B] stream-0 uniforms drawn one position ahead
   uint4* esw;      // optional: the drafted token's W1 row for the next tile pass
-  int opnd_rows;   // 0: W1 rows of tokens.  n > 0: W1 is a table of operand rows (row
-                   // b * gamma + k - 1), each of n parts of r values summed to the operand
 };
 
 // Store W1 row x (bf16, r = 256) in the ring tile pass's operand layout for
@@ -70,18 +68,18 @@ __device__ __forceinline__ float w1_at(const void* W1, size_t idx) {
   }
 }
 
-// Element j of the operand row `row` (a token's W1 row, or the sum of the
-// parts of an operand-table row).
-template <bool kBf16>
+// Element j of W1 row `row`.  kParts == 1: a token's row.  kParts == 2: W1 is
+// a table of operand rows (row b * gamma + k - 1) of two parts of r values,
+// summed.
+template <bool kBf16, int kParts>
 __device__ __forceinline__ float opnd_at(const SelectArgs& a, int row, int j) {
-  const int parts = a.opnd_rows > 0 ? a.opnd_rows : 1;
-  const size_t base = (size_t)row * parts * a.r + j;
+  const size_t base = (size_t)row * kParts * a.r + j;
   float v = w1_at<kBf16>(a.W1, base);
-  for (int p = 1; p < parts; ++p) v += w1_at<kBf16>(a.W1, base + (size_t)p * a.r);
+  if constexpr (kParts == 2) v += w1_at<kBf16>(a.W1, base + a.r);
   return v;
 }
 
-template <bool kGreedy, bool kBf16>
+template <bool kGreedy, bool kBf16, int kParts = 1>
 __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a) {
   __shared__ PickScratch ps;
   __shared__ float sw1[512];
@@ -107,7 +105,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
     }
   }
   const int ptok = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
-  const int prev = a.opnd_rows ? b * a.gamma + a.k - 1 : ptok;  // the W1 row
+  const int prev = kParts > 1 ? b * a.gamma + a.k - 1 : ptok;  // the W1 row
   if (ptok < 0 || ptok >= a.V) {  // invalid anchor or earlier position: propagate
     if (tid == 0) {
       a.tokens[out] = -1;
@@ -140,7 +138,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int j = tid + q * kSelThreads;
-      const float v = opnd_at<kBf16>(a, prev, j < a.r ? j : 0);  // clamped: no branch
+      const float v = opnd_at<kBf16, kParts>(a, prev, j < a.r ? j : 0);  // clamped: no branch
       w1v[q] = j < a.r ? v : 0.0f;
     }
     float lm = -__builtin_inff();
@@ -278,7 +276,7 @@ constexpr int kMaxRQuarter = 512 / 4;             // k per wave (r <= 512)
 // kWavePer: summaries per lane, the smallest instantiated count that covers
 // the row (the searches are unrolled over it, and they sit on the critical
 // path of every position).
-template <bool kBf16, int kWavePer>
+template <bool kBf16, int kWavePer, int kParts = 1>
 __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectArgs a) {
   __shared__ float sbias[4][kTileCols];
   const int b = blockIdx.x;
@@ -300,7 +298,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
     pr[j] = P[t < t1 ? t : (t1 > 0 ? t1 - 1 : 0)];
   }
   const int ptok = a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2];
-  const int prev = a.opnd_rows ? b * a.gamma + a.k - 1 : ptok;  // the W1 row
+  const int prev = kParts > 1 ? b * a.gamma + a.k - 1 : ptok;  // the W1 row
   const uint64_t seed = a.seeds[b];
   const double u_pre = a.k == 1 ? 0.0 : a.u_next[(size_t)((a.k - 1) & 1) * a.B + b];
   if (ptok < 0 || ptok >= a.V) {  // invalid anchor or earlier position: propagate
@@ -388,7 +386,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
     float w[16][8];
     // clamped k: every load of the chunk is issued before the first use
 #pragma unroll
-    for (int i = 0; i < 16; ++i) e[i] = opnd_at<kBf16>(a, prev, wave * kq + kr + 4 * min(i0 + i, nk - 1));
+    for (int i = 0; i < 16; ++i) e[i] = opnd_at<kBf16, kParts>(a, prev, wave * kq + kr + 4 * min(i0 + i, nk - 1));
     if (kBf16 && vec) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -478,19 +476,19 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
   store_ring_operand<kBf16>(a, b, lane_i32(mytok, own2), lane);
 }
 
-template <bool kBf16>
+template <bool kBf16, int kParts = 1>
 static hipError_t launch_select_wave(const SelectArgs& sa, hipStream_t s) {
   const int per = (sa.ntiles + kWave - 1) / kWave;
   ProfScope prof(s, kProfDraftSelect);
   if (per <= 8) {
-    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 8>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 8, kParts>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
   } else if (per <= 16) {
-    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 16>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 16, kParts>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
   } else if (per <= 20) {
-    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 20>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 20, kParts>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
   } else {
     static_assert(kWaveTiles == 32 * kWave, "largest instantiation covers kWaveTiles");
-    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 32>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
+    hipLaunchKernelGGL((draft_select_wave_kernel<kBf16, 32, kParts>), dim3(sa.B), dim3(kSelThreads), 0, s, sa);
   }
   return hipGetLastError();
 }
@@ -502,10 +500,10 @@ size_t draft_workspace(int B, int gamma, int V, int r) {
          (r == 256 ? align256(ring_operand_bytes(B)) : 0);
 }
 
-template <bool kGreedy, bool kBf16>
+template <bool kGreedy, bool kBf16, int kParts = 1>
 static hipError_t launch_select(const SelectArgs& s, hipStream_t st) {
   ProfScope prof(st, kProfDraftSelect);
-  hipLaunchKernelGGL((draft_select_kernel<kGreedy, kBf16>), dim3(s.B), dim3(kSelThreads), 0, st, s);
+  hipLaunchKernelGGL((draft_select_kernel<kGreedy, kBf16, kParts>), dim3(s.B), dim3(kSelThreads), 0, st, s);
   return hipGetLastError();
 }
 
@@ -820,7 +818,6 @@ hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
   sa.prob = a.prob;
   sa.lse = a.lse;
   sa.u_next = u_next;
-  sa.opnd_rows = 2;
 
   const int mode = greedy ? kModeGreedy : kModeSample;
   for (int k = 1; k <= a.gamma; ++k) {
@@ -836,11 +833,11 @@ hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     sa.k = k;
     if (greedy) {
-      e = launch_select<true, true>(sa, s);
+      e = launch_select<true, true, 2>(sa, s);
     } else if (ntiles <= kWaveTiles) {
-      e = launch_select_wave<true>(sa, s);
+      e = launch_select_wave<true, 2>(sa, s);
     } else {
-      e = launch_select<false, true>(sa, s);
+      e = launch_select<false, true, 2>(sa, s);
     }
     if (e != hipSuccess) return e;
   }
