@@ -95,6 +95,14 @@ def test_full_size_sampled_rnn_parity():
     torch.cuda.empty_cache()
 
 
+def test_full_size_sampled_rnn_parity_greedy():
+    """V = 151936, B = 512, gamma = 7, r = 256, T = 0 (argmax summaries on
+    the two-part pipelined tile kernel)."""
+    wl = workloads.make("greedy_v151936_b512")
+    run_rnn(wl, [0, 300, 511], "greedy_v151936_b512", seed=1)
+    torch.cuda.empty_cache()
+
+
 def test_invalid_anchor_is_reported_per_request():
     wl = workloads.make("v151936_b32", V=1001, B=6, gamma=3, r=32)
     wl.x0[1] = -1
