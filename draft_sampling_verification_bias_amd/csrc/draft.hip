@@ -610,7 +610,11 @@ struct CellArgs {
   int B, gamma, V, r, k, nreq, jn;
 };
 
-constexpr int kCellThreads = 256;
+// The cell's workgroup: two halves of kCellHalf threads.  Half h sums the
+// columns [h r, h r + r) of z (h = 0: the state, h = 1: the token row), so
+// every (request, unit) has two threads; the halves' sums meet in LDS.
+constexpr int kCellHalf = 256;
+constexpr int kCellThreads = 2 * kCellHalf;
 
 __device__ __forceinline__ uint16_t bf16_round(float f) {
   const uint32_t u = __float_as_uint(f);  // finite here: |e| <= 1
@@ -619,38 +623,41 @@ __device__ __forceinline__ uint16_t bf16_round(float f) {
 
 template <bool kBf16>
 __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
-  // LDS: z of the group [nreq][2r], then one chunk of the workgroup's 3 jn
-  // rows of Wp, [3 jn][chunk + 1] (the odd pitch puts the rows a wave reads
-  // in different banks).
+  // LDS: z of the group [nreq][2r], then per half one chunk of the
+  // workgroup's 3 jn rows of Wp, [3 jn][chunk + 1] (the odd pitch puts the
+  // rows a wave reads in different banks).
   extern __shared__ float zs[];
   const int r = a.r, r2 = 2 * a.r;
-  const int jn = a.jn, chunk = kCellThreads * 8 / jn, pitch = chunk + 1;
-  float* sw = zs + (size_t)a.nreq * r2;
+  const int half = threadIdx.x / kCellHalf, t = threadIdx.x - half * kCellHalf;
+  const int jn = a.jn, chunk = kCellHalf * 4 / jn, pitch = chunk + 1;
+  float* sw = zs + (size_t)a.nreq * r2 + (size_t)half * 3 * jn * pitch;
   const int b0 = blockIdx.x * a.nreq;
   const int j0 = blockIdx.y * jn;
   const float* sprev = a.state + (size_t)((a.k - 1) & 1) * a.B * r;
   float* snext = a.state + (size_t)(a.k & 1) * a.B * r;
 
-  // Wp chunk loads: 3 jn rows x chunk columns = 6 float4 per thread,
-  // consecutive threads along a row (chunk * 4 contiguous bytes per row).
-  constexpr int kLoads = 6;
+  // Wp chunk loads of this half: 3 jn rows x chunk columns = 3 float4 per
+  // thread, consecutive threads along a row.
+  constexpr int kLoads = 3;
   const int q4 = chunk / 4;
+  const int cbase = half * r;
   float4 wv[kLoads];
   auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
-      const int idx = l * kCellThreads + threadIdx.x;
+      const int idx = l * kCellHalf + t;
       const int lr = idx / q4, cq = idx - (idx / q4) * q4;     // local row 0 .. 3 jn - 1
       const int g = lr / jn, jj = lr - (lr / jn) * jn;
       const int j = min(j0 + jj, r - 1);                         // rows past r: clamped, unused
-      wv[l] = c0 + 4 * cq < r2 ? *reinterpret_cast<const float4*>(a.Wp + (size_t)(g * r + j) * r2 + c0 + 4 * cq)
-                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);  // past the row (2r % chunk != 0)
+      wv[l] = c0 + 4 * cq < r
+                  ? *reinterpret_cast<const float4*>(a.Wp + (size_t)(g * r + j) * r2 + cbase + c0 + 4 * cq)
+                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);       // past the half (r % chunk != 0)
     }
   };
   auto store_chunk = [&]() {
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
-      const int idx = l * kCellThreads + threadIdx.x;
+      const int idx = l * kCellHalf + t;
       const int lr = idx / q4, cq = idx - (idx / q4) * q4;
       float* d = sw + (size_t)lr * pitch + 4 * cq;
       d[0] = wv[l].x;
@@ -659,16 +666,17 @@ __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
       d[3] = wv[l].w;
     }
   };
+
   __shared__ int sx[8];  // x_{k-1} of each request of the group
   if (threadIdx.x < a.nreq) {
     const int b = b0 + threadIdx.x;
     sx[threadIdx.x] = b >= a.B ? -1 : (a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2]);
   }
   load_chunk(0);
-  const int i = threadIdx.x / jn, jj = threadIdx.x - (threadIdx.x / jn) * jn;
+  const int i = t / jn, jj = t - (t / jn) * jn;
   const int j = j0 + jj;
   const int b = b0 + i;
-  const bool mine = b < a.B && j < r;
+  const bool mine = half == 0 && b < a.B && j < r;
   const size_t row = (size_t)b * a.gamma + a.k - 1;
   float hv[3] = {0.0f, 0.0f, 0.0f};
   if (mine) {
@@ -680,13 +688,13 @@ __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
   __syncthreads();
 
   // z = [s_{k-1}; W1[x_{k-1}]]: every load issued before the first LDS store
-  // (nreq * 2r <= 4096, so at most 16 values per thread).
-  constexpr int kZ = 16;
+  // (nreq * 2r <= 4096, so at most 8 values per thread).
+  constexpr int kZ = 8;
   const int nz = a.nreq * r2;
   float zv[kZ];
 #pragma unroll
-  for (int t = 0; t < kZ; ++t) {
-    const int idx = t * kCellThreads + threadIdx.x;
+  for (int q = 0; q < kZ; ++q) {
+    const int idx = q * kCellThreads + threadIdx.x;
     const int zi = idx / r2, zc = idx - (idx / r2) * r2, zb = b0 + zi;
     float v = 0.0f;
     if (idx < nz && zb < a.B) {
@@ -697,26 +705,26 @@ __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
         if ((unsigned)x < (unsigned)a.V) v = w1_at<kBf16>(a.W1, (size_t)x * r + (zc - r));
       }
     }
-    zv[t] = v;
+    zv[q] = v;
   }
 #pragma unroll
-  for (int t = 0; t < kZ; ++t) {
-    const int idx = t * kCellThreads + threadIdx.x;
-    if (idx < nz) zs[idx] = zv[t];
+  for (int q = 0; q < kZ; ++q) {
+    const int idx = q * kCellThreads + threadIdx.x;
+    if (idx < nz) zs[idx] = zv[q];
   }
 
-  const float* z = zs + (size_t)i * r2;
+  const float* z = zs + (size_t)i * r2 + cbase;
   const float* wg = sw + (size_t)jj * pitch;
   const float* wc = sw + (size_t)(jn + jj) * pitch;
   const float* wo = sw + (size_t)(2 * jn + jj) * pitch;
   // two partial sums per projection (even and odd columns): shorter chains
   float g = 0.0f, c = 0.0f, o = 0.0f, g2 = 0.0f, c2 = 0.0f, o2 = 0.0f;
-  for (int c0 = 0; c0 < r2; c0 += chunk) {
+  for (int c0 = 0; c0 < r; c0 += chunk) {
     __syncthreads();  // the previous chunk is consumed (first pass: z is staged)
     store_chunk();
     __syncthreads();
-    if (c0 + chunk < r2) load_chunk(c0 + chunk);  // in flight during the products
-    const int cn = min(chunk, r2 - c0);  // even: 2r % 32 == 0
+    if (c0 + chunk < r) load_chunk(c0 + chunk);  // in flight during the products
+    const int cn = min(chunk, r - c0);  // even: r % 16 == 0
 #pragma unroll 4
     for (int q = 0; q < cn; q += 2) {
       const float za = z[c0 + q], zb = z[c0 + q + 1];
@@ -728,13 +736,25 @@ __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
       o2 = fmaf(wo[q + 1], zb, o2);
     }
   }
+  g += g2;
+  c += c2;
+  o += o2;
 
+  // the token half's sums to the state half (the Wp stages are free now)
+  __syncthreads();
+  float* xch = zs + (size_t)a.nreq * r2;  // [3][kCellHalf]
+  if (half == 1) {
+    xch[t] = g;
+    xch[kCellHalf + t] = c;
+    xch[2 * kCellHalf + t] = o;
+  }
+  __syncthreads();
   if (!mine) return;
-  g += g2 + hv[0];
-  c += c2 + hv[1];
-  o += o2 + hv[2];
+  g += xch[t] + hv[0];
+  c += xch[kCellHalf + t] + hv[1];
+  o += xch[2 * kCellHalf + t] + hv[2];
   const float sg = 1.0f / (1.0f + expf(-g));
-  snext[(size_t)b * r + j] = sg * z[j] + (1.0f - sg) * tanhf(c);
+  snext[(size_t)b * r + j] = sg * zs[(size_t)i * r2 + j] + (1.0f - sg) * tanhf(c);
   const float e = tanhf(o);
   const uint16_t hi = bf16_round(e);
   const uint16_t lo = bf16_round(e - bf16_to_float(hi));
@@ -777,10 +797,10 @@ hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
   ca.V = a.V;
   ca.r = a.r;
   ca.nreq = a.r <= 256 ? 8 : 4;          // z of the group: at most 16 KB of LDS
-  ca.jn = kCellThreads / ca.nreq;
+  ca.jn = kCellHalf / ca.nreq;
   const dim3 cgrid((a.B + ca.nreq - 1) / ca.nreq, (a.r + ca.jn - 1) / ca.jn);
-  const int chunk = kCellThreads * 8 / ca.jn;  // Wp columns per LDS stage: 6 float4 loads per thread
-  const size_t clds = ((size_t)ca.nreq * 2 * a.r + (size_t)3 * ca.jn * (chunk + 1)) * sizeof(float);
+  const int chunk = kCellHalf * 4 / ca.jn;  // Wp columns per LDS stage: 3 float4 loads per thread
+  const size_t clds = ((size_t)ca.nreq * 2 * a.r + (size_t)2 * 3 * ca.jn * (chunk + 1)) * sizeof(float);
 
   TileArgs t = {};
   t.U = a.U;
