@@ -70,7 +70,7 @@ SMALL = [
     # r = 512: four requests per cell workgroup, 64 state units each
     ("v151936_b32", dict(V=130, B=3, gamma=2, r=512)),
     ("v151936_b32", dict(V=5, B=2, gamma=3, r=16)),
-    # 2r not a multiple of the cell's 64-column Wp stage: a ragged last stage
+    # r not a multiple of the cell's 32-column Wp stage: a ragged last stage
     ("v151936_b32", dict(V=777, B=11, gamma=3, r=48)),
     # many full tiles and a ragged one under the generic tile kernel, several
     # row groups, a ragged request group of the cell
