@@ -589,8 +589,9 @@ hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s) {
 //
 // One cell launch per position: workgroup (request group, slice of jn state
 // units) stages z = [s_{k-1}; W1[x_{k-1}]] of its requests in LDS and streams
-// its rows of Wp through LDS in column chunks; each thread forms the three
-// projections of one (request, unit).  The cell computes in float32, the
+// its rows of Wp through LDS in column chunks; two threads (one per half of
+// the columns of z) form the three projections of one (request, unit).  The
+// cell computes in float32, the
 // precision of its inputs Wp and hp.  e_k goes to the operand table as two
 // bf16 parts (hi = bf16(e), lo = bf16(e - hi)), so that the bf16 MFMA tile
 // pass multiplies W2 by hi + lo, which is e to about 2^-18 relative.  The
