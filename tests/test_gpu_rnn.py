@@ -103,6 +103,14 @@ def test_full_size_sampled_rnn_parity_greedy():
     torch.cuda.empty_cache()
 
 
+def test_full_size_sampled_rnn_parity_v262144():
+    """V = 262144 (2048 tiles, the wave-level selection's largest rows),
+    B = 128, gamma = 7, r = 256, T = 1."""
+    wl = workloads.make("v262144_b128")
+    run_rnn(wl, [0, 64, 127], "v262144_b128", seed=2)
+    torch.cuda.empty_cache()
+
+
 def test_invalid_anchor_is_reported_per_request():
     wl = workloads.make("v151936_b32", V=1001, B=6, gamma=3, r=32)
     wl.x0[1] = -1
