@@ -26,6 +26,7 @@ from .dspark_ref import (  # noqa: F401
     inverse_cdf,
     markov_bias,
     markov_draft,
+    residual_law,
     residual_sample,
     rnn_draft,
     round_to_bf16,

@@ -157,6 +157,16 @@ def markov_draft(U, W1, W2, x0, T, seeds, rnd, requests=None):
 # Verify: lossless rejection sampling
 # ----------------------------------------------------------------------------
 
+def residual_law(pt, pd):
+    """The resampling law at the first rejection, written out as [E] section 2
+    states it: norm(max(0, p_t - p_d)), the positive part of the difference
+    divided by its total.  When the difference has no positive mass (which a
+    rejection rules out in exact arithmetic) the law is p_t."""
+    res = np.maximum(0.0, np.asarray(pt, dtype=np.float64) - np.asarray(pd, dtype=np.float64))
+    mass = res.sum()
+    return res / mass if mass > 0 else np.asarray(pt, dtype=np.float64)
+
+
 def residual_sample(pt, pd, seed, rnd, j, max_proposals, dists):
     """Draw from norm(max(0, p_t - p_d)), the resampling law at the first
     rejection ([E] section 2).

@@ -93,13 +93,12 @@ def test_residual_inverse_cdf_when_no_proposals():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("max_prop", [0, 1, 16])
+@pytest.mark.parametrize("max_prop", [0, 1, 16, 64])
 def test_residual_law(max_prop):
     rng = np.random.default_rng(3)
     pt = rng.dirichlet(np.ones(6))
     pd = rng.dirichlet(np.ones(6))
-    res = np.maximum(0, pt - pd)
-    law = res / res.sum()
+    law = ref.residual_law(pt, pd)
     n = 12000
     counts = np.zeros(6)
     for rnd in range(n):
