@@ -6,7 +6,11 @@ step is one round of the gated path -- dspark_markov_draft followed by
 dspark_verify -- over one batch of the V=151936, r=256, gamma=7, B=256,
 T=0.7 synthetic workload (bf16 Markov weights, float32 logits), with the
 inputs resident in HBM.  The round counter changes every step, so the drafts
-and the accepted lengths change while the input bytes stay fixed.
+and the accepted lengths change while the input bytes stay fixed.  Each
+step runs after a 512 MiB write that evicts the memory-side cache (as the
+target's forward pass does between rounds) and is timed alone with HIP events
+on the launch stream; the value is the median step, with p10 and p90 beside
+it and the back-to-back warm-cache rate as an extra field.
 
 Printed (one JSON line): the metric, the fraction of the 8 TB/s HBM peak that
 the step's compulsory bytes reach, the roofline of the dominant kernel (the
@@ -86,17 +90,38 @@ def cpu_baseline(wl, nreq, nrounds):
         pool.map(_oracle_round, tasks, chunksize=1)
         t1 = time.perf_counter()
     secs = t1 - t0
+    visible, model = host_cpus()
     return {"value": len(tasks) * wl.gamma / secs, "unit": "positions/s", "cores": workers, "kind": "oracle",
+            "host_cores_visible": visible, "cpu_model": model,
             "sample": "draft+verify of requests 0..%d of %s over %d rounds (float64 numpy, %d worker processes x "
-                      "1 thread, %.1f s wall)" % (nreq - 1, wl.name, nrounds, workers, secs)}
+                      "1 thread on %d visible cores, %.1f s wall)" % (nreq - 1, wl.name, nrounds, workers, visible,
+                                                                      secs)}
+
+
+def host_cpus():
+    """Cores this process may run on, and the CPU model name."""
+    visible = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return visible, model
 
 
 # ---------------------------------------------------------------------------
-def tile_pass_bytes(B, V, r):
-    """Algorithmic bytes of one draft tile-pass launch: the U_k rows, the whole
-    of W2 once, the gathered W1 rows and the per-(row, tile) summaries."""
+def tile_pass_bytes(B, gamma, V, r):
+    """Algorithmic bytes of one draft tile-pass launch (one block position):
+    the U_k rows, the launch's share of W2 -- read once per round, so r V / gamma
+    of its 2-byte values per position -- the gathered W1 rows and the
+    per-(row, tile) summaries.  Re-reads of W2 at every position are not
+    algorithmic bytes."""
     ntiles = (V + TILE_COLS - 1) // TILE_COLS
-    return 4 * B * V + 2 * r * V + 2 * B * r + 8 * B * ntiles
+    return 4 * B * V + 2 * r * V / gamma + 2 * B * r + 8 * B * ntiles
 
 
 def step_bytes(B, gamma, V, r, accept_len):
@@ -131,7 +156,9 @@ def main():
     ap.add_argument("--cpu-rounds", type=int, default=6, help="rounds of those requests in the oracle baseline")
     ap.add_argument("--survival-steps", type=int, default=10)
     ap.add_argument("--flush-mb", type=int, default=512,
-                    help="cold-cache figure: write this many MiB before each of K separately timed steps (0: skip)")
+                    help="MiB written before every step to evict the memory-side cache (0: no eviction)")
+    ap.add_argument("--warm-steps", type=int, default=20,
+                    help="extra back-to-back steps without eviction, reported as 'warm' (0: skip)")
     ap.add_argument("--schedule-steps", type=int, default=20,
                     help="timed calls of the prefix scheduler and of verification with its lengths (0: skip)")
     ap.add_argument("--rnn-steps", type=int, default=10,
@@ -199,72 +226,80 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Every step runs after a write of flush_mb MiB that evicts the 256 MB
+    # memory-side cache, as the target model's forward pass does between
+    # rounds in real use; the write is outside the step's timed interval (HIP
+    # events on the launch stream around the step alone).
+    scratch = torch.empty(args.flush_mb << 18, dtype=torch.float32, device=dev) if args.flush_mb > 0 else None
+
+    def run_steps(n, rnd0):
+        ev = []
+        for i in range(n):
+            if scratch is not None:
+                scratch.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(i, rnd0 + i)
+            e1.record(stream)
+            ev.append((e0, e1))
+        return ev
+
     log("warmup %d steps" % args.warmup)
-    for i in range(args.warmup):
-        step(i, i)
+    run_steps(args.warmup, 0)
     torch.cuda.synchronize()
 
     log("timing %d steps" % nsteps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(nsteps):
-        step(i, 1000 + i)
+    events = run_steps(nsteps, 1000)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    times = np.array([a.elapsed_time(b) for a, b in events])
+    med = float(np.median(times))
 
     # The same steps again with a HIP event pair around every kernel launch
-    # (on the launch stream) for the per-kernel durations.
+    # (recorded by the library on the launch stream) for the per-kernel
+    # durations.
     log("timing %d steps with per-kernel events" % nsteps)
     dsp.profile_enable(True)
     torch.cuda.synchronize()
     p0 = time.perf_counter()
-    for i in range(nsteps):
-        step(i, 1000 + i)
+    run_steps(nsteps, 1000)
     torch.cuda.synchronize()
     p1 = time.perf_counter()
     prof = dsp.profile_read()
     dsp.profile_enable(False)
 
-    # Cold caches: before each step a write of flush_mb MiB evicts the 256 MB
-    # memory-side cache, as the target model's forward pass does between
-    # rounds.  Each step is timed alone with events on the launch stream; the
-    # flush is outside the timed interval.
-    cold = None
-    if args.flush_mb > 0:
-        scratch = torch.empty(args.flush_mb << 18, dtype=torch.float32, device=dev)
-        times = []
-        for i in range(nsteps):
-            scratch.fill_(float(i))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+    # Back to back without the cache-evicting writes (warm memory-side cache).
+    warm = None
+    if args.warm_steps > 0:
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for i in range(args.warm_steps):
             step(i, 1000 + i)
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1))
-        del scratch
-        med = float(np.median(times))
-        cold = {"flush_mib": args.flush_mb, "ms_per_step_median": med,
-                "ms_per_step_p10": float(np.percentile(times, 10)), "ms_per_step_p90": float(np.percentile(times, 90)),
-                "value": B * gamma / (med * 1e-3)}
+        torch.cuda.synchronize()
+        wms = (time.perf_counter() - w0) / args.warm_steps * 1e3
+        warm = {"ms_per_step": wms, "value": B * gamma / (wms * 1e-3), "steps": args.warm_steps}
+    del scratch
 
-    secs = t1 - t0
-    ms_per_step = secs / nsteps * 1e3
     lens = np.stack([vouts[i][0].cpu().numpy() for i in range(nsteps)])
     bytes_steps = [step_bytes(B, gamma, V, r, lens[i]) for i in range(nsteps)]
     mean_bytes = float(np.mean(bytes_steps))
-    hbm_frac = mean_bytes / (secs / nsteps) / HBM_PEAK
-    accepted = float((lens + 1).sum()) / secs
+    hbm_frac = mean_bytes / (med * 1e-3) / HBM_PEAK
+    accepted = float((lens + 1).mean()) / (med * 1e-3)
 
     # dominant kernel: the draft tile pass (sample mode at T > 0, argmax mode at T = 0)
     kname = "tile_pass_sample" if T > 0 else "tile_pass_greedy"
     launches, kms = prof.get(kname, (0, 0.0))
     k_avg_s = kms / max(launches, 1) / 1e3
-    k_bytes = tile_pass_bytes(B, V, r)
+    k_bytes = tile_pass_bytes(B, gamma, V, r)
     achieved = k_bytes / k_avg_s if k_avg_s > 0 else 0.0
     traffic = pmc_traffic()
     roofline = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": kname,
-                "avg_launch_us": k_avg_s * 1e6, "bytes_per_launch": k_bytes}
+                "avg_launch_us": k_avg_s * 1e6, "bytes_per_launch": k_bytes,
+                "bytes_per_launch_w2_every_launch": k_bytes + 2 * r * V * (1 - 1 / gamma),
+                "traffic_over_bytes": (traffic / k_bytes) if traffic else None}
     kernels = {k: {"launches": n, "avg_us": ms / n * 1e3, "ms_per_step": ms / nsteps} for k, (n, ms) in prof.items()}
 
     # survival (analytical), timed beside the gated path
@@ -384,12 +419,16 @@ def main():
     flops = 2.0 * r * V * (B * gamma + float((lens < gamma).sum()) / nsteps)
     out = {
         "metric": METRIC,
-        "value": B * gamma * nsteps / secs,
+        "value": B * gamma / (med * 1e-3),
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": nsteps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": med,
+        "ms_per_step_p10": float(np.percentile(times, 10)),
+        "ms_per_step_p90": float(np.percentile(times, 90)),
+        "timing": "median over the timed steps, each after a %d MiB cache-evicting write (HIP events on the launch "
+                  "stream around the step)" % args.flush_mb,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -399,13 +438,14 @@ def main():
                    "weights": wl.wdtype, "logits": "f32"},
         "hbm_fraction": hbm_frac,
         "bytes_per_step": mean_bytes,
-        "mfma_fraction": flops / (secs / nsteps) / MFMA_BF16_PEAK,
+        "mfma_fraction": flops / (med * 1e-3) / MFMA_BF16_PEAK,
         "accepted_tokens_per_s": accepted,
         "mean_accept_len": float(lens.mean()),
         "roofline": roofline,
         "kernels": kernels,
-        "ms_per_step_with_events": (p1 - p0) / nsteps * 1e3,
-        "cold_cache": cold,
+        "wall_ms_per_step_with_flush": (t1 - t0) / nsteps * 1e3,
+        "wall_ms_per_step_with_events": (p1 - p0) / nsteps * 1e3,
+        "warm": warm,
         "survival_ms": surv_ms,
         "schedule": sched,
         "rnn_draft": rnn,
