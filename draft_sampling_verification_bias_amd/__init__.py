@@ -18,7 +18,7 @@ __all__ = [
     "DsparkError", "OP_DRAFT", "OP_VERIFY", "OP_SURVIVAL", "OP_RNN_DRAFT", "MAX_RESIDUAL_PROPOSALS",
     "SCHEDULE_EARLY_STOP", "SCHEDULE_CAPACITY", "SCHEDULE_TOP_K",
     "library_path", "load", "version", "workspace_size", "markov_bias",
-    "markov_draft", "rnn_draft", "verify", "transpose_w2", "survival", "confidence", "schedule", "profile_enable",
+    "markov_draft", "markov_draft_noalloc", "static_scratch_bytes", "rnn_draft", "verify", "transpose_w2", "survival", "confidence", "schedule", "profile_enable",
     "profile_read",
 ]
 
@@ -62,6 +62,10 @@ def load():
     lib.dspark_markov_bias.argtypes = [P, P, I, P, I, I, I, P, P]
     lib.dspark_markov_draft.restype = I
     lib.dspark_markov_draft.argtypes = [P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_markov_draft_noalloc.restype = I
+    lib.dspark_markov_draft_noalloc.argtypes = [P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P]
+    lib.dspark_static_scratch_bytes.restype = SZ
+    lib.dspark_static_scratch_bytes.argtypes = []
     lib.dspark_rnn_draft.restype = I
     lib.dspark_rnn_draft.argtypes = [P, P, P, I, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, P, SZ, P]
     lib.dspark_verify.restype = I
@@ -199,6 +203,38 @@ def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=Non
                                     _p(ws), nbytes, _stream(stream, dev))
     _check("dspark_markov_draft", st)
     return tok, prob, lse
+
+
+def markov_draft_noalloc(U, W1, W2, x0, temperature, seeds, rnd, out=None, stream=None):
+    """markov_draft with the library's static scratch array instead of a
+    workspace (dspark_markov_draft_noalloc).  Returns (draft_tokens,
+    draft_prob, draft_lse); pass ``out`` to allocate nothing here either."""
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    _dev(U, "U", torch.float32)
+    _dev(W1, "W1", None, (V, r))
+    _dev(W2, "W2", W1.dtype, (r, V))
+    _dev(x0, "x0", torch.int32, (B,))
+    if seeds is not None:
+        _dev(seeds, "seeds", torch.uint64, (B,))
+    if out is None:
+        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    tok, prob, lse = out
+    _dev(tok, "draft_tokens", torch.int32, (B, gamma))
+    _dev(prob, "draft_prob", torch.float32, (B, gamma))
+    _dev(lse, "draft_lse", torch.float32, (B, gamma))
+    st = load().dspark_markov_draft_noalloc(_p(U), _p(W1), _p(W2), _wdtype(W1, W2), _p(x0), B, gamma, V, r,
+                                            float(temperature), _p(seeds), int(rnd), _p(tok), _p(prob), _p(lse),
+                                            _stream(stream, dev))
+    _check("dspark_markov_draft_noalloc", st)
+    return tok, prob, lse
+
+
+def static_scratch_bytes():
+    return int(load().dspark_static_scratch_bytes())
 
 
 def rnn_draft(U, W1, W2, Wp, hp, x0, temperature, seeds, rnd, out=None, with_e=False, workspace=None,

@@ -46,6 +46,7 @@ const char* dspark_status_string(dspark_status s) {
     case DSPARK_ERR_UNSUPPORTED: return "unsupported weight dtype";
     case DSPARK_ERR_WORKSPACE: return "workspace too small";
     case DSPARK_ERR_HIP: return "HIP launch error";
+    case DSPARK_ERR_SCRATCH_LIMIT: return "sizes exceed the static scratch array of the allocation-free entry point";
     default: return "unknown status";
   }
 }
@@ -98,6 +99,41 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
   a.ws = workspace;
   return from_hip(launch_draft(a, wdtype == DSPARK_BF16, stream));
 }
+
+dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
+                                          const int32_t* x0, int B, int gamma, int V, int r, float temperature,
+                                          const uint64_t* seeds, uint64_t round, int32_t* draft_tokens,
+                                          float* draft_prob, float* draft_lse, hipStream_t stream) {
+  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(x0, 4) || !req(draft_tokens, 4) ||
+      !req(draft_prob, 4) || !req(draft_lse, 4))
+    return DSPARK_ERR_INVALID_ARGUMENT;
+  if (temperature > 0.0f && !req(seeds, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
+  if (draft_workspace(B, gamma, V, r) > static_scratch_bytes()) return DSPARK_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (static_scratch(&ws) != hipSuccess) return DSPARK_ERR_HIP;
+  ProfSuppress quiet;
+  DraftArgs a = {};
+  a.U = U;
+  a.W1 = W1;
+  a.W2 = W2;
+  a.x0 = x0;
+  a.seeds = seeds;
+  a.round = round;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.r = r;
+  a.temperature = temperature;
+  a.tokens = draft_tokens;
+  a.prob = draft_prob;
+  a.lse = draft_lse;
+  a.ws = ws;
+  return from_hip(launch_draft(a, wdtype == DSPARK_BF16, stream));
+}
+
+size_t dspark_static_scratch_bytes(void) { return static_scratch_bytes(); }
 
 dspark_status dspark_rnn_draft(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
                                const float* Wp, const float* hp, const int32_t* x0, int B, int gamma, int V, int r,

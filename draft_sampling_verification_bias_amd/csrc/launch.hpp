@@ -231,6 +231,21 @@ class ProfScope {
   int index_;
 };
 
+// While one exists on the calling thread, ProfScope records nothing (no
+// events are created or recorded): used by the allocation-free entry point.
+class ProfSuppress {
+ public:
+  ProfSuppress();
+  ~ProfSuppress();
+  ProfSuppress(const ProfSuppress&) = delete;
+  ProfSuppress& operator=(const ProfSuppress&) = delete;
+};
+
+// The library's static device scratch array (noalloc.hip): its size, and its
+// address on the current device (looked up once per device).
+size_t static_scratch_bytes();
+hipError_t static_scratch(void** ptr);
+
 // Round a byte count up to a 256-byte boundary (workspace carving).
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -39,7 +39,13 @@ hipEvent_t take_event() {
 
 }  // namespace
 
+thread_local int g_suppress = 0;
+
+ProfSuppress::ProfSuppress() { ++g_suppress; }
+ProfSuppress::~ProfSuppress() { --g_suppress; }
+
 ProfScope::ProfScope(hipStream_t s, int kind) : stream_(s), index_(-1) {
+  if (g_suppress) return;
   std::lock_guard<std::mutex> lock(g_mu);
   if (!g_on) return;
   hipEvent_t a = take_event(), b = take_event();

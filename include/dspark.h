@@ -25,7 +25,8 @@
  * memory, aligned to 16 bytes, owned by the caller.  The library allocates
  * nothing and keeps no state between calls; scratch memory is the caller's
  * `workspace` of at least dspark_workspace_size(op, ...) bytes, which must not
- * be shared by calls that may run concurrently.
+ * be shared by calls that may run concurrently.  The one exception is
+ * dspark_markov_draft_noalloc, whose scratch is a static device array.
  *
  * Layouts.
  *   U       float32 [B][gamma][V]      base logits U_k of the parallel backbone
@@ -80,7 +81,8 @@ typedef enum {
   DSPARK_ERR_INVALID_ARGUMENT = -1,
   DSPARK_ERR_UNSUPPORTED = -2,
   DSPARK_ERR_WORKSPACE = -3,
-  DSPARK_ERR_HIP = -4
+  DSPARK_ERR_HIP = -4,
+  DSPARK_ERR_SCRATCH_LIMIT = -5
 } dspark_status;
 
 /* Storage type of W1 and W2. */
@@ -152,6 +154,33 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
                                   const uint64_t* seeds, uint64_t round,
                                   int32_t* draft_tokens, float* draft_prob, float* draft_lse,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_markov_draft_noalloc -- dspark_markov_draft without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, outputs and results are exactly those of dspark_markov_draft
+ * (the same kernels run).  Its scratch memory is a static device array of
+ * dspark_static_scratch_bytes() bytes (16 MiB) inside the library, one per
+ * GPU, held until the process ends; the call allocates nothing (no hipMalloc,
+ * hipFree or allocating routine; the per-kernel event timing records nothing
+ * for it).  Sizes whose dspark_workspace_size(DSPARK_OP_DRAFT, ...) exceeds
+ * that array return DSPARK_ERR_SCRATCH_LIMIT before any HIP call.  Every call
+ * on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race on it and must be serialised by the caller.
+ * The array is that of the device current at the call, which must be the
+ * device of `stream`.
+ */
+dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const void* W2,
+                                          dspark_dtype wdtype, const int32_t* x0,
+                                          int B, int gamma, int V, int r, float temperature,
+                                          const uint64_t* seeds, uint64_t round,
+                                          int32_t* draft_tokens, float* draft_prob, float* draft_lse,
+                                          hipStream_t stream);
+
+/* Bytes of the static scratch array of dspark_markov_draft_noalloc. */
+size_t dspark_static_scratch_bytes(void);
 
 /*
  * dspark_rnn_draft -- the same block sampling with the RNN head of [R]

@@ -14,7 +14,7 @@ dsp = pytest.importorskip("draft_sampling_verification_bias_amd")
 
 HEADER = os.path.join(ROOT, "include", "dspark.h")
 
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH = 0, -1, -2, -3, -4, -5
 FAKE = 0x100000          # non-null, 16-byte aligned, never dereferenced (validation fails first)
 MISALIGNED = 0x100004
 FAKE2 = 0x200000         # a second distinct fake pointer
@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dspark_markov_draft", "dspark_verify", "dspark_survival", "dspark_markov_bias", "dspark_schedule",
-              "dspark_confidence", "dspark_rnn_draft",
+              "dspark_confidence", "dspark_rnn_draft", "dspark_markov_draft_noalloc", "dspark_static_scratch_bytes",
               "dspark_workspace_size", "dspark_status_string", "dspark_version"):
         assert n in names
 
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.dspark_version() >= 100
-    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH):
         s = lib.dspark_status_string(code)
         assert s and len(s) > 1
     assert lib.dspark_status_string(123) == b"unknown status"
@@ -84,6 +84,34 @@ def _draft(lib, **kw):
 ])
 def test_draft_rejects_bad_arguments(lib, kw, status):
     assert _draft(lib, **kw) == status
+
+
+def _draft_noalloc(lib, **kw):
+    a = dict(U=FAKE, W1=FAKE, W2=FAKE, wd=1, x0=FAKE, B=4, gamma=4, V=1000, r=16, T=1.0, seeds=FAKE,
+             rnd=0, tok=FAKE, prob=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.dspark_markov_draft_noalloc(a["U"], a["W1"], a["W2"], a["wd"], a["x0"], a["B"], a["gamma"],
+                                           a["V"], a["r"], a["T"], a["seeds"], a["rnd"], a["tok"], a["prob"],
+                                           a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(gamma=33), INVALID), (dict(V=1), INVALID), (dict(r=40), INVALID),
+    (dict(T=-1.0), INVALID), (dict(U=None), INVALID), (dict(seeds=None), INVALID), (dict(U=MISALIGNED), INVALID),
+    (dict(wd=5), UNSUPPORTED),
+    # sizes whose draft workspace exceeds the static array: rejected on the host
+    (dict(B=4096, V=151936, r=256, gamma=7), SCRATCH), (dict(B=65536, V=8000, r=16), SCRATCH),
+])
+def test_draft_noalloc_rejects_bad_arguments_and_sizes_beyond_its_scratch(lib, kw, status):
+    assert _draft_noalloc(lib, **kw) == status
+
+
+def test_static_scratch_holds_the_timed_workloads(lib):
+    cap = lib.dspark_static_scratch_bytes()
+    assert cap == 16 << 20
+    for B, gamma, V in ((256, 7, 151936), (512, 7, 151936), (128, 7, 262144), (32, 7, 151936)):
+        assert 0 < dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, 256) <= cap
+    assert dsp.workspace_size(dsp.OP_DRAFT, 4096, 7, 151936, 256) > cap
 
 
 def _rnn_draft(lib, **kw):
