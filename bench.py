@@ -44,8 +44,10 @@ HBM_PEAK = 8.0e12            # bytes/s, MI355X published peak
 MFMA_BF16_PEAK = 2.5e15      # dense bf16 FLOP/s, MI355X published peak
 METRIC = "verified draft positions/sec, V=151936 γ=7 B=256; % of HBM roofline"
 TILE_COLS = 128              # vocabulary columns per tile of the tile pass
-PMC_FILE = os.path.join(ROOT, "profiles", "tile_pass_sample_v151936_b256_pmc.json")
-TILE_SRC = os.path.join(ROOT, "draft_sampling_verification_bias_amd", "csrc", "tile_pass.hip")
+PMC_FILES = {"tile_pass_sample": os.path.join(ROOT, "profiles", "tile_pass_sample_v151936_b256_pmc.json"),
+             "draft_resident": os.path.join(ROOT, "profiles", "draft_resident_v151936_b256_pmc.json")}
+KERNEL_SRC = {"tile_pass_sample": os.path.join(ROOT, "draft_sampling_verification_bias_amd", "csrc", "tile_pass.hip"),
+              "draft_resident": os.path.join(ROOT, "draft_sampling_verification_bias_amd", "csrc", "resident.hip")}
 
 
 def log(msg):
@@ -124,6 +126,13 @@ def tile_pass_bytes(B, gamma, V, r):
     return 4 * B * V + 2 * r * V / gamma + 2 * B * r + 8 * B * ntiles
 
 
+def resident_draft_bytes(B, gamma, V, r):
+    """Algorithmic bytes of one device-resident draft launch (all gamma
+    positions): every U row, W2 once (from its vocabulary-major copy), the W1
+    rows of the previous tokens and the three outputs."""
+    return 4 * B * gamma * V + 2 * r * V + 2 * r * B * gamma + 12 * B * gamma
+
+
 def step_bytes(B, gamma, V, r, accept_len):
     """Compulsory bytes of one round (draft + verify): all U rows, target rows
     1..n_b+1 of each request, W2 once, the W1 rows gathered by the draft and by
@@ -133,15 +142,16 @@ def step_bytes(B, gamma, V, r, accept_len):
     return 4 * B * gamma * V + 4 * V * int((n + 1).sum()) + 2 * r * V + 2 * r * (B * gamma + rej)
 
 
-def pmc_traffic():
-    """HBM bytes per tile-pass launch from the committed counter summary, or
+def pmc_traffic(kname):
+    """HBM bytes per launch of a kernel from its committed counter summary, or
     None if there is none or the kernel source changed since it was taken."""
-    if not os.path.exists(PMC_FILE):
+    path = PMC_FILES.get(kname)
+    if path is None or not os.path.exists(path):
         return None
-    with open(PMC_FILE) as f:
+    with open(path) as f:
         rec = json.load(f)
-    src = hashlib.sha256(open(TILE_SRC, "rb").read()).hexdigest()
-    if rec.get("tile_pass_sha256") != src:
+    src = hashlib.sha256(open(KERNEL_SRC[kname], "rb").read()).hexdigest()
+    if rec.get("source_sha256", rec.get("tile_pass_sha256")) != src:
         return None
     return rec.get("bytes_per_launch")
 
@@ -163,6 +173,9 @@ def main():
                     help="timed calls of the prefix scheduler and of verification with its lengths (0: skip)")
     ap.add_argument("--rnn-steps", type=int, default=10,
                     help="timed calls of the RNN-head draft beside the Markov draft (0: skip)")
+    ap.add_argument("--resident", action="store_true",
+                    help="draft with the W2T copy: all positions in one device-resident launch "
+                         "(default: one tile pass and one selection launch per position)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="copy this many MiB device to device once before timing (a reference kernel of known "
                          "traffic for hardware counter runs)")
@@ -201,6 +214,10 @@ def main():
     # The Markov projection is also held vocabulary-major: a constant weight
     # layout prepared once per model, outside the timed region.
     W2T = dsp.transpose_w2(W2) if T > 0 else None
+    # the draft uses the copy at every temperature (it holds W2 on chip from it)
+    W2T_d = dsp.transpose_w2(W2) if (W2T is None and wl.wdtype == "bf16") else W2T
+    if not args.resident:
+        W2T_d = None
 
     ws_d = torch.empty(dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, r), dtype=torch.uint8, device=dev)
     ws_v = torch.empty(dsp.workspace_size(dsp.OP_VERIFY, B, gamma, V, r), dtype=torch.uint8, device=dev)
@@ -215,7 +232,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(i, rnd):
-        dsp.markov_draft(U, W1, W2, x0, T, seeds, rnd, out=dout, workspace=ws_d, stream=stream)
+        dsp.markov_draft(U, W1, W2, x0, T, seeds, rnd, out=dout, workspace=ws_d, stream=stream, W2T=W2T_d)
         dsp.verify(U, W1, W2, x0, dout[0], dout[1], tgt, T, seeds, rnd, out=vouts[i % len(vouts)], W2T=W2T,
                    workspace=ws_v, stream=stream)
 
@@ -288,18 +305,25 @@ def main():
     hbm_frac = mean_bytes / (med * 1e-3) / HBM_PEAK
     accepted = float((lens + 1).mean()) / (med * 1e-3)
 
-    # dominant kernel: the draft tile pass (sample mode at T > 0, argmax mode at T = 0)
-    kname = "tile_pass_sample" if T > 0 else "tile_pass_greedy"
+    # dominant kernel: the device-resident draft (one launch per step) when it
+    # runs, else the per-position draft tile pass (sample mode at T > 0,
+    # argmax mode at T = 0)
+    if "draft_resident" in prof:
+        kname = "draft_resident"
+        k_bytes = resident_draft_bytes(B, gamma, V, r)
+    else:
+        kname = "tile_pass_sample" if T > 0 else "tile_pass_greedy"
+        k_bytes = tile_pass_bytes(B, gamma, V, r)
     launches, kms = prof.get(kname, (0, 0.0))
     k_avg_s = kms / max(launches, 1) / 1e3
-    k_bytes = tile_pass_bytes(B, gamma, V, r)
     achieved = k_bytes / k_avg_s if k_avg_s > 0 else 0.0
-    traffic = pmc_traffic()
+    traffic = pmc_traffic(kname)
     roofline = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": kname,
                 "avg_launch_us": k_avg_s * 1e6, "bytes_per_launch": k_bytes,
-                "bytes_per_launch_w2_every_launch": k_bytes + 2 * r * V * (1 - 1 / gamma),
                 "traffic_over_bytes": (traffic / k_bytes) if traffic else None}
+    if kname != "draft_resident":
+        roofline["bytes_per_launch_w2_every_launch"] = k_bytes + 2 * r * V * (1 - 1 / gamma)
     kernels = {k: {"launches": n, "avg_us": ms / n * 1e3, "ms_per_step": ms / nsteps} for k, (n, ms) in prof.items()}
 
     # survival (analytical), timed beside the gated path
@@ -363,7 +387,7 @@ def main():
         sch_len = vo[0].cpu().numpy()
 
         def round_scheduled(i):
-            dsp.markov_draft(U, W1, W2, x0, T, seeds, 3000 + i, out=dout, workspace=ws_d, stream=stream)
+            dsp.markov_draft(U, W1, W2, x0, T, seeds, 3000 + i, out=dout, workspace=ws_d, stream=stream, W2T=W2T_d)
             plan()
             verify_at(lengths, 3000 + i)
 
@@ -391,7 +415,7 @@ def main():
             dsp.rnn_draft(U, W1, W2, Wp_d, hp_d, x0, T, seeds, 4000 + i, out=rout, workspace=ws_r, stream=stream)
 
         def markov_step(i):
-            dsp.markov_draft(U, W1, W2, x0, T, seeds, 4000 + i, out=dout, workspace=ws_d, stream=stream)
+            dsp.markov_draft(U, W1, W2, x0, T, seeds, 4000 + i, out=dout, workspace=ws_d, stream=stream, W2T=W2T_d)
 
         def per_call_ms(fn):
             fn(0)

@@ -61,9 +61,9 @@ def load():
     lib.dspark_markov_bias.restype = I
     lib.dspark_markov_bias.argtypes = [P, P, I, P, I, I, I, P, P]
     lib.dspark_markov_draft.restype = I
-    lib.dspark_markov_draft.argtypes = [P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_markov_draft.argtypes = [P, P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
     lib.dspark_markov_draft_noalloc.restype = I
-    lib.dspark_markov_draft_noalloc.argtypes = [P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P]
+    lib.dspark_markov_draft_noalloc.argtypes = [P, P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P]
     lib.dspark_static_scratch_bytes.restype = SZ
     lib.dspark_static_scratch_bytes.argtypes = []
     lib.dspark_rnn_draft.restype = I
@@ -178,8 +178,10 @@ def markov_bias(W1, W2, tokens, out=None, stream=None):
     return out
 
 
-def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=None, stream=None):
-    """Draft gamma tokens per request.  Returns (draft_tokens, draft_prob, draft_lse)."""
+def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=None, stream=None, W2T=None):
+    """Draft gamma tokens per request.  Returns (draft_tokens, draft_prob, draft_lse).
+    W2T: optional transposed copy of W2 (transpose_w2), which lets the library
+    run all positions in one device-resident launch."""
     B, gamma, V = U.shape
     r = W1.shape[1]
     dev = U.device
@@ -198,14 +200,16 @@ def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=Non
     _dev(prob, "draft_prob", torch.float32, (B, gamma))
     _dev(lse, "draft_lse", torch.float32, (B, gamma))
     ws, nbytes = _workspace(OP_DRAFT, B, gamma, V, r, workspace, dev)
-    st = load().dspark_markov_draft(_p(U), _p(W1), _p(W2), _wdtype(W1, W2), _p(x0), B, gamma, V, r,
+    if W2T is not None:
+        _dev(W2T, "W2T", W2.dtype, (V, r))
+    st = load().dspark_markov_draft(_p(U), _p(W1), _p(W2), _p(W2T), _wdtype(W1, W2), _p(x0), B, gamma, V, r,
                                     float(temperature), _p(seeds), int(rnd), _p(tok), _p(prob), _p(lse),
                                     _p(ws), nbytes, _stream(stream, dev))
     _check("dspark_markov_draft", st)
     return tok, prob, lse
 
 
-def markov_draft_noalloc(U, W1, W2, x0, temperature, seeds, rnd, out=None, stream=None):
+def markov_draft_noalloc(U, W1, W2, x0, temperature, seeds, rnd, out=None, stream=None, W2T=None):
     """markov_draft with the library's static scratch array instead of a
     workspace (dspark_markov_draft_noalloc).  Returns (draft_tokens,
     draft_prob, draft_lse); pass ``out`` to allocate nothing here either."""
@@ -226,7 +230,9 @@ def markov_draft_noalloc(U, W1, W2, x0, temperature, seeds, rnd, out=None, strea
     _dev(tok, "draft_tokens", torch.int32, (B, gamma))
     _dev(prob, "draft_prob", torch.float32, (B, gamma))
     _dev(lse, "draft_lse", torch.float32, (B, gamma))
-    st = load().dspark_markov_draft_noalloc(_p(U), _p(W1), _p(W2), _wdtype(W1, W2), _p(x0), B, gamma, V, r,
+    if W2T is not None:
+        _dev(W2T, "W2T", W2.dtype, (V, r))
+    st = load().dspark_markov_draft_noalloc(_p(U), _p(W1), _p(W2), _p(W2T), _wdtype(W1, W2), _p(x0), B, gamma, V, r,
                                             float(temperature), _p(seeds), int(rnd), _p(tok), _p(prob), _p(lse),
                                             _stream(stream, dev))
     _check("dspark_markov_draft_noalloc", st)

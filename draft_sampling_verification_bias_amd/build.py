@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "profile.cpp", "noalloc.hip", "tile_pass.hip", "draft.hip", "verify.hip", "survival.hip", "weights.hip",
+SOURCES = ["api.cpp", "profile.cpp", "noalloc.hip", "tile_pass.hip", "draft.hip", "resident.hip", "verify.hip", "survival.hip", "weights.hip",
            "schedule.hip", "confidence.hip"]
 
 

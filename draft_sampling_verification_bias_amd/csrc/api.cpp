@@ -2,6 +2,7 @@
 // workspace sizing and dispatch to the kernel launchers.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "dspark.h"
 #include "launch.hpp"
@@ -29,7 +30,19 @@ bool req(const void* p, size_t a) { return p != nullptr && aligned(p, a); }
 // An optional pointer: null, or aligned.
 bool opt(const void* p, size_t a) { return p == nullptr || aligned(p, a); }
 
-bool dtype_ok(dspark_dtype d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
+// The integer a caller passed for an enum parameter.  A C caller may pass any
+// int there, and in C++ reading an enum object whose value lies outside the
+// range of its enumerators is undefined, so every enum argument is first
+// read through its bytes and range-checked as an int.
+template <class E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "the enums of the C ABI are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool dtype_ok(int d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
 
 dspark_status from_hip(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
 
@@ -39,8 +52,8 @@ extern "C" {
 
 int dspark_version(void) { return 100; }
 
-const char* dspark_status_string(dspark_status s) {
-  switch (s) {
+const char* dspark_status_string(dspark_status status) {
+  switch (enum_value(status)) {
     case DSPARK_OK: return "ok";
     case DSPARK_ERR_INVALID_ARGUMENT: return "invalid argument";
     case DSPARK_ERR_UNSUPPORTED: return "unsupported weight dtype";
@@ -51,9 +64,9 @@ const char* dspark_status_string(dspark_status s) {
   }
 }
 
-size_t dspark_workspace_size(dspark_op op, int B, int gamma, int V, int r) {
+size_t dspark_workspace_size(dspark_op op_arg, int B, int gamma, int V, int r) {
   if (!sizes_ok(B, gamma, V, r)) return 0;
-  switch (op) {
+  switch (enum_value(op_arg)) {
     case DSPARK_OP_DRAFT: return draft_workspace(B, gamma, V, r);
     case DSPARK_OP_VERIFY: return verify_workspace(B, gamma, V, r);
     case DSPARK_OP_SURVIVAL: return survival_workspace(B, gamma, V, r);
@@ -64,20 +77,21 @@ size_t dspark_workspace_size(dspark_op op, int B, int gamma, int V, int r) {
 
 dspark_status dspark_markov_bias(const void* W1, const void* W2, dspark_dtype wdtype, const int32_t* tokens,
                                  int n, int V, int r, float* out, hipStream_t stream) {
-  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(1, 1, V, r) || n < 1 || n > (1 << 20)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (!req(W1, 16) || !req(W2, 16) || !req(tokens, 4) || !req(out, 4)) return DSPARK_ERR_INVALID_ARGUMENT;
   return from_hip(launch_markov_bias(W1, W2, wdtype == DSPARK_BF16, tokens, n, V, r, out, stream));
 }
 
-dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
-                                  const int32_t* x0, int B, int gamma, int V, int r, float temperature,
+dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2, const void* W2T,
+                                  dspark_dtype wdtype, const int32_t* x0, int B, int gamma, int V, int r,
+                                  float temperature,
                                   const uint64_t* seeds, uint64_t round, int32_t* draft_tokens, float* draft_prob,
                                   float* draft_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
-  if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(x0, 4) || !req(draft_tokens, 4) ||
-      !req(draft_prob, 4) || !req(draft_lse, 4) || !req(workspace, 16))
+  if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !opt(W2T, 16) || W2T == W2 || !req(x0, 4) ||
+      !req(draft_tokens, 4) || !req(draft_prob, 4) || !req(draft_lse, 4) || !req(workspace, 16))
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (temperature > 0.0f && !req(seeds, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < draft_workspace(B, gamma, V, r)) return DSPARK_ERR_WORKSPACE;
@@ -85,6 +99,7 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
   a.U = U;
   a.W1 = W1;
   a.W2 = W2;
+  a.W2T = W2T;
   a.x0 = x0;
   a.seeds = seeds;
   a.round = round;
@@ -100,14 +115,15 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
   return from_hip(launch_draft(a, wdtype == DSPARK_BF16, stream));
 }
 
-dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
-                                          const int32_t* x0, int B, int gamma, int V, int r, float temperature,
+dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const void* W2, const void* W2T,
+                                          dspark_dtype wdtype, const int32_t* x0, int B, int gamma, int V, int r,
+                                          float temperature,
                                           const uint64_t* seeds, uint64_t round, int32_t* draft_tokens,
                                           float* draft_prob, float* draft_lse, hipStream_t stream) {
-  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
-  if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(x0, 4) || !req(draft_tokens, 4) ||
-      !req(draft_prob, 4) || !req(draft_lse, 4))
+  if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !opt(W2T, 16) || W2T == W2 || !req(x0, 4) ||
+      !req(draft_tokens, 4) || !req(draft_prob, 4) || !req(draft_lse, 4))
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (temperature > 0.0f && !req(seeds, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (draft_workspace(B, gamma, V, r) > static_scratch_bytes()) return DSPARK_ERR_SCRATCH_LIMIT;
@@ -118,6 +134,7 @@ dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const 
   a.U = U;
   a.W1 = W1;
   a.W2 = W2;
+  a.W2T = W2T;
   a.x0 = x0;
   a.seeds = seeds;
   a.round = round;
@@ -140,7 +157,7 @@ dspark_status dspark_rnn_draft(const float* U, const void* W1, const void* W2, d
                                float temperature, const uint64_t* seeds, uint64_t round, int32_t* draft_tokens,
                                float* draft_prob, float* draft_lse, float* e_out, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-  if (wdtype != DSPARK_BF16) return DSPARK_ERR_UNSUPPORTED;
+  if (enum_value(wdtype) != DSPARK_BF16) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(Wp, 16) || !req(hp, 4) || !req(x0, 4) ||
       !req(draft_tokens, 4) || !req(draft_prob, 4) || !req(draft_lse, 4) || !opt(e_out, 4) ||
@@ -176,7 +193,7 @@ dspark_status dspark_verify(const float* U, const void* W1, const void* W2, cons
                             const int32_t* lengths, int B, int gamma, int V, int r, float temperature,
                             const uint64_t* seeds, uint64_t round, int32_t* accept_len, int32_t* out_tokens,
                             float* accept_prob, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
   const bool greedy = temperature == 0.0f;
   if (!req(x0, 4) || !req(draft_tokens, 4) || !req(target_logits, 16) || !req(accept_len, 4) ||
@@ -213,7 +230,7 @@ dspark_status dspark_verify(const float* U, const void* W1, const void* W2, cons
 dspark_status dspark_confidence(const float* h, const float* w, const void* W1, dspark_dtype wdtype,
                                 const int32_t* x0, const int32_t* draft_tokens, const float* sts, int B, int gamma,
                                 int d, int V, int r, float* conf, hipStream_t stream) {
-  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma, V, r) || d < 1 || d > (1 << 20)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (!req(h, 16) || !req(w, 16) || !req(W1, 16) || !req(x0, 4) || !req(draft_tokens, 4) || !opt(sts, 4) ||
       !req(conf, 4))
@@ -240,7 +257,8 @@ dspark_status dspark_schedule(const float* survival, const double* sps, int sps_
   if (B < 1 || gamma < 1 || gamma > kMaxGamma || (long long)B * gamma > kScheduleMax) return DSPARK_ERR_INVALID_ARGUMENT;
   if ((long long)sps_len < (long long)B * (gamma + 1) + 1) return DSPARK_ERR_INVALID_ARGUMENT;
   if (!req(survival, 4) || !req(sps, 8) || !req(lengths, 4) || !opt(theta, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
-  if (mode != DSPARK_SCHEDULE_EARLY_STOP && mode != DSPARK_SCHEDULE_CAPACITY && mode != DSPARK_SCHEDULE_TOP_K)
+  const int m = enum_value(mode);
+  if (m != DSPARK_SCHEDULE_EARLY_STOP && m != DSPARK_SCHEDULE_CAPACITY && m != DSPARK_SCHEDULE_TOP_K)
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (mode == DSPARK_SCHEDULE_TOP_K && !req(capacity_in, 4)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (!opt(capacity_out, 4)) return DSPARK_ERR_INVALID_ARGUMENT;
@@ -249,7 +267,7 @@ dspark_status dspark_schedule(const float* survival, const double* sps, int sps_
 }
 
 dspark_status dspark_transpose_w2(const void* W2, dspark_dtype wdtype, int r, int V, void* W2T, hipStream_t stream) {
-  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(1, 1, V, r) || !req(W2, 16) || !req(W2T, 16) || W2 == W2T) return DSPARK_ERR_INVALID_ARGUMENT;
   return from_hip(launch_transpose_w2(W2, wdtype == DSPARK_BF16, r, V, W2T, stream));
 }
@@ -269,7 +287,7 @@ dspark_status dspark_survival(const float* U, const void* W1, const void* W2, ds
     a.conf = conf;
     return from_hip(launch_survival(a, false, stream));
   }
-  if (!dtype_ok(wdtype)) return DSPARK_ERR_UNSUPPORTED;
+  if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
   const bool greedy = temperature == 0.0f;
   if (!req(x0, 4) || !req(draft_tokens, 4) || !req(target_logits, 16) || !opt(c_star, 4) || !req(workspace, 16))

@@ -494,10 +494,13 @@ static hipError_t launch_select_wave(const SelectArgs& sa, hipStream_t s) {
 }
 
 size_t draft_workspace(int B, int gamma, int V, int r) {
-  (void)gamma;
-  // tile summaries, look-ahead uniforms, ring-kernel operands (r = 256 only)
-  return align256((size_t)B * tiles_of(V, kTileCols) * sizeof(float2)) + align256((size_t)2 * B * sizeof(double)) +
-         (r == 256 ? align256(ring_operand_bytes(B)) : 0);
+  // per-position launches: tile summaries, look-ahead uniforms, ring-kernel
+  // operands (r = 256 only); the resident loop carves its own layout from the
+  // same bytes
+  const size_t launches = align256((size_t)B * tiles_of(V, kTileCols) * sizeof(float2)) +
+                          align256((size_t)2 * B * sizeof(double)) + (r == 256 ? align256(ring_operand_bytes(B)) : 0);
+  const size_t resident = resident_workspace(B, gamma, V, r);
+  return launches > resident ? launches : resident;
 }
 
 template <bool kGreedy, bool kBf16, int kParts = 1>
@@ -508,6 +511,11 @@ static hipError_t launch_select(const SelectArgs& s, hipStream_t st) {
 }
 
 hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s) {
+  if (resident_draft_applies(a, bf16)) {
+    bool launched = false;
+    const hipError_t e = launch_resident_draft(a, s, &launched);
+    if (e != hipSuccess || launched) return e;
+  }
   const bool greedy = a.temperature == 0.0f;
   const int ntiles = tiles_of(a.V, kTileCols);
   float2* partials = reinterpret_cast<float2*>(a.ws);

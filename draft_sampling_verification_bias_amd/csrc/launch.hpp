@@ -14,7 +14,8 @@ namespace dspark {
 constexpr int kTileCols = 128;
 constexpr int kTgtCols = 256;
 
-inline int tiles_of(int V, int cols) { return (V + cols - 1) / cols; }
+// ceil(V / cols), in 64 bits: V may be as large as 2^31 - 1
+inline int tiles_of(int V, int cols) { return (int)(((long long)V + cols - 1) / cols); }
 
 // Which per-(row, tile) summary the tile pass writes.
 enum TileMode : int {
@@ -74,6 +75,7 @@ struct DraftArgs {
   const float* U;
   const void* W1;
   const void* W2;
+  const void* W2T;   // optional [V][r] copy of W2 (enables the resident loop)
   const int32_t* x0;
   const uint64_t* seeds;
   uint64_t round;
@@ -87,6 +89,13 @@ struct DraftArgs {
 
 size_t draft_workspace(int B, int gamma, int V, int r);
 hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s);
+
+// The device-resident draft loop (resident.hip): whether it applies to these
+// arguments, its workspace, and its launch (*launched false: not enqueued,
+// the caller uses the per-position launches).
+bool resident_draft_applies(const DraftArgs& a, bool bf16);
+size_t resident_workspace(int B, int gamma, int V, int r);
+hipError_t launch_resident_draft(const DraftArgs& a, hipStream_t s, bool* launched);
 
 // Block sampling with the RNN head (bf16 W1 and W2 only).
 struct RnnDraftArgs {
@@ -214,7 +223,8 @@ hipError_t launch_markov_bias(const void* W1, const void* W2, bool bf16, const i
 enum ProfKind : int {
   kProfTileSample = 0, kProfTileGreedy, kProfTileOverlap, kProfTileBias, kProfDraftSelect,
   kProfVerifyInit, kProfTargetStats, kProfVerifyDecide, kProfResidualStats, kProfResidualSelect,
-  kProfSurvivalConf, kProfSurvivalTnorm, kProfSurvivalFinish, kProfSchedule, kProfConfidence, kProfRnnCell, kProfKinds
+  kProfSurvivalConf, kProfSurvivalTnorm, kProfSurvivalFinish, kProfSchedule, kProfConfidence, kProfRnnCell,
+  kProfResidentDraft, kProfKinds
 };
 
 // Brackets the launches made during its lifetime with HIP events when timing

@@ -8,9 +8,10 @@
 
 namespace dspark {
 
-// 16 MiB.  The draft needs draft_workspace(B, gamma, V, r) bytes of it:
-// about 5.1 MB at B = 512, V = 151936, r = 256.
-constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+// 32 MiB.  The draft needs draft_workspace(B, gamma, V, r) bytes of it, the
+// larger of its two schedules: 14.1 MiB at B = 256, V = 151936, r = 256 and
+// 28.3 MiB at B = 512 (the device-resident loop's summaries).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
 
 static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 

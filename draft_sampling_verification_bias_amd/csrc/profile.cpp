@@ -15,6 +15,7 @@ const char* const kNames[kProfKinds] = {
     "tile_pass_sample", "tile_pass_greedy", "tile_pass_overlap", "tile_pass_bias", "draft_select",
     "verify_init",      "target_stats",     "verify_decide",     "residual_stats", "residual_select",
     "survival_conf",    "survival_tnorm",   "survival_finish",   "schedule",   "confidence",   "rnn_cell",
+    "draft_resident",
 };
 
 struct Record {

@@ -1,0 +1,813 @@
+// The device-resident block loop of dspark_markov_draft: all gamma positions
+// of the left-to-right sampler of the DSpark technical review ("The
+// Sequential Correction", Eq. 4, with the Markov head of "Instantiation 1:
+// The Markov Head", Eq. 5; the decode-round pseudocode's draft loop) in ONE
+// launch, with W2 held on chip for the whole call.
+//
+// One workgroup per compute unit (8 waves, two per SIMD), all co-resident
+// (cooperative launch).  The vocabulary is cut into 16-column sub-blocks and
+// every wave owns a contiguous range of at most five of them; the wave's
+// slice of W2 -- its columns for all r = 256 rows, up to 40 KB -- is loaded
+// once, from the vocabulary-major copy W2T, into MFMA operand registers (A
+// fragments of v_mfma_f32_16x16x32_bf16: lane l holds column l % 16 of a
+// sub-block, k = 8 (l / 16) .. + 7 of a 32-wide k step; 160 VGPRs) and stays
+// there for all positions.  Per position the only HBM stream is U_k.
+//
+// Position k, per 16-row group g:
+//   E rows (the W1 rows of the previous tokens, 8 KB, one DMA per wave) and
+//   each wave's U_k block (16 rows x its columns, 5 KB) arrive in LDS by
+//   global -> LDS DMA, the U blocks three groups ahead and E two groups
+//   ahead; 40 MFMAs per wave form bias^T = W2^T E^T for the wave's columns
+//   (exact bf16 products, fp32 accumulation); the epilogue adds U and
+//   reduces each row of the wave's range to (max, sum of 2^((l - max)
+//   log2(e) / T)) plus one partial sum per sub-block (argmax at T = 0).
+// Between positions:
+//   barrier A (every range summary of position k written), the selection of
+//   each request's x_k by one wave (float64 search over the range summaries,
+//   then over the chosen range's sub-block sums, then a rescan of one
+//   16-column sub-block with W2T rows: the stream-0 inverse CDF), the store
+//   of W1[x_k] as the next position's E row, barrier B.  The other waves
+//   meanwhile DMA the first U blocks of position k + 1 (they do not depend
+//   on x_k).
+// Barriers are flag arrays (one word per workgroup, written with release
+// semantics at agent scope, polled by one wave with acquire semantics); every
+// wait is bounded in time, and a wait that times out sets an error word, the
+// workgroup drains its DMAs and exits, and a follow-up kernel marks every
+// request invalid (-1 / NaN), so no launch can hang.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dspark {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void res_lds_void;
+
+constexpr int kResThreads = 512;
+constexpr int kResWaves = kResThreads / kWave;      // 8: two per SIMD
+constexpr int kResR = 256;                          // Markov rank of this path
+constexpr int kResSub = 5;                          // 16-column sub-blocks per wave (at most)
+constexpr int kResKSteps = kResR / 32;              // k steps of 32
+constexpr int kResRows = 16;                        // rows per group
+constexpr int kResStages = 3;                       // U blocks in flight per wave
+constexpr int kResStageBytes = kResSub * 1024;      // one U block: 16 rows x 80 columns
+constexpr int kResWaveU = kResStages * kResStageBytes;
+constexpr int kResEBytes = kResKSteps * 1024;       // E rows of one group in fragment order
+constexpr int kResESlots = 3;                       // E(g) is issued two groups ahead
+constexpr int kResLdsE = kResWaves * kResWaveU;     // 120 KB of U stages before it
+constexpr int kResERegion = 32 * 1024;              // E slots (24 KB); the selections' stages between positions
+constexpr int kResSelStage = 16 * 1024;             // per selecting wave
+constexpr int kResSelWave = 1024;                   // per selecting wave: E row, uniforms
+constexpr int kResLdsSel = kResLdsE + kResERegion;
+constexpr int kResMaxRowsPerWg = 2;
+constexpr int kResLdsMisc = kResLdsSel + kResMaxRowsPerWg * kResSelWave;
+constexpr int kResLds = kResLdsMisc + 64;
+constexpr int kResMaxWg = 256;
+constexpr int kResMaxNW = kResWaves * kResMaxWg;    // range summaries per row
+constexpr int kResSumPerLane = kResMaxNW / kWave;   // 32
+constexpr int kResWgSub = kResWaves * kResSub;      // sub-block sums per row per workgroup (slots)
+
+static_assert(kResLds <= 160 * 1024, "LDS budget");
+static_assert(kResESlots * kResEBytes <= kResERegion, "E slots");
+static_assert(kResMaxRowsPerWg * kResSelStage <= kResERegion, "selection stages");
+
+struct ResArgs {
+  const float* U;
+  const uint16_t* W1;
+  const uint16_t* W2T;
+  const int32_t* x0;
+  const uint64_t* seeds;
+  uint64_t round;
+  int B, gamma, V, nsb, NW, G, rows_per_wg;
+  float cf;        // log2(e) / T (0 at T == 0)
+  double inv_t;    // 1 / T
+  int32_t* tokens;
+  float* prob;
+  float* lse;
+  float2* part;    // [G][nwg][16][8]: range summaries; one workgroup writes 1 KB per group
+  float* ssum;     // [G][nwg][16][40]: sub-block sums (relative to the range maximum)
+  uint16_t* eops;  // [B][256] W1 row of each request's previous token
+  uint32_t* flags; // [nwg] barrier phases, then the error word
+  long long timeout;  // ticks of the 100 MHz real-time counter
+};
+
+// ---------------------------------------------------------------------------
+// Low-level helpers
+// ---------------------------------------------------------------------------
+// One 16-byte global -> LDS DMA per lane (lane l writes LDS [dst + 16 l, +16)).
+// The compiler does not see it: callers order it with explicit vmcnt waits
+// and barriers.
+__device__ __forceinline__ void res_dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// LDS address of the dynamic shared array (taken once per kernel).
+__device__ __forceinline__ uint32_t res_lds_base(unsigned char* smem) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)((res_lds_void*)smem));
+}
+
+template <int N>
+__device__ __forceinline__ void res_wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void res_wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0) only
+
+__device__ __forceinline__ long long res_clock() { return (long long)__builtin_amdgcn_s_memrealtime(); }
+
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 that hold one
+// row in the MFMA result layout, with the gfx950 row swaps (no LDS): after
+// v_permlane16_swap (v, v) the two results hold, in every lane, the values
+// of l and l ^ 16; after v_permlane32_swap those of l and l ^ 32.
+__device__ __forceinline__ float res_max_rows(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float res_sum_rows(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// (value, column) argmax over the same four lanes: larger value, then lower
+// column.  Both lanes of a pair merge the same two candidates.
+__device__ __forceinline__ void res_argmax_rows(float& v, int& c) {
+  auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  auto rc = __builtin_amdgcn_permlane16_swap((unsigned)c, (unsigned)c, false, false);
+  v = __uint_as_float(rv[0]);
+  c = (int)rc[0];
+  argmax_merge(v, c, __uint_as_float(rv[1]), (int)rc[1]);
+  rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  rc = __builtin_amdgcn_permlane32_swap((unsigned)c, (unsigned)c, false, false);
+  v = __uint_as_float(rv[0]);
+  c = (int)rc[0];
+  argmax_merge(v, c, __uint_as_float(rv[1]), (int)rc[1]);
+}
+
+// Barrier arrival: every wave of the workgroup has completed its stores
+// (the caller waited vmcnt(0) and passed a workgroup barrier); the release
+// makes them visible at agent scope before the phase number is.
+__device__ __forceinline__ void res_arrive(uint32_t* flags, int wg, uint32_t phase) {
+  __hip_atomic_store(flags + wg, phase, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (one wave) until every workgroup has reached `phase`; false on the
+// error word or on timeout (then the error word is set).  Acquire on success.
+__device__ bool res_wait_phase(uint32_t* flags, int nwg, uint32_t phase, long long timeout) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long t0 = res_clock();
+  for (;;) {
+    // the flags and the error word in one batch of loads (one round trip)
+    uint32_t f[kResMaxWg / kWave];
+#pragma unroll
+    for (int j = 0; j < kResMaxWg / kWave; ++j) {
+      const int i = lane + j * kWave;
+      f[j] = i < nwg ? __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0xffffffffu;
+    }
+    const uint32_t err = __hip_atomic_load(flags + nwg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t mn = 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < kResMaxWg / kWave; ++j) mn = f[j] < mn ? f[j] : mn;
+    if (__ballot(mn < phase) == 0) break;
+    if (err != 0u) return false;
+    if (res_clock() - t0 > timeout) {
+      if (lane == 0) __hip_atomic_store(flags + nwg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Column ranges: wave gw (of NW) owns sub-blocks [sb0, sb0 + n) of the
+// V / 16, n <= kResSub.
+// ---------------------------------------------------------------------------
+struct Range {
+  int sb0, n;
+};
+
+__device__ __forceinline__ Range res_range(const ResArgs& a, int gw) {
+  Range r;
+  r.sb0 = (int)((long long)gw * a.nsb / a.NW);
+  r.n = (int)((long long)(gw + 1) * a.nsb / a.NW) - r.sb0;
+  return r;
+}
+
+// U block of (position k, group g) for the wave owning range `rg`: kResSub
+// DMAs, sub-block s from lane l: row 16 g + l % 16 (clamped to B - 1),
+// columns 16 (sb0 + s) + 4 (l / 16) .. + 3 (sub-blocks past the range repeat
+// the first one; their values are never used).
+//
+// With real == false the same number of DMAs is issued, every lane reading
+// the first 16 bytes of U (one cache line): the wait counts of the group
+// loop then do not depend on the group, and the stage receives values that
+// are never read.
+__device__ __forceinline__ void res_issue_u(const ResArgs& a, Range rg, int k, int g, uint32_t stage,
+                                            bool real = true) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int row = kResRows * g + (lane & 15);
+  row = row < a.B ? row : a.B - 1;
+  const int cbase = rg.n > 0 ? 16 * rg.sb0 : 0;
+  const uint32_t rowoff = (uint32_t)row * (uint32_t)a.gamma * (uint32_t)a.V + (uint32_t)(k - 1) * (uint32_t)a.V;
+#pragma unroll
+  for (int s = 0; s < kResSub; ++s) {
+    const int se = s < rg.n ? s : 0;
+    const uint32_t off = real ? (rowoff + (uint32_t)(cbase + 16 * se + 4 * (lane >> 4))) * 4u : 0u;
+    res_dma16(a.U, off, stage + (uint32_t)(s * 1024));
+  }
+}
+
+// E rows of group g (the previous tokens' W1 rows): k step ks = wave, from
+// lane l row 16 g + l % 16, k = 32 ks + 8 (l / 16) .. + 7.  real == false as
+// for res_issue_u (the first 16 bytes of the E rows).
+__device__ __forceinline__ void res_issue_e(const ResArgs& a, int g, uint32_t ebuf, bool real = true) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ks = threadIdx.x / kWave;
+  int row = kResRows * g + (lane & 15);
+  row = row < a.B ? row : a.B - 1;
+  const uint32_t off = real ? ((uint32_t)row * kResR + 32u * ks + 8u * (lane >> 4)) * 2u : 0u;
+  res_dma16(a.eops, off, ebuf + (uint32_t)(ks * 1024));
+}
+
+// The first U blocks of position k for all eight waves of the workgroup --
+// min(3, G) for waves 0-3, min(2, G) for waves 4-7, whose epilogues run one
+// step later -- issued by the waves [w0, 8) in turn.
+__device__ __forceinline__ void res_prefetch(const ResArgs& a, int k, int w0, uint32_t lds) {
+  const int wave = threadIdx.x / kWave;
+  const int np = kResWaves - w0;
+  const int nst = a.G < kResStages ? a.G : kResStages;
+  for (int item = wave - w0; item < kResWaves * nst; item += np) {
+    const int tw = item % kResWaves, g = item / kResWaves;
+    if (tw >= kResWaves / 2 && g == kResStages - 1) continue;
+    const Range rg = res_range(a, blockIdx.x * kResWaves + tw);
+    res_issue_u(a, rg, k, g, lds + (uint32_t)(tw * kResWaveU + (g % kResStages) * kResStageBytes));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection of one request's token at position k by one wave.  `stage` (16
+// KB of the E region, idle between positions) receives the row's range
+// summaries and then the rescan's W2T rows.
+// ---------------------------------------------------------------------------
+template <bool kGreedy>
+__device__ void res_select(const ResArgs& a, int b, int k, int& prev, unsigned char* sel, const unsigned char* stage,
+                           uint32_t stage_lds) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nwg = gridDim.x;
+  const size_t out = (size_t)b * a.gamma + (k - 1);
+  const double* utab = reinterpret_cast<const double*>(sel + 512);
+  const unsigned char* erow = sel;
+  if (prev < 0) {  // invalid anchor or earlier position
+    if (lane == 0) {
+      a.tokens[out] = -1;
+      a.prob[out] = __builtin_nanf("");
+      a.lse[out] = __builtin_nanf("");
+    }
+    return;
+  }
+  const uint32_t g = (uint32_t)b >> 4, n = (uint32_t)b & 15u;
+  // The row's NW = 8 nwg range summaries into the stage, in wave order: the
+  // 64 bytes of workgroup w (its eight waves) sit at part[g][w][n][0..7];
+  // DMA i gathers workgroups 16 i .. 16 i + 15, four lanes each.
+  {
+    for (int i = 0; i < (nwg + 15) / 16; ++i) {
+      uint32_t w = (uint32_t)(16 * i) + ((uint32_t)lane >> 2);
+      w = w < (uint32_t)nwg ? w : 0u;
+      const uint32_t off = (((g * (uint32_t)nwg + w) * 16u + n) * 8u) * 8u + 16u * ((uint32_t)lane & 3u);
+      res_dma16(a.part, off, stage_lds + (uint32_t)(1024 * i));
+    }
+    res_wait_vmem<0>();
+  }
+  // summaries 2 j2, 2 j2 + 1 of lane l's [32 l, 32 l + 32) as (m, s, m, s);
+  // -inf past NW
+  const float4* P4 = reinterpret_cast<const float4*>(stage) + (kResSumPerLane / 2) * lane;
+  auto pair = [&](int j2) -> float4 {
+    const float4 q = P4[j2];
+    return kResSumPerLane * lane + 2 * j2 < a.NW ? q : make_float4(-__builtin_inff(), 0.0f, -__builtin_inff(), 0.0f);
+  };
+  int x;
+  if constexpr (kGreedy) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll 2
+    for (int j2 = 0; j2 < kResSumPerLane / 2; ++j2) {
+      const float4 q = pair(j2);
+      argmax_merge(bv, bi, q.x, __float_as_int(q.y));
+      argmax_merge(bv, bi, q.z, __float_as_int(q.w));
+    }
+    wave_argmax(bv, bi);
+    x = bi;
+    if (lane == 0) {
+      a.tokens[out] = x;
+      a.prob[out] = 1.0f;
+      a.lse[out] = 0.0f;
+    }
+  } else {
+    // (the loops over the lane's summaries stay rolled: every register they
+    // would take is one less for the W2 slice held across this function)
+    float lm = -__builtin_inff();
+#pragma unroll 2
+    for (int j2 = 0; j2 < kResSumPerLane / 2; ++j2) {
+      const float4 q = pair(j2);
+      lm = fmaxf(lm, fmaxf(q.x, q.z));
+    }
+    const float M = wave_max_dpp(lm);
+    auto weight = [&](float mj, float sj) -> double {
+      return mj != -__builtin_inff() ? (double)sj * (double)fast_exp2((mj - M) * a.cf) : 0.0;
+    };
+    double local = 0.0;
+#pragma unroll 2
+    for (int j2 = 0; j2 < kResSumPerLane / 2; ++j2) {
+      const float4 q = pair(j2);
+      local += weight(q.x, q.y);
+      local += weight(q.z, q.w);
+    }
+    const double incl = wave_inclusive_scan_dpp(local);
+    const double total = lane_f64(incl, kWave - 1);
+    const double u = utab[k - 1];
+    const double q = u * total;
+    const unsigned long long cross = __ballot(local > 0.0 && incl > q);
+    const unsigned long long pos = __ballot(local > 0.0);
+    const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+    // the owner's range: first positive weight whose inclusive sum exceeds q,
+    // else the last positive one (selects, every lane runs it)
+    int ri = -1, lastpos = -1;
+    double base = 0.0, lastbase = 0.0;
+    float mi = 0.0f, lastm = 0.0f;
+    {
+      double cum = incl - local;
+#pragma unroll 1
+      for (int j = 0; j < kResSumPerLane; ++j) {
+        const float2 qq = reinterpret_cast<const float2*>(P4)[j];
+        const bool live = kResSumPerLane * lane + j < a.NW;
+        const float mj = live ? qq.x : -__builtin_inff(), sj = qq.y;
+        const double w = weight(mj, sj);
+        const bool posw = w > 0.0;
+        const bool hit = posw && ri < 0 && cum + w > q;
+        lastpos = posw ? j : lastpos;
+        lastbase = posw ? cum : lastbase;
+        lastm = posw ? mj : lastm;
+        ri = hit ? j : ri;
+        base = hit ? cum : base;
+        mi = hit ? mj : mi;
+        cum += w;
+      }
+      const bool none = ri < 0;
+      ri = kResSumPerLane * lane + (none ? (lastpos < 0 ? 0 : lastpos) : ri);
+      base = none ? (lastpos < 0 ? 0.0 : lastbase) : base;
+      mi = none ? (lastpos < 0 ? M : lastm) : mi;
+    }
+    ri = lane_i32(ri, owner);
+    base = lane_f64(base, owner);
+    mi = lane_f32(mi, owner);
+    // the same factor as in the range's weight, so the sub-block and column
+    // weights below add up to it
+    const double scale = (double)fast_exp2((mi - M) * a.cf);
+    // the sub-block of the range (its sums are relative to mi)
+    const Range rg = res_range(a, ri);
+    const int rw = ri / kResWaves;  // the workgroup that wrote the range
+    const int loc = rg.sb0 - res_range(a, rw * kResWaves).sb0;
+    const float sbv = lane < rg.n ? a.ssum[((size_t)(g * (uint32_t)nwg + rw) * 16 + n) * kResWgSub + loc + lane] : 0.0f;
+    const double wb = lane < rg.n ? (double)sbv * scale : 0.0;
+    const double bincl = wave_inclusive_scan_dpp(wb);
+    const double q1 = q - base;
+    const unsigned long long bcross = __ballot(wb > 0.0 && bincl > q1);
+    const unsigned long long bpos = __ballot(wb > 0.0);
+    const int bj = bcross ? __ffsll((long long)bcross) - 1 : (bpos ? 63 - __clzll((long long)bpos) : 0);
+    const double base1 = lane_f64(bincl - wb, bj);
+    const int c0 = 16 * (rg.sb0 + bj);
+    res_wait_lgkm0();  // every LDS read of the summaries is done before the stage is overwritten
+    // Rescan of sub-block bj: the logits U + W1[x_{k-1}] . W2[:, c] of its 16
+    // columns.  Its W2T rows (16 x 512 B) arrive in the stage (DMA i: columns
+    // 2 i, 2 i + 1); lane l owns column l % 16 and the 64-wide k quarter
+    // l / 16 (16-byte chunks read in a rotated order against bank conflicts).
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t off = ((uint32_t)(c0 + 2 * i + (lane >> 5)) * kResR + 8u * (lane & 31)) * 2u;
+      res_dma16(a.W2T, off, stage_lds + (uint32_t)(i * 1024));
+    }
+    const int cl = lane & 15, qk = lane >> 4;
+    const float uval = a.U[((size_t)b * a.gamma + (k - 1)) * a.V + c0 + cl];
+    res_wait_vmem<0>();
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ch = 8 * qk + ((i + cl) & 7);  // 16-byte chunk of the 512-byte row
+      const uint4 wv = *reinterpret_cast<const uint4*>(stage + cl * 512 + ch * 16);
+      const uint4 ev = *reinterpret_cast<const uint4*>(erow + ch * 16);
+      const uint32_t we[4] = {wv.x, wv.y, wv.z, wv.w};
+      const uint32_t ee[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc = fmaf(__uint_as_float(ee[t] << 16), __uint_as_float(we[t] << 16), acc);
+        acc = fmaf(__uint_as_float(ee[t] & 0xffff0000u), __uint_as_float(we[t] & 0xffff0000u), acc);
+      }
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    const float l = uval + acc;
+    const bool lv = lane < 16 && l != -__builtin_inff();
+    const double wc = lv ? (double)fast_exp2((l - mi) * a.cf) * scale : 0.0;
+    const double cincl = wave_inclusive_scan_dpp(wc);
+    const double q2 = q1 - base1;
+    const unsigned long long ccross = __ballot(wc > 0.0 && cincl > q2);
+    const unsigned long long cpos = __ballot(wc > 0.0);
+    const int cj = ccross ? __ffsll((long long)ccross) - 1 : (cpos ? 63 - __clzll((long long)cpos) : 0);
+    x = c0 + cj;
+    const float lx = lane_f32(l, cj);
+    if (lane == 0) {
+      a.tokens[out] = x;
+      a.prob[out] = (float)((double)fast_exp2((lx - M) * a.cf) / total);
+      // hardware log2 (about 1 ulp of log2(total)): the double library log
+      // would hold its polynomial constants in registers across the kernel
+      a.lse[out] = (float)((double)M * a.inv_t + 0.6931471805599453 * (double)__builtin_amdgcn_logf((float)total));
+    }
+  }
+  if ((unsigned)x >= (unsigned)a.V) {  // only an all -inf row (outside the preconditions) gets here
+    if (lane == 0) {
+      a.tokens[out] = -1;
+      a.prob[out] = __builtin_nanf("");
+      a.lse[out] = __builtin_nanf("");
+    }
+    prev = -1;
+    return;
+  }
+  prev = x;
+  // W1[x] is the next position's E row: in the shared array for the tile
+  // passes and in this wave's LDS for its own rescan
+  if (k < a.gamma) {
+    const uint2 v = reinterpret_cast<const uint2*>(a.W1 + (size_t)x * kResR)[lane];
+    reinterpret_cast<uint2*>(a.eops + (size_t)b * kResR)[lane] = v;
+    reinterpret_cast<uint2*>(sel)[lane] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+template <bool kGreedy>
+__global__ __launch_bounds__(kResThreads, 1) void draft_resident_kernel(ResArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int gw = wg * kResWaves + wave;
+  const Range my = res_range(a, gw);
+  const int cbase = my.n > 0 ? 16 * my.sb0 : 0;
+  const int myloc = my.sb0 - res_range(a, wg * kResWaves).sb0;  // first sub-block slot of the wave in its workgroup
+  const uint32_t lds = res_lds_base(smem);
+  const uint32_t ustage_l = lds + (uint32_t)(wave * kResWaveU);
+  const uint32_t ebufs_l = lds + (uint32_t)kResLdsE;
+  const unsigned char* ustage = smem + wave * kResWaveU;
+  const unsigned char* ebufs = smem + kResLdsE;
+  const bool selw = wave < a.rows_per_wg;
+  const int mrow = wg + wave * nwg;  // the request this wave selects (if selw)
+  unsigned char* sel = smem + kResLdsSel + wave * kResSelWave;
+  volatile int* ok_flag = reinterpret_cast<volatile int*>(smem + kResLdsMisc);
+
+  // the first U blocks of position 1 (they depend on nothing) stream in
+  // while W2 is loaded
+  if (!selw) res_prefetch(a, 1, a.rows_per_wg, lds);
+
+  // the wave's slice of W2 as MFMA A fragments, for the whole call
+  bf16x8 wf[kResSub][kResKSteps];
+#pragma unroll
+  for (int s = 0; s < kResSub; ++s) {
+    const int se = s < my.n ? s : 0;
+    const uint16_t* src = a.W2T + (size_t)(cbase + 16 * se + (lane & 15)) * kResR + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < kResKSteps; ++ks) wf[s][ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
+  }
+
+  // selecting waves: uniforms of every position, the first E row
+  int prev = -1;
+  if (selw && mrow < a.B) {
+    double* utab = reinterpret_cast<double*>(sel + 512);
+    if constexpr (!kGreedy) {
+      if (lane < a.gamma)
+        utab[lane] = unit_uniform(draw_block(a.seeds[mrow], a.round, lane + 1, kStreamDraft, 0).w[0]);
+    }
+    const int x0 = a.x0[mrow];
+    prev = (unsigned)x0 < (unsigned)a.V ? x0 : -1;
+    uint2 v = make_uint2(0u, 0u);
+    if (prev >= 0) v = reinterpret_cast<const uint2*>(a.W1 + (size_t)prev * kResR)[lane];
+    reinterpret_cast<uint2*>(a.eops + (size_t)mrow * kResR)[lane] = v;
+    reinterpret_cast<uint2*>(sel)[lane] = v;
+  }
+  res_wait_vmem<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) res_arrive(a.flags, wg, 1u);
+  if (wave == 0) {
+    const bool ok = res_wait_phase(a.flags, nwg, 1u, a.timeout);
+    if (lane == 0) *ok_flag = ok ? 1 : 0;
+  }
+  __syncthreads();
+  if (!*ok_flag) {
+    res_wait_vmem<0>();
+    return;
+  }
+
+  const int G = a.G;
+  // E(0) and E(1) of a position are issued at its start, E(g + 2) at the
+  // start of step g (three slots), so that the wait for E(g) leaves the U
+  // blocks issued after it in flight
+  auto e_slot = [&](int g) -> uint32_t { return ebufs_l + (uint32_t)((g % kResESlots) * kResEBytes); };
+  res_issue_e(a, 0, e_slot(0));
+  res_issue_e(a, 1, e_slot(1), G > 1);
+
+  const int n16 = lane & 15, q4 = lane >> 4;
+  // Waves w and w + 4 share a SIMD.  In step g, waves 0-3 form the products
+  // of group g and then finish it (the epilogue), while waves 4-7 first
+  // finish group g - 1 (whose products they formed in step g - 1) and then
+  // form the products of group g: on each SIMD one wave's MFMAs overlap the
+  // other's vector work.  Waves 4-7 take one more step per position.
+  const bool products_first = wave < kResWaves / 2;
+  for (int k = 1; k <= a.gamma; ++k) {
+    f32x4 acc[kResSub];
+    for (int g = 0; g <= G; ++g) {
+      // E(g) and the U block this step's epilogue reads (U(k, e), e = g for
+      // waves 0-3 and g - 1 for waves 4-7) have landed.  Issue order per
+      // step g < G, the same for every wave: E(g + 2) (1 DMA) at its start,
+      // U(k, e + 3) (5 DMAs) right after the epilogue has read U(k, e), real
+      // or not, and summary stores; E(0), E(1) at the position start and
+      // U(k, 0), U(k, 1) (and U(k, 2) for waves 0-3) before it, by some wave
+      // of the workgroup, all of which wait for them here at step 0.  So
+      // after E(g) come E(1) at step 0, 1 + 5 at step 1 and 5 + 1 + 5 at steps
+      // g >= 2, and U(k, e) is issued before E(g).
+      __builtin_amdgcn_sched_barrier(0);
+      if (g == 0) {
+        res_wait_vmem<1>();
+      } else if (g == 1) {
+        res_wait_vmem<kResSub + 1>();
+      } else {
+        res_wait_vmem<2 * kResSub + 1>();
+      }
+      __syncthreads();
+      if (g < G) res_issue_e(a, g + 2, e_slot(g + 2), g + 2 < G);
+
+      // bias^T of the wave's columns for the 16 rows of group g
+      auto products = [&]() {
+        const unsigned char* ebuf = ebufs + (g % kResESlots) * kResEBytes;
+        // all eight E fragments are requested at once (32 VGPRs), so the
+        // LDS latency is paid once and the MFMAs of k step ks start as soon
+        // as its fragment is in
+        bf16x8 ev[kResKSteps];
+#pragma unroll
+        for (int ks = 0; ks < kResKSteps; ++ks) ev[ks] = *reinterpret_cast<const bf16x8*>(ebuf + ks * 1024 + 16 * lane);
+#pragma unroll
+        for (int s = 0; s < kResSub; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < kResKSteps; ++ks) {
+#pragma unroll
+          for (int s = 0; s < kResSub; ++s)
+            acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s][ks], ev[ks], acc[s], 0, 0, 0);
+        }
+        // schedule: the eight LDS reads, then the 40 MFMAs (left alone, the
+        // scheduler re-reads one fragment per k step to save registers)
+        __builtin_amdgcn_sched_group_barrier(0x100, kResKSteps, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kResKSteps * kResSub, 0);
+      };
+      // U(k, e + 3) into the stage of U(k, e) once this wave has read it
+      auto issue_u = [&](int e) {
+        if (g < G)
+          res_issue_u(a, my, k, e + kResStages, ustage_l + (uint32_t)(((e + kResStages) % kResStages) * kResStageBytes),
+                      e + kResStages < G);
+      };
+      // group e: acc[s][i] + U is the logit of row 16 e + l % 16,
+      // column 16 (sb0 + s) + 4 (l / 16) + i (U added to the finished bias,
+      // not accumulated through it: the float32 rounding then stays at the
+      // bias's magnitude, as in the selection's rescan).  Sub-blocks past the
+      // range repeat sub-block 0 (same columns, same values): they leave
+      // maxima unchanged and are dropped from sums.
+      auto epilogue = [&](int gp) {
+        const unsigned char* ub = ustage + (gp % kResStages) * kResStageBytes;
+#pragma unroll
+        for (int s = 0; s < kResSub; ++s) {
+          const float4 u = *reinterpret_cast<const float4*>(ub + s * 1024 + 16 * lane);
+          acc[s][0] += u.x;
+          acc[s][1] += u.y;
+          acc[s][2] += u.z;
+          acc[s][3] += u.w;
+        }
+        res_wait_lgkm0();
+        issue_u(gp);
+        const int row = kResRows * gp + n16;
+        const bool rowok = row < a.B;
+        const uint32_t pidx =
+            (((uint32_t)gp * (uint32_t)nwg + (uint32_t)wg) * 16u + (uint32_t)n16) * 8u + (uint32_t)wave;
+        if constexpr (kGreedy) {
+          float bv = -__builtin_inff();
+          int bc = 0x7fffffff;
+#pragma unroll
+          for (int s = 0; s < kResSub; ++s) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              // ascending columns within the lane and strict comparison: the
+              // lowest index wins ties, and a repeated sub-block never wins
+              const bool better = acc[s][i] > bv;
+              bv = better ? acc[s][i] : bv;
+              bc = better ? cbase + 16 * s + 4 * q4 + i : bc;
+            }
+          }
+          res_argmax_rows(bv, bc);
+          if (my.n == 0) bv = -__builtin_inff(), bc = 0x7fffffff;
+          if (lane < 16 && rowok) a.part[pidx] = make_float2(bv, __int_as_float(bc));
+        } else {
+          float m = -__builtin_inff();
+#pragma unroll
+          for (int s = 0; s < kResSub; ++s)
+            m = fmaxf(m, fmaxf(fmaxf(acc[s][0], acc[s][1]), fmaxf(acc[s][2], acc[s][3])));
+          m = res_max_rows(m);  // the row's maximum over the four lanes that hold it
+          // with m = -inf every logit is -inf and every term 2^-inf = 0
+          const float mc = m == -__builtin_inff() ? 0.0f : m * a.cf;
+          float bp[kResSub];
+#pragma unroll
+          for (int s = 0; s < kResSub; ++s) {
+            const float v = (fast_exp2(fmaf(acc[s][0], a.cf, -mc)) + fast_exp2(fmaf(acc[s][1], a.cf, -mc))) +
+                            (fast_exp2(fmaf(acc[s][2], a.cf, -mc)) + fast_exp2(fmaf(acc[s][3], a.cf, -mc)));
+            bp[s] = res_sum_rows(s < my.n ? v : 0.0f);
+          }
+          const float S = (((bp[0] + bp[1]) + bp[2]) + bp[3]) + bp[4];
+          if (lane < 16 && rowok) a.part[pidx] = make_float2(my.n > 0 ? m : -__builtin_inff(), S);
+          const float bq = q4 == 0 ? bp[0] : q4 == 1 ? bp[1] : q4 == 2 ? bp[2] : bp[3];
+          const uint32_t so =
+              (((uint32_t)gp * (uint32_t)nwg + (uint32_t)wg) * 16u + (uint32_t)n16) * kResWgSub + (uint32_t)myloc;
+          if (rowok && q4 < my.n) a.ssum[so + (uint32_t)q4] = bq;
+          if (rowok && q4 == 0 && my.n > 4) a.ssum[so + 4u] = bp[4];
+        }
+      };
+      if (products_first) {
+        if (g < G) {
+          products();
+          epilogue(g);
+        }
+      } else {
+        if (g > 0) epilogue(g - 1); else issue_u(-1);
+        if (g < G) products();
+      }
+    }
+
+    // ---- between positions: barrier A, selection, barrier B
+    res_wait_vmem<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) res_arrive(a.flags, wg, (uint32_t)(2 * k));
+    if (!selw && k < a.gamma) res_prefetch(a, k + 1, a.rows_per_wg, lds);
+    if (selw) {
+      const bool ok = res_wait_phase(a.flags, nwg, (uint32_t)(2 * k), a.timeout);
+      if (!ok && lane == 0) *ok_flag = 0;
+      const int sw = wave * kResSelStage;
+      if (ok && mrow < a.B) res_select<kGreedy>(a, mrow, k, prev, sel, ebufs + sw, ebufs_l + (uint32_t)sw);
+      res_wait_vmem<0>();
+    }
+    __syncthreads();
+    if (!*ok_flag) {
+      res_wait_vmem<0>();
+      return;
+    }
+    if (k == a.gamma) break;
+    if (threadIdx.x == 0) res_arrive(a.flags, wg, (uint32_t)(2 * k + 1));
+    if (wave == 0) {
+      const bool ok = res_wait_phase(a.flags, nwg, (uint32_t)(2 * k + 1), a.timeout);
+      if (lane == 0) *ok_flag = ok ? 1 : 0;
+    }
+    __syncthreads();
+    if (!*ok_flag) {
+      res_wait_vmem<0>();
+      return;
+    }
+    res_issue_e(a, 0, e_slot(0));
+    res_issue_e(a, 1, e_slot(1), G > 1);
+  }
+}
+
+// Outputs of every request become invalid (-1 / NaN) when the resident loop
+// reported a failed wait.
+__global__ void resident_fixup_kernel(const uint32_t* err, int32_t* tokens, float* prob, float* lse, int n) {
+  if (*err == 0u) return;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    tokens[i] = -1;
+    prob[i] = __builtin_nanf("");
+    lse[i] = __builtin_nanf("");
+  }
+}
+
+__global__ void resident_clear_kernel(uint32_t* flags, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) flags[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+struct ResLayout {
+  size_t part, ssum, eops, flags, total;
+};
+
+static ResLayout res_layout(int B) {
+  ResLayout l;
+  const size_t rows = (size_t)(B + kResRows - 1) / kResRows * kResRows;  // whole groups
+  l.part = 0;
+  l.ssum = align256(rows * kResMaxNW * sizeof(float2));
+  l.eops = l.ssum + align256(rows * kResMaxWg * kResWgSub * sizeof(float));
+  l.flags = l.eops + align256((size_t)B * kResR * sizeof(uint16_t));
+  l.total = l.flags + align256((size_t)(kResMaxWg + 1) * sizeof(uint32_t));
+  return l;
+}
+
+size_t resident_workspace(int B, int gamma, int V, int r) {
+  (void)gamma;
+  if (r != kResR || V % 16 != 0) return 0;
+  return res_layout(B).total;
+}
+
+template <bool kGreedy>
+static hipError_t res_prepare(int& max_blocks) {
+  static hipError_t state = hipErrorNotReady;
+  static int blocks = 0;
+  if (state == hipErrorNotReady) {
+    state = hipFuncSetAttribute((const void*)draft_resident_kernel<kGreedy>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kResLds);
+    if (state == hipSuccess)
+      state = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)draft_resident_kernel<kGreedy>,
+                                                           kResThreads, kResLds);
+  }
+  max_blocks = blocks;
+  return state;
+}
+
+bool resident_draft_applies(const DraftArgs& a, bool bf16) {
+  if (!bf16 || a.W2T == nullptr || a.r != kResR || a.V % 16 != 0) return false;
+  const int nwg = compute_units_of_device();
+  if (nwg < 1 || nwg > kResMaxWg) return false;
+  const long long NW = (long long)nwg * kResWaves;
+  const long long nsb = a.V / 16;
+  if ((nsb + NW - 1) / NW > kResSub) return false;               // W2 slice fits the registers
+  if ((a.B + nwg - 1) / nwg > kResMaxRowsPerWg) return false;    // selections per workgroup
+  if ((double)a.B * a.gamma * a.V * 4.0 >= 4294967296.0) return false;  // 32-bit DMA offsets
+  return true;
+}
+
+// Launches the resident loop; *launched is false (and nothing was enqueued)
+// when the device cannot hold the grid, so the caller can use the per-position
+// launches instead.
+hipError_t launch_resident_draft(const DraftArgs& d, hipStream_t s, bool* launched) {
+  *launched = false;
+  const bool greedy = d.temperature == 0.0f;
+  int maxb = 0;
+  hipError_t e = greedy ? res_prepare<true>(maxb) : res_prepare<false>(maxb);
+  if (e != hipSuccess || maxb < 1) return hipSuccess;
+  const int nwg = compute_units_of_device();
+  const ResLayout L = res_layout(d.B);
+  char* ws = reinterpret_cast<char*>(d.ws);
+  ResArgs a = {};
+  a.U = d.U;
+  a.W1 = reinterpret_cast<const uint16_t*>(d.W1);
+  a.W2T = reinterpret_cast<const uint16_t*>(d.W2T);
+  a.x0 = d.x0;
+  a.seeds = d.seeds;
+  a.round = d.round;
+  a.B = d.B;
+  a.gamma = d.gamma;
+  a.V = d.V;
+  a.nsb = d.V / 16;
+  a.NW = nwg * kResWaves;
+  a.G = (d.B + kResRows - 1) / kResRows;
+  a.rows_per_wg = (d.B + nwg - 1) / nwg;
+  a.cf = greedy ? 0.0f : (float)(1.4426950408889634 / (double)d.temperature);
+  a.inv_t = greedy ? 0.0 : 1.0 / (double)d.temperature;
+  a.tokens = d.tokens;
+  a.prob = d.prob;
+  a.lse = d.lse;
+  a.part = reinterpret_cast<float2*>(ws + L.part);
+  a.ssum = reinterpret_cast<float*>(ws + L.ssum);
+  a.eops = reinterpret_cast<uint16_t*>(ws + L.eops);
+  a.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
+  a.timeout = 20000000;  // 0.2 s at 100 MHz: orders of magnitude above a normal wait
+  {
+    ProfScope prof(s, kProfResidentDraft);
+    hipLaunchKernelGGL(resident_clear_kernel, dim3(1), dim3(256), 0, s, a.flags, nwg + 1);
+    void* args[] = {&a};
+    e = hipLaunchCooperativeKernel(greedy ? (const void*)draft_resident_kernel<true>
+                                          : (const void*)draft_resident_kernel<false>,
+                                   dim3(nwg), dim3(kResThreads), args, kResLds, s);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return hipSuccess;  // not launched: the caller falls back (the clear kernel is harmless)
+    }
+    *launched = true;
+    const int n = d.B * d.gamma;
+    hipLaunchKernelGGL(resident_fixup_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0,
+                       s, a.flags + nwg, d.tokens, d.prob, d.lse, n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void transpose_w2_kernel(const T* __restrict__
 }
 
 hipError_t launch_transpose_w2(const void* W2, bool bf16, int r, int V, void* W2T, hipStream_t s) {
-  const dim3 grid((V + kTrTile - 1) / kTrTile, (r + kTrTile - 1) / kTrTile);
+  const dim3 grid((unsigned)(((long long)V + kTrTile - 1) / kTrTile), (r + kTrTile - 1) / kTrTile);
   if (bf16) {
     hipLaunchKernelGGL(transpose_w2_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(W2), r, V,
                        static_cast<uint16_t*>(W2T));

@@ -140,6 +140,17 @@ dspark_status dspark_markov_bias(const void* W1, const void* W2, dspark_dtype wd
  *   x_k     = categorical draw from p_d^k with the stream-0 uniform at (round, k)
  * At T == 0, x_k = argmax l_k, draft_prob = 1 and draft_lse = 0.
  *
+ * W2T is optional (NULL to skip): W2 transposed, [V][r] in the weight dtype,
+ * as dspark_transpose_w2 writes it.  When it is given, the weights are bf16,
+ * r == 256, V % 16 == 0, V <= 80 * 8 * (compute units) (163840 on MI355X),
+ * B <= 2 * (compute units) and 4 B gamma V < 2^32, all gamma positions run
+ * in one cooperative launch that keeps W2 on chip (the "device-resident"
+ * loop); otherwise, or when the device cannot hold that launch, each
+ * position is its own pair of launches.  Both give the same draws up to the
+ * summation order of float32 sums.  If a grid-wide wait of the resident loop
+ * ever times out (it cannot while the launch is co-resident), every request's
+ * outputs are -1 / NaN.
+ *
  * Outputs:
  *   draft_tokens  int32   [B][gamma]  x_1..x_gamma
  *   draft_prob    float32 [B][gamma]  p_d^k(x_k)
@@ -148,7 +159,7 @@ dspark_status dspark_markov_bias(const void* W1, const void* W2, dspark_dtype wd
  *                                     dspark_survival)
  * Workspace: dspark_workspace_size(DSPARK_OP_DRAFT, B, gamma, V, r).
  */
-dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2,
+dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2, const void* W2T,
                                   dspark_dtype wdtype, const int32_t* x0,
                                   int B, int gamma, int V, int r, float temperature,
                                   const uint64_t* seeds, uint64_t round,
@@ -162,7 +173,7 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
  *
  * Arguments, outputs and results are exactly those of dspark_markov_draft
  * (the same kernels run).  Its scratch memory is a static device array of
- * dspark_static_scratch_bytes() bytes (16 MiB) inside the library, one per
+ * dspark_static_scratch_bytes() bytes (32 MiB) inside the library, one per
  * GPU, held until the process ends; the call allocates nothing (no hipMalloc,
  * hipFree or allocating routine; the per-kernel event timing records nothing
  * for it).  Sizes whose dspark_workspace_size(DSPARK_OP_DRAFT, ...) exceeds
@@ -172,7 +183,7 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
  * The array is that of the device current at the call, which must be the
  * device of `stream`.
  */
-dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const void* W2,
+dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const void* W2, const void* W2T,
                                           dspark_dtype wdtype, const int32_t* x0,
                                           int B, int gamma, int V, int r, float temperature,
                                           const uint64_t* seeds, uint64_t round,

@@ -67,10 +67,10 @@ def test_workspace_size(lib, op):
 
 
 def _draft(lib, **kw):
-    a = dict(U=FAKE, W1=FAKE, W2=FAKE, wd=1, x0=FAKE, B=4, gamma=4, V=1000, r=16, T=1.0, seeds=FAKE,
+    a = dict(U=FAKE, W1=FAKE, W2=FAKE, W2T=None, wd=1, x0=FAKE, B=4, gamma=4, V=1000, r=16, T=1.0, seeds=FAKE,
              rnd=0, tok=FAKE, prob=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30)
     a.update(kw)
-    return lib.dspark_markov_draft(a["U"], a["W1"], a["W2"], a["wd"], a["x0"], a["B"], a["gamma"], a["V"],
+    return lib.dspark_markov_draft(a["U"], a["W1"], a["W2"], a["W2T"], a["wd"], a["x0"], a["B"], a["gamma"], a["V"],
                                    a["r"], a["T"], a["seeds"], a["rnd"], a["tok"], a["prob"], a["lse"],
                                    a["ws"], a["wsb"], None)
 
@@ -81,16 +81,17 @@ def _draft(lib, **kw):
     (dict(T=float("inf")), INVALID), (dict(U=None), INVALID), (dict(W2=None), INVALID),
     (dict(tok=None), INVALID), (dict(seeds=None), INVALID), (dict(U=MISALIGNED), INVALID),
     (dict(ws=None), INVALID), (dict(wd=5), UNSUPPORTED), (dict(wsb=16), WORKSPACE),
+    (dict(W2T=MISALIGNED), INVALID), (dict(W2T=FAKE), INVALID),  # W2T may not alias W2
 ])
 def test_draft_rejects_bad_arguments(lib, kw, status):
     assert _draft(lib, **kw) == status
 
 
 def _draft_noalloc(lib, **kw):
-    a = dict(U=FAKE, W1=FAKE, W2=FAKE, wd=1, x0=FAKE, B=4, gamma=4, V=1000, r=16, T=1.0, seeds=FAKE,
+    a = dict(U=FAKE, W1=FAKE, W2=FAKE, W2T=None, wd=1, x0=FAKE, B=4, gamma=4, V=1000, r=16, T=1.0, seeds=FAKE,
              rnd=0, tok=FAKE, prob=FAKE, lse=FAKE)
     a.update(kw)
-    return lib.dspark_markov_draft_noalloc(a["U"], a["W1"], a["W2"], a["wd"], a["x0"], a["B"], a["gamma"],
+    return lib.dspark_markov_draft_noalloc(a["U"], a["W1"], a["W2"], a["W2T"], a["wd"], a["x0"], a["B"], a["gamma"],
                                            a["V"], a["r"], a["T"], a["seeds"], a["rnd"], a["tok"], a["prob"],
                                            a["lse"], None)
 
@@ -100,7 +101,7 @@ def _draft_noalloc(lib, **kw):
     (dict(T=-1.0), INVALID), (dict(U=None), INVALID), (dict(seeds=None), INVALID), (dict(U=MISALIGNED), INVALID),
     (dict(wd=5), UNSUPPORTED),
     # sizes whose draft workspace exceeds the static array: rejected on the host
-    (dict(B=4096, V=151936, r=256, gamma=7), SCRATCH), (dict(B=65536, V=8000, r=16), SCRATCH),
+    (dict(B=4096, V=151936, r=256, gamma=7), SCRATCH), (dict(B=65536, V=16000, r=16), SCRATCH),
 ])
 def test_draft_noalloc_rejects_bad_arguments_and_sizes_beyond_its_scratch(lib, kw, status):
     assert _draft_noalloc(lib, **kw) == status
@@ -108,7 +109,7 @@ def test_draft_noalloc_rejects_bad_arguments_and_sizes_beyond_its_scratch(lib, k
 
 def test_static_scratch_holds_the_timed_workloads(lib):
     cap = lib.dspark_static_scratch_bytes()
-    assert cap == 16 << 20
+    assert cap == 32 << 20
     for B, gamma, V in ((256, 7, 151936), (512, 7, 151936), (128, 7, 262144), (32, 7, 151936)):
         assert 0 < dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, 256) <= cap
     assert dsp.workspace_size(dsp.OP_DRAFT, 4096, 7, 151936, 256) > cap
@@ -135,9 +136,21 @@ def test_rnn_draft_rejects_bad_arguments(lib, kw, status):
 
 def test_rnn_draft_workspace_holds_the_state_and_operands():
     B, gamma, V, r = 256, 7, 151936, 256
-    extra = dsp.workspace_size(dsp.OP_RNN_DRAFT, B, gamma, V, r) - dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, r)
-    # float32 state (two buffers) and bf16 operand rows of 2r, less the ring operands
-    assert extra >= 2 * B * r * 4 + B * gamma * 2 * r * 2 - ((B + 255) // 256) * 256 * 512
+    need = dsp.workspace_size(dsp.OP_RNN_DRAFT, B, gamma, V, r)
+    # tile summaries and look-ahead uniforms, float32 state (two buffers),
+    # bf16 operand rows of 2r values
+    ntiles = (V + 127) // 128
+    assert need >= B * ntiles * 8 + 2 * B * 8 + 2 * B * r * 4 + B * gamma * 2 * r * 2
+
+
+def test_draft_workspace_holds_either_schedule_of_the_loop():
+    B, gamma, V, r = 256, 7, 151936, 256
+    need = dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, r)
+    # per-position launches: summaries, uniforms, ring operands
+    assert need >= B * ((V + 127) // 128) * 8 + 2 * B * 8 + B * 512
+    # the resident loop: range summaries (2048 per row), sub-block sums (40
+    # per row and workgroup), E rows, flags
+    assert need >= B * 2048 * 8 + B * 256 * 40 * 4 + B * 512 + 257 * 4
 
 
 def _verify(lib, **kw):

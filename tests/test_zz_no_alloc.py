@@ -54,11 +54,11 @@ def test_noalloc_draft_greedy_and_float32_weights():
 
 
 def test_noalloc_draft_rejects_sizes_beyond_its_scratch():
-    assert dsp.static_scratch_bytes() == 16 << 20
+    assert dsp.static_scratch_bytes() == 32 << 20
     U, W1, W2, x0, seeds = _inputs(4, 2, 256, 16, seed=5)
     # a workspace need above the array is refused on the host, before any launch
     lib = dsp.load()
-    st = lib.dspark_markov_draft_noalloc(U.data_ptr(), W1.data_ptr(), W2.data_ptr(), 1, x0.data_ptr(), 4096, 7,
+    st = lib.dspark_markov_draft_noalloc(U.data_ptr(), W1.data_ptr(), W2.data_ptr(), None, 1, x0.data_ptr(), 4096, 7,
                                          151936, 256, 1.0, seeds.data_ptr(), 0, x0.data_ptr(), U.data_ptr(),
                                          U.data_ptr(), None)
     assert st == -5
