@@ -4,36 +4,42 @@
 // The Markov Head", Eq. 5; the decode-round pseudocode's draft loop) in ONE
 // launch, with W2 held on chip for the whole call.
 //
-// One workgroup per compute unit (8 waves, two per SIMD), all co-resident
-// (cooperative launch).  The vocabulary is cut into 16-column sub-blocks and
-// every wave owns a contiguous range of at most five of them; the wave's
-// slice of W2 -- its columns for all r = 256 rows, up to 40 KB -- is loaded
-// once, from the vocabulary-major copy W2T, into MFMA operand registers (A
+// One workgroup of eight waves per compute unit, all co-resident
+// (cooperative launch).  All but kResSelWg of them are tile workgroups; the
+// others are selector workgroups.
+//
+// Tile workgroups.  The vocabulary is cut into 16-column sub-blocks and every
+// tile wave owns a contiguous range of at most five of them; the wave's slice
+// of W2 -- its columns for all r = 256 rows, up to 40 KB -- is loaded once,
+// from the vocabulary-major copy W2T, into MFMA operand registers (A
 // fragments of v_mfma_f32_16x16x32_bf16: lane l holds column l % 16 of a
 // sub-block, k = 8 (l / 16) .. + 7 of a 32-wide k step; 160 VGPRs) and stays
-// there for all positions.  Per position the only HBM stream is U_k.
+// there for all positions.  The loop runs over steps t = (position k,
+// 16-row group g), position-major: E rows of the group (the W1 rows of the
+// previous tokens, 8 KB, one DMA per wave) and each wave's U_k block (16
+// rows x its columns, 5 KB) arrive in LDS by global -> LDS DMA, U three
+// steps ahead and E two steps ahead; 40 MFMAs per wave form bias^T = W2^T E^T
+// for the wave's columns (exact bf16 products, fp32 accumulation); the
+// epilogue adds U and reduces each row of the wave's range to (max, sum of
+// 2^((l - max) log2(e) / T)) plus one partial sum per sub-block (argmax at
+// T = 0).  Per position the only HBM stream is U_k.
 //
-// Position k, per 16-row group g:
-//   E rows (the W1 rows of the previous tokens, 8 KB, one DMA per wave) and
-//   each wave's U_k block (16 rows x its columns, 5 KB) arrive in LDS by
-//   global -> LDS DMA, the U blocks three groups ahead and E two groups
-//   ahead; 40 MFMAs per wave form bias^T = W2^T E^T for the wave's columns
-//   (exact bf16 products, fp32 accumulation); the epilogue adds U and
-//   reduces each row of the wave's range to (max, sum of 2^((l - max)
-//   log2(e) / T)) plus one partial sum per sub-block (argmax at T = 0).
-// Between positions:
-//   barrier A (every range summary of position k written), the selection of
-//   each request's x_k by one wave (float64 search over the range summaries,
-//   then over the chosen range's sub-block sums, then a rescan of one
-//   16-column sub-block with W2T rows: the stream-0 inverse CDF), the store
-//   of W1[x_k] as the next position's E row, barrier B.  The other waves
-//   meanwhile DMA the first U blocks of position k + 1 (they do not depend
-//   on x_k).
-// Barriers are flag arrays (one word per workgroup, written with release
-// semantics at agent scope, polled by one wave with acquire semantics); every
-// wait is bounded in time, and a wait that times out sets an error word, the
-// workgroup drains its DMAs and exits, and a follow-up kernel marks every
-// request invalid (-1 / NaN), so no launch can hang.
+// The rows are split into two halves (the first ceil(G / 2) groups and the
+// rest).  A tile workgroup announces each finished half of a position on its
+// flag; the selector workgroups wait for all tile workgroups on a half, pick
+// that half's tokens (one wave per request: float64 search over the range
+// summaries, then over the chosen range's sub-block sums, then a rescan of
+// one 16-column sub-block with W2T rows -- the stream-0 inverse CDF) and
+// write W1[x_k] as the request's next E row, then announce the half on their
+// flags.  A tile workgroup checks those flags only before its first E DMA of
+// a half of the next position, so the selections of one half run while the
+// tiles stream the other half.
+//
+// Flags are words written with release semantics at agent scope and polled by
+// one wave with acquire semantics; every wait is bounded in time, and a wait
+// that times out sets an error word, the workgroup drains its DMAs and exits,
+// and a follow-up kernel marks every request invalid (-1 / NaN), so no launch
+// can hang.
 #include <math.h>
 
 #include "common.hpp"
@@ -55,23 +61,24 @@ constexpr int kResStages = 3;                       // U blocks in flight per wa
 constexpr int kResStageBytes = kResSub * 1024;      // one U block: 16 rows x 80 columns
 constexpr int kResWaveU = kResStages * kResStageBytes;
 constexpr int kResEBytes = kResKSteps * 1024;       // E rows of one group in fragment order
-constexpr int kResESlots = 3;                       // E(g) is issued two groups ahead
-constexpr int kResLdsE = kResWaves * kResWaveU;     // 120 KB of U stages before it
-constexpr int kResERegion = 32 * 1024;              // E slots (24 KB); the selections' stages between positions
-constexpr int kResSelStage = 16 * 1024;             // per selecting wave
-constexpr int kResSelWave = 1024;                   // per selecting wave: E row, uniforms
-constexpr int kResLdsSel = kResLdsE + kResERegion;
-constexpr int kResMaxRowsPerWg = 2;
-constexpr int kResLdsMisc = kResLdsSel + kResMaxRowsPerWg * kResSelWave;
+constexpr int kResESlots = 3;                       // E(t) is issued two steps ahead
+constexpr int kResLdsE = kResWaves * kResWaveU;     // tile: 120 KB of U stages, then the E slots
+constexpr int kResSelStage = 16 * 1024;             // selector: per wave, summaries then W2T rows
+constexpr int kResSelReq = 4;                       // selector: requests per wave (two per half)
+constexpr int kResLdsSelE = kResWaves * kResSelStage;  // selector: then their E rows
+constexpr int kResLdsMisc = 144 * 1024;
 constexpr int kResLds = kResLdsMisc + 64;
 constexpr int kResMaxWg = 256;
-constexpr int kResMaxNW = kResWaves * kResMaxWg;    // range summaries per row
+constexpr int kResSelWg = 16;                       // selector workgroups
+constexpr int kResSelWaves = kResSelWg * kResWaves;
+constexpr int kResMaxNW = kResWaves * kResMaxWg;    // range summaries per row (bound)
 constexpr int kResSumPerLane = kResMaxNW / kWave;   // 32
 constexpr int kResWgSub = kResWaves * kResSub;      // sub-block sums per row per workgroup (slots)
+constexpr int kResErr = kResMaxWg;                  // index of the error word among the flags
 
+static_assert(kResLdsE + kResESlots * kResEBytes <= kResLdsMisc, "tile LDS");
+static_assert(kResLdsSelE + kResWaves * kResSelReq * 512 <= kResLdsMisc, "selector LDS");
 static_assert(kResLds <= 160 * 1024, "LDS budget");
-static_assert(kResESlots * kResEBytes <= kResERegion, "E slots");
-static_assert(kResMaxRowsPerWg * kResSelStage <= kResERegion, "selection stages");
 
 struct ResArgs {
   const float* U;
@@ -80,16 +87,19 @@ struct ResArgs {
   const int32_t* x0;
   const uint64_t* seeds;
   uint64_t round;
-  int B, gamma, V, nsb, NW, G, rows_per_wg;
+  int B, gamma, V, nsb;
+  int nt;          // tile workgroups (the first nt of the grid)
+  int NW;          // tile waves: 8 nt
+  int G, G0;       // groups of 16 rows; the first half is groups [0, G0)
   float cf;        // log2(e) / T (0 at T == 0)
   double inv_t;    // 1 / T
   int32_t* tokens;
   float* prob;
   float* lse;
-  float2* part;    // [G][nwg][16][8]: range summaries; one workgroup writes 1 KB per group
-  float* ssum;     // [G][nwg][16][40]: sub-block sums (relative to the range maximum)
+  float2* part;    // [G][nt][16][8]: range summaries; one workgroup writes 1 KB per group
+  float* ssum;     // [G][nt][16][40]: sub-block sums (relative to the range maximum)
   uint16_t* eops;  // [B][256] W1 row of each request's previous token
-  uint32_t* flags; // [nwg] barrier phases, then the error word
+  uint32_t* flags; // [nt] tile phases, [nt, nt + kResSelWg) selector phases; [kResErr] the error word
   long long timeout;  // ticks of the 100 MHz real-time counter
 };
 
@@ -152,16 +162,17 @@ __device__ __forceinline__ void res_argmax_rows(float& v, int& c) {
   argmax_merge(v, c, __uint_as_float(rv[1]), (int)rc[1]);
 }
 
-// Barrier arrival: every wave of the workgroup has completed its stores
-// (the caller waited vmcnt(0) and passed a workgroup barrier); the release
-// makes them visible at agent scope before the phase number is.
-__device__ __forceinline__ void res_arrive(uint32_t* flags, int wg, uint32_t phase) {
-  __hip_atomic_store(flags + wg, phase, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+// Flag arrival: every wave of the workgroup has completed its stores (the
+// caller waited vmcnt(0) and passed a workgroup barrier); the release makes
+// them visible at agent scope before the phase number is.
+__device__ __forceinline__ void res_arrive(uint32_t* flag, uint32_t phase) {
+  __hip_atomic_store(flag, phase, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait (one wave) until every workgroup has reached `phase`; false on the
-// error word or on timeout (then the error word is set).  Acquire on success.
-__device__ bool res_wait_phase(uint32_t* flags, int nwg, uint32_t phase, long long timeout) {
+// Wait (one wave) until flags[0, n) all reach `phase` (n <= 256); false on
+// the error word or on timeout (then the error word is set).  Acquire on
+// success.
+__device__ bool res_wait_flags(const uint32_t* flags, int n, uint32_t phase, uint32_t* err, long long timeout) {
   const int lane = threadIdx.x & (kWave - 1);
   const long long t0 = res_clock();
   for (;;) {
@@ -170,16 +181,16 @@ __device__ bool res_wait_phase(uint32_t* flags, int nwg, uint32_t phase, long lo
 #pragma unroll
     for (int j = 0; j < kResMaxWg / kWave; ++j) {
       const int i = lane + j * kWave;
-      f[j] = i < nwg ? __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0xffffffffu;
+      f[j] = i < n ? __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0xffffffffu;
     }
-    const uint32_t err = __hip_atomic_load(flags + nwg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t mn = 0xffffffffu;
 #pragma unroll
     for (int j = 0; j < kResMaxWg / kWave; ++j) mn = f[j] < mn ? f[j] : mn;
     if (__ballot(mn < phase) == 0) break;
-    if (err != 0u) return false;
+    if (e != 0u) return false;
     if (res_clock() - t0 > timeout) {
-      if (lane == 0) __hip_atomic_store(flags + nwg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -189,8 +200,8 @@ __device__ bool res_wait_phase(uint32_t* flags, int nwg, uint32_t phase, long lo
 }
 
 // ---------------------------------------------------------------------------
-// Column ranges: wave gw (of NW) owns sub-blocks [sb0, sb0 + n) of the
-// V / 16, n <= kResSub.
+// Column ranges: tile wave gw (of NW) owns sub-blocks [sb0, sb0 + n) of
+// the V / 16, n <= kResSub.
 // ---------------------------------------------------------------------------
 struct Range {
   int sb0, n;
@@ -239,34 +250,18 @@ __device__ __forceinline__ void res_issue_e(const ResArgs& a, int g, uint32_t eb
   res_dma16(a.eops, off, ebuf + (uint32_t)(ks * 1024));
 }
 
-// The first U blocks of position k for all eight waves of the workgroup --
-// min(3, G) for waves 0-3, min(2, G) for waves 4-7, whose epilogues run one
-// step later -- issued by the waves [w0, 8) in turn.
-__device__ __forceinline__ void res_prefetch(const ResArgs& a, int k, int w0, uint32_t lds) {
-  const int wave = threadIdx.x / kWave;
-  const int np = kResWaves - w0;
-  const int nst = a.G < kResStages ? a.G : kResStages;
-  for (int item = wave - w0; item < kResWaves * nst; item += np) {
-    const int tw = item % kResWaves, g = item / kResWaves;
-    if (tw >= kResWaves / 2 && g == kResStages - 1) continue;
-    const Range rg = res_range(a, blockIdx.x * kResWaves + tw);
-    res_issue_u(a, rg, k, g, lds + (uint32_t)(tw * kResWaveU + (g % kResStages) * kResStageBytes));
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Selection of one request's token at position k by one wave.  `stage` (16
-// KB of the E region, idle between positions) receives the row's range
-// summaries and then the rescan's W2T rows.
+// Selection of one request's token at position k by one selector wave.
+// `erow` is the request's current E row (W1[x_{k-1}], 512 B of LDS), which
+// the call replaces with W1[x_k]; `stage` (16 KB of LDS) receives the row's
+// range summaries and then the rescan's W2T rows.
 // ---------------------------------------------------------------------------
 template <bool kGreedy>
-__device__ void res_select(const ResArgs& a, int b, int k, int& prev, unsigned char* sel, const unsigned char* stage,
+__device__ void res_select(const ResArgs& a, int b, int k, int& prev, unsigned char* erow, const unsigned char* stage,
                            uint32_t stage_lds) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int nwg = gridDim.x;
+  const int nwg = a.nt;
   const size_t out = (size_t)b * a.gamma + (k - 1);
-  const double* utab = reinterpret_cast<const double*>(sel + 512);
-  const unsigned char* erow = sel;
   if (prev < 0) {  // invalid anchor or earlier position
     if (lane == 0) {
       a.tokens[out] = -1;
@@ -334,7 +329,7 @@ __device__ void res_select(const ResArgs& a, int b, int k, int& prev, unsigned c
     }
     const double incl = wave_inclusive_scan_dpp(local);
     const double total = lane_f64(incl, kWave - 1);
-    const double u = utab[k - 1];
+    const double u = unit_uniform(draw_block(a.seeds[b], a.round, (uint64_t)k, kStreamDraft, 0).w[0]);
     const double q = u * total;
     const unsigned long long cross = __ballot(local > 0.0 && incl > q);
     const unsigned long long pos = __ballot(local > 0.0);
@@ -443,23 +438,30 @@ __device__ void res_select(const ResArgs& a, int b, int k, int& prev, unsigned c
   }
   prev = x;
   // W1[x] is the next position's E row: in the shared array for the tile
-  // passes and in this wave's LDS for its own rescan
+  // workgroups and in this wave's LDS for its own next rescan
   if (k < a.gamma) {
     const uint2 v = reinterpret_cast<const uint2*>(a.W1 + (size_t)x * kResR)[lane];
     reinterpret_cast<uint2*>(a.eops + (size_t)b * kResR)[lane] = v;
-    reinterpret_cast<uint2*>(sel)[lane] = v;
+    res_wait_lgkm0();  // the rescan's reads of the old row are done
+    reinterpret_cast<uint2*>(erow)[lane] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
-// The kernel.
+// Tile workgroups
 // ---------------------------------------------------------------------------
+// Phase of half h of position k on the flags: tile workgroups set it when
+// their summaries of the half are written; selector workgroups set 2 k + h + 1
+// when the half's tokens are chosen and its E rows for position k + 1 written
+// (2 after writing the E rows of position 1).  E rows of half h of position k
+// are ready once every selector flag is >= res_phase(k, h).
+__device__ __forceinline__ uint32_t res_phase(int k, int h) { return (uint32_t)(2 * (k - 1) + h + 1); }
+
 template <bool kGreedy>
-__global__ __launch_bounds__(kResThreads, 1) void draft_resident_kernel(ResArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
+__device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int wg = blockIdx.x, nt = a.nt;
   const int gw = wg * kResWaves + wave;
   const Range my = res_range(a, gw);
   const int cbase = my.n > 0 ? 16 * my.sb0 : 0;
@@ -469,14 +471,45 @@ __global__ __launch_bounds__(kResThreads, 1) void draft_resident_kernel(ResArgs 
   const uint32_t ebufs_l = lds + (uint32_t)kResLdsE;
   const unsigned char* ustage = smem + wave * kResWaveU;
   const unsigned char* ebufs = smem + kResLdsE;
-  const bool selw = wave < a.rows_per_wg;
-  const int mrow = wg + wave * nwg;  // the request this wave selects (if selw)
-  unsigned char* sel = smem + kResLdsSel + wave * kResSelWave;
   volatile int* ok_flag = reinterpret_cast<volatile int*>(smem + kResLdsMisc);
+  uint32_t* err = a.flags + kResErr;
+  const uint32_t* sel_flags = a.flags + nt;
+  const int G = a.G, G0 = a.G0, T = a.gamma * G;
+  const int n16 = lane & 15, q4 = lane >> 4;
 
-  // the first U blocks of position 1 (they depend on nothing) stream in
-  // while W2 is loaded
-  if (!selw) res_prefetch(a, 1, a.rows_per_wg, lds);
+  auto pos_of = [&](int t) { return t / G + 1; };
+  auto grp_of = [&](int t) { return t % G; };
+  auto half_of = [&](int g) { return g < G0 ? 0 : 1; };
+  // the last step of the half whose selections the E rows of step t need
+  // (-1 for position 1: its E rows are written before any step)
+  auto dep_of = [&](int t) {
+    const int k = pos_of(t), g = grp_of(t);
+    if (k == 1) return -1;
+    return (k - 2) * G + (half_of(g) == 0 ? G0 - 1 : G - 1);
+  };
+  // E(t) is issued at step t - 2 if the half it depends on ended before that
+  // step (or it depends on none), else at step t itself
+  auto e_early = [&](int t) { return pos_of(t) == 1 || dep_of(t) <= t - 3; };
+  uint32_t confirmed = 0;  // selector phase already observed by this workgroup (uniform)
+  // wave 0 waits for the E rows of step t (before the workgroup barrier that
+  // follows); false when the wait failed
+  auto check = [&](int t) -> bool {
+    const uint32_t need = res_phase(pos_of(t), half_of(grp_of(t)));
+    if (need <= confirmed) return true;
+    confirmed = need;
+    if (wave == 0) {
+      const bool ok = res_wait_flags(sel_flags, kResSelWg, need, err, a.timeout);
+      if (lane == 0) *ok_flag = ok ? 1 : 0;
+    }
+    return true;
+  };
+  auto e_slot = [&](int t) -> uint32_t { return ebufs_l + (uint32_t)((t % kResESlots) * kResEBytes); };
+  auto issue_e = [&](int t, bool real) { res_issue_e(a, grp_of(t), e_slot(t), real); };
+
+  if (threadIdx.x == 0) *ok_flag = 1;
+  // U of steps 0..2 stream in while W2 is loaded
+  for (int t = 0; t < kResStages; ++t)
+    res_issue_u(a, my, pos_of(t < T ? t : 0), grp_of(t < T ? t : 0), ustage_l + (uint32_t)(t * kResStageBytes), t < T);
 
   // the wave's slice of W2 as MFMA A fragments, for the whole call
   bf16x8 wf[kResSub][kResKSteps];
@@ -488,205 +521,219 @@ __global__ __launch_bounds__(kResThreads, 1) void draft_resident_kernel(ResArgs 
     for (int ks = 0; ks < kResKSteps; ++ks) wf[s][ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
   }
 
-  // selecting waves: uniforms of every position, the first E row
-  int prev = -1;
-  if (selw && mrow < a.B) {
-    double* utab = reinterpret_cast<double*>(sel + 512);
-    if constexpr (!kGreedy) {
-      if (lane < a.gamma)
-        utab[lane] = unit_uniform(draw_block(a.seeds[mrow], a.round, lane + 1, kStreamDraft, 0).w[0]);
-    }
-    const int x0 = a.x0[mrow];
-    prev = (unsigned)x0 < (unsigned)a.V ? x0 : -1;
-    uint2 v = make_uint2(0u, 0u);
-    if (prev >= 0) v = reinterpret_cast<const uint2*>(a.W1 + (size_t)prev * kResR)[lane];
-    reinterpret_cast<uint2*>(a.eops + (size_t)mrow * kResR)[lane] = v;
-    reinterpret_cast<uint2*>(sel)[lane] = v;
-  }
-  res_wait_vmem<0>();
-  __syncthreads();
-  if (threadIdx.x == 0) res_arrive(a.flags, wg, 1u);
-  if (wave == 0) {
-    const bool ok = res_wait_phase(a.flags, nwg, 1u, a.timeout);
-    if (lane == 0) *ok_flag = ok ? 1 : 0;
-  }
+  // E of steps 0 and 1
+  check(0);
+  if (T > 1 && e_early(1)) check(1);
   __syncthreads();
   if (!*ok_flag) {
     res_wait_vmem<0>();
     return;
   }
+  issue_e(0, true);
+  issue_e(1, T > 1 && e_early(1));
 
-  const int G = a.G;
-  // E(0) and E(1) of a position are issued at its start, E(g + 2) at the
-  // start of step g (three slots), so that the wait for E(g) leaves the U
-  // blocks issued after it in flight
-  auto e_slot = [&](int g) -> uint32_t { return ebufs_l + (uint32_t)((g % kResESlots) * kResEBytes); };
-  res_issue_e(a, 0, e_slot(0));
-  res_issue_e(a, 1, e_slot(1), G > 1);
+  for (int t = 0; t < T; ++t) {
+    const int k = pos_of(t), g = grp_of(t);
+    // E(t) and this wave's U block of step t have landed.  Issue order per
+    // step: one E DMA at its start (E(t + 2), real or not), 5 U DMAs (U of
+    // step t + 3, real or not) and the summary stores; so after E(t) come E(1)
+    // at t = 0, 1 + 5 at t = 1 and 5 + 1 + 5 at t >= 2.  U(t) is issued
+    // before E(t).  An E issued late (at its own step) is waited for there,
+    // and flag waits drain everything: both only make these counts safer.
+    __builtin_amdgcn_sched_barrier(0);
+    if (t == 0) {
+      res_wait_vmem<1>();
+    } else if (t == 1) {
+      res_wait_vmem<kResSub + 1>();
+    } else {
+      res_wait_vmem<2 * kResSub + 1>();
+    }
+    const bool late = !e_early(t);
+    if (late) check(t);
+    if (t + 2 < T && e_early(t + 2)) check(t + 2);
+    __syncthreads();
+    if (!*ok_flag) {
+      res_wait_vmem<0>();
+      return;
+    }
+    if (late) {
+      issue_e(t, true);
+      res_wait_vmem<0>();
+      __syncthreads();
+    }
+    issue_e(t + 2, t + 2 < T && e_early(t + 2));
 
-  const int n16 = lane & 15, q4 = lane >> 4;
-  // Waves w and w + 4 share a SIMD.  In step g, waves 0-3 form the products
-  // of group g and then finish it (the epilogue), while waves 4-7 first
-  // finish group g - 1 (whose products they formed in step g - 1) and then
-  // form the products of group g: on each SIMD one wave's MFMAs overlap the
-  // other's vector work.  Waves 4-7 take one more step per position.
-  const bool products_first = wave < kResWaves / 2;
-  for (int k = 1; k <= a.gamma; ++k) {
+    // bias^T of the wave's columns for the group's 16 rows
     f32x4 acc[kResSub];
-    for (int g = 0; g <= G; ++g) {
-      // E(g) and the U block this step's epilogue reads (U(k, e), e = g for
-      // waves 0-3 and g - 1 for waves 4-7) have landed.  Issue order per
-      // step g < G, the same for every wave: E(g + 2) (1 DMA) at its start,
-      // U(k, e + 3) (5 DMAs) right after the epilogue has read U(k, e), real
-      // or not, and summary stores; E(0), E(1) at the position start and
-      // U(k, 0), U(k, 1) (and U(k, 2) for waves 0-3) before it, by some wave
-      // of the workgroup, all of which wait for them here at step 0.  So
-      // after E(g) come E(1) at step 0, 1 + 5 at step 1 and 5 + 1 + 5 at steps
-      // g >= 2, and U(k, e) is issued before E(g).
-      __builtin_amdgcn_sched_barrier(0);
-      if (g == 0) {
-        res_wait_vmem<1>();
-      } else if (g == 1) {
-        res_wait_vmem<kResSub + 1>();
-      } else {
-        res_wait_vmem<2 * kResSub + 1>();
+    {
+      const unsigned char* ebuf = ebufs + (t % kResESlots) * kResEBytes;
+      bf16x8 ev[kResKSteps];
+#pragma unroll
+      for (int ks = 0; ks < kResKSteps; ++ks) ev[ks] = *reinterpret_cast<const bf16x8*>(ebuf + ks * 1024 + 16 * lane);
+#pragma unroll
+      for (int s = 0; s < kResSub; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < kResKSteps; ++ks) {
+#pragma unroll
+        for (int s = 0; s < kResSub; ++s)
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s][ks], ev[ks], acc[s], 0, 0, 0);
+      }
+      // schedule: the eight LDS reads, then the MFMAs five at a time (left
+      // alone, the scheduler re-reads one fragment per k step to save
+      // registers)
+      __builtin_amdgcn_sched_group_barrier(0x100, kResKSteps, 0);
+#pragma unroll
+      for (int ks = 0; ks < kResKSteps; ++ks) __builtin_amdgcn_sched_group_barrier(0x008, kResSub, 0);
+    }
+
+    // epilogue: acc[s][i] + U is the logit of row 16 g + l % 16, column
+    // 16 (sb0 + s) + 4 (l / 16) + i (U added to the finished bias, not
+    // accumulated through it: the float32 rounding then stays at the bias's
+    // magnitude, as in the selection's rescan).  Sub-blocks past the range
+    // repeat sub-block 0 (same columns, same values): they leave maxima
+    // unchanged and are dropped from sums.
+    {
+      const unsigned char* ub = ustage + (t % kResStages) * kResStageBytes;
+#pragma unroll
+      for (int s = 0; s < kResSub; ++s) {
+        const float4 u = *reinterpret_cast<const float4*>(ub + s * 1024 + 16 * lane);
+        acc[s][0] += u.x;
+        acc[s][1] += u.y;
+        acc[s][2] += u.z;
+        acc[s][3] += u.w;
+      }
+      res_wait_lgkm0();
+      // U of step t + 3 into the stage just read
+      const int tn = t + kResStages;
+      res_issue_u(a, my, pos_of(tn < T ? tn : 0), grp_of(tn < T ? tn : 0),
+                  ustage_l + (uint32_t)((t % kResStages) * kResStageBytes), tn < T);
+    }
+    const int row = kResRows * g + n16;
+    const bool rowok = row < a.B;
+    const uint32_t pidx = (((uint32_t)g * (uint32_t)nt + (uint32_t)wg) * 16u + (uint32_t)n16) * 8u + (uint32_t)wave;
+    if constexpr (kGreedy) {
+      float bv = -__builtin_inff();
+      int bc = 0x7fffffff;
+#pragma unroll
+      for (int s = 0; s < kResSub; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // ascending columns within the lane and strict comparison: the
+          // lowest index wins ties, and a repeated sub-block never wins
+          const bool better = acc[s][i] > bv;
+          bv = better ? acc[s][i] : bv;
+          bc = better ? cbase + 16 * s + 4 * q4 + i : bc;
+        }
+      }
+      res_argmax_rows(bv, bc);
+      if (my.n == 0) bv = -__builtin_inff(), bc = 0x7fffffff;
+      if (lane < 16 && rowok) a.part[pidx] = make_float2(bv, __int_as_float(bc));
+    } else {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int s = 0; s < kResSub; ++s) m = fmaxf(m, fmaxf(fmaxf(acc[s][0], acc[s][1]), fmaxf(acc[s][2], acc[s][3])));
+      m = res_max_rows(m);  // the row's maximum over the four lanes that hold it
+      // with m = -inf every logit is -inf and every term 2^-inf = 0
+      const float mc = m == -__builtin_inff() ? 0.0f : m * a.cf;
+      float bp[kResSub];
+#pragma unroll
+      for (int s = 0; s < kResSub; ++s) {
+        const float v = (fast_exp2(fmaf(acc[s][0], a.cf, -mc)) + fast_exp2(fmaf(acc[s][1], a.cf, -mc))) +
+                        (fast_exp2(fmaf(acc[s][2], a.cf, -mc)) + fast_exp2(fmaf(acc[s][3], a.cf, -mc)));
+        bp[s] = res_sum_rows(s < my.n ? v : 0.0f);
+      }
+      const float S = (((bp[0] + bp[1]) + bp[2]) + bp[3]) + bp[4];
+      if (lane < 16 && rowok) a.part[pidx] = make_float2(my.n > 0 ? m : -__builtin_inff(), S);
+      const float bq = q4 == 0 ? bp[0] : q4 == 1 ? bp[1] : q4 == 2 ? bp[2] : bp[3];
+      const uint32_t so =
+          (((uint32_t)g * (uint32_t)nt + (uint32_t)wg) * 16u + (uint32_t)n16) * kResWgSub + (uint32_t)myloc;
+      if (rowok && q4 < my.n) a.ssum[so + (uint32_t)q4] = bq;
+      if (rowok && q4 == 0 && my.n > 4) a.ssum[so + 4u] = bp[4];
+    }
+
+    // the end of a half: announce it (an empty second half with the first)
+    if (g == G0 - 1 || g == G - 1) {
+      res_wait_vmem<0>();
+      __syncthreads();
+      if (threadIdx.x == 0) res_arrive(a.flags + wg, res_phase(k, g == G - 1 ? 1 : 0));
+    }
+  }
+  res_wait_vmem<0>();
+}
+
+// ---------------------------------------------------------------------------
+// Selector workgroups
+// ---------------------------------------------------------------------------
+// Selector wave sw (of kResSelWaves) owns, in half h, the requests
+// R_h + sw + i kResSelWaves (i = 0, 1) below R_{h + 1}, with R_0 = 0,
+// R_1 = min(B, 16 G0), R_2 = B.
+template <bool kGreedy>
+__device__ void res_selector(const ResArgs& a, unsigned char* smem) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int sw = (blockIdx.x - a.nt) * kResWaves + wave;
+  const uint32_t lds = res_lds_base(smem);
+  unsigned char* stage = smem + wave * kResSelStage;
+  const uint32_t stage_l = lds + (uint32_t)(wave * kResSelStage);
+  volatile int* ok_flag = reinterpret_cast<volatile int*>(smem + kResLdsMisc);
+  uint32_t* err = a.flags + kResErr;
+  uint32_t* my_flag = a.flags + a.nt + (blockIdx.x - a.nt);
+  const int R1 = a.B < kResRows * a.G0 ? a.B : kResRows * a.G0;
+  auto req = [&](int h, int i) { return (h == 0 ? 0 : R1) + sw + i * kResSelWaves; };
+  auto live = [&](int h, int i) { return req(h, i) < (h == 0 ? R1 : a.B); };
+  auto erow = [&](int h, int i) { return smem + kResLdsSelE + (wave * kResSelReq + 2 * h + i) * 512; };
+
+  // E rows of position 1: W1[x_0] (zero rows for invalid anchors)
+  int prev[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      prev[h][i] = -1;
+      if (live(h, i)) {
+        const int b = req(h, i);
+        const int x0 = a.x0[b];
+        prev[h][i] = (unsigned)x0 < (unsigned)a.V ? x0 : -1;
+        uint2 v = make_uint2(0u, 0u);
+        if (prev[h][i] >= 0) v = reinterpret_cast<const uint2*>(a.W1 + (size_t)prev[h][i] * kResR)[lane];
+        reinterpret_cast<uint2*>(a.eops + (size_t)b * kResR)[lane] = v;
+        reinterpret_cast<uint2*>(erow(h, i))[lane] = v;
+      }
+    }
+  }
+  res_wait_vmem<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) res_arrive(my_flag, 2u);
+
+  for (int k = 1; k <= a.gamma; ++k) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wave == 0) {
+        const bool ok = res_wait_flags(a.flags, a.nt, res_phase(k, h), err, a.timeout);
+        if (lane == 0) *ok_flag = ok ? 1 : 0;
       }
       __syncthreads();
-      if (g < G) res_issue_e(a, g + 2, e_slot(g + 2), g + 2 < G);
-
-      // bias^T of the wave's columns for the 16 rows of group g
-      auto products = [&]() {
-        const unsigned char* ebuf = ebufs + (g % kResESlots) * kResEBytes;
-        // all eight E fragments are requested at once (32 VGPRs), so the
-        // LDS latency is paid once and the MFMAs of k step ks start as soon
-        // as its fragment is in
-        bf16x8 ev[kResKSteps];
-#pragma unroll
-        for (int ks = 0; ks < kResKSteps; ++ks) ev[ks] = *reinterpret_cast<const bf16x8*>(ebuf + ks * 1024 + 16 * lane);
-#pragma unroll
-        for (int s = 0; s < kResSub; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < kResKSteps; ++ks) {
-#pragma unroll
-          for (int s = 0; s < kResSub; ++s)
-            acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s][ks], ev[ks], acc[s], 0, 0, 0);
-        }
-        // schedule: the eight LDS reads, then the 40 MFMAs (left alone, the
-        // scheduler re-reads one fragment per k step to save registers)
-        __builtin_amdgcn_sched_group_barrier(0x100, kResKSteps, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, kResKSteps * kResSub, 0);
-      };
-      // U(k, e + 3) into the stage of U(k, e) once this wave has read it
-      auto issue_u = [&](int e) {
-        if (g < G)
-          res_issue_u(a, my, k, e + kResStages, ustage_l + (uint32_t)(((e + kResStages) % kResStages) * kResStageBytes),
-                      e + kResStages < G);
-      };
-      // group e: acc[s][i] + U is the logit of row 16 e + l % 16,
-      // column 16 (sb0 + s) + 4 (l / 16) + i (U added to the finished bias,
-      // not accumulated through it: the float32 rounding then stays at the
-      // bias's magnitude, as in the selection's rescan).  Sub-blocks past the
-      // range repeat sub-block 0 (same columns, same values): they leave
-      // maxima unchanged and are dropped from sums.
-      auto epilogue = [&](int gp) {
-        const unsigned char* ub = ustage + (gp % kResStages) * kResStageBytes;
-#pragma unroll
-        for (int s = 0; s < kResSub; ++s) {
-          const float4 u = *reinterpret_cast<const float4*>(ub + s * 1024 + 16 * lane);
-          acc[s][0] += u.x;
-          acc[s][1] += u.y;
-          acc[s][2] += u.z;
-          acc[s][3] += u.w;
-        }
-        res_wait_lgkm0();
-        issue_u(gp);
-        const int row = kResRows * gp + n16;
-        const bool rowok = row < a.B;
-        const uint32_t pidx =
-            (((uint32_t)gp * (uint32_t)nwg + (uint32_t)wg) * 16u + (uint32_t)n16) * 8u + (uint32_t)wave;
-        if constexpr (kGreedy) {
-          float bv = -__builtin_inff();
-          int bc = 0x7fffffff;
-#pragma unroll
-          for (int s = 0; s < kResSub; ++s) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // ascending columns within the lane and strict comparison: the
-              // lowest index wins ties, and a repeated sub-block never wins
-              const bool better = acc[s][i] > bv;
-              bv = better ? acc[s][i] : bv;
-              bc = better ? cbase + 16 * s + 4 * q4 + i : bc;
-            }
-          }
-          res_argmax_rows(bv, bc);
-          if (my.n == 0) bv = -__builtin_inff(), bc = 0x7fffffff;
-          if (lane < 16 && rowok) a.part[pidx] = make_float2(bv, __int_as_float(bc));
-        } else {
-          float m = -__builtin_inff();
-#pragma unroll
-          for (int s = 0; s < kResSub; ++s)
-            m = fmaxf(m, fmaxf(fmaxf(acc[s][0], acc[s][1]), fmaxf(acc[s][2], acc[s][3])));
-          m = res_max_rows(m);  // the row's maximum over the four lanes that hold it
-          // with m = -inf every logit is -inf and every term 2^-inf = 0
-          const float mc = m == -__builtin_inff() ? 0.0f : m * a.cf;
-          float bp[kResSub];
-#pragma unroll
-          for (int s = 0; s < kResSub; ++s) {
-            const float v = (fast_exp2(fmaf(acc[s][0], a.cf, -mc)) + fast_exp2(fmaf(acc[s][1], a.cf, -mc))) +
-                            (fast_exp2(fmaf(acc[s][2], a.cf, -mc)) + fast_exp2(fmaf(acc[s][3], a.cf, -mc)));
-            bp[s] = res_sum_rows(s < my.n ? v : 0.0f);
-          }
-          const float S = (((bp[0] + bp[1]) + bp[2]) + bp[3]) + bp[4];
-          if (lane < 16 && rowok) a.part[pidx] = make_float2(my.n > 0 ? m : -__builtin_inff(), S);
-          const float bq = q4 == 0 ? bp[0] : q4 == 1 ? bp[1] : q4 == 2 ? bp[2] : bp[3];
-          const uint32_t so =
-              (((uint32_t)gp * (uint32_t)nwg + (uint32_t)wg) * 16u + (uint32_t)n16) * kResWgSub + (uint32_t)myloc;
-          if (rowok && q4 < my.n) a.ssum[so + (uint32_t)q4] = bq;
-          if (rowok && q4 == 0 && my.n > 4) a.ssum[so + 4u] = bp[4];
-        }
-      };
-      if (products_first) {
-        if (g < G) {
-          products();
-          epilogue(g);
-        }
-      } else {
-        if (g > 0) epilogue(g - 1); else issue_u(-1);
-        if (g < G) products();
+      if (!*ok_flag) {
+        res_wait_vmem<0>();
+        return;
       }
-    }
-
-    // ---- between positions: barrier A, selection, barrier B
-    res_wait_vmem<0>();
-    __syncthreads();
-    if (threadIdx.x == 0) res_arrive(a.flags, wg, (uint32_t)(2 * k));
-    if (!selw && k < a.gamma) res_prefetch(a, k + 1, a.rows_per_wg, lds);
-    if (selw) {
-      const bool ok = res_wait_phase(a.flags, nwg, (uint32_t)(2 * k), a.timeout);
-      if (!ok && lane == 0) *ok_flag = 0;
-      const int sw = wave * kResSelStage;
-      if (ok && mrow < a.B) res_select<kGreedy>(a, mrow, k, prev, sel, ebufs + sw, ebufs_l + (uint32_t)sw);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (live(h, i)) res_select<kGreedy>(a, req(h, i), k, prev[h][i], erow(h, i), stage, stage_l);
       res_wait_vmem<0>();
+      __syncthreads();
+      if (threadIdx.x == 0) res_arrive(my_flag, (uint32_t)(2 * k + h + 1));
     }
-    __syncthreads();
-    if (!*ok_flag) {
-      res_wait_vmem<0>();
-      return;
-    }
-    if (k == a.gamma) break;
-    if (threadIdx.x == 0) res_arrive(a.flags, wg, (uint32_t)(2 * k + 1));
-    if (wave == 0) {
-      const bool ok = res_wait_phase(a.flags, nwg, (uint32_t)(2 * k + 1), a.timeout);
-      if (lane == 0) *ok_flag = ok ? 1 : 0;
-    }
-    __syncthreads();
-    if (!*ok_flag) {
-      res_wait_vmem<0>();
-      return;
-    }
-    res_issue_e(a, 0, e_slot(0));
-    res_issue_e(a, 1, e_slot(1), G > 1);
   }
+}
+
+template <bool kGreedy>
+__global__ __launch_bounds__(kResThreads, 1) void draft_resident_kernel(ResArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if ((int)blockIdx.x < a.nt)
+    res_tile<kGreedy>(a, smem);
+  else
+    res_selector<kGreedy>(a, smem);
 }
 
 // Outputs of every request become invalid (-1 / NaN) when the resident loop
@@ -746,11 +793,11 @@ static hipError_t res_prepare(int& max_blocks) {
 bool resident_draft_applies(const DraftArgs& a, bool bf16) {
   if (!bf16 || a.W2T == nullptr || a.r != kResR || a.V % 16 != 0) return false;
   const int nwg = compute_units_of_device();
-  if (nwg < 1 || nwg > kResMaxWg) return false;
-  const long long NW = (long long)nwg * kResWaves;
+  if (nwg > kResMaxWg || nwg <= kResSelWg) return false;
+  const long long NW = (long long)(nwg - kResSelWg) * kResWaves;
   const long long nsb = a.V / 16;
-  if ((nsb + NW - 1) / NW > kResSub) return false;               // W2 slice fits the registers
-  if ((a.B + nwg - 1) / nwg > kResMaxRowsPerWg) return false;    // selections per workgroup
+  if ((nsb + NW - 1) / NW > kResSub) return false;                     // W2 slice fits the registers
+  if ((long long)a.B > 2LL * 2 * kResSelWaves) return false;           // two requests per selector wave per half
   if ((double)a.B * a.gamma * a.V * 4.0 >= 4294967296.0) return false;  // 32-bit DMA offsets
   return true;
 }
@@ -778,9 +825,10 @@ hipError_t launch_resident_draft(const DraftArgs& d, hipStream_t s, bool* launch
   a.gamma = d.gamma;
   a.V = d.V;
   a.nsb = d.V / 16;
-  a.NW = nwg * kResWaves;
+  a.nt = nwg - kResSelWg;
+  a.NW = a.nt * kResWaves;
   a.G = (d.B + kResRows - 1) / kResRows;
-  a.rows_per_wg = (d.B + nwg - 1) / nwg;
+  a.G0 = (a.G + 1) / 2;
   a.cf = greedy ? 0.0f : (float)(1.4426950408889634 / (double)d.temperature);
   a.inv_t = greedy ? 0.0 : 1.0 / (double)d.temperature;
   a.tokens = d.tokens;
@@ -793,7 +841,7 @@ hipError_t launch_resident_draft(const DraftArgs& d, hipStream_t s, bool* launch
   a.timeout = 20000000;  // 0.2 s at 100 MHz: orders of magnitude above a normal wait
   {
     ProfScope prof(s, kProfResidentDraft);
-    hipLaunchKernelGGL(resident_clear_kernel, dim3(1), dim3(256), 0, s, a.flags, nwg + 1);
+    hipLaunchKernelGGL(resident_clear_kernel, dim3(1), dim3(256), 0, s, a.flags, kResMaxWg + 1);
     void* args[] = {&a};
     e = hipLaunchCooperativeKernel(greedy ? (const void*)draft_resident_kernel<true>
                                           : (const void*)draft_resident_kernel<false>,
@@ -805,7 +853,7 @@ hipError_t launch_resident_draft(const DraftArgs& d, hipStream_t s, bool* launch
     *launched = true;
     const int n = d.B * d.gamma;
     hipLaunchKernelGGL(resident_fixup_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0,
-                       s, a.flags + nwg, d.tokens, d.prob, d.lse, n);
+                       s, a.flags + kResErr, d.tokens, d.prob, d.lse, n);
   }
   return hipGetLastError();
 }

@@ -148,9 +148,8 @@ def test_draft_workspace_holds_either_schedule_of_the_loop():
     need = dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, r)
     # per-position launches: summaries, uniforms, ring operands
     assert need >= B * ((V + 127) // 128) * 8 + 2 * B * 8 + B * 512
-    # the resident loop: range summaries (2048 per row), sub-block sums (40
-    # per row and workgroup), E rows, flags
-    assert need >= B * 2048 * 8 + B * 256 * 40 * 4 + B * 512 + 257 * 4
+    # the resident loop: range summaries (2048 per row), E rows, flags
+    assert need >= B * 2048 * 8 + B * 512 + 257 * 4
 
 
 def _verify(lib, **kw):

@@ -7,7 +7,7 @@ compares tokens, draft_prob and draft_lse with the float64 oracle to the
 parity bar.
 
 Cases: vocabularies with most waves' column ranges empty (V = 8192) and with
-every range full (V = 163840), ragged last row groups, two selections per
+every range full (V = 153600), ragged last row groups, two selections per
 workgroup (B > 256), greedy, invalid anchors,
 determinism, and the full-size workloads whose draft the benchmark times --
 every request of V=151936 B=256 T=0.7 and B=32, and every request of the
@@ -60,7 +60,7 @@ def resident_draft(d, wl, W2T, rnd=None, x0=None):
 SMALL = [
     ("v151936_b256_t07", dict(B=16, V=8192, gamma=4)),      # most column ranges empty
     ("v151936_b32", dict(B=40, V=40960, gamma=3)),           # ragged last group of 16 rows
-    ("v151936_b32", dict(B=7, V=163840, gamma=2)),           # five 16-column sub-blocks in every range
+    ("v151936_b32", dict(B=7, V=153600, gamma=2)),           # five 16-column sub-blocks in every range
     ("v151936_b256_t07", dict(B=300, V=16384, gamma=2)),     # two selections per workgroup
     ("greedy_v151936_b512", dict(B=24, V=16384, gamma=3)),
     ("greedy_v151936_b512", dict(B=300, V=8192, gamma=2)),
