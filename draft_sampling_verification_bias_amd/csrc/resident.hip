@@ -27,9 +27,11 @@
 // The rows are split into two halves (the first ceil(G / 2) groups and the
 // rest).  A tile workgroup announces each finished half of a position on its
 // flag; the selector workgroups wait for all tile workgroups on a half, pick
-// that half's tokens (one wave per request: float64 search over the range
-// summaries, then over the chosen range's sub-block sums, then a rescan of
-// one 16-column sub-block with W2T rows -- the stream-0 inverse CDF) and
+// that half's tokens (one wave per request: float64 search over the row's
+// range summaries grouped by tile workgroup, then over the chosen
+// workgroup's eight ranges and the chosen range's sub-block sums, then a
+// rescan of one 16-column sub-block with W2T rows -- the stream-0 inverse
+// CDF) and
 // write W1[x_k] as the request's next E row, then announce the half on their
 // flags.  A tile workgroup checks those flags only before its first E DMA of
 // a half of the next position, so the selections of one half run while the
@@ -66,8 +68,12 @@ constexpr int kResLdsE = kResWaves * kResWaveU;     // tile: 120 KB of U stages,
 constexpr int kResSelStage = 16 * 1024;             // selector: per wave, summaries then W2T rows
 constexpr int kResSelReq = 4;                       // selector: requests per wave (two per half)
 constexpr int kResLdsSelE = kResWaves * kResSelStage;  // selector: then their E rows
-constexpr int kResLdsMisc = 144 * 1024;
+constexpr int kResLdsCtlU = 144 * 1024;              // tile: the fourth U stage of the control wave
+constexpr int kResLdsMisc = kResLdsCtlU + kResStageBytes;  // the ok word
 constexpr int kResLds = kResLdsMisc + 64;
+constexpr int kResCtl = kResWaves - 1;              // tile: the control wave (no DMAs of its own)
+constexpr int kResEHelper = kResSub;                // tile: issues the control wave's E chunk
+static_assert(kResSub < kResCtl && kResEHelper < kResCtl, "helpers of the control wave");
 constexpr int kResMaxWg = 256;
 constexpr int kResSelWg = 16;                       // selector workgroups
 constexpr int kResSelWaves = kResSelWg * kResWaves;
@@ -76,7 +82,7 @@ constexpr int kResSumPerLane = kResMaxNW / kWave;   // 32
 constexpr int kResWgSub = kResWaves * kResSub;      // sub-block sums per row per workgroup (slots)
 constexpr int kResErr = kResMaxWg;                  // index of the error word among the flags
 
-static_assert(kResLdsE + kResESlots * kResEBytes <= kResLdsMisc, "tile LDS");
+static_assert(kResLdsE + kResESlots * kResEBytes <= kResLdsCtlU, "tile LDS");
 static_assert(kResLdsSelE + kResWaves * kResSelReq * 512 <= kResLdsMisc, "selector LDS");
 static_assert(kResLds <= 160 * 1024, "LDS budget");
 
@@ -162,11 +168,29 @@ __device__ __forceinline__ void res_argmax_rows(float& v, int& c) {
   argmax_merge(v, c, __uint_as_float(rv[1]), (int)rc[1]);
 }
 
-// Flag arrival: every wave of the workgroup has completed its stores (the
-// caller waited vmcnt(0) and passed a workgroup barrier); the release makes
-// them visible at agent scope before the phase number is.
+// Data that crosses workgroups (summaries, E rows) is written with
+// agent-scope stores, which write through to the device's coherence point:
+// once such a store has completed (vmcnt), every agent-scope reader that
+// acquires afterwards sees it, without an L2 write-back.
+__device__ __forceinline__ void res_put(float2* p, float2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                     ((unsigned long long)__float_as_uint(v.y) << 32) | __float_as_uint(v.x), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void res_put(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void res_put(uint2* p, uint2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), ((unsigned long long)v.y << 32) | v.x,
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Flag arrival: every store the flag publishes was made with res_put and has
+// completed (the caller made sure of it, for every wave of the workgroup,
+// before a workgroup barrier), so a plain agent-scope store of the phase
+// suffices: no write-back of the L2 and no wait for this wave's DMAs.
 __device__ __forceinline__ void res_arrive(uint32_t* flag, uint32_t phase) {
-  __hip_atomic_store(flag, phase, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(flag, phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait (one wave) until flags[0, n) all reach `phase` (n <= 256); false on
@@ -207,10 +231,11 @@ struct Range {
   int sb0, n;
 };
 
+// (gw + 1) nsb <= NW * 5 NW < 2^32: 32-bit unsigned arithmetic is exact
 __device__ __forceinline__ Range res_range(const ResArgs& a, int gw) {
   Range r;
-  r.sb0 = (int)((long long)gw * a.nsb / a.NW);
-  r.n = (int)((long long)(gw + 1) * a.nsb / a.NW) - r.sb0;
+  r.sb0 = (int)((uint32_t)gw * (uint32_t)a.nsb / (uint32_t)a.NW);
+  r.n = (int)((uint32_t)(gw + 1) * (uint32_t)a.nsb / (uint32_t)a.NW) - r.sb0;
   return r;
 }
 
@@ -238,16 +263,30 @@ __device__ __forceinline__ void res_issue_u(const ResArgs& a, Range rg, int k, i
   }
 }
 
-// E rows of group g (the previous tokens' W1 rows): k step ks = wave, from
-// lane l row 16 g + l % 16, k = 32 ks + 8 (l / 16) .. + 7.  real == false as
-// for res_issue_u (the first 16 bytes of the E rows).
-__device__ __forceinline__ void res_issue_e(const ResArgs& a, int g, uint32_t ebuf, bool real = true) {
+// Sub-block s of the same U block (one DMA).
+__device__ __forceinline__ void res_issue_u1(const ResArgs& a, Range rg, int k, int g, uint32_t stage, bool real,
+                                             int s) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int ks = threadIdx.x / kWave;
   int row = kResRows * g + (lane & 15);
   row = row < a.B ? row : a.B - 1;
-  const uint32_t off = real ? ((uint32_t)row * kResR + 32u * ks + 8u * (lane >> 4)) * 2u : 0u;
-  res_dma16(a.eops, off, ebuf + (uint32_t)(ks * 1024));
+  const int cbase = rg.n > 0 ? 16 * rg.sb0 : 0;
+  const int se = s < rg.n ? s : 0;
+  const uint32_t rowoff = (uint32_t)row * (uint32_t)a.gamma * (uint32_t)a.V + (uint32_t)(k - 1) * (uint32_t)a.V;
+  const uint32_t off = real ? (rowoff + (uint32_t)(cbase + 16 * se + 4 * (lane >> 4))) * 4u : 0u;
+  res_dma16(a.U, off, stage + (uint32_t)(s * 1024));
+}
+
+// E rows of group g (the previous tokens' W1 rows): k steps ks0 .. ks0 +
+// nks - 1, from lane l row 16 g + l % 16, k = 32 ks + 8 (l / 16) .. + 7.
+// real == false as for res_issue_u (the first 16 bytes of the E rows).
+__device__ __forceinline__ void res_issue_e(const ResArgs& a, int g, uint32_t ebuf, bool real, int ks0, int nks) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int row = kResRows * g + (lane & 15);
+  row = row < a.B ? row : a.B - 1;
+  for (int ks = ks0; ks < ks0 + nks; ++ks) {
+    const uint32_t off = real ? ((uint32_t)row * kResR + 32u * ks + 8u * (lane >> 4)) * 2u : 0u;
+    res_dma16(a.eops, off, ebuf + (uint32_t)(ks * 1024));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -271,32 +310,37 @@ __device__ void res_select(const ResArgs& a, int b, int k, int& prev, unsigned c
     return;
   }
   const uint32_t g = (uint32_t)b >> 4, n = (uint32_t)b & 15u;
-  // The row's NW = 8 nwg range summaries into the stage, in wave order: the
-  // 64 bytes of workgroup w (its eight waves) sit at part[g][w][n][0..7];
-  // DMA i gathers workgroups 16 i .. 16 i + 15, four lanes each.
-  {
-    for (int i = 0; i < (nwg + 15) / 16; ++i) {
-      uint32_t w = (uint32_t)(16 * i) + ((uint32_t)lane >> 2);
-      w = w < (uint32_t)nwg ? w : 0u;
-      const uint32_t off = (((g * (uint32_t)nwg + w) * 16u + n) * 8u) * 8u + 16u * ((uint32_t)lane & 3u);
-      res_dma16(a.part, off, stage_lds + (uint32_t)(1024 * i));
-    }
-    res_wait_vmem<0>();
+  // The row's NW = 8 nt range summaries into the stage: the 64 bytes of tile
+  // workgroup w (its eight ranges) sit at part[g][w][n][0..7]; DMA i gathers
+  // workgroups 16 i .. 16 i + 15, four lanes each, so workgroup w lands at
+  // byte 64 w and lane l's workgroups 4 l .. 4 l + 3 at [256 l, 256 l + 256).
+  for (int i = 0; i < (nwg + 15) / 16; ++i) {
+    uint32_t w = (uint32_t)(16 * i) + ((uint32_t)lane >> 2);
+    w = w < (uint32_t)nwg ? w : 0u;
+    const uint32_t off = (((g * (uint32_t)nwg + w) * 16u + n) * 8u) * 8u + 16u * ((uint32_t)lane & 3u);
+    res_dma16(a.part, off, stage_lds + (uint32_t)(1024 * i));
   }
-  // summaries 2 j2, 2 j2 + 1 of lane l's [32 l, 32 l + 32) as (m, s, m, s);
-  // -inf past NW
-  const float4* P4 = reinterpret_cast<const float4*>(stage) + (kResSumPerLane / 2) * lane;
-  auto pair = [&](int j2) -> float4 {
-    const float4 q = P4[j2];
-    return kResSumPerLane * lane + 2 * j2 < a.NW ? q : make_float4(-__builtin_inff(), 0.0f, -__builtin_inff(), 0.0f);
+  res_wait_vmem<0>();
+  // Chunk c (16 bytes: two ranges) of lane l is read at step (c - l) mod 16:
+  // the 16 lanes of each quarter-wave then hit 16 different bank groups.
+  // Workgroups past nt read as (-inf, no column / 0).
+  constexpr int kWgPerLane = kResMaxWg / kWave;
+  const float4* lane_chunks = reinterpret_cast<const float4*>(stage) + 16 * lane;
+  auto chunk = [&](int step, int& c) -> float4 {
+    c = (step + lane) & 15;
+    const float4 q = lane_chunks[c];
+    const bool live = kWgPerLane * lane + (c >> 2) < nwg;
+    const float dead = kGreedy ? __int_as_float(0x7fffffff) : 0.0f;
+    return live ? q : make_float4(-__builtin_inff(), dead, -__builtin_inff(), dead);
   };
   int x;
   if constexpr (kGreedy) {
     float bv = -__builtin_inff();
     int bi = 0x7fffffff;
-#pragma unroll 2
-    for (int j2 = 0; j2 < kResSumPerLane / 2; ++j2) {
-      const float4 q = pair(j2);
+#pragma unroll 4
+    for (int st = 0; st < 16; ++st) {
+      int c;
+      const float4 q = chunk(st, c);
       argmax_merge(bv, bi, q.x, __float_as_int(q.y));
       argmax_merge(bv, bi, q.z, __float_as_int(q.w));
     }
@@ -308,25 +352,31 @@ __device__ void res_select(const ResArgs& a, int b, int k, int& prev, unsigned c
       a.lse[out] = 0.0f;
     }
   } else {
-    // (the loops over the lane's summaries stay rolled: every register they
-    // would take is one less for the W2 slice held across this function)
     float lm = -__builtin_inff();
-#pragma unroll 2
-    for (int j2 = 0; j2 < kResSumPerLane / 2; ++j2) {
-      const float4 q = pair(j2);
+#pragma unroll 4
+    for (int st = 0; st < 16; ++st) {
+      int c;
+      const float4 q = chunk(st, c);
       lm = fmaxf(lm, fmaxf(q.x, q.z));
     }
     const float M = wave_max_dpp(lm);
     auto weight = [&](float mj, float sj) -> double {
       return mj != -__builtin_inff() ? (double)sj * (double)fast_exp2((mj - M) * a.cf) : 0.0;
     };
-    double local = 0.0;
-#pragma unroll 2
-    for (int j2 = 0; j2 < kResSumPerLane / 2; ++j2) {
-      const float4 q = pair(j2);
-      local += weight(q.x, q.y);
-      local += weight(q.z, q.w);
+    // level 1: the weight of each of the lane's four workgroups (the sum of
+    // its eight range weights)
+    double wwg[kWgPerLane] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int st = 0; st < 16; ++st) {
+      int c;
+      const float4 q = chunk(st, c);
+      const double w2 = weight(q.x, q.y) + weight(q.z, q.w);
+#pragma unroll
+      for (int qq = 0; qq < kWgPerLane; ++qq) wwg[qq] += (c >> 2) == qq ? w2 : 0.0;
     }
+    double local = 0.0;
+#pragma unroll
+    for (int c = 0; c < kWgPerLane; ++c) local += wwg[c];
     const double incl = wave_inclusive_scan_dpp(local);
     const double total = lane_f64(incl, kWave - 1);
     const double u = unit_uniform(draw_block(a.seeds[b], a.round, (uint64_t)k, kStreamDraft, 0).w[0]);
@@ -334,45 +384,51 @@ __device__ void res_select(const ResArgs& a, int b, int k, int& prev, unsigned c
     const unsigned long long cross = __ballot(local > 0.0 && incl > q);
     const unsigned long long pos = __ballot(local > 0.0);
     const int owner = cross ? __ffsll((long long)cross) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
-    // the owner's range: first positive weight whose inclusive sum exceeds q,
-    // else the last positive one (selects, every lane runs it)
-    int ri = -1, lastpos = -1;
+    // the workgroup: first positive weight whose inclusive sum exceeds q,
+    // else the last positive one (every lane finds its candidate, the
+    // owner's is taken)
+    int wsel = -1, lastc = -1;
     double base = 0.0, lastbase = 0.0;
-    float mi = 0.0f, lastm = 0.0f;
     {
       double cum = incl - local;
-#pragma unroll 1
-      for (int j = 0; j < kResSumPerLane; ++j) {
-        const float2 qq = reinterpret_cast<const float2*>(P4)[j];
-        const bool live = kResSumPerLane * lane + j < a.NW;
-        const float mj = live ? qq.x : -__builtin_inff(), sj = qq.y;
-        const double w = weight(mj, sj);
-        const bool posw = w > 0.0;
-        const bool hit = posw && ri < 0 && cum + w > q;
-        lastpos = posw ? j : lastpos;
+#pragma unroll
+      for (int c = 0; c < kWgPerLane; ++c) {
+        const bool posw = wwg[c] > 0.0;
+        const bool hit = posw && wsel < 0 && cum + wwg[c] > q;
+        lastc = posw ? c : lastc;
         lastbase = posw ? cum : lastbase;
-        lastm = posw ? mj : lastm;
-        ri = hit ? j : ri;
+        wsel = hit ? c : wsel;
         base = hit ? cum : base;
-        mi = hit ? mj : mi;
-        cum += w;
+        cum += wwg[c];
       }
-      const bool none = ri < 0;
-      ri = kResSumPerLane * lane + (none ? (lastpos < 0 ? 0 : lastpos) : ri);
-      base = none ? (lastpos < 0 ? 0.0 : lastbase) : base;
-      mi = none ? (lastpos < 0 ? M : lastm) : mi;
+      const bool none = wsel < 0;
+      wsel = kWgPerLane * lane + (none ? (lastc < 0 ? 0 : lastc) : wsel);
+      base = none ? (lastc < 0 ? 0.0 : lastbase) : base;
     }
-    ri = lane_i32(ri, owner);
+    wsel = lane_i32(wsel, owner);
     base = lane_f64(base, owner);
-    mi = lane_f32(mi, owner);
-    // the same factor as in the range's weight, so the sub-block and column
-    // weights below add up to it
+    // level 2: that workgroup's eight ranges (lanes 0-7, from the stage), in
+    // vocabulary order
+    const float2 pv = lane < kResWaves ? reinterpret_cast<const float2*>(stage)[kResWaves * wsel + lane]
+                                       : make_float2(-__builtin_inff(), 0.0f);
+    const double wr = lane < kResWaves ? weight(pv.x, pv.y) : 0.0;
+    const double rincl = wave_inclusive_scan_dpp(wr);
+    const double qr = q - base;
+    const unsigned long long rcross = __ballot(wr > 0.0 && rincl > qr);
+    const unsigned long long rpos = __ballot(wr > 0.0);
+    const int rj = rcross ? __ffsll((long long)rcross) - 1 : (rpos ? 63 - __clzll((long long)rpos) : 0);
+    base += lane_f64(rincl - wr, rj);
+    const int ri = kResWaves * wsel + rj;
+    const float mi = lane_f32(pv.x, rj);
     const double scale = (double)fast_exp2((mi - M) * a.cf);
-    // the sub-block of the range (its sums are relative to mi)
+    const size_t wrow = ((size_t)g * nwg + wsel) * 16 + n;
+    const float sv = lane < kResWgSub ? a.ssum[wrow * kResWgSub + lane] : 0.0f;
+    // the sub-block of the range (its sums are relative to mi), from the
+    // slots already loaded
     const Range rg = res_range(a, ri);
-    const int rw = ri / kResWaves;  // the workgroup that wrote the range
-    const int loc = rg.sb0 - res_range(a, rw * kResWaves).sb0;
-    const float sbv = lane < rg.n ? a.ssum[((size_t)(g * (uint32_t)nwg + rw) * 16 + n) * kResWgSub + loc + lane] : 0.0f;
+    const int loc = rg.sb0 - res_range(a, wsel * kResWaves).sb0;
+    const float sbl = __shfl(sv, (loc + lane) & (kWave - 1));
+    const float sbv = lane < rg.n ? sbl : 0.0f;
     const double wb = lane < rg.n ? (double)sbv * scale : 0.0;
     const double bincl = wave_inclusive_scan_dpp(wb);
     const double q1 = q - base;
@@ -441,7 +497,7 @@ __device__ void res_select(const ResArgs& a, int b, int k, int& prev, unsigned c
   // workgroups and in this wave's LDS for its own next rescan
   if (k < a.gamma) {
     const uint2 v = reinterpret_cast<const uint2*>(a.W1 + (size_t)x * kResR)[lane];
-    reinterpret_cast<uint2*>(a.eops + (size_t)b * kResR)[lane] = v;
+    res_put(reinterpret_cast<uint2*>(a.eops + (size_t)b * kResR) + lane, v);
     res_wait_lgkm0();  // the rescan's reads of the old row are done
     reinterpret_cast<uint2*>(erow)[lane] = v;
   }
@@ -467,10 +523,21 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   const int cbase = my.n > 0 ? 16 * my.sb0 : 0;
   const int myloc = my.sb0 - res_range(a, wg * kResWaves).sb0;  // first sub-block slot of the wave in its workgroup
   const uint32_t lds = res_lds_base(smem);
-  const uint32_t ustage_l = lds + (uint32_t)(wave * kResWaveU);
   const uint32_t ebufs_l = lds + (uint32_t)kResLdsE;
-  const unsigned char* ustage = smem + wave * kResWaveU;
   const unsigned char* ebufs = smem + kResLdsE;
+  // The control wave (7) issues no DMAs: its polls and releases then wait for
+  // nothing but its own stores.  Waves 0-4 issue one sub-block each of its U
+  // blocks, into four stages (they cannot see when the control wave has read
+  // a stage, so the stage they refill is the one of the step before, which
+  // the workgroup barrier has retired), and wave 5 its E chunk.
+  const bool ctl = wave == kResCtl;
+  const Range ctl_rg = res_range(a, wg * kResWaves + kResCtl);
+  const int nstage = ctl ? 4 : kResStages;
+  auto stage_off = [&](int w, int st) -> int {
+    return (w == kResCtl && st == kResStages) ? kResLdsCtlU : w * kResWaveU + st * kResStageBytes;
+  };
+  auto ustage_of = [&](int t) -> const unsigned char* { return smem + stage_off(wave, t % nstage); };
+  auto ctl_stage_l = [&](int t) -> uint32_t { return lds + (uint32_t)stage_off(kResCtl, t % 4); };
   volatile int* ok_flag = reinterpret_cast<volatile int*>(smem + kResLdsMisc);
   uint32_t* err = a.flags + kResErr;
   const uint32_t* sel_flags = a.flags + nt;
@@ -490,26 +557,56 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   // E(t) is issued at step t - 2 if the half it depends on ended before that
   // step (or it depends on none), else at step t itself
   auto e_early = [&](int t) { return pos_of(t) == 1 || dep_of(t) <= t - 3; };
+  auto half_end = [&](int t) { const int g = grp_of(t); return g == G0 - 1 || g == G - 1; };
+  // the flag phase of the half that ends at step t
+  auto end_phase = [&](int t) { return res_phase(pos_of(t), grp_of(t) == G - 1 ? 1 : 0); };
+  uint32_t released = 0;   // tile phase already announced by this workgroup (uniform)
   uint32_t confirmed = 0;  // selector phase already observed by this workgroup (uniform)
-  // wave 0 waits for the E rows of step t (before the workgroup barrier that
-  // follows); false when the wait failed
-  auto check = [&](int t) -> bool {
+  auto release = [&](uint32_t phase) {
+    if (phase <= released) return;
+    released = phase;
+    if (ctl && lane == 0) res_arrive(a.flags + wg, phase);
+  };
+  // The control wave waits for the E rows of step t (before the workgroup
+  // barrier that follows; the ok word reports a failed wait).  The selectors
+  // need this workgroup's announcement of the half that those rows depend
+  // on: when the lazy announcement (two steps after the half's end, below)
+  // has not been made yet, everything is drained and it is made now.
+  auto check = [&](int t, int now) {
     const uint32_t need = res_phase(pos_of(t), half_of(grp_of(t)));
-    if (need <= confirmed) return true;
+    if (need <= confirmed) return;
     confirmed = need;
-    if (wave == 0) {
+    // this workgroup's phase for that half of the previous position (none
+    // at position 1, whose E rows the selectors write before any step)
+    if (need > 2 && released < need - 2) {
+      res_wait_vmem<0>();
+      __syncthreads();
+      int last = now - 1;
+      while (last > 0 && !half_end(last)) --last;
+      release(end_phase(last));
+    }
+    if (ctl) {
       const bool ok = res_wait_flags(sel_flags, kResSelWg, need, err, a.timeout);
       if (lane == 0) *ok_flag = ok ? 1 : 0;
     }
-    return true;
   };
   auto e_slot = [&](int t) -> uint32_t { return ebufs_l + (uint32_t)((t % kResESlots) * kResEBytes); };
-  auto issue_e = [&](int t, bool real) { res_issue_e(a, grp_of(t), e_slot(t), real); };
+  auto issue_e = [&](int t, bool real) {
+    if (!ctl) res_issue_e(a, grp_of(t), e_slot(t), real, wave, 1);
+    if (wave == kResEHelper) res_issue_e(a, grp_of(t), e_slot(t), real, kResCtl, 1);
+  };
+  // U of step t (real or not) for this wave and, from waves 0-4, one
+  // sub-block each for the control wave
+  auto issue_u = [&](int t, uint32_t own_stage) {
+    const bool real = t < T;
+    const int tt = real ? t : 0;
+    if (!ctl) res_issue_u(a, my, pos_of(tt), grp_of(tt), own_stage, real);
+    if (wave < kResSub) res_issue_u1(a, ctl_rg, pos_of(tt), grp_of(tt), ctl_stage_l(t), real, wave);
+  };
 
   if (threadIdx.x == 0) *ok_flag = 1;
   // U of steps 0..2 stream in while W2 is loaded
-  for (int t = 0; t < kResStages; ++t)
-    res_issue_u(a, my, pos_of(t < T ? t : 0), grp_of(t < T ? t : 0), ustage_l + (uint32_t)(t * kResStageBytes), t < T);
+  for (int t = 0; t < kResStages; ++t) issue_u(t, lds + (uint32_t)stage_off(wave, t));
 
   // the wave's slice of W2 as MFMA A fragments, for the whole call
   bf16x8 wf[kResSub][kResKSteps];
@@ -522,8 +619,8 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   }
 
   // E of steps 0 and 1
-  check(0);
-  if (T > 1 && e_early(1)) check(1);
+  check(0, 0);
+  if (T > 1 && e_early(1)) check(1, 0);
   __syncthreads();
   if (!*ok_flag) {
     res_wait_vmem<0>();
@@ -534,28 +631,58 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
 
   for (int t = 0; t < T; ++t) {
     const int k = pos_of(t), g = grp_of(t);
-    // E(t) and this wave's U block of step t have landed.  Issue order per
-    // step: one E DMA at its start (E(t + 2), real or not), 5 U DMAs (U of
-    // step t + 3, real or not) and the summary stores; so after E(t) come E(1)
-    // at t = 0, 1 + 5 at t = 1 and 5 + 1 + 5 at t >= 2.  U(t) is issued
-    // before E(t).  An E issued late (at its own step) is waited for there,
-    // and flag waits drain everything: both only make these counts safer.
+    // E(t) and the U blocks of step t this wave issued have landed.  Issue
+    // order per step: e E DMAs at its start (E(t + 2), real or not), u U DMAs
+    // (U of step t + 3, real or not) and summary stores (at least one), with
+    // (e, u) = (1, 6) for waves 0-4, (2, 5) for wave 5, (1, 5) for wave 6 and
+    // (0, 0) for the control wave; so after E(t) come e at t = 0, e + u at
+    // t = 1 and 2 u + e at t >= 2.  U(t) is issued before E(t).
+    // Two steps after the end of a half, the summary stores of its last step
+    // must have completed too: only e + u ops (one store for the control
+    // wave) are known to follow them, so those steps wait for that many.  An
+    // E issued late (at its own step) is waited for there, and drains only
+    // make these counts safer.  The control wave issues no loads and
+    // otherwise waits for nothing.
     __builtin_amdgcn_sched_barrier(0);
-    if (t == 0) {
-      res_wait_vmem<1>();
-    } else if (t == 1) {
-      res_wait_vmem<kResSub + 1>();
+    const bool rel = t >= 2 && half_end(t - 2);
+    if (ctl) {
+      if (rel) res_wait_vmem<1>();
+    } else if (wave < kResSub) {
+      if (t == 0) {
+        res_wait_vmem<1>();
+      } else if (t == 1 || rel) {
+        res_wait_vmem<kResSub + 2>();
+      } else {
+        res_wait_vmem<2 * kResSub + 3>();
+      }
+    } else if (wave == kResEHelper) {
+      if (t == 0) {
+        res_wait_vmem<2>();
+      } else if (t == 1 || rel) {
+        res_wait_vmem<kResSub + 2>();
+      } else {
+        res_wait_vmem<2 * kResSub + 2>();
+      }
     } else {
-      res_wait_vmem<2 * kResSub + 1>();
+      if (t == 0) {
+        res_wait_vmem<1>();
+      } else if (t == 1 || rel) {
+        res_wait_vmem<kResSub + 1>();
+      } else {
+        res_wait_vmem<2 * kResSub + 1>();
+      }
     }
     const bool late = !e_early(t);
-    if (late) check(t);
-    if (t + 2 < T && e_early(t + 2)) check(t + 2);
+    if (late) check(t, t);
+    if (t + 2 < T && e_early(t + 2)) check(t + 2, t);
     __syncthreads();
     if (!*ok_flag) {
       res_wait_vmem<0>();
       return;
     }
+    // the half that ended two steps ago: every wave's summary stores of it
+    // are complete (the waits above) and all waves have passed the barrier
+    if (rel) release(end_phase(t - 2));
     if (late) {
       issue_e(t, true);
       res_wait_vmem<0>();
@@ -593,7 +720,7 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
     // repeat sub-block 0 (same columns, same values): they leave maxima
     // unchanged and are dropped from sums.
     {
-      const unsigned char* ub = ustage + (t % kResStages) * kResStageBytes;
+      const unsigned char* ub = ustage_of(t);
 #pragma unroll
       for (int s = 0; s < kResSub; ++s) {
         const float4 u = *reinterpret_cast<const float4*>(ub + s * 1024 + 16 * lane);
@@ -603,10 +730,9 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
         acc[s][3] += u.w;
       }
       res_wait_lgkm0();
-      // U of step t + 3 into the stage just read
-      const int tn = t + kResStages;
-      res_issue_u(a, my, pos_of(tn < T ? tn : 0), grp_of(tn < T ? tn : 0),
-                  ustage_l + (uint32_t)((t % kResStages) * kResStageBytes), tn < T);
+      // U of step t + 3 into the stage just read (waves 0-4 also refill the
+      // control wave's stage of step t - 1)
+      issue_u(t + kResStages, lds + (uint32_t)stage_off(wave, t % nstage));
     }
     const int row = kResRows * g + n16;
     const bool rowok = row < a.B;
@@ -627,7 +753,7 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
       }
       res_argmax_rows(bv, bc);
       if (my.n == 0) bv = -__builtin_inff(), bc = 0x7fffffff;
-      if (lane < 16 && rowok) a.part[pidx] = make_float2(bv, __int_as_float(bc));
+      if (lane < 16 && rowok) res_put(a.part + pidx, make_float2(bv, __int_as_float(bc)));
     } else {
       float m = -__builtin_inff();
 #pragma unroll
@@ -643,22 +769,19 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
         bp[s] = res_sum_rows(s < my.n ? v : 0.0f);
       }
       const float S = (((bp[0] + bp[1]) + bp[2]) + bp[3]) + bp[4];
-      if (lane < 16 && rowok) a.part[pidx] = make_float2(my.n > 0 ? m : -__builtin_inff(), S);
+      if (lane < 16 && rowok) res_put(a.part + pidx, make_float2(my.n > 0 ? m : -__builtin_inff(), S));
       const float bq = q4 == 0 ? bp[0] : q4 == 1 ? bp[1] : q4 == 2 ? bp[2] : bp[3];
       const uint32_t so =
           (((uint32_t)g * (uint32_t)nt + (uint32_t)wg) * 16u + (uint32_t)n16) * kResWgSub + (uint32_t)myloc;
-      if (rowok && q4 < my.n) a.ssum[so + (uint32_t)q4] = bq;
-      if (rowok && q4 == 0 && my.n > 4) a.ssum[so + 4u] = bp[4];
+      if (rowok && q4 < my.n) res_put(a.ssum + so + (uint32_t)q4, bq);
+      if (rowok && q4 == 0 && my.n > 4) res_put(a.ssum + so + 4u, bp[4]);
     }
 
-    // the end of a half: announce it (an empty second half with the first)
-    if (g == G0 - 1 || g == G - 1) {
-      res_wait_vmem<0>();
-      __syncthreads();
-      if (threadIdx.x == 0) res_arrive(a.flags + wg, res_phase(k, g == G - 1 ? 1 : 0));
-    }
   }
+  // the halves not announced yet
   res_wait_vmem<0>();
+  __syncthreads();
+  release(res_phase(a.gamma, 1));
 }
 
 // ---------------------------------------------------------------------------
@@ -696,7 +819,7 @@ __device__ void res_selector(const ResArgs& a, unsigned char* smem) {
         prev[h][i] = (unsigned)x0 < (unsigned)a.V ? x0 : -1;
         uint2 v = make_uint2(0u, 0u);
         if (prev[h][i] >= 0) v = reinterpret_cast<const uint2*>(a.W1 + (size_t)prev[h][i] * kResR)[lane];
-        reinterpret_cast<uint2*>(a.eops + (size_t)b * kResR)[lane] = v;
+        res_put(reinterpret_cast<uint2*>(a.eops + (size_t)b * kResR) + lane, v);
         reinterpret_cast<uint2*>(erow(h, i))[lane] = v;
       }
     }
