@@ -26,6 +26,7 @@ from .dspark_ref import (  # noqa: F401
     inverse_cdf,
     markov_bias,
     markov_draft,
+    position_logits,
     residual_law,
     residual_sample,
     rnn_draft,

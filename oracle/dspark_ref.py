@@ -79,6 +79,18 @@ def draft_logits(U_row, W1, W2, prev, T):
     return l / T if T > 0 else l
 
 
+def position_logits(U, W1, W2, E, b, k, prev, T):
+    """Draft logits of block position k (1-based) of request b, as the draft
+    produced them: the Markov head's (Eq. 5 of [R], from the previous token
+    ``prev``) when E is None, otherwise the RNN head's of [R] "Instantiation
+    2: The RNN Head" (Eq. 6), U_k + e_k W2 with e_k = E[b][k-1] the operand
+    row the RNN draft used."""
+    if E is None:
+        return draft_logits(U[b, k - 1], W1, W2, prev, T)
+    l = np.asarray(U[b, k - 1], dtype=np.float64) + np.asarray(E[b, k - 1], dtype=np.float64) @ W2
+    return l / T if T > 0 else l
+
+
 def target_logits(tgt_row, T):
     """Target logits of one position, divided by the temperature when T > 0."""
     l = np.asarray(tgt_row, dtype=np.float64)
@@ -197,7 +209,7 @@ def residual_sample(pt, pd, seed, rnd, j, max_proposals, dists):
 
 
 def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=64,
-           requests=None, lengths=None):
+           requests=None, lengths=None, E=None):
     """Rejection-sampling verification of every request's drafted block
     ([R] "Speculative Decoding: Draft, Then Verify" step 3; [E] section 2).
 
@@ -221,6 +233,12 @@ def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=64,
     from the target row l+1 (stream 2 at position l+1, index 0), so l = 0
     emits one token drawn from p_t^1 (plain decoding) and l = gamma is the
     full block.
+
+    ``E`` ([B][gamma][r], optional): the operand rows e_k of an RNN draft
+    ([R] "Instantiation 2: The RNN Head", Eq. 6; ``rnn_draft`` returns them).
+    p_d^k is then softmax((U_k + e_k W2) / T), the law the RNN head drew x_k
+    from, in place of the Markov head's (the decode round of [R] "Putting It
+    All Together" feeds either head's draft to verification).
     """
     B, gamma, V = U.shape
     reqs = range(B) if requests is None else requests
@@ -248,7 +266,7 @@ def verify(U, W1, W2, x0, draft_tokens, tgt, T, seeds, rnd, max_proposals=64,
                 emitted.append(y)
                 n = k - 1
                 break
-            pd, _ = softmax(draft_logits(U[b, k - 1], W1, W2, prev, T))
+            pd, _ = softmax(position_logits(U, W1, W2, E, b, k, prev, T))
             pt, _ = softmax(lt)
             alpha = min(1.0, pt[x] / pd[x])
             accept_prob[b, k - 1] = alpha
@@ -289,7 +307,7 @@ def acceptance_rate(pd, pt):
     return min(1.0, max(0.0, float(np.minimum(pd, pt).sum())))
 
 
-def survival(U, W1, W2, x0, draft_tokens, tgt, T, conf=None, requests=None):
+def survival(U, W1, W2, x0, draft_tokens, tgt, T, conf=None, requests=None, E=None):
     """Prefix survival a_{b,k} = prod_{i<=k} c_{b,i} ([R] "The Hardware-Aware
     Prefix Scheduler", step 1 of Algorithm 1).
 
@@ -297,7 +315,9 @@ def survival(U, W1, W2, x0, draft_tokens, tgt, T, conf=None, requests=None):
     confidences.  Otherwise c_{b,k} is the analytical acceptance c*_k of Eq. 8
     at every block position along the drafted prefix (all gamma positions,
     also those after a rejection); at T = 0 it is the indicator
-    x_k == argmax tgt_k.  Returns (c_star [B][gamma] or None, survival).
+    x_k == argmax tgt_k.  With ``E`` (the operand rows of an RNN draft, as in
+    ``verify``) p_d^k is the RNN head's law.  Returns (c_star [B][gamma] or
+    None, survival).
     """
     if conf is not None:
         conf = np.asarray(conf, dtype=np.float64)
@@ -313,7 +333,7 @@ def survival(U, W1, W2, x0, draft_tokens, tgt, T, conf=None, requests=None):
             if T == 0:
                 c[b, k - 1] = 1.0 if first_argmax(lt) == x else 0.0
             else:
-                pd, _ = softmax(draft_logits(U[b, k - 1], W1, W2, prev, T))
+                pd, _ = softmax(position_logits(U, W1, W2, E, b, k, prev, T))
                 pt, _ = softmax(lt)
                 c[b, k - 1] = acceptance_rate(pd, pt)
             prev = x

@@ -244,3 +244,102 @@ def test_draft_block_law_is_the_product_of_position_softmaxes():
             want *= sp_softmax(l)[x]
             prev = x
         assert abs(p - want) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Drafts of the RNN head ([R] "Instantiation 2: The RNN Head", Eq. 6): the
+# decode round of [R] "Putting It All Together" verifies either head's block.
+# Verification given the RNN draft's operand rows E is lossless; given the
+# Markov head's law in their place it is not.
+# ---------------------------------------------------------------------------
+
+def _rnn_problem(V, gamma, r, d, seed):
+    U, W1, W2, G = _problem(V, gamma, r, seed)
+    rng = np.random.default_rng(seed + 1000)
+    Wp = rng.normal(0, 0.9, size=(3 * r, 2 * r + d))
+    h = rng.normal(0, 1.0, size=(1, gamma, d))
+    return U, W1, W2, Wp, h, G
+
+
+def _rnn_round(V, gamma, T, seed, use_e=True, r=2, d=2):
+    U, W1, W2, Wp, h, G = _rnn_problem(V, gamma, r, d, seed)
+    anchor = V // 2
+    x0 = np.array([anchor], dtype=np.int32)
+    seeds = np.array([99], dtype=np.uint64)
+
+    def run(paths):
+        dr = ref.rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, 5)
+        tgt = np.empty((1, gamma + 1, V), dtype=np.float32)
+        prev = anchor
+        for k in range(gamma + 1):
+            tgt[0, k] = G[k, prev]
+            if k < gamma:
+                prev = int(dr["tokens"][0, k])
+        v = ref.verify(U, W1, W2, x0, dr["tokens"], tgt, T, seeds, 5, max_proposals=0,
+                       E=dr["E"] if use_e else None)
+        n = int(v["accept_len"][0])
+        return tuple(int(t) for t in v["out_tokens"][0, :n + 1])
+
+    law, _ = _enumerate(run)
+    return law, (U, W1, W2, Wp, h, G, x0, anchor)
+
+
+@pytest.mark.parametrize("V,gamma,T", [(4, 3, 1.0), (5, 2, 0.7), (6, 2, 1.3)])
+def test_rnn_draft_round_law_is_the_target_law_exactly(V, gamma, T):
+    law, prob = _rnn_round(V, gamma, T, seed=50 + V)
+    G, anchor = prob[5], prob[7]
+    _assert_lossless(law, G, anchor, T, gamma)
+
+
+def test_rnn_draft_verified_with_the_markov_law_is_not_lossless():
+    law, prob = _rnn_round(4, 2, 1.0, seed=54, use_e=False)
+    with pytest.raises(AssertionError):
+        _assert_lossless(law, prob[5], prob[7], 1.0, 2)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.6])
+def test_rnn_survival_is_the_exact_acceptance_of_each_prefix(T):
+    # c*_k along a drafted prefix s = x_1..x_{k-1} equals the exact probability
+    # that position k is accepted given that s was drafted and accepted: the
+    # ratio of the round-law masses of "n >= k, prefix s" and "n >= k-1, prefix
+    # s", read off the enumerated round
+    V, gamma = 4, 3
+    U, W1, W2, Wp, h, G, x0, anchor = _rnn_problem(V, gamma, 2, 2, 77)[:6] + (
+        np.array([V // 2], dtype=np.int32), V // 2)
+    seeds = np.array([99], dtype=np.uint64)
+
+    def run(paths):
+        dr = ref.rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, 5)
+        tgt = np.empty((1, gamma + 1, V), dtype=np.float32)
+        prev = anchor
+        for k in range(gamma + 1):
+            tgt[0, k] = G[k, prev]
+            if k < gamma:
+                prev = int(dr["tokens"][0, k])
+        v = ref.verify(U, W1, W2, x0, dr["tokens"], tgt, T, seeds, 5, max_proposals=0, E=dr["E"])
+        n = int(v["accept_len"][0])
+        return n, tuple(int(t) for t in v["out_tokens"][0, :n])
+
+    law, _ = _enumerate(run)
+    checked = 0
+    for k in range(1, gamma + 1):
+        tested = collections.defaultdict(float)
+        passed = collections.defaultdict(float)
+        for (n, acc), p in law.items():
+            if n >= k - 1:
+                tested[acc[:k - 1]] += p
+            if n >= k:
+                passed[acc[:k - 1]] += p
+        for s, pm in tested.items():
+            forced = np.array([list(s) + [0] * (gamma - len(s))], dtype=np.int32)
+            dr = ref.rnn_draft(U, W1, W2, Wp, h, x0, T, seeds, 5, forced=forced)
+            tgt = np.empty((1, gamma + 1, V), dtype=np.float32)
+            prev = anchor
+            for j in range(gamma + 1):
+                tgt[0, j] = G[j, prev]
+                if j < gamma:
+                    prev = int(forced[0, j])
+            c, _ = ref.survival(U, W1, W2, x0, forced, tgt, T, E=dr["E"])
+            assert abs(passed[s] / pm - c[0, k - 1]) < 1e-12, (k, s)
+            checked += 1
+    assert checked == 1 + V + V * V
