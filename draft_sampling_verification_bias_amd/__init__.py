@@ -69,7 +69,7 @@ def load():
     lib.dspark_rnn_draft.restype = I
     lib.dspark_rnn_draft.argtypes = [P, P, P, I, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, P, SZ, P]
     lib.dspark_verify.restype = I
-    lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
     lib.dspark_confidence.restype = I
     lib.dspark_confidence.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, P, P]
     lib.dspark_schedule.restype = I
@@ -77,7 +77,7 @@ def load():
     lib.dspark_transpose_w2.restype = I
     lib.dspark_transpose_w2.argtypes = [P, I, I, I, P, P]
     lib.dspark_survival.restype = I
-    lib.dspark_survival.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P]
+    lib.dspark_survival.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, F, P, P, P, SZ, P]
     lib.dspark_profile_enable.restype = I
     lib.dspark_profile_enable.argtypes = [I]
     lib.dspark_profile_kinds.restype = I
@@ -279,10 +279,12 @@ def rnn_draft(U, W1, W2, Wp, hp, x0, temperature, seeds, rnd, out=None, with_e=F
 
 
 def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, rnd, out=None,
-           with_accept_prob=True, workspace=None, stream=None, W2T=None, lengths=None):
+           with_accept_prob=True, workspace=None, stream=None, W2T=None, lengths=None, E=None):
     """Rejection-sampling verification.  Returns (accept_len, out_tokens, accept_prob or None).
     W2T: optional transposed copy of W2 from transpose_w2.  lengths: optional
-    int32 [B] scheduled verification lengths (from schedule)."""
+    int32 [B] scheduled verification lengths (from schedule).  E: the
+    float32 [B][gamma][r] operand rows of an RNN draft (rnn_draft with_e=True)
+    when the tokens come from the RNN head."""
     B, g1, V = target.shape
     gamma = g1 - 1
     dev = target.device
@@ -304,6 +306,8 @@ def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, 
         _dev(seeds, "seeds", torch.uint64, (B,))
     if lengths is not None:
         _dev(lengths, "lengths", torch.int32, (B,))
+    if E is not None:
+        _dev(E, "E", torch.float32, (B, gamma, r))
     if out is None:
         out = (torch.empty((B,), dtype=torch.int32, device=dev),
                torch.empty((B, gamma + 1), dtype=torch.int32, device=dev),
@@ -314,8 +318,8 @@ def verify(U, W1, W2, x0, draft_tokens, draft_prob, target, temperature, seeds, 
     if aprob is not None:
         _dev(aprob, "accept_prob", torch.float32, (B, gamma))
     ws, nbytes = _workspace(OP_VERIFY, B, gamma, V, r, workspace, dev)
-    st = load().dspark_verify(_p(U), _p(W1), _p(W2), _p(W2T), wd, _p(x0), _p(draft_tokens), _p(draft_prob), _p(target),
-                              _p(lengths), B, gamma, V, r, float(temperature), _p(seeds), int(rnd), _p(alen),
+    st = load().dspark_verify(_p(U), _p(W1), _p(W2), _p(W2T), wd, _p(x0), _p(draft_tokens), _p(draft_prob), _p(E),
+                              _p(target), _p(lengths), B, gamma, V, r, float(temperature), _p(seeds), int(rnd), _p(alen),
                               _p(otok), _p(aprob), _p(ws), nbytes, _stream(stream, dev))
     _check("dspark_verify", st)
     return alen, otok, aprob
@@ -389,15 +393,16 @@ def transpose_w2(W2, out=None, stream=None):
 
 
 def survival(U, W1, W2, x0, draft_tokens, draft_lse, target, temperature, conf=None, out=None,
-             with_c_star=True, workspace=None, stream=None):
-    """Prefix survival products.  Returns (c_star or None, survival)."""
+             with_c_star=True, workspace=None, stream=None, E=None):
+    """Prefix survival products.  Returns (c_star or None, survival).  E: the
+    operand rows of an RNN draft, as for verify."""
     if conf is not None:
         B, gamma = conf.shape
         dev = conf.device
         _dev(conf, "conf", torch.float32)
         surv = out[1] if out is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
         _dev(surv, "survival", torch.float32, (B, gamma))
-        st = load().dspark_survival(None, None, None, _BF16, None, None, None, None, _p(conf), B, gamma, 2, 16,
+        st = load().dspark_survival(None, None, None, _BF16, None, None, None, None, None, _p(conf), B, gamma, 2, 16,
                                     0.0, None, _p(surv), None, 0, _stream(stream, dev))
         _check("dspark_survival", st)
         return None, surv
@@ -416,6 +421,8 @@ def survival(U, W1, W2, x0, draft_tokens, draft_lse, target, temperature, conf=N
     _dev(draft_tokens, "draft_tokens", torch.int32, (B, gamma))
     if draft_lse is not None:
         _dev(draft_lse, "draft_lse", torch.float32, (B, gamma))
+    if E is not None:
+        _dev(E, "E", torch.float32, (B, gamma, r))
     if out is None:
         out = (torch.empty((B, gamma), dtype=torch.float32, device=dev) if with_c_star else None,
                torch.empty((B, gamma), dtype=torch.float32, device=dev))
@@ -424,8 +431,8 @@ def survival(U, W1, W2, x0, draft_tokens, draft_lse, target, temperature, conf=N
         _dev(cst, "c_star", torch.float32, (B, gamma))
     _dev(surv, "survival", torch.float32, (B, gamma))
     ws, nbytes = _workspace(OP_SURVIVAL, B, gamma, V, r, workspace, dev)
-    st = load().dspark_survival(_p(U), _p(W1), _p(W2), wd, _p(x0), _p(draft_tokens), _p(draft_lse), _p(target),
-                                None, B, gamma, V, r, float(temperature), _p(cst), _p(surv), _p(ws), nbytes,
+    st = load().dspark_survival(_p(U), _p(W1), _p(W2), wd, _p(x0), _p(draft_tokens), _p(draft_lse), _p(E),
+                                _p(target), None, B, gamma, V, r, float(temperature), _p(cst), _p(surv), _p(ws), nbytes,
                                 _stream(stream, dev))
     _check("dspark_survival", st)
     return cst, surv

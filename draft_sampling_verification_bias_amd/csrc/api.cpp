@@ -189,8 +189,9 @@ dspark_status dspark_rnn_draft(const float* U, const void* W1, const void* W2, d
 
 dspark_status dspark_verify(const float* U, const void* W1, const void* W2, const void* W2T, dspark_dtype wdtype,
                             const int32_t* x0,
-                            const int32_t* draft_tokens, const float* draft_prob, const float* target_logits,
-                            const int32_t* lengths, int B, int gamma, int V, int r, float temperature,
+                            const int32_t* draft_tokens, const float* draft_prob, const float* draft_rows,
+                            const float* target_logits, const int32_t* lengths, int B, int gamma, int V, int r,
+                            float temperature,
                             const uint64_t* seeds, uint64_t round, int32_t* accept_len, int32_t* out_tokens,
                             float* accept_prob, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
@@ -200,7 +201,7 @@ dspark_status dspark_verify(const float* U, const void* W1, const void* W2, cons
       !req(out_tokens, 4) || !opt(accept_prob, 4) || !opt(lengths, 4) || !req(workspace, 16))
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (!greedy && (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !opt(W2T, 16) || !req(draft_prob, 4) ||
-                  !req(seeds, 8)))
+                  !opt(draft_rows, 4) || !req(seeds, 8)))
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < verify_workspace(B, gamma, V, r)) return DSPARK_ERR_WORKSPACE;
   VerifyArgs a = {};
@@ -223,6 +224,7 @@ dspark_status dspark_verify(const float* U, const void* W1, const void* W2, cons
   a.out_tokens = out_tokens;
   a.accept_prob = accept_prob;
   a.lengths = lengths;
+  a.E = greedy ? nullptr : draft_rows;
   a.ws = workspace;
   return from_hip(launch_verify(a, wdtype == DSPARK_BF16, stream));
 }
@@ -273,8 +275,9 @@ dspark_status dspark_transpose_w2(const void* W2, dspark_dtype wdtype, int r, in
 }
 
 dspark_status dspark_survival(const float* U, const void* W1, const void* W2, dspark_dtype wdtype, const int32_t* x0,
-                              const int32_t* draft_tokens, const float* draft_lse, const float* target_logits,
-                              const float* conf, int B, int gamma, int V, int r, float temperature, float* c_star,
+                              const int32_t* draft_tokens, const float* draft_lse, const float* draft_rows,
+                              const float* target_logits, const float* conf, int B, int gamma, int V, int r,
+                              float temperature, float* c_star,
                               float* survival, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!req(survival, 4)) return DSPARK_ERR_INVALID_ARGUMENT;
   SurvivalArgs a = {};
@@ -292,7 +295,7 @@ dspark_status dspark_survival(const float* U, const void* W1, const void* W2, ds
   const bool greedy = temperature == 0.0f;
   if (!req(x0, 4) || !req(draft_tokens, 4) || !req(target_logits, 16) || !opt(c_star, 4) || !req(workspace, 16))
     return DSPARK_ERR_INVALID_ARGUMENT;
-  if (!greedy && (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(draft_lse, 4)))
+  if (!greedy && (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !req(draft_lse, 4) || !opt(draft_rows, 4)))
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < survival_workspace(B, gamma, V, r)) return DSPARK_ERR_WORKSPACE;
   a.U = U;
@@ -301,6 +304,7 @@ dspark_status dspark_survival(const float* U, const void* W1, const void* W2, ds
   a.x0 = x0;
   a.draft_tokens = draft_tokens;
   a.draft_lse = draft_lse;
+  a.E = greedy ? nullptr : draft_rows;
   a.target = target_logits;
   a.V = V;
   a.r = r;

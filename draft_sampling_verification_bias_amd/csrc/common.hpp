@@ -240,6 +240,12 @@ __device__ __forceinline__ double block_exclusive_scan(double x, double* scratch
 }
 
 // bf16 bit pattern to float (exact).
+// Nearest bf16 of a finite float (ties to even).
+__device__ __forceinline__ uint16_t bf16_round(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
 __device__ __forceinline__ float bf16_to_float(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }

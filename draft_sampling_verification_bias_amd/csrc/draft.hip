@@ -625,11 +625,6 @@ struct CellArgs {
 constexpr int kCellHalf = 256;
 constexpr int kCellThreads = 2 * kCellHalf;
 
-__device__ __forceinline__ uint16_t bf16_round(float f) {
-  const uint32_t u = __float_as_uint(f);  // finite here: |e| <= 1
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
 template <bool kBf16>
 __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
   // LDS: z of the group [nreq][2r], then per half one chunk of the

@@ -136,6 +136,7 @@ struct VerifyArgs {
   int32_t* out_tokens;
   float* accept_prob;
   const int32_t* lengths;  // optional [B] scheduled verification lengths (null: gamma)
+  const float* E;          // optional [B][gamma][r] operand rows e_k of an RNN draft (null: W1[x_{k-1}])
   void* ws;
   double inv_t_d;  // 1 / T, filled in by launch_verify
 };
@@ -152,6 +153,7 @@ struct SurvivalArgs {
   const float* draft_lse;
   const float* target;
   const float* conf;
+  const float* E;  // optional [B][gamma][r] operand rows e_k of an RNN draft (null: W1[x_{k-1}])
   int B, gamma, V, r;
   float temperature;
   float* c_star;

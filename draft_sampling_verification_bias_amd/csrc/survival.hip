@@ -12,7 +12,11 @@
 //   3. the MFMA tile pass in overlap mode: bias + U for every (request,
 //      position) row at once -- all drafted tokens are known, so the whole
 //      (B*gamma) x r x V contraction is one dense pass -- fused with
-//      sum min(p_d, p_t) over each 128-column tile;
+//      sum min(p_d, p_t) over each 128-column tile.  The bias operand is the
+//      Markov head's W1[x_{k-1}], or the RNN head's e_k ("Instantiation 2:
+//      The RNN Head", Eq. 6) when the draft's operand rows are given: with
+//      bf16 weights as two bf16 parts (hi = bf16(e), lo = bf16(e - hi)),
+//      the split the RNN draft's own tile pass uses;
 //   4. per request: float64 sums over tiles, clamp, cumulative product.
 #include <math.h>
 
@@ -27,6 +31,7 @@ struct SurvWs {
   float2* tpart;  // [B*gamma][ntv]
   float* lt2;     // [B*gamma] target log2 normaliser, or the greedy indicator
   float2* opart;  // [B*gamma][ntd]
+  uint16_t* opnd; // [B*gamma][2r] two-part bf16 operand rows of an RNN draft
 };
 
 static SurvWs carve_survival(void* ws, int B, int gamma, int V) {
@@ -39,14 +44,29 @@ static SurvWs carve_survival(void* ws, int B, int gamma, int V) {
   w.lt2 = reinterpret_cast<float*>(p);
   p += align256(rows * sizeof(float));
   w.opart = reinterpret_cast<float2*>(p);
+  p += align256(rows * tiles_of(V, kTileCols) * sizeof(float2));
+  w.opnd = reinterpret_cast<uint16_t*>(p);
   return w;
 }
 
 size_t survival_workspace(int B, int gamma, int V, int r) {
-  (void)r;
   const size_t rows = (size_t)B * gamma;
   return align256(rows * tiles_of(V, kTgtCols) * sizeof(float2)) + align256(rows * sizeof(float)) +
-         align256(rows * tiles_of(V, kTileCols) * sizeof(float2));
+         align256(rows * tiles_of(V, kTileCols) * sizeof(float2)) + align256(rows * 2 * r * sizeof(uint16_t));
+}
+
+// The RNN draft's operand rows e (float32) as two bf16 parts per element,
+// row R = [hi(e_R) ; lo(e_R)], for the bf16 tile pass.
+__global__ void split_rows_kernel(const float* E, long long n, int r, uint16_t* opnd) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const long long row = i / r;
+  const int j = (int)(i - row * r);
+  const float e = E[i];
+  const uint16_t hi = bf16_round(e);
+  const uint16_t lo = bf16_round(e - bf16_to_float(hi));
+  opnd[row * 2 * r + j] = hi;
+  opnd[row * 2 * r + r + j] = lo;
 }
 
 __device__ __forceinline__ bool request_valid(const int32_t* x0, const int32_t* dt, int b, int gamma, int V) {
@@ -169,6 +189,20 @@ hipError_t launch_survival(const SurvivalArgs& a, bool bf16, hipStream_t s) {
     TileArgs ta = {};
     ta.U = a.U;
     ta.W1 = a.W1;
+    if (a.E != nullptr) {
+      if (bf16) {
+        const long long n = (long long)rows * a.r;
+        hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.E, n, a.r,
+                           w.opnd);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ta.W1 = w.opnd;
+        ta.opnd_rows = 2;
+      } else {
+        ta.W1 = a.E;
+        ta.opnd_rows = 1;
+      }
+    }
     ta.W2 = a.W2;
     ta.x0 = a.x0;
     ta.tokens = a.draft_tokens;

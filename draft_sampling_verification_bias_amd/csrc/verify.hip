@@ -134,6 +134,16 @@ __device__ __forceinline__ double wval(const void* W, size_t idx) {
   }
 }
 
+// Element j of the draft's operand row at block position k (1-based) of
+// request b: the RNN head's e_k (float32, "Instantiation 2: The RNN Head",
+// Eq. 6) when the draft's rows are given, else the Markov head's W1[prev]
+// (Eq. 5).
+template <bool kBf16>
+__device__ __forceinline__ double opnd_val(const VerifyArgs& a, int b, int k, int prev, int j) {
+  if (a.E != nullptr) return (double)a.E[((size_t)b * a.gamma + (k - 1)) * a.r + j];
+  return wval<kBf16>(a.W1, (size_t)prev * a.r + j);
+}
+
 // ---------------------------------------------------------------------------
 // Target-row statistics, shared with dspark_survival.
 //   list mode (list != null): row li is request list[li / rows_per_req] at
@@ -333,8 +343,8 @@ __global__ __launch_bounds__(kVThreads) void verify_init_kernel(VerifyArgs a, Ve
   const int draw_blocks = (a.B * per_req + kVThreads - 1) / kVThreads;
   if (blockIdx.x > draw_blocks) {
     // The draft logit of every drafted token (needed after a rejection), one
-    // wave per (request, position): l = U[x] + W1[x_prev] . W2[:, x] with
-    // float64 products of the exact weights.
+    // wave per (request, position): l = U[x] + e . W2[:, x] with float64
+    // products of the exact weights, e = W1[x_prev] or the RNN draft's e_k.
     const int item = (blockIdx.x - 1 - draw_blocks) * (kVThreads / kWave) + threadIdx.x / kWave;
     if (item >= a.B * g) return;
     const int b = item / g, k = item - b * g;  // k 0-based
@@ -350,8 +360,9 @@ __global__ __launch_bounds__(kVThreads) void verify_init_kernel(VerifyArgs a, Ve
       for (int m = 0; m < 4; ++m) {
         const int j = j0 + lane + m * kWave;
         const int jc = j < a.r ? j : 0;
-        e[m] = wbf16 ? bf16_to_float(reinterpret_cast<const uint16_t*>(a.W1)[(size_t)prev * a.r + jc])
-                     : reinterpret_cast<const float*>(a.W1)[(size_t)prev * a.r + jc];
+        e[m] = a.E ? a.E[((size_t)b * g + k) * a.r + jc]
+                   : wbf16 ? bf16_to_float(reinterpret_cast<const uint16_t*>(a.W1)[(size_t)prev * a.r + jc])
+                           : reinterpret_cast<const float*>(a.W1)[(size_t)prev * a.r + jc];
         const size_t wi = a.W2T ? (size_t)x * a.r + jc : (size_t)jc * a.V + x;
         const void* W2x = a.W2T ? a.W2T : a.W2;
         wv[m] = wbf16 ? bf16_to_float(reinterpret_cast<const uint16_t*>(W2x)[wi])
@@ -449,7 +460,8 @@ __device__ int sample_target(const DecideCtx& c, double u, PickScratch& ps, doub
   return ts * kTgtCols + col;
 }
 
-// Draft logit U[v] + W1[prev] . W2[:, v] in float64 (all threads receive it).
+// Draft logit U[v] + e . W2[:, v] in float64 with the operand row e staged in
+// sw1 (all threads receive it).
 template <bool kBf16>
 __device__ double draft_logit(const VerifyArgs& a, const float* urow, const double* sw1, int v, double* red) {
   double s = 0.0;
@@ -536,7 +548,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_generic_kernel(Verify
           }
           if (!accepted) {
             const int prev = k == 1 ? a.x0[b] : a.draft_tokens[(size_t)b * g + k - 2];
-            for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1[j] = wval<kBf16>(a.W1, (size_t)prev * a.r + j);
+            for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1[j] = opnd_val<kBf16>(a, b, k, prev, j);
             __syncthreads();
             const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
             const double lx = draft_logit<kBf16>(a, urow, sw1, x, sred);
@@ -752,10 +764,12 @@ __device__ __forceinline__ void col_draw(const float* trow, int V, int ts, float
   x_out = __shfl(xc, owner);
 }
 
-// Draft logit U[v] + W1[prev] . W2[:, v] in float64, summed by a group of kW
-// lanes (lane li takes k = li + kW m); v may differ between groups.
+// Draft logit U[v] + e . W2[:, v] in float64, summed by a group of kW lanes
+// (lane li takes k = li + kW m); v may differ between groups.  e is the RNN
+// draft's operand row erow when given, else W1[prev].
 template <int kW, bool kBf16>
-__device__ __forceinline__ double draft_logit_at(const VerifyArgs& a, const float* urow, int prev, int v) {
+__device__ __forceinline__ double draft_logit_at(const VerifyArgs& a, const float* urow, const float* erow, int prev,
+                                                 int v) {
   constexpr int kCh = 256 / kW;  // products per lane per 256 k
   const int li = threadIdx.x & (kW - 1);
   const float uv = urow[v];
@@ -766,7 +780,7 @@ __device__ __forceinline__ double draft_logit_at(const VerifyArgs& a, const floa
     for (int m = 0; m < kCh; ++m) {
       const int k = k0 + li + kW * m;
       const int kc = k < a.r ? k : 0;  // clamped: all loads issued before the first use
-      e[m] = (float)wval<kBf16>(a.W1, (size_t)prev * a.r + kc);
+      e[m] = erow ? erow[kc] : (float)wval<kBf16>(a.W1, (size_t)prev * a.r + kc);
       // with the transposed copy, the k of one load instruction are contiguous
       wv[m] = a.W2T ? (float)wval<kBf16>(a.W2T, (size_t)v * a.r + kc) : (float)wval<kBf16>(a.W2, (size_t)kc * a.V + v);
     }
@@ -923,6 +937,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
       // always holds a kept proposal, so a second batch (another three
       // dependent memory round trips) is rare.
       const float* urow = a.U + ((size_t)b * g + (k - 1)) * (size_t)a.V;
+      const float* erow = a.E ? a.E + ((size_t)b * g + (k - 1)) * a.r : nullptr;
       auto keep_test = [&](double ua, int v, float tv, double lv) -> bool {
         const double ptv = exp2((double)(tv - s.M) * cf) / s.Z;
         const double pdv = pdx * exp((lv - lx) * a.inv_t_d);
@@ -986,7 +1001,7 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
         int v;
         float tv;
         col_draw<16>(trow, a.V, ts, mt, s.M, cf_f, cf, ql, v, tv);
-        const double lv = draft_logit_at<16, kBf16>(a, urow, prev, v);
+        const double lv = draft_logit_at<16, kBf16>(a, urow, erow, prev, v);
         const int i = i0 + 4 * wave + grp;
         const bool pass = i < DSPARK_MAX_RESIDUAL_PROPOSALS && keep_test(ua, v, tv, lv);
         const unsigned long long kept = __ballot(pass && (lane & 15) == 0);
@@ -1108,7 +1123,7 @@ __global__ __launch_bounds__(kVThreads) void residual_stats_kernel(VerifyArgs a,
     const int chunk = (int)(it - (long long)li * ntr);
     const int b = w.fb_list[li];
     const FallbackInfo f = w.fb[b];
-    for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1f[j] = (float)wval<kBf16>(a.W1, (size_t)f.prev * a.r + j);
+    for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1f[j] = (float)opnd_val<kBf16>(a, b, f.j, f.prev, j);
     __syncthreads();
     const double res = residual_term<kBf16>(a, f, b, chunk, sw1f, sbias, (double)cf_f);
     const double s = block_sum<kVThreads, double>(res, sred);
@@ -1135,7 +1150,7 @@ __global__ __launch_bounds__(kVThreads) void residual_select_kernel(VerifyArgs a
     const int ts = block_pick_uniform<kVThreads>(ntr, chunk_mass, u, ps, &base, &total);
     int y;
     if (total > 0.0 && ts >= 0) {
-      for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1f[j] = (float)wval<kBf16>(a.W1, (size_t)f.prev * a.r + j);
+      for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1f[j] = (float)opnd_val<kBf16>(a, b, f.j, f.prev, j);
       __syncthreads();
       const double res = residual_term<kBf16>(a, f, b, ts, sw1f, sbias, (double)cf_f);
       sterm[threadIdx.x] = res;

@@ -215,6 +215,13 @@ size_t dspark_static_scratch_bytes(void);
  * The cell computes in float32 (the precision of Wp and hp); e_k enters the
  * bf16 tile pass as two bf16 parts (e_k to about 2^-18 relative).  A position after an invalid anchor or
  * token is -1 / NaN as in dspark_markov_draft.
+ * The hidden state enters only through hp: the library takes the product
+ * W_p[:, 2r:] h_k, not h_k and that block of W_p, because it depends on no
+ * drafted token and is one dense GEMM of the backbone's parallel stage.
+ * To verify an RNN draft or take its survival products, pass e_out as the
+ * draft_rows argument of dspark_verify and dspark_survival: without it they
+ * rebuild p_d from the Markov head, which is not the law these tokens were
+ * drawn from.
  * Workspace: dspark_workspace_size(DSPARK_OP_RNN_DRAFT, B, gamma, V, r).
  * Errors: DSPARK_ERR_UNSUPPORTED for float32 weights, otherwise as
  * dspark_markov_draft.
@@ -239,7 +246,9 @@ dspark_status dspark_rnn_draft(const float* U, const void* W1, const void* W2, d
  * index i) are kept with probability max(0, 1 - p_d^j(v) / p_t^j(v)) (stream 2,
  * word 1); after DSPARK_MAX_RESIDUAL_PROPOSALS misses the residual itself is
  * drawn by inverse CDF with the stream-3 uniform at (round, j).  p_d^j(v) is
- * rebuilt from U, W1, W2 and x_{j-1}.  If all gamma positions pass (n = gamma)
+ * rebuilt from U, W2 and the draft's operand row: W1[x_{j-1}] of the Markov
+ * head, or e_j of an RNN draft when draft_rows is given.  If all gamma
+ * positions pass (n = gamma)
  * a bonus token is drawn from p_t^{gamma+1} with the stream-2 uniform at
  * (round, gamma+1, index 0).
  * At T == 0 acceptance is the exact match x_k == argmax target[b][k] and the
@@ -261,7 +270,14 @@ dspark_status dspark_rnn_draft(const float* U, const void* W1, const void* W2, d
  * as written by dspark_transpose_w2.  When given, p_d at a single token reads
  * one contiguous row of W2T instead of r elements spread over W2; the results
  * differ from the W2-only path only by the summation order of float64 sums.
- * Inputs draft_tokens / draft_prob are dspark_markov_draft's outputs.
+ * Inputs draft_tokens / draft_prob are the draft's outputs (dspark_markov_draft
+ * or dspark_rnn_draft).
+ * draft_rows is optional: NULL for a Markov-head draft; for a draft of the RNN
+ * head ([R] "Instantiation 2: The RNN Head", Eq. 6, which the decode round of
+ * [R] "Putting It All Together" verifies like the Markov head's), float32
+ * [B][gamma][r], the e_k rows dspark_rnn_draft writes to e_out, so that p_d^k
+ * = softmax((U_k + e_k W2) / T) is the law x_k was drawn from.  Not read at
+ * T == 0.
  * Outputs:
  *   accept_len   int32   [B]          n in 0..l (l = gamma without lengths)
  *   out_tokens   int32   [B][gamma+1] x_1..x_n, then the correction or bonus
@@ -272,7 +288,8 @@ dspark_status dspark_rnn_draft(const float* U, const void* W1, const void* W2, d
  */
 dspark_status dspark_verify(const float* U, const void* W1, const void* W2, const void* W2T, dspark_dtype wdtype,
                             const int32_t* x0, const int32_t* draft_tokens,
-                            const float* draft_prob, const float* target_logits, const int32_t* lengths,
+                            const float* draft_prob, const float* draft_rows, const float* target_logits,
+                            const int32_t* lengths,
                             int B, int gamma, int V, int r, float temperature,
                             const uint64_t* seeds, uint64_t round,
                             int32_t* accept_len, int32_t* out_tokens, float* accept_prob,
@@ -302,6 +319,10 @@ dspark_status dspark_transpose_w2(const void* W2, dspark_dtype wdtype, int r, in
  * clamp of [Z], at every block position k = 1..gamma along the drafted prefix;
  * p_d^k(v) = exp(l_k(v) / T - draft_lse[b][k]).  At T == 0, c*_k is the
  * indicator x_k == argmax target[b][k].
+ * draft_rows as for dspark_verify: NULL for a Markov-head draft (l_k = U_k +
+ * W1[x_{k-1}] W2), or float32 [B][gamma][r], the e_k rows of an RNN draft
+ * (l_k = U_k + e_k W2; finite values; with bf16 weights e_k enters the tile
+ * pass as two bf16 parts, as in dspark_rnn_draft).
  *
  * Outputs: c_star float32 [B][gamma] (analytical mode; NULL to skip) and
  * survival float32 [B][gamma].
@@ -310,7 +331,7 @@ dspark_status dspark_transpose_w2(const void* W2, dspark_dtype wdtype, int r, in
  */
 dspark_status dspark_survival(const float* U, const void* W1, const void* W2, dspark_dtype wdtype,
                               const int32_t* x0, const int32_t* draft_tokens,
-                              const float* draft_lse, const float* target_logits,
+                              const float* draft_lse, const float* draft_rows, const float* target_logits,
                               const float* conf, int B, int gamma, int V, int r,
                               float temperature, float* c_star, float* survival,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);

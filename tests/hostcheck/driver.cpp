@@ -120,39 +120,53 @@ int main() {
   const size_t wsv = dspark_workspace_size(DSPARK_OP_VERIFY, 8, 4, 5000, 64);
   reset();
   CHECK(dspark_verify((const float*)P(A), P(Bp), P(C), P(J), DSPARK_BF16, (const int32_t*)P(D), (const int32_t*)P(F),
-                      (const float*)P(G), (const float*)P(K), (const int32_t*)P(L), 8, 4, 5000, 64, 1.0f,
+                      (const float*)P(G), nullptr, (const float*)P(K), (const int32_t*)P(L), 8, 4, 5000, 64, 1.0f,
                       (const uint64_t*)P(E), 5, (int32_t*)P(H), (int32_t*)P(I), (float*)P(A + 0x1000), P(0xD0000), wsv,
                       nullptr) == DSPARK_OK);
-  CHECK(strcmp(last.op, "verify") == 0 && last.p[1] == P(J) && last.p[2] == P(K) && last.p[3] == P(L));
+  CHECK(strcmp(last.op, "verify") == 0 && last.p[1] == P(J) && last.p[2] == P(K) && last.p[3] == P(L) &&
+        last.p[5] == nullptr);
+  reset();
+  CHECK(dspark_verify((const float*)P(A), P(Bp), P(C), nullptr, DSPARK_BF16, (const int32_t*)P(D),
+                      (const int32_t*)P(F), (const float*)P(G), (const float*)P(A + 0x2000), (const float*)P(K),
+                      nullptr, 8, 4, 5000, 64, 1.0f, (const uint64_t*)P(E), 5, (int32_t*)P(H), (int32_t*)P(I), nullptr,
+                      P(0xD0000), wsv, nullptr) == DSPARK_OK);
+  CHECK(last.p[5] == P(A + 0x2000));  // the RNN draft's operand rows
   reset();
   CHECK(dspark_verify(nullptr, nullptr, nullptr, nullptr, DSPARK_BF16, (const int32_t*)P(D), (const int32_t*)P(F),
-                      nullptr, (const float*)P(K), nullptr, 8, 4, 5000, 64, 0.0f, nullptr, 5, (int32_t*)P(H),
+                      nullptr, nullptr, (const float*)P(K), nullptr, 8, 4, 5000, 64, 0.0f, nullptr, 5, (int32_t*)P(H),
                       (int32_t*)P(I), nullptr, P(0xD0000), wsv, nullptr) == DSPARK_OK);
   CHECK(last.p[1] == nullptr);  // no W2T at T == 0
   reset();
   CHECK(dspark_verify(nullptr, nullptr, nullptr, nullptr, DSPARK_BF16, (const int32_t*)P(D), (const int32_t*)P(F),
-                      nullptr, (const float*)P(K), nullptr, 8, 4, 5000, 64, 1.0f, nullptr, 5, (int32_t*)P(H),
+                      nullptr, nullptr, (const float*)P(K), nullptr, 8, 4, 5000, 64, 1.0f, nullptr, 5, (int32_t*)P(H),
                       (int32_t*)P(I), nullptr, P(0xD0000), wsv, nullptr) == DSPARK_ERR_INVALID_ARGUMENT);
   CHECK(last.op[0] == 0);
   reset();
   CHECK(dspark_verify((const float*)P(A), P(Bp), P(C), nullptr, DSPARK_BF16, (const int32_t*)P(D),
-                      (const int32_t*)P(F), (const float*)P(G), (const float*)P(K), nullptr, 8, 4, 5000, 64, 1.0f,
-                      (const uint64_t*)P(E), 5, (int32_t*)P(H), (int32_t*)P(I), nullptr, P(0xD0000), wsv - 1,
+                      (const int32_t*)P(F), (const float*)P(G), nullptr, (const float*)P(K), nullptr, 8, 4, 5000, 64,
+                      1.0f, (const uint64_t*)P(E), 5, (int32_t*)P(H), (int32_t*)P(I), nullptr, P(0xD0000), wsv - 1,
                       nullptr) == DSPARK_ERR_WORKSPACE);
 
   // survival: confidence mode needs nothing else; analytical mode validates
   reset();
-  CHECK(dspark_survival(nullptr, nullptr, nullptr, DSPARK_BF16, nullptr, nullptr, nullptr, nullptr,
+  CHECK(dspark_survival(nullptr, nullptr, nullptr, DSPARK_BF16, nullptr, nullptr, nullptr, nullptr, nullptr,
                         (const float*)P(A), 8, 4, 2, 16, 0.0f, nullptr, (float*)P(Bp), nullptr, 0, nullptr) ==
         DSPARK_OK);
   CHECK(strcmp(last.op, "survival_conf") == 0 && last.p[0] == P(A) && last.p[1] == P(Bp));
   reset();
-  CHECK(dspark_survival(nullptr, nullptr, nullptr, DSPARK_BF16, nullptr, nullptr, nullptr, nullptr,
+  CHECK(dspark_survival(nullptr, nullptr, nullptr, DSPARK_BF16, nullptr, nullptr, nullptr, nullptr, nullptr,
                         (const float*)P(A + 2), 8, 4, 2, 16, 0.0f, nullptr, (float*)P(Bp), nullptr, 0, nullptr) ==
         DSPARK_ERR_INVALID_ARGUMENT);
-  CHECK(dspark_survival(nullptr, nullptr, nullptr, DSPARK_BF16, nullptr, nullptr, nullptr, nullptr, nullptr, 8, 4,
-                        5000, 64, 1.0f, nullptr, (float*)P(Bp), P(C), 1 << 30, nullptr) ==
+  CHECK(dspark_survival(nullptr, nullptr, nullptr, DSPARK_BF16, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        8, 4, 5000, 64, 1.0f, nullptr, (float*)P(Bp), P(C), 1 << 30, nullptr) ==
         DSPARK_ERR_INVALID_ARGUMENT);
+  // analytical mode forwards the RNN draft's operand rows
+  reset();
+  CHECK(dspark_survival((const float*)P(A), P(Bp), P(C), DSPARK_BF16, (const int32_t*)P(D), (const int32_t*)P(F),
+                        (const float*)P(G), (const float*)P(A + 0x2000), (const float*)P(K), nullptr, 8, 4, 5000, 64,
+                        1.0f, nullptr, (float*)P(H), P(0xD0000), dspark_workspace_size(DSPARK_OP_SURVIVAL, 8, 4, 5000,
+                        64), nullptr) == DSPARK_OK);
+  CHECK(strcmp(last.op, "survival") == 0 && last.p[3] == P(A + 0x2000));
 
   // schedule: candidate limit, table length, modes
   reset();

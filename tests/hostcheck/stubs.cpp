@@ -48,6 +48,7 @@ hipError_t launch_verify(const VerifyArgs& a, bool bf16, hipStream_t) {
   last.B = a.B; last.gamma = a.gamma; last.V = a.V; last.r = a.r; last.T = a.temperature; last.bf16 = bf16;
   last.ws = a.ws; last.round = a.round;
   last.p[0] = a.U; last.p[1] = a.W2T; last.p[2] = a.target; last.p[3] = a.lengths; last.p[4] = a.accept_prob;
+  last.p[5] = a.E;
   return hipSuccess;
 }
 
@@ -55,7 +56,7 @@ hipError_t launch_survival(const SurvivalArgs& a, bool, hipStream_t) {
   last = hostcheck::Record{};
   strcpy(last.op, a.conf ? "survival_conf" : "survival");
   last.B = a.B; last.gamma = a.gamma; last.V = a.V; last.r = a.r; last.ws = a.ws;
-  last.p[0] = a.conf; last.p[1] = a.survival; last.p[2] = a.c_star;
+  last.p[0] = a.conf; last.p[1] = a.survival; last.p[2] = a.c_star; last.p[3] = a.E;
   return hipSuccess;
 }
 

@@ -47,8 +47,20 @@ def _verify(task):
     return b, {k: v[b].copy() for k, v in r.items()}
 
 
+def _survival(task):
+    import oracle
+    b, tokens = task
+    w = _W
+    B, gamma = w["U"].shape[:2]
+    tok = np.full((B, gamma), -1, dtype=np.int32)
+    tok[b] = tokens
+    c, a = oracle.survival(w["U"], w["W1"], w["W2"], w["x0"], tok, w["tgt"], w["T"], requests=[b])
+    return b, {"c_star": c[b].copy(), "survival": a[b].copy()}
+
+
 class OraclePool:
-    """with OraclePool(wl) as pool: pool.draft(reqs), pool.verify(reqs, tokens)."""
+    """with OraclePool(wl) as pool: pool.draft(reqs), pool.verify(reqs, tokens),
+    pool.survival(reqs, tokens)."""
 
     def __init__(self, wl, workers=None):
         self.wl = wl
@@ -94,3 +106,12 @@ class OraclePool:
         return self._merge(res, {"accept_len": ((B,), -1, np.int32), "out_tokens": ((B, gamma + 1), -1, np.int32),
                                  "accept_prob": ((B, gamma), np.nan, np.float64),
                                  "min_dist": ((B,), np.inf, np.float64)})
+
+    def survival(self, reqs, tokens):
+        """(c_star, survival) of the analytical mode, [B][gamma] each (NaN
+        outside ``reqs``)."""
+        B, gamma = self.wl.B, self.wl.gamma
+        res = self.pool.map(_survival, [(b, np.asarray(tokens[b], dtype=np.int32)) for b in reqs], chunksize=1)
+        out = self._merge(res, {"c_star": ((B, gamma), np.nan, np.float64),
+                                "survival": ((B, gamma), np.nan, np.float64)})
+        return out["c_star"], out["survival"]

@@ -153,10 +153,10 @@ def test_draft_workspace_holds_either_schedule_of_the_loop():
 
 
 def _verify(lib, **kw):
-    a = dict(U=FAKE, W1=FAKE, W2=FAKE, W2T=None, wd=1, x0=FAKE, dt=FAKE, dp=FAKE, tgt=FAKE, lens=None, B=4, gamma=4,
-             V=1000, r=16, T=1.0, seeds=FAKE, rnd=0, alen=FAKE, otok=FAKE, aprob=None, ws=FAKE, wsb=1 << 30)
+    a = dict(U=FAKE, W1=FAKE, W2=FAKE, W2T=None, wd=1, x0=FAKE, dt=FAKE, dp=FAKE, E=None, tgt=FAKE, lens=None, B=4,
+             gamma=4, V=1000, r=16, T=1.0, seeds=FAKE, rnd=0, alen=FAKE, otok=FAKE, aprob=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
-    return lib.dspark_verify(a["U"], a["W1"], a["W2"], a["W2T"], a["wd"], a["x0"], a["dt"], a["dp"], a["tgt"],
+    return lib.dspark_verify(a["U"], a["W1"], a["W2"], a["W2T"], a["wd"], a["x0"], a["dt"], a["dp"], a["E"], a["tgt"],
                              a["lens"], a["B"], a["gamma"], a["V"], a["r"], a["T"], a["seeds"], a["rnd"], a["alen"],
                              a["otok"], a["aprob"], a["ws"], a["wsb"], None)
 
@@ -165,7 +165,7 @@ def _verify(lib, **kw):
     (dict(B=70000), INVALID), (dict(tgt=None), INVALID), (dict(alen=None), INVALID),
     (dict(dp=None), INVALID), (dict(tgt=MISALIGNED), INVALID), (dict(wd=9), UNSUPPORTED),
     (dict(wsb=0), WORKSPACE), (dict(T=-0.5), INVALID), (dict(W2T=MISALIGNED), INVALID),
-    (dict(lens=MISALIGNED - 2), INVALID),
+    (dict(lens=MISALIGNED - 2), INVALID), (dict(E=MISALIGNED - 2), INVALID),
 ])
 def test_verify_rejects_bad_arguments(lib, kw, status):
     assert _verify(lib, **kw) == status
@@ -174,15 +174,19 @@ def test_verify_rejects_bad_arguments(lib, kw, status):
 def test_survival_rejects_bad_arguments(lib):
     s = lib.dspark_survival
     # confidence mode: bad sizes, missing output
-    assert s(None, None, None, 1, None, None, None, None, FAKE, 0, 4, 2, 16, 0.0, None, FAKE, None, 0, None) == INVALID
-    assert s(None, None, None, 1, None, None, None, None, FAKE, 4, 4, 2, 16, 0.0, None, None, None, 0, None) == INVALID
-    # analytical mode: missing target, bad dtype, small workspace
-    assert s(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 1 << 30,
+    assert s(None, None, None, 1, None, None, None, None, None, FAKE, 0, 4, 2, 16, 0.0, None, FAKE, None, 0,
              None) == INVALID
-    assert s(FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 1 << 30,
+    assert s(None, None, None, 1, None, None, None, None, None, FAKE, 4, 4, 2, 16, 0.0, None, None, None, 0,
+             None) == INVALID
+    # analytical mode: missing target, bad dtype, small workspace, misaligned draft rows
+    assert s(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, None, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 1 << 30,
+             None) == INVALID
+    assert s(FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None, FAKE, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 1 << 30,
              None) == UNSUPPORTED
-    assert s(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 8,
+    assert s(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE, 8,
              None) == WORKSPACE
+    assert s(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, MISALIGNED - 2, FAKE, None, 4, 4, 1000, 16, 1.0, None, FAKE, FAKE,
+             1 << 30, None) == INVALID
 
 
 def test_transpose_w2_rejects_bad_arguments(lib):

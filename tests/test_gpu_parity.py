@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 import workloads
+from oracle_pool import OraclePool
 from parity import (Dev, compare_draft, compare_survival, compare_verify, f64_weights, seeds_tensor)
 
 torch = pytest.importorskip("torch")
@@ -190,18 +191,48 @@ def test_tiny_fp32_temperature_07():
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads: GPU on all requests, oracle on a sample.
+# Full-size workloads, every request: the GPU path as the benchmark launches
+# it (per-position draft, verify with and without W2T, analytical survival),
+# then the oracle over all requests in a pool of worker processes.  At most
+# one request may differ, and only where the oracle's uniform lies within the
+# exemption radius of a decision boundary.
 # ---------------------------------------------------------------------------
 FULL = ["v151936_b32", "v151936_b256_t07", "greedy_v151936_b512", "v262144_b128"]
 
 
+@pytest.mark.slow
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_parity(name):
+def test_full_size_every_request(name):
     wl = workloads.make(name)
-    rng = np.random.default_rng(11)
-    reqs = sorted(set([0, wl.B - 1] + rng.choice(wl.B, size=4, replace=False).tolist()))
-    run_path(wl, reqs, name)
+    B = wl.B
+    say("[full %s] B=%d V=%d r=%d gamma=%d T=%g" % (name, B, wl.V, wl.r, wl.gamma, wl.T))
+    d = Dev(wl)
+    tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
+    outs = [dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd)]
+    if wl.T > 0:
+        outs.append(dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd,
+                               W2T=dsp.transpose_w2(d.W2)))
+    cst, surv = dsp.survival(d.U, d.W1, d.W2, d.x0, tok, lse, d.tgt, wl.T)
+    torch.cuda.synchronize()
+    tok_h, prob_h, lse_h = tok.cpu().numpy(), prob.cpu().numpy(), lse.cpu().numpy()
+    vouts = [[t.cpu().numpy() for t in o] for o in outs]
+    cst_h, surv_h = cst.cpu().numpy(), surv.cpu().numpy()
+    del d, outs, tok, prob, lse, cst, surv
     torch.cuda.empty_cache()
+    with OraclePool(wl) as pool:
+        ref = pool.draft(range(B))
+        n, ex, whole = compare_draft(ref, tok_h, prob_h, lse_h, range(B), wl.T)
+        say("[full %s] draft: %d positions equal, %d exempt, %d whole requests" % (name, n, ex, len(whole)))
+        assert ex <= 1 and len(whole) >= B - 1
+        reqs = sorted(whole)
+        vref = pool.verify(reqs, tok_h)
+        for i, (alen, otok, aprob) in enumerate(vouts):
+            nv, exv = compare_verify(vref, alen, otok, aprob, reqs, wl.T)
+            say("[full %s] verify%s: %d requests equal, %d exempt" % (name, " with W2T" if i else "", nv, exv))
+            assert exv <= 1 and nv >= len(reqs) - 1
+        rc, ra = pool.survival(reqs, tok_h)
+        compare_survival(rc, ra, cst_h, surv_h, reqs)
+        say("[full %s] survival: %d requests equal" % (name, len(reqs)))
 
 
 @pytest.mark.parametrize("dtype,r,V", [(torch.bfloat16, 256, 151936), (torch.bfloat16, 48, 1001),
@@ -347,3 +378,32 @@ def test_exact_residual_fallback_rows():
     rejected = int((alen.cpu().numpy() < gamma).sum())
     say("[fallback] %d requests equal, %d exempt, %d rejected" % (nv, exv, rejected))
     assert rejected >= 20
+
+
+@pytest.mark.parametrize("name,kw", [("v151936_b32", dict(B=21, V=5003, gamma=4, r=64)),
+                                     ("tiny_v1000_b4", dict(B=9, V=2000, gamma=3, r=32))])
+def test_operand_rows_of_the_markov_head_reproduce_its_verify_and_survival(name, kw):
+    # draft_rows = the Markov draft's own operand rows W1[x_{k-1}] (float32)
+    # give the same law as no rows, so verify and survival agree with the
+    # oracle run without rows, for bf16 (two-part split with a zero remainder)
+    # and float32 weights alike
+    wl = workloads.make(name, **kw)
+    say("[markov rows %s %s]" % (name, kw))
+    d = Dev(wl)
+    tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, wl.rnd)
+    prev = torch.cat([d.x0[:, None], tok[:, :-1]], dim=1).long()
+    E = d.W1.float()[prev].contiguous()
+    tok_h = tok.cpu().numpy()
+    W1f, W2f = f64_weights(wl)
+    ref = oracle.markov_draft(wl.U, W1f, W2f, wl.x0, wl.T, wl.seeds, wl.rnd)
+    _, _, whole = compare_draft(ref, tok_h, prob.cpu().numpy(), lse.cpu().numpy(), range(wl.B), wl.T)
+    reqs = sorted(whole)
+    vref = oracle.verify(wl.U, W1f, W2f, wl.x0, tok_h, wl.tgt, wl.T, wl.seeds, wl.rnd, requests=reqs)
+    alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd, E=E)
+    torch.cuda.synchronize()
+    nv, exv = compare_verify(vref, alen.cpu().numpy(), otok.cpu().numpy(), aprob.cpu().numpy(), reqs, wl.T)
+    assert nv > 0 and exv <= 1
+    cst, surv = dsp.survival(d.U, d.W1, d.W2, d.x0, tok, lse, d.tgt, wl.T, E=E)
+    torch.cuda.synchronize()
+    rc, ra = oracle.survival(wl.U, W1f, W2f, wl.x0, tok_h, wl.tgt, wl.T, requests=reqs)
+    compare_survival(rc, ra, cst.cpu().numpy(), surv.cpu().numpy(), reqs)

@@ -1,6 +1,9 @@
 """GPU parity of dspark_rnn_draft (block sampling with the RNN head of DSpark,
 "Instantiation 2: The RNN Head", Eq. 6) against the float64 oracle, through
-the C ABI.
+the C ABI -- and of the verification and survival products of its drafts
+(dspark_verify / dspark_survival given the draft's operand rows e_k, the
+decode round of "Putting It All Together" feeding either head's block to the
+target) against oracle.verify / oracle.survival with the oracle's own e_k.
 
 The oracle runs the cell in float64 with e_k unrounded; the library runs the
 cell in float32 (the precision of its inputs Wp and hp) and feeds e_k to the
@@ -15,7 +18,7 @@ import pytest
 
 import oracle
 import workloads
-from parity import Dev, compare_draft, f64_weights
+from parity import Dev, compare_draft, compare_survival, compare_verify, f64_weights
 
 torch = pytest.importorskip("torch")
 dsp = pytest.importorskip("draft_sampling_verification_bias_amd")
@@ -42,7 +45,7 @@ def _device():
     torch.cuda.synchronize()
 
 
-def run_rnn(wl, reqs, label, seed=0):
+def run_rnn(wl, reqs, label, seed=0, check_verify=True):
     say("[%s] rnn draft B=%d V=%d r=%d gamma=%d T=%g" % (label, wl.B, wl.V, wl.r, wl.gamma, wl.T))
     assert wl.wdtype == "bf16"
     Wp, hp = workloads.rnn_inputs(wl.B, wl.gamma, wl.r, seed=seed)
@@ -60,6 +63,24 @@ def run_rnn(wl, reqs, label, seed=0):
     for b in whole:
         err = np.abs(e_h[b] - ref["E"][b]).max()
         assert err <= E_ATOL, "e_k of request %d: max |gpu - oracle| = %.3g" % (b, err)
+    if check_verify and whole:
+        vreq = sorted(whole)
+        vref = oracle.verify(wl.U, W1f, W2f, wl.x0, tok_h, wl.tgt, wl.T, wl.seeds, wl.rnd, requests=vreq,
+                             E=ref["E"])
+        variants = [None] + ([dsp.transpose_w2(d.W2)] if wl.T > 0 else [])
+        for W2T in variants:
+            alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd, E=e,
+                                           W2T=W2T)
+            torch.cuda.synchronize()
+            nv, exv = compare_verify(vref, alen.cpu().numpy(), otok.cpu().numpy(), aprob.cpu().numpy(), vreq, wl.T)
+            say("[%s] verify of the rnn draft%s: %d requests equal, %d exempt; mean accepted %.3f"
+                % (label, " with W2T" if W2T is not None else "", nv, exv, alen.cpu().numpy()[vreq].mean()))
+            assert nv > 0 and exv <= 1
+        cst, surv = dsp.survival(d.U, d.W1, d.W2, d.x0, tok, lse, d.tgt, wl.T, E=e)
+        torch.cuda.synchronize()
+        rc, ra = oracle.survival(wl.U, W1f, W2f, wl.x0, tok_h, wl.tgt, wl.T, requests=vreq, E=ref["E"])
+        compare_survival(rc, ra, cst.cpu().numpy(), surv.cpu().numpy(), vreq)
+        say("[%s] survival of the rnn draft: %d requests equal" % (label, len(vreq)))
     return tok_h, e_h, ref
 
 
