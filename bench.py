@@ -342,8 +342,8 @@ def main():
         surv_ms = (time.perf_counter() - s0) / args.survival_steps * 1e3
 
     # The scheduled round of the pages' production flow, reported beside the
-    # gated path: confidence head (Eq. 7, synthetic hidden states of width
-    # 4096 and per-position temperatures) on the drafted tokens, survival
+    # gated path: the draft with its fused confidence head (Eq. 7, synthetic
+    # hidden states of width 4096 and per-position temperatures), survival
     # products of the confidences, prefix scheduler with a synthetic profiled
     # throughput table, verification at the scheduled lengths.  The same
     # drafted round is also verified whole for comparison.
@@ -361,8 +361,14 @@ def main():
         theta = torch.empty((1,), dtype=torch.float64, device=dev)
         vo = vouts[0]
 
+        head = (hd, wd_, stsd)
+        dcout = (dout[0], dout[1], dout[2], conf)
+
+        def draft_conf(rnd):
+            dsp.markov_draft(U, W1, W2, x0, T, seeds, rnd, out=dcout, workspace=ws_d, stream=stream, W2T=W2T_d,
+                             conf_head=head)
+
         def plan():
-            dsp.confidence(hd, wd_, W1, x0, dout[0], sts=stsd, out=conf, stream=stream)
             dsp.survival(None, None, None, None, None, None, None, T, conf=conf, out=(None, sv), stream=stream)
             dsp.schedule(sv, sps, out=(lengths, theta), stream=stream)
 
@@ -379,7 +385,9 @@ def main():
             torch.cuda.synchronize()
             return (time.perf_counter() - t) / args.schedule_steps * 1e3
 
-        dsp.markov_draft(U, W1, W2, x0, T, seeds, 2000, out=dout, workspace=ws_d, stream=stream)
+        draft_ms = timed(lambda i: dsp.markov_draft(U, W1, W2, x0, T, seeds, 2000, out=dout, workspace=ws_d,
+                                                    stream=stream, W2T=W2T_d))
+        draft_conf_ms = timed(lambda i: draft_conf(2000))
         plan_ms = timed(lambda i: plan())
         full_ms = timed(lambda i: verify_at(None, 2000))
         full_len = vo[0].cpu().numpy()
@@ -387,14 +395,15 @@ def main():
         sch_len = vo[0].cpu().numpy()
 
         def round_scheduled(i):
-            dsp.markov_draft(U, W1, W2, x0, T, seeds, 3000 + i, out=dout, workspace=ws_d, stream=stream, W2T=W2T_d)
+            draft_conf(3000 + i)
             plan()
             verify_at(lengths, 3000 + i)
 
         round_ms = timed(round_scheduled)
         lens_h = lengths.cpu().numpy()
-        sched = {"flow": "draft, confidence head (d=%d, STS), survival of the confidences, schedule, verify at the "
-                         "scheduled lengths" % d_hidden,
+        sched = {"flow": "draft with the fused confidence head (d=%d, STS), survival of the confidences, "
+                         "schedule, verify at the scheduled lengths" % d_hidden,
+                 "draft_ms": draft_ms, "draft_with_confidence_ms": draft_conf_ms,
                  "sps": "1/(1+(n/%g)^%g), n = verified tokens" % (half, power),
                  "plan_ms": plan_ms, "mean_length": float(lens_h.mean()),
                  "theta_best": float(theta.cpu().numpy()[0]),

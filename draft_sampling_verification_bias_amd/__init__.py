@@ -61,9 +61,9 @@ def load():
     lib.dspark_markov_bias.restype = I
     lib.dspark_markov_bias.argtypes = [P, P, I, P, I, I, I, P, P]
     lib.dspark_markov_draft.restype = I
-    lib.dspark_markov_draft.argtypes = [P, P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, SZ, P]
+    lib.dspark_markov_draft.argtypes = [P, P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, P, P, I, P, P, SZ, P]
     lib.dspark_markov_draft_noalloc.restype = I
-    lib.dspark_markov_draft_noalloc.argtypes = [P, P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P]
+    lib.dspark_markov_draft_noalloc.argtypes = [P, P, P, P, I, P, I, I, I, I, F, P, U64, P, P, P, P, P, P, I, P, P]
     lib.dspark_static_scratch_bytes.restype = SZ
     lib.dspark_static_scratch_bytes.argtypes = []
     lib.dspark_rnn_draft.restype = I
@@ -178,65 +178,69 @@ def markov_bias(W1, W2, tokens, out=None, stream=None):
     return out
 
 
-def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=None, stream=None, W2T=None):
-    """Draft gamma tokens per request.  Returns (draft_tokens, draft_prob, draft_lse).
+def _draft_outputs(U, W1, W2, x0, seeds, out, conf_head, W2T):
+    """Checks the draft's arguments; returns (B, gamma, V, r, outputs, conf args)."""
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    _dev(U, "U", torch.float32)
+    _dev(W1, "W1", None, (V, r))
+    _dev(W2, "W2", W1.dtype, (r, V))
+    _dev(x0, "x0", torch.int32, (B,))
+    if seeds is not None:
+        _dev(seeds, "seeds", torch.uint64, (B,))
+    if W2T is not None:
+        _dev(W2T, "W2T", W2.dtype, (V, r))
+    n = 3 if conf_head is None else 4
+    if out is None:
+        out = tuple(torch.empty((B, gamma), dtype=torch.int32 if i == 0 else torch.float32, device=dev)
+                    for i in range(n))
+    if len(out) != n:
+        raise ValueError("out needs %d tensors" % n)
+    for t, name, dt in zip(out, ("draft_tokens", "draft_prob", "draft_lse", "conf"),
+                           (torch.int32, torch.float32, torch.float32, torch.float32)):
+        _dev(t, name, dt, (B, gamma))
+    cargs = (None, None, None, 0, None)
+    if conf_head is not None:
+        h, w, sts = conf_head
+        d = h.shape[2]
+        _dev(h, "conf h", torch.float32, (B, gamma, d))
+        _dev(w, "conf w", torch.float32, (d + r,))
+        if sts is not None:
+            _dev(sts, "sts", torch.float32, (gamma,))
+        cargs = (_p(h), _p(w), _p(sts), d, _p(out[3]))
+    return B, gamma, V, r, out, cargs
+
+
+def markov_draft(U, W1, W2, x0, temperature, seeds, rnd, out=None, workspace=None, stream=None, W2T=None,
+                 conf_head=None):
+    """Draft gamma tokens per request.  Returns (draft_tokens, draft_prob,
+    draft_lse), and the confidences as a fourth tensor when ``conf_head`` =
+    (h [B][gamma][d], w [d + r], sts [gamma] or None) is given (the
+    confidence head, computed inside the draft's selections).
     W2T: optional transposed copy of W2 (transpose_w2), which lets the library
     run all positions in one device-resident launch."""
-    B, gamma, V = U.shape
-    r = W1.shape[1]
+    B, gamma, V, r, out, cargs = _draft_outputs(U, W1, W2, x0, seeds, out, conf_head, W2T)
     dev = U.device
-    _dev(U, "U", torch.float32)
-    _dev(W1, "W1", None, (V, r))
-    _dev(W2, "W2", W1.dtype, (r, V))
-    _dev(x0, "x0", torch.int32, (B,))
-    if seeds is not None:
-        _dev(seeds, "seeds", torch.uint64, (B,))
-    if out is None:
-        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
-               torch.empty((B, gamma), dtype=torch.float32, device=dev),
-               torch.empty((B, gamma), dtype=torch.float32, device=dev))
-    tok, prob, lse = out
-    _dev(tok, "draft_tokens", torch.int32, (B, gamma))
-    _dev(prob, "draft_prob", torch.float32, (B, gamma))
-    _dev(lse, "draft_lse", torch.float32, (B, gamma))
     ws, nbytes = _workspace(OP_DRAFT, B, gamma, V, r, workspace, dev)
-    if W2T is not None:
-        _dev(W2T, "W2T", W2.dtype, (V, r))
     st = load().dspark_markov_draft(_p(U), _p(W1), _p(W2), _p(W2T), _wdtype(W1, W2), _p(x0), B, gamma, V, r,
-                                    float(temperature), _p(seeds), int(rnd), _p(tok), _p(prob), _p(lse),
-                                    _p(ws), nbytes, _stream(stream, dev))
+                                    float(temperature), _p(seeds), int(rnd), _p(out[0]), _p(out[1]), _p(out[2]),
+                                    *cargs, _p(ws), nbytes, _stream(stream, dev))
     _check("dspark_markov_draft", st)
-    return tok, prob, lse
+    return out
 
 
-def markov_draft_noalloc(U, W1, W2, x0, temperature, seeds, rnd, out=None, stream=None, W2T=None):
+def markov_draft_noalloc(U, W1, W2, x0, temperature, seeds, rnd, out=None, stream=None, W2T=None,
+                         conf_head=None):
     """markov_draft with the library's static scratch array instead of a
-    workspace (dspark_markov_draft_noalloc).  Returns (draft_tokens,
-    draft_prob, draft_lse); pass ``out`` to allocate nothing here either."""
-    B, gamma, V = U.shape
-    r = W1.shape[1]
-    dev = U.device
-    _dev(U, "U", torch.float32)
-    _dev(W1, "W1", None, (V, r))
-    _dev(W2, "W2", W1.dtype, (r, V))
-    _dev(x0, "x0", torch.int32, (B,))
-    if seeds is not None:
-        _dev(seeds, "seeds", torch.uint64, (B,))
-    if out is None:
-        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
-               torch.empty((B, gamma), dtype=torch.float32, device=dev),
-               torch.empty((B, gamma), dtype=torch.float32, device=dev))
-    tok, prob, lse = out
-    _dev(tok, "draft_tokens", torch.int32, (B, gamma))
-    _dev(prob, "draft_prob", torch.float32, (B, gamma))
-    _dev(lse, "draft_lse", torch.float32, (B, gamma))
-    if W2T is not None:
-        _dev(W2T, "W2T", W2.dtype, (V, r))
+    workspace (dspark_markov_draft_noalloc).  Returns what markov_draft
+    returns; pass ``out`` to allocate nothing here either."""
+    B, gamma, V, r, out, cargs = _draft_outputs(U, W1, W2, x0, seeds, out, conf_head, W2T)
     st = load().dspark_markov_draft_noalloc(_p(U), _p(W1), _p(W2), _p(W2T), _wdtype(W1, W2), _p(x0), B, gamma, V, r,
-                                            float(temperature), _p(seeds), int(rnd), _p(tok), _p(prob), _p(lse),
-                                            _stream(stream, dev))
+                                            float(temperature), _p(seeds), int(rnd), _p(out[0]), _p(out[1]),
+                                            _p(out[2]), *cargs, _stream(stream, U.device))
     _check("dspark_markov_draft_noalloc", st)
-    return tok, prob, lse
+    return out
 
 
 def static_scratch_bytes():

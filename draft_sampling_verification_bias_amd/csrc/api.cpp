@@ -44,6 +44,13 @@ int enum_value(const E& e) {
 
 bool dtype_ok(int d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
 
+// The optional confidence head of dspark_markov_draft: conf == null, or its
+// inputs present, aligned and sized.
+bool conf_head_ok(const float* h, const float* w, const float* sts, int d, const float* conf) {
+  if (conf == nullptr) return true;
+  return aligned(conf, 4) && req(h, 16) && req(w, 16) && opt(sts, 4) && d >= 1 && d <= (1 << 20);
+}
+
 dspark_status from_hip(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
 
 }  // namespace
@@ -87,11 +94,14 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
                                   dspark_dtype wdtype, const int32_t* x0, int B, int gamma, int V, int r,
                                   float temperature,
                                   const uint64_t* seeds, uint64_t round, int32_t* draft_tokens, float* draft_prob,
-                                  float* draft_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                  float* draft_lse, const float* conf_h, const float* conf_w, const float* conf_sts,
+                                  int conf_d, float* conf, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
   if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !opt(W2T, 16) || W2T == W2 || !req(x0, 4) ||
-      !req(draft_tokens, 4) || !req(draft_prob, 4) || !req(draft_lse, 4) || !req(workspace, 16))
+      !req(draft_tokens, 4) || !req(draft_prob, 4) || !req(draft_lse, 4) || !req(workspace, 16) ||
+      !conf_head_ok(conf_h, conf_w, conf_sts, conf_d, conf))
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (temperature > 0.0f && !req(seeds, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < draft_workspace(B, gamma, V, r)) return DSPARK_ERR_WORKSPACE;
@@ -111,6 +121,13 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
   a.tokens = draft_tokens;
   a.prob = draft_prob;
   a.lse = draft_lse;
+  if (conf) {
+    a.ch = conf_h;
+    a.cw = conf_w;
+    a.csts = conf_sts;
+    a.cd = conf_d;
+    a.conf = conf;
+  }
   a.ws = workspace;
   return from_hip(launch_draft(a, wdtype == DSPARK_BF16, stream));
 }
@@ -119,11 +136,14 @@ dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const 
                                           dspark_dtype wdtype, const int32_t* x0, int B, int gamma, int V, int r,
                                           float temperature,
                                           const uint64_t* seeds, uint64_t round, int32_t* draft_tokens,
-                                          float* draft_prob, float* draft_lse, hipStream_t stream) {
+                                          float* draft_prob, float* draft_lse, const float* conf_h,
+                                          const float* conf_w, const float* conf_sts, int conf_d, float* conf,
+                                          hipStream_t stream) {
   if (!dtype_ok(enum_value(wdtype))) return DSPARK_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma, V, r) || !temp_ok(temperature)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (!req(U, 16) || !req(W1, 16) || !req(W2, 16) || !opt(W2T, 16) || W2T == W2 || !req(x0, 4) ||
-      !req(draft_tokens, 4) || !req(draft_prob, 4) || !req(draft_lse, 4))
+      !req(draft_tokens, 4) || !req(draft_prob, 4) || !req(draft_lse, 4) ||
+      !conf_head_ok(conf_h, conf_w, conf_sts, conf_d, conf))
     return DSPARK_ERR_INVALID_ARGUMENT;
   if (temperature > 0.0f && !req(seeds, 8)) return DSPARK_ERR_INVALID_ARGUMENT;
   if (draft_workspace(B, gamma, V, r) > static_scratch_bytes()) return DSPARK_ERR_SCRATCH_LIMIT;
@@ -146,6 +166,13 @@ dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const 
   a.tokens = draft_tokens;
   a.prob = draft_prob;
   a.lse = draft_lse;
+  if (conf) {
+    a.ch = conf_h;
+    a.cw = conf_w;
+    a.csts = conf_sts;
+    a.cd = conf_d;
+    a.conf = conf;
+  }
   a.ws = ws;
   return from_hip(launch_draft(a, wdtype == DSPARK_BF16, stream));
 }

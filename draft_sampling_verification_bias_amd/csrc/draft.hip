@@ -36,6 +36,12 @@ struct SelectArgs {
   float* lse;
   double* u_next;  // [2][B] stream-0 uniforms drawn one position ahead
   uint4* esw;      // optional: the drafted token's W1 row for the next tile pass
+  // optional confidence head (conf != null), see conf_hidden below
+  const float* ch;
+  const float* cw;
+  const float* csts;
+  int cd;
+  float* conf;
 };
 
 // Store W1 row x (bf16, r = 256) in the ring tile pass's operand layout for
@@ -79,6 +85,57 @@ __device__ __forceinline__ float opnd_at(const SelectArgs& a, int row, int j) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// The confidence head of "The Confidence Head" (Eq. 7) with the per-position
+// temperatures of Sequential Temperature Scaling (same section), fused into
+// the selection:
+//   c_{b,kk} = sigma((w_h . h_{b,kk} + w_e . W1[x_{kk-1}]) / t_kk).
+// The selection of position k draws x_k and reads its W1 row for the next
+// position's operand, so it emits c_{k+1}; the first selection also emits
+// c_1 from the anchor.  The hidden part depends on no drafted token, so its
+// loads go out at the start of the selection.  The float32 products are
+// exact in float64 and summed there.  A position whose previous token is
+// outside [0, V) gets NaN.
+// ---------------------------------------------------------------------------
+
+// This thread's share of w_h . h_{b,kk} (elements tid, tid + nthr, ...).
+__device__ __forceinline__ double conf_hidden(const SelectArgs& a, int b, int kk, int tid, int nthr) {
+  const float* hrow = a.ch + ((size_t)b * a.gamma + (kk - 1)) * a.cd;
+  double s = 0.0;
+  if ((a.cd & 3) == 0) {  // rows 16-byte aligned
+    for (int i = 4 * tid; i < a.cd; i += 4 * nthr) {
+      const float4 x = *reinterpret_cast<const float4*>(hrow + i);
+      const float4 y = *reinterpret_cast<const float4*>(a.cw + i);
+      s += (double)x.x * (double)y.x + (double)x.y * (double)y.y + (double)x.z * (double)y.z +
+           (double)x.w * (double)y.w;
+    }
+  } else {
+    for (int i = tid; i < a.cd; i += nthr) s += (double)hrow[i] * (double)a.cw[i];
+  }
+  return s;
+}
+
+// This thread's share of w_e . W1[x] for a token x in [0, V).
+template <bool kBf16>
+__device__ __forceinline__ double conf_embed(const SelectArgs& a, int x, int tid, int nthr) {
+  double s = 0.0;
+  for (int j = tid; j < a.r; j += nthr) s += (double)w1_at<kBf16>(a.W1, (size_t)x * a.r + j) * (double)a.cw[a.cd + j];
+  return s;
+}
+
+__device__ __forceinline__ void conf_store(const SelectArgs& a, int b, int kk, double z) {
+  const double t = a.csts ? (double)a.csts[kk - 1] : 1.0;
+  a.conf[(size_t)b * a.gamma + (kk - 1)] = (float)(1.0 / (1.0 + exp(-z / t)));
+}
+
+// Invalid previous token at position k (x_{k-1} outside [0, V)): x_k is not
+// drawn, so c_{k+1} (and at k == 1, c_1) are NaN.
+__device__ __forceinline__ void conf_invalid(const SelectArgs& a, int b) {
+  if (a.conf == nullptr) return;
+  if (a.k < a.gamma) a.conf[(size_t)b * a.gamma + a.k] = __builtin_nanf("");
+  if (a.k == 1) a.conf[(size_t)b * a.gamma] = __builtin_nanf("");
+}
+
 template <bool kGreedy, bool kBf16, int kParts = 1>
 __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a) {
   __shared__ PickScratch ps;
@@ -89,6 +146,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
   __shared__ double sterm[kTileCols];
   __shared__ float sv[kSelThreads / kWave];
   __shared__ int si[kSelThreads / kWave];
+  __shared__ double sred[kSelThreads / kWave];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -111,9 +169,29 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
       a.tokens[out] = -1;
       a.prob[out] = __builtin_nanf("");
       a.lse[out] = __builtin_nanf("");
+      conf_invalid(a, b);
     }
     return;
   }
+  // confidence head: this thread's shares of the hidden part of c_{k+1} and
+  // of the whole logit of c_1
+  double c_next = 0.0, c_first = 0.0;
+  if (a.conf != nullptr) {
+    if (a.k < a.gamma) c_next = conf_hidden(a, b, a.k + 1, tid, kSelThreads);
+    if (a.k == 1) c_first = conf_hidden(a, b, 1, tid, kSelThreads) + conf_embed<kBf16>(a, ptok, tid, kSelThreads);
+  }
+  // emits the confidences once x_k is known (every thread holds it)
+  auto emit_conf = [&](int x) {
+    if (a.conf == nullptr) return;
+    if (a.k == 1) {
+      const double z1 = block_sum<kSelThreads, double>(c_first, sred);
+      if (tid == 0) conf_store(a, b, 1, z1);
+    }
+    if (a.k < a.gamma) {
+      const double z = block_sum<kSelThreads, double>(c_next + conf_embed<kBf16>(a, x, tid, kSelThreads), sred);
+      if (tid == 0) conf_store(a, b, a.k + 1, z);
+    }
+  };
 
   if constexpr (kGreedy) {
     float bv = -__builtin_inff();
@@ -129,6 +207,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
       a.lse[out] = 0.0f;
     }
     store_ring_operand<kBf16>(a, b, bi, tid);
+    emit_conf(bi);
     return;
   } else {
     // One read of the tile summaries (kept in LDS when they fit) together
@@ -249,6 +328,7 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_kernel(SelectArgs a)
       a.lse[out] = (float)((double)M * a.inv_t + log(total));
     }
     store_ring_operand<kBf16>(a, b, ts * kTileCols + c, tid);
+    emit_conf(ts * kTileCols + c);
   }
 }
 
@@ -279,6 +359,7 @@ constexpr int kMaxRQuarter = 512 / 4;             // k per wave (r <= 512)
 template <bool kBf16, int kWavePer, int kParts = 1>
 __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectArgs a) {
   __shared__ float sbias[4][kTileCols];
+  __shared__ double sconf[2][4];  // per wave: hidden part of c_{k+1}, logit of c_1
   const int b = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -306,8 +387,17 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
       a.tokens[out] = -1;
       a.prob[out] = __builtin_nanf("");
       a.lse[out] = __builtin_nanf("");
+      conf_invalid(a, b);
     }
     return;
+  }
+  // confidence head: this thread's shares of the hidden part of c_{k+1} and
+  // of the whole logit of c_1 (summed over the waves before the barrier)
+  double c_next = 0.0, c_first = 0.0;
+  if (a.conf != nullptr) {
+    if (a.k < a.gamma) c_next = conf_hidden(a, b, a.k + 1, threadIdx.x, kSelThreads);
+    if (a.k == 1)
+      c_first = conf_hidden(a, b, 1, threadIdx.x, kSelThreads) + conf_embed<kBf16>(a, ptok, threadIdx.x, kSelThreads);
   }
 
   // row max, tile weights, their lane prefix, the picked tile
@@ -434,6 +524,14 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
 #pragma unroll
     for (int j = 0; j < 8; ++j) sbias[wave][8 * cg + j] = acc[j];
   }
+  if (a.conf != nullptr) {
+    c_next = wave_sum(c_next);
+    c_first = wave_sum(c_first);
+    if (lane == 0) {
+      sconf[0][wave] = c_next;
+      sconf[1][wave] = c_first;
+    }
+  }
   __syncthreads();
   if (wave != 0) return;
 
@@ -473,7 +571,15 @@ __global__ __launch_bounds__(kSelThreads) void draft_select_wave_kernel(SelectAr
     a.prob[out] = (float)(exp2((double)(l - M) * cf) / total);
     a.lse[out] = (float)((double)M * a.inv_t + log(total));
   }
-  store_ring_operand<kBf16>(a, b, lane_i32(mytok, own2), lane);
+  const int xk = lane_i32(mytok, own2);
+  store_ring_operand<kBf16>(a, b, xk, lane);
+  if (a.conf != nullptr) {
+    const double emb = wave_sum(a.k < a.gamma ? conf_embed<kBf16>(a, xk, lane, kWave) : 0.0);
+    if (lane == 0) {
+      if (a.k < a.gamma) conf_store(a, b, a.k + 1, ((sconf[0][0] + sconf[0][1]) + (sconf[0][2] + sconf[0][3])) + emb);
+      if (a.k == 1) conf_store(a, b, 1, (sconf[1][0] + sconf[1][1]) + (sconf[1][2] + sconf[1][3]));
+    }
+  }
 }
 
 template <bool kBf16, int kParts = 1>
@@ -555,6 +661,11 @@ hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t s) {
   sa.tokens = a.tokens;
   sa.prob = a.prob;
   sa.lse = a.lse;
+  sa.ch = a.ch;
+  sa.cw = a.cw;
+  sa.csts = a.csts;
+  sa.cd = a.cd;
+  sa.conf = a.conf;
   sa.u_next = reinterpret_cast<double*>(reinterpret_cast<char*>(a.ws) +
                                         align256((size_t)a.B * ntiles * sizeof(float2)));
   // When the tile passes run the ring kernel, each selection also stores the

@@ -84,6 +84,13 @@ struct DraftArgs {
   int32_t* tokens;
   float* prob;
   float* lse;
+  // optional confidence head (conf != null): hidden states [B][gamma][cd],
+  // head weights [cd + r], temperatures [gamma] (null: 1), output [B][gamma]
+  const float* ch;
+  const float* cw;
+  const float* csts;
+  int cd;
+  float* conf;
   void* ws;
 };
 

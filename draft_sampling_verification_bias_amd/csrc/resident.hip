@@ -915,6 +915,7 @@ static hipError_t res_prepare(int& max_blocks) {
 
 bool resident_draft_applies(const DraftArgs& a, bool bf16) {
   if (!bf16 || a.W2T == nullptr || a.r != kResR || a.V % 16 != 0) return false;
+  if (a.conf != nullptr) return false;  // the confidence head runs in the per-position selections
   const int nwg = compute_units_of_device();
   if (nwg > kResMaxWg || nwg <= kResSelWg) return false;
   const long long NW = (long long)(nwg - kResSelWg) * kResWaves;

@@ -142,11 +142,11 @@ dspark_status dspark_markov_bias(const void* W1, const void* W2, dspark_dtype wd
  *
  * W2T is optional (NULL to skip): W2 transposed, [V][r] in the weight dtype,
  * as dspark_transpose_w2 writes it.  When it is given, the weights are bf16,
- * r == 256, V % 16 == 0, V <= 80 * 8 * (compute units) (163840 on MI355X),
- * B <= 2 * (compute units) and 4 B gamma V < 2^32, all gamma positions run
- * in one cooperative launch that keeps W2 on chip (the "device-resident"
- * loop); otherwise, or when the device cannot hold that launch, each
- * position is its own pair of launches.  Both give the same draws up to the
+ * r == 256, V % 16 == 0, V <= 80 * 8 * (compute units - 16) (153600 on
+ * MI355X), B <= 512, 4 B gamma V < 2^32 and no confidence output is asked
+ * for, all gamma positions run in one cooperative launch that keeps W2 on
+ * chip (the "device-resident" loop); otherwise, or when the device cannot
+ * hold that launch, each position is its own pair of launches.  Both give the same draws up to the
  * summation order of float32 sums.  If a grid-wide wait of the resident loop
  * ever times out (it cannot while the launch is co-resident), every request's
  * outputs are -1 / NaN.
@@ -157,6 +157,23 @@ dspark_status dspark_markov_bias(const void* W1, const void* W2, dspark_dtype wd
  *   draft_lse     float32 [B][gamma]  log sum_v exp(l_k(v) / T), the log
  *                                     normaliser of p_d^k (used by
  *                                     dspark_survival)
+ *
+ * Confidence head (optional; conf == NULL skips it and conf_h, conf_w,
+ * conf_sts, conf_d are not read): the per-position confidence of [R] "The
+ * Confidence Head" (Eq. 7; the decode round of "Putting It All Together"
+ * computes it inside the draft loop, step 6) with the temperatures of
+ * Sequential Temperature Scaling (same section), computed by the selection
+ * that draws x_{k-1}, where that token's W1 row is read anyway:
+ *   c_{b,k} = sigma(z / t_k),  z = w . [h_{b,k} ; W1[x_{k-1}]]   (x_0 = x0[b])
+ *   conf_h    float32 [B][gamma][conf_d]  hidden states h_k (16-byte aligned)
+ *   conf_w    float32 [conf_d + r]        head weights: hidden part, then
+ *                                         embedding part (16-byte aligned)
+ *   conf_sts  float32 [gamma]             calibrated temperatures t_k > 0
+ *                                         (NULL: 1, the raw head)
+ *   conf      float32 [B][gamma]          out: c_{b,k}; NaN where x_{k-1} is
+ *                                         outside [0, V)
+ * 1 <= conf_d <= 2^20; z is summed in float64 from the float32 products, as
+ * dspark_confidence computes it for given tokens.
  * Workspace: dspark_workspace_size(DSPARK_OP_DRAFT, B, gamma, V, r).
  */
 dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2, const void* W2T,
@@ -164,7 +181,8 @@ dspark_status dspark_markov_draft(const float* U, const void* W1, const void* W2
                                   int B, int gamma, int V, int r, float temperature,
                                   const uint64_t* seeds, uint64_t round,
                                   int32_t* draft_tokens, float* draft_prob, float* draft_lse,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                  const float* conf_h, const float* conf_w, const float* conf_sts, int conf_d,
+                                  float* conf, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dspark_markov_draft_noalloc -- dspark_markov_draft without a workspace, for
@@ -188,7 +206,8 @@ dspark_status dspark_markov_draft_noalloc(const float* U, const void* W1, const 
                                           int B, int gamma, int V, int r, float temperature,
                                           const uint64_t* seeds, uint64_t round,
                                           int32_t* draft_tokens, float* draft_prob, float* draft_lse,
-                                          hipStream_t stream);
+                                          const float* conf_h, const float* conf_w, const float* conf_sts,
+                                          int conf_d, float* conf, hipStream_t stream);
 
 /* Bytes of the static scratch array of dspark_markov_draft_noalloc. */
 size_t dspark_static_scratch_bytes(void);
@@ -343,7 +362,9 @@ dspark_status dspark_survival(const float* U, const void* W1, const void* W2, ds
  *   c_{b,k} = sigma(z / t_k),  z = w . [h_{b,k} ; W1[x_{k-1}]]   (x_0 = x0[b])
  * for k = 1..gamma, the scalar the scheduler's survival products are built
  * from (dspark_survival in confidence mode, then dspark_schedule) before the
- * target runs.
+ * target runs.  A Markov-head draft gets the same values from
+ * dspark_markov_draft's own confidence output with no launch of its own;
+ * this entry point serves tokens drafted elsewhere (an RNN-head draft).
  *
  *   h             float32 [B][gamma][d]  backbone hidden states h_k
  *   w             float32 [d + r]        head weights: hidden part, then

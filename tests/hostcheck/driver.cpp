@@ -31,8 +31,8 @@ static void reset() { memset(&last, 0, sizeof(last)); }
 static dspark_status draft(int B, int gamma, int V, int r, float T, const void* W2T, size_t wsb, uintptr_t U = A,
                            uintptr_t x0 = D) {
   return dspark_markov_draft((const float*)P(U), P(Bp), P(C), W2T, DSPARK_BF16, (const int32_t*)P(x0), B, gamma, V,
-                             r, T, (const uint64_t*)P(E), 42, (int32_t*)P(F), (float*)P(G), (float*)P(H), P(I),
-                             wsb, nullptr);
+                             r, T, (const uint64_t*)P(E), 42, (int32_t*)P(F), (float*)P(G), (float*)P(H), nullptr,
+                             nullptr, nullptr, 0, nullptr, P(I), wsb, nullptr);
 }
 
 int main() {
@@ -59,7 +59,27 @@ int main() {
   CHECK(strcmp(last.op, "draft") == 0 && last.B == 256 && last.gamma == 7 && last.V == 151936 && last.r == 256);
   CHECK(last.T == 0.7f && last.round == 42 && last.bf16 && last.ws == P(I) && last.suppressed == 0);
   CHECK(last.p[0] == P(A) && last.p[1] == P(Bp) && last.p[2] == P(C) && last.p[3] == P(J) && last.p[4] == P(D));
-  CHECK(last.p[5] == P(E) && last.p[6] == P(F) && last.p[7] == P(G) && last.p[8] == P(H));
+  CHECK(last.p[5] == P(E) && last.p[6] == P(F) && last.p[7] == P(G) && last.p[8] == P(H) && last.p[9] == nullptr);
+  // the confidence head: forwarded with its output; its inputs are not read
+  // (not even checked) without one
+  reset();
+  CHECK(dspark_markov_draft((const float*)P(A), P(Bp), P(C), nullptr, DSPARK_BF16, (const int32_t*)P(D), 8, 4, 1000,
+                            16, 1.0f, (const uint64_t*)P(E), 0, (int32_t*)P(F), (float*)P(G), (float*)P(H),
+                            (const float*)P(K), (const float*)P(L), nullptr, 4096, (float*)P(J), P(I), 1 << 30,
+                            nullptr) == DSPARK_OK);
+  CHECK(last.p[9] == P(J) && last.d == 4096);
+  reset();
+  CHECK(dspark_markov_draft((const float*)P(A), P(Bp), P(C), nullptr, DSPARK_BF16, (const int32_t*)P(D), 8, 4, 1000,
+                            16, 1.0f, (const uint64_t*)P(E), 0, (int32_t*)P(F), (float*)P(G), (float*)P(H),
+                            (const float*)P(K + 4), nullptr, nullptr, -3, nullptr, P(I), 1 << 30,
+                            nullptr) == DSPARK_OK);
+  CHECK(last.p[9] == nullptr && last.d == 0);
+  reset();
+  CHECK(dspark_markov_draft((const float*)P(A), P(Bp), P(C), nullptr, DSPARK_BF16, (const int32_t*)P(D), 8, 4, 1000,
+                            16, 1.0f, (const uint64_t*)P(E), 0, (int32_t*)P(F), (float*)P(G), (float*)P(H),
+                            (const float*)P(K + 4), (const float*)P(L), nullptr, 4096, (float*)P(J), P(I), 1 << 30,
+                            nullptr) == DSPARK_ERR_INVALID_ARGUMENT);
+  CHECK(last.op[0] == 0);
   // draft: each bad argument returns its status and launches nothing
   struct Bad {
     int B, gamma, V, r;
@@ -95,24 +115,25 @@ int main() {
   reset();
   CHECK(dspark_markov_draft((const float*)P(A), P(Bp), P(C), nullptr, (dspark_dtype)7, (const int32_t*)P(D), 4, 4,
                             1000, 16, 1.0f, (const uint64_t*)P(E), 0, (int32_t*)P(F), (float*)P(G), (float*)P(H),
-                            P(I), 1 << 30, nullptr) == DSPARK_ERR_UNSUPPORTED);
+                            nullptr, nullptr, nullptr, 0, nullptr, P(I), 1 << 30, nullptr) == DSPARK_ERR_UNSUPPORTED);
   // T == 0 needs no seeds
   reset();
   CHECK(dspark_markov_draft((const float*)P(A), P(Bp), P(C), nullptr, DSPARK_BF16, (const int32_t*)P(D), 4, 4, 1000,
-                            16, 0.0f, nullptr, 0, (int32_t*)P(F), (float*)P(G), (float*)P(H), P(I), 1 << 30,
-                            nullptr) == DSPARK_OK);
+                            16, 0.0f, nullptr, 0, (int32_t*)P(F), (float*)P(G), (float*)P(H), nullptr, nullptr,
+                            nullptr, 0, nullptr, P(I), 1 << 30, nullptr) == DSPARK_OK);
   CHECK(strcmp(last.op, "draft") == 0 && last.p[5] == nullptr);
 
   // allocation-free draft: the static array, profiling suppressed, size limit
   reset();
   CHECK(dspark_markov_draft_noalloc((const float*)P(A), P(Bp), P(C), P(J), DSPARK_BF16, (const int32_t*)P(D), 256, 7,
                                     151936, 256, 1.0f, (const uint64_t*)P(E), 3, (int32_t*)P(F), (float*)P(G),
-                                    (float*)P(H), nullptr) == DSPARK_OK);
+                                    (float*)P(H), nullptr, nullptr, nullptr, 0, nullptr, nullptr) == DSPARK_OK);
   CHECK(strcmp(last.op, "draft") == 0 && last.ws != nullptr && last.suppressed == 1 && last.p[3] == P(J));
   reset();
   CHECK(dspark_markov_draft_noalloc((const float*)P(A), P(Bp), P(C), nullptr, DSPARK_BF16, (const int32_t*)P(D),
                                     65536, 32, 1 << 20, 256, 1.0f, (const uint64_t*)P(E), 3, (int32_t*)P(F),
-                                    (float*)P(G), (float*)P(H), nullptr) == DSPARK_ERR_SCRATCH_LIMIT);
+                                    (float*)P(G), (float*)P(H), nullptr, nullptr, nullptr, 0, nullptr,
+                                    nullptr) == DSPARK_ERR_SCRATCH_LIMIT);
   CHECK(last.op[0] == 0);
   CHECK(dspark_static_scratch_bytes() == (size_t)32 << 20);
 

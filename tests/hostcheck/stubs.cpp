@@ -30,7 +30,8 @@ hipError_t launch_draft(const DraftArgs& a, bool bf16, hipStream_t) {
   last.B = a.B; last.gamma = a.gamma; last.V = a.V; last.r = a.r; last.T = a.temperature;
   last.round = a.round; last.bf16 = bf16; last.ws = a.ws; last.suppressed = hostcheck::suppress_depth;
   last.p[0] = a.U; last.p[1] = a.W1; last.p[2] = a.W2; last.p[3] = a.W2T; last.p[4] = a.x0;
-  last.p[5] = a.seeds; last.p[6] = a.tokens; last.p[7] = a.prob; last.p[8] = a.lse;
+  last.p[5] = a.seeds; last.p[6] = a.tokens; last.p[7] = a.prob; last.p[8] = a.lse; last.p[9] = a.conf;
+  last.d = a.cd;
   return hipSuccess;
 }
 

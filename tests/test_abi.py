@@ -68,11 +68,12 @@ def test_workspace_size(lib, op):
 
 def _draft(lib, **kw):
     a = dict(U=FAKE, W1=FAKE, W2=FAKE, W2T=None, wd=1, x0=FAKE, B=4, gamma=4, V=1000, r=16, T=1.0, seeds=FAKE,
-             rnd=0, tok=FAKE, prob=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30)
+             rnd=0, tok=FAKE, prob=FAKE, lse=FAKE, ch=None, cw=None, csts=None, cd=0, conf=None, ws=FAKE,
+             wsb=1 << 30)
     a.update(kw)
     return lib.dspark_markov_draft(a["U"], a["W1"], a["W2"], a["W2T"], a["wd"], a["x0"], a["B"], a["gamma"], a["V"],
                                    a["r"], a["T"], a["seeds"], a["rnd"], a["tok"], a["prob"], a["lse"],
-                                   a["ws"], a["wsb"], None)
+                                   a["ch"], a["cw"], a["csts"], a["cd"], a["conf"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -82,6 +83,12 @@ def _draft(lib, **kw):
     (dict(tok=None), INVALID), (dict(seeds=None), INVALID), (dict(U=MISALIGNED), INVALID),
     (dict(ws=None), INVALID), (dict(wd=5), UNSUPPORTED), (dict(wsb=16), WORKSPACE),
     (dict(W2T=MISALIGNED), INVALID), (dict(W2T=FAKE), INVALID),  # W2T may not alias W2
+    # the confidence head: its inputs are checked only when its output is asked for
+    (dict(conf=FAKE, ch=None, cw=FAKE, cd=64), INVALID),
+    (dict(conf=FAKE, ch=FAKE, cw=MISALIGNED, cd=64), INVALID), (dict(conf=FAKE, ch=FAKE, cw=FAKE, cd=0), INVALID),
+    (dict(conf=FAKE, ch=FAKE, cw=FAKE, cd=(1 << 20) + 1), INVALID),
+    (dict(conf=MISALIGNED - 2, ch=FAKE, cw=FAKE, cd=64), INVALID),
+    (dict(conf=FAKE, ch=FAKE, cw=FAKE, csts=MISALIGNED - 2, cd=64), INVALID),
 ])
 def test_draft_rejects_bad_arguments(lib, kw, status):
     assert _draft(lib, **kw) == status
@@ -89,17 +96,17 @@ def test_draft_rejects_bad_arguments(lib, kw, status):
 
 def _draft_noalloc(lib, **kw):
     a = dict(U=FAKE, W1=FAKE, W2=FAKE, W2T=None, wd=1, x0=FAKE, B=4, gamma=4, V=1000, r=16, T=1.0, seeds=FAKE,
-             rnd=0, tok=FAKE, prob=FAKE, lse=FAKE)
+             rnd=0, tok=FAKE, prob=FAKE, lse=FAKE, ch=None, cw=None, csts=None, cd=0, conf=None)
     a.update(kw)
     return lib.dspark_markov_draft_noalloc(a["U"], a["W1"], a["W2"], a["W2T"], a["wd"], a["x0"], a["B"], a["gamma"],
                                            a["V"], a["r"], a["T"], a["seeds"], a["rnd"], a["tok"], a["prob"],
-                                           a["lse"], None)
+                                           a["lse"], a["ch"], a["cw"], a["csts"], a["cd"], a["conf"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), INVALID), (dict(gamma=33), INVALID), (dict(V=1), INVALID), (dict(r=40), INVALID),
     (dict(T=-1.0), INVALID), (dict(U=None), INVALID), (dict(seeds=None), INVALID), (dict(U=MISALIGNED), INVALID),
-    (dict(wd=5), UNSUPPORTED),
+    (dict(wd=5), UNSUPPORTED), (dict(conf=FAKE, ch=FAKE, cw=MISALIGNED, cd=64), INVALID),
     # sizes whose draft workspace exceeds the static array: rejected on the host
     (dict(B=4096, V=151936, r=256, gamma=7), SCRATCH), (dict(B=65536, V=16000, r=16), SCRATCH),
 ])

@@ -125,3 +125,84 @@ def test_confidence_scheduled_round_full_size():
     assert nv > 0
     del dv, W2T
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# The confidence head fused into the draft: dspark_markov_draft's optional
+# confidence output, computed by the selection that draws x_{k-1} ("The
+# Confidence Head", Eq. 7 and the draft loop of "Putting It All Together").
+# The oracle drafts its own tokens and evaluates Eq. 7 on them; the requests
+# whose whole block matches are compared.
+# ---------------------------------------------------------------------------
+FUSED = [
+    ("tiny_v1000_b4", {}, 1000, False),                                # float32 weights
+    ("v151936_b32", dict(V=4099, B=9, gamma=3, r=48), 17, True),       # d % 4 != 0: scalar loads
+    ("v151936_b256_t07", dict(V=3001, B=40, r=64), 4096, True),
+    ("greedy_v151936_b512", dict(V=5003, B=70, r=32), 64, True),       # greedy: the block-wide selection
+    ("v151936_b32", dict(V=264000, B=9, gamma=2), 256, True),          # > 2048 tiles: block-wide sampling
+    ("v151936_b256_t07", dict(B=300, V=20000, gamma=3), 4096, True),   # the ring tile pass, r = 256
+    ("v151936_b256_t07", {}, 4096, True),                              # full size
+]
+
+
+@pytest.mark.parametrize("name,kw,d,use_sts", FUSED,
+                         ids=["%s-d%d-%s" % (n, d, "-".join("%s%s" % i for i in kw.items())) for n, kw, d, _ in FUSED])
+def test_draft_confidence_output_matches_the_oracle(name, kw, d, use_sts):
+    from oracle_pool import OraclePool
+    wl = workloads.make(name, **kw)
+    say("[fused conf %s %s d=%d]" % (name, kw, d))
+    h, w, sts = workloads.confidence_inputs(wl.B, wl.gamma, d, wl.r, seed=d + 1)
+    dv = Dev(wl)
+    head = (torch.from_numpy(h).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(sts).cuda() if use_sts else None)
+    tok, prob, lse, conf = dsp.markov_draft(dv.U, dv.W1, dv.W2, dv.x0, wl.T, dv.seeds, wl.rnd, conf_head=head)
+    t2, p2, l2 = dsp.markov_draft(dv.U, dv.W1, dv.W2, dv.x0, wl.T, dv.seeds, wl.rnd)
+    torch.cuda.synchronize()
+    # the confidence output leaves the draft itself unchanged
+    assert torch.equal(tok, t2) and torch.equal(prob, p2) and torch.equal(lse, l2)
+    tok_h, prob_h, lse_h, conf_h = (t.cpu().numpy() for t in (tok, prob, lse, conf))
+    del dv, head, tok, prob, lse, conf, t2, p2, l2
+    torch.cuda.empty_cache()
+    W1f, W2f = f64_weights(wl)
+    if wl.B * wl.V * wl.gamma > 1 << 26:
+        with OraclePool(wl) as pool:
+            ref = pool.draft(range(wl.B))
+    else:
+        ref = oracle.markov_draft(wl.U, W1f, W2f, wl.x0, wl.T, wl.seeds, wl.rnd)
+    n, ex, whole = compare_draft(ref, tok_h, prob_h, lse_h, range(wl.B), wl.T)
+    assert ex <= 1 and len(whole) >= wl.B - 1
+    reqs = sorted(whole)
+    c_ref = oracle.confidence(h, w, W1f, wl.x0, ref["tokens"], sts=sts if use_sts else None, requests=reqs)
+    _compare(conf_h[reqs], c_ref[reqs], name)
+    say("[fused conf %s] %d confidences equal, range %.3f..%.3f" % (name, len(reqs) * wl.gamma,
+                                                                     np.nanmin(c_ref), np.nanmax(c_ref)))
+
+
+def test_draft_confidence_output_invalid_anchor_and_resident_fallback():
+    # an invalid anchor makes the whole block -1 and every confidence of that
+    # request NaN; with W2T given, the draft that also returns confidences
+    # runs the per-position launches (same draws, same confidences)
+    wl = workloads.make("v151936_b256_t07", B=20, V=16384, gamma=3)
+    d = 256
+    h, w, sts = workloads.confidence_inputs(wl.B, wl.gamma, d, wl.r, seed=4)
+    x0 = wl.x0.copy()
+    x0[5], x0[13] = -1, wl.V
+    dv = Dev(wl)
+    dx0 = torch.from_numpy(x0.astype(np.int32)).cuda()
+    head = (torch.from_numpy(h).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(sts).cuda())
+    W2T = dsp.transpose_w2(dv.W2)
+    dsp.profile_enable(True)
+    tok, prob, lse, conf = dsp.markov_draft(dv.U, dv.W1, dv.W2, dx0, wl.T, dv.seeds, wl.rnd, conf_head=head, W2T=W2T)
+    torch.cuda.synchronize()
+    prof = dsp.profile_read()
+    dsp.profile_enable(False)
+    assert "draft_resident" not in prof and prof.get("draft_select", (0, 0.0))[0] == wl.gamma, prof
+    tok_h, conf_h = tok.cpu().numpy(), conf.cpu().numpy()
+    assert (tok_h[[5, 13]] == -1).all() and np.isnan(conf_h[[5, 13]]).all()
+    good = [b for b in range(wl.B) if b not in (5, 13)]
+    W1f, W2f = f64_weights(wl)
+    ref = oracle.markov_draft(wl.U, W1f, W2f, x0, wl.T, wl.seeds, wl.rnd, requests=good)
+    _, ex, whole = compare_draft(ref, tok_h, prob.cpu().numpy(), lse.cpu().numpy(), good, wl.T)
+    reqs = sorted(whole)
+    assert len(reqs) >= len(good) - 1
+    c_ref = oracle.confidence(h, w, W1f, x0, ref["tokens"], sts=sts, requests=reqs)
+    _compare(conf_h[reqs], c_ref[reqs], "invalid anchors")

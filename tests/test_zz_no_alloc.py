@@ -60,5 +60,22 @@ def test_noalloc_draft_rejects_sizes_beyond_its_scratch():
     lib = dsp.load()
     st = lib.dspark_markov_draft_noalloc(U.data_ptr(), W1.data_ptr(), W2.data_ptr(), None, 1, x0.data_ptr(), 4096, 7,
                                          151936, 256, 1.0, seeds.data_ptr(), 0, x0.data_ptr(), U.data_ptr(),
-                                         U.data_ptr(), None)
+                                         U.data_ptr(), None, None, None, 0, None, None)
     assert st == -5
+
+
+def test_noalloc_draft_confidence_output():
+    # the fused confidence head through the allocation-free entry point: the
+    # same confidences as the workspace draft's
+    B, gamma, V, r, d = 48, 5, 8192, 256, 512
+    U, W1, W2, x0, seeds = _inputs(B, gamma, V, r, seed=6)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    head = (torch.randn((B, gamma, d), generator=g).cuda(), (torch.randn((d + r,), generator=g) * 0.05).cuda(),
+            torch.linspace(0.8, 1.6, gamma).cuda())
+    ref = dsp.markov_draft(U, W1, W2, x0, 1.0, seeds, 12, conf_head=head)
+    got = dsp.markov_draft_noalloc(U, W1, W2, x0, 1.0, seeds, 12, conf_head=head)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got[0].cpu().numpy(), ref[0].cpu().numpy())
+    rc, gc = ref[3].cpu().numpy(), got[3].cpu().numpy()
+    assert np.isfinite(rc).all()
+    np.testing.assert_allclose(gc, rc, rtol=1e-6, atol=0)
