@@ -142,14 +142,17 @@ def step_bytes(B, gamma, V, r, accept_len):
     return 4 * B * gamma * V + 4 * V * int((n + 1).sum()) + 2 * r * V + 2 * r * (B * gamma + rej)
 
 
-def pmc_traffic(kname):
+def pmc_traffic(kname, workload):
     """HBM bytes per launch of a kernel from its committed counter summary, or
-    None if there is none or the kernel source changed since it was taken."""
+    None if there is none for this workload or the kernel source changed since
+    it was taken."""
     path = PMC_FILES.get(kname)
     if path is None or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if rec.get("workload") != workload:
+        return None
     src = hashlib.sha256(open(KERNEL_SRC[kname], "rb").read()).hexdigest()
     if rec.get("source_sha256", rec.get("tile_pass_sha256")) != src:
         return None
@@ -317,7 +320,7 @@ def main():
     launches, kms = prof.get(kname, (0, 0.0))
     k_avg_s = kms / max(launches, 1) / 1e3
     achieved = k_bytes / k_avg_s if k_avg_s > 0 else 0.0
-    traffic = pmc_traffic(kname)
+    traffic = pmc_traffic(kname, args.workload)
     roofline = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": kname,
                 "avg_launch_us": k_avg_s * 1e6, "bytes_per_launch": k_bytes,

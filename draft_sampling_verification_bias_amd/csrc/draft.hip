@@ -735,6 +735,7 @@ struct CellArgs {
 // every (request, unit) has two threads; the halves' sums meet in LDS.
 constexpr int kCellHalf = 256;
 constexpr int kCellThreads = 2 * kCellHalf;
+constexpr int kCellZ = 8;  // values of z = [s_{k-1}; W1[x_{k-1}]] staged per thread: nreq * 2r <= kCellZ * kCellThreads
 
 template <bool kBf16>
 __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
@@ -802,9 +803,9 @@ __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
   }
   __syncthreads();
 
-  // z = [s_{k-1}; W1[x_{k-1}]]: every load issued before the first LDS store
-  // (nreq * 2r <= 4096, so at most 8 values per thread).
-  constexpr int kZ = 8;
+  // z = [s_{k-1}; W1[x_{k-1}]]: every load issued before the first LDS store,
+  // at most kCellZ values per thread (launch_rnn_draft checks nreq * 2r).
+  constexpr int kZ = kCellZ;
   const int nz = a.nreq * r2;
   float zv[kZ];
 #pragma unroll
@@ -912,6 +913,7 @@ hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
   ca.V = a.V;
   ca.r = a.r;
   ca.nreq = a.r <= 256 ? 8 : 4;          // z of the group: at most 16 KB of LDS
+  if ((long long)ca.nreq * 2 * a.r > (long long)kCellZ * kCellThreads) return hipErrorInvalidValue;  // r > 512
   ca.jn = kCellHalf / ca.nreq;
   const dim3 cgrid((a.B + ca.nreq - 1) / ca.nreq, (a.r + ca.jn - 1) / ca.jn);
   const int chunk = kCellHalf * 4 / ca.jn;  // Wp columns per LDS stage: 3 float4 loads per thread
