@@ -388,8 +388,10 @@ def main():
             torch.cuda.synchronize()
             return (time.perf_counter() - t) / args.schedule_steps * 1e3
 
+        # the same per-position launches with and without the confidence head
+        # (a draft that returns confidences does not take the resident loop)
         draft_ms = timed(lambda i: dsp.markov_draft(U, W1, W2, x0, T, seeds, 2000, out=dout, workspace=ws_d,
-                                                    stream=stream, W2T=W2T_d))
+                                                    stream=stream))
         draft_conf_ms = timed(lambda i: draft_conf(2000))
         plan_ms = timed(lambda i: plan())
         full_ms = timed(lambda i: verify_at(None, 2000))
