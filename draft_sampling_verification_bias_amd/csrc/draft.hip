@@ -727,155 +727,149 @@ struct CellArgs {
   float* state;        // [2][B][r]
   uint16_t* opnd;      // [B * gamma][2r]: bf16 hi parts, then lo parts
   float* e_out;        // optional [B][gamma][r]
-  int B, gamma, V, r, k, nreq, jn;
+  int B, gamma, V, r, k;
 };
 
-// The cell's workgroup: two halves of kCellHalf threads.  Half h sums the
-// columns [h r, h r + r) of z (h = 0: the state, h = 1: the token row), so
-// every (request, unit) has two threads; the halves' sums meet in LDS.
-constexpr int kCellHalf = 256;
-constexpr int kCellThreads = 2 * kCellHalf;
-constexpr int kCellZ = 8;  // values of z = [s_{k-1}; W1[x_{k-1}]] staged per thread: nreq * 2r <= kCellZ * kCellThreads
+// The cell's workgroup owns 16 requests and 16 state units: per gate
+// (g, c, o) a 16 x 16 block of [B x 2r] . [2r x 3r], the product z W_p^T
+// with z = [s_{k-1}; W1[x_{k-1}]], on the float32 MFMA
+// v_mfma_f32_16x16x4_f32.  Six waves: (gate, half of z), the state half
+// (columns 0..r-1) and the token half (r..2r-1); the halves' blocks meet in
+// LDS, where one thread per (request, unit) finishes the cell.
+constexpr int kCellReq = 16;
+constexpr int kCellUnits = 16;
+constexpr int kCellWaves = 6;
+constexpr int kCellThreads = kCellWaves * kWave;
+constexpr int kCellChunks = 16;  // 16-column k chunks loaded together (all of a half at r <= 256)
+
+typedef float cellx4 __attribute__((ext_vector_type(4)));
+
+// One wave's half of z against its gate's W_p rows.  Lane l: request row
+// l % 16 of z (zrow, at column 4 (l / 16) of the half) and unit row l % 16 of
+// W_p (wrow, likewise).  The k order inside a 16-column chunk m is chosen so
+// that each lane loads four consecutive columns: MFMA i of the chunk takes
+// column 16 m + 4 (l / 16) + i from both operands.  Every load of a pass is
+// issued before the first MFMA.  kZbf: z is a bf16 row (the token half with
+// bf16 weights), else float32.  zrow_of(zrow, zmask) gives the lane's z row
+// and a mask ANDed into its bits (0: this lane's z is zero); it is called
+// after the first W_p loads are issued, so that a token load overlaps them.
+template <bool kZbf, class ZRowOf>
+__device__ __forceinline__ void cell_half(ZRowOf zrow_of, const float* wrow, int nchunk, cellx4& acc0,
+                                          cellx4& acc1) {
+  const void* zrow = nullptr;
+  uint32_t zmask = 0;
+  for (int p0 = 0; p0 < nchunk; p0 += kCellChunks) {
+    // chunks past the end repeat the last one (loaded, not used)
+    float4 w[kCellChunks];
+    uint4 z[kCellChunks];  // float32 bits
+#pragma unroll
+    for (int q = 0; q < kCellChunks; ++q) w[q] = *reinterpret_cast<const float4*>(wrow + 16 * min(p0 + q, nchunk - 1));
+    if (p0 == 0) zrow_of(zrow, zmask);
+    if constexpr (kZbf) {
+      uint2 zr[kCellChunks];
+#pragma unroll
+      for (int q = 0; q < kCellChunks; ++q)
+        zr[q] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(zrow) + 16 * min(p0 + q, nchunk - 1));
+#pragma unroll
+      for (int q = 0; q < kCellChunks; ++q) {
+        // a bf16 value is the high half of its float32
+        const uint32_t x = zr[q].x & zmask, y = zr[q].y & zmask;
+        z[q] = make_uint4(x << 16, x & 0xffff0000u, y << 16, y & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kCellChunks; ++q) {
+        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(zrow) + 16 * min(p0 + q, nchunk - 1));
+        z[q] = make_uint4(v.x & zmask, v.y & zmask, v.z & zmask, v.w & zmask);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kCellChunks; ++q) {
+      if (p0 + q < nchunk) {
+        // two accumulators: no MFMA waits on the one just issued
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(z[q].x), w[q].x, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(z[q].y), w[q].y, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(z[q].z), w[q].z, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(z[q].w), w[q].w, acc1, 0, 0, 0);
+      }
+    }
+  }
+}
 
 template <bool kBf16>
 __global__ __launch_bounds__(kCellThreads) void rnn_cell_kernel(CellArgs a) {
-  // LDS: z of the group [nreq][2r], then per half one chunk of the
-  // workgroup's 3 jn rows of Wp, [3 jn][chunk + 1] (the odd pitch puts the
-  // rows a wave reads in different banks).
-  extern __shared__ float zs[];
-  const int r = a.r, r2 = 2 * a.r;
-  const int half = threadIdx.x / kCellHalf, t = threadIdx.x - half * kCellHalf;
-  const int jn = a.jn, chunk = kCellHalf * 4 / jn, pitch = chunk + 1;
-  float* sw = zs + (size_t)a.nreq * r2 + (size_t)half * 3 * jn * pitch;
-  const int b0 = blockIdx.x * a.nreq;
-  const int j0 = blockIdx.y * jn;
+  __shared__ float part[kCellWaves][kCellReq][kCellUnits + 1];
+  const int r = a.r;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gate = wave >> 1, zh = wave & 1;
+  const int b0 = blockIdx.x * kCellReq, j0 = blockIdx.y * kCellUnits;
   const float* sprev = a.state + (size_t)((a.k - 1) & 1) * a.B * r;
   float* snext = a.state + (size_t)(a.k & 1) * a.B * r;
 
-  // Wp chunk loads of this half: 3 jn rows x chunk columns = 3 float4 per
-  // thread, consecutive threads along a row.
-  constexpr int kLoads = 3;
-  const int q4 = chunk / 4;
-  const int cbase = half * r;
-  float4 wv[kLoads];
-  auto load_chunk = [&](int c0) {
-#pragma unroll
-    for (int l = 0; l < kLoads; ++l) {
-      const int idx = l * kCellHalf + t;
-      const int lr = idx / q4, cq = idx - (idx / q4) * q4;     // local row 0 .. 3 jn - 1
-      const int g = lr / jn, jj = lr - (lr / jn) * jn;
-      const int j = min(j0 + jj, r - 1);                         // rows past r: clamped, unused
-      wv[l] = c0 + 4 * cq < r
-                  ? *reinterpret_cast<const float4*>(a.Wp + (size_t)(g * r + j) * r2 + cbase + c0 + 4 * cq)
-                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);       // past the half (r % chunk != 0)
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int l = 0; l < kLoads; ++l) {
-      const int idx = l * kCellHalf + t;
-      const int lr = idx / q4, cq = idx - (idx / q4) * q4;
-      float* d = sw + (size_t)lr * pitch + 4 * cq;
-      d[0] = wv[l].x;
-      d[1] = wv[l].y;
-      d[2] = wv[l].z;
-      d[3] = wv[l].w;
-    }
-  };
+  // lane l: request b0 + l % 16 (rows past B repeat the last request and are
+  // not stored) and unit j0 + l % 16 (r % 16 == 0: every unit exists)
+  const int lr = lane & 15, kq = 4 * (lane >> 4);
+  const int bl = min(b0 + lr, a.B - 1);
+  const float* wrow = a.Wp + ((size_t)gate * r + j0 + lr) * (size_t)(2 * r) + (size_t)zh * r + kq;
 
-  __shared__ int sx[8];  // x_{k-1} of each request of the group
-  if (threadIdx.x < a.nreq) {
-    const int b = b0 + threadIdx.x;
-    sx[threadIdx.x] = b >= a.B ? -1 : (a.k == 1 ? a.x0[b] : a.tokens[(size_t)b * a.gamma + a.k - 2]);
-  }
-  load_chunk(0);
-  const int i = t / jn, jj = t - (t / jn) * jn;
-  const int j = j0 + jj;
-  const int b = b0 + i;
-  const bool mine = half == 0 && b < a.B && j < r;
-  const size_t row = (size_t)b * a.gamma + a.k - 1;
-  float hv[3] = {0.0f, 0.0f, 0.0f};
-  if (mine) {
+  // the finishing thread's inputs, loaded before the products: thread t <
+  // 256 finishes (request b0 + t / 16, unit j0 + t % 16)
+  const int t = threadIdx.x;
+  const int ri = (t / kCellUnits) & (kCellReq - 1), ui = t & (kCellUnits - 1);
+  const int b = b0 + ri, j = j0 + ui;
+  const bool fin = t < kCellReq * kCellUnits && b < a.B;
+  const size_t row = (size_t)min(b, a.B - 1) * a.gamma + a.k - 1;
+  float hg = 0.0f, hc = 0.0f, ho = 0.0f, sp = 0.0f;
+  if (fin) {
     const float* h = a.hp + row * 3 * r;
-    hv[0] = h[j];
-    hv[1] = h[r + j];
-    hv[2] = h[2 * r + j];
+    hg = h[j];
+    hc = h[r + j];
+    ho = h[2 * r + j];
+    if (a.k > 1) sp = sprev[(size_t)b * r + j];
   }
-  __syncthreads();
 
-  // z = [s_{k-1}; W1[x_{k-1}]]: every load issued before the first LDS store,
-  // at most kCellZ values per thread (launch_rnn_draft checks nreq * 2r).
-  constexpr int kZ = kCellZ;
-  const int nz = a.nreq * r2;
-  float zv[kZ];
-#pragma unroll
-  for (int q = 0; q < kZ; ++q) {
-    const int idx = q * kCellThreads + threadIdx.x;
-    const int zi = idx / r2, zc = idx - (idx / r2) * r2, zb = b0 + zi;
-    float v = 0.0f;
-    if (idx < nz && zb < a.B) {
-      if (zc < r) {
-        if (a.k > 1) v = sprev[(size_t)zb * r + zc];
+  cellx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (zh == 0) {
+    // the state half; zero at k = 1 (s_0 = 0)
+    auto srow = [&](const void*& zrow, uint32_t& zmask) {
+      zrow = sprev + (size_t)bl * r + kq;
+      zmask = 0xffffffffu;
+    };
+    if (a.k > 1) cell_half<false>(srow, wrow, r / 16, acc0, acc1);
+  } else {
+    // the token half: W1[x_{k-1}], zero for an out-of-range token (its
+    // request is reported invalid by the selection)
+    auto trow = [&](const void*& zrow, uint32_t& zmask) {
+      const int x = a.k == 1 ? a.x0[bl] : a.tokens[(size_t)bl * a.gamma + a.k - 2];
+      const bool bad = (unsigned)x >= (unsigned)a.V;
+      const size_t xo = (bad ? 0 : (size_t)x * r) + kq;
+      zmask = bad ? 0u : 0xffffffffu;
+      if constexpr (kBf16) {
+        zrow = reinterpret_cast<const uint16_t*>(a.W1) + xo;
       } else {
-        const int x = sx[zi];
-        if ((unsigned)x < (unsigned)a.V) v = w1_at<kBf16>(a.W1, (size_t)x * r + (zc - r));
+        zrow = reinterpret_cast<const float*>(a.W1) + xo;
       }
-    }
-    zv[q] = v;
+    };
+    cell_half<kBf16>(trow, wrow, r / 16, acc0, acc1);
   }
+  // lane l holds rows (requests) 4 (l / 16) + i, column (unit) l % 16
 #pragma unroll
-  for (int q = 0; q < kZ; ++q) {
-    const int idx = q * kCellThreads + threadIdx.x;
-    if (idx < nz) zs[idx] = zv[q];
-  }
-
-  const float* z = zs + (size_t)i * r2 + cbase;
-  const float* wg = sw + (size_t)jj * pitch;
-  const float* wc = sw + (size_t)(jn + jj) * pitch;
-  const float* wo = sw + (size_t)(2 * jn + jj) * pitch;
-  // two partial sums per projection (even and odd columns): shorter chains
-  float g = 0.0f, c = 0.0f, o = 0.0f, g2 = 0.0f, c2 = 0.0f, o2 = 0.0f;
-  for (int c0 = 0; c0 < r; c0 += chunk) {
-    __syncthreads();  // the previous chunk is consumed (first pass: z is staged)
-    store_chunk();
-    __syncthreads();
-    if (c0 + chunk < r) load_chunk(c0 + chunk);  // in flight during the products
-    const int cn = min(chunk, r - c0);  // even: r % 16 == 0
-#pragma unroll 4
-    for (int q = 0; q < cn; q += 2) {
-      const float za = z[c0 + q], zb = z[c0 + q + 1];
-      g = fmaf(wg[q], za, g);
-      c = fmaf(wc[q], za, c);
-      o = fmaf(wo[q], za, o);
-      g2 = fmaf(wg[q + 1], zb, g2);
-      c2 = fmaf(wc[q + 1], zb, c2);
-      o2 = fmaf(wo[q + 1], zb, o2);
-    }
-  }
-  g += g2;
-  c += c2;
-  o += o2;
-
-  // the token half's sums to the state half (the Wp stages are free now)
+  for (int i = 0; i < 4; ++i) part[wave][kq + i][lr] = acc0[i] + acc1[i];
   __syncthreads();
-  float* xch = zs + (size_t)a.nreq * r2;  // [3][kCellHalf]
-  if (half == 1) {
-    xch[t] = g;
-    xch[kCellHalf + t] = c;
-    xch[2 * kCellHalf + t] = o;
-  }
-  __syncthreads();
-  if (!mine) return;
-  g += xch[t] + hv[0];
-  c += xch[kCellHalf + t] + hv[1];
-  o += xch[2 * kCellHalf + t] + hv[2];
+
+  // one thread per (request, unit): g, c, o of both halves plus h^p
+  if (!fin) return;
+  const float g = part[0][ri][ui] + part[1][ri][ui] + hg;
+  const float c = part[2][ri][ui] + part[3][ri][ui] + hc;
+  const float o = part[4][ri][ui] + part[5][ri][ui] + ho;
   const float sg = 1.0f / (1.0f + expf(-g));
-  snext[(size_t)b * r + j] = sg * zs[(size_t)i * r2 + j] + (1.0f - sg) * tanhf(c);
+  snext[(size_t)b * r + j] = sg * sp + (1.0f - sg) * tanhf(c);
   const float e = tanhf(o);
   const uint16_t hi = bf16_round(e);
   const uint16_t lo = bf16_round(e - bf16_to_float(hi));
-  a.opnd[row * r2 + j] = hi;
-  a.opnd[row * r2 + r + j] = lo;
+  a.opnd[row * 2 * r + j] = hi;
+  a.opnd[row * 2 * r + r + j] = lo;
   if (a.e_out) a.e_out[row * r + j] = e;
 }
 
@@ -912,12 +906,8 @@ hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
   ca.gamma = a.gamma;
   ca.V = a.V;
   ca.r = a.r;
-  ca.nreq = a.r <= 256 ? 8 : 4;          // z of the group: at most 16 KB of LDS
-  if ((long long)ca.nreq * 2 * a.r > (long long)kCellZ * kCellThreads) return hipErrorInvalidValue;  // r > 512
-  ca.jn = kCellHalf / ca.nreq;
-  const dim3 cgrid((a.B + ca.nreq - 1) / ca.nreq, (a.r + ca.jn - 1) / ca.jn);
-  const int chunk = kCellHalf * 4 / ca.jn;  // Wp columns per LDS stage: 3 float4 loads per thread
-  const size_t clds = ((size_t)ca.nreq * 2 * a.r + (size_t)2 * 3 * ca.jn * (chunk + 1)) * sizeof(float);
+  if (a.r % 16 != 0) return hipErrorInvalidValue;  // whole 16-unit blocks and 16-column k chunks
+  const dim3 cgrid((a.B + kCellReq - 1) / kCellReq, a.r / kCellUnits);
 
   TileArgs t = {};
   t.U = a.U;
@@ -961,7 +951,7 @@ hipError_t launch_rnn_draft(const RnnDraftArgs& a, hipStream_t s) {
     ca.k = k;
     {
       ProfScope prof(s, kProfRnnCell);
-      hipLaunchKernelGGL(rnn_cell_kernel<true>, cgrid, dim3(kCellThreads), clds, s, ca);
+      hipLaunchKernelGGL(rnn_cell_kernel<true>, cgrid, dim3(kCellThreads), 0, s, ca);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

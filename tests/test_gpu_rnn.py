@@ -88,10 +88,10 @@ SMALL = [
     ("v151936_b32", dict(V=4099, B=37, gamma=5, r=64)),
     ("v151936_b256_t07", dict(V=3001, B=40, r=256)),
     ("greedy_v151936_b512", dict(V=5003, B=70, r=32)),
-    # r = 512: four requests per cell workgroup, 64 state units each
+    # r = 512: two load passes of the cell's 16-column chunks
     ("v151936_b32", dict(V=130, B=3, gamma=2, r=512)),
     ("v151936_b32", dict(V=5, B=2, gamma=3, r=16)),
-    # r not a multiple of the cell's 32-column Wp stage: a ragged last stage
+    # r = 48: three chunks, the rest of the cell's load pass repeats the last
     ("v151936_b32", dict(V=777, B=11, gamma=3, r=48)),
     # many full tiles and a ragged one under the generic tile kernel, several
     # row groups, a ragged request group of the cell
