@@ -474,26 +474,35 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap || kParts == 2 
 // halves in flight; the two-buffer kernel waits for all of its loads at every
 // half and so leaves the memory system idle while it computes.
 //
-// Wait counts.  Per wave a half is kRingDma DMA instructions (which the
+// Wait counts.  Per wave a half is kDma DMA instructions (which the
 // compiler does not see) and 8 U loads (which it does), issued in the order
 // W2(j+2) ... U(j+2), so at the start of step j the operations issued after
 // U(j) are W2(j+1) and U(j+1) (when half j+1 exists) and at most one summary
-// store; a vmcnt of kRingDma + 8 lets exactly those stay in flight (a store
+// store; a vmcnt of (DMA instructions) + 8 lets exactly those stay in flight (a store
 // among them only makes the wait one operation stricter).  The compiler adds
 // its own waits for the U registers from the loads it sees; those are always
 // sufficient and at most somewhat stricter.
+// ---------------------------------------------------------------------------
+//
+// Two-part operand rows (kParts == 2, the RNN head's e_hi, e_lo) need twice
+// the operand registers, which eight waves per CU cannot hold; that variant
+// runs four waves (groups of 128 rows) with the same ring, one workgroup per
+// CU.
 // ---------------------------------------------------------------------------
 constexpr int kRingWaves = 8;
 constexpr int kRingThreads = kWave * kRingWaves;
 constexpr int kRingRows = 32 * kRingWaves;            // rows per group
 constexpr int kRingStages = 3;                        // W2 buffers in LDS
-constexpr int kRingKPerWave = kFastR / kRingWaves;    // W2 rows k staged per wave
-constexpr int kRingDma = kRingKPerWave / 8;           // DMA instructions per wave per half
-constexpr int kRingWait = kRingDma + 8;               // ops of one later half
+constexpr int kRing2Waves = 4;                        // waves of the two-part variant
 
-template <int kMode>
-__global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int nslices) {
+template <int kMode, int kWaves = kRingWaves, int kParts = 1>
+__global__ __launch_bounds__(kWave * kWaves) void tile_ring_kernel(TileArgs a, int nslices) {
   static_assert(kMode == kModeSample || kMode == kModeGreedy, "ring kernel modes");
+  static_assert(kParts == 1 || kParts == 2, "one or two operand parts");
+  constexpr int kRows = 32 * kWaves;            // rows per group
+  constexpr int kKPerWave = kFastR / kWaves;    // W2 rows k staged per wave
+  constexpr int kDma = kKPerWave / 8;           // DMA instructions per wave per half
+  constexpr int kWait = kDma + 8;               // ops of one later half
   extern __shared__ __align__(16) unsigned char smem[];
   int group, slice;
   pipe_block(a.ngroups, nslices, group, slice);
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
   // Lane (n, hh) of wave w owns request row R = 256 group + 32 w + n and, in a
   // half starting at column c, columns c + 32 nb + 8 q + 4 hh + 0..3.  Rows at
   // or past row_end read a valid row, get no previous token and write nothing.
-  const int R = group * kRingRows + 32 * wave + n;
+  const int R = group * kRows + 32 * wave + n;
   const bool rowok = R < a.row_end;
   const int Rc = rowok ? R : a.row_end - 1;
   const size_t rs = a.kper == 1 ? (size_t)a.gamma * V : V;
@@ -520,7 +529,7 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
   // DMA lane mapping: wave w stages rows k = 32 w .. 32 w + 31, 8 per
   // instruction, lane l the 16-byte slot l % 8 of row 32 w + 8 i + l / 8 (the
   // XOR permutation depends on (k / 2) mod 2 only, the same for every i).
-  const int w2row = kRingKPerWave * wave + (lane >> 3);
+  const int w2row = kKPerWave * wave + (lane >> 3);
   const uint32_t w2off = ((uint32_t)w2row * (uint32_t)V + 8u * (uint32_t)w2h_slot(w2row, lane & 7)) * 2u;
   const int c00 = t_begin * kTileCols;
   auto bufp = [&](int j) -> unsigned char* { return smem + (size_t)(j % kRingStages) * kHalfBytes; };
@@ -528,8 +537,8 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
     unsigned char* buf = bufp(j);
     const int c = c00 + kHalfCols * j;
 #pragma unroll
-    for (int i = 0; i < kRingDma; ++i) {
-      const int rbase = kRingKPerWave * wave + 8 * i;
+    for (int i = 0; i < kDma; ++i) {
+      const int rbase = kKPerWave * wave + 8 * i;
       dma16(W2 + c, w2off + (uint32_t)(i * 16) * (uint32_t)V, buf + (size_t)rbase * 128);
     }
   };
@@ -545,35 +554,47 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
   // nothing else), the W1 row, W2(0), U(0), W2(1), U(1).  Everything a
   // workgroup needs for step 0 is thus requested before the bulk of the
   // kernel's loads, and the W1 row ahead of the halves.
-  bf16x8 ev[16];
+  bf16x8 ev[kParts][16];
   float4 uA[2][4], uB[2][4];
-  if (a.esw) {
-    // The operand stored by the previous position's selection: 16
-    // fully-coalesced 1 KB loads per wave, no dependence on the previous
-    // token.  (Rows whose previous token was invalid read a stale operand;
-    // their summaries are never used, the selection propagating the
-    // invalid token.)
-    const uint4* ew = a.esw + ((size_t)group * kRingWaves + wave) * 16 * kWave + lane;
+  bool stored = false;
+  if constexpr (kParts == 1 && kWaves == kRingWaves) {
+    if (a.esw) {
+      // The operand stored by the previous position's selection: 16
+      // fully-coalesced 1 KB loads per wave, no dependence on the previous
+      // token.  (Rows whose previous token was invalid read a stale operand;
+      // their summaries are never used, the selection propagating the
+      // invalid token.)
+      const uint4* ew = a.esw + ((size_t)group * kRingWaves + wave) * 16 * kWave + lane;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint4 v = ew[(size_t)j * kWave];
-      ev[j] = __builtin_bit_cast(bf16x8, v);
+      for (int j = 0; j < 16; ++j) {
+        const uint4 v = ew[(size_t)j * kWave];
+        ev[0][j] = __builtin_bit_cast(bf16x8, v);
+      }
+      issue_w2(0);
+      issue_u(0, uA);
+      stored = true;
     }
-    issue_w2(0);
-    issue_u(0, uA);
-  } else {
+  }
+  if (!stored) {
+    // the W1 row of the previous token, or operand-table row b gamma + kk of
+    // kParts parts
     const int prev = prev_token(a, row_info(a, Rc));
     const bool ok = rowok && prev_ok(a, prev);
-    const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
+    const uint16_t* w1row =
+        reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kParts * kFastR + 8 * hh;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ev[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
+    for (int p = 0; p < kParts; ++p)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ev[p][j] = *reinterpret_cast<const bf16x8*>(w1row + p * kFastR + j * 16);
     issue_w2(0);
     issue_u(0, uA);
     if (!ok) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int p = 0; p < kParts; ++p)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ev[j][e] = (__bf16)0.0f;
+        for (int j = 0; j < 16; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ev[p][j][e] = (__bf16)0.0f;
     }
   }
   issue_w2(1);
@@ -587,21 +608,39 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[nb][i] = 0.0f;
+    auto w2frag = [&](int j, int nb) -> bf16x8 {
+      bf16x8 av;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+      for (int h = 0; h < 2; ++h) {
+        const int row = 16 * j + 4 * h + trow;
+        const int col = 32 * nb + tcol;
+        const int addr = row * 128 + w2h_slot(row, col >> 3) * 16 + (col & 7) * 2;
+        const bf16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + addr));
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        bf16x8 av;
+        for (int e = 0; e < 4; ++e) av[4 * h + e] = t[e];
+      }
+      return av;
+    };
+    if constexpr (kParts == 1) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 16 * j + 4 * h + trow;
-          const int col = 32 * nb + tcol;
-          const int addr = row * 128 + w2h_slot(row, col >> 3) * 16 + (col & 7) * 2;
-          const bf16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + addr));
+      for (int j = 0; j < 16; ++j) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) av[4 * h + e] = t[e];
+        for (int nb = 0; nb < 2; ++nb) {
+          const bf16x8 av = w2frag(j, nb);
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[0][j], acc[nb], 0, 0, 0);
         }
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[j], acc[nb], 0, 0, 0);
+      }
+    } else {
+      // both parts against the same W2 fragments; the accumulators alternate
+      // so that no MFMA waits on the one just issued
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bf16x8 av0 = w2frag(j, 0), av1 = w2frag(j, 1);
+#pragma unroll
+        for (int p = 0; p < kParts; ++p) {
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0, ev[p][j], acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1, ev[p][j], acc[1], 0, 0, 0);
+        }
       }
     }
 #pragma unroll
@@ -621,7 +660,7 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
 
     // first half: step j (uA); half j + 1 always exists
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmem<kRingWait>();
+    wait_vmem<kWait>();
     __syncthreads();
     if (more) issue_w2(j + 2);
     logits(bufp(j), uA, x);
@@ -665,7 +704,7 @@ __global__ __launch_bounds__(kRingThreads) void tile_ring_kernel(TileArgs a, int
     __builtin_amdgcn_sched_barrier(0);
     // after U(j + 1): W2(j + 2) if it exists, then the eight loads into uA
     if (more) {
-      wait_vmem<kRingWait>();
+      wait_vmem<kWait>();
     } else {
       wait_vmem<8>();
     }
@@ -931,12 +970,12 @@ int compute_units_of_device() {
 // The ring kernel's LDS (96 KB) is above the default dynamic limit: raise the
 // limit once per process for each instantiation (the attribute belongs to the
 // kernel, not to a device).
-template <int kMode>
+template <int kMode, int kWaves = kRingWaves, int kParts = 1>
 static hipError_t ring_lds_attribute(size_t lds) {
   static hipError_t state = hipErrorNotReady;
   if (state == hipErrorNotReady)
-    state = hipFuncSetAttribute((const void*)tile_ring_kernel<kMode>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds);
+    state = hipFuncSetAttribute((const void*)tile_ring_kernel<kMode, kWaves, kParts>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   return state;
 }
 
@@ -1004,6 +1043,30 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
       if (nslices >= 8) nslices &= ~7;
       nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
       hipLaunchKernelGGL((tile_ring_kernel<kMode>), dim3(rgroups * nslices), dim3(kRingThreads), lds, s, g, nslices);
+      launch_tiles<kMode, kBf16>(a, 0, a.nrows, full_tiles, a.ntiles - full_tiles, s);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
+    if (a.opnd_rows == 2 && a.kper == 1) {
+      // two-part operand rows: the four-wave ring, one workgroup per CU
+      constexpr int kRows2 = 32 * kRing2Waves;
+      const int rgroups = (a.nrows + kRows2 - 1) / kRows2;
+      const size_t lds = (size_t)kRingStages * kHalfBytes;
+      const hipError_t e = ring_lds_attribute<kMode, kRing2Waves, 2>(lds);
+      if (e != hipSuccess) return e;
+      TileArgs g = a;
+      g.ngroups = rgroups;
+      g.rows_per_group = kRows2;
+      g.row_begin = 0;
+      g.row_end = a.nrows;
+      g.tile_begin = 0;
+      g.tile_count = full_tiles;
+      int nslices = compute_units_of_device() / rgroups;
+      if (nslices >= 8) nslices &= ~7;
+      nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
+      hipLaunchKernelGGL((tile_ring_kernel<kMode, kRing2Waves, 2>), dim3(rgroups * nslices),
+                         dim3(kWave * kRing2Waves), lds, s, g, nslices);
       launch_tiles<kMode, kBf16>(a, 0, a.nrows, full_tiles, a.ntiles - full_tiles, s);
       return hipGetLastError();
     }
