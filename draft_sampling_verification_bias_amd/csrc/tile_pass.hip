@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap || kParts == 2 
 // Two-part operand rows (kParts == 2, the RNN head's e_hi, e_lo) need twice
 // the operand registers, which eight waves per CU cannot hold; that variant
 // runs four waves (groups of 128 rows) with the same ring, one workgroup per
-// CU.
+// CU, as do single-part launches of at most 64 rows.
 // ---------------------------------------------------------------------------
 constexpr int kRingWaves = 8;
 constexpr int kRingThreads = kWave * kRingWaves;
@@ -1048,12 +1048,16 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
     }
   }
   if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
-    if (a.opnd_rows == 2 && a.kper == 1) {
-      // two-part operand rows: the four-wave ring, one workgroup per CU
+    // Two-part operand rows, and single-part launches of at most 64 rows
+    // (most of a 128-row group idle: the W2 stream sets the time, and the
+    // ring keeps more of it in flight than two two-buffer workgroups do):
+    // the four-wave ring, one workgroup per CU.
+    if (a.kper == 1 && (a.opnd_rows == 2 || (a.opnd_rows == 0 && a.nrows <= 64))) {
       constexpr int kRows2 = 32 * kRing2Waves;
       const int rgroups = (a.nrows + kRows2 - 1) / kRows2;
       const size_t lds = (size_t)kRingStages * kHalfBytes;
-      const hipError_t e = ring_lds_attribute<kMode, kRing2Waves, 2>(lds);
+      const hipError_t e = a.opnd_rows == 2 ? ring_lds_attribute<kMode, kRing2Waves, 2>(lds)
+                                            : ring_lds_attribute<kMode, kRing2Waves, 1>(lds);
       if (e != hipSuccess) return e;
       TileArgs g = a;
       g.ngroups = rgroups;
@@ -1065,8 +1069,13 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
       int nslices = compute_units_of_device() / rgroups;
       if (nslices >= 8) nslices &= ~7;
       nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
-      hipLaunchKernelGGL((tile_ring_kernel<kMode, kRing2Waves, 2>), dim3(rgroups * nslices),
-                         dim3(kWave * kRing2Waves), lds, s, g, nslices);
+      if (a.opnd_rows == 2) {
+        hipLaunchKernelGGL((tile_ring_kernel<kMode, kRing2Waves, 2>), dim3(rgroups * nslices),
+                           dim3(kWave * kRing2Waves), lds, s, g, nslices);
+      } else {
+        hipLaunchKernelGGL((tile_ring_kernel<kMode, kRing2Waves, 1>), dim3(rgroups * nslices),
+                           dim3(kWave * kRing2Waves), lds, s, g, nslices);
+      }
       launch_tiles<kMode, kBf16>(a, 0, a.nrows, full_tiles, a.ntiles - full_tiles, s);
       return hipGetLastError();
     }

@@ -131,6 +131,10 @@ SMALL = [
     # path, the ragged last tile and the 2-row tail group the general one
     ("v151936_b32", dict(V=4100, B=130, gamma=3)),
     ("greedy_v151936_b512", dict(V=2052, B=131, gamma=3)),
+    # at most 64 rows: the four-wave ring kernel, one partial 128-row group,
+    # then the ragged last tile
+    ("v151936_b32", dict(V=8200, B=64, gamma=3)),
+    ("greedy_v151936_b512", dict(V=8200, B=50, gamma=3)),
     # 200 rows: the 256-row ring kernel with a partial row group, two or more
     # tiles per workgroup, then the ragged last tile
     ("v151936_b256_t07", dict(V=65540, B=200, gamma=2)),
