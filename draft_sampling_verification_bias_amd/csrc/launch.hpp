@@ -216,7 +216,7 @@ hipError_t launch_confidence(const ConfArgs& a, bool bf16, hipStream_t s);
 
 // Hardware-aware prefix scheduler (schedule.hip): one workgroup, at most
 // kScheduleMax candidates (B * gamma).
-constexpr int kScheduleMax = 4096;
+constexpr int kScheduleMax = 16384;
 constexpr int kScheduleEarlyStop = 0;  // Algorithm 1
 constexpr int kScheduleCapacity = 1;   // first maximum of Theta over the whole scan
 constexpr int kScheduleTopK = 2;       // the first K candidates, K given on the device

@@ -22,7 +22,9 @@
 // by a bitonic network held in registers (shuffles within a wave, LDS only for
 // partners in other waves), the sorted survivals are summed in float64 by a
 // block scan, every thread tests Theta at its own admission counts, and the
-// first non-improving count is found by an LDS atomic minimum.
+// first non-improving count is found by an LDS atomic minimum.  Up to 16 keys
+// per lane (16384 candidates); the key array (up to 128 KB of LDS) is reused
+// for the per-request lengths once the scan has read it.
 #include <limits.h>
 
 #include "common.hpp"
@@ -32,7 +34,7 @@ namespace dspark {
 
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedWaves = kSchedThreads / kWave;
-constexpr int kSchedPer = kScheduleMax / kSchedThreads;  // keys per lane at most (4)
+constexpr int kSchedPer = kScheduleMax / kSchedThreads;  // keys per lane at most (16)
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x, int m) {
   const unsigned lo = __shfl_xor((unsigned)x, m), hi = __shfl_xor((unsigned)(x >> 32), m);
@@ -46,16 +48,16 @@ __device__ __forceinline__ void cmp_swap(unsigned long long& a, unsigned long lo
   b = up ? hi : lo;
 }
 
-// kE keys per lane: the sort covers 1024 kE keys (kE = 1, 2 or 4), and every
-// stage of the network is resolved at compile time.
+// kE keys per lane: the sort covers 1024 kE keys (kE = 1, 2, 4, 8 or 16),
+// every stage of the network is resolved at compile time, and the dynamic LDS
+// holds 1024 kE keys.
 template <int kE>
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __restrict__ surv,
                                                                  const double* __restrict__ sps, int B, int gamma,
                                                                  int mode, const int32_t* __restrict__ cap_in,
                                                                  int32_t* __restrict__ cap_out,
                                                                  int32_t* __restrict__ lengths, double* theta_out) {
-  __shared__ unsigned long long key[kScheduleMax];
-  __shared__ int len[kScheduleMax];
+  extern __shared__ unsigned long long key[];
   __shared__ double wtot[kSchedWaves];
   __shared__ double s_bt[kSchedWaves];
   __shared__ int s_bm[kSchedWaves];
@@ -72,18 +74,17 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
     s_valid = 0;
     s_stop = INT_MAX;
   }
-  for (int i = tid; i < B; i += kSchedThreads) len[i] = 0;
   // Key of candidate i = r gamma + (j - 1): the complemented bits of its
   // (positive) survival above its index, so ascending keys are descending
   // survivals with ties in index order.  Non-candidates (a <= 0 or NaN) and
   // the padding sort last.
-  unsigned long long v[kSchedPer];
+  unsigned long long v[E];
   int mine = 0;
 #pragma unroll
-  for (int q = 0; q < kSchedPer; ++q) {
+  for (int q = 0; q < E; ++q) {
     const int i = idx(q);
     unsigned long long k = ~0ull;
-    if (q < E && i < n) {
+    if (i < n) {
       const float a = surv[i];
       if (a > 0.0f) {
         k = ((unsigned long long)(~__float_as_uint(a)) << 32) | (unsigned)i;
@@ -97,13 +98,17 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
   __syncthreads();
 
   // This thread's share of the admission counts, and its throughput table
-  // entries, loaded now so that they arrive during the sort.
+  // entries, loaded now so that they arrive during the sort (after it at 8
+  // and 16 keys per lane, where holding them through the sort would spill).
   const int M = s_valid;
-  const int per = (M + kSchedThreads - 1) / kSchedThreads;  // <= kSchedPer
+  const int per = (M + kSchedThreads - 1) / kSchedThreads;  // <= E
   const int c0 = min(M, tid * per), c1 = min(M, c0 + per);
-  double sp[kSchedPer + 1];
+  double sp[E + 1];
+  auto load_sp = [&]() {
 #pragma unroll
-  for (int t = 0; t <= kSchedPer; ++t) sp[t] = sps[B + min(c0 + t, c1)];
+    for (int t = 0; t <= E; ++t) sp[t] = sps[B + min(c0 + t, c1)];
+  };
+  if constexpr (E <= 4) load_sp();
 
   // Bitonic sort, ascending.  Partners at distance j < 64 are in other lanes
   // of the wave (shuffles), 64 <= j < 64E in other registers of the lane,
@@ -114,27 +119,21 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
     for (int j = k >> 1; j > 0; j >>= 1) {
       if (j >= kWave * E) {
 #pragma unroll
-        for (int q = 0; q < kSchedPer; ++q)
-          if (q < E) key[idx(q)] = v[q];
+        for (int q = 0; q < E; ++q) key[idx(q)] = v[q];
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < kSchedPer; ++q) {
-          if (q < E) {
-            const int i = idx(q), p = i ^ j;
-            const unsigned long long y = key[p];
-            const bool keep_min = ((i & k) == 0) == (i < p);
-            v[q] = keep_min ? (v[q] < y ? v[q] : y) : (v[q] < y ? y : v[q]);
-          }
+        for (int q = 0; q < E; ++q) {
+          const int i = idx(q), p = i ^ j;
+          const unsigned long long y = key[p];
+          const bool keep_min = ((i & k) == 0) == (i < p);
+          v[q] = keep_min ? (v[q] < y ? v[q] : y) : (v[q] < y ? y : v[q]);
         }
         __syncthreads();
-      } else if (j >= kWave) {  // j = 64 or 128: pairs of registers (E >= 2)
-        if (j == kWave) {
-          cmp_swap(v[0], v[1], (idx(0) & k) == 0);
-          if (E == 4) cmp_swap(v[2], v[3], (idx(2) & k) == 0);
-        } else {
-          cmp_swap(v[0], v[2], (idx(0) & k) == 0);
-          cmp_swap(v[1], v[3], (idx(1) & k) == 0);
-        }
+      } else if (j >= kWave) {  // 64 <= j < 64 E: registers q and q + j / 64 of the lane
+        const int d = j / kWave;
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+          if ((q & d) == 0) cmp_swap(v[q], v[q + d], (idx(q) & k) == 0);
       } else {
 #pragma unroll
         for (int q = 0; q < E; ++q) {
@@ -147,16 +146,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
     }
   }
 #pragma unroll
-  for (int q = 0; q < kSchedPer; ++q)
-    if (q < E) key[idx(q)] = v[q];
+  for (int q = 0; q < E; ++q) key[idx(q)] = v[q];
+  if constexpr (E > 4) load_sp();
   __syncthreads();
 
   // Thread t owns the sorted candidates [c0, c1) of the M valid.
   auto value = [&](int pos) -> double { return (double)__uint_as_float(~(unsigned)(key[pos] >> 32)); };
-  double vals[kSchedPer];
+  double vals[E];
   double local = 0.0;
 #pragma unroll
-  for (int t = 0; t < kSchedPer; ++t) {
+  for (int t = 0; t < E; ++t) {
     vals[t] = c0 + t < c1 ? value(c0 + t) : 0.0;
     local += vals[t];
   }
@@ -180,7 +179,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
     double prev_theta = (Bd + S) * sp[0];
     bool going = true;
 #pragma unroll
-    for (int t = 0; t < kSchedPer; ++t) {
+    for (int t = 0; t < E; ++t) {
       if (going && c0 + t < c1) {
         S += vals[t];
         const double theta = (Bd + S) * sp[t + 1];
@@ -201,7 +200,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
     double bt = (Bd + S) * sp[0];
     int bm = c0;
 #pragma unroll
-    for (int t = 0; t < kSchedPer; ++t) {
+    for (int t = 0; t < E; ++t) {
       if (c0 + t < c1) {
         S += vals[t];
         const double theta = (Bd + S) * sp[t + 1];
@@ -242,10 +241,21 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
     mstar = min(max(cap_in[0], 0), M);
   }
 
-  for (int pos = tid; pos < mstar; pos += kSchedThreads) {
-    const unsigned id = (unsigned)key[pos];
-    atomicMax(&len[id / (unsigned)gamma], (int)(id % (unsigned)gamma) + 1);
+  // The candidate ids of the admitted positions this thread visits, then the
+  // key array becomes the lengths (B <= 1024 E ints).
+  unsigned ids[E];
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    const int pos = tid + q * kSchedThreads;
+    ids[q] = pos < mstar ? (unsigned)key[pos] : ~0u;
   }
+  __syncthreads();
+  int* len = reinterpret_cast<int*>(key);
+  for (int i = tid; i < B; i += kSchedThreads) len[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < E; ++q)
+    if (ids[q] != ~0u) atomicMax(&len[ids[q] / (unsigned)gamma], (int)(ids[q] % (unsigned)gamma) + 1);
   // Theta(m*), summed in the order of the comparisons above by the thread
   // that owns candidate m* - 1
   if (theta_out != nullptr) {
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
     } else if (c0 < mstar && mstar <= c1) {
       double S = S0, th = 0.0;
 #pragma unroll
-      for (int t = 0; t < kSchedPer; ++t) {
+      for (int t = 0; t < E; ++t) {
         if (c0 + t < mstar) {
           S += vals[t];
           th = (Bd + S) * sp[t + 1];
@@ -267,22 +277,37 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const float* __
   for (int i = tid; i < B; i += kSchedThreads) lengths[i] = len[i];
 }
 
+template <int kE>
+static hipError_t launch_schedule_e(const float* survival, const double* sps, int B, int gamma, int mode,
+                                    const int32_t* cap_in, int32_t* cap_out, int32_t* lengths, double* theta,
+                                    hipStream_t s) {
+  const size_t lds = sizeof(unsigned long long) * kSchedThreads * kE;
+  if (lds > 64 * 1024) {
+    // once per instantiation (the attribute belongs to the kernel)
+    static hipError_t state = hipErrorNotReady;
+    if (state == hipErrorNotReady)
+      state = hipFuncSetAttribute((const void*)schedule_kernel<kE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+    if (state != hipSuccess) return state;
+  }
+  hipLaunchKernelGGL(schedule_kernel<kE>, dim3(1), dim3(kSchedThreads), lds, s, survival, sps, B, gamma, mode,
+                     cap_in, cap_out, lengths, theta);
+  return hipGetLastError();
+}
+
 hipError_t launch_schedule(const float* survival, const double* sps, int B, int gamma, int mode,
                            const int32_t* cap_in, int32_t* cap_out, int32_t* lengths, double* theta, hipStream_t s) {
   ProfScope prof(s, kProfSchedule);
   const int n = B * gamma;
-  if (n <= kSchedThreads) {
-    hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, mode, cap_in,
-                       cap_out, lengths, theta);
-  } else if (n <= 2 * kSchedThreads) {
-    hipLaunchKernelGGL(schedule_kernel<2>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, mode, cap_in,
-                       cap_out, lengths, theta);
-  } else {
-    static_assert(kScheduleMax == 4 * kSchedThreads, "the largest instantiation covers kScheduleMax");
-    hipLaunchKernelGGL(schedule_kernel<4>, dim3(1), dim3(kSchedThreads), 0, s, survival, sps, B, gamma, mode, cap_in,
-                       cap_out, lengths, theta);
-  }
-  return hipGetLastError();
+  static_assert(kScheduleMax == 16 * kSchedThreads, "the largest instantiation covers kScheduleMax");
+  if (n <= kSchedThreads) return launch_schedule_e<1>(survival, sps, B, gamma, mode, cap_in, cap_out, lengths, theta, s);
+  if (n <= 2 * kSchedThreads)
+    return launch_schedule_e<2>(survival, sps, B, gamma, mode, cap_in, cap_out, lengths, theta, s);
+  if (n <= 4 * kSchedThreads)
+    return launch_schedule_e<4>(survival, sps, B, gamma, mode, cap_in, cap_out, lengths, theta, s);
+  if (n <= 8 * kSchedThreads)
+    return launch_schedule_e<8>(survival, sps, B, gamma, mode, cap_in, cap_out, lengths, theta, s);
+  return launch_schedule_e<16>(survival, sps, B, gamma, mode, cap_in, cap_out, lengths, theta, s);
 }
 
 }  // namespace dspark

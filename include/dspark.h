@@ -431,7 +431,7 @@ dspark_status dspark_confidence(const float* h, const float* w, const void* W1, 
  * survival products of positions that are admitted before them, which keeps
  * verification lossless; a capacity computed from the current round's
  * products would not.
- * 1 <= gamma <= 32, 1 <= B * gamma <= 4096.  Asynchronous on `stream`; needs
+ * 1 <= gamma <= 32, 1 <= B * gamma <= 16384.  Asynchronous on `stream`; needs
  * no workspace.
  */
 dspark_status dspark_schedule(const float* survival, const double* sps, int sps_len, int B, int gamma,

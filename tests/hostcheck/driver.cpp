@@ -191,12 +191,15 @@ int main() {
 
   // schedule: candidate limit, table length, modes
   reset();
+  CHECK(dspark_schedule((const float*)P(A), (const double*)P(Bp), 1 << 20, 2048, 8, DSPARK_SCHEDULE_EARLY_STOP,
+                        nullptr, nullptr, (int32_t*)P(C), nullptr, nullptr) == DSPARK_OK);  // 16384 candidates
+  reset();
   CHECK(dspark_schedule((const float*)P(A), (const double*)P(Bp), 256 * 8 + 1, 256, 7, DSPARK_SCHEDULE_EARLY_STOP,
                         nullptr, nullptr, (int32_t*)P(C), nullptr, nullptr) == DSPARK_OK);
   CHECK(strcmp(last.op, "schedule") == 0 && last.B == 256 && last.mode == 0);
   CHECK(dspark_schedule((const float*)P(A), (const double*)P(Bp), 256 * 8, 256, 7, DSPARK_SCHEDULE_EARLY_STOP,
                         nullptr, nullptr, (int32_t*)P(C), nullptr, nullptr) == DSPARK_ERR_INVALID_ARGUMENT);
-  CHECK(dspark_schedule((const float*)P(A), (const double*)P(Bp), 1 << 20, 4097, 1, DSPARK_SCHEDULE_EARLY_STOP,
+  CHECK(dspark_schedule((const float*)P(A), (const double*)P(Bp), 1 << 20, 16385, 1, DSPARK_SCHEDULE_EARLY_STOP,
                         nullptr, nullptr, (int32_t*)P(C), nullptr, nullptr) == DSPARK_ERR_INVALID_ARGUMENT);
   CHECK(dspark_schedule((const float*)P(A), (const double*)P(Bp), 1 << 20, 16, 4, DSPARK_SCHEDULE_TOP_K, nullptr,
                         nullptr, (int32_t*)P(C), nullptr, nullptr) == DSPARK_ERR_INVALID_ARGUMENT);

@@ -221,7 +221,7 @@ def test_schedule_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, 20, 4, 4, 0, None, None, FAKE, None, None) == INVALID   # sps shorter than B (gamma + 1) + 1
     assert f(FAKE, FAKE, 1 << 20, 0, 4, 0, None, None, FAKE, None, None) == INVALID
     assert f(FAKE, FAKE, 1 << 20, 4, 33, 0, None, None, FAKE, None, None) == INVALID
-    assert f(FAKE, FAKE, 1 << 20, 1024, 5, 0, None, None, FAKE, None, None) == INVALID  # more than 4096 candidates
+    assert f(FAKE, FAKE, 1 << 20, 4097, 4, 0, None, None, FAKE, None, None) == INVALID  # more than 16384 candidates
     assert f(None, FAKE, 1 << 20, 4, 4, 0, None, None, FAKE, None, None) == INVALID
     assert f(FAKE, FAKE, 1 << 20, 4, 4, 0, None, None, None, None, None) == INVALID
     assert f(FAKE, MISALIGNED, 1 << 20, 4, 4, 0, None, None, FAKE, None, None) == INVALID

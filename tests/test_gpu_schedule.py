@@ -90,7 +90,8 @@ def test_schedule_printed_examples():
         assert _check_schedule(a, e["sps"], "printed") == 0
 
 
-@pytest.mark.parametrize("B,gamma", [(1, 1), (1, 7), (7, 3), (256, 7), (512, 7), (585, 7), (128, 32), (4096, 1)])
+@pytest.mark.parametrize("B,gamma", [(1, 1), (1, 7), (7, 3), (256, 7), (512, 7), (585, 7), (128, 32), (4096, 1),
+                                     (1000, 7), (1171, 7), (2048, 8), (16384, 1)])
 def test_schedule_random_parity(B, gamma):
     rng = np.random.default_rng(B * 100 + gamma)
     exempt = 0
@@ -241,7 +242,7 @@ def _theta_at(a, sps, K):
     return B * sps[B] if K == 0 else trace[K - 1][4]
 
 
-@pytest.mark.parametrize("B,gamma", [(1, 3), (7, 3), (256, 7), (512, 7), (128, 32)])
+@pytest.mark.parametrize("B,gamma", [(1, 3), (7, 3), (256, 7), (512, 7), (128, 32), (1171, 7), (2048, 8)])
 def test_capacity_search_and_top_k_parity(B, gamma):
     rng = np.random.default_rng(7 * B + gamma)
     exempt = 0
