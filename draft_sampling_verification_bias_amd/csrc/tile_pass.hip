@@ -219,12 +219,9 @@ __device__ __forceinline__ void pipe_block(int ngroups, int nslices, int& group,
   slice = idx / ngroups;
 }
 
-// kParts == 2: operand-table rows of two bf16 parts (value, remainder), each
-// multiplied by the same W2 fragments; the second operand set needs the
-// register file of one workgroup per CU, as the overlap mode's target values do.
-template <int kMode, int kParts>
-__global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap || kParts == 2 ? 1 : 2) void tile_pipe_kernel(
-    TileArgs a, int nslices) {
+template <int kMode>
+__global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap ? 1 : 2) void tile_pipe_kernel(TileArgs a,
+                                                                                                 int nslices) {
   constexpr bool kOv = kMode == kModeOverlap;  // also streams the target rows
   extern __shared__ __align__(16) unsigned char smem[];
   int group, slice;
@@ -297,20 +294,15 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap || kParts == 2 
   // B operand: row R of E = W1[prev], k-chunk hh of each 16-wide k step.
   const int prev = prev_token(a, row_info(a, Rc));
   const bool ok = rowok && prev_ok(a, prev);
-  const uint16_t* w1row =
-      reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kParts * kFastR + 8 * hh;
-  bf16x8 ev[kParts][16];
+  const uint16_t* w1row = reinterpret_cast<const uint16_t*>(a.W1) + (size_t)(ok ? prev : 0) * kFastR + 8 * hh;
+  bf16x8 ev[16];
 #pragma unroll
-  for (int p = 0; p < kParts; ++p)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) ev[p][j] = *reinterpret_cast<const bf16x8*>(w1row + p * kFastR + j * 16);
+  for (int j = 0; j < 16; ++j) ev[j] = *reinterpret_cast<const bf16x8*>(w1row + j * 16);
   if (!ok) {
 #pragma unroll
-    for (int p = 0; p < kParts; ++p)
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ev[p][j][e] = (__bf16)0.0f;
+      for (int e = 0; e < 8; ++e) ev[j][e] = (__bf16)0.0f;
   }
 
   const int trow = 8 * hh + ((lane & 15) >> 2);             // + 16 j + 4 h
@@ -336,9 +328,7 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap || kParts == 2 
 #pragma unroll
           for (int e = 0; e < 4; ++e) av[4 * h + e] = t[e];
         }
-#pragma unroll
-        for (int p = 0; p < kParts; ++p)
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[p][j], acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ev[j], acc[nb], 0, 0, 0);
       }
     }
 #pragma unroll
@@ -484,10 +474,12 @@ __global__ __launch_bounds__(kTileThreads, kMode == kModeOverlap || kParts == 2 
 // sufficient and at most somewhat stricter.
 // ---------------------------------------------------------------------------
 //
-// Two-part operand rows (kParts == 2, the RNN head's e_hi, e_lo) need twice
-// the operand registers, which eight waves per CU cannot hold; that variant
-// runs four waves (groups of 128 rows) with the same ring, one workgroup per
-// CU, as do single-part launches of at most 64 rows.
+// Two-part operand rows (kParts == 2, the RNN head's e_hi, e_lo) are
+// multiplied by the same W2 fragments; their second operand set fills the
+// register file of eight waves (252 VGPRs).  A four-wave form (groups of 128
+// rows, one workgroup per CU) serves launches whose 256-row groups would be
+// mostly empty: two-part rows below 3/4 of a group, and single-part
+// launches of at most 64 rows.
 // ---------------------------------------------------------------------------
 constexpr int kRingWaves = 8;
 constexpr int kRingThreads = kWave * kRingWaves;
@@ -1004,17 +996,50 @@ static int fast_full_tiles(const TileArgs& a) { return (a.V & 3) == 0 ? a.V / kT
 // two-part operand rows, pipelined kernel only), at least one full tile, rows
 // at a constant stride, and W2 addressed with 32-bit byte offsets (2 r V < 2^32).
 static bool fast_path(const TileArgs& a, int mode, bool bf16) {
+  // two-part operand rows: sample and argmax modes, one block position per
+  // launch (the ring kernels)
   return bf16 && (mode == kModeSample || mode == kModeGreedy || mode == kModeOverlap) && a.r == kFastR &&
-         (a.opnd_rows == 0 || (a.opnd_rows == 2 && mode != kModeOverlap)) && (a.kper == 1 || a.kper == a.gamma) && fast_full_tiles(a) > 0 &&
+         (a.opnd_rows == 0 || (a.opnd_rows == 2 && mode != kModeOverlap && a.kper == 1)) &&
+         (a.kper == 1 || a.kper == a.gamma) && fast_full_tiles(a) > 0 &&
          (size_t)2 * kFastR * (size_t)a.V < ((size_t)1 << 32);
 }
 
-bool tile_pass_uses_ring(const TileArgs& a, int mode, bool bf16) {
+// The eight-wave ring's 256-row groups are at least 3/4 filled.
+static bool ring_wide(const TileArgs& a) {
   const int rgroups = (a.nrows + kRingRows - 1) / kRingRows;
-  // the ring kernel when its 256-row groups are at least 3/4 filled
+  return 4 * a.nrows >= 3 * rgroups * kRingRows;
+}
+
+bool tile_pass_uses_ring(const TileArgs& a, int mode, bool bf16) {
+  // the eight-wave ring with W1 rows (whose previous position's selection can
+  // store them in the ring's operand layout)
   return fast_path(a, mode, bf16) && (mode == kModeSample || mode == kModeGreedy) && a.kper == 1 &&
-         a.opnd_rows == 0 &&
-         4 * a.nrows >= 3 * rgroups * kRingRows;
+         a.opnd_rows == 0 && ring_wide(a);
+}
+
+// The full tiles of all rows on tile_ring_kernel<kMode, kWaves, kParts>: one
+// workgroup per CU, the column slices of every row group together filling
+// the CUs once.
+template <int kMode, int kWaves, int kParts>
+static hipError_t launch_ring(const TileArgs& a, int full_tiles, hipStream_t s) {
+  constexpr int kRows = 32 * kWaves;
+  const int rgroups = (a.nrows + kRows - 1) / kRows;
+  const size_t lds = (size_t)kRingStages * kHalfBytes;
+  const hipError_t e = ring_lds_attribute<kMode, kWaves, kParts>(lds);
+  if (e != hipSuccess) return e;
+  TileArgs g = a;
+  g.ngroups = rgroups;
+  g.rows_per_group = kRows;
+  g.row_begin = 0;
+  g.row_end = a.nrows;
+  g.tile_begin = 0;
+  g.tile_count = full_tiles;
+  int nslices = compute_units_of_device() / rgroups;
+  if (nslices >= 8) nslices &= ~7;
+  nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
+  hipLaunchKernelGGL((tile_ring_kernel<kMode, kWaves, kParts>), dim3(rgroups * nslices), dim3(kWave * kWaves), lds, s,
+                     g, nslices);
+  return hipGetLastError();
 }
 
 template <int kMode, bool kBf16>
@@ -1027,55 +1052,28 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
-    const int rgroups = (a.nrows + kRingRows - 1) / kRingRows;
-    if (tile_pass_uses_ring(a, kMode, kBf16)) {
-      const size_t lds = (size_t)kRingStages * kHalfBytes;
-      const hipError_t e = ring_lds_attribute<kMode>(lds);
-      if (e != hipSuccess) return e;
-      TileArgs g = a;
-      g.ngroups = rgroups;
-      g.rows_per_group = kRingRows;
-      g.row_begin = 0;
-      g.row_end = a.nrows;
-      g.tile_begin = 0;
-      g.tile_count = full_tiles;
-      int nslices = compute_units_of_device() / rgroups;  // one workgroup per CU
-      if (nslices >= 8) nslices &= ~7;
-      nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
-      hipLaunchKernelGGL((tile_ring_kernel<kMode>), dim3(rgroups * nslices), dim3(kRingThreads), lds, s, g, nslices);
-      launch_tiles<kMode, kBf16>(a, 0, a.nrows, full_tiles, a.ntiles - full_tiles, s);
-      return hipGetLastError();
+    // The ring kernels (one launch of rows at a constant stride):
+    //   eight waves (256-row groups) when those groups are at least 3/4
+    //   filled, for W1 rows and for two-part operand rows alike;
+    //   otherwise four waves (128-row groups) for two-part operand rows, and
+    //   for single-part launches of at most 64 rows (most of a 128-row group
+    //   idle: the W2 stream sets the time, and the ring keeps more of it in
+    //   flight than two two-buffer workgroups do).
+    hipError_t e = hipSuccess;
+    bool ring = a.kper == 1;
+    if (ring && a.opnd_rows == 0 && ring_wide(a)) {
+      e = launch_ring<kMode, kRingWaves, 1>(a, full_tiles, s);
+    } else if (ring && a.opnd_rows == 2 && ring_wide(a)) {
+      e = launch_ring<kMode, kRingWaves, 2>(a, full_tiles, s);
+    } else if (ring && a.opnd_rows == 2) {
+      e = launch_ring<kMode, kRing2Waves, 2>(a, full_tiles, s);
+    } else if (ring && a.opnd_rows == 0 && a.nrows <= 64) {
+      e = launch_ring<kMode, kRing2Waves, 1>(a, full_tiles, s);
+    } else {
+      ring = false;
     }
-  }
-  if constexpr (kBf16 && (kMode == kModeSample || kMode == kModeGreedy)) {
-    // Two-part operand rows, and single-part launches of at most 64 rows
-    // (most of a 128-row group idle: the W2 stream sets the time, and the
-    // ring keeps more of it in flight than two two-buffer workgroups do):
-    // the four-wave ring, one workgroup per CU.
-    if (a.kper == 1 && (a.opnd_rows == 2 || (a.opnd_rows == 0 && a.nrows <= 64))) {
-      constexpr int kRows2 = 32 * kRing2Waves;
-      const int rgroups = (a.nrows + kRows2 - 1) / kRows2;
-      const size_t lds = (size_t)kRingStages * kHalfBytes;
-      const hipError_t e = a.opnd_rows == 2 ? ring_lds_attribute<kMode, kRing2Waves, 2>(lds)
-                                            : ring_lds_attribute<kMode, kRing2Waves, 1>(lds);
+    if (ring) {
       if (e != hipSuccess) return e;
-      TileArgs g = a;
-      g.ngroups = rgroups;
-      g.rows_per_group = kRows2;
-      g.row_begin = 0;
-      g.row_end = a.nrows;
-      g.tile_begin = 0;
-      g.tile_count = full_tiles;
-      int nslices = compute_units_of_device() / rgroups;
-      if (nslices >= 8) nslices &= ~7;
-      nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
-      if (a.opnd_rows == 2) {
-        hipLaunchKernelGGL((tile_ring_kernel<kMode, kRing2Waves, 2>), dim3(rgroups * nslices),
-                           dim3(kWave * kRing2Waves), lds, s, g, nslices);
-      } else {
-        hipLaunchKernelGGL((tile_ring_kernel<kMode, kRing2Waves, 1>), dim3(rgroups * nslices),
-                           dim3(kWave * kRing2Waves), lds, s, g, nslices);
-      }
       launch_tiles<kMode, kBf16>(a, 0, a.nrows, full_tiles, a.ntiles - full_tiles, s);
       return hipGetLastError();
     }
@@ -1089,20 +1087,14 @@ static hipError_t launch_mode(const TileArgs& a, hipStream_t s) {
     g.tile_begin = 0;
     g.tile_count = full_tiles;
     // Two resident workgroups per CU (64 KB of LDS each; one in overlap mode,
-    // whose waves also hold the target values, and with two-part operands);
-    // the column slices of every row group together fill them once.
-    const bool one_per_cu = kMode == kModeOverlap || a.opnd_rows == 2;
+    // whose waves also hold the target values); the column slices of every
+    // row group together fill them once.
+    const bool one_per_cu = kMode == kModeOverlap;
     int nslices = (one_per_cu ? 1 : 2) * compute_units_of_device() / groups;
     if (nslices >= 8) nslices &= ~7;
     nslices = nslices < 1 ? 1 : (nslices > full_tiles ? full_tiles : nslices);
     const size_t lds = 2 * (size_t)kHalfBytes;
-    if (kMode != kModeOverlap && a.opnd_rows == 2) {
-      hipLaunchKernelGGL((tile_pipe_kernel<kMode, kMode == kModeOverlap ? 1 : 2>), dim3(groups * nslices),
-                         dim3(kTileThreads), lds, s, g, nslices);
-    } else {
-      hipLaunchKernelGGL((tile_pipe_kernel<kMode, 1>), dim3(groups * nslices), dim3(kTileThreads), lds, s, g,
-                         nslices);
-    }
+    hipLaunchKernelGGL((tile_pipe_kernel<kMode>), dim3(groups * nslices), dim3(kTileThreads), lds, s, g, nslices);
   }
   // The partial last tile, all rows.
   launch_tiles<kMode, kBf16>(a, 0, a.nrows, full_tiles, a.ntiles - full_tiles, s);
