@@ -306,7 +306,9 @@ def main():
     bytes_steps = [step_bytes(B, gamma, V, r, lens[i]) for i in range(nsteps)]
     mean_bytes = float(np.mean(bytes_steps))
     hbm_frac = mean_bytes / (med * 1e-3) / HBM_PEAK
-    accepted = float((lens + 1).mean()) / (med * 1e-3)
+    # tokens a round emits over all requests: the accepted draft tokens plus
+    # each request's correction or bonus token
+    emitted = float((lens + 1).sum(axis=1).mean()) / (med * 1e-3)
 
     # dominant kernel: the device-resident draft (one launch per step) when it
     # runs, else the per-position draft tile pass (sample mode at T > 0,
@@ -477,7 +479,7 @@ def main():
         "hbm_fraction": hbm_frac,
         "bytes_per_step": mean_bytes,
         "mfma_fraction": flops / (med * 1e-3) / MFMA_BF16_PEAK,
-        "accepted_tokens_per_s": accepted,
+        "emitted_tokens_per_s": emitted,
         "mean_accept_len": float(lens.mean()),
         "roofline": roofline,
         "kernels": kernels,
