@@ -118,7 +118,7 @@ def test_full_size_sampled_rnn_parity():
 
 def test_full_size_sampled_rnn_parity_greedy():
     """V = 151936, B = 512, gamma = 7, r = 256, T = 0 (argmax summaries on
-    the two-part pipelined tile kernel)."""
+    the eight-wave two-part ring tile kernel, two row groups)."""
     wl = workloads.make("greedy_v151936_b512")
     run_rnn(wl, [0, 300, 511], "greedy_v151936_b512", seed=1)
     torch.cuda.empty_cache()
@@ -164,3 +164,41 @@ def test_rnn_draft_is_deterministic_and_differs_from_markov():
     m = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, wl.T, d.seeds, 5)
     assert not np.array_equal(m[1].cpu().numpy(), a[1])
 
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("v151936_b256_t07", dict(V=20000, B=200, gamma=3)),   # the eight-wave two-part ring
+    ("greedy_v151936_b512", dict(V=20000, B=70, gamma=3)),  # the four-wave two-part ring, greedy
+])
+def test_rnn_draft_verified_at_scheduled_lengths(name, kw):
+    """An RNN-head draft verified with its e_k rows at fixed scheduled
+    lengths l_b (every length 0..gamma) against oracle.verify with the same
+    lengths and the oracle's own e_k."""
+    wl = workloads.make(name, **kw)
+    Wp, hp = workloads.rnn_inputs(wl.B, wl.gamma, wl.r, seed=4)
+    d = Dev(wl)
+    tok, prob, lse, e = dsp.rnn_draft(d.U, d.W1, d.W2, torch.from_numpy(Wp).cuda(), torch.from_numpy(hp).cuda(),
+                                      d.x0, wl.T, d.seeds, wl.rnd, with_e=True)
+    torch.cuda.synchronize()
+    tok_h = tok.cpu().numpy()
+    W1f, W2f = f64_weights(wl)
+    reqs = list(range(wl.B))
+    ref = oracle.rnn_draft(wl.U, W1f, W2f, Wp.astype(np.float64), None, wl.x0, wl.T, wl.seeds, wl.rnd,
+                           requests=reqs, hp=hp.astype(np.float64))
+    n, ex, whole = compare_draft(ref, tok_h, prob.cpu().numpy(), lse.cpu().numpy(), reqs, wl.T)
+    assert n > 0 and whole
+    lengths = (np.arange(wl.B) % (wl.gamma + 1)).astype(np.int32)
+    lens_d = torch.from_numpy(lengths).cuda()
+    W2T = dsp.transpose_w2(d.W2) if wl.T > 0 else None
+    alen, otok, aprob = dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, d.tgt, wl.T, d.seeds, wl.rnd, E=e,
+                                   W2T=W2T, lengths=lens_d)
+    torch.cuda.synchronize()
+    vreq = sorted(whole)
+    vref = oracle.verify(wl.U, W1f, W2f, wl.x0, tok_h, wl.tgt, wl.T, wl.seeds, wl.rnd, requests=vreq,
+                         lengths=lengths, E=ref["E"])
+    alen_h = alen.cpu().numpy()
+    nv, exv = compare_verify(vref, alen_h, otok.cpu().numpy(), aprob.cpu().numpy(), vreq, wl.T)
+    say("[%s] rnn draft at scheduled lengths: %d requests equal, %d exempt; mean accepted %.3f"
+        % (name, nv, exv, alen_h[vreq].mean()))
+    assert nv > 0 and exv <= 1
+    assert (alen_h[vreq] <= lengths[vreq]).all()
