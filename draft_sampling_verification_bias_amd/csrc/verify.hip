@@ -1056,24 +1056,50 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(VerifyArgs a, 
 // then one inverse-CDF draw with the stream-3 uniform.  p_d needs the bias at
 // every column of the row, so each chunk rebuilds 256 bias values: thread t
 // owns columns 4 (t % 64) .. +3 of the chunk and a quarter of the r products,
-// with all of its W2 loads in flight; the quarters are summed in LDS in a
-// fixed order, so both kernels obtain bit-identical residual terms.
+// kResBatch W2 rows of loads in flight at a time; the quarters are summed in
+// LDS in a fixed order.  Up to kResGroup fallback requests share each W2 load (their
+// biases are accumulated side by side, each in the same order as alone), and
+// both kernels run this one function, so they obtain bit-identical residual
+// terms.
 // ---------------------------------------------------------------------------
 constexpr int kResCols = 256;
+constexpr int kResGroup = 4;  // fallback requests per residual-mass item
+constexpr int kResBatch = 16;  // W2 rows per load batch of a thread
 
+struct ResGroup {
+  int n;                    // requests in the group (1..kResGroup)
+  int b[kResGroup];
+  FallbackInfo f[kResGroup];
+};
+
+// The operand rows of the group's requests into sw1f.
 template <bool kBf16>
-__device__ double residual_term(const VerifyArgs& a, const FallbackInfo& f, int b, int chunk, const float* sw1f,
-                                float (*sbias)[kResCols], double cf) {
+__device__ void residual_rows(const VerifyArgs& a, const ResGroup& rg, float (*sw1f)[512]) {
+  for (int i = 0; i < rg.n; ++i)
+    for (int j = threadIdx.x; j < a.r; j += kVThreads)
+      sw1f[i][j] = (float)opnd_val<kBf16>(a, rg.b[i], rg.f[i].j, rg.f[i].prev, j);
+  __syncthreads();
+}
+
+// Residual terms of column chunk * kResCols + threadIdx.x for the group's
+// requests (res[i], i < rg.n); sw1f[i] holds request i's operand row.
+template <bool kBf16>
+__device__ void residual_terms(const VerifyArgs& a, const ResGroup& rg, int chunk, const float (*sw1f)[512],
+                               float (*sbias)[4][kResCols], double cf, double (&res)[kResGroup]) {
   const int g = a.gamma;
   const int quad = threadIdx.x & 63, slice = threadIdx.x >> 6;
   const int kq = a.r / 4;  // r % 16 == 0
   const int c = chunk * kResCols + 4 * quad;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const bool vec = kBf16 && (c + 4 <= a.V) && ((a.V & 3) == 0);
-  for (int j0 = slice * kq; j0 < (slice + 1) * kq; j0 += 32) {
-    float wv[32][4];
+  float acc[kResGroup][4];
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) {
+  for (int i = 0; i < kResGroup; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
+  const bool vec = kBf16 && (c + 4 <= a.V) && ((a.V & 3) == 0);
+  for (int j0 = slice * kq; j0 < (slice + 1) * kq; j0 += kResBatch) {
+    float wv[kResBatch][4];
+#pragma unroll
+    for (int jj = 0; jj < kResBatch; ++jj) {
       const int j = j0 + jj;
       if (j < (slice + 1) * kq && vec) {
         const uint2 p = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.W2) + (size_t)j * a.V + c);
@@ -1088,46 +1114,71 @@ __device__ double residual_term(const VerifyArgs& a, const FallbackInfo& f, int 
       }
     }
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) {
-      const float e = j0 + jj < (slice + 1) * kq ? sw1f[j0 + jj] : 0.0f;
+    for (int i = 0; i < kResGroup; ++i) {
+      if (i >= rg.n) break;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(e, wv[jj][q], acc[q]);
+      for (int jj = 0; jj < kResBatch; ++jj) {
+        const float e = j0 + jj < (slice + 1) * kq ? sw1f[i][j0 + jj] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(e, wv[jj][q], acc[i][q]);
+      }
     }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) sbias[slice][4 * quad + q] = acc[q];
+  for (int i = 0; i < kResGroup; ++i) {
+    if (i >= rg.n) break;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sbias[i][slice][4 * quad + q] = acc[i][q];
+  }
   __syncthreads();
   const int v = chunk * kResCols + threadIdx.x;
-  double res = 0.0;
-  if (v < a.V) {
-    const float bias = (sbias[0][threadIdx.x] + sbias[1][threadIdx.x]) + (sbias[2][threadIdx.x] + sbias[3][threadIdx.x]);
+#pragma unroll
+  for (int i = 0; i < kResGroup; ++i) {
+    res[i] = 0.0;
+    if (i >= rg.n || v >= a.V) continue;
+    const int b = rg.b[i];
+    const FallbackInfo& f = rg.f[i];
+    const float bias = (sbias[i][0][threadIdx.x] + sbias[i][1][threadIdx.x]) +
+                       (sbias[i][2][threadIdx.x] + sbias[i][3][threadIdx.x]);
     const float t = a.target[((size_t)b * (g + 1) + (f.j - 1)) * (size_t)a.V + v];
     const float uu = a.U[((size_t)b * g + (f.j - 1)) * (size_t)a.V + v];
     const double pt = t == -__builtin_inff() ? 0.0 : exp2((double)(t - (float)f.M) * cf) / f.Z;
     const double pd = uu == -__builtin_inff() ? 0.0 : f.pdx * exp(((double)uu + (double)bias - f.lx) * a.inv_t_d);
-    res = fmax(0.0, pt - pd);
+    res[i] = fmax(0.0, pt - pd);
   }
   __syncthreads();
-  return res;
 }
 
+// Items are (chunk, group of kResGroup fallback requests), numbered so that
+// every group of one chunk has the same index mod 8: with a grid that is a
+// multiple of 8 they run on one XCD (workgroups are dealt to the XCDs round
+// robin), whose L2 then holds that chunk's W2 columns for all of them.
 template <bool kBf16>
 __global__ __launch_bounds__(kVThreads) void residual_stats_kernel(VerifyArgs a, VerifyWs w, float cf_f, int ntr) {
-  __shared__ float sw1f[512];
-  __shared__ float sbias[4][kResCols];
+  __shared__ float sw1f[kResGroup][512];
+  __shared__ float sbias[kResGroup][4][kResCols];
   __shared__ double sred[kVThreads / kWave];
   const int count = w.counts[0];
-  const long long items = (long long)count * ntr;
+  const int ngroups = (count + kResGroup - 1) / kResGroup;
+  const long long items = 8LL * ((ntr + 7) / 8) * ngroups;
   for (long long it = blockIdx.x; it < items; it += gridDim.x) {
-    const int li = (int)(it / ntr);
-    const int chunk = (int)(it - (long long)li * ntr);
-    const int b = w.fb_list[li];
-    const FallbackInfo f = w.fb[b];
-    for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1f[j] = (float)opnd_val<kBf16>(a, b, f.j, f.prev, j);
-    __syncthreads();
-    const double res = residual_term<kBf16>(a, f, b, chunk, sw1f, sbias, (double)cf_f);
-    const double s = block_sum<kVThreads, double>(res, sred);
-    if (threadIdx.x == 0) w.fb_part[(size_t)b * ntr + chunk] = s;
+    const long long y = it >> 3;
+    const int chunk = (int)(y / ngroups) * 8 + (int)(it & 7);
+    const int grp = (int)(y % ngroups);
+    if (chunk >= ntr) continue;
+    ResGroup rg;
+    rg.n = min(kResGroup, count - grp * kResGroup);
+    for (int i = 0; i < rg.n; ++i) {
+      rg.b[i] = w.fb_list[grp * kResGroup + i];
+      rg.f[i] = w.fb[rg.b[i]];
+    }
+    residual_rows<kBf16>(a, rg, sw1f);
+    double res[kResGroup];
+    residual_terms<kBf16>(a, rg, chunk, sw1f, sbias, (double)cf_f, res);
+    for (int i = 0; i < rg.n; ++i) {
+      const double s = block_sum<kVThreads, double>(res[i], sred);
+      if (threadIdx.x == 0) w.fb_part[(size_t)rg.b[i] * ntr + chunk] = s;
+    }
   }
 }
 
@@ -1136,8 +1187,8 @@ __global__ __launch_bounds__(kVThreads) void residual_select_kernel(VerifyArgs a
                                                                    int ntr) {
   __shared__ PickScratch ps;
   __shared__ double sterm[kTgtCols];
-  __shared__ float sw1f[512];
-  __shared__ float sbias[4][kResCols];
+  __shared__ float sw1f[kResGroup][512];
+  __shared__ float sbias[kResGroup][4][kResCols];
   const int count = w.counts[0];
   const int g = a.gamma;
   for (int li = blockIdx.x; li < count; li += gridDim.x) {
@@ -1150,10 +1201,15 @@ __global__ __launch_bounds__(kVThreads) void residual_select_kernel(VerifyArgs a
     const int ts = block_pick_uniform<kVThreads>(ntr, chunk_mass, u, ps, &base, &total);
     int y;
     if (total > 0.0 && ts >= 0) {
-      for (int j = threadIdx.x; j < a.r; j += kVThreads) sw1f[j] = (float)opnd_val<kBf16>(a, b, f.j, f.prev, j);
-      __syncthreads();
-      const double res = residual_term<kBf16>(a, f, b, ts, sw1f, sbias, (double)cf_f);
-      sterm[threadIdx.x] = res;
+      // the chosen chunk's terms again, by the same function as the masses
+      ResGroup rg;
+      rg.n = 1;
+      rg.b[0] = b;
+      rg.f[0] = f;
+      residual_rows<kBf16>(a, rg, sw1f);
+      double res[kResGroup];
+      residual_terms<kBf16>(a, rg, ts, sw1f, sbias, (double)cf_f, res);
+      sterm[threadIdx.x] = res[0];
       __syncthreads();
       auto col_weight = [&](int j) -> double { return sterm[j]; };
       int col = block_pick_target<kVThreads>(kResCols, col_weight, u * total - base, ps, nullptr);
