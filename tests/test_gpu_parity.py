@@ -8,6 +8,7 @@ requests, which the oracle computes one by one, in the launch configuration
 the benchmark times.
 """
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -382,6 +383,62 @@ def test_exact_residual_fallback_rows():
     rejected = int((alen.cpu().numpy() < gamma).sum())
     say("[fallback] %d requests equal, %d exempt, %d rejected" % (nv, exv, rejected))
     assert rejected >= 20
+
+
+@pytest.mark.slow
+def test_exact_residual_fallback_bf16_many_chunks():
+    """The exact-residual fallback with bf16 weights at r = 256 over 33
+    residual chunks of 256 columns (the last one 8 columns wide), for many
+    fallback requests at once: target rows within N(0, 0.02^2) of the oracle's
+    draft logits leave a residual mass of about 1 % at each rejection, so
+    about half of the rejecting requests miss all 64 proposals and the
+    masses run for several groups of fallback requests, the last one
+    partial.  Every request is compared, with and without W2T."""
+    B, V, gamma, sigma = 512, 8200, 7, 0.02
+    wl = workloads.make("v151936_b256_t07", B=B, V=V)
+    T = wl.T
+    say("[fallback bf16] B=%d V=%d r=%d gamma=%d T=%g sigma=%g" % (B, V, wl.r, gamma, T, sigma))
+    d = Dev(wl)
+    tok, prob, lse = dsp.markov_draft(d.U, d.W1, d.W2, d.x0, T, d.seeds, wl.rnd)
+    tok_h = tok.cpu().numpy()
+    W1f, W2f = f64_weights(wl)
+    with OraclePool(wl) as pool:
+        ref = pool.draft(range(B))
+    n, ex, whole = compare_draft(ref, tok_h, prob.cpu().numpy(), lse.cpu().numpy(), range(B), T)
+    say("[fallback bf16] draft: %d positions equal, %d exempt" % (n, ex))
+    assert ex <= 1 and len(whole) >= B - 1
+    # target rows: the oracle's draft logits along its own drafted prefix,
+    # plus small noise; the bonus row stays the workload's
+    prefix = np.concatenate([wl.x0[:, None].astype(np.int64), ref["tokens"][:, :-1].astype(np.int64)], axis=1)
+    base = wl.U.astype(np.float64) + (W1f[prefix.reshape(-1)] @ W2f).reshape(B, gamma, V)
+    rng = np.random.default_rng(23)
+    tgt = wl.tgt.copy()
+    tgt[:, :gamma] = (base + rng.normal(0.0, sigma, base.shape)).astype(np.float32)
+    wl2 = dataclasses.replace(wl, tgt=tgt)
+    dtgt = torch.from_numpy(tgt).cuda()
+    outs = [dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, dtgt, T, d.seeds, wl.rnd),
+            dsp.verify(d.U, d.W1, d.W2, d.x0, tok, prob, dtgt, T, d.seeds, wl.rnd, W2T=dsp.transpose_w2(d.W2))]
+    torch.cuda.synchronize()
+    reqs = sorted(whole)
+    with OraclePool(wl2) as pool:
+        vref = pool.verify(reqs, tok_h)
+    for i, (alen, otok, aprob) in enumerate(outs):
+        nv, exv = compare_verify(vref, alen.cpu().numpy(), otok.cpu().numpy(), aprob.cpu().numpy(), reqs, T)
+        say("[fallback bf16] verify%s: %d requests equal, %d exempt" % (" with W2T" if i else "", nv, exv))
+        assert exv <= 1 and nv >= len(reqs) - 1
+    # the expected number of requests that reached the exact residual:
+    # (1 - residual mass)^64 summed over the oracle's rejections
+    expect, rejected = 0.0, 0
+    for b in reqs:
+        j = int(vref["accept_len"][b])
+        if j >= gamma:
+            continue
+        rejected += 1
+        pd, _ = oracle.softmax(base[b, j] / T)
+        pt, _ = oracle.softmax(tgt[b, j].astype(np.float64) / T)
+        expect += (1.0 - float(np.maximum(pt - pd, 0.0).sum())) ** 64
+    say("[fallback bf16] %d rejecting requests, %.1f expected to take the exact residual" % (rejected, expect))
+    assert expect >= 8.0
 
 
 @pytest.mark.parametrize("name,kw", [("v151936_b32", dict(B=21, V=5003, gamma=4, r=64)),
