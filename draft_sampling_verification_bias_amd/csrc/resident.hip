@@ -81,6 +81,8 @@ constexpr int kResMaxNW = kResWaves * kResMaxWg;    // range summaries per row (
 constexpr int kResSumPerLane = kResMaxNW / kWave;   // 32
 constexpr int kResWgSub = kResWaves * kResSub;      // sub-block sums per row per workgroup (slots)
 constexpr int kResErr = kResMaxWg;                  // index of the error word among the flags
+constexpr int kResEagerG0 = 4;                      // tile: halves announced at once up to this many groups
+constexpr int kResSelSteps = 4;                     // tile: a half's selections, in tile steps (about)
 
 static_assert(kResLdsE + kResESlots * kResEBytes <= kResLdsCtlU, "tile LDS");
 static_assert(kResLdsSelE + kResWaves * kResSelReq * 512 <= kResLdsMisc, "selector LDS");
@@ -554,9 +556,14 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
     if (k == 1) return -1;
     return (k - 2) * G + (half_of(g) == 0 ? G0 - 1 : G - 1);
   };
-  // E(t) is issued at step t - 2 if the half it depends on ended before that
-  // step (or it depends on none), else at step t itself
-  auto e_early = [&](int t) { return pos_of(t) == 1 || dep_of(t) <= t - 3; };
+  // E(t) is issued at step t - 2 (or depends on no selection) if the
+  // selections it depends on are expected to be finished by then: announced
+  // one step (short halves) or two steps after the half's last step, they
+  // take about kResSelSteps steps.  Otherwise it is issued at step t itself,
+  // which exposes one E load instead of stalling the workgroup two steps
+  // early.
+  const int e_lead = 2 + (G0 <= kResEagerG0 ? 1 : 2) + kResSelSteps;
+  auto e_early = [&](int t) { return pos_of(t) == 1 || dep_of(t) <= t - e_lead; };
   auto half_end = [&](int t) { const int g = grp_of(t); return g == G0 - 1 || g == G - 1; };
   // the flag phase of the half that ends at step t
   auto end_phase = [&](int t) { return res_phase(pos_of(t), grp_of(t) == G - 1 ? 1 : 0); };
@@ -631,6 +638,14 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
 
   for (int t = 0; t < T; ++t) {
     const int k = pos_of(t), g = grp_of(t);
+    // Halves of at most kResEagerG0 groups are announced right after their
+    // last step (a full drain, then the release) rather than two steps
+    // later: their selections, not the tile steps, set the pace there.
+    if (G0 <= kResEagerG0 && t >= 1 && half_end(t - 1) && released < end_phase(t - 1)) {
+      res_wait_vmem<0>();
+      __syncthreads();
+      release(end_phase(t - 1));
+    }
     // E(t) and the U blocks of step t this wave issued have landed.  Issue
     // order per step: e E DMAs at its start (E(t + 2), real or not), u U DMAs
     // (U of step t + 3, real or not) and summary stores (at least one), with
@@ -789,7 +804,9 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
 // ---------------------------------------------------------------------------
 // Selector wave sw (of kResSelWaves) owns, in half h, the requests
 // R_h + sw + i kResSelWaves (i = 0, 1) below R_{h + 1}, with R_0 = 0,
-// R_1 = min(B, 16 G0), R_2 = B.
+// R_1 = min(B, 16 G0), R_2 = B; when both halves hold at most
+// kResSelWaves / 2 requests, the one request R_h + sw - h kResSelWaves / 2
+// instead (waves of the other half own none).
 template <bool kGreedy>
 __device__ void res_selector(const ResArgs& a, unsigned char* smem) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -802,8 +819,20 @@ __device__ void res_selector(const ResArgs& a, unsigned char* smem) {
   uint32_t* err = a.flags + kResErr;
   uint32_t* my_flag = a.flags + a.nt + (blockIdx.x - a.nt);
   const int R1 = a.B < kResRows * a.G0 ? a.B : kResRows * a.G0;
-  auto req = [&](int h, int i) { return (h == 0 ? 0 : R1) + sw + i * kResSelWaves; };
-  auto live = [&](int h, int i) { return req(h, i) < (h == 0 ? R1 : a.B); };
+  // Halves of at most kResSelWaves / 2 requests each (B <= 128) go to
+  // disjoint waves, one request per wave: the selections of one half then
+  // never queue behind those of the other, which matters when a half is only
+  // a step or two of tile work.  Larger halves use every wave, up to two
+  // requests per wave.
+  constexpr int kHalfWaves = kResSelWaves / 2;
+  const bool split = R1 <= kHalfWaves && a.B - R1 <= kHalfWaves;
+  auto req = [&](int h, int i) {
+    return split ? (h == 0 ? 0 : R1) + sw - h * kHalfWaves : (h == 0 ? 0 : R1) + sw + i * kResSelWaves;
+  };
+  auto live = [&](int h, int i) {
+    if (split && (i != 0 || sw < h * kHalfWaves)) return false;
+    return req(h, i) < (h == 0 ? R1 : a.B);
+  };
   auto erow = [&](int h, int i) { return smem + kResLdsSelE + (wave * kResSelReq + 2 * h + i) * 512; };
 
   // E rows of position 1: W1[x_0] (zero rows for invalid anchors)

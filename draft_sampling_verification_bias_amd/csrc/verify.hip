@@ -1322,7 +1322,9 @@ hipError_t launch_verify(const VerifyArgs& a_in, bool bf16, hipStream_t s) {
   }
   if (!greedy) {
     const int ntr = tiles_of(a.V, kResCols);
-    const long long items = (long long)a.B * ntr;
+    // the most items the fallback can have (every request falling back): a
+    // multiple of 8, as the grid then is
+    const long long items = 8LL * ((ntr + 7) / 8) * ((a.B + kResGroup - 1) / kResGroup);
     const int sgrid = (int)(items < 1024 ? items : 1024);
     {
       ProfScope prof(s, kProfResidualStats);
