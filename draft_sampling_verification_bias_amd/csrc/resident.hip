@@ -70,7 +70,12 @@ constexpr int kResSelReq = 4;                       // selector: requests per wa
 constexpr int kResLdsSelE = kResWaves * kResSelStage;  // selector: then their E rows
 constexpr int kResLdsCtlU = 144 * 1024;              // tile: the fourth U stage of the control wave
 constexpr int kResLdsMisc = kResLdsCtlU + kResStageBytes;  // the ok word
-constexpr int kResLds = kResLdsMisc + 64;
+// tile: the workgroup's summaries of one step, two buffers: range summaries
+// [16 rows][8 waves] float2, then sub-block sums [16 rows][kResWgSub] float
+constexpr int kResPartBytes = kResRows * kResWaves * 8;
+constexpr int kResSsumBytes = kResRows * kResWaves * kResSub * 4;
+constexpr int kResLdsSum = kResLdsMisc + 64;
+constexpr int kResLds = kResLdsSum + 2 * (kResPartBytes + kResSsumBytes);
 constexpr int kResCtl = kResWaves - 1;              // tile: the control wave (no DMAs of its own)
 constexpr int kResEHelper = kResSub;                // tile: issues the control wave's E chunk
 static_assert(kResSub < kResCtl && kResEHelper < kResCtl, "helpers of the control wave");
@@ -543,6 +548,14 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   volatile int* ok_flag = reinterpret_cast<volatile int*>(smem + kResLdsMisc);
   uint32_t* err = a.flags + kResErr;
   const uint32_t* sel_flags = a.flags + nt;
+  // the summaries of step t: written to LDS by every wave, copied to the
+  // global arrays by the control wave at the next step (whole 512-byte runs
+  // per store instruction, the other waves' vector-memory queues holding
+  // only their DMAs)
+  auto spart = [&](int t) { return reinterpret_cast<float2*>(smem + kResLdsSum + (t & 1) * kResPartBytes); };
+  auto sssum = [&](int t) {
+    return reinterpret_cast<float*>(smem + kResLdsSum + 2 * kResPartBytes + (t & 1) * kResSsumBytes);
+  };
   const int G = a.G, G0 = a.G0, T = a.gamma * G;
   const int n16 = lane & 15, q4 = lane >> 4;
 
@@ -574,20 +587,38 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
     released = phase;
     if (ctl && lane == 0) res_arrive(a.flags + wg, phase);
   };
-  // The control wave waits for the E rows of step t (before the workgroup
-  // barrier that follows; the ok word reports a failed wait).  The selectors
-  // need this workgroup's announcement of the half that those rows depend
-  // on: when the lazy announcement (two steps after the half's end, below)
-  // has not been made yet, everything is drained and it is made now.
-  auto check = [&](int t, int now) {
+  // The control wave copies step tc's summaries to the global arrays.  The
+  // copies are the only vector-memory operations of the control wave apart
+  // from its polls (which it waits for itself), so its vmcnt counts them.
+  constexpr int kFlushOps = kGreedy ? 2 : 2 + kResSsumBytes / 512;
+  auto flush = [&](int tc) {
+    if (!ctl) return;
+    const size_t blk = (size_t)grp_of(tc) * nt + wg;
+    const uint2* sp = reinterpret_cast<const uint2*>(spart(tc));
+    uint2* gp = reinterpret_cast<uint2*>(a.part) + blk * (kResPartBytes / 8);
+#pragma unroll
+    for (int i = 0; i < kResPartBytes / 512; ++i) res_put(gp + 64 * i + lane, sp[64 * i + lane]);
+    if constexpr (!kGreedy) {
+      const uint2* ss = reinterpret_cast<const uint2*>(sssum(tc));
+      uint2* gs = reinterpret_cast<uint2*>(a.ssum) + blk * (kResSsumBytes / 8);
+#pragma unroll
+      for (int i = 0; i < kResSsumBytes / 512; ++i) res_put(gs + 64 * i + lane, ss[64 * i + lane]);
+    }
+  };
+  // The control wave waits for the E rows of step t (the ok word reports a
+  // failed wait; true if it polled).  The selectors need this workgroup's
+  // announcement of the half that those rows depend on: when the lazy
+  // announcement (below) has not been made yet, it is made now, once the
+  // control wave's copies (every step up to now - 1 has been copied) are
+  // complete.
+  auto check = [&](int t, int now) -> bool {
     const uint32_t need = res_phase(pos_of(t), half_of(grp_of(t)));
-    if (need <= confirmed) return;
+    if (need <= confirmed) return false;
     confirmed = need;
     // this workgroup's phase for that half of the previous position (none
     // at position 1, whose E rows the selectors write before any step)
     if (need > 2 && released < need - 2) {
-      res_wait_vmem<0>();
-      __syncthreads();
+      if (ctl) res_wait_vmem<0>();
       int last = now - 1;
       while (last > 0 && !half_end(last)) --last;
       release(end_phase(last));
@@ -596,6 +627,7 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
       const bool ok = res_wait_flags(sel_flags, kResSelWg, need, err, a.timeout);
       if (lane == 0) *ok_flag = ok ? 1 : 0;
     }
+    return true;
   };
   auto e_slot = [&](int t) -> uint32_t { return ebufs_l + (uint32_t)((t % kResESlots) * kResEBytes); };
   auto issue_e = [&](int t, bool real) {
@@ -637,35 +669,19 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   issue_e(1, T > 1 && e_early(1));
 
   for (int t = 0; t < T; ++t) {
-    const int k = pos_of(t), g = grp_of(t);
-    // Halves of at most kResEagerG0 groups are announced right after their
-    // last step (a full drain, then the release) rather than two steps
-    // later: their selections, not the tile steps, set the pace there.
-    if (G0 <= kResEagerG0 && t >= 1 && half_end(t - 1) && released < end_phase(t - 1)) {
-      res_wait_vmem<0>();
-      __syncthreads();
-      release(end_phase(t - 1));
-    }
     // E(t) and the U blocks of step t this wave issued have landed.  Issue
-    // order per step: e E DMAs at its start (E(t + 2), real or not), u U DMAs
-    // (U of step t + 3, real or not) and summary stores (at least one), with
-    // (e, u) = (1, 6) for waves 0-4, (2, 5) for wave 5, (1, 5) for wave 6 and
-    // (0, 0) for the control wave; so after E(t) come e at t = 0, e + u at
-    // t = 1 and 2 u + e at t >= 2.  U(t) is issued before E(t).
-    // Two steps after the end of a half, the summary stores of its last step
-    // must have completed too: only e + u ops (one store for the control
-    // wave) are known to follow them, so those steps wait for that many.  An
-    // E issued late (at its own step) is waited for there, and drains only
-    // make these counts safer.  The control wave issues no loads and
-    // otherwise waits for nothing.
+    // order per step: e E DMAs at its start (E(t + 2), real or not), then u
+    // U DMAs (U of step t + 3, real or not), with (e, u) = (1, 6) for waves
+    // 0-4, (2, 5) for wave 5 and (1, 5) for wave 6; so after E(t) come e at
+    // t = 0, e + u at t = 1 and 2 u + e at t >= 2.  U(t) is issued before
+    // E(t).  An E issued late (at its own step) is waited for there, and
+    // drains only make these counts safer.  The control wave issues no DMAs.
     __builtin_amdgcn_sched_barrier(0);
-    const bool rel = t >= 2 && half_end(t - 2);
     if (ctl) {
-      if (rel) res_wait_vmem<1>();
     } else if (wave < kResSub) {
       if (t == 0) {
         res_wait_vmem<1>();
-      } else if (t == 1 || rel) {
+      } else if (t == 1) {
         res_wait_vmem<kResSub + 2>();
       } else {
         res_wait_vmem<2 * kResSub + 3>();
@@ -673,7 +689,7 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
     } else if (wave == kResEHelper) {
       if (t == 0) {
         res_wait_vmem<2>();
-      } else if (t == 1 || rel) {
+      } else if (t == 1) {
         res_wait_vmem<kResSub + 2>();
       } else {
         res_wait_vmem<2 * kResSub + 2>();
@@ -681,26 +697,42 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
     } else {
       if (t == 0) {
         res_wait_vmem<1>();
-      } else if (t == 1 || rel) {
+      } else if (t == 1) {
         res_wait_vmem<kResSub + 1>();
       } else {
         res_wait_vmem<2 * kResSub + 1>();
       }
     }
-    const bool late = !e_early(t);
-    if (late) check(t, t);
-    if (t + 2 < T && e_early(t + 2)) check(t + 2, t);
+    // every wave's summaries of step t - 1 are in LDS
     __syncthreads();
-    if (!*ok_flag) {
-      res_wait_vmem<0>();
-      return;
+    if (t >= 1) flush(t - 1);
+    // Announcements, once the control wave's copies of the half's last step
+    // are complete: halves of at most kResEagerG0 groups right away (their
+    // selections, not the tile steps, set the pace there), others one step
+    // later, when only the copies of the step after are still in flight.
+    if (G0 <= kResEagerG0) {
+      if (t >= 1 && half_end(t - 1) && released < end_phase(t - 1)) {
+        if (ctl) res_wait_vmem<0>();
+        release(end_phase(t - 1));
+      }
+    } else if (t >= 2 && half_end(t - 2) && released < end_phase(t - 2)) {
+      if (ctl) res_wait_vmem<kFlushOps>();
+      release(end_phase(t - 2));
     }
-    // the half that ended two steps ago: every wave's summary stores of it
-    // are complete (the waits above) and all waves have passed the barrier
-    if (rel) release(end_phase(t - 2));
+    const bool late = !e_early(t);
+    bool polled = false;
+    if (late) polled = check(t, t);
+    if (t + 2 < T && e_early(t + 2)) polled = check(t + 2, t) || polled;
+    if (polled) {
+      __syncthreads();
+      if (!*ok_flag) {
+        res_wait_vmem<0>();
+        return;
+      }
+    }
     if (late) {
       issue_e(t, true);
-      res_wait_vmem<0>();
+      if (!ctl) res_wait_vmem<0>();
       __syncthreads();
     }
     issue_e(t + 2, t + 2 < T && e_early(t + 2));
@@ -749,9 +781,6 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
       // control wave's stage of step t - 1)
       issue_u(t + kResStages, lds + (uint32_t)stage_off(wave, t % nstage));
     }
-    const int row = kResRows * g + n16;
-    const bool rowok = row < a.B;
-    const uint32_t pidx = (((uint32_t)g * (uint32_t)nt + (uint32_t)wg) * 16u + (uint32_t)n16) * 8u + (uint32_t)wave;
     if constexpr (kGreedy) {
       float bv = -__builtin_inff();
       int bc = 0x7fffffff;
@@ -768,7 +797,7 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
       }
       res_argmax_rows(bv, bc);
       if (my.n == 0) bv = -__builtin_inff(), bc = 0x7fffffff;
-      if (lane < 16 && rowok) res_put(a.part + pidx, make_float2(bv, __int_as_float(bc)));
+      if (lane < 16) spart(t)[n16 * kResWaves + wave] = make_float2(bv, __int_as_float(bc));
     } else {
       float m = -__builtin_inff();
 #pragma unroll
@@ -784,18 +813,18 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
         bp[s] = res_sum_rows(s < my.n ? v : 0.0f);
       }
       const float S = (((bp[0] + bp[1]) + bp[2]) + bp[3]) + bp[4];
-      if (lane < 16 && rowok) res_put(a.part + pidx, make_float2(my.n > 0 ? m : -__builtin_inff(), S));
+      if (lane < 16) spart(t)[n16 * kResWaves + wave] = make_float2(my.n > 0 ? m : -__builtin_inff(), S);
       const float bq = q4 == 0 ? bp[0] : q4 == 1 ? bp[1] : q4 == 2 ? bp[2] : bp[3];
-      const uint32_t so =
-          (((uint32_t)g * (uint32_t)nt + (uint32_t)wg) * 16u + (uint32_t)n16) * kResWgSub + (uint32_t)myloc;
-      if (rowok && q4 < my.n) res_put(a.ssum + so + (uint32_t)q4, bq);
-      if (rowok && q4 == 0 && my.n > 4) res_put(a.ssum + so + 4u, bp[4]);
+      float* ss = sssum(t) + n16 * kResWgSub + myloc;
+      if (q4 < my.n) ss[q4] = bq;
+      if (q4 == 0 && my.n > 4) ss[4] = bp[4];
     }
 
   }
-  // the halves not announced yet
-  res_wait_vmem<0>();
+  // the last step's summaries, then the halves not announced yet
   __syncthreads();
+  flush(T - 1);
+  res_wait_vmem<0>();
   release(res_phase(a.gamma, 1));
 }
 
