@@ -12,9 +12,15 @@ target's forward pass does between rounds) and is timed alone with HIP events
 on the launch stream; the value is the median step, with p10 and p90 beside
 it and the back-to-back warm-cache rate as an extra field.
 
+The draft is the device-resident one (all positions in one launch, from the
+vocabulary-major copy of W2 prepared once outside the timed region) wherever
+the library can run it, else one tile pass and one selection per position;
+--per-position forces the latter.
+
 Printed (one JSON line): the metric, the fraction of the 8 TB/s HBM peak that
 the step's compulsory bytes reach, the roofline of the dominant kernel (the
-draft tile pass, timed live with HIP events on its own stream), the analytical
+resident draft, or the per-position draft's tile pass, timed live with HIP
+events on its own stream), the analytical
 dspark_survival time and the scheduled round (confidence head, prefix
 scheduler, verification at its lengths; both reported beside the gated
 path), the RNN-head draft at the same sizes beside the Markov draft, and the
@@ -176,9 +182,9 @@ def main():
                     help="timed calls of the prefix scheduler and of verification with its lengths (0: skip)")
     ap.add_argument("--rnn-steps", type=int, default=10,
                     help="timed calls of the RNN-head draft beside the Markov draft (0: skip)")
-    ap.add_argument("--resident", action="store_true",
-                    help="draft with the W2T copy: all positions in one device-resident launch "
-                         "(default: one tile pass and one selection launch per position)")
+    ap.add_argument("--per-position", action="store_true",
+                    help="draft with one tile pass and one selection launch per position (default: all "
+                         "positions in one device-resident launch from the W2T copy, where it applies)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="copy this many MiB device to device once before timing (a reference kernel of known "
                          "traffic for hardware counter runs)")
@@ -219,7 +225,7 @@ def main():
     W2T = dsp.transpose_w2(W2) if T > 0 else None
     # the draft uses the copy at every temperature (it holds W2 on chip from it)
     W2T_d = dsp.transpose_w2(W2) if (W2T is None and wl.wdtype == "bf16") else W2T
-    if not args.resident:
+    if args.per_position:
         W2T_d = None
 
     ws_d = torch.empty(dsp.workspace_size(dsp.OP_DRAFT, B, gamma, V, r), dtype=torch.uint8, device=dev)
@@ -475,7 +481,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "V": V, "r": r, "gamma": gamma, "T": T,
-                   "weights": wl.wdtype, "logits": "f32"},
+                   "weights": wl.wdtype, "logits": "f32",
+                   "draft": "device-resident" if "draft_resident" in prof else "per-position"},
         "hbm_fraction": hbm_frac,
         "bytes_per_step": mean_bytes,
         "mfma_fraction": flops / (med * 1e-3) / MFMA_BF16_PEAK,

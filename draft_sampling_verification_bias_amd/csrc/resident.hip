@@ -86,7 +86,6 @@ constexpr int kResMaxNW = kResWaves * kResMaxWg;    // range summaries per row (
 constexpr int kResSumPerLane = kResMaxNW / kWave;   // 32
 constexpr int kResWgSub = kResWaves * kResSub;      // sub-block sums per row per workgroup (slots)
 constexpr int kResErr = kResMaxWg;                  // index of the error word among the flags
-constexpr int kResEagerG0 = 4;                      // tile: halves announced at once up to this many groups
 constexpr int kResSelSteps = 4;                     // tile: a half's selections, in tile steps (about)
 
 static_assert(kResLdsE + kResESlots * kResEBytes <= kResLdsCtlU, "tile LDS");
@@ -571,11 +570,10 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   };
   // E(t) is issued at step t - 2 (or depends on no selection) if the
   // selections it depends on are expected to be finished by then: announced
-  // one step (short halves) or two steps after the half's last step, they
-  // take about kResSelSteps steps.  Otherwise it is issued at step t itself,
-  // which exposes one E load instead of stalling the workgroup two steps
-  // early.
-  const int e_lead = 2 + (G0 <= kResEagerG0 ? 1 : 2) + kResSelSteps;
+  // at the step after the half's last step, they take about kResSelSteps
+  // steps.  Otherwise it is issued at step t itself, which exposes one E
+  // load instead of stalling the workgroup two steps early.
+  const int e_lead = 3 + kResSelSteps;
   auto e_early = [&](int t) { return pos_of(t) == 1 || dep_of(t) <= t - e_lead; };
   auto half_end = [&](int t) { const int g = grp_of(t); return g == G0 - 1 || g == G - 1; };
   // the flag phase of the half that ends at step t
@@ -590,7 +588,6 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   // The control wave copies step tc's summaries to the global arrays.  The
   // copies are the only vector-memory operations of the control wave apart
   // from its polls (which it waits for itself), so its vmcnt counts them.
-  constexpr int kFlushOps = kGreedy ? 2 : 2 + kResSsumBytes / 512;
   auto flush = [&](int tc) {
     if (!ctl) return;
     const size_t blk = (size_t)grp_of(tc) * nt + wg;
@@ -607,10 +604,9 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   };
   // The control wave waits for the E rows of step t (the ok word reports a
   // failed wait; true if it polled).  The selectors need this workgroup's
-  // announcement of the half that those rows depend on: when the lazy
-  // announcement (below) has not been made yet, it is made now, once the
-  // control wave's copies (every step up to now - 1 has been copied) are
-  // complete.
+  // announcement of the half that those rows depend on, which the top of
+  // each step makes as soon as the half's copies are complete; should it be
+  // missing, it is made here (every step up to now - 1 has been copied).
   auto check = [&](int t, int now) -> bool {
     const uint32_t need = res_phase(pos_of(t), half_of(grp_of(t)));
     if (need <= confirmed) return false;
@@ -706,18 +702,13 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
     // every wave's summaries of step t - 1 are in LDS
     __syncthreads();
     if (t >= 1) flush(t - 1);
-    // Announcements, once the control wave's copies of the half's last step
-    // are complete: halves of at most kResEagerG0 groups right away (their
-    // selections, not the tile steps, set the pace there), others one step
-    // later, when only the copies of the step after are still in flight.
-    if (G0 <= kResEagerG0) {
-      if (t >= 1 && half_end(t - 1) && released < end_phase(t - 1)) {
-        if (ctl) res_wait_vmem<0>();
-        release(end_phase(t - 1));
-      }
-    } else if (t >= 2 && half_end(t - 2) && released < end_phase(t - 2)) {
-      if (ctl) res_wait_vmem<kFlushOps>();
-      release(end_phase(t - 2));
+    // A half is announced as soon as the control wave's copies of its last
+    // step are complete (the control wave waits for them here; the other
+    // waves meet it at the next barrier), so that its selections start one
+    // step after its last tile step.
+    if (t >= 1 && half_end(t - 1) && released < end_phase(t - 1)) {
+      if (ctl) res_wait_vmem<0>();
+      release(end_phase(t - 1));
     }
     const bool late = !e_early(t);
     bool polled = false;
