@@ -242,6 +242,8 @@ class ProfScope {
  public:
   ProfScope(hipStream_t s, int kind);
   ~ProfScope();
+  // the bracketed launch did not happen: the record is kept out of the sums
+  void discard();
   ProfScope(const ProfScope&) = delete;
   ProfScope& operator=(const ProfScope&) = delete;
 

@@ -56,6 +56,12 @@ ProfScope::ProfScope(hipStream_t s, int kind) : stream_(s), index_(-1) {
   index_ = (int)g_records.size() - 1;
 }
 
+void ProfScope::discard() {
+  if (index_ < 0) return;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (index_ < (int)g_records.size()) g_records[index_].kind = -1;
+}
+
 ProfScope::~ProfScope() {
   if (index_ < 0) return;
   std::lock_guard<std::mutex> lock(g_mu);

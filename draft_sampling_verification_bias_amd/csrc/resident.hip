@@ -1012,22 +1012,23 @@ hipError_t launch_resident_draft(const DraftArgs& d, hipStream_t s, bool* launch
   a.eops = reinterpret_cast<uint16_t*>(ws + L.eops);
   a.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
   a.timeout = 20000000;  // 0.2 s at 100 MHz: orders of magnitude above a normal wait
+  hipLaunchKernelGGL(resident_clear_kernel, dim3(1), dim3(256), 0, s, a.flags, kResMaxWg + 1);
+  void* args[] = {&a};
   {
-    ProfScope prof(s, kProfResidentDraft);
-    hipLaunchKernelGGL(resident_clear_kernel, dim3(1), dim3(256), 0, s, a.flags, kResMaxWg + 1);
-    void* args[] = {&a};
+    ProfScope prof(s, kProfResidentDraft);  // the resident kernel alone
     e = hipLaunchCooperativeKernel(greedy ? (const void*)draft_resident_kernel<true>
                                           : (const void*)draft_resident_kernel<false>,
                                    dim3(nwg), dim3(kResThreads), args, kResLds, s);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      return hipSuccess;  // not launched: the caller falls back (the clear kernel is harmless)
-    }
-    *launched = true;
-    const int n = d.B * d.gamma;
-    hipLaunchKernelGGL(resident_fixup_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0,
-                       s, a.flags + kResErr, d.tokens, d.prob, d.lse, n);
+    if (e != hipSuccess) prof.discard();
   }
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hipSuccess;  // not launched: the caller falls back (the clear kernel is harmless)
+  }
+  *launched = true;
+  const int n = d.B * d.gamma;
+  hipLaunchKernelGGL(resident_fixup_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, s,
+                     a.flags + kResErr, d.tokens, d.prob, d.lse, n);
   return hipGetLastError();
 }
 
