@@ -22,11 +22,13 @@
 // for the wave's columns (exact bf16 products, fp32 accumulation); the
 // epilogue adds U and reduces each row of the wave's range to (max, sum of
 // 2^((l - max) log2(e) / T)) plus one partial sum per sub-block (argmax at
-// T = 0).  Per position the only HBM stream is U_k.
+// T = 0), written to LDS; at the next step the control wave (the one wave
+// that issues no DMAs) copies the workgroup's summaries of the step to the
+// global arrays.  Per position the only HBM stream is U_k.
 //
 // The rows are split into two halves (the first ceil(G / 2) groups and the
 // rest).  A tile workgroup announces each finished half of a position on its
-// flag; the selector workgroups wait for all tile workgroups on a half, pick
+// flag once the copies of the half's last step are complete; the selector workgroups wait for all tile workgroups on a half, pick
 // that half's tokens (one wave per request: float64 search over the row's
 // range summaries grouped by tile workgroup, then over the chosen
 // workgroup's eight ranges and the chosen range's sub-block sums, then a

@@ -65,6 +65,11 @@ SMALL = [
     ("greedy_v151936_b512", dict(B=24, V=16384, gamma=3)),
     ("greedy_v151936_b512", dict(B=300, V=8192, gamma=2)),
     ("v262144_b128", dict(B=33, V=65536, gamma=3, T=0.5)),
+    # halves of 64 and 36 requests on disjoint selector waves, E rows issued
+    # late and early over five positions
+    ("v151936_b256_t07", dict(B=100, V=24576, gamma=5)),
+    ("greedy_v151936_b512", dict(B=128, V=16384, gamma=4)),  # two halves of exactly 64
+    ("v151936_b32", dict(B=129, V=8192, gamma=3)),            # first half of 80: every wave on both halves
 ]
 
 
