@@ -833,7 +833,7 @@ template <bool kGreedy>
 __device__ void res_selector(const ResArgs& a, unsigned char* smem) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int sw = (blockIdx.x - a.nt) * kResWaves + wave;
+
   const uint32_t lds = res_lds_base(smem);
   unsigned char* stage = smem + wave * kResSelStage;
   const uint32_t stage_l = lds + (uint32_t)(wave * kResSelStage);
@@ -848,6 +848,13 @@ __device__ void res_selector(const ResArgs& a, unsigned char* smem) {
   // requests per wave.
   constexpr int kHalfWaves = kResSelWaves / 2;
   const bool split = R1 <= kHalfWaves && a.B - R1 <= kHalfWaves;
+  // Selector wave number: with split halves, wave-major, so that consecutive
+  // requests land on different workgroups (each selection DMAs 15 KB of
+  // summaries, and the selections of a short half are the critical path);
+  // otherwise workgroup-major, so that a workgroup's waves take neighbouring
+  // rows, whose summaries share cache lines.
+  const int wgi = (int)blockIdx.x - a.nt;
+  const int sw = split ? wave * kResSelWg + wgi : wgi * kResWaves + wave;
   auto req = [&](int h, int i) {
     return split ? (h == 0 ? 0 : R1) + sw - h * kHalfWaves : (h == 0 ? 0 : R1) + sw + i * kResSelWaves;
   };
