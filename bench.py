@@ -148,9 +148,24 @@ def step_bytes(B, gamma, V, r, accept_len):
     return 4 * B * gamma * V + 4 * V * int((n + 1).sum()) + 2 * r * V + 2 * r * (B * gamma + rej)
 
 
+def code_digest(path):
+    """sha256 of a kernel source's code: the text with // comments, trailing
+    blanks and empty lines removed, so that edits of comments alone keep it."""
+    lines = []
+    with open(path) as f:
+        for line in f:
+            i = line.find("//")
+            if i >= 0:
+                line = line[:i]
+            line = line.rstrip()
+            if line.strip():
+                lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def pmc_traffic(kname, workload):
     """HBM bytes per launch of a kernel from its committed counter summary, or
-    None if there is none for this workload or the kernel source changed since
+    None if there is none for this workload or the kernel's code changed since
     it was taken."""
     path = PMC_FILES.get(kname)
     if path is None or not os.path.exists(path):
@@ -159,8 +174,7 @@ def pmc_traffic(kname, workload):
         rec = json.load(f)
     if rec.get("workload") != workload:
         return None
-    src = hashlib.sha256(open(KERNEL_SRC[kname], "rb").read()).hexdigest()
-    if rec.get("source_sha256", rec.get("tile_pass_sha256")) != src:
+    if rec.get("code_sha256") != code_digest(KERNEL_SRC[kname]):
         return None
     return rec.get("bytes_per_launch")
 

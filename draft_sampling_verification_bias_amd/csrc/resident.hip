@@ -28,16 +28,16 @@
 //
 // The rows are split into two halves (the first ceil(G / 2) groups and the
 // rest).  A tile workgroup announces each finished half of a position on its
-// flag once the copies of the half's last step are complete; the selector workgroups wait for all tile workgroups on a half, pick
-// that half's tokens (one wave per request: float64 search over the row's
-// range summaries grouped by tile workgroup, then over the chosen
-// workgroup's eight ranges and the chosen range's sub-block sums, then a
-// rescan of one 16-column sub-block with W2T rows -- the stream-0 inverse
-// CDF) and
-// write W1[x_k] as the request's next E row, then announce the half on their
-// flags.  A tile workgroup checks those flags only before its first E DMA of
-// a half of the next position, so the selections of one half run while the
-// tiles stream the other half.
+// flag once the copies of the half's last step are complete; the selector
+// workgroups wait for all tile workgroups on a half, pick that half's tokens
+// (one wave per request: float64 search over the row's range summaries
+// grouped by tile workgroup, then over the chosen workgroup's eight ranges
+// and the chosen range's sub-block sums, then a rescan of one 16-column
+// sub-block with W2T rows -- the stream-0 inverse CDF) and write W1[x_k] as
+// the request's next E row, then announce the half on their flags.  A tile
+// workgroup checks those flags only before its first E DMA of a half of the
+// next position, so the selections of one half run while the tiles stream
+// the other half.
 //
 // Flags are words written with release semantics at agent scope and polled by
 // one wave with acquire semantics; every wait is bounded in time, and a wait
