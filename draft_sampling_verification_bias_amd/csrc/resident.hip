@@ -88,7 +88,7 @@ constexpr int kResMaxNW = kResWaves * kResMaxWg;    // range summaries per row (
 constexpr int kResSumPerLane = kResMaxNW / kWave;   // 32
 constexpr int kResWgSub = kResWaves * kResSub;      // sub-block sums per row per workgroup (slots)
 constexpr int kResErr = kResMaxWg;                  // index of the error word among the flags
-constexpr int kResSelSteps = 4;                     // tile: a half's selections, in tile steps (about)
+constexpr int kResSelSteps = 7;                     // tile: a half's selections, in tile steps (measured best)
 
 static_assert(kResLdsE + kResESlots * kResEBytes <= kResLdsCtlU, "tile LDS");
 static_assert(kResLdsSelE + kResWaves * kResSelReq * 512 <= kResLdsMisc, "selector LDS");
@@ -572,9 +572,10 @@ __device__ void res_tile(const ResArgs& a, unsigned char* smem) {
   };
   // E(t) is issued at step t - 2 (or depends on no selection) if the
   // selections it depends on are expected to be finished by then: announced
-  // at the step after the half's last step, they take about kResSelSteps
-  // steps.  Otherwise it is issued at step t itself, which exposes one E
-  // load instead of stalling the workgroup two steps early.
+  // at the step after the half's last step, they take up to kResSelSteps
+  // steps (the lead that measured fastest from B = 32 to 256).  Otherwise it
+  // is issued at step t itself, which exposes one E load instead of stalling
+  // the workgroup two steps early.
   const int e_lead = 3 + kResSelSteps;
   auto e_early = [&](int t) { return pos_of(t) == 1 || dep_of(t) <= t - e_lead; };
   auto half_end = [&](int t) { const int g = grp_of(t); return g == G0 - 1 || g == G - 1; };
