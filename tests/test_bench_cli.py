@@ -15,3 +15,18 @@ def test_bench_refuses_more_than_one_gpu():
     assert res.returncode == 2
     assert "one GPU" in res.stderr
     assert res.stdout.strip() == ""
+
+
+def test_counter_records_follow_the_kernel_code_not_its_comments(tmp_path):
+    """bench.py keeps a kernel's committed counter figures while only its
+    comments change, and drops them once its code changes."""
+    sys.path.insert(0, ROOT)
+    import bench
+    a = tmp_path / "a.hip"
+    a.write_text("__global__ void k(float* x) {\n  x[0] = 1.0f;  // one\n}\n")
+    b = tmp_path / "b.hip"
+    b.write_text("// a header\n__global__ void k(float* x) {\n\n  x[0] = 1.0f;  // another comment\n}\n")
+    c = tmp_path / "c.hip"
+    c.write_text("__global__ void k(float* x) {\n  x[0] = 2.0f;  // one\n}\n")
+    assert bench.code_digest(str(a)) == bench.code_digest(str(b))
+    assert bench.code_digest(str(a)) != bench.code_digest(str(c))
